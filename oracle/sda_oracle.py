@@ -1,0 +1,294 @@
+"""CPU oracle for top-k block-sparse decode attention (test infrastructure).
+
+This module is the plain, slow, float64 statement of what the decode path
+computes.  It is test infrastructure: only the test suite, the package smoke
+check and the benchmark's CPU-baseline leg may import it.  The HIP library
+never calls it, and it shares no code, table or helper with the HIP library.
+
+Sources (cited by page title and section/equation):
+  [SparDA]  reading note "SparDA：稀疏解耦注意力，让长上下文推理又快又准"
+            (zhongzhuzhou.org, 2026-06-24) on SparDA: Sparse Decoupled
+            Attention (arXiv 2606.04511).
+  [SSV]     reading note "SSV：稀疏投机验证——在动态稀疏注意力中做投机解码"
+            (zhongzhuzhou.org, 2026-07-01) on SSV: Sparse Speculative
+            Verification (arXiv 2605.19893).
+
+Arithmetic is float64 throughout.  bf16 inputs arrive as uint16 bit patterns
+and are decoded exactly.  Two places store or decide in float32, because the
+kernel's stored tensor or decision is float32 and an integer result must be
+decided in the same precision on both sides:
+  * the compressed key cache is stored rounded to float32 (``store_f32``);
+  * top-k ranks block scores after rounding them to float32
+    (``decision_scores``); equal float32 scores go to the lower block index.
+
+Readings of points the pages leave open (numbered as in the design notes):
+  block = pooling kernel = stride = 64 tokens; a partial last block is the
+  mean of the tokens present; the local window is the last n_local blocks;
+  init/local blocks do not compete in top-k; output block lists ascend;
+  query head h reads KV head floor(h / G); attention scale 1/sqrt(d);
+  the G-head comparator sums per-head softmax over all blocks with tau = sqrt(d).
+
+Parity pins: every function here is pinned by tests under tests/ against
+closed forms, brute force or an independent library routine, except the
+comparator's temperature tau, which the pages never give ("parity unpinned"
+for the value of tau only; its ranking with G = 1 is pinned).
+"""
+import numpy as np
+
+BLOCK = 64
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits):
+    """Exact decode of bf16 bit patterns (uint16 array) to float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def store_f32(x):
+    """Round float64 values to the float32 the compressed-key cache stores."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def decision_scores(s):
+    """Scores as ranked by top-k: float64 values rounded to float32."""
+    return np.asarray(s, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def num_blocks(T, block=BLOCK):
+    return -(-int(T) // block)
+
+
+# ---------------------------------------------------------------------------
+# O1  compressed keys  ([SparDA] prerequisites §3, eq. (4); §4.2 step 1; §4.6)
+# ---------------------------------------------------------------------------
+
+def compressed_keys(k, T, block=BLOCK):
+    """Mean-pooled keys over non-overlapping blocks.
+
+    k: float64 [>=T, d] keys of one (sequence, KV head); T cached tokens.
+    Returns float64 [ceil(T/block), d]; block j is the mean of tokens
+    j*block .. min(j*block+block, T)-1 (eq. (4) with kernel = stride = block;
+    a partial last block averages the tokens it has).
+    """
+    T = int(T)
+    nb = num_blocks(T, block)
+    out = np.empty((nb, k.shape[-1]), dtype=np.float64)
+    for j in range(nb):
+        lo, hi = j * block, min(j * block + block, T)
+        out[j] = np.mean(k[lo:hi], axis=0)
+    return out
+
+
+def append_token(kt, T_old, k_new, block=BLOCK):
+    """Per-token incremental update of the compressed keys, O(d) work.
+
+    The decode step appends one key and refreshes the pooled cache
+    incrementally ([SparDA] §4.2 step 1, §4.6).  kt: float64 [>=ceil(T_old/block), d]
+    (rows past the last block are ignored); returns the array for T_old + 1
+    tokens.  A key that opens a new block becomes that block's mean; otherwise
+    the running mean of the last block moves by (k_new - mean) / (n + 1).
+    """
+    T_old = int(T_old)
+    nb_old = num_blocks(T_old, block)
+    n_in_last = T_old - (nb_old - 1) * block if T_old > 0 else 0
+    if T_old % block == 0:
+        out = np.zeros((nb_old + 1, k_new.shape[-1]), dtype=np.float64)
+        out[:nb_old] = kt[:nb_old]
+        out[nb_old] = k_new
+        return out
+    out = np.array(kt[:nb_old], dtype=np.float64, copy=True)
+    out[nb_old - 1] = out[nb_old - 1] + (k_new - out[nb_old - 1]) / (n_in_last + 1)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O2-O6  block selection  ([SparDA] eq. (3), eq. (6), eq. (9), §4.2 step 2;
+#        [SSV] NSA selection branch, steps 1-2)
+# ---------------------------------------------------------------------------
+
+def init_local(nb, n_init, n_local):
+    """Initial blocks {0..n_init-1} and local blocks {nb-n_local..nb-1},
+    both clipped to [0, nb) (eq. (3)): returns (init_set, local_set)."""
+    init = set(range(0, min(n_init, nb)))
+    local = set(range(max(0, nb - n_local), nb))
+    return init, local
+
+
+def candidates(nb, n_init, n_local):
+    """Blocks that compete in top-k: all blocks minus the initial and local
+    ones (§4.2 step 2 excludes the fixed blocks before top-k).  Ascending."""
+    init, local = init_local(nb, n_init, n_local)
+    return np.array([j for j in range(nb) if j not in init and j not in local], dtype=np.int64)
+
+
+def indexer_scores(f, kt):
+    """Raw block scores s_j = f . K~_j for every block (eq. (6) and (9)).
+
+    The softmax over blocks with temperature in eq. (9) is monotone, so it
+    does not change which blocks are chosen; the raw dot product is what the
+    decode-time indexer ranks.  f: float64 [d]; kt: float64 [nb, d].
+    """
+    return kt @ np.asarray(f, dtype=np.float64)
+
+
+def top_k(scores, cand, k):
+    """The k candidates of largest score, ties to the lower block index
+    (f_top in eq. (6)).  scores: [nb] (decision precision); cand: ascending
+    candidate block ids.  Returns the chosen ids in rank order."""
+    cand = np.asarray(cand, dtype=np.int64)
+    if k <= 0 or cand.size == 0:
+        return np.zeros(0, dtype=np.int64)
+    s = np.asarray(scores, dtype=np.float64)[cand]
+    order = np.lexsort((cand, -s))          # primary: -score, secondary: index
+    return cand[order[: min(int(k), cand.size)]]
+
+
+def block_set(nb, n_init, n_local, chosen):
+    """B = B_init U B_local U B_topk as an ascending list without repeats (eq. (3))."""
+    init, local = init_local(nb, n_init, n_local)
+    return np.array(sorted(init | local | set(int(j) for j in chosen)), dtype=np.int64)
+
+
+def select_row(f, kt_stored, n_init, n_local, k):
+    """Steps O2-O6 for one row: returns (ascending block ids, decision scores)."""
+    nb = kt_stored.shape[0]
+    s = decision_scores(indexer_scores(f, kt_stored))
+    cand = candidates(nb, n_init, n_local)
+    return block_set(nb, n_init, n_local, top_k(s, cand, k)), s
+
+
+def cut_gap(scores, cand, k):
+    """Gap between the k-th and (k+1)-th best candidate scores (inf when
+    every candidate or none is chosen).  Used to build inputs without
+    near-ties at the top-k cut."""
+    cand = np.asarray(cand, dtype=np.int64)
+    if k <= 0 or k >= cand.size:
+        return np.inf
+    s = np.sort(np.asarray(scores, dtype=np.float64)[cand])[::-1]
+    return float(s[k - 1] - s[k])
+
+
+# ---------------------------------------------------------------------------
+# O10  G-head comparator  ([SparDA] §4.3 eq. (8); §4.4 eq. (10))
+# ---------------------------------------------------------------------------
+
+def multihead_scores(q_heads, kt, tau):
+    """InfLLM-V2-style block importance from all G query heads of a group:
+    s_j = sum_h softmax_j(q_h . K~_j / tau), softmax over all nb blocks.
+    q_heads: float64 [G, d]; kt: float64 [nb, d].  With kernel = stride =
+    block the max-pool onto the block grid is the identity."""
+    z = (np.asarray(q_heads, dtype=np.float64) @ kt.T) / float(tau)   # [G, nb]
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    p = e / e.sum(axis=1, keepdims=True)
+    return p.sum(axis=0)
+
+
+def select_row_multihead(q_heads, kt_stored, n_init, n_local, k, tau):
+    nb = kt_stored.shape[0]
+    s = decision_scores(multihead_scores(q_heads, kt_stored, tau))
+    cand = candidates(nb, n_init, n_local)
+    return block_set(nb, n_init, n_local, top_k(s, cand, k)), s
+
+
+# ---------------------------------------------------------------------------
+# O7  attention over the selected blocks  ([SparDA] eq. (7); [SSV] NSA
+#     selection-branch attention, step 3)
+# ---------------------------------------------------------------------------
+
+def block_tokens(blocks, T, block=BLOCK):
+    """Token positions covered by the blocks, clipped at T, in block order."""
+    T = int(T)
+    parts = [np.arange(j * block, min(j * block + block, T)) for j in blocks if j * block < T]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+def attend(q, k, v, blocks, T, scale):
+    """softmax(q K_B^T * scale) V_B for one query head; two-pass softmax.
+
+    q: float64 [d]; k, v: float64 [>=T, d]; returns (o [d], lse) with lse the
+    natural-log sum of exp of the scaled scores."""
+    tok = block_tokens(blocks, T)
+    z = (k[tok] @ np.asarray(q, dtype=np.float64)) * float(scale)
+    m = z.max()
+    p = np.exp(z - m)
+    l = p.sum()
+    return (p @ v[tok]) / l, float(m + np.log(l))
+
+
+def decode_row(q_heads, k, v, blocks, T, scale):
+    """O7 for every query head that shares one KV head: q_heads [G, d]."""
+    outs, lses = [], []
+    for h in range(q_heads.shape[0]):
+        o, lse = attend(q_heads[h], k, v, blocks, T, scale)
+        outs.append(o)
+        lses.append(lse)
+    return np.stack(outs), np.array(lses)
+
+
+# ---------------------------------------------------------------------------
+# O8-O9  grouped verification  ([SSV] core mechanism 1: grouping, mode A
+#        exact merge, mode B shared representative, bandwidth-saving formula;
+#        verification-kernel algorithm steps 2-3)
+# ---------------------------------------------------------------------------
+
+MODE_EXACT = 0
+MODE_SHARED_REP = 1
+
+
+def groups(nq, C):
+    """Consecutive groups of C queries; the last one may be smaller."""
+    return [list(range(s, min(s + C, nq))) for s in range(0, nq, C)]
+
+
+def union_blocks(lists):
+    """I_merged = union of the group's block lists, ascending."""
+    u = set()
+    for lst in lists:
+        u |= set(int(j) for j in lst)
+    return np.array(sorted(u), dtype=np.int64)
+
+
+def load_counts(lists):
+    """How many times each block would be loaded if every query loaded its own list."""
+    c = {}
+    for lst in lists:
+        for j in lst:
+            c[int(j)] = c.get(int(j), 0) + 1
+    return c
+
+
+def grouped_row(q_rows, k, v, lists, T, scale, mode):
+    """Grouped attention for one (sequence, group, KV head).
+
+    q_rows: float64 [C, G, d] (query c, head h); lists: the C block lists.
+    Mode A: query c attends to its own list (the merged set is only what is
+    loaded).  Mode B: every query attends to the first query's list.
+    Returns (out [C, G, d], lse [C, G], union_count)."""
+    C = len(lists)
+    if mode == MODE_EXACT:
+        active = list(lists)
+        ucount = len(union_blocks(lists))
+    else:
+        active = [lists[0]] * C
+        ucount = len(union_blocks([lists[0]]))
+    outs, lses = [], []
+    for c in range(C):
+        o, l = decode_row(q_rows[c], k, v, active[c], T, scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses), ucount
+
+
+def union_size_formula(n, C, gamma):
+    """Approximate merged-set size n * (1 + (C-1)(1-gamma)) ([SSV] bandwidth-saving formula)."""
+    return n * (1.0 + (C - 1) * (1.0 - gamma))
+
+
+def saving_formula(C, gamma):
+    """Fraction of block loads saved by merging: (C-1) * gamma / C."""
+    return (C - 1) * gamma / C

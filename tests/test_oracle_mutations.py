@@ -1,0 +1,145 @@
+"""Planted mistakes: each test swaps one oracle function for a plausibly wrong
+version (on the CPU, in this process only) and checks that at least one pin
+in test_oracle_pins.py then fails.  This is how the pins are shown to bind.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.sda_oracle as impl
+from tests import test_oracle_pins as pins
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(impl, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def _fails(*pin_fns):
+    for fn in pin_fns:
+        try:
+            fn()
+        except (AssertionError, IndexError, ValueError):
+            return True
+    return False
+
+
+def _param_pin(fn, *args):
+    return lambda: fn(*args)
+
+
+def test_mutant_pool_divides_by_full_block(monkeypatch):
+    def bad(k, T, block=64):
+        nb = impl.num_blocks(T, block)
+        return np.stack([k[j * block:min(j * block + block, T)].sum(0) / block for j in range(nb)])
+    _patch(monkeypatch, "compressed_keys", bad)
+    assert _fails(pins.test_compressed_keys_partial_last_block)
+
+
+def test_mutant_pool_shifted_window(monkeypatch):
+    def bad(k, T, block=64):
+        nb = impl.num_blocks(T, block)
+        return np.stack([k[j * block + 1:min(j * block + block + 1, T)].mean(0) for j in range(nb)])
+    _patch(monkeypatch, "compressed_keys", bad)
+    assert _fails(pins.test_compressed_keys_constant_block)
+
+
+def test_mutant_incremental_wrong_count(monkeypatch):
+    def bad(kt, T_old, k_new, block=64):
+        nb_old = impl.num_blocks(T_old, block)
+        if T_old % block == 0:
+            out = np.zeros((nb_old + 1, k_new.shape[-1]))
+            out[:nb_old] = kt[:nb_old]
+            out[nb_old] = k_new
+            return out
+        n = T_old - (nb_old - 1) * block
+        out = np.array(kt[:nb_old], copy=True)
+        out[nb_old - 1] += (k_new - out[nb_old - 1]) / n          # should be n + 1
+        return out
+    _patch(monkeypatch, "append_token", bad)
+    assert _fails(pins.test_incremental_update_matches_bulk)
+
+
+def test_mutant_score_sign(monkeypatch):
+    _patch(monkeypatch, "indexer_scores", lambda f, kt: -(kt @ f))
+    assert _fails(pins.test_indexer_scores_orientation)
+
+
+def test_mutant_top_k_smallest(monkeypatch):
+    def bad(scores, cand, k):
+        cand = np.asarray(cand)
+        if k <= 0 or cand.size == 0:
+            return np.zeros(0, dtype=np.int64)
+        order = np.lexsort((cand, np.asarray(scores)[cand]))
+        return cand[order[:k]]
+    _patch(monkeypatch, "top_k", bad)
+    assert _fails(pins.test_top_k_brute_force_small, pins.test_top_k_certificate_and_counts)
+
+
+def test_mutant_tie_to_higher_index(monkeypatch):
+    def bad(scores, cand, k):
+        cand = np.asarray(cand)
+        if k <= 0 or cand.size == 0:
+            return np.zeros(0, dtype=np.int64)
+        order = np.lexsort((-cand, -np.asarray(scores)[cand]))
+        return cand[order[:k]]
+    _patch(monkeypatch, "top_k", bad)
+    assert _fails(pins.test_top_k_ties_go_to_lower_index)
+
+
+def test_mutant_local_window_off_by_one(monkeypatch):
+    def bad(nb, n_init, n_local):
+        return set(range(min(n_init, nb))), set(range(max(0, nb - n_local - 1), nb - 1))
+    _patch(monkeypatch, "init_local", bad)
+    assert _fails(pins.test_init_local_hand_cases, pins.test_select_all_and_none)
+
+
+def test_mutant_attention_without_scale(monkeypatch):
+    real = impl.attend
+    _patch(monkeypatch, "attend", lambda q, k, v, b, T, scale: real(q, k, v, b, T, 1.0))
+    assert _fails(pins.test_attend_all_blocks_equals_dense_sdpa)
+
+
+def test_mutant_attention_ignores_length(monkeypatch):
+    def bad(blocks, T, block=64):
+        return np.concatenate([np.arange(j * block, j * block + block) for j in blocks])
+    _patch(monkeypatch, "block_tokens", bad)
+    assert _fails(pins.test_attend_selected_blocks_equals_sdpa_on_gathered_tokens,
+                  pins.test_attend_all_blocks_equals_dense_sdpa)
+
+
+def test_mutant_attention_transposed_value(monkeypatch):
+    def bad(q, k, v, blocks, T, scale):
+        tok = impl.block_tokens(blocks, T)
+        z = (k[tok] @ q) * scale
+        p = np.exp(z - z.max())
+        return (p @ k[tok]) / p.sum(), float(z.max() + np.log(p.sum()))     # K used as V
+    _patch(monkeypatch, "attend", bad)
+    assert _fails(pins.test_attend_closed_forms)
+
+
+def test_mutant_softmax_over_heads(monkeypatch):
+    def bad(q_heads, kt, tau):
+        z = (q_heads @ kt.T) / tau
+        e = np.exp(z - z.max(axis=0, keepdims=True))
+        return (e / e.sum(axis=0, keepdims=True)).sum(0)             # normalised over heads
+    _patch(monkeypatch, "multihead_scores", bad)
+    assert _fails(pins.test_multihead_scores_sum_and_symmetry)
+
+
+def test_mutant_mode_b_uses_last_query(monkeypatch):
+    real = impl.grouped_row
+
+    def bad(q_rows, k, v, lists, T, scale, mode):
+        if mode == impl.MODE_SHARED_REP:
+            lists = [lists[-1]] + list(lists[1:])
+        return real(q_rows, k, v, lists, T, scale, mode)
+    _patch(monkeypatch, "grouped_row", bad)
+    assert _fails(pins.test_grouped_modes)
+
+
+@pytest.mark.parametrize("gamma,want", [(0.75, 28)])
+def test_mutant_union_formula_sign(monkeypatch, gamma, want):
+    _patch(monkeypatch, "union_size_formula", lambda n, C, g: n * (1 + (C - 1) * g))
+    assert _fails(pins.test_union_formula_printed_values,
+                  _param_pin(pins.test_union_size_on_chain_constructed_sets, gamma, want))
