@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark: top-k block-sparse decode on one MI355X.
+
+One step = one layer's decode step of the 70B-shaped 128K workload: the
+indexer vectors of layer l score layer l+1's compressed keys, top-k picks
+the blocks (sda_score_select), and the query heads of layer l+1 attend to
+them (sda_sparse_decode).  Steps walk a ring of distinct layers whose K/V,
+compressed keys and vectors are all resident in HBM, so every step reads
+cold data as a real layer stack does (the ring is larger than the L2 and
+Infinity caches together).
+
+Prints one JSON line.  `value` is whole-job queries/s over the timed steps
+(one query = one sequence's decode token); `roofline` prices the decode
+call (attention kernel + split combine) against the 8 TB/s HBM peak on its
+algorithmic bytes (the selected K/V blocks); `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--config 3] [--layers L]
+  python bench.py --copy-calibration     (plain copy of known size, for counter scaling)
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_sparse_attention_pool_amd as sda  # noqa: E402
+import synth  # noqa: E402
+from synth import inputs  # noqa: E402
+
+METRIC = "sparse-decode queries/s + achieved HBM GB/s (% of peak) at 128K ctx"
+HBM_PEAK_GBS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "sparse_decode_c3_counters.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_pool_amd", "csrc", "k_attention.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def build_layers(cfg, n_layers, dev):
+    """K, V, compressed keys, indexer vectors and queries for a ring of layers."""
+    layers = []
+    for l in range(n_layers):
+        t0 = time.time()
+        K, V, _ = inputs.kv_layer(cfg, l, device=dev)
+        kt = torch.zeros((cfg.B, cfg.H_kv, cfg.NB, cfg.d), dtype=torch.float32, device=dev)
+        lo = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+        hi = torch.full((cfg.B,), cfg.T, dtype=torch.int32, device=dev)
+        sda.sda_update_compressed_keys(K, kt, lo, hi, cfg.T)
+        F = inputs.to_bf16(inputs.indexer_vectors(cfg, l), dev)
+        Q = inputs.to_bf16(inputs.attention_queries(cfg, l), dev)
+        torch.cuda.synchronize()
+        layers.append(dict(K=K, V=V, kt=kt, F=F, Q=Q))
+        log(f"layer {l}: K/V {2 * K.numel() * 2 / 1e9:.2f} GB drawn, compressed keys built "
+            f"({time.time() - t0:.1f} s)")
+    return layers
+
+
+def cpu_baseline(cfg, layer_l, layer_n, budget_s=12.0, max_rows=64):
+    """Time the CPU oracle's per-step work (scores, top-k, block set,
+    attention) on rows of the same workload: F of layer l against layer l+1.
+    Building the oracle's compressed keys is setup, not timed."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    Fd = O.bf16_to_f64(inputs.bf16_bits(layer_l["F"]))
+    Qd = O.bf16_to_f64(inputs.bf16_bits(layer_n["Q"]))
+    G, T = cfg.G, cfg.T
+    scale = 1.0 / math.sqrt(cfg.d)
+    rows = [(b, g) for b in range(cfg.B) for g in range(cfg.H_kv)]
+    timed = 0.0
+    done = 0
+    for (b, g) in rows[:max_rows]:
+        kk = O.bf16_to_f64(inputs.bf16_bits(layer_n["K"][b, g]))
+        vv = O.bf16_to_f64(inputs.bf16_bits(layer_n["V"][b, g]))
+        kt = O.store_f32(O.compressed_keys(kk, T))
+        t0 = time.perf_counter()
+        blocks, _ = O.select_row(Fd[b, 0, g], kt, cfg.n_init, cfg.n_local, cfg.top_k)
+        O.decode_row(Qd[b, 0, g * G:(g + 1) * G], kk, vv, blocks, T, scale)
+        timed += time.perf_counter() - t0
+        done += 1
+        if timed > budget_s:
+            break
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    rows_per_s = done / timed
+    return {
+        "value": rows_per_s / cfg.H_kv,
+        "unit": "queries/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {len(rows)} (batch, KV head) rows of the 128K workload, "
+                  f"float64 NumPy, one thread; scoring + top-k + block set + attention per row, "
+                  f"{timed:.2f} s timed; a query = all {cfg.H_kv} KV heads of one sequence",
+    }
+
+
+def copy_calibration(nbytes=1 << 30):
+    dev = "cuda"
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--split-k", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the decode path has no multi-GPU mode "
+              "(sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    cfg = synth.get_config(args.config)
+    dev = "cuda"
+    sda.lib()
+    log(f"config {cfg.cid}: {cfg.name}; ring of {args.layers} layers")
+    layers = build_layers(cfg, args.layers, dev)
+    L = len(layers)
+    seq = torch.full((cfg.B,), cfg.T, dtype=torch.int32, device=dev)
+    n_sel_max = cfg.n_init + cfg.n_local + cfg.top_k
+    bi = [torch.empty((cfg.B, 1, cfg.H_kv, n_sel_max), dtype=torch.int32, device=dev) for _ in range(L)]
+    ns = [torch.empty((cfg.B, 1, cfg.H_kv), dtype=torch.int32, device=dev) for _ in range(L)]
+    out = torch.empty((cfg.B, 1, cfg.H_q, cfg.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, 1, cfg.H_q), dtype=torch.float32, device=dev)
+    ws_sel = torch.empty(sda.lib().sda_score_select_workspace(cfg.B, 1, cfg.H_kv, cfg.NB, cfg.top_k),
+                         dtype=torch.uint8, device=dev)
+    nb_dec = sda.lib().sda_sparse_decode_workspace(cfg.B, 1, cfg.H_q, cfg.H_kv, n_sel_max, cfg.d, args.split_k)
+    ws_dec = torch.empty(max(nb_dec, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        lc, ln = layers[(i - 1) % L], layers[i % L]
+        if ev is not None:
+            ev[0].record(stream)
+        sda.sda_score_select(lc["F"], ln["kt"], seq, cfg.n_init, cfg.n_local, cfg.top_k,
+                             block_idx=bi[i % L], n_sel=ns[i % L], ws=ws_sel)
+        if ev is not None:
+            ev[1].record(stream)
+        sda.sda_sparse_decode(ln["Q"], ln["K"], ln["V"], seq, bi[i % L], ns[i % L], out=out, lse=lse,
+                              split_k=args.split_k, ws=ws_dec)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events on the launch stream around each call
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_sel = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_dec = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+
+    queries = cfg.B * cfg.NQ
+    value = queries * args.steps / wall
+    dec_bytes = cfg.selected_kv_bytes()
+    sel_bytes = cfg.ktilde_bytes()
+    dec_gbs = dec_bytes / t_dec.mean() / 1e9
+    traffic = None
+    if os.path.exists(PROFILE_COUNTERS):
+        try:
+            pc = json.load(open(PROFILE_COUNTERS))
+            if pc.get("kernel_hash") == kernel_hash() and pc.get("config") == cfg.cid:
+                traffic = pc.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: B={cfg.B}, H_q={cfg.H_q}, H_kv={cfg.H_kv}, d={cfg.d}, T={cfg.T}, "
+                        f"64-token blocks, {cfg.n_init} init + {cfg.n_local} local + top-{cfg.top_k}, "
+                        f"F(layer l) . K~(layer l+1), ring of {L} resident layers",
+            "global_batch": cfg.B,
+            "seq_len": cfg.T,
+            "parallelism": "single GPU",
+            "config_id": cfg.cid,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": dec_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": dec_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "sda_sparse_decode (attention kernel + split combine)",
+            "algorithmic_bytes_per_launch": dec_bytes,
+        },
+        "kernels_us": {
+            "score_select_mean": t_sel.mean() * 1e6, "score_select_p50": float(np.median(t_sel)) * 1e6,
+            "sparse_decode_mean": t_dec.mean() * 1e6, "sparse_decode_p50": float(np.median(t_dec)) * 1e6,
+            "sparse_decode_p10": float(np.percentile(t_dec, 10)) * 1e6,
+            "sparse_decode_p90": float(np.percentile(t_dec, 90)) * 1e6,
+        },
+        "score_select_gbs": sel_bytes / t_sel.mean() / 1e9,
+        "queries_per_s_from_kernels": queries / (t_sel.mean() + t_dec.mean()),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, layers[0], layers[1 % L])
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

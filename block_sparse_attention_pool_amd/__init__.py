@@ -1,0 +1,298 @@
+"""Python binding of libsda (top-k block-sparse decode attention, gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of libsda.so.
+torch supplies device memory and the current stream.  The functions carry
+the C names; each checks dtypes, contiguity and devices, derives the sizes
+from the tensor shapes, allocates outputs and workspace when they are not
+given, and raises SdaError when the library returns a non-zero status.
+
+Layouts (bf16 given as torch.bfloat16, int32 as torch.int32):
+  K, V      [B, H_kv, T_cap, d]      k_tilde   [B, H_kv, NB_cap, d] float32
+  f         [B, NQ, H_kv, d]         q         [B, NQ, H_q, d]
+  block_idx [B, NQ, H_kv, n_sel_max] n_sel     [B, NQ, H_kv]
+  out       [B, NQ, H_q, d] float32  lse       [B, NQ, H_q] float32
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsda.so")
+
+SDA_GROUP_EXACT = 0
+SDA_GROUP_SHARED_REP = 1
+BLOCK = 64
+
+_c_void_p = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_float = ctypes.c_float
+_c_size_t = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/sda.h
+_SIGNATURES = {
+    "sda_status_string": (ctypes.c_char_p, [_c_int]),
+    "sda_last_error": (ctypes.c_char_p, []),
+    "sda_version": (ctypes.c_char_p, []),
+    "sda_update_compressed_keys": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                                            _c_int, _c_int, _c_int, _c_int, _c_void_p]),
+    "sda_score_select_workspace": (_c_size_t, [_c_int] * 5),
+    "sda_score_select": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                  _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_void_p, _c_size_t, _c_void_p]),
+    "sda_score_select_multihead_workspace": (_c_size_t, [_c_int] * 6),
+    "sda_score_select_multihead": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                                            _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
+                                            _c_void_p]),
+    "sda_sparse_decode_workspace": (_c_size_t, [_c_int] * 7),
+    "sda_sparse_decode": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                   _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                   _c_void_p, _c_void_p, _c_int, _c_void_p, _c_size_t, _c_void_p]),
+    "sda_grouped_decode_workspace": (_c_size_t, [_c_int] * 8),
+    "sda_grouped_decode": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
+                                    _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_size_t,
+                                    _c_void_p]),
+    "sda_gather_blocks": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int,
+                                   _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p]),
+}
+
+_lib = None
+
+
+class SdaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{status_string(status) if _lib else status}: {msg}")
+        self.status = status
+
+
+def lib():
+    """The loaded libsda.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_attention_pool_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGNATURES)
+
+
+def status_string(s):
+    return lib().sda_status_string(int(s)).decode()
+
+
+def last_error():
+    return lib().sda_last_error().decode()
+
+
+def version():
+    return lib().sda_version().decode()
+
+
+def _check(st):
+    if st != 0:
+        raise SdaError(st, last_error())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t, name, dtype, ndim=None, device=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _workspace(nbytes, device, ws=None):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None:
+        return ws, ws.numel() * ws.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+# ---------------------------------------------------------------------------
+
+def sda_update_compressed_keys(k, k_tilde, len_old, len_new, max_new_tokens, stream=None):
+    """Recompute the mean-pooled block keys touched by tokens [len_old, len_new)."""
+    _need(k, "k", torch.bfloat16, 4)
+    _need(k_tilde, "k_tilde", torch.float32, 4)
+    _need(len_old, "len_old", torch.int32, 1)
+    _need(len_new, "len_new", torch.int32, 1)
+    B, H, T_cap, d = k.shape
+    if k_tilde.shape[:2] != (B, H) or k_tilde.shape[3] != d or len_old.numel() != B or len_new.numel() != B:
+        raise ValueError("shape mismatch between k, k_tilde and the length arrays")
+    _check(lib().sda_update_compressed_keys(_ptr(k), _ptr(k_tilde), _ptr(len_old), _ptr(len_new),
+                                            int(max_new_tokens), B, H, d, T_cap, k_tilde.shape[2],
+                                            _stream(stream)))
+    return k_tilde
+
+
+def sda_score_select(f, k_tilde, seq_len, n_init, n_local, top_k, n_sel_max=None, block_idx=None,
+                     n_sel=None, scores=None, ws=None, stream=None):
+    """Indexer scores, exact top-k and block-set assembly; returns (block_idx, n_sel)."""
+    _need(f, "f", torch.bfloat16, 4)
+    _need(k_tilde, "k_tilde", torch.float32, 4)
+    _need(seq_len, "seq_len", torch.int32, 1)
+    B, NQ, H, d = f.shape
+    NB_cap = k_tilde.shape[2]
+    if k_tilde.shape[:2] != (B, H) or k_tilde.shape[3] != d:
+        raise ValueError("k_tilde must be [B, H_kv, NB_cap, d] matching f")
+    if n_sel_max is None:
+        n_sel_max = n_init + n_local + top_k
+    if block_idx is None:
+        block_idx = torch.empty((B, NQ, H, n_sel_max), dtype=torch.int32, device=f.device)
+    if n_sel is None:
+        n_sel = torch.empty((B, NQ, H), dtype=torch.int32, device=f.device)
+    _need(block_idx, "block_idx", torch.int32, 4)
+    _need(n_sel, "n_sel", torch.int32, 3)
+    if scores is not None:
+        _need(scores, "scores", torch.float32, 4)
+        nbytes = 0
+    else:
+        nbytes = lib().sda_score_select_workspace(B, NQ, H, NB_cap, top_k)
+    ws, wsb = _workspace(nbytes, f.device, ws)
+    _check(lib().sda_score_select(_ptr(f), _ptr(k_tilde), _ptr(seq_len), B, NQ, H, d, NB_cap, n_init, n_local,
+                                  top_k, n_sel_max, _ptr(block_idx), _ptr(n_sel), _ptr(scores), _ptr(ws), wsb,
+                                  _stream(stream)))
+    return block_idx, n_sel
+
+
+def sda_score_select_multihead(q, k_tilde, seq_len, n_init, n_local, top_k, tau, H_kv=None, n_sel_max=None,
+                               block_idx=None, n_sel=None, scores=None, ws=None, stream=None):
+    """G-head softmax-sum selector (comparator); returns (block_idx, n_sel)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_tilde, "k_tilde", torch.float32, 4)
+    _need(seq_len, "seq_len", torch.int32, 1)
+    B, NQ, H_q, d = q.shape
+    H = k_tilde.shape[1] if H_kv is None else H_kv
+    NB_cap = k_tilde.shape[2]
+    if n_sel_max is None:
+        n_sel_max = n_init + n_local + top_k
+    if block_idx is None:
+        block_idx = torch.empty((B, NQ, H, n_sel_max), dtype=torch.int32, device=q.device)
+    if n_sel is None:
+        n_sel = torch.empty((B, NQ, H), dtype=torch.int32, device=q.device)
+    if scores is not None:
+        _need(scores, "scores", torch.float32, 4)
+    nbytes = lib().sda_score_select_multihead_workspace(B, NQ, H_q, H, NB_cap, top_k)
+    ws, wsb = _workspace(nbytes, q.device, ws)
+    _check(lib().sda_score_select_multihead(_ptr(q), _ptr(k_tilde), _ptr(seq_len), B, NQ, H_q, H, d, NB_cap,
+                                            n_init, n_local, top_k, n_sel_max, float(tau), _ptr(block_idx),
+                                            _ptr(n_sel), _ptr(scores), _ptr(ws), wsb, _stream(stream)))
+    return block_idx, n_sel
+
+
+def sda_sparse_decode(q, k, v, seq_len, block_idx, n_sel, scale=None, out=None, lse=None, slot=None,
+                      split_k=0, ws=None, stream=None):
+    """Block-sparse decode attention; returns (out, lse)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(seq_len, "seq_len", torch.int32, 1)
+    _need(block_idx, "block_idx", torch.int32, 4)
+    _need(n_sel, "n_sel", torch.int32, 3)
+    B, NQ, H_q, d = q.shape
+    H_kv, T_cap = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must both be [B, H_kv, T_cap, d] matching q")
+    n_sel_max = block_idx.shape[3]
+    if slot is not None:
+        _need(slot, "slot", torch.int32, 4)
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty((B, NQ, H_q, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, NQ, H_q), dtype=torch.float32, device=q.device)
+    nbytes = lib().sda_sparse_decode_workspace(B, NQ, H_q, H_kv, n_sel_max, d, int(split_k))
+    ws, wsb = _workspace(nbytes, q.device, ws)
+    _check(lib().sda_sparse_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(block_idx), _ptr(n_sel),
+                                   n_sel_max, _ptr(slot), T_cap, B, NQ, H_q, H_kv, d, float(scale), _ptr(out),
+                                   _ptr(lse), int(split_k), _ptr(ws), wsb, _stream(stream)))
+    return out, lse
+
+
+def sda_grouped_decode(q, k, v, seq_len, block_idx, n_sel, group_C, mode=SDA_GROUP_EXACT, scale=None,
+                       NB_cap=None, out=None, lse=None, union_count=None, split_k=0, ws=None, stream=None):
+    """SSV grouped verification decode; returns (out, lse, union_count)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(seq_len, "seq_len", torch.int32, 1)
+    _need(block_idx, "block_idx", torch.int32, 4)
+    _need(n_sel, "n_sel", torch.int32, 3)
+    B, NQ, H_q, d = q.shape
+    H_kv, T_cap = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must both be [B, H_kv, T_cap, d] matching q")
+    n_sel_max = block_idx.shape[3]
+    if NB_cap is None:
+        NB_cap = -(-T_cap // BLOCK)
+    if scale is None:
+        scale = d ** -0.5
+    n_groups = -(-NQ // group_C)
+    if out is None:
+        out = torch.empty((B, NQ, H_q, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, NQ, H_q), dtype=torch.float32, device=q.device)
+    if union_count is None:
+        union_count = torch.empty((B, n_groups, H_kv), dtype=torch.int32, device=q.device)
+    nbytes = lib().sda_grouped_decode_workspace(B, NQ, H_q, H_kv, n_sel_max, d, int(group_C), int(split_k))
+    ws, wsb = _workspace(nbytes, q.device, ws)
+    _check(lib().sda_grouped_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(block_idx), _ptr(n_sel),
+                                    n_sel_max, T_cap, int(NB_cap), B, NQ, H_q, H_kv, d, float(scale),
+                                    int(group_C), int(mode), _ptr(out), _ptr(lse), _ptr(union_count),
+                                    int(split_k), _ptr(ws), wsb, _stream(stream)))
+    return out, lse, union_count
+
+
+def sda_gather_blocks(k_host, v_host, block_idx, n_sel, k_stage=None, v_stage=None, slot=None,
+                      max_workgroups=0, stream=None):
+    """Copy the selected blocks of pinned host K/V into a device stage.
+
+    k_host, v_host: pinned CPU bf16 [B, H_kv, T_cap, d]; block_idx [B, 1, H_kv, n_sel_max]
+    or [B, H_kv, n_sel_max]; returns (k_stage, v_stage, slot) with slot shaped like block_idx."""
+    _need(k_host, "k_host", torch.bfloat16, 4, device=False)
+    _need(v_host, "v_host", torch.bfloat16, 4, device=False)
+    if not (k_host.is_pinned() and v_host.is_pinned()):
+        raise ValueError("k_host and v_host must be pinned host memory")
+    B, H_kv, T_cap, d = k_host.shape
+    n_sel_max = block_idx.shape[-1]
+    if block_idx.numel() != B * H_kv * n_sel_max or n_sel.numel() != B * H_kv:
+        raise ValueError("block_idx / n_sel must hold one row per (batch, KV head)")
+    dev = block_idx.device
+    if k_stage is None:
+        k_stage = torch.empty((B, H_kv, n_sel_max * BLOCK, d), dtype=torch.bfloat16, device=dev)
+    if v_stage is None:
+        v_stage = torch.empty((B, H_kv, n_sel_max * BLOCK, d), dtype=torch.bfloat16, device=dev)
+    if slot is None:
+        slot = torch.empty(block_idx.shape, dtype=torch.int32, device=dev)
+    _check(lib().sda_gather_blocks(_ptr(k_host), _ptr(v_host), _ptr(block_idx), _ptr(n_sel), n_sel_max, B,
+                                   H_kv, d, T_cap, _ptr(k_stage), _ptr(v_stage), _ptr(slot),
+                                   int(max_workgroups), _stream(stream)))
+    return k_stage, v_stage, slot

@@ -1,0 +1,351 @@
+// Block scoring, exact top-k and block-set assembly.
+//
+// Scoring ([SparDA] note eq. (6) and (9), §4.2 step 2; [SSV] note, NSA
+// selection-branch step 1): s_j = f . K~_j for every block of a row, fp32.
+// One workgroup per (batch, KV head, 256-block chunk, vector tile): the
+// chunk of K~ (fp32, 512 bytes per block at d = 128) is streamed once and
+// scored against every vector of the tile.  Sixteen lanes share a block row
+// (two 16-byte loads each, 256 contiguous bytes per half row across the
+// sixteen lanes); the 16-lane partial sums are reduced with DPP.  The same
+// kernel serves the G-head comparator, whose vectors are the G query heads
+// of a KV group (eq. (8)).
+//
+// Selection ([SparDA] eq. (3), eq. (6); §4.2 step 2): one workgroup per row.
+// Keys are the order-preserving uint32 image of the fp32 score; an 8-bit
+// radix select over the candidates (blocks neither initial nor local) finds
+// the k-th largest key, equal keys go to the lower block index, and an
+// ordered compaction writes init U local U top-k ascending, padded with -1.
+#include <math.h>
+
+#include "sda_device.hpp"
+#include "sda_internal.h"
+
+namespace sda {
+
+constexpr int kChunk = 256;          // blocks per scoring workgroup
+
+int score_chunks(int NB_cap) { return (NB_cap + kChunk - 1) / kChunk; }
+
+// vectors: [B, NQ, H_vec, D] bf16; K~ row (b, g) is scored by vectors
+// (q, hv) with hv in [g*VPR, (g+1)*VPR).  out[((b*NQ + q)*H_vec + hv)*NB_cap + j].
+template <int D, int NV>
+__global__ __launch_bounds__(256) void score_kernel(const uint16_t* __restrict__ vec,
+                                                    const float* __restrict__ kt,
+                                                    const int32_t* __restrict__ seq_len, int NQ,
+                                                    int H_kv, int VPR, int NB_cap, float mult,
+                                                    float* __restrict__ out) {
+    constexpr int HALVES = D / 64;          // 16-byte loads per lane per block
+    const int row = blockIdx.y;             // b * H_kv + g
+    const int b = row / H_kv, g = row - (row / H_kv) * H_kv;
+    const int nb = min((seq_len[b] + kBlock - 1) / kBlock, NB_cap);
+    const int j0 = blockIdx.x * kChunk;
+    if (j0 >= nb) return;
+    const int H_vec = H_kv * VPR;
+    const int nvec = NQ * VPR;
+    const int v0 = blockIdx.z * NV;
+    const int lane = __lane_id();
+    const int li = lane & 15;
+    const int wave = threadIdx.x / kWave;
+
+    // this lane's slice of each vector: dims 4*li..+4 and 64+4*li..+4
+    float fv[NV][HALVES * 4];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int vi = v0 + v;
+        const int q = vi / VPR, hv = g * VPR + (vi - (vi / VPR) * VPR);
+        if (vi < nvec) {
+            const uint16_t* p = vec + (((size_t)b * NQ + q) * H_vec + hv) * D;
+#pragma unroll
+            for (int h = 0; h < HALVES; ++h) {
+                const uint2 w = *reinterpret_cast<const uint2*>(p + h * 64 + li * 4);
+                fv[v][h * 4 + 0] = bf16lo(w.x);
+                fv[v][h * 4 + 1] = bf16hi(w.x);
+                fv[v][h * 4 + 2] = bf16lo(w.y);
+                fv[v][h * 4 + 3] = bf16hi(w.y);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < HALVES * 4; ++i) fv[v][i] = 0.f;
+        }
+    }
+
+    const float* ktr = kt + (size_t)row * NB_cap * D;
+    constexpr int UNR = 4;                       // steps in flight
+    constexpr int STEPS = kChunk / 16;           // 16 blocks per workgroup step
+    for (int s0 = 0; s0 < STEPS; s0 += UNR) {
+        floatx4 kv[UNR][HALVES];
+        int jj[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            jj[u] = j0 + (s0 + u) * 16 + wave * 4 + (lane >> 4);
+            const bool ok = jj[u] < nb;
+#pragma unroll
+            for (int h = 0; h < HALVES; ++h) {
+                if (ok) kv[u][h] = __builtin_nontemporal_load(
+                            reinterpret_cast<const floatx4*>(ktr + (size_t)jj[u] * D + h * 64 + li * 4));
+                else kv[u][h] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                float acc = 0.f;
+#pragma unroll
+                for (int h = 0; h < HALVES; ++h) {
+                    acc = fmaf(fv[v][h * 4 + 0], kv[u][h][0], acc);
+                    acc = fmaf(fv[v][h * 4 + 1], kv[u][h][1], acc);
+                    acc = fmaf(fv[v][h * 4 + 2], kv[u][h][2], acc);
+                    acc = fmaf(fv[v][h * 4 + 3], kv[u][h][3], acc);
+                }
+                acc = row16_sum(acc);
+                const int vi = v0 + v;
+                if (li == 0 && jj[u] < nb && vi < nvec) {
+                    const int q = vi / VPR, hv = g * VPR + (vi - (vi / VPR) * VPR);
+                    out[(((size_t)b * NQ + q) * H_vec + hv) * NB_cap + jj[u]] = acc * mult;
+                }
+            }
+        }
+    }
+}
+
+template <int D>
+static void launch_score_d(const uint16_t* vec, const float* kt, const int32_t* seq_len, int B, int NQ,
+                           int H_kv, int VPR, int NB_cap, float mult, float* out, hipStream_t s) {
+    const int nvec = NQ * VPR;
+    int nv = 1;
+    while (nv < nvec && nv < 16) nv *= 2;
+    dim3 grid(score_chunks(NB_cap), B * H_kv, (nvec + nv - 1) / nv);
+    switch (nv) {
+        case 1: hipLaunchKernelGGL((score_kernel<D, 1>), grid, dim3(256), 0, s, vec, kt, seq_len, NQ, H_kv, VPR, NB_cap, mult, out); break;
+        case 2: hipLaunchKernelGGL((score_kernel<D, 2>), grid, dim3(256), 0, s, vec, kt, seq_len, NQ, H_kv, VPR, NB_cap, mult, out); break;
+        case 4: hipLaunchKernelGGL((score_kernel<D, 4>), grid, dim3(256), 0, s, vec, kt, seq_len, NQ, H_kv, VPR, NB_cap, mult, out); break;
+        case 8: hipLaunchKernelGGL((score_kernel<D, 8>), grid, dim3(256), 0, s, vec, kt, seq_len, NQ, H_kv, VPR, NB_cap, mult, out); break;
+        default: hipLaunchKernelGGL((score_kernel<D, 16>), grid, dim3(256), 0, s, vec, kt, seq_len, NQ, H_kv, VPR, NB_cap, mult, out); break;
+    }
+}
+
+hipError_t launch_scores(const uint16_t* f, const float* kt, const int32_t* seq_len, int B, int NQ,
+                         int H_kv, int d, int NB_cap, float* scores, hipStream_t s) {
+    if (d == 128) launch_score_d<128>(f, kt, seq_len, B, NQ, H_kv, 1, NB_cap, 1.f, scores, s);
+    else launch_score_d<64>(f, kt, seq_len, B, NQ, H_kv, 1, NB_cap, 1.f, scores, s);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// block-wide helpers (256 threads)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    const int lane = __lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t t = __shfl_up(v, off, kWave);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+// inclusive scan over the 256 threads in thread order; `sh` holds 4 words
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* sh) {
+    const int lane = __lane_id(), w = threadIdx.x / kWave;
+    v = wave_incl_scan(v);
+    if (lane == kWave - 1) sh[w] = v;
+    __syncthreads();
+    uint32_t add = 0;
+    for (int i = 0; i < w; ++i) add += sh[i];
+    __syncthreads();
+    return v + add;
+}
+__device__ __forceinline__ float block_reduce_max(float v, float* sh) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    if (__lane_id() == 0) sh[threadIdx.x / kWave] = v;
+    __syncthreads();
+    const float r = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ float block_reduce_sum(float v, float* sh) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    if (__lane_id() == 0) sh[threadIdx.x / kWave] = v;
+    __syncthreads();
+    const float r = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+    __syncthreads();
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// exact top-k + block set, one workgroup per row
+// ---------------------------------------------------------------------------
+template <int EPT>
+__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t scan_sh[4];
+    __shared__ uint32_t sh_digit, sh_gt;
+    const int row = blockIdx.x;                         // (b*NQ + q)*H_kv + g
+    const int b = row / (a.NQ * a.H_kv);
+    const int tid = threadIdx.x;
+    const int nb = min((a.seq_len[b] + kBlock - 1) / kBlock, a.NB_cap);
+    const int lo = min(a.n_init, nb);                   // candidates are [lo, hi)
+    const int hi = max(lo, nb - a.n_local);
+    const int ncand = hi - lo;
+    const int k = min(a.top_k, ncand);
+    const float* s = a.scores + (size_t)row * a.NB_cap;
+    const int base = tid * EPT;                          // this thread owns [base, base+EPT)
+
+    uint32_t key[EPT];
+    uint64_t cand = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int j = base + i;
+        const bool c = (j >= lo && j < hi);
+        key[i] = c ? float_key(s[j]) : 0u;
+        cand |= (uint64_t)c << i;
+    }
+
+    // radix select: find the k-th largest key among candidates
+    uint32_t prefix = 0, pmask = 0;
+    int krem = k;
+    const bool partial = (k > 0 && k < ncand);
+    if (partial) {
+#pragma unroll 1
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            hist[tid] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < EPT; ++i)
+                if (((cand >> i) & 1) && (key[i] & pmask) == prefix)
+                    atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
+            __syncthreads();
+            // thread t looks at digit 255 - t: inclusive scan = count of digits >= it
+            const uint32_t c = hist[255 - tid];
+            const uint32_t incl = block_incl_scan(c, scan_sh);
+            if (incl >= (uint32_t)krem && incl - c < (uint32_t)krem) {
+                sh_digit = 255 - tid;
+                sh_gt = incl - c;
+            }
+            __syncthreads();
+            const uint32_t dg = sh_digit;
+            krem -= (int)sh_gt;
+            prefix |= dg << shift;
+            pmask |= 255u << shift;
+            __syncthreads();
+        }
+    }
+    // prefix is now the k-th largest key; krem keys equal to it are taken,
+    // lowest block index first
+    uint32_t ties = 0;
+    if (partial) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) ties += (((cand >> i) & 1) && key[i] == prefix) ? 1u : 0u;
+    }
+    const uint32_t ties_before = block_incl_scan(ties, scan_sh) - ties;
+
+    const int n_init_eff = lo;                   // blocks [0, lo) are initial
+    const int local_lo = max(0, nb - a.n_local);
+    uint64_t take = 0;
+    uint32_t tcount = ties_before;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int j = base + i;
+        bool t = false;
+        if (j < nb) {
+            if (j < n_init_eff || j >= local_lo) t = true;
+            else if ((cand >> i) & 1) {
+                if (!partial) t = (k > 0);
+                else if (key[i] > prefix) t = true;
+                else if (key[i] == prefix) {
+                    t = tcount < (uint32_t)krem;
+                    ++tcount;
+                }
+            }
+        }
+        take |= (uint64_t)t << i;
+    }
+    const uint32_t mine = __popcll(take);
+    const uint32_t incl = block_incl_scan(mine, scan_sh);
+    uint32_t pos = incl - mine;
+    int32_t* out = a.block_idx + (size_t)row * a.n_sel_max;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+        if ((take >> i) & 1) {
+            if (pos < (uint32_t)a.n_sel_max) out[pos] = base + i;
+            ++pos;
+        }
+    __shared__ uint32_t total;
+    if (tid == 255) total = incl;
+    __syncthreads();
+    const int tot = (int)min(total, (uint32_t)a.n_sel_max);
+    for (int p = tot + tid; p < a.n_sel_max; p += 256) out[p] = -1;
+    if (tid == 0) a.n_sel[row] = tot;
+}
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+    const int ept = (a.NB_cap + 255) / 256;
+    dim3 grid(a.rows), block(256);
+    if (ept <= 1) hipLaunchKernelGGL(select_kernel<1>, grid, block, 0, s, a);
+    else if (ept <= 2) hipLaunchKernelGGL(select_kernel<2>, grid, block, 0, s, a);
+    else if (ept <= 4) hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, s, a);
+    else if (ept <= 8) hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, s, a);
+    else if (ept <= 16) hipLaunchKernelGGL(select_kernel<16>, grid, block, 0, s, a);
+    else if (ept <= 32) hipLaunchKernelGGL(select_kernel<32>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(select_kernel<64>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// G-head comparator: z = q_h . K~_j / tau, then s_j = sum_h softmax_j(z_h)
+// ---------------------------------------------------------------------------
+size_t multihead_ws_floats(int B, int NQ, int H_q, int H_kv, int NB_cap) {
+    (void)H_kv;
+    return (size_t)B * NQ * H_q * NB_cap;     // z
+}
+
+// one workgroup per row (b, q, g): per head, max and sum of exp over the row's
+// blocks, then the per-block sum over heads of the normalised weights
+__global__ __launch_bounds__(256) void softmax_sum_kernel(const float* __restrict__ z,
+                                                          const int32_t* __restrict__ seq_len,
+                                                          int NQ, int H_kv, int G, int NB_cap,
+                                                          float* __restrict__ scores) {
+    __shared__ float red[4];
+    __shared__ float mh[32], inv_lh[32];
+    const int row = blockIdx.x;                          // (b*NQ + q)*H_kv + g
+    const int b = row / (NQ * H_kv);
+    const int nb = min((seq_len[b] + kBlock - 1) / kBlock, NB_cap);
+    const float* zr = z + (size_t)row * G * NB_cap;      // heads g*G .. g*G+G-1 are contiguous
+    for (int h = 0; h < G; ++h) {
+        float m = -INFINITY;
+        for (int j = threadIdx.x; j < nb; j += 256) m = fmaxf(m, zr[(size_t)h * NB_cap + j]);
+        m = block_reduce_max(m, red);
+        float l = 0.f;
+        for (int j = threadIdx.x; j < nb; j += 256) l += expf(zr[(size_t)h * NB_cap + j] - m);
+        l = block_reduce_sum(l, red);
+        if (threadIdx.x == 0) {
+            mh[h] = m;
+            inv_lh[h] = 1.f / l;
+        }
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < nb; j += 256) {
+        float acc = 0.f;
+        for (int h = 0; h < G; ++h) acc += expf(zr[(size_t)h * NB_cap + j] - mh[h]) * inv_lh[h];
+        scores[(size_t)row * NB_cap + j] = acc;
+    }
+}
+
+hipError_t launch_multihead_scores(const uint16_t* q, const float* kt, const int32_t* seq_len,
+                                   int B, int NQ, int H_q, int H_kv, int d, int NB_cap, float tau,
+                                   float* z, float* stats, float* scores, hipStream_t s) {
+    (void)stats;
+    const int G = H_q / H_kv;
+    if (d == 128) launch_score_d<128>(q, kt, seq_len, B, NQ, H_kv, G, NB_cap, 1.f / tau, z, s);
+    else launch_score_d<64>(q, kt, seq_len, B, NQ, H_kv, G, NB_cap, 1.f / tau, z, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(softmax_sum_kernel, dim3(B * NQ * H_kv), dim3(256), 0, s, z, seq_len, NQ,
+                       H_kv, G, NB_cap, scores);
+    return hipGetLastError();
+}
+
+}  // namespace sda

@@ -1,0 +1,377 @@
+// C-ABI layer of libsda: argument validation, workspace sizing, launch
+// selection.  Validation runs on the host before any HIP call, so every
+// invalid-argument path returns without touching the GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/sda.h"
+#include "sda_internal.h"
+
+using namespace sda;
+
+namespace {
+
+thread_local std::string g_err;
+
+sda_status_t fail(sda_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sda_status_t fail(sda_status_t st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+sda_status_t hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return SDA_OK;
+    return fail(SDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int kBlock = SDA_BLOCK_TOKENS;
+constexpr int kMaxGridYZ = 65535;
+constexpr int kMaxNBCap = 16384;      // select keeps <= 64 keys per lane
+constexpr int kMaxSplits = 1024;
+constexpr size_t kLdsBytes = 160 * 1024;
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+#define REQUIRE(cond, st, ...)                    \
+    do {                                          \
+        if (!(cond)) return fail(st, __VA_ARGS__); \
+    } while (0)
+
+sda_status_t check_d(int d) {
+    REQUIRE(d == 64 || d == 128, SDA_ERR_UNSUPPORTED, "head dim d=%d: only 64 and 128 are supported", d);
+    return SDA_OK;
+}
+
+sda_status_t check_heads(int H_q, int H_kv) {
+    REQUIRE(H_q >= 1 && H_kv >= 1, SDA_ERR_SHAPE, "H_q=%d H_kv=%d must be >= 1", H_q, H_kv);
+    REQUIRE(H_q % H_kv == 0, SDA_ERR_SHAPE, "H_q=%d is not a multiple of H_kv=%d", H_q, H_kv);
+    REQUIRE(H_q / H_kv <= 32, SDA_ERR_UNSUPPORTED, "G=%d query heads per KV head: at most 32", H_q / H_kv);
+    return SDA_OK;
+}
+
+int decode_splits(int split_k, int list_max) {
+    int s = split_k > 0 ? split_k : attn_default_splits(list_max);
+    if (s < 1) s = 1;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s;
+}
+
+#define TRY(expr)                          \
+    do {                                   \
+        sda_status_t _st = (expr);         \
+        if (_st != SDA_OK) return _st;     \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* sda_status_string(sda_status_t s) {
+    switch (s) {
+        case SDA_OK: return "SDA_OK";
+        case SDA_ERR_NULL: return "SDA_ERR_NULL";
+        case SDA_ERR_SHAPE: return "SDA_ERR_SHAPE";
+        case SDA_ERR_UNSUPPORTED: return "SDA_ERR_UNSUPPORTED";
+        case SDA_ERR_WORKSPACE: return "SDA_ERR_WORKSPACE";
+        case SDA_ERR_ALIGN: return "SDA_ERR_ALIGN";
+        case SDA_ERR_HIP: return "SDA_ERR_HIP";
+    }
+    return "SDA_ERR_UNKNOWN";
+}
+
+const char* sda_last_error(void) { return g_err.c_str(); }
+
+const char* sda_version(void) { return "sda 0.1 gfx950"; }
+
+// ---------------------------------------------------------------------------
+sda_status_t sda_update_compressed_keys(const void* k, float* k_tilde, const int32_t* len_old,
+                                        const int32_t* len_new, int max_new_tokens, int B,
+                                        int H_kv, int d, int T_cap, int NB_cap, void* stream) {
+    REQUIRE(k && k_tilde && len_old && len_new, SDA_ERR_NULL, "update_compressed_keys: null pointer");
+    TRY(check_d(d));
+    REQUIRE(B >= 1 && H_kv >= 1 && T_cap >= 1, SDA_ERR_SHAPE, "B=%d H_kv=%d T_cap=%d must be >= 1", B, H_kv, T_cap);
+    REQUIRE(NB_cap >= ceil_div(T_cap, kBlock), SDA_ERR_SHAPE, "NB_cap=%d < ceil(T_cap/64)=%d", NB_cap, ceil_div(T_cap, kBlock));
+    REQUIRE((long long)B * H_kv <= kMaxGridYZ, SDA_ERR_SHAPE, "B*H_kv=%lld exceeds %d", (long long)B * H_kv, kMaxGridYZ);
+    REQUIRE(max_new_tokens >= 0, SDA_ERR_SHAPE, "max_new_tokens=%d < 0", max_new_tokens);
+    REQUIRE(aligned16(k) && aligned16(k_tilde), SDA_ERR_ALIGN, "k and k_tilde must be 16-byte aligned");
+    REQUIRE(aligned4(len_old) && aligned4(len_new), SDA_ERR_ALIGN, "length arrays must be 4-byte aligned");
+    if (max_new_tokens == 0) return SDA_OK;
+    int blocks = ceil_div(max_new_tokens, kBlock) + 1;
+    if (blocks > NB_cap) blocks = NB_cap;
+    return hip_status(launch_update_compressed_keys(static_cast<const uint16_t*>(k), k_tilde, len_old, len_new,
+                                                    blocks, B, H_kv, d, T_cap, NB_cap,
+                                                    static_cast<hipStream_t>(stream)),
+                      "update_compressed_keys launch");
+}
+
+// ---------------------------------------------------------------------------
+size_t sda_score_select_workspace(int B, int NQ, int H_kv, int NB_cap, int top_k) {
+    (void)top_k;
+    if (B < 1 || NQ < 1 || H_kv < 1 || NB_cap < 1) return 0;
+    return (size_t)B * NQ * H_kv * NB_cap * sizeof(float);
+}
+
+static sda_status_t check_select_common(const float* k_tilde, const int32_t* seq_len, int B, int NQ,
+                                        int H_kv, int d, int NB_cap, int n_init, int n_local, int top_k,
+                                        int n_sel_max, const int32_t* block_idx, const int32_t* n_sel) {
+    REQUIRE(k_tilde && seq_len && block_idx && n_sel, SDA_ERR_NULL, "score_select: null pointer");
+    TRY(check_d(d));
+    REQUIRE(B >= 1 && NQ >= 1 && H_kv >= 1 && NB_cap >= 1, SDA_ERR_SHAPE,
+            "B=%d NQ=%d H_kv=%d NB_cap=%d must be >= 1", B, NQ, H_kv, NB_cap);
+    REQUIRE(NB_cap <= kMaxNBCap, SDA_ERR_UNSUPPORTED, "NB_cap=%d exceeds %d blocks", NB_cap, kMaxNBCap);
+    REQUIRE(n_init >= 0 && n_local >= 0 && top_k >= 0, SDA_ERR_SHAPE,
+            "n_init=%d n_local=%d top_k=%d must be >= 0", n_init, n_local, top_k);
+    REQUIRE(n_sel_max >= 1 && (long long)n_sel_max >= (long long)n_init + n_local + top_k, SDA_ERR_SHAPE,
+            "n_sel_max=%d < n_init+n_local+top_k=%lld", n_sel_max, (long long)n_init + n_local + top_k);
+    REQUIRE((long long)B * H_kv <= kMaxGridYZ, SDA_ERR_SHAPE, "B*H_kv exceeds %d", kMaxGridYZ);
+    REQUIRE((long long)B * NQ * H_kv <= (1LL << 31) - 1, SDA_ERR_SHAPE, "too many rows");
+    REQUIRE(aligned16(k_tilde), SDA_ERR_ALIGN, "k_tilde must be 16-byte aligned");
+    REQUIRE(aligned4(seq_len) && aligned4(block_idx) && aligned4(n_sel), SDA_ERR_ALIGN,
+            "int32 arrays must be 4-byte aligned");
+    return SDA_OK;
+}
+
+sda_status_t sda_score_select(const void* f, const float* k_tilde, const int32_t* seq_len, int B, int NQ,
+                              int H_kv, int d, int NB_cap, int n_init, int n_local, int top_k,
+                              int n_sel_max, int32_t* block_idx, int32_t* n_sel, float* scores_opt,
+                              void* ws, size_t ws_bytes, void* stream) {
+    REQUIRE(f, SDA_ERR_NULL, "score_select: f is null");
+    TRY(check_select_common(k_tilde, seq_len, B, NQ, H_kv, d, NB_cap, n_init, n_local, top_k, n_sel_max,
+                            block_idx, n_sel));
+    REQUIRE(aligned16(f), SDA_ERR_ALIGN, "f must be 16-byte aligned");
+    REQUIRE(ceil_div(NQ, 16) <= kMaxGridYZ, SDA_ERR_SHAPE, "NQ too large");
+    float* scores = scores_opt;
+    if (!scores) {
+        const size_t need = sda_score_select_workspace(B, NQ, H_kv, NB_cap, top_k);
+        REQUIRE(ws && ws_bytes >= need, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, need);
+        REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+        scores = static_cast<float*>(ws);
+    } else {
+        REQUIRE(aligned4(scores_opt), SDA_ERR_ALIGN, "scores_opt must be 4-byte aligned");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TRY(hip_status(launch_scores(static_cast<const uint16_t*>(f), k_tilde, seq_len, B, NQ, H_kv, d, NB_cap,
+                                 scores, s),
+                   "score launch"));
+    SelectArgs a{seq_len, scores, B * NQ * H_kv, NQ, H_kv, NB_cap, n_init, n_local, top_k, n_sel_max,
+                 block_idx, n_sel};
+    return hip_status(launch_select(a, s), "select launch");
+}
+
+size_t sda_score_select_multihead_workspace(int B, int NQ, int H_q, int H_kv, int NB_cap, int top_k) {
+    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || NB_cap < 1) return 0;
+    return (multihead_ws_floats(B, NQ, H_q, H_kv, NB_cap) + (size_t)B * NQ * H_kv * NB_cap) * sizeof(float) +
+           0 * (size_t)top_k;
+}
+
+sda_status_t sda_score_select_multihead(const void* q, const float* k_tilde, const int32_t* seq_len, int B,
+                                        int NQ, int H_q, int H_kv, int d, int NB_cap, int n_init, int n_local,
+                                        int top_k, int n_sel_max, float tau, int32_t* block_idx,
+                                        int32_t* n_sel, float* scores_opt, void* ws, size_t ws_bytes,
+                                        void* stream) {
+    REQUIRE(q, SDA_ERR_NULL, "score_select_multihead: q is null");
+    TRY(check_select_common(k_tilde, seq_len, B, NQ, H_kv, d, NB_cap, n_init, n_local, top_k, n_sel_max,
+                            block_idx, n_sel));
+    TRY(check_heads(H_q, H_kv));
+    REQUIRE(H_q / H_kv <= 16, SDA_ERR_UNSUPPORTED, "comparator supports G <= 16");
+    REQUIRE(tau > 0.f && isfinite(tau), SDA_ERR_SHAPE, "tau must be finite and > 0");
+    REQUIRE(aligned16(q), SDA_ERR_ALIGN, "q must be 16-byte aligned");
+    const size_t need = sda_score_select_multihead_workspace(B, NQ, H_q, H_kv, NB_cap, top_k);
+    REQUIRE(ws && ws_bytes >= need, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, need);
+    REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    float* z = static_cast<float*>(ws);
+    float* scores = scores_opt ? scores_opt : z + multihead_ws_floats(B, NQ, H_q, H_kv, NB_cap);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TRY(hip_status(launch_multihead_scores(static_cast<const uint16_t*>(q), k_tilde, seq_len, B, NQ, H_q, H_kv,
+                                           d, NB_cap, tau, z, nullptr, scores, s),
+                   "multihead score launch"));
+    SelectArgs a{seq_len, scores, B * NQ * H_kv, NQ, H_kv, NB_cap, n_init, n_local, top_k, n_sel_max,
+                 block_idx, n_sel};
+    return hip_status(launch_select(a, s), "select launch");
+}
+
+// ---------------------------------------------------------------------------
+size_t sda_sparse_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int split_k) {
+    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || H_q % H_kv) return 0;
+    const int G = H_q / H_kv;
+    const int ns = decode_splits(split_k, n_sel_max);
+    return attn_ws_bytes(B * NQ * H_kv, ns, attn_rows_pad(1, G), d);
+}
+
+static sda_status_t check_attn_common(const void* q, const void* k, const void* v, const int32_t* seq_len,
+                                      const int32_t* block_idx, const int32_t* n_sel, int n_sel_max, int T_cap,
+                                      int B, int NQ, int H_q, int H_kv, int d, float scale, float* out,
+                                      int split_k) {
+    REQUIRE(q && k && v && seq_len && block_idx && n_sel && out, SDA_ERR_NULL, "decode: null pointer");
+    TRY(check_d(d));
+    TRY(check_heads(H_q, H_kv));
+    REQUIRE(B >= 1 && NQ >= 1 && T_cap >= 1 && n_sel_max >= 1, SDA_ERR_SHAPE,
+            "B=%d NQ=%d T_cap=%d n_sel_max=%d must be >= 1", B, NQ, T_cap, n_sel_max);
+    REQUIRE(split_k >= 0 && split_k <= kMaxSplits, SDA_ERR_SHAPE, "split_k=%d outside [0, %d]", split_k, kMaxSplits);
+    REQUIRE(isfinite(scale) && scale > 0.f, SDA_ERR_SHAPE, "scale must be finite and > 0");
+    REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), SDA_ERR_ALIGN,
+            "q, k, v, out must be 16-byte aligned");
+    REQUIRE(aligned4(seq_len) && aligned4(block_idx) && aligned4(n_sel), SDA_ERR_ALIGN,
+            "int32 arrays must be 4-byte aligned");
+    return SDA_OK;
+}
+
+sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, const int32_t* seq_len,
+                               const int32_t* block_idx, const int32_t* n_sel, int n_sel_max,
+                               const int32_t* slot_opt, int T_cap, int B, int NQ, int H_q, int H_kv, int d,
+                               float scale, float* out, float* lse_opt, int split_k, void* ws, size_t ws_bytes,
+                               void* stream) {
+    TRY(check_attn_common(q, k, v, seq_len, block_idx, n_sel, n_sel_max, T_cap, B, NQ, H_q, H_kv, d, scale, out,
+                          split_k));
+    const long long tasks = (long long)B * NQ * H_kv;
+    REQUIRE(tasks <= kMaxGridYZ, SDA_ERR_SHAPE, "B*NQ*H_kv=%lld exceeds %d", tasks, kMaxGridYZ);
+    REQUIRE(!slot_opt || aligned4(slot_opt), SDA_ERR_ALIGN, "slot_opt must be 4-byte aligned");
+    const int G = H_q / H_kv;
+    const int ns = decode_splits(split_k, n_sel_max);
+    const size_t need = attn_ws_bytes((int)tasks, ns, attn_rows_pad(1, G), d);
+    REQUIRE(need == 0 || (ws && ws_bytes >= need), SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
+            ws ? ws_bytes : 0, need);
+    REQUIRE(need == 0 || aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    AttnArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.seq_len = seq_len;
+    a.block_idx = block_idx;
+    a.n_sel = n_sel;
+    a.slot = slot_opt;
+    a.out = out;
+    a.lse = lse_opt;
+    a.union_count = nullptr;
+    const int rp = attn_rows_pad(1, G);
+    a.part_ml = static_cast<float*>(ws);
+    a.part_o = need ? static_cast<float*>(ws) + (size_t)tasks * ns * rp * 2 : nullptr;
+    a.n_sel_max = n_sel_max;
+    a.T_cap = T_cap;
+    a.NB_cap = ceil_div(T_cap, kBlock);
+    a.B = B;
+    a.NQ = NQ;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.G = G;
+    a.d = d;
+    a.C = 1;
+    a.mode = SDA_GROUP_EXACT;
+    a.n_groups = NQ;
+    a.n_split = ns;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)), "sparse_decode launch");
+}
+
+size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int group_C,
+                                    int split_k) {
+    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || group_C < 1 || H_q % H_kv) return 0;
+    const int G = H_q / H_kv;
+    const int n_groups = ceil_div(NQ, group_C);
+    const int ns = decode_splits(split_k, group_C * n_sel_max);
+    return attn_ws_bytes(B * n_groups * H_kv, ns, attn_rows_pad(group_C, G), d);
+}
+
+sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, const int32_t* seq_len,
+                                const int32_t* block_idx, const int32_t* n_sel, int n_sel_max, int T_cap,
+                                int NB_cap, int B, int NQ, int H_q, int H_kv, int d, float scale, int group_C,
+                                int mode, float* out, float* lse_opt, int32_t* union_count_opt, int split_k,
+                                void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_attn_common(q, k, v, seq_len, block_idx, n_sel, n_sel_max, T_cap, B, NQ, H_q, H_kv, d, scale, out,
+                          split_k));
+    REQUIRE(group_C >= 1 && group_C <= 8, SDA_ERR_UNSUPPORTED, "group_C=%d outside [1, 8]", group_C);
+    REQUIRE(mode == SDA_GROUP_EXACT || mode == SDA_GROUP_SHARED_REP, SDA_ERR_SHAPE, "mode=%d", mode);
+    const int G = H_q / H_kv;
+    REQUIRE(group_C * G <= 32, SDA_ERR_UNSUPPORTED, "group_C*G=%d exceeds 32 rows", group_C * G);
+    REQUIRE(NB_cap >= ceil_div(T_cap, kBlock) && NB_cap <= kMaxNBCap, SDA_ERR_SHAPE,
+            "NB_cap=%d must lie in [ceil(T_cap/64), %d]", NB_cap, kMaxNBCap);
+    REQUIRE(!union_count_opt || aligned4(union_count_opt), SDA_ERR_ALIGN, "union_count must be 4-byte aligned");
+    const int n_groups = ceil_div(NQ, group_C);
+    const long long tasks = (long long)B * n_groups * H_kv;
+    REQUIRE(tasks <= kMaxGridYZ, SDA_ERR_SHAPE, "B*groups*H_kv=%lld exceeds %d", tasks, kMaxGridYZ);
+    const int rp = attn_rows_pad(group_C, G);
+    const size_t lds = (size_t)4 * 64 * d * 2 + (size_t)group_C * ((NB_cap + 31) / 32) * 4 +
+                       (size_t)group_C * n_sel_max * 8 + 257 * 4;
+    REQUIRE(lds <= kLdsBytes, SDA_ERR_UNSUPPORTED, "group needs %zu bytes of LDS", lds);
+    const int list_max = (mode == SDA_GROUP_EXACT) ? group_C * n_sel_max : n_sel_max;
+    const int ns = decode_splits(split_k, list_max);
+    const int ns_ws = decode_splits(split_k, group_C * n_sel_max);
+    const size_t need = attn_ws_bytes((int)tasks, ns, rp, d);
+    const size_t need_doc = attn_ws_bytes((int)tasks, ns_ws, rp, d);
+    REQUIRE(need == 0 || (ws && ws_bytes >= need), SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
+            ws ? ws_bytes : 0, need_doc);
+    REQUIRE(need == 0 || aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    AttnArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.seq_len = seq_len;
+    a.block_idx = block_idx;
+    a.n_sel = n_sel;
+    a.slot = nullptr;
+    a.out = out;
+    a.lse = lse_opt;
+    a.union_count = union_count_opt;
+    a.part_ml = static_cast<float*>(ws);
+    a.part_o = need ? static_cast<float*>(ws) + (size_t)tasks * ns * rp * 2 : nullptr;
+    a.n_sel_max = n_sel_max;
+    a.T_cap = T_cap;
+    a.NB_cap = NB_cap;
+    a.B = B;
+    a.NQ = NQ;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.G = G;
+    a.d = d;
+    a.C = group_C;
+    a.mode = mode;
+    a.n_groups = n_groups;
+    a.n_split = ns;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)), "grouped_decode launch");
+}
+
+// ---------------------------------------------------------------------------
+sda_status_t sda_gather_blocks(const void* k_src, const void* v_src, const int32_t* block_idx,
+                               const int32_t* n_sel, int n_sel_max, int B, int H_kv, int d, int T_cap,
+                               void* k_stage, void* v_stage, int32_t* slot_out, int max_workgroups,
+                               void* stream) {
+    REQUIRE(k_src && v_src && block_idx && n_sel && k_stage && v_stage && slot_out, SDA_ERR_NULL,
+            "gather_blocks: null pointer");
+    TRY(check_d(d));
+    REQUIRE(B >= 1 && H_kv >= 1 && n_sel_max >= 1 && T_cap >= 1, SDA_ERR_SHAPE,
+            "B=%d H_kv=%d n_sel_max=%d T_cap=%d must be >= 1", B, H_kv, n_sel_max, T_cap);
+    REQUIRE(max_workgroups >= 0, SDA_ERR_SHAPE, "max_workgroups=%d < 0", max_workgroups);
+    REQUIRE((long long)B * H_kv * n_sel_max <= (1LL << 31) - 1, SDA_ERR_SHAPE, "too many entries");
+    REQUIRE(aligned16(k_src) && aligned16(v_src) && aligned16(k_stage) && aligned16(v_stage), SDA_ERR_ALIGN,
+            "source and stage buffers must be 16-byte aligned");
+    REQUIRE(aligned4(block_idx) && aligned4(n_sel) && aligned4(slot_out), SDA_ERR_ALIGN,
+            "int32 arrays must be 4-byte aligned");
+    void* kd = nullptr;
+    void* vd = nullptr;
+    hipError_t e = hipHostGetDevicePointer(&kd, const_cast<void*>(k_src), 0);
+    if (e != hipSuccess)
+        return fail(SDA_ERR_HIP, "k_src is not pinned, device-mapped host memory: %s", hipGetErrorString(e));
+    e = hipHostGetDevicePointer(&vd, const_cast<void*>(v_src), 0);
+    if (e != hipSuccess)
+        return fail(SDA_ERR_HIP, "v_src is not pinned, device-mapped host memory: %s", hipGetErrorString(e));
+    return hip_status(launch_gather(static_cast<const uint16_t*>(kd), static_cast<const uint16_t*>(vd), block_idx,
+                                    n_sel, n_sel_max, B, H_kv, d, T_cap, static_cast<uint16_t*>(k_stage),
+                                    static_cast<uint16_t*>(v_stage), slot_out, max_workgroups,
+                                    static_cast<hipStream_t>(stream)),
+                      "gather launch");
+}
+
+}  // extern "C"

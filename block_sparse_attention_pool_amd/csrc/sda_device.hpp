@@ -1,0 +1,93 @@
+// Device helpers shared by the gfx950 kernels: bf16 storage, vector types,
+// wave64 cross-lane reductions (DPP inside a 16-lane row, permute across
+// rows) and the 16x16x32 bf16 MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sda {
+
+constexpr int kBlock = 64;       // tokens per block
+constexpr int kWave = 64;        // wavefront width on CDNA
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+// bf16 bits -> float (exact)
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t f2bf(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+// ---- DPP reductions inside a 16-lane row -----------------------------------
+// quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_ror:4 = 0x124,
+// row_ror:8 = 0x128.  After the four steps every lane of the row holds the
+// row's total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x124>(x);
+    x += dpp_f<0x128>(x);
+    return x;
+}
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x124>(x));
+    x = fmaxf(x, dpp_f<0x128>(x));
+    return x;
+}
+
+// value of lane (lane ^ mask) for mask in {16, 32}: across 16-lane rows
+__device__ __forceinline__ float xor_lane(float x, int mask) {
+    int lane = __lane_id();
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+// max / sum over the four lanes {l, l^16, l^32, l^48}
+__device__ __forceinline__ float cross4_max(float x) {
+    x = fmaxf(x, xor_lane(x, 16));
+    return fmaxf(x, xor_lane(x, 32));
+}
+__device__ __forceinline__ float cross4_sum(float x) {
+    x += xor_lane(x, 16);
+    return x + xor_lane(x, 32);
+}
+
+// ---- MFMA -------------------------------------------------------------------
+// D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16).  Lane l supplies
+// A[l % 16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l % 16]; it receives
+// D[4*(l/16) + i][l % 16], i = 0..3.
+__device__ __forceinline__ floatx4 mfma16x16x32(const u32x4& a, const u32x4& b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ldg16_cached(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// order-preserving map float -> uint32 (larger float -> larger key); -0 == +0
+__device__ __forceinline__ uint32_t float_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    if (u == 0x80000000u) u = 0;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace sda

@@ -1,0 +1,67 @@
+// Internal host-side declarations shared by the C-ABI layer and the kernel
+// translation units.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sda {
+
+// ---- compressed keys ----------------------------------------------------------
+hipError_t launch_update_compressed_keys(const uint16_t* k, float* kt, const int32_t* len_old,
+                                         const int32_t* len_new, int max_blocks_per_row, int B,
+                                         int H_kv, int d, int T_cap, int NB_cap, hipStream_t s);
+
+// ---- scoring and selection ----------------------------------------------------
+struct SelectArgs {
+    const int32_t* seq_len;
+    const float* scores;     // [rows, NB_cap]
+    int rows, NQ, H_kv, NB_cap;
+    int n_init, n_local, top_k, n_sel_max;
+    int32_t* block_idx;
+    int32_t* n_sel;
+};
+hipError_t launch_scores(const uint16_t* f, const float* kt, const int32_t* seq_len, int B, int NQ,
+                         int H_kv, int d, int NB_cap, float* scores, hipStream_t s);
+hipError_t launch_multihead_scores(const uint16_t* q, const float* kt, const int32_t* seq_len,
+                                   int B, int NQ, int H_q, int H_kv, int d, int NB_cap, float tau,
+                                   float* z, float* stats, float* scores, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+size_t multihead_ws_floats(int B, int NQ, int H_q, int H_kv, int NB_cap);
+int score_chunks(int NB_cap);
+
+// ---- attention ------------------------------------------------------------------
+struct AttnArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* seq_len;
+    const int32_t* block_idx;
+    const int32_t* n_sel;
+    const int32_t* slot;      // may be null
+    float* out;
+    float* lse;               // may be null
+    int32_t* union_count;     // may be null
+    float* part_o;            // [tasks, n_split, rows_pad, d]
+    float* part_ml;           // [tasks, n_split, rows_pad, 2]
+    int n_sel_max, T_cap, NB_cap;
+    int B, NQ, H_q, H_kv, G, d;
+    int C;                    // queries per group (1 = plain decode)
+    int mode;                 // 0 exact, 1 shared representative
+    int n_groups;             // ceil(NQ / C)
+    int n_split;
+    float scale_log2;         // scale * log2(e)
+};
+int attn_rows_pad(int C, int G);                 // 16 or 32
+int attn_default_splits(int list_max);
+size_t attn_ws_bytes(int tasks, int n_split, int rows_pad, int d);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// ---- offload gather -----------------------------------------------------------------
+hipError_t launch_gather(const uint16_t* k_src, const uint16_t* v_src, const int32_t* block_idx,
+                         const int32_t* n_sel, int n_sel_max, int B, int H_kv, int d, int T_cap,
+                         uint16_t* k_stage, uint16_t* v_stage, int32_t* slot_out,
+                         int max_workgroups, hipStream_t s);
+
+}  // namespace sda

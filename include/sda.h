@@ -1,0 +1,199 @@
+/*
+ * sda.h - top-k block-sparse decode attention on MI355X (gfx950).
+ *
+ * C ABI of libsda.so.  Every call validates its arguments on the host before
+ * anything is enqueued; on a validation error nothing is launched and a
+ * non-zero status is returned (details in sda_last_error()).  Calls are
+ * asynchronous on `stream` (a hipStream_t; NULL = the default stream) and
+ * never synchronise the host.  The library allocates no memory: callers pass
+ * device buffers and a workspace sized by the matching *_workspace() call.
+ * All pointers are device pointers unless the comment says "host".
+ * Tensors are dense, row-major, in the shapes given in brackets.
+ *
+ * Sources (by page title, section and equation):
+ *   [SparDA] reading note "SparDA：稀疏解耦注意力，让长上下文推理又快又准"
+ *            (zhongzhuzhou.org, 2026-06-24), on SparDA: Sparse Decoupled
+ *            Attention (arXiv 2606.04511).
+ *   [SSV]    reading note "SSV：稀疏投机验证——在动态稀疏注意力中做投机解码"
+ *            (zhongzhuzhou.org, 2026-07-01), on SSV (arXiv 2605.19893).
+ *
+ * Shapes and symbols: B batch, NQ queries per sequence (1 for plain decode),
+ * H_q query heads, H_kv KV heads, G = H_q / H_kv, d head dim (64 or 128),
+ * T_cap token capacity of the K/V buffers, NB_cap = block capacity of the
+ * compressed-key buffer (>= ceil(T_cap / 64)).  Blocks are 64 tokens.  Query
+ * head h uses KV head h / G.  bf16 tensors are passed as raw 16-bit storage.
+ * A "row" is one (batch, query, KV head).
+ */
+#ifndef SDA_H
+#define SDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SDA_OK = 0,
+    SDA_ERR_NULL = 1,        /* a required pointer is NULL */
+    SDA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes */
+    SDA_ERR_UNSUPPORTED = 3, /* valid request outside what the kernels cover (e.g. d = 96) */
+    SDA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than *_workspace() asks */
+    SDA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+    SDA_ERR_HIP = 6          /* the HIP runtime reported an error (launch or query) */
+} sda_status_t;
+
+enum { SDA_GROUP_EXACT = 0, SDA_GROUP_SHARED_REP = 1 };
+
+#define SDA_BLOCK_TOKENS 64
+
+/* Name of a status code (static string). */
+const char* sda_status_string(sda_status_t s);
+
+/* Detail of the last error returned on the calling thread (thread-local,
+ * valid until the next failing call on that thread; "" when none). */
+const char* sda_last_error(void);
+
+/* Library version string, e.g. "sda 0.1 gfx950". */
+const char* sda_version(void);
+
+/*
+ * Compressed keys: K~[b,g,j,:] = mean of K[b,g,64j : min(64j+64, len), :]
+ * ([SparDA] prerequisites §3, eq. (4) with kernel = stride = 64; kept on the
+ * GPU and refreshed as tokens are appended, §4.2 step 1 and §4.6).
+ *
+ *   k        bf16 [B, H_kv, T_cap, d]        keys (read only)
+ *   k_tilde  f32  [B, H_kv, NB_cap, d]       updated in place
+ *   len_old  i32  [B]  tokens already pooled; len_new i32 [B] tokens now cached
+ *
+ * Every block touched by tokens [len_old[b], len_new[b]) is recomputed from
+ * K (the whole block, so an incremental update equals a bulk build bit for
+ * bit).  Bulk build: len_old = 0, len_new = T.  max_new_tokens must bound
+ * len_new[b] - len_old[b] for every b (it sizes the grid; rows needing more
+ * are truncated).  Device-side guards: len_new is clamped to T_cap and rows
+ * with len_new <= len_old are left unchanged.
+ */
+sda_status_t sda_update_compressed_keys(const void* k, float* k_tilde,
+                                        const int32_t* len_old, const int32_t* len_new,
+                                        int max_new_tokens, int B, int H_kv, int d,
+                                        int T_cap, int NB_cap, void* stream);
+
+/*
+ * Indexer scoring, top-k and block-set assembly for every row
+ * ([SparDA] §4.2 step 2, eq. (3), (6), (9); [SSV] NSA selection branch
+ * steps 1-2):
+ *   s_j = f . K~_j for each of the row's nb = ceil(seq_len[b] / 64) blocks;
+ *   B = {0..n_init-1} U {nb-n_local..nb-1} U top_k(s over the other blocks),
+ *   ties to the lower block index; written ascending, padded with -1.
+ * f is one indexer (Forecast) vector per row; with SparDA's lookahead it is
+ * layer l's vector scored against layer l+1's compressed keys (eq. (6)).
+ *
+ *   f          bf16 [B, NQ, H_kv, d]
+ *   k_tilde    f32  [B, H_kv, NB_cap, d]
+ *   seq_len    i32  [B]               (1 <= seq_len <= 64 * NB_cap)
+ *   block_idx  i32  [B, NQ, H_kv, n_sel_max] out; n_sel i32 [B, NQ, H_kv] out
+ *   scores_opt f32  [B, NQ, H_kv, NB_cap] out or NULL (raw scores, entries past nb undefined)
+ * n_sel_max >= n_init + n_local + top_k.  Scores are fp32 (fp32 K~, fp32 sums).
+ * Workspace: sda_score_select_workspace() bytes.
+ */
+size_t sda_score_select_workspace(int B, int NQ, int H_kv, int NB_cap, int top_k);
+sda_status_t sda_score_select(const void* f, const float* k_tilde, const int32_t* seq_len,
+                              int B, int NQ, int H_kv, int d, int NB_cap,
+                              int n_init, int n_local, int top_k, int n_sel_max,
+                              int32_t* block_idx, int32_t* n_sel, float* scores_opt,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * G-head block selector used as the comparator to the one-head indexer
+ * ([SparDA] §4.3 eq. (8) and the target of §4.4 eq. (10)): for each row,
+ * s_j = sum over the G query heads h of the row's KV group of
+ * softmax over all nb blocks of (q_h . K~_j / tau); then the same top-k and
+ * block-set assembly as sda_score_select.  With 64-token pooling windows the
+ * max-pool onto the block grid is the identity.
+ *
+ *   q  bf16 [B, NQ, H_q, d]; other arguments as sda_score_select; tau > 0.
+ * Workspace: sda_score_select_multihead_workspace() bytes.
+ */
+size_t sda_score_select_multihead_workspace(int B, int NQ, int H_q, int H_kv, int NB_cap, int top_k);
+sda_status_t sda_score_select_multihead(const void* q, const float* k_tilde, const int32_t* seq_len,
+                                        int B, int NQ, int H_q, int H_kv, int d, int NB_cap,
+                                        int n_init, int n_local, int top_k, int n_sel_max, float tau,
+                                        int32_t* block_idx, int32_t* n_sel, float* scores_opt,
+                                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Block-sparse decode attention ([SparDA] eq. (7) and §4.2 step 4; [SSV] NSA
+ * selection branch step 3): for every query head h of every row,
+ *   O = softmax(q_h K_B^T * scale) V_B
+ * over the tokens of the row's selected blocks that lie below seq_len[b].
+ * Split-K over the block list with online softmax state (m, l, o) per split
+ * and a log-sum-exp combine ([SSV] online-softmax section).
+ *
+ *   q          bf16 [B, NQ, H_q, d]
+ *   k, v       bf16 [B, H_kv, T_cap, d]   (a cache, or a staging buffer with slot_opt)
+ *   seq_len    i32  [B]
+ *   block_idx  i32  [B, NQ, H_kv, n_sel_max] logical block ids (ascending not required)
+ *   n_sel      i32  [B, NQ, H_kv]  entries used per row (<= n_sel_max)
+ *   slot_opt   i32  [B, NQ, H_kv, n_sel_max] or NULL: the physical 64-token block of
+ *              each entry inside the row's K/V buffer (NULL: the logical id itself)
+ *   out        f32  [B, NQ, H_q, d];  lse_opt f32 [B, NQ, H_q] (natural log) or NULL
+ *   split_k    splits per row (0 = chosen by the library)
+ * Entries with ids outside [0, nb) or slots outside the buffer are skipped.
+ * A row with no valid token gets out = 0 and lse = -inf.
+ */
+size_t sda_sparse_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int split_k);
+sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, const int32_t* seq_len,
+                               const int32_t* block_idx, const int32_t* n_sel, int n_sel_max,
+                               const int32_t* slot_opt, int T_cap,
+                               int B, int NQ, int H_q, int H_kv, int d, float scale,
+                               float* out, float* lse_opt, int split_k,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Grouped verification decode ([SSV] core mechanism 1 and its verification
+ * kernel algorithm): the NQ queries of a sequence form consecutive groups of
+ * group_C (the last group may be smaller).  For each (batch, group, KV head)
+ * the kernel loads each block of the group's merged set once and serves all
+ * C*G query heads from it.
+ *   SDA_GROUP_EXACT      merged set = union of the group's lists; query c
+ *                        attends only to its own list (exact per-query result).
+ *   SDA_GROUP_SHARED_REP every query attends to the group's first list.
+ *   block_idx must be ascending per row (as sda_score_select writes it).
+ *   union_count_opt i32 [B, ceil(NQ / group_C), H_kv] out or NULL: blocks loaded
+ *   per group (size of the merged set, or of the first list in shared mode).
+ * Other arguments as sda_sparse_decode.  group_C * G <= 32, group_C <= 8.
+ */
+size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d,
+                                    int group_C, int split_k);
+sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, const int32_t* seq_len,
+                                const int32_t* block_idx, const int32_t* n_sel, int n_sel_max,
+                                int T_cap, int NB_cap, int B, int NQ, int H_q, int H_kv, int d,
+                                float scale, int group_C, int mode,
+                                float* out, float* lse_opt, int32_t* union_count_opt,
+                                int split_k, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Offloaded-KV gather ([SparDA] §4.2 steps 3 and 6, §4.5): copy the K and V
+ * rows of each row's selected blocks from pinned host memory into a compact
+ * device staging buffer, with GPU loads over the host link, on the caller's
+ * (side) stream; sda_sparse_decode then reads the stage through slot_out.
+ *
+ *   k_src, v_src  host bf16 [B, H_kv, T_cap, d]; must be pinned host memory
+ *                 mapped for the device (hipHostMalloc / torch pin_memory)
+ *   block_idx     i32 [B, H_kv, n_sel_max] (one query per sequence); n_sel i32 [B, H_kv]
+ *   k_stage, v_stage  bf16 [B, H_kv, n_sel_max * 64, d] out
+ *   slot_out      i32 [B, H_kv, n_sel_max] out: entry e lives in stage block e (-1 past n_sel)
+ *   max_workgroups  upper bound on workgroups the copy occupies (0 = library choice)
+ */
+sda_status_t sda_gather_blocks(const void* k_src, const void* v_src,
+                               const int32_t* block_idx, const int32_t* n_sel, int n_sel_max,
+                               int B, int H_kv, int d, int T_cap,
+                               void* k_stage, void* v_stage, int32_t* slot_out,
+                               int max_workgroups, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDA_H */

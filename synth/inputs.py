@@ -150,12 +150,15 @@ def bias_directions(F):
     return torch.from_numpy(u.astype(np.float32))
 
 
-def attention_queries(cfg, layer, sigma=None):
+def attention_queries(cfg, layer, sigma=None, attempts=None):
     """Attention queries Q, float32 numpy [B, NQ, H_q, d], N(0,1).
 
     Draft-query configs: q = q0 + sigma * eps with q0 shared across the
-    sequence's queries."""
+    sequence's queries.  ``attempts`` [B, NQ, H_kv] re-draws the G heads of a
+    KV group: attempt a >= 1 adds REDRAW_SCALE * N(0,1) from a seed that
+    includes a."""
     B, NQ, H, d = cfg.B, cfg.NQ, cfg.H_q, cfg.d
+    G = H // cfg.H_kv
     Q = np.empty((B, NQ, H, d), dtype=np.float64)
     for b in range(B):
         base = _row_rng(cfg.cid, "Q0", layer, b).standard_normal((H, d))
@@ -166,6 +169,12 @@ def attention_queries(cfg, layer, sigma=None):
                 Q[b, q] = _row_rng(cfg.cid, "Qq", layer, b, q).standard_normal((H, d))
             else:
                 Q[b, q] = base + sigma * _row_rng(cfg.cid, "Qeps", layer, b, q).standard_normal((H, d))
+            if attempts is not None:
+                for g in range(cfg.H_kv):
+                    a = int(attempts[b, q, g])
+                    if a > 0:
+                        Q[b, q, g * G:(g + 1) * G] += REDRAW_SCALE * _row_rng(
+                            cfg.cid, "Qredraw", layer, b, q, g, a).standard_normal((G, d))
     return Q.astype(np.float32)
 
 

@@ -1,0 +1,170 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, sizes workspaces, and rejects bad arguments on the host before any
+HIP call (each call here fails validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_pool_amd as sda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sda.h")
+
+OK, NULL, SHAPE, UNSUP, WS, ALIGN, HIP = range(7)
+P = 0x10000          # a 16-byte aligned stand-in address; never dereferenced
+P_ODD = 0x10004
+
+
+@pytest.fixture(scope="module")
+def L():
+    # these calls pass stand-in addresses that must be rejected on the host;
+    # keep them off machines with a GPU so a validation slip can never launch
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-validation tests run only where no GPU is visible")
+    if not os.path.exists(sda.LIB_PATH):
+        from block_sparse_attention_pool_amd import _build
+        _build.build()
+    return sda.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sda_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_bound(L):
+    names = header_functions()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in sda.exported_symbols(), n
+    assert set(sda.exported_symbols()) == set(names)
+
+
+def test_status_strings(L):
+    assert sda.status_string(0) == "SDA_OK"
+    assert sda.status_string(4) == "SDA_ERR_WORKSPACE"
+    assert sda.version().startswith("sda ")
+
+
+def test_workspace_sizes(L):
+    assert L.sda_score_select_workspace(8, 1, 8, 2048, 32) == 8 * 8 * 2048 * 4
+    assert L.sda_score_select_workspace(0, 1, 8, 2048, 32) == 0
+    # multihead: per-head logits plus the summed scores
+    assert L.sda_score_select_multihead_workspace(8, 1, 64, 8, 2048, 32) == (8 * 64 * 2048 + 8 * 8 * 2048) * 4
+    # decode: one split per 4 blocks; (m, l) + d floats per padded row per split
+    n = L.sda_sparse_decode_workspace(8, 1, 64, 8, 35, 128, 0)
+    assert n == 64 * 9 * 16 * (128 + 2) * 4
+    assert L.sda_sparse_decode_workspace(8, 1, 64, 8, 35, 128, 1) == 0
+    assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 4, 0) == 4 * 4 * 8 * 16 * 16 * 130 * 4
+
+
+def _last():
+    return sda.last_error()
+
+
+def test_update_validation(L):
+    f = L.sda_update_compressed_keys
+    assert f(None, P, P, P, 64, 1, 2, 64, 4096, 64, None) == NULL
+    assert f(P, P, P, P, 64, 1, 2, 96, 4096, 64, None) == UNSUP
+    assert "96" in _last()
+    assert f(P, P, P, P, 64, 1, 2, 64, 4096, 63, None) == SHAPE          # NB_cap too small
+    assert f(P_ODD, P, P, P, 64, 1, 2, 64, 4096, 64, None) == ALIGN
+    assert f(P, P, P, P, -1, 1, 2, 64, 4096, 64, None) == SHAPE
+    assert f(P, P, P, P, 0, 1, 2, 64, 4096, 64, None) == OK               # nothing to do, nothing launched
+
+
+def test_score_select_validation(L):
+    f = L.sda_score_select
+    args = [P, P, P, 1, 1, 2, 64, 64, 1, 2, 8, 11, P, P, None, P, 1 << 20, None]
+    bad = list(args); bad[0] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[11] = 10                                        # n_sel_max < 1 + 2 + 8
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[16] = 100                                       # workspace too small
+    assert f(*bad) == WS
+    bad = list(args); bad[15] = None
+    assert f(*bad) == WS
+    bad = list(args); bad[6] = 32
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[7] = 20000                                      # NB_cap beyond the select kernel
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[10] = -1
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[1] = P_ODD
+    assert f(*bad) == ALIGN
+
+
+def test_multihead_validation(L):
+    f = L.sda_score_select_multihead
+    base = [P, P, P, 1, 1, 8, 2, 64, 64, 1, 2, 8, 11, 8.0, P, P, None, P, 1 << 24, None]
+    bad = list(base); bad[5] = 7                                          # H_q not a multiple of H_kv
+    assert f(*bad) == SHAPE
+    bad = list(base); bad[13] = 0.0
+    assert f(*bad) == SHAPE
+    bad = list(base); bad[18] = 16
+    assert f(*bad) == WS
+
+
+def test_decode_validation(L):
+    f = L.sda_sparse_decode
+    base = [P, P, P, P, P, P, 11, None, 4096, 1, 1, 8, 2, 64, 0.125, P, None, 0, P, 1 << 24, None]
+    bad = list(base); bad[1] = None
+    assert f(*bad) == NULL
+    bad = list(base); bad[13] = 80
+    assert f(*bad) == UNSUP
+    bad = list(base); bad[11] = 6; bad[12] = 4                            # 6 heads over 4 KV heads
+    assert f(*bad) == SHAPE
+    bad = list(base); bad[11] = 128; bad[12] = 2                          # G = 64
+    assert f(*bad) == UNSUP
+    bad = list(base); bad[14] = float("nan")
+    assert f(*bad) == SHAPE
+    bad = list(base); bad[17] = -1
+    assert f(*bad) == SHAPE
+    bad = list(base); bad[18] = None; bad[19] = 0                         # auto split needs a workspace
+    assert f(*bad) == WS
+    bad = list(base); bad[2] = P_ODD
+    assert f(*bad) == ALIGN
+
+
+def test_grouped_validation(L):
+    f = L.sda_grouped_decode
+    base = [P, P, P, P, P, P, 16, 65536, 1024, 4, 16, 32, 8, 128, 0.088, 4, 0, P, None, None, 0, P,
+            1 << 28, None]
+    bad = list(base); bad[15] = 9                                         # C > 8
+    assert f(*bad) == UNSUP
+    bad = list(base); bad[16] = 2
+    assert f(*bad) == SHAPE
+    bad = list(base); bad[11] = 64; bad[15] = 8                            # C*G = 64 rows
+    assert f(*bad) == UNSUP
+    bad = list(base); bad[8] = 10                                         # NB_cap below T_cap/64
+    assert f(*bad) == SHAPE
+
+
+def test_gather_validation(L):
+    f = L.sda_gather_blocks
+    base = [P, P, P, P, 35, 4, 8, 128, 262144, P, P, P, 0, None]
+    bad = list(base); bad[0] = None
+    assert f(*bad) == NULL
+    bad = list(base); bad[7] = 32
+    assert f(*bad) == UNSUP
+    bad = list(base); bad[12] = -3
+    assert f(*bad) == SHAPE
+    bad = list(base); bad[9] = P_ODD
+    assert f(*bad) == ALIGN
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    k = torch.zeros((1, 2, 64, 64), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        sda.sda_update_compressed_keys(k, k, torch.zeros(1, dtype=torch.int32),
+                                       torch.zeros(1, dtype=torch.int32), 64)
+    kb = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):                                        # CPU tensors are refused
+        sda.sda_update_compressed_keys(kb, torch.zeros((1, 2, 1, 64)), torch.zeros(1, dtype=torch.int32),
+                                       torch.zeros(1, dtype=torch.int32), 64)

@@ -1,0 +1,275 @@
+"""GPU parity on the five workload configurations at full size.
+
+Config 2 and 4 are checked whole; config 3 checks selection on sampled rows
+(the oracle pools their 131072 keys in float64) and attention on every row;
+config 5 checks the offloaded (pinned host) path against the resident one
+and against the oracle on sampled rows.  Launch configurations are the
+library defaults, as the benchmark uses them.
+"""
+import dataclasses
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_pool_amd as sda
+import oracle as O
+import synth
+from synth import inputs
+from tests.parity_util import (DEV, TOL, SparseRows, bits, gpu_ktilde, oracle_decode, oracle_kt, oracle_select,
+                               rows_of, scale_of, seq, tie_free_indexer, tie_free_queries_mh)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    sda.lib()
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _mismatches(bi, ns, want):
+    bi = bi.cpu().numpy()
+    ns = ns.cpu().numpy()
+    bad = []
+    for r, w in want.items():
+        n = int(ns[r])
+        if n != len(w) or not np.array_equal(bi[r][:n], w) or not np.all(bi[r][n:] == -1):
+            bad.append(r)
+    return bad
+
+
+def _decode_err(cfg, out, Qd, rk, lists, T):
+    G = cfg.G
+    err = 0.0
+    for (b, q, g), blocks in lists.items():
+        o, _ = oracle_decode(Qd, rk, b, q, g, G, blocks, T, scale_of(cfg))
+        err = max(err, float(np.abs(out[b, q, g * G:(g + 1) * G].double().cpu().numpy() - o).max()))
+    return err
+
+
+def _gpu_lists(bi, ns, rows):
+    bi = bi.cpu().numpy()
+    ns = ns.cpu().numpy()
+    return {r: bi[r][:ns[r]] for r in rows}
+
+
+# ---------------------------------------------------------------------------
+
+def test_c2_llama8b_shaped_full():
+    cfg = synth.get_config(2)
+    _say("c2: draw (bias along the attempt-0 indexer directions)")
+    dirs = inputs.bias_directions(inputs.indexer_vectors(cfg, 0))
+    K, V, bmask = inputs.kv_layer(cfg, 0, device=DEV, bias_dirs=dirs)
+    kv_rows = [(b, g) for b in range(cfg.B) for g in range(cfg.H_kv)]
+    kt = oracle_kt(K, cfg.T, kv_rows)
+    rows = rows_of(cfg)
+    F, att = tie_free_indexer(cfg, 0, kt, rows)
+    _say("c2: redrawn rows", int((att > 0).sum()))
+    ktg = gpu_ktilde(K, cfg.T)
+    for (b, g) in kv_rows:
+        assert np.abs(ktg[b, g].double().cpu().numpy() - kt[(b, g)]).max() < 1e-6
+    bi, ns = sda.sda_score_select(F.to(DEV), ktg, seq(cfg), cfg.n_init, cfg.n_local, cfg.top_k)
+    want = oracle_select(cfg, O.bf16_to_f64(bits(F)), kt, rows)
+    assert _mismatches(bi, ns, want) == []
+    # structure: the chosen top-k blocks are the biased ones
+    inside = np.mean([np.mean(bmask[b, g][want[(b, q, g)][1:-2]]) for (b, q, g) in rows])
+    _say("c2: fraction of top-k inside biased blocks", inside)
+    assert inside > 0.9
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0))
+    out, _ = sda.sda_sparse_decode(Q.to(DEV), K, V, seq(cfg), bi, ns)
+    err = _decode_err(cfg, out, O.bf16_to_f64(bits(Q)), SparseRows(K, V, cfg.T), want, cfg.T)
+    _say("c2: max abs err", err)
+    assert err <= TOL
+
+
+def _c3_sample(cfg):
+    return [(b, 0, (3 * b + s) % cfg.H_kv) for b in range(cfg.B) for s in (0, 4)]
+
+
+def test_c3_70b_shaped_128k():
+    cfg = synth.get_config(3)
+    _say("c3: draw layer l+1 K/V on the GPU")
+    K, V, _ = inputs.kv_layer(cfg, 1, device=DEV)
+    sample = _c3_sample(cfg)
+    kt = oracle_kt(K, cfg.T, [(b, g) for (b, _, g) in sample])
+    F, att = tie_free_indexer(cfg, 0, kt, sample)          # F of layer l scores layer l+1
+    ktg = gpu_ktilde(K, cfg.T)
+    for (b, _, g) in sample:
+        assert np.abs(ktg[b, g].double().cpu().numpy() - kt[(b, g)]).max() < 1e-6
+    bi, ns = sda.sda_score_select(F.to(DEV), ktg, seq(cfg), cfg.n_init, cfg.n_local, cfg.top_k)
+    want = oracle_select(cfg, O.bf16_to_f64(bits(F)), kt, sample)
+    assert _mismatches(bi, ns, want) == []
+    assert int(ns.min()) == int(ns.max()) == 35
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 1))
+    out, lse = sda.sda_sparse_decode(Q.to(DEV), K, V, seq(cfg), bi, ns)
+    # every row: the oracle's list on sampled rows, the GPU's (checked format) elsewhere
+    lists = _gpu_lists(bi, ns, rows_of(cfg))
+    lists.update(want)
+    err = _decode_err(cfg, out, O.bf16_to_f64(bits(Q)), SparseRows(K, V, cfg.T), lists, cfg.T)
+    _say("c3: max abs err", err)
+    assert err <= TOL
+
+    # the G-head comparator on the same compressed keys (eq. (8)/(10) reading, tau = sqrt(d))
+    tau = math.sqrt(cfg.d)
+    Qm, _ = tie_free_queries_mh(cfg, 1, kt, sample, tau)
+    bm, nm = sda.sda_score_select_multihead(Qm.to(DEV), ktg, seq(cfg), cfg.n_init, cfg.n_local, cfg.top_k,
+                                            tau)
+    Qmd = O.bf16_to_f64(bits(Qm))
+    G = cfg.G
+    want_m = {r: O.select_row_multihead(Qmd[r[0], r[1], r[2] * G:(r[2] + 1) * G], kt[(r[0], r[2])],
+                                        cfg.n_init, cfg.n_local, cfg.top_k, tau)[0] for r in sample}
+    assert _mismatches(bm, nm, want_m) == []
+
+
+def test_comparator_one_head_equals_indexer():
+    # G = 1 and q = f: softmax over blocks is monotone, so the selections agree
+    cfg = dataclasses.replace(synth.get_config(1), H_q=2)
+    K, _, _ = inputs.kv_layer(cfg, 0, device="cpu")
+    ktg = gpu_ktilde(K.to(DEV), cfg.T)
+    kt = oracle_kt(K, cfg.T, [(0, 0), (0, 1)])
+    F, _ = tie_free_indexer(cfg, 0, kt, rows_of(cfg))
+    Fg = F.to(DEV)
+    a, na = sda.sda_score_select(Fg, ktg, seq(cfg), 1, 2, 8)
+    b, nb_ = sda.sda_score_select_multihead(Fg, ktg, seq(cfg), 1, 2, 8, math.sqrt(cfg.d))
+    assert torch.equal(a, b) and torch.equal(na, nb_)
+
+
+# ---------------------------------------------------------------------------
+# config 4: SSV grouped verification
+# ---------------------------------------------------------------------------
+
+def _adjacent_overlap(cfg, lists):
+    vals = []
+    for b in range(cfg.B):
+        for g in range(cfg.H_kv):
+            for grp in O.groups(cfg.NQ, cfg.group_C):
+                for c0, c1 in zip(grp[:-1], grp[1:]):
+                    a, bb = set(lists[(b, c0, g)]), set(lists[(b, c1, g)])
+                    vals.append(len(a & bb) / max(1, len(a)))
+    return float(np.mean(vals))
+
+
+def _tune_sigma(cfg, kt, gamma, iters=14):
+    """Bisection on the draft-query noise so that adjacent queries of a group
+    share a fraction gamma of their blocks (oracle selections)."""
+    rows = rows_of(cfg)
+    lo, hi = 0.0, 4.0
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        Fd = O.bf16_to_f64(bits(inputs.to_bf16(inputs.indexer_vectors(cfg, 0, sigma=mid))))
+        ov = _adjacent_overlap(cfg, oracle_select(cfg, Fd, kt, rows))
+        if ov > gamma:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+@pytest.fixture(scope="module")
+def c4_data():
+    cfg = synth.get_config(4)
+    _say("c4: draw K/V")
+    K, V, _ = inputs.kv_layer(cfg, 0, device=DEV)
+    kv_rows = [(b, g) for b in range(cfg.B) for g in range(cfg.H_kv)]
+    kt = oracle_kt(K, cfg.T, kv_rows)
+    ktg = gpu_ktilde(K, cfg.T)
+    return cfg, K, V, kt, ktg
+
+
+@pytest.mark.parametrize("gamma", [0.5, 0.75, 0.9])
+def test_c4_grouped_verification(c4_data, gamma):
+    cfg, K, V, kt, ktg = c4_data
+    sigma = _tune_sigma(cfg, kt, gamma)
+    rows = rows_of(cfg)
+    F, att = tie_free_indexer(cfg, 0, kt, rows, sigma=sigma)
+    Fd = O.bf16_to_f64(bits(F))
+    want = oracle_select(cfg, Fd, kt, rows)
+    measured = _adjacent_overlap(cfg, want)
+    _say(f"c4: gamma target {gamma} sigma {sigma:.4f} measured {measured:.3f} redrawn {(att > 0).sum()}")
+    assert abs(measured - gamma) < 0.05
+    bi, ns = sda.sda_score_select(F.to(DEV), ktg, seq(cfg), 0, 0, cfg.top_k)
+    assert _mismatches(bi, ns, want) == []
+
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0, sigma=sigma))
+    Qg = Q.to(DEV)
+    Qd = O.bf16_to_f64(bits(Q))
+    rk = SparseRows(K, V, cfg.T)
+    C, G = cfg.group_C, cfg.G
+    outA, _, uA = sda.sda_grouped_decode(Qg, K, V, seq(cfg), bi, ns, C, sda.SDA_GROUP_EXACT)
+    outB, _, uB = sda.sda_grouped_decode(Qg, K, V, seq(cfg), bi, ns, C, sda.SDA_GROUP_SHARED_REP)
+    per_q, _ = sda.sda_sparse_decode(Qg, K, V, seq(cfg), bi, ns)
+    uA, uB = uA.cpu().numpy(), uB.cpu().numpy()
+    errA = errB = 0.0
+    unions = []
+    for b in range(cfg.B):
+        for gi, grp in enumerate(O.groups(cfg.NQ, C)):
+            for g in range(cfg.H_kv):
+                lists = [want[(b, c, g)] for c in grp]
+                qrows = np.stack([Qd[b, c, g * G:(g + 1) * G] for c in grp])
+                kf, vf = rk.get(b, g, O.union_blocks(lists))
+                oa, _, ua = O.grouped_row(qrows, kf, vf, lists, cfg.T, scale_of(cfg), O.MODE_EXACT)
+                ob, _, ub = O.grouped_row(qrows, kf, vf, lists, cfg.T, scale_of(cfg), O.MODE_SHARED_REP)
+                assert uA[b, gi, g] == ua and uB[b, gi, g] == ub
+                unions.append(ua)
+                for ci, c in enumerate(grp):
+                    sl = slice(g * G, (g + 1) * G)
+                    errA = max(errA, np.abs(outA[b, c, sl].double().cpu().numpy() - oa[ci]).max())
+                    errB = max(errB, np.abs(outB[b, c, sl].double().cpu().numpy() - ob[ci]).max())
+    dAB = (outA - per_q).abs().max().item()
+    n = cfg.top_k
+    _say(f"c4: gamma {gamma}: errA {errA:.2e} errB {errB:.2e} |A - per-query| {dAB:.2e} "
+         f"mean union {np.mean(unions):.2f} formula {O.union_size_formula(n, C, measured):.2f}")
+    assert errA <= TOL and errB <= TOL
+    assert dAB < 1e-4
+
+
+# ---------------------------------------------------------------------------
+# config 5: offloaded K/V in pinned host memory
+# ---------------------------------------------------------------------------
+
+def test_c5_offloaded_gather_matches_resident():
+    cfg = synth.get_config(5)
+    T = cfg.T
+    dev_layers = []
+    host = []
+    for l in range(2):
+        _say(f"c5: draw layer {l}")
+        K, V, _ = inputs.kv_layer(cfg, l, device=DEV)
+        Kh = torch.empty(K.shape, dtype=torch.bfloat16, pin_memory=True)
+        Vh = torch.empty(V.shape, dtype=torch.bfloat16, pin_memory=True)
+        Kh.copy_(K)
+        Vh.copy_(V)
+        dev_layers.append((K, V, gpu_ktilde(K, T)))
+        host.append((Kh, Vh))
+    K1, V1, ktg1 = dev_layers[1]
+    sample = [(b, 0, (5 * b + 1) % cfg.H_kv) for b in range(cfg.B)]
+    kt = oracle_kt(K1, T, [(b, g) for (b, _, g) in sample])
+    F0, _ = tie_free_indexer(cfg, 0, kt, sample)            # layer 0's F scores layer 1
+    bi, ns = sda.sda_score_select(F0.to(DEV), ktg1, seq(cfg), cfg.n_init, cfg.n_local, cfg.top_k)
+    want = oracle_select(cfg, O.bf16_to_f64(bits(F0)), kt, sample)
+    assert _mismatches(bi, ns, want) == []
+    side = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    ev.record()
+    with torch.cuda.stream(side):
+        side.wait_event(ev)
+        ks, vs, slot = sda.sda_gather_blocks(host[1][0], host[1][1], bi, ns, max_workgroups=256)
+        done = torch.cuda.Event()
+        done.record(side)
+    torch.cuda.current_stream().wait_event(done)
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 1)).to(DEV)
+    staged, _ = sda.sda_sparse_decode(Q, ks, vs, seq(cfg), bi, ns, slot=slot)
+    resident, _ = sda.sda_sparse_decode(Q, K1, V1, seq(cfg), bi, ns)
+    assert torch.equal(staged, resident)
+    err = _decode_err(cfg, staged, O.bf16_to_f64(bits(Q.cpu())), SparseRows(K1, V1, T), want, T)
+    _say("c5: max abs err", err)
+    assert err <= TOL

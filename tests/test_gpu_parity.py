@@ -1,0 +1,259 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on
+the same seeded inputs.  Block indices must match bit for bit; outputs must
+lie within 2e-3 max-abs.  Small cases run whole; the full-size workloads
+compare every row that the oracle can afford and sample the rest.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_pool_amd as sda
+import oracle as O
+import synth
+from synth import inputs
+from tests.parity_util import (DEV, TOL, SparseRows, bits, f64, gpu_ktilde, oracle_decode, oracle_kt,
+                               oracle_select, rows_of, scale_of, seq, tie_free_indexer)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    sda.lib()          # raises if libsda.so is missing: there is no fallback path
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _check_selection(cfg, bi, ns, want, rows):
+    bi = bi.cpu().numpy()
+    ns = ns.cpu().numpy()
+    bad = 0
+    for r in rows:
+        w = want[r]
+        n = int(ns[r])
+        if n != len(w) or not np.array_equal(bi[r][:n], w) or not np.all(bi[r][n:] == -1):
+            bad += 1
+    return bad
+
+
+# ---------------------------------------------------------------------------
+# config 1: the whole path on the tiny decode step
+# ---------------------------------------------------------------------------
+
+def test_c1_full_path():
+    cfg = synth.get_config(1)
+    _say("c1: draw")
+    K, V, _ = inputs.kv_layer(cfg, 0, device="cpu")
+    Kg, Vg = K.to(DEV), V.to(DEV)
+    kv_rows = [(b, g) for b in range(cfg.B) for g in range(cfg.H_kv)]
+    kt = oracle_kt(K, cfg.T, kv_rows)
+    _say("c1: compressed keys")
+    ktg = gpu_ktilde(Kg, cfg.T)
+    for (b, g) in kv_rows:
+        assert np.abs(ktg[b, g].double().cpu().numpy() - kt[(b, g)]).max() < 1e-6
+    rows = rows_of(cfg)
+    F, _ = tie_free_indexer(cfg, 0, kt, rows)
+    want = oracle_select(cfg, O.bf16_to_f64(bits(F)), kt, rows)
+    _say("c1: select")
+    scores = torch.empty((cfg.B, cfg.NQ, cfg.H_kv, ktg.shape[2]), dtype=torch.float32, device=DEV)
+    bi, ns = sda.sda_score_select(F.to(DEV), ktg, seq(cfg), cfg.n_init, cfg.n_local, cfg.top_k, scores=scores)
+    assert _check_selection(cfg, bi, ns, want, rows) == 0
+    Fd = O.bf16_to_f64(bits(F))
+    for (b, q, g) in rows:
+        s = O.indexer_scores(Fd[b, q, g], kt[(b, g)])
+        assert np.abs(scores[b, q, g, :cfg.NB].double().cpu().numpy() - s).max() < 1e-5
+    _say("c1: decode")
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0))
+    out, lse = sda.sda_sparse_decode(Q.to(DEV), Kg, Vg, seq(cfg), bi, ns)
+    torch.cuda.synchronize()
+    Qd = O.bf16_to_f64(bits(Q))
+    rk = SparseRows(K, V, cfg.T)
+    G = cfg.G
+    err = 0.0
+    for (b, q, g) in rows:
+        o, l = oracle_decode(Qd, rk, b, q, g, G, want[(b, q, g)], cfg.T, scale_of(cfg))
+        err = max(err, np.abs(out[b, q, g * G:(g + 1) * G].double().cpu().numpy() - o).max())
+        assert np.abs(lse[b, q, g * G:(g + 1) * G].double().cpu().numpy() - l).max() < 1e-3
+    _say("c1: max abs err", err)
+    assert err <= TOL
+
+
+def test_c1_dense_special_case_matches_sdpa():
+    # k >= every candidate: the block set is all blocks, so the result is
+    # dense attention over the T tokens (torch SDPA on the CPU, float64)
+    cfg = synth.get_config(1)
+    K, V, _ = inputs.kv_layer(cfg, 0, device="cpu")
+    Kg, Vg = K.to(DEV), V.to(DEV)
+    ktg = gpu_ktilde(Kg, cfg.T)
+    F = inputs.to_bf16(inputs.indexer_vectors(cfg, 0)).to(DEV)
+    bi, ns = sda.sda_score_select(F, ktg, seq(cfg), 1, 2, cfg.NB)
+    assert ns.min().item() == cfg.NB == ns.max().item()
+    for g in range(cfg.H_kv):
+        assert torch.equal(bi[0, 0, g, :cfg.NB].cpu(), torch.arange(cfg.NB, dtype=torch.int32))
+        assert torch.all(bi[0, 0, g, cfg.NB:] == -1)
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0))
+    out, _ = sda.sda_sparse_decode(Q.to(DEV), Kg, Vg, seq(cfg), bi, ns)
+    G = cfg.G
+    for g in range(cfg.H_kv):
+        q = Q[0, 0, g * G:(g + 1) * G].double()[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, K[0, g].double()[None, None],
+                                                               V[0, g].double()[None, None])[0]
+        assert (out[0, 0, g * G:(g + 1) * G].double().cpu() - ref).abs().max().item() <= TOL
+
+
+# ---------------------------------------------------------------------------
+# compressed keys: partial blocks and incremental updates
+# ---------------------------------------------------------------------------
+
+def test_ktilde_partial_block_and_incremental_update():
+    cfg = synth.get_config(1)
+    K, _, _ = inputs.kv_layer(cfg, 0, device="cpu")
+    Kg = K.to(DEV)
+    T0, T1 = 3000, 3131
+    kt0 = oracle_kt(K, T1, [(0, 0), (0, 1)])
+    bulk = gpu_ktilde(Kg, T1)
+    nb = O.num_blocks(T1)
+    for g in range(2):
+        assert np.abs(bulk[0, g, :nb].double().cpu().numpy() - kt0[(0, g)]).max() < 1e-6
+    # token-by-token on the GPU equals the bulk build bit for bit
+    inc = gpu_ktilde(Kg, T0)
+    for t in range(T0, T1):
+        lo = torch.tensor([t], dtype=torch.int32, device=DEV)
+        hi = torch.tensor([t + 1], dtype=torch.int32, device=DEV)
+        sda.sda_update_compressed_keys(Kg, inc, lo, hi, 1)
+    assert torch.equal(inc[:, :, :nb], bulk[:, :, :nb])
+    # and stays within fp32 noise of the oracle's running-mean update
+    kk = f64(K[0, 0, :T1])
+    run = O.compressed_keys(kk, T0)
+    for t in range(T0, T1):
+        run = O.append_token(run, t, kk[t])
+    assert np.abs(inc[0, 0, :nb].double().cpu().numpy() - run).max() < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# selection edge cases
+# ---------------------------------------------------------------------------
+
+def _select_direct(kt_np, F_np, T, n_init, n_local, k):
+    """Run score_select on a hand-made K~ (float32) and F (float32 -> bf16)."""
+    B, H, NB, d = kt_np.shape
+    ktg = torch.from_numpy(kt_np.astype(np.float32)).to(DEV)
+    Fb = inputs.to_bf16(F_np)
+    bi, ns = sda.sda_score_select(Fb.to(DEV), ktg, torch.full((B,), T, dtype=torch.int32, device=DEV),
+                                  n_init, n_local, k)
+    return bi.cpu().numpy(), ns.cpu().numpy(), O.bf16_to_f64(bits(Fb))
+
+
+@pytest.mark.parametrize("T,k", [(1, 8), (64, 8), (65, 8), (128, 8), (192, 8), (640, 0), (640, 7),
+                                 (640, 100), (4000, 5)])
+def test_select_small_and_degenerate(T, k):
+    rng = np.random.default_rng(T * 31 + k)
+    NB, d = 70, 64
+    kt = rng.standard_normal((1, 2, NB, d)) / 8
+    F = rng.standard_normal((1, 1, 2, d)) / 8
+    bi, ns, Fd = _select_direct(kt, F, T, 1, 2, k)
+    nb = O.num_blocks(T)
+    for g in range(2):
+        want, _ = O.select_row(Fd[0, 0, g], O.store_f32(kt[0, g, :nb]), 1, 2, k)
+        n = int(ns[0, 0, g])
+        assert n == len(want)
+        assert list(bi[0, 0, g, :n]) == list(want)
+        assert np.all(bi[0, 0, g, n:] == -1)
+
+
+def test_select_ties_go_to_lower_index():
+    rng = np.random.default_rng(5)
+    NB, d = 300, 128
+    kt = rng.standard_normal((1, 1, NB, d)) / 64
+    kt[0, 0, [40, 90, 91, 150, 260]] = kt[0, 0, 7]       # six identical pooled keys
+    F = np.zeros((1, 1, 1, d))
+    F[0, 0, 0] = kt[0, 0, 7] * 50                          # they score highest
+    bi, ns, Fd = _select_direct(kt, F, NB * 64, 1, 2, 4)
+    assert list(bi[0, 0, 0, :ns[0, 0, 0]]) == [0, 7, 40, 90, 91, 298, 299]
+    want, _ = O.select_row(Fd[0, 0, 0], O.store_f32(kt[0, 0]), 1, 2, 4)
+    assert list(want) == [0, 7, 40, 90, 91, 298, 299]
+
+
+# ---------------------------------------------------------------------------
+# decode invariants
+# ---------------------------------------------------------------------------
+
+def _c1_decode_inputs(T=None):
+    cfg = synth.get_config(1)
+    T = cfg.T if T is None else T
+    K, V, _ = inputs.kv_layer(cfg, 0, device="cpu")
+    Kg, Vg = K.to(DEV), V.to(DEV)
+    ktg = gpu_ktilde(Kg, T)
+    F = inputs.to_bf16(inputs.indexer_vectors(cfg, 0)).to(DEV)
+    bi, ns = sda.sda_score_select(F, ktg, seq(cfg, T), cfg.n_init, cfg.n_local, cfg.top_k)
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0))
+    return cfg, K, V, Kg, Vg, bi, ns, Q, T
+
+
+def test_decode_split_invariance_and_determinism():
+    cfg, K, V, Kg, Vg, bi, ns, Q, T = _c1_decode_inputs()
+    Qg = Q.to(DEV)
+    ref, lref = sda.sda_sparse_decode(Qg, Kg, Vg, seq(cfg), bi, ns, split_k=1)
+    for sk in (2, 3, 5, 11, 0):
+        o, l = sda.sda_sparse_decode(Qg, Kg, Vg, seq(cfg), bi, ns, split_k=sk)
+        assert (o - ref).abs().max().item() < 1e-5
+        assert (l - lref).abs().max().item() < 1e-5
+        o2, _ = sda.sda_sparse_decode(Qg, Kg, Vg, seq(cfg), bi, ns, split_k=sk)
+        assert torch.equal(o, o2)
+
+
+def test_decode_partial_last_block():
+    cfg, K, V, Kg, Vg, bi, ns, Q, T = _c1_decode_inputs(T=4000)
+    out, lse = sda.sda_sparse_decode(Q.to(DEV), Kg, Vg, seq(cfg, T), bi, ns)
+    bi_h, ns_h = bi.cpu().numpy(), ns.cpu().numpy()
+    Qd = O.bf16_to_f64(bits(Q))
+    rk = SparseRows(K, V, T)
+    G = cfg.G
+    for g in range(cfg.H_kv):
+        blocks = bi_h[0, 0, g, :ns_h[0, 0, g]]
+        assert O.num_blocks(T) - 1 in blocks                # the partial block is local
+        o, l = oracle_decode(Qd, rk, 0, 0, g, G, blocks, T, scale_of(cfg))
+        assert np.abs(out[0, 0, g * G:(g + 1) * G].double().cpu().numpy() - o).max() <= TOL
+
+
+def test_decode_empty_and_invalid_entries():
+    cfg, K, V, Kg, Vg, bi, ns, Q, T = _c1_decode_inputs()
+    bi2 = bi.clone()
+    ns2 = ns.clone()
+    ns2[0, 0, 1] = 0                                          # empty row
+    bi2[0, 0, 0, 3] = 10_000                                  # out-of-range ids are skipped
+    bi2[0, 0, 0, 4] = -5
+    out, lse = sda.sda_sparse_decode(Q.to(DEV), Kg, Vg, seq(cfg), bi2, ns2)
+    G = cfg.G
+    assert torch.all(out[0, 0, G:2 * G] == 0)
+    assert torch.all(torch.isneginf(lse[0, 0, G:2 * G]))
+    keep = [int(j) for i, j in enumerate(bi.cpu().numpy()[0, 0, 0, :ns[0, 0, 0]]) if i not in (3, 4)]
+    o, _ = oracle_decode(O.bf16_to_f64(bits(Q)), SparseRows(K, V, T), 0, 0, 0, G, keep, T, scale_of(cfg))
+    assert np.abs(out[0, 0, :G].double().cpu().numpy() - o).max() <= TOL
+
+
+def test_multi_query_plain_decode_each_query_own_list():
+    cfg = synth.get_config(1)
+    import dataclasses
+    cfg = dataclasses.replace(cfg, NQ=3)
+    K, V, _ = inputs.kv_layer(cfg, 0, device="cpu")
+    Kg, Vg = K.to(DEV), V.to(DEV)
+    ktg = gpu_ktilde(Kg, cfg.T)
+    F = inputs.to_bf16(inputs.indexer_vectors(cfg, 0)).to(DEV)
+    bi, ns = sda.sda_score_select(F, ktg, seq(cfg), 1, 2, 8)
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0))
+    out, _ = sda.sda_sparse_decode(Q.to(DEV), Kg, Vg, seq(cfg), bi, ns)
+    Qd = O.bf16_to_f64(bits(Q))
+    rk = SparseRows(K, V, cfg.T)
+    for (b, q, g) in rows_of(cfg):
+        blocks = bi.cpu().numpy()[b, q, g, :ns[b, q, g].item()]
+        o, _ = oracle_decode(Qd, rk, b, q, g, cfg.G, blocks, cfg.T, scale_of(cfg))
+        assert np.abs(out[b, q, g * cfg.G:(g + 1) * cfg.G].double().cpu().numpy() - o).max() <= TOL
