@@ -128,11 +128,39 @@ def _need(t, name, dtype, ndim=None, device=True):
 
 
 def _workspace(nbytes, device, ws=None):
-    if nbytes == 0:
-        return None, 0
+    """Caller's workspace, or a new zero-filled one (the split decode keeps
+    arrival counters in it that must start at zero)."""
     if ws is not None:
         return ws, ws.numel() * ws.element_size()
-    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+    if nbytes == 0:
+        return None, 0
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+class PreparedCall:
+    """A library call whose ctypes arguments are converted once.
+
+    run() re-sends them with the current (or given) stream, so a decode loop
+    pays only the foreign-call cost per launch.  The tensors the call was
+    prepared with must stay alive and keep their storage."""
+
+    def __init__(self, name, args, keep):
+        self._fn = getattr(lib(), name)
+        self._args = list(args)
+        self._keep = keep
+        self.name = name
+
+    def run(self, stream=None):
+        self._args[-1] = _stream(stream)
+        _check(self._fn(*self._args))
+
+
+def prepare(fn_py, *a, **kw):
+    """Run a binding function's checks and allocations without launching and
+    return (PreparedCall, outputs); supported for sda_score_select and
+    sda_sparse_decode."""
+    kw["_prepare"] = True
+    return fn_py(*a, **kw)
 
 
 # ---------------------------------------------------------------------------
@@ -153,7 +181,7 @@ def sda_update_compressed_keys(k, k_tilde, len_old, len_new, max_new_tokens, str
 
 
 def sda_score_select(f, k_tilde, seq_len, n_init, n_local, top_k, n_sel_max=None, block_idx=None,
-                     n_sel=None, scores=None, ws=None, stream=None):
+                     n_sel=None, scores=None, ws=None, stream=None, _prepare=False):
     """Indexer scores, exact top-k and block-set assembly; returns (block_idx, n_sel)."""
     _need(f, "f", torch.bfloat16, 4)
     _need(k_tilde, "k_tilde", torch.float32, 4)
@@ -176,9 +204,12 @@ def sda_score_select(f, k_tilde, seq_len, n_init, n_local, top_k, n_sel_max=None
     else:
         nbytes = lib().sda_score_select_workspace(B, NQ, H, NB_cap, top_k)
     ws, wsb = _workspace(nbytes, f.device, ws)
-    _check(lib().sda_score_select(_ptr(f), _ptr(k_tilde), _ptr(seq_len), B, NQ, H, d, NB_cap, n_init, n_local,
-                                  top_k, n_sel_max, _ptr(block_idx), _ptr(n_sel), _ptr(scores), _ptr(ws), wsb,
-                                  _stream(stream)))
+    args = (_ptr(f), _ptr(k_tilde), _ptr(seq_len), B, NQ, H, d, NB_cap, n_init, n_local,
+            top_k, n_sel_max, _ptr(block_idx), _ptr(n_sel), _ptr(scores), _ptr(ws), wsb, None)
+    if _prepare:
+        return PreparedCall("sda_score_select", args, (f, k_tilde, seq_len, block_idx, n_sel, scores, ws)), \
+            (block_idx, n_sel)
+    _check(lib().sda_score_select(*args[:-1], _stream(stream)))
     return block_idx, n_sel
 
 
@@ -208,7 +239,7 @@ def sda_score_select_multihead(q, k_tilde, seq_len, n_init, n_local, top_k, tau,
 
 
 def sda_sparse_decode(q, k, v, seq_len, block_idx, n_sel, scale=None, out=None, lse=None, slot=None,
-                      split_k=0, ws=None, stream=None):
+                      split_k=0, ws=None, stream=None, _prepare=False):
     """Block-sparse decode attention; returns (out, lse)."""
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
@@ -231,9 +262,13 @@ def sda_sparse_decode(q, k, v, seq_len, block_idx, n_sel, scale=None, out=None, 
         lse = torch.empty((B, NQ, H_q), dtype=torch.float32, device=q.device)
     nbytes = lib().sda_sparse_decode_workspace(B, NQ, H_q, H_kv, n_sel_max, d, int(split_k))
     ws, wsb = _workspace(nbytes, q.device, ws)
-    _check(lib().sda_sparse_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(block_idx), _ptr(n_sel),
-                                   n_sel_max, _ptr(slot), T_cap, B, NQ, H_q, H_kv, d, float(scale), _ptr(out),
-                                   _ptr(lse), int(split_k), _ptr(ws), wsb, _stream(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(block_idx), _ptr(n_sel),
+            n_sel_max, _ptr(slot), T_cap, B, NQ, H_q, H_kv, d, float(scale), _ptr(out),
+            _ptr(lse), int(split_k), _ptr(ws), wsb, None)
+    if _prepare:
+        return PreparedCall("sda_sparse_decode", args, (q, k, v, seq_len, block_idx, n_sel, out, lse, slot, ws)), \
+            (out, lse)
+    _check(lib().sda_sparse_decode(*args[:-1], _stream(stream)))
     return out, lse
 
 

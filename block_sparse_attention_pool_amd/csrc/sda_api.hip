@@ -61,11 +61,25 @@ sda_status_t check_heads(int H_q, int H_kv) {
     return SDA_OK;
 }
 
-int decode_splits(int split_k, int list_max) {
-    int s = split_k > 0 ? split_k : attn_default_splits(list_max);
+int decode_splits(int split_k, int list_max, int d, int rows_pad) {
+    int s = split_k > 0 ? split_k : attn_default_splits(list_max, attn_waves(d, rows_pad));
     if (s < 1) s = 1;
     if (s > kMaxSplits) s = kMaxSplits;
     return s;
+}
+
+// workspace of the split decode: [counters, 256-byte padded][(m, l) partials][o partials]
+void set_workspace(AttnArgs& a, void* ws, size_t need, int tasks, int ns, int rp) {
+    if (need == 0) {
+        a.counters = nullptr;
+        a.part_ml = a.part_o = nullptr;
+        return;
+    }
+    char* base = static_cast<char*>(ws);
+    const size_t cbytes = ((size_t)tasks * sizeof(int) + 255) / 256 * 256;
+    a.counters = reinterpret_cast<int*>(base);
+    a.part_ml = reinterpret_cast<float*>(base + cbytes);
+    a.part_o = a.part_ml + (size_t)tasks * ns * rp * 2;
 }
 
 #define TRY(expr)                          \
@@ -206,8 +220,9 @@ sda_status_t sda_score_select_multihead(const void* q, const float* k_tilde, con
 size_t sda_sparse_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int split_k) {
     if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || H_q % H_kv) return 0;
     const int G = H_q / H_kv;
-    const int ns = decode_splits(split_k, n_sel_max);
-    return attn_ws_bytes(B * NQ * H_kv, ns, attn_rows_pad(1, G), d);
+    const int rp = attn_rows_pad(1, G);
+    const int ns = decode_splits(split_k, n_sel_max, d, rp);
+    return attn_ws_bytes(B * NQ * H_kv, ns, rp, d);
 }
 
 static sda_status_t check_attn_common(const void* q, const void* k, const void* v, const int32_t* seq_len,
@@ -239,8 +254,9 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
     REQUIRE(tasks <= kMaxGridYZ, SDA_ERR_SHAPE, "B*NQ*H_kv=%lld exceeds %d", tasks, kMaxGridYZ);
     REQUIRE(!slot_opt || aligned4(slot_opt), SDA_ERR_ALIGN, "slot_opt must be 4-byte aligned");
     const int G = H_q / H_kv;
-    const int ns = decode_splits(split_k, n_sel_max);
-    const size_t need = attn_ws_bytes((int)tasks, ns, attn_rows_pad(1, G), d);
+    const int rp = attn_rows_pad(1, G);
+    const int ns = decode_splits(split_k, n_sel_max, d, rp);
+    const size_t need = attn_ws_bytes((int)tasks, ns, rp, d);
     REQUIRE(need == 0 || (ws && ws_bytes >= need), SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
             ws ? ws_bytes : 0, need);
     REQUIRE(need == 0 || aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -255,9 +271,7 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
     a.out = out;
     a.lse = lse_opt;
     a.union_count = nullptr;
-    const int rp = attn_rows_pad(1, G);
-    a.part_ml = static_cast<float*>(ws);
-    a.part_o = need ? static_cast<float*>(ws) + (size_t)tasks * ns * rp * 2 : nullptr;
+    set_workspace(a, ws, need, (int)tasks, ns, rp);
     a.n_sel_max = n_sel_max;
     a.T_cap = T_cap;
     a.NB_cap = ceil_div(T_cap, kBlock);
@@ -280,8 +294,9 @@ size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_
     if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || group_C < 1 || H_q % H_kv) return 0;
     const int G = H_q / H_kv;
     const int n_groups = ceil_div(NQ, group_C);
-    const int ns = decode_splits(split_k, group_C * n_sel_max);
-    return attn_ws_bytes(B * n_groups * H_kv, ns, attn_rows_pad(group_C, G), d);
+    const int rp = attn_rows_pad(group_C, G);
+    const int ns = decode_splits(split_k, group_C * n_sel_max, d, rp);
+    return attn_ws_bytes(B * n_groups * H_kv, ns, rp, d);
 }
 
 sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, const int32_t* seq_len,
@@ -302,12 +317,11 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
     const long long tasks = (long long)B * n_groups * H_kv;
     REQUIRE(tasks <= kMaxGridYZ, SDA_ERR_SHAPE, "B*groups*H_kv=%lld exceeds %d", tasks, kMaxGridYZ);
     const int rp = attn_rows_pad(group_C, G);
-    const size_t lds = (size_t)4 * 64 * d * 2 + (size_t)group_C * ((NB_cap + 31) / 32) * 4 +
-                       (size_t)group_C * n_sel_max * 8 + 257 * 4;
+    const size_t lds = attn_smem_bytes_host(d, rp, group_C, mode, NB_cap, n_sel_max);
     REQUIRE(lds <= kLdsBytes, SDA_ERR_UNSUPPORTED, "group needs %zu bytes of LDS", lds);
     const int list_max = (mode == SDA_GROUP_EXACT) ? group_C * n_sel_max : n_sel_max;
-    const int ns = decode_splits(split_k, list_max);
-    const int ns_ws = decode_splits(split_k, group_C * n_sel_max);
+    const int ns = decode_splits(split_k, list_max, d, rp);
+    const int ns_ws = decode_splits(split_k, group_C * n_sel_max, d, rp);
     const size_t need = attn_ws_bytes((int)tasks, ns, rp, d);
     const size_t need_doc = attn_ws_bytes((int)tasks, ns_ws, rp, d);
     REQUIRE(need == 0 || (ws && ws_bytes >= need), SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
@@ -324,8 +338,7 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
     a.out = out;
     a.lse = lse_opt;
     a.union_count = union_count_opt;
-    a.part_ml = static_cast<float*>(ws);
-    a.part_o = need ? static_cast<float*>(ws) + (size_t)tasks * ns * rp * 2 : nullptr;
+    set_workspace(a, ws, need, (int)tasks, ns, rp);
     a.n_sel_max = n_sel_max;
     a.T_cap = T_cap;
     a.NB_cap = NB_cap;

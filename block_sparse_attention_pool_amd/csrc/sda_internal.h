@@ -45,17 +45,21 @@ struct AttnArgs {
     int32_t* union_count;     // may be null
     float* part_o;            // [tasks, n_split, rows_pad, d]
     float* part_ml;           // [tasks, n_split, rows_pad, 2]
+    int* counters;            // [tasks] split arrivals; zero between calls
     int n_sel_max, T_cap, NB_cap;
     int B, NQ, H_q, H_kv, G, d;
     int C;                    // queries per group (1 = plain decode)
     int mode;                 // 0 exact, 1 shared representative
     int n_groups;             // ceil(NQ / C)
     int n_split;
+    int fused_combine;        // 1: the last split's workgroup merges; 0: separate merge launch
     float scale_log2;         // scale * log2(e)
 };
 int attn_rows_pad(int C, int G);                 // 16 or 32
-int attn_default_splits(int list_max);
+int attn_waves(int d, int rows_pad);             // waves per workgroup
+int attn_default_splits(int list_max, int waves);
 size_t attn_ws_bytes(int tasks, int n_split, int rows_pad, int d);
+size_t attn_smem_bytes_host(int d, int rows_pad, int C, int mode, int NB_cap, int n_sel_max);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 // ---- offload gather -----------------------------------------------------------------

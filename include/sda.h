@@ -141,6 +141,10 @@ sda_status_t sda_score_select_multihead(const void* q, const float* k_tilde, con
  *   split_k    splits per row (0 = chosen by the library)
  * Entries with ids outside [0, nb) or slots outside the buffer are skipped.
  * A row with no valid token gets out = 0 and lse = -inf.
+ * Workspace: sda_sparse_decode_workspace() bytes (0 when one split per row).
+ * It holds per-row arrival counters: zero-fill it before its first use; every
+ * completed call leaves it zero-filled again.  Calls that share a workspace
+ * must not overlap in time.
  */
 size_t sda_sparse_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int split_k);
 sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, const int32_t* seq_len,
@@ -162,7 +166,8 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
  *   block_idx must be ascending per row (as sda_score_select writes it).
  *   union_count_opt i32 [B, ceil(NQ / group_C), H_kv] out or NULL: blocks loaded
  *   per group (size of the merged set, or of the first list in shared mode).
- * Other arguments as sda_sparse_decode.  group_C * G <= 32, group_C <= 8.
+ * Other arguments (workspace contract included) as sda_sparse_decode.
+ * group_C * G <= 32, group_C <= 8.
  */
 size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d,
                                     int group_C, int split_k);

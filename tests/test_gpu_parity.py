@@ -257,3 +257,39 @@ def test_multi_query_plain_decode_each_query_own_list():
         blocks = bi.cpu().numpy()[b, q, g, :ns[b, q, g].item()]
         o, _ = oracle_decode(Qd, rk, b, q, g, cfg.G, blocks, cfg.T, scale_of(cfg))
         assert np.abs(out[b, q, g * cfg.G:(g + 1) * cfg.G].double().cpu().numpy() - o).max() <= TOL
+
+
+def test_graph_replay_matches_eager():
+    # the decode step captured as a HIP graph; every replay, with eager work and
+    # synchronisations in between, reproduces the eager result bit for bit
+    cfg = synth.get_config(1)
+    K, V, _ = inputs.kv_layer(cfg, 0, device=DEV)
+    ktg = gpu_ktilde(K, cfg.T)
+    F = inputs.to_bf16(inputs.indexer_vectors(cfg, 0)).to(DEV)
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0)).to(DEV)
+    s = seq(cfg)
+    sc, (bi, ns) = sda.prepare(sda.sda_score_select, F, ktg, s, 1, 2, 8)
+    dc, (out, lse) = sda.prepare(sda.sda_sparse_decode, Q, K, V, s, bi, ns, split_k=3)
+    sc.run()
+    dc.run()
+    torch.cuda.synchronize()
+    ref_bi, ref_out, ref_lse = bi.clone(), out.clone(), lse.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sc.run()
+        dc.run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sc.run()
+        dc.run()
+    for r in range(4):
+        out.zero_()
+        bi.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bi, ref_bi) and torch.equal(out, ref_out) and torch.equal(lse, ref_lse), r
+        # eager work between replays, on other buffers
+        sda.sda_sparse_decode(Q, K, V, s, ref_bi, ns, split_k=2)
+        torch.cuda.synchronize()
