@@ -129,6 +129,33 @@ def copy_calibration(nbytes=1 << 30):
     print(json.dumps({"copy_bytes": nbytes, "launches": 3}))
 
 
+def timed_graph(step, L, steps):
+    """Capture the L-step layer ring as one HIP graph, replay it for exactly
+    `steps` steps (the remainder eagerly) between synchronisations; returns
+    (wall seconds, steps)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(L):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(L):
+            step(i)
+    torch.cuda.synchronize()
+    replays, rest = divmod(steps, L)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(replays):
+        graph.replay()
+    for i in range(rest):
+        step(i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, steps
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +165,7 @@ def main():
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager prepared calls (for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -203,29 +231,16 @@ def main():
     t_sel = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
     t_dec = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
 
-    # timed region: the layer ring captured once as a HIP graph and replayed
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for i in range(L):
+    if args.no_graph:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
             step(i)
-    torch.cuda.current_stream().wait_stream(side)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(L):
-            step(i)
-    torch.cuda.synchronize()
-    replays, rest = divmod(args.steps, L)
-    graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(replays):
-        graph.replay()
-    for i in range(rest):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    steps_timed = args.steps
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        steps_timed = args.steps
+    else:
+        wall, steps_timed = timed_graph(step, L, args.steps)
 
     queries = cfg.B * cfg.NQ
     value = queries * steps_timed / wall
@@ -261,7 +276,8 @@ def main():
             "seq_len": cfg.T,
             "parallelism": "single GPU",
             "config_id": cfg.cid,
-            "launch": f"HIP graph of the {L}-layer ring (score_select + sparse_decode per layer), replayed",
+            "launch": ("eager prepared calls" if args.no_graph else
+                       f"HIP graph of the {L}-layer ring (score_select + sparse_decode per layer), replayed"),
         },
         "roofline": {
             "bound": "hbm",

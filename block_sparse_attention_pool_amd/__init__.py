@@ -49,7 +49,7 @@ _SIGNATURES = {
     "sda_sparse_decode": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
                                    _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                                    _c_void_p, _c_void_p, _c_int, _c_void_p, _c_size_t, _c_void_p]),
-    "sda_grouped_decode_workspace": (_c_size_t, [_c_int] * 8),
+    "sda_grouped_decode_workspace": (_c_size_t, [_c_int] * 10),
     "sda_grouped_decode": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
                                     _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_size_t,
@@ -297,7 +297,8 @@ def sda_grouped_decode(q, k, v, seq_len, block_idx, n_sel, group_C, mode=SDA_GRO
         lse = torch.empty((B, NQ, H_q), dtype=torch.float32, device=q.device)
     if union_count is None:
         union_count = torch.empty((B, n_groups, H_kv), dtype=torch.int32, device=q.device)
-    nbytes = lib().sda_grouped_decode_workspace(B, NQ, H_q, H_kv, n_sel_max, d, int(group_C), int(split_k))
+    nbytes = lib().sda_grouped_decode_workspace(B, NQ, H_q, H_kv, n_sel_max, d, int(NB_cap), int(group_C),
+                                                int(mode), int(split_k))
     ws, wsb = _workspace(nbytes, q.device, ws)
     _check(lib().sda_grouped_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(block_idx), _ptr(n_sel),
                                     n_sel_max, T_cap, int(NB_cap), B, NQ, H_q, H_kv, d, float(scale),

@@ -38,6 +38,7 @@
 namespace sda {
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4i16;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 #define SDA_LDS __attribute__((address_space(3)))
 
 // token held in QK A-operand row m of m-tile mt
@@ -60,13 +61,14 @@ struct VTile {
     }
 };
 
-template <int D, int NT, int W>
-struct SmemPlan {
-    static constexpr int RP = NT * 16;
-    static constexpr size_t kV = (size_t)W * VTile<D>::kBytes;
-    static constexpr size_t kM = (size_t)W * RP * (D + 2) * sizeof(float);
-    static constexpr size_t kBase = ((kV > kM ? kV : kM) + 15) / 16 * 16;   // union lists start here
-};
+// LDS of a workgroup of W waves: W V tiles, reused for the wave merge; the
+// union lists of the grouped mode follow
+__host__ __device__ inline size_t smem_base(int D, int RP, int W) {
+    const size_t v = (size_t)W * kBlock * D * 2;
+    const size_t m = (size_t)W * RP * (D + 2) * sizeof(float);
+    return ((v > m ? v : m) + 15) / 16 * 16;
+}
+constexpr int kMaxWaves = 10;
 
 // list of blocks a workgroup walks, and which of the group's queries use each
 struct ListView {
@@ -80,7 +82,60 @@ __device__ __forceinline__ void lds_dma16(const void* g, SDA_LDS void* l) {
     __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 }
 
-template <int D, int NT, int W>
+// Merge the n_split partials (m, l, o) of one output row by log-sum-exp: one
+// wave, lane owns columns lane + 64 i.  Partials are read in batches of
+// kCombineMax with every load of a batch in flight at once.  `coherent`
+// reads with agent-scope atomic loads (partials written moments ago by
+// workgroups on other XCDs); the merge launch reads plainly.  Both paths do
+// the same arithmetic in the same order, so they agree bit for bit.
+constexpr int kCombineMax = 8;
+template <int D, bool coherent>
+__device__ __forceinline__ float ld_part(const float* p) {
+    if constexpr (coherent) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+}
+template <int D, int RP, bool coherent>
+__device__ __forceinline__ void merge_row(const AttnArgs& a, int task, int r, size_t oi, int lane) {
+    constexpr int PER = D / kWave;
+    const float* ml = a.part_ml + ((size_t)task * a.n_split * RP + r) * 2;
+    const float* po = a.part_o + ((size_t)task * a.n_split * RP + r) * D + lane;
+    float M = -INFINITY, Ls = 0.f, Os[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) Os[i] = 0.f;
+    for (int s0 = 0; s0 < a.n_split; s0 += kCombineMax) {
+        float mv[kCombineMax], lv[kCombineMax], ov[kCombineMax][PER];
+#pragma unroll
+        for (int k = 0; k < kCombineMax; ++k) {
+            const int s2 = s0 + k;
+            const bool ok = s2 < a.n_split;
+            mv[k] = ok ? ld_part<D, coherent>(ml + (size_t)s2 * RP * 2) : -INFINITY;
+            lv[k] = ok ? ld_part<D, coherent>(ml + (size_t)s2 * RP * 2 + 1) : 0.f;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) ov[k][i] = ok ? ld_part<D, coherent>(po + (size_t)s2 * RP * D + i * kWave) : 0.f;
+        }
+        float Mn = M;
+#pragma unroll
+        for (int k = 0; k < kCombineMax; ++k) Mn = fmaxf(Mn, mv[k]);
+        if (Mn == -INFINITY) continue;
+        const float al = __builtin_amdgcn_exp2f(M - Mn);        // 0 on the first batch
+        Ls *= al;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) Os[i] *= al;
+#pragma unroll
+        for (int k = 0; k < kCombineMax; ++k) {
+            const float sc = __builtin_amdgcn_exp2f(mv[k] - Mn);
+            Ls += lv[k] * sc;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) Os[i] += ov[k][i] * sc;
+        }
+        M = Mn;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) a.out[oi * D + lane + i * kWave] = (Ls > 0.f) ? Os[i] / Ls : 0.f;
+    if (lane == 0 && a.lse) a.lse[oi] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
+}
+
+template <int D, int NT>
 __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, const ListView& L, int b, int g, int q0,
                                                 int Cg, int split, int task, char* smem) {
     constexpr int KS = D / 32;            // QK k-steps
@@ -88,6 +143,7 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, const ListVie
     constexpr int RP = NT * 16;           // padded rows
     const int lane = __lane_id();
     const int wave = threadIdx.x / kWave;
+    const int W = blockDim.x / kWave;     // waves per workgroup (one block each, normally)
     const int li = lane & 15;
     const int lg = lane >> 4;
     const int G = a.G;
@@ -172,6 +228,7 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, const ListVie
         const char* kb = reinterpret_cast<const char*>(kv_k + (size_t)phys * kBlock * D);
         const char* vb = reinterpret_cast<const char*>(kv_v + (size_t)phys * kBlock * D);
         const int tmax = nvalid - 1;
+        const bool full = (nvalid == kBlock) && (memb == 0xffffffffu);   // wave-uniform
 
         // ---- V into LDS by direct loads, then K into registers (MFMA A layout);
         //      everything is in flight before the first wait ----------------------------
@@ -204,56 +261,62 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, const ListVie
                 s[mt][nt] = acc;
             }
 
-        // ---- online softmax per row ---------------------------------------------
+        // ---- online softmax per row (log2 domain; the scale is folded into the exponent)
         u32x4 pf[NT][2], pl[NT][2];
+        const float c = a.scale_log2;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const bool live = rowok[nt] && ((memb >> rowq[nt]) & 1u);
+            if (!full) {
+                const bool live = (memb >> rowq[nt]) & 1u;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!(live && tok_of(mt, lg * 4 + i) < nvalid)) s[mt][nt][i] = -INFINITY;
+            }
             float mx = -INFINITY;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = tok_of(mt, lg * 4 + i);
-                    float x = s[mt][nt][i] * a.scale_log2;
-                    x = (live && t < nvalid) ? x : -INFINITY;
-                    s[mt][nt][i] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = cross4_max(mx);
+                mx = fmaxf(mx, fmaxf(fmaxf(s[mt][nt][0], s[mt][nt][1]), fmaxf(s[mt][nt][2], s[mt][nt][3])));
+            mx = cross4_max(mx) * c;                            // raw max, scaled (c > 0)
             const float m_new = fmaxf(m_run[nt], mx);
             const bool any = m_new != -INFINITY;
             const float m_use = any ? m_new : 0.f;
-            const float alpha = any ? __builtin_amdgcn_exp2f(m_run[nt] - m_use) : 1.f;
             float psum = 0.f;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(s[mt][nt][i] - m_use);   // exp2(-inf) = 0
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[mt][nt][i], c, -m_use));   // exp2(-inf) = 0
                     s[mt][nt][i] = p;
                     psum += p;
                 }
             psum = cross4_sum(psum);
-            l_run[nt] = l_run[nt] * alpha + psum;
-            m_run[nt] = m_new;
+            if (m_run[nt] != -INFINITY) {                       // earlier blocks of this wave: rescale
+                const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
+                l_run[nt] *= alpha;
 #pragma unroll
-            for (int i = 0; i < MTD; ++i) {
-                o[i][nt][0] *= alpha;
-                o[i][nt][1] *= alpha;
-                o[i][nt][2] *= alpha;
-                o[i][nt][3] *= alpha;
+                for (int i = 0; i < MTD; ++i) {
+                    o[i][nt][0] *= alpha;
+                    o[i][nt][1] *= alpha;
+                    o[i][nt][2] *= alpha;
+                    o[i][nt][3] *= alpha;
+                }
             }
-            // P^T B operand for token half kh: slot jj = (mt&1)*4 + i with mt = 2*kh + (jj>>2)
+            l_run[nt] += psum;
+            m_run[nt] = m_new;
+            // P^T B operand for token half kh: slot jj = (mt&1)*4 + i with mt = 2*kh + (jj>>2);
+            // P = hi + lo, both bf16 (hardware round-to-nearest-even packs)
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const float p0 = s[2 * kh + (w >> 1)][nt][(w & 1) * 2];
                     const float p1 = s[2 * kh + (w >> 1)][nt][(w & 1) * 2 + 1];
-                    const uint32_t h0 = f2bf(p0), h1 = f2bf(p1);
-                    pf[nt][kh][w] = h0 | (h1 << 16);
-                    pl[nt][kh][w] = pack_bf16(p0 - __uint_as_float(h0 << 16), p1 - __uint_as_float(h1 << 16));
+                    const bf16x2 h = {(__bf16)p0, (__bf16)p1};
+                    const bf16x2 r = {(__bf16)(p0 - (float)h[0]), (__bf16)(p1 - (float)h[1])};
+                    pf[nt][kh][w] = __builtin_bit_cast(uint32_t, h);
+                    pl[nt][kh][w] = __builtin_bit_cast(uint32_t, r);
                 }
         }
 
@@ -284,6 +347,9 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, const ListVie
     }
 
     // ---- merge the waves of this workgroup through LDS -------------------------------
+    // Each wave publishes (m, l) per row and its o; after one barrier a thread
+    // owns four consecutive columns of one row and reads every wave's values
+    // in one unrolled batch (no dependent LDS round trips).
     __syncthreads();
     float* sm_m = reinterpret_cast<float*>(smem);        // [W][RP]
     float* sm_l = sm_m + W * RP;                          // [W][RP]
@@ -302,68 +368,90 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, const ListVie
     __syncthreads();
 
     const bool final_out = (a.n_split == 1);
-    for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x) {
-        const int r = idx / D, d = idx - (idx / D) * D;
+    constexpr int QPR = D / 4;                            // column quads per row
+    for (int qi = threadIdx.x; qi < R * QPR; qi += blockDim.x) {
+        const int r = qi / QPR, d4 = (qi - r * QPR) * 4;
+        float mw[kMaxWaves], lw[kMaxWaves];
+        floatx4 ow[kMaxWaves];
+#pragma unroll
+        for (int w = 0; w < kMaxWaves; ++w) {
+            if (w < W) {
+                mw[w] = sm_m[w * RP + r];
+                lw[w] = sm_l[w * RP + r];
+                ow[w] = *reinterpret_cast<const floatx4*>(&sm_o[(w * RP + r) * D + d4]);
+            } else {
+                mw[w] = -INFINITY;
+                lw[w] = 0.f;
+                ow[w] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w * RP + r]);
-        float Ls = 0.f, Os = 0.f;
+        for (int w = 0; w < kMaxWaves; ++w) M = fmaxf(M, mw[w]);
+        float Ls = 0.f;
+        floatx4 Os = floatx4{0.f, 0.f, 0.f, 0.f};
         if (M != -INFINITY) {
 #pragma unroll
-            for (int w = 0; w < W; ++w) {
-                const float sc = __builtin_amdgcn_exp2f(sm_m[w * RP + r] - M);
-                Ls += sm_l[w * RP + r] * sc;
-                Os += sm_o[(w * RP + r) * D + d] * sc;
+            for (int w = 0; w < kMaxWaves; ++w) {
+                const float sc = __builtin_amdgcn_exp2f(mw[w] - M);      // 0 for absent waves
+                Ls += lw[w] * sc;
+                Os[0] += ow[w][0] * sc;
+                Os[1] += ow[w][1] * sc;
+                Os[2] += ow[w][2] * sc;
+                Os[3] += ow[w][3] * sc;
             }
         }
         if (final_out) {
             const int c = r / G, h = r - (r / G) * G;
             const size_t oi = ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h;
-            a.out[oi * D + d] = (Ls > 0.f) ? Os / Ls : 0.f;
-            if (d == 0 && a.lse) a.lse[oi] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
+            const float inv = (Ls > 0.f) ? 1.f / Ls : 0.f;
+            *reinterpret_cast<floatx4*>(&a.out[oi * D + d4]) =
+                floatx4{Os[0] * inv, Os[1] * inv, Os[2] * inv, Os[3] * inv};
+            if (d4 == 0 && a.lse) a.lse[oi] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
         } else {
             const size_t pi = ((size_t)task * a.n_split + split) * RP + r;
-            a.part_o[pi * D + d] = Os;
-            if (d == 0) {
-                a.part_ml[pi * 2] = M;
-                a.part_ml[pi * 2 + 1] = Ls;
+            if (a.fused_combine) {        // write-through stores: the merging workgroup may sit on another XCD
+                uint64_t* po = reinterpret_cast<uint64_t*>(&a.part_o[pi * D + d4]);
+                __hip_atomic_store(po, ((uint64_t)__float_as_uint(Os[1]) << 32) | __float_as_uint(Os[0]),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(po + 1, ((uint64_t)__float_as_uint(Os[3]) << 32) | __float_as_uint(Os[2]),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (d4 == 0)
+                    __hip_atomic_store(reinterpret_cast<uint64_t*>(&a.part_ml[pi * 2]),
+                                       ((uint64_t)__float_as_uint(Ls) << 32) | __float_as_uint(M),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                *reinterpret_cast<floatx4*>(&a.part_o[pi * D + d4]) = Os;
+                if (d4 == 0) {
+                    a.part_ml[pi * 2] = M;
+                    a.part_ml[pi * 2 + 1] = Ls;
+                }
             }
         }
     }
     if (final_out || !a.fused_combine) return;
 
-    // ---- the last workgroup of this row merges the splits ------------------------------
+    // ---- the last workgroup of this row group merges the splits ----------------------
+    // This workgroup's partial stores are written through to the coherent level;
+    // once they have completed (vmcnt), one agent-scope counter increment per
+    // workgroup tells the last arrival that every split is readable.
     int* last = reinterpret_cast<int*>(smem);           // the merge area is free again
-    __threadfence();                 // release this split's partials to the other XCDs
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (threadIdx.x == 0) *last = (atomicAdd(&a.counters[task], 1) == a.n_split - 1);
+    if (threadIdx.x == 0)
+        *last = __hip_atomic_fetch_add(&a.counters[task], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                a.n_split - 1;
     __syncthreads();
     if (!*last) return;
-    __threadfence();                 // acquire every split's partials
-    for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x) {
-        const int r = idx / D, d = idx - (idx / D) * D;
-        const float* ml = a.part_ml + ((size_t)task * a.n_split * RP + r) * 2;
-        const float* po = a.part_o + ((size_t)task * a.n_split * RP + r) * D + d;
-        float M = -INFINITY;
-        for (int s2 = 0; s2 < a.n_split; ++s2) M = fmaxf(M, __builtin_nontemporal_load(ml + (size_t)s2 * RP * 2));
-        float Ls = 0.f, Os = 0.f;
-        if (M != -INFINITY) {
-            for (int s2 = 0; s2 < a.n_split; ++s2) {
-                const float sc = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(ml + (size_t)s2 * RP * 2) - M);
-                Ls += __builtin_nontemporal_load(ml + (size_t)s2 * RP * 2 + 1) * sc;
-                Os += __builtin_nontemporal_load(po + (size_t)s2 * RP * D) * sc;
-            }
-        }
+    for (int r = wave; r < R; r += W) {
         const int c = r / G, h = r - (r / G) * G;
-        const size_t oi = ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h;
-        a.out[oi * D + d] = (Ls > 0.f) ? Os / Ls : 0.f;
-        if (d == 0 && a.lse) a.lse[oi] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
+        merge_row<D, RP, true>(a, task, r, ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h, lane);
     }
-    if (threadIdx.x == 0) a.counters[task] = 0;          // ready for the next call
+    if (threadIdx.x == 0) __hip_atomic_store(&a.counters[task], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int NT, int W, int MINB>
-__global__ __launch_bounds__(W * 64, MINB) void attn_kernel(AttnArgs a) {
+template <int D, int NT>
+__global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int task = blockIdx.y;
     const int split = blockIdx.x;
@@ -377,7 +465,7 @@ __global__ __launch_bounds__(W * 64, MINB) void attn_kernel(AttnArgs a) {
     const int nb = (T + kBlock - 1) / kBlock;
 
     ListView L{};
-    char* after_v = smem + SmemPlan<D, NT, W>::kBase;
+    char* after_v = smem + smem_base(D, NT * 16, blockDim.x / kWave);
     const size_t row0 = ((size_t)b * a.NQ + q0) * a.H_kv + g;   // block_idx row of the group's first query
     if (a.C == 1 || a.mode == 1) {
         L.gidx = a.block_idx + row0 * a.n_sel_max;
@@ -444,11 +532,10 @@ __global__ __launch_bounds__(W * 64, MINB) void attn_kernel(AttnArgs a) {
         if (a.union_count && split == 0 && threadIdx.x == 0)
             a.union_count[((size_t)b * a.n_groups + grp) * a.H_kv + g] = L.n;
     }
-    run_tile_engine<D, NT, W>(a, L, b, g, q0, Cg, split, task, smem);
+    run_tile_engine<D, NT>(a, L, b, g, q0, Cg, split, task, smem);
 }
 
-// Split merge as its own launch: one wave per (row group, row); lane s reads
-// split s's (m, l), the wave reduces, then each lane merges D/64 columns.
+// Split merge as its own launch: one wave per (row group, row).
 template <int D, int RP>
 __global__ __launch_bounds__(64) void combine_kernel(AttnArgs a) {
     const int task = blockIdx.x;
@@ -460,31 +547,8 @@ __global__ __launch_bounds__(64) void combine_kernel(AttnArgs a) {
     const int q0 = grp * a.C;
     const int Cg = min(a.C, a.NQ - q0);
     if (r >= Cg * a.G) return;
-    const int lane = threadIdx.x;
-    const float* ml = a.part_ml + ((size_t)task * a.n_split * RP + r) * 2;
-    float M = -INFINITY;
-    for (int s2 = lane; s2 < a.n_split; s2 += kWave) M = fmaxf(M, ml[(size_t)s2 * RP * 2]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
-    constexpr int PER = D / kWave;
-    float Os[PER], Ls = 0.f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) Os[i] = 0.f;
-    if (M != -INFINITY) {
-        const float* po = a.part_o + ((size_t)task * a.n_split * RP + r) * D + lane;
-#pragma unroll 4
-        for (int s2 = 0; s2 < a.n_split; ++s2) {
-            const float sc = __builtin_amdgcn_exp2f(ml[(size_t)s2 * RP * 2] - M);
-            Ls += ml[(size_t)s2 * RP * 2 + 1] * sc;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) Os[i] += po[(size_t)s2 * RP * D + i * kWave] * sc;
-        }
-    }
     const int c = r / a.G, h = r - (r / a.G) * a.G;
-    const size_t oi = ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * a.G + h;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) a.out[oi * D + lane + i * kWave] = (Ls > 0.f) ? Os[i] / Ls : 0.f;
-    if (lane == 0 && a.lse) a.lse[oi] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
+    merge_row<D, RP, false>(a, task, r, ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * a.G + h, threadIdx.x);
 }
 
 static int env_int(const char* name, int dflt) {
@@ -494,17 +558,54 @@ static int env_int(const char* name, int dflt) {
 
 int attn_rows_pad(int C, int G) { return (C * G <= 16) ? 16 : 32; }
 
-// workgroup size (waves) of the main decode variant; SDA_ATTN_WAVES overrides (2, 4, 5)
-int attn_waves(int d, int rows_pad) {
-    if (d == 128 && rows_pad == 16) {
-        static const int w = env_int("SDA_ATTN_WAVES", 4);
-        return (w == 2 || w == 5) ? w : 4;
-    }
-    return 4;
+constexpr int kCUs = 256;                  // MI355X compute units
+constexpr size_t kLdsPerCU = 160 * 1024;
+
+static size_t union_extra(int C, int mode, int NB_cap, int n_sel_max, int W) {
+    if (C <= 1 || mode != 0) return 0;
+    return (size_t)C * ((NB_cap + 31) / 32) * 4 + (size_t)C * n_sel_max * 8 + ((size_t)W * 64 + 1) * 4;
 }
 
-int attn_default_splits(int list_max, int waves) {
-    return (list_max + waves - 1) / waves;      // about one block per wave
+// Launch shape of the attention kernel: W waves per workgroup, n_split
+// workgroups per row group.  Each wave owns one block of its split, so
+// W = ceil(list / n_split); among the shapes whose workgroups fit the LDS,
+// keep those that need the fewest dispatch rounds, prefer ones that give
+// every CU a workgroup, then the fewest splits (less partial traffic).
+AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode, int NB_cap, int n_sel_max,
+                   int split_k) {
+    const int max_w = rows_pad == 16 ? kMaxWaves : 4;
+    const int slots = rows_pad == 16 ? 12 : 4;          // resident waves per CU (VGPR-bound)
+    AttnPlan best{1, 1};
+    long long best_rounds = -1;
+    bool best_full = false;
+    auto consider = [&](int ns, int W) {
+        const size_t lds = smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W);
+        if (lds > kLdsPerCU) return;
+        int per_cu = (int)(kLdsPerCU / lds);
+        if (per_cu * W > slots) per_cu = slots / W;
+        if (per_cu < 1) per_cu = 1;
+        const long long wgs = (long long)tasks * ns;
+        const long long rounds = (wgs + (long long)kCUs * per_cu - 1) / ((long long)kCUs * per_cu);
+        const bool full = wgs >= kCUs;
+        if (best_rounds < 0 || rounds < best_rounds || (rounds == best_rounds && full && !best_full)) {
+            best = AttnPlan{W, ns};
+            best_rounds = rounds;
+            best_full = full;
+        }
+    };
+    if (split_k > 0) {
+        int W = (list_max + split_k - 1) / split_k;
+        if (W > max_w) W = max_w;
+        if (W < 1) W = 1;
+        return AttnPlan{W, split_k};
+    }
+    static const int force_w = env_int("SDA_ATTN_WAVES", 0);
+    for (int ns = 1; ns <= list_max; ++ns) {
+        const int W = (list_max + ns - 1) / ns;
+        if (W > max_w || (force_w && W != force_w)) continue;
+        consider(ns, W);
+    }
+    return best;
 }
 
 size_t attn_ws_bytes(int tasks, int n_split, int rows_pad, int d) {
@@ -513,39 +614,23 @@ size_t attn_ws_bytes(int tasks, int n_split, int rows_pad, int d) {
     return counters + (size_t)tasks * n_split * rows_pad * ((size_t)d + 2) * sizeof(float);
 }
 
-template <int D, int NT, int W>
-static size_t attn_smem_bytes(const AttnArgs& a) {
-    size_t extra = 0;
-    if (a.C > 1 && a.mode == 0) {
-        const size_t words = (size_t)(a.NB_cap + 31) / 32;
-        extra = (size_t)a.C * words * 4 + (size_t)a.C * a.n_sel_max * 8 + ((size_t)W * 64 + 1) * 4;
-    }
-    return SmemPlan<D, NT, W>::kBase + extra;
+size_t attn_smem_bytes_host(int d, int rows_pad, int W, int C, int mode, int NB_cap, int n_sel_max) {
+    return smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W);
 }
 
-size_t attn_smem_bytes_host(int d, int rows_pad, int C, int mode, int NB_cap, int n_sel_max) {
-    const int W = attn_waves(d, rows_pad);
-    const size_t vb = (size_t)W * kBlock * d * 2;
-    const size_t mb = (size_t)W * rows_pad * (d + 2) * 4;
-    size_t base = ((vb > mb ? vb : mb) + 15) / 16 * 16;
-    if (C > 1 && mode == 0)
-        base += (size_t)C * ((NB_cap + 31) / 32) * 4 + (size_t)C * n_sel_max * 8 + ((size_t)W * 64 + 1) * 4;
-    return base;
-}
-
-template <int D, int NT, int W, int MINB>
+template <int D, int NT>
 static hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     const int tasks = a.B * a.n_groups * a.H_kv;
-    const size_t smem = attn_smem_bytes<D, NT, W>(a);
-    auto kern = attn_kernel<D, NT, W, MINB>;
-    static size_t smem_set = 32 * 1024;      // dynamic LDS limit already granted to this variant
-    if (smem > smem_set) {
+    const size_t smem = attn_smem_bytes_host(D, NT * 16, a.waves, a.C, a.mode, a.NB_cap, a.n_sel_max);
+    auto kern = attn_kernel<D, NT>;
+    static bool lds_granted = false;
+    if (!lds_granted) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCU);
         if (e != hipSuccess) return e;
-        smem_set = 160 * 1024;
+        lds_granted = true;
     }
-    hipLaunchKernelGGL(kern, dim3(a.n_split, tasks), dim3(W * 64), smem, s, a);
+    hipLaunchKernelGGL(kern, dim3(a.n_split, tasks), dim3(a.waves * kWave), smem, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1 || a.fused_combine) return e;
     hipLaunchKernelGGL((combine_kernel<D, NT * 16>), dim3(tasks, NT * 16), dim3(64), 0, s, a);
@@ -553,22 +638,11 @@ static hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attention(const AttnArgs& a0, hipStream_t s) {
-    static const int fused = env_int("SDA_ATTN_FUSED_COMBINE", 0);
     AttnArgs a = a0;
-    a.fused_combine = fused;
+    a.fused_combine = env_int("SDA_ATTN_FUSED_COMBINE", 1);   // 0: merge splits in a second launch
     const int rp = attn_rows_pad(a.C, a.G);
-    if (a.d == 128) {
-        if (rp == 16) {
-            switch (attn_waves(128, 16)) {
-                case 2: return launch_t<128, 1, 2, 3>(a, s);
-                case 4: return launch_t<128, 1, 4, 3>(a, s);
-                default: return launch_t<128, 1, 5, 3>(a, s);
-            }
-        }
-        return launch_t<128, 2, 4, 1>(a, s);
-    }
-    if (rp == 16) return launch_t<64, 1, 4, 2>(a, s);
-    return launch_t<64, 2, 4, 1>(a, s);
+    if (a.d == 128) return rp == 16 ? launch_t<128, 1>(a, s) : launch_t<128, 2>(a, s);
+    return rp == 16 ? launch_t<64, 1>(a, s) : launch_t<64, 2>(a, s);
 }
 
 }  // namespace sda

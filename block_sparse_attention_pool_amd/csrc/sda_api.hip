@@ -61,11 +61,12 @@ sda_status_t check_heads(int H_q, int H_kv) {
     return SDA_OK;
 }
 
-int decode_splits(int split_k, int list_max, int d, int rows_pad) {
-    int s = split_k > 0 ? split_k : attn_default_splits(list_max, attn_waves(d, rows_pad));
-    if (s < 1) s = 1;
-    if (s > kMaxSplits) s = kMaxSplits;
-    return s;
+// list length the grouped kernel plans for: the whole first list in shared
+// mode; in exact mode the merged size at half overlap between neighbours,
+// n (1 + (C-1)/2), a middle estimate (the real union is only known on the GPU)
+int grouped_list_estimate(int C, int mode, int n_sel_max) {
+    if (C <= 1 || mode == SDA_GROUP_SHARED_REP) return n_sel_max;
+    return n_sel_max + (C - 1) * n_sel_max / 2;
 }
 
 // workspace of the split decode: [counters, 256-byte padded][(m, l) partials][o partials]
@@ -221,8 +222,9 @@ size_t sda_sparse_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_m
     if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || H_q % H_kv) return 0;
     const int G = H_q / H_kv;
     const int rp = attn_rows_pad(1, G);
-    const int ns = decode_splits(split_k, n_sel_max, d, rp);
-    return attn_ws_bytes(B * NQ * H_kv, ns, rp, d);
+    const int tasks = B * NQ * H_kv;
+    const AttnPlan p = attn_plan(d, rp, tasks, n_sel_max, 1, SDA_GROUP_EXACT, 1, n_sel_max, split_k);
+    return attn_ws_bytes(tasks, p.n_split, rp, d);
 }
 
 static sda_status_t check_attn_common(const void* q, const void* k, const void* v, const int32_t* seq_len,
@@ -255,7 +257,8 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
     REQUIRE(!slot_opt || aligned4(slot_opt), SDA_ERR_ALIGN, "slot_opt must be 4-byte aligned");
     const int G = H_q / H_kv;
     const int rp = attn_rows_pad(1, G);
-    const int ns = decode_splits(split_k, n_sel_max, d, rp);
+    const AttnPlan plan = attn_plan(d, rp, (int)tasks, n_sel_max, 1, SDA_GROUP_EXACT, 1, n_sel_max, split_k);
+    const int ns = plan.n_split;
     const size_t need = attn_ws_bytes((int)tasks, ns, rp, d);
     REQUIRE(need == 0 || (ws && ws_bytes >= need), SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
             ws ? ws_bytes : 0, need);
@@ -285,18 +288,22 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
     a.mode = SDA_GROUP_EXACT;
     a.n_groups = NQ;
     a.n_split = ns;
+    a.waves = plan.waves;
     a.scale_log2 = scale * 1.4426950408889634f;
     return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)), "sparse_decode launch");
 }
 
-size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int group_C,
-                                    int split_k) {
-    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || group_C < 1 || H_q % H_kv) return 0;
+size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap,
+                                    int group_C, int mode, int split_k) {
+    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || group_C < 1 || H_q % H_kv || NB_cap < 1)
+        return 0;
     const int G = H_q / H_kv;
     const int n_groups = ceil_div(NQ, group_C);
     const int rp = attn_rows_pad(group_C, G);
-    const int ns = decode_splits(split_k, group_C * n_sel_max, d, rp);
-    return attn_ws_bytes(B * n_groups * H_kv, ns, rp, d);
+    const int tasks = B * n_groups * H_kv;
+    const AttnPlan p = attn_plan(d, rp, tasks, grouped_list_estimate(group_C, mode, n_sel_max), group_C, mode,
+                                 NB_cap, n_sel_max, split_k);
+    return attn_ws_bytes(tasks, p.n_split, rp, d);
 }
 
 sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, const int32_t* seq_len,
@@ -317,15 +324,14 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
     const long long tasks = (long long)B * n_groups * H_kv;
     REQUIRE(tasks <= kMaxGridYZ, SDA_ERR_SHAPE, "B*groups*H_kv=%lld exceeds %d", tasks, kMaxGridYZ);
     const int rp = attn_rows_pad(group_C, G);
-    const size_t lds = attn_smem_bytes_host(d, rp, group_C, mode, NB_cap, n_sel_max);
+    const AttnPlan plan = attn_plan(d, rp, (int)tasks, grouped_list_estimate(group_C, mode, n_sel_max), group_C,
+                                    mode, NB_cap, n_sel_max, split_k);
+    const size_t lds = attn_smem_bytes_host(d, rp, plan.waves, group_C, mode, NB_cap, n_sel_max);
     REQUIRE(lds <= kLdsBytes, SDA_ERR_UNSUPPORTED, "group needs %zu bytes of LDS", lds);
-    const int list_max = (mode == SDA_GROUP_EXACT) ? group_C * n_sel_max : n_sel_max;
-    const int ns = decode_splits(split_k, list_max, d, rp);
-    const int ns_ws = decode_splits(split_k, group_C * n_sel_max, d, rp);
+    const int ns = plan.n_split;
     const size_t need = attn_ws_bytes((int)tasks, ns, rp, d);
-    const size_t need_doc = attn_ws_bytes((int)tasks, ns_ws, rp, d);
     REQUIRE(need == 0 || (ws && ws_bytes >= need), SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
-            ws ? ws_bytes : 0, need_doc);
+            ws ? ws_bytes : 0, need);
     REQUIRE(need == 0 || aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
     AttnArgs a{};
     a.q = static_cast<const uint16_t*>(q);
@@ -352,6 +358,7 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
     a.mode = mode;
     a.n_groups = n_groups;
     a.n_split = ns;
+    a.waves = plan.waves;
     a.scale_log2 = scale * 1.4426950408889634f;
     return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)), "grouped_decode launch");
 }

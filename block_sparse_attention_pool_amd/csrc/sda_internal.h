@@ -52,14 +52,19 @@ struct AttnArgs {
     int mode;                 // 0 exact, 1 shared representative
     int n_groups;             // ceil(NQ / C)
     int n_split;
+    int waves;                // waves per workgroup
     int fused_combine;        // 1: the last split's workgroup merges; 0: separate merge launch
     float scale_log2;         // scale * log2(e)
 };
+struct AttnPlan {
+    int waves;                // waves per workgroup
+    int n_split;              // workgroups per row group
+};
 int attn_rows_pad(int C, int G);                 // 16 or 32
-int attn_waves(int d, int rows_pad);             // waves per workgroup
-int attn_default_splits(int list_max, int waves);
+AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode, int NB_cap, int n_sel_max,
+                   int split_k);
 size_t attn_ws_bytes(int tasks, int n_split, int rows_pad, int d);
-size_t attn_smem_bytes_host(int d, int rows_pad, int C, int mode, int NB_cap, int n_sel_max);
+size_t attn_smem_bytes_host(int d, int rows_pad, int W, int C, int mode, int NB_cap, int n_sel_max);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 // ---- offload gather -----------------------------------------------------------------

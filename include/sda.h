@@ -169,8 +169,8 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
  * Other arguments (workspace contract included) as sda_sparse_decode.
  * group_C * G <= 32, group_C <= 8.
  */
-size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d,
-                                    int group_C, int split_k);
+size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap,
+                                    int group_C, int mode, int split_k);
 sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, const int32_t* seq_len,
                                 const int32_t* block_idx, const int32_t* n_sel, int n_sel_max,
                                 int T_cap, int NB_cap, int B, int NQ, int H_q, int H_kv, int d,

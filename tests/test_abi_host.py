@@ -63,7 +63,8 @@ def test_workspace_sizes(L):
     assert n in {dec(64, s) for s in range(2, 36)}
     assert L.sda_sparse_decode_workspace(8, 1, 64, 8, 35, 128, 7) == dec(64, 7)
     assert L.sda_sparse_decode_workspace(8, 1, 64, 8, 35, 128, 1) == 0
-    assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 4, 3) == dec(4 * 4 * 8, 3)
+    assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 1024, 4, 0, 3) == dec(4 * 4 * 8, 3)
+    assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 0, 4, 0, 3) == 0      # NB_cap < 1
 
 
 def _last():

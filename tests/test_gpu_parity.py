@@ -293,3 +293,31 @@ def test_graph_replay_matches_eager():
         # eager work between replays, on other buffers
         sda.sda_sparse_decode(Q, K, V, s, ref_bi, ns, split_k=2)
         torch.cuda.synchronize()
+
+
+def test_fused_split_merge_matches_merge_launch():
+    # the last-arriving workgroup's merge and the separate merge launch do the
+    # same arithmetic: identical bits, call after call (counters reset each time)
+    import os
+    cfg = synth.get_config(2)
+    K, V, _ = inputs.kv_layer(cfg, 0, device=DEV)
+    ktg = gpu_ktilde(K, cfg.T)
+    F = inputs.to_bf16(inputs.indexer_vectors(cfg, 0)).to(DEV)
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0)).to(DEV)
+    bi, ns = sda.sda_score_select(F, ktg, seq(cfg), cfg.n_init, cfg.n_local, cfg.top_k)
+    old = os.environ.get("SDA_ATTN_FUSED_COMBINE")
+    try:
+        os.environ["SDA_ATTN_FUSED_COMBINE"] = "0"
+        ref, lref = sda.sda_sparse_decode(Q, K, V, seq(cfg), bi, ns)
+        os.environ["SDA_ATTN_FUSED_COMBINE"] = "1"
+        ws = torch.zeros(sda.lib().sda_sparse_decode_workspace(cfg.B, 1, cfg.H_q, cfg.H_kv, bi.shape[-1], cfg.d, 0),
+                         dtype=torch.uint8, device=DEV)
+        for it in range(20):
+            out, lse = sda.sda_sparse_decode(Q, K, V, seq(cfg), bi, ns, ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref) and torch.equal(lse, lref), it
+    finally:
+        if old is None:
+            os.environ.pop("SDA_ATTN_FUSED_COMBINE", None)
+        else:
+            os.environ["SDA_ATTN_FUSED_COMBINE"] = old
