@@ -133,12 +133,12 @@ def timed_graph(step, L, steps):
     """Capture the L-step layer ring as one HIP graph, replay it for exactly
     `steps` steps (the remainder eagerly) between synchronisations; returns
     (wall seconds, steps)."""
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
+    warm = torch.cuda.Stream()
+    warm.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(warm):
         for i in range(L):
             step(i)
-    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.current_stream().wait_stream(warm)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for i in range(L):
@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager prepared calls (for counter runs)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run layer l+1's selection on a side stream beside layer l's decode "
+                         "(slower on this GPU: the two kernels contend for the same bandwidth and CUs)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -218,7 +221,22 @@ def main():
         if ev is not None:
             ev[2].record()
 
-    for i in range(args.warmup):
+    # The selection for layer i+1 needs only layer i's indexer vectors and layer
+    # i+1's compressed keys, so it runs on a side stream beside layer i's decode
+    # (the lookahead overlap); the step joins both before layer i+1.
+    side = torch.cuda.Stream()
+
+    def pipelined_step(i):
+        sc = calls[(i + 1) % L][0]
+        dc = calls[i % L][1]
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            sc.run()
+        dc.run()
+        main.wait_stream(side)
+
+    for i in range(max(args.warmup, L)):
         step(i)
     torch.cuda.synchronize()
 
@@ -231,16 +249,17 @@ def main():
     t_sel = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
     t_dec = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
 
+    run_step = pipelined_step if args.overlap else step
     if args.no_graph:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(i)
+            run_step(i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         steps_timed = args.steps
     else:
-        wall, steps_timed = timed_graph(step, L, args.steps)
+        wall, steps_timed = timed_graph(run_step, L, args.steps)
 
     queries = cfg.B * cfg.NQ
     value = queries * steps_timed / wall
@@ -276,8 +295,9 @@ def main():
             "seq_len": cfg.T,
             "parallelism": "single GPU",
             "config_id": cfg.cid,
-            "launch": ("eager prepared calls" if args.no_graph else
-                       f"HIP graph of the {L}-layer ring (score_select + sparse_decode per layer), replayed"),
+            "launch": ("eager prepared calls" if args.no_graph else f"HIP graph of the {L}-layer ring, replayed")
+                      + (", layer l+1's score_select beside layer l's sparse_decode (two streams)"
+                         if args.overlap else ", score_select then sparse_decode per layer"),
         },
         "roofline": {
             "bound": "hbm",

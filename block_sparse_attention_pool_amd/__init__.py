@@ -200,10 +200,7 @@ def sda_score_select(f, k_tilde, seq_len, n_init, n_local, top_k, n_sel_max=None
     _need(n_sel, "n_sel", torch.int32, 3)
     if scores is not None:
         _need(scores, "scores", torch.float32, 4)
-        nbytes = 0
-    else:
-        nbytes = lib().sda_score_select_workspace(B, NQ, H, NB_cap, top_k)
-    ws, wsb = _workspace(nbytes, f.device, ws)
+    ws, wsb = _workspace(lib().sda_score_select_workspace(B, NQ, H, NB_cap, top_k), f.device, ws)
     args = (_ptr(f), _ptr(k_tilde), _ptr(seq_len), B, NQ, H, d, NB_cap, n_init, n_local,
             top_k, n_sel_max, _ptr(block_idx), _ptr(n_sel), _ptr(scores), _ptr(ws), wsb, None)
     if _prepare:

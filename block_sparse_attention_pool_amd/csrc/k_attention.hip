@@ -551,7 +551,7 @@ __global__ __launch_bounds__(64) void combine_kernel(AttnArgs a) {
     merge_row<D, RP, false>(a, task, r, ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * a.G + h, threadIdx.x);
 }
 
-static int env_int(const char* name, int dflt) {
+int env_int(const char* name, int dflt) {
     const char* v = getenv(name);
     return v ? atoi(v) : dflt;
 }

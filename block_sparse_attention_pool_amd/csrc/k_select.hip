@@ -26,112 +26,6 @@ constexpr int kChunk = 256;          // blocks per scoring workgroup
 
 int score_chunks(int NB_cap) { return (NB_cap + kChunk - 1) / kChunk; }
 
-// vectors: [B, NQ, H_vec, D] bf16; K~ row (b, g) is scored by vectors
-// (q, hv) with hv in [g*VPR, (g+1)*VPR).  out[((b*NQ + q)*H_vec + hv)*NB_cap + j].
-template <int D, int NV>
-__global__ __launch_bounds__(256) void score_kernel(const uint16_t* __restrict__ vec,
-                                                    const float* __restrict__ kt,
-                                                    const int32_t* __restrict__ seq_len, int NQ,
-                                                    int H_kv, int VPR, int NB_cap, float mult,
-                                                    float* __restrict__ out) {
-    constexpr int HALVES = D / 64;          // 16-byte loads per lane per block
-    const int row = blockIdx.y;             // b * H_kv + g
-    const int b = row / H_kv, g = row - (row / H_kv) * H_kv;
-    const int nb = min((seq_len[b] + kBlock - 1) / kBlock, NB_cap);
-    const int j0 = blockIdx.x * kChunk;
-    if (j0 >= nb) return;
-    const int H_vec = H_kv * VPR;
-    const int nvec = NQ * VPR;
-    const int v0 = blockIdx.z * NV;
-    const int lane = __lane_id();
-    const int li = lane & 15;
-    const int wave = threadIdx.x / kWave;
-
-    // this lane's slice of each vector: dims 4*li..+4 and 64+4*li..+4
-    float fv[NV][HALVES * 4];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const int vi = v0 + v;
-        const int q = vi / VPR, hv = g * VPR + (vi - (vi / VPR) * VPR);
-        if (vi < nvec) {
-            const uint16_t* p = vec + (((size_t)b * NQ + q) * H_vec + hv) * D;
-#pragma unroll
-            for (int h = 0; h < HALVES; ++h) {
-                const uint2 w = *reinterpret_cast<const uint2*>(p + h * 64 + li * 4);
-                fv[v][h * 4 + 0] = bf16lo(w.x);
-                fv[v][h * 4 + 1] = bf16hi(w.x);
-                fv[v][h * 4 + 2] = bf16lo(w.y);
-                fv[v][h * 4 + 3] = bf16hi(w.y);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < HALVES * 4; ++i) fv[v][i] = 0.f;
-        }
-    }
-
-    const float* ktr = kt + (size_t)row * NB_cap * D;
-    constexpr int UNR = 4;                       // steps in flight
-    constexpr int STEPS = kChunk / 16;           // 16 blocks per workgroup step
-    for (int s0 = 0; s0 < STEPS; s0 += UNR) {
-        floatx4 kv[UNR][HALVES];
-        int jj[UNR];
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            jj[u] = j0 + (s0 + u) * 16 + wave * 4 + (lane >> 4);
-            const bool ok = jj[u] < nb;
-#pragma unroll
-            for (int h = 0; h < HALVES; ++h) {
-                if (ok) kv[u][h] = __builtin_nontemporal_load(
-                            reinterpret_cast<const floatx4*>(ktr + (size_t)jj[u] * D + h * 64 + li * 4));
-                else kv[u][h] = floatx4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                float acc = 0.f;
-#pragma unroll
-                for (int h = 0; h < HALVES; ++h) {
-                    acc = fmaf(fv[v][h * 4 + 0], kv[u][h][0], acc);
-                    acc = fmaf(fv[v][h * 4 + 1], kv[u][h][1], acc);
-                    acc = fmaf(fv[v][h * 4 + 2], kv[u][h][2], acc);
-                    acc = fmaf(fv[v][h * 4 + 3], kv[u][h][3], acc);
-                }
-                acc = row16_sum(acc);
-                const int vi = v0 + v;
-                if (li == 0 && jj[u] < nb && vi < nvec) {
-                    const int q = vi / VPR, hv = g * VPR + (vi - (vi / VPR) * VPR);
-                    out[(((size_t)b * NQ + q) * H_vec + hv) * NB_cap + jj[u]] = acc * mult;
-                }
-            }
-        }
-    }
-}
-
-template <int D>
-static void launch_score_d(const uint16_t* vec, const float* kt, const int32_t* seq_len, int B, int NQ,
-                           int H_kv, int VPR, int NB_cap, float mult, float* out, hipStream_t s) {
-    const int nvec = NQ * VPR;
-    int nv = 1;
-    while (nv < nvec && nv < 16) nv *= 2;
-    dim3 grid(score_chunks(NB_cap), B * H_kv, (nvec + nv - 1) / nv);
-    switch (nv) {
-        case 1: hipLaunchKernelGGL((score_kernel<D, 1>), grid, dim3(256), 0, s, vec, kt, seq_len, NQ, H_kv, VPR, NB_cap, mult, out); break;
-        case 2: hipLaunchKernelGGL((score_kernel<D, 2>), grid, dim3(256), 0, s, vec, kt, seq_len, NQ, H_kv, VPR, NB_cap, mult, out); break;
-        case 4: hipLaunchKernelGGL((score_kernel<D, 4>), grid, dim3(256), 0, s, vec, kt, seq_len, NQ, H_kv, VPR, NB_cap, mult, out); break;
-        case 8: hipLaunchKernelGGL((score_kernel<D, 8>), grid, dim3(256), 0, s, vec, kt, seq_len, NQ, H_kv, VPR, NB_cap, mult, out); break;
-        default: hipLaunchKernelGGL((score_kernel<D, 16>), grid, dim3(256), 0, s, vec, kt, seq_len, NQ, H_kv, VPR, NB_cap, mult, out); break;
-    }
-}
-
-hipError_t launch_scores(const uint16_t* f, const float* kt, const int32_t* seq_len, int B, int NQ,
-                         int H_kv, int d, int NB_cap, float* scores, hipStream_t s) {
-    if (d == 128) launch_score_d<128>(f, kt, seq_len, B, NQ, H_kv, 1, NB_cap, 1.f, scores, s);
-    else launch_score_d<64>(f, kt, seq_len, B, NQ, H_kv, 1, NB_cap, 1.f, scores, s);
-    return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // block-wide helpers (256 threads)
 // ---------------------------------------------------------------------------
@@ -177,12 +71,13 @@ __device__ __forceinline__ float block_reduce_sum(float v, float* sh) {
 // ---------------------------------------------------------------------------
 // exact top-k + block set, one workgroup per row
 // ---------------------------------------------------------------------------
+// Exact top-k and block set of one row by one 256-lane workgroup.
 template <int EPT>
-__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
+__device__ __forceinline__ void select_row(const SelectArgs& a, int row) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t scan_sh[4];
     __shared__ uint32_t sh_digit, sh_gt;
-    const int row = blockIdx.x;                         // (b*NQ + q)*H_kv + g
+    __shared__ uint32_t total;
     const int b = row / (a.NQ * a.H_kv);
     const int tid = threadIdx.x;
     const int nb = min((a.seq_len[b] + kBlock - 1) / kBlock, a.NB_cap);
@@ -199,7 +94,9 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     for (int i = 0; i < EPT; ++i) {
         const int j = base + i;
         const bool c = (j >= lo && j < hi);
-        key[i] = c ? float_key(s[j]) : 0u;
+        float sv = 0.f;
+        if (c) sv = s[j];
+        key[i] = c ? float_key(sv) : 0u;
         cand |= (uint64_t)c << i;
     }
 
@@ -273,12 +170,17 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
             if (pos < (uint32_t)a.n_sel_max) out[pos] = base + i;
             ++pos;
         }
-    __shared__ uint32_t total;
     if (tid == 255) total = incl;
     __syncthreads();
     const int tot = (int)min(total, (uint32_t)a.n_sel_max);
     for (int p = tot + tid; p < a.n_sel_max; p += 256) out[p] = -1;
     if (tid == 0) a.n_sel[row] = tot;
+    __syncthreads();                        // the shared state may be reused by another row
+}
+
+template <int EPT>
+__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
+    select_row<EPT>(a, blockIdx.x);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
@@ -292,6 +194,257 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
     else if (ept <= 32) hipLaunchKernelGGL(select_kernel<32>, grid, block, 0, s, a);
     else hipLaunchKernelGGL(select_kernel<64>, grid, block, 0, s, a);
     return hipGetLastError();
+}
+
+// vectors: [B, NQ, H_vec, D] bf16; K~ row (b, g) is scored by vectors
+// (q, hv) with hv in [g*VPR, (g+1)*VPR).  out[((b*NQ + q)*H_vec + hv)*NB_cap + j]
+// (out may be NULL when FUSED).
+//
+// FUSED (one vector per query, VPR = 1): the selection runs in the same launch
+// in two levels.  Each chunk workgroup ranks its 256 candidate blocks by the
+// key (score, then lower block index) and writes its best top_k keys, in rank
+// order, to `cand` with write-through stores.  Every chunk workgroup of a
+// (kv row, vector tile) then bumps an agent-scope arrival counter; the last
+// one merges the per-chunk sorted lists (a key's global rank is its rank in
+// its own list plus the number of larger keys in every other list) and writes
+// the block set.  Each block lives in exactly one chunk and a global top-k
+// block is within its chunk's top-k, so the merge is exact.
+struct ScoreArgs {
+    const uint16_t* vec;
+    const float* kt;
+    const int32_t* seq_len;
+    float* out;
+    int NQ, H_kv, VPR, NB_cap;
+    float mult;
+    SelectArgs sel;          // FUSED only
+    uint64_t* cand;          // FUSED: [B*NQ*H_kv, chunks, top_k] keys
+    int* counters;           // FUSED: [B*H_kv*vector tiles], zero between calls
+};
+
+constexpr int kFusedTopK = 64;       // longest per-chunk list the fused selection keeps
+constexpr int kFusedChunks = 16;     // most chunks it merges (NB_cap <= 4096)
+
+// ordered 64-bit key: larger score first, then lower block index; 0 = no block
+__device__ __forceinline__ uint64_t block_key(float s, int j) {
+    return ((uint64_t)float_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+
+// number of keys in the descending list L[0..n) that are larger than x
+__device__ __forceinline__ int count_larger(const uint64_t* L, int n, uint64_t x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (L[mid] > x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+template <int D, int NV, bool FUSED>
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+    constexpr int HALVES = D / 64;          // 16-byte loads per lane per block
+    const int row = blockIdx.y;             // b * H_kv + g
+    const int b = row / a.H_kv, g = row - (row / a.H_kv) * a.H_kv;
+    const int nb = min((a.seq_len[b] + kBlock - 1) / kBlock, a.NB_cap);
+    const int j0 = blockIdx.x * kChunk;
+    const int H_vec = a.H_kv * a.VPR;
+    const int nvec = a.NQ * a.VPR;
+    const int v0 = blockIdx.z * NV;
+    const int lane = __lane_id();
+    const int li = lane & 15;
+    const int wave = threadIdx.x / kWave;
+    __shared__ float sc[FUSED ? NV : 1][FUSED ? kChunk : 1];
+
+    if (j0 < nb) {
+        // this lane's slice of each vector: dims 4*li..+4 and 64+4*li..+4
+        float fv[NV][HALVES * 4];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int vi = v0 + v;
+            const int q = vi / a.VPR, hv = g * a.VPR + (vi - (vi / a.VPR) * a.VPR);
+            if (vi < nvec) {
+                const uint16_t* p = a.vec + (((size_t)b * a.NQ + q) * H_vec + hv) * D;
+#pragma unroll
+                for (int h = 0; h < HALVES; ++h) {
+                    const uint2 w = *reinterpret_cast<const uint2*>(p + h * 64 + li * 4);
+                    fv[v][h * 4 + 0] = bf16lo(w.x);
+                    fv[v][h * 4 + 1] = bf16hi(w.x);
+                    fv[v][h * 4 + 2] = bf16lo(w.y);
+                    fv[v][h * 4 + 3] = bf16hi(w.y);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < HALVES * 4; ++i) fv[v][i] = 0.f;
+            }
+        }
+
+        const float* ktr = a.kt + (size_t)row * a.NB_cap * D;
+        constexpr int UNR = 4;                       // steps in flight
+        constexpr int STEPS = kChunk / 16;           // 16 blocks per workgroup step
+        for (int s0 = 0; s0 < STEPS; s0 += UNR) {
+            floatx4 kv[UNR][HALVES];
+            int jj[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                jj[u] = j0 + (s0 + u) * 16 + wave * 4 + (lane >> 4);
+                const bool ok = jj[u] < nb;
+#pragma unroll
+                for (int h = 0; h < HALVES; ++h) {
+                    if (ok) kv[u][h] = __builtin_nontemporal_load(
+                                reinterpret_cast<const floatx4*>(ktr + (size_t)jj[u] * D + h * 64 + li * 4));
+                    else kv[u][h] = floatx4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int h = 0; h < HALVES; ++h) {
+                        acc = fmaf(fv[v][h * 4 + 0], kv[u][h][0], acc);
+                        acc = fmaf(fv[v][h * 4 + 1], kv[u][h][1], acc);
+                        acc = fmaf(fv[v][h * 4 + 2], kv[u][h][2], acc);
+                        acc = fmaf(fv[v][h * 4 + 3], kv[u][h][3], acc);
+                    }
+                    acc = row16_sum(acc) * a.mult;
+                    const int vi = v0 + v;
+                    if (li == 0 && jj[u] < nb && vi < nvec) {
+                        if constexpr (FUSED) sc[v][jj[u] - j0] = acc;
+                        if (!FUSED || a.out) {
+                            const int q = vi / a.VPR, hv = g * a.VPR + (vi - (vi / a.VPR) * a.VPR);
+                            a.out[(((size_t)b * a.NQ + q) * H_vec + hv) * a.NB_cap + jj[u]] = acc;
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    if constexpr (FUSED) {
+        __shared__ uint64_t keys[kChunk];
+        __shared__ uint64_t lists[kFusedTopK * kFusedChunks];
+        __shared__ int sel_j[kFusedTopK];
+        __shared__ int last;
+        const SelectArgs& s = a.sel;
+        const int K = s.top_k;
+        const int nch = gridDim.x;
+        const int tid = threadIdx.x;
+        const int lo = min(s.n_init, nb);                 // candidates are [lo, hi)
+        const int hi = max(lo, nb - s.n_local);
+        __syncthreads();                                   // sc complete
+
+        // level 1: this chunk's best K candidates, in rank order
+        const int j = j0 + tid;
+        const bool valid = j >= lo && j < hi;
+        const int nvalid = max(0, min(j0 + kChunk, hi) - max(j0, lo));
+        for (int v = 0; v < NV; ++v) {
+            const int vi = v0 + v;
+            if (vi >= nvec) break;                         // uniform over the workgroup
+            const uint64_t key = valid ? block_key(sc[v][tid], j) : 0ull;
+            keys[tid] = key;
+            __syncthreads();
+            int rank = 0;
+#pragma unroll 8
+            for (int u = 0; u < kChunk; u += 2) {
+                const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(keys + u);
+                rank += (kk.x > key) + (kk.y > key);
+            }
+            uint64_t* dst = a.cand + ((size_t)((b * a.NQ + vi) * a.H_kv + g) * nch + blockIdx.x) * K;
+            if (valid && rank < K) __hip_atomic_store(dst + rank, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid >= nvalid && tid < K) __hip_atomic_store(dst + tid, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();                               // keys is rewritten for the next vector
+        }
+
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's lists have landed
+        __syncthreads();
+        int* cnt = a.counters + (size_t)row * gridDim.z + blockIdx.z;
+        if (tid == 0) last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nch - 1;
+        __syncthreads();
+        if (!last) return;
+
+        // level 2: merge the nch sorted lists of each vector and write its block set
+        const int kk = min(K, hi - lo);
+        const int n = nch * K;
+        for (int v = 0; v < NV; ++v) {
+            const int vi = v0 + v;
+            if (vi >= nvec) break;
+            const int vrow = (b * a.NQ + vi) * a.H_kv + g;
+            const uint64_t* src = a.cand + (size_t)vrow * n;
+            for (int i = tid; i < n; i += 256)
+                lists[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            for (int i = tid; i < n; i += 256) {
+                const uint64_t x = lists[i];
+                if (!x) continue;
+                const int c = i / K;
+                int r = i - c * K;
+                for (int c2 = 0; c2 < nch; ++c2)
+                    if (c2 != c) r += count_larger(lists + c2 * K, K, x);
+                if (r < kk) sel_j[r] = (int)(0xFFFFFFFFu - (uint32_t)x);
+            }
+            __syncthreads();
+            int32_t* out = s.block_idx + (size_t)vrow * s.n_sel_max;
+            for (int i = tid; i < lo; i += 256) out[i] = i;                 // initial blocks
+            if (tid < kk) {                                                  // top-k, ascending
+                const int jt = sel_j[tid];
+                int pos = 0;
+                for (int u = 0; u < kk; ++u) pos += sel_j[u] < jt;
+                out[lo + pos] = jt;
+            }
+            for (int i = tid; i < nb - hi; i += 256) out[lo + kk + i] = hi + i;  // local blocks
+            const int total = lo + kk + (nb - hi);
+            for (int p = total + tid; p < s.n_sel_max; p += 256) out[p] = -1;
+            if (tid == 0) s.n_sel[vrow] = total;
+            __syncthreads();                               // lists / sel_j are reused
+        }
+        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <int D, bool FUSED>
+static void launch_score_d(const ScoreArgs& a, int B, hipStream_t s) {
+    const int nvec = a.NQ * a.VPR;
+    int nv = 1;
+    while (nv < nvec && nv < 16) nv *= 2;
+    dim3 grid(score_chunks(a.NB_cap), B * a.H_kv, (nvec + nv - 1) / nv), block(256);
+    switch (nv) {
+        case 1: hipLaunchKernelGGL((score_kernel<D, 1, FUSED>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((score_kernel<D, 2, FUSED>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((score_kernel<D, 4, FUSED>), grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((score_kernel<D, 8, FUSED>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((score_kernel<D, 16, FUSED>), grid, block, 0, s, a); break;
+    }
+}
+
+int score_tiles(int NQ) {
+    int nv = 1;
+    while (nv < NQ && nv < 16) nv *= 2;
+    return (NQ + nv - 1) / nv;
+}
+
+bool fused_select_ok(int NB_cap, int top_k) {
+    return top_k >= 1 && top_k <= kFusedTopK && score_chunks(NB_cap) <= kFusedChunks;
+}
+
+hipError_t launch_score_select(const uint16_t* f, const float* kt, const SelectArgs& sel, int B, int d,
+                               float* scores_opt, float* scores_ws, uint64_t* cand, int* counters,
+                               hipStream_t s) {
+    if (cand && counters) {
+        ScoreArgs a{f, kt, sel.seq_len, scores_opt, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, cand, counters};
+        if (d == 128) launch_score_d<128, true>(a, B, s);
+        else launch_score_d<64, true>(a, B, s);
+        return hipGetLastError();
+    }
+    float* scores = scores_opt ? scores_opt : scores_ws;
+    ScoreArgs a{f, kt, sel.seq_len, scores, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, nullptr, nullptr};
+    if (d == 128) launch_score_d<128, false>(a, B, s);
+    else launch_score_d<64, false>(a, B, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SelectArgs sa = sel;
+    sa.scores = scores;
+    return launch_select(sa, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -339,8 +492,9 @@ hipError_t launch_multihead_scores(const uint16_t* q, const float* kt, const int
                                    float* z, float* stats, float* scores, hipStream_t s) {
     (void)stats;
     const int G = H_q / H_kv;
-    if (d == 128) launch_score_d<128>(q, kt, seq_len, B, NQ, H_kv, G, NB_cap, 1.f / tau, z, s);
-    else launch_score_d<64>(q, kt, seq_len, B, NQ, H_kv, G, NB_cap, 1.f / tau, z, s);
+    ScoreArgs a{q, kt, seq_len, z, NQ, H_kv, G, NB_cap, 1.f / tau, SelectArgs{}, nullptr, nullptr};
+    if (d == 128) launch_score_d<128, false>(a, B, s);
+    else launch_score_d<64, false>(a, B, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(softmax_sum_kernel, dim3(B * NQ * H_kv), dim3(256), 0, s, z, seq_len, NQ,

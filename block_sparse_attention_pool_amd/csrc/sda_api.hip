@@ -132,10 +132,21 @@ sda_status_t sda_update_compressed_keys(const void* k, float* k_tilde, const int
 }
 
 // ---------------------------------------------------------------------------
+// [scores: B*NQ*H_kv*NB_cap f32][candidate keys: B*NQ*H_kv*chunks*top_k u64]
+// [arrival counters: B*H_kv*vector tiles i32], each region padded to 256 B
+static size_t pad256(size_t n) { return (n + 255) & ~(size_t)255; }
+static size_t score_region_bytes(int B, int NQ, int H_kv, int NB_cap) {
+    return pad256((size_t)B * NQ * H_kv * NB_cap * sizeof(float));
+}
+static size_t cand_region_bytes(int B, int NQ, int H_kv, int NB_cap, int top_k) {
+    if (!fused_select_ok(NB_cap, top_k)) return 0;
+    return pad256((size_t)B * NQ * H_kv * score_chunks(NB_cap) * top_k * sizeof(uint64_t));
+}
+
 size_t sda_score_select_workspace(int B, int NQ, int H_kv, int NB_cap, int top_k) {
-    (void)top_k;
-    if (B < 1 || NQ < 1 || H_kv < 1 || NB_cap < 1) return 0;
-    return (size_t)B * NQ * H_kv * NB_cap * sizeof(float);
+    if (B < 1 || NQ < 1 || H_kv < 1 || NB_cap < 1 || top_k < 0) return 0;
+    return score_region_bytes(B, NQ, H_kv, NB_cap) + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k) +
+           (size_t)B * H_kv * score_tiles(NQ) * sizeof(int);
 }
 
 static sda_status_t check_select_common(const float* k_tilde, const int32_t* seq_len, int B, int NQ,
@@ -167,22 +178,23 @@ sda_status_t sda_score_select(const void* f, const float* k_tilde, const int32_t
                             block_idx, n_sel));
     REQUIRE(aligned16(f), SDA_ERR_ALIGN, "f must be 16-byte aligned");
     REQUIRE(ceil_div(NQ, 16) <= kMaxGridYZ, SDA_ERR_SHAPE, "NQ too large");
-    float* scores = scores_opt;
-    if (!scores) {
-        const size_t need = sda_score_select_workspace(B, NQ, H_kv, NB_cap, top_k);
-        REQUIRE(ws && ws_bytes >= need, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, need);
-        REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
-        scores = static_cast<float*>(ws);
-    } else {
-        REQUIRE(aligned4(scores_opt), SDA_ERR_ALIGN, "scores_opt must be 4-byte aligned");
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    TRY(hip_status(launch_scores(static_cast<const uint16_t*>(f), k_tilde, seq_len, B, NQ, H_kv, d, NB_cap,
-                                 scores, s),
-                   "score launch"));
-    SelectArgs a{seq_len, scores, B * NQ * H_kv, NQ, H_kv, NB_cap, n_init, n_local, top_k, n_sel_max,
+    const size_t need = sda_score_select_workspace(B, NQ, H_kv, NB_cap, top_k);
+    REQUIRE(ws && ws_bytes >= need, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, need);
+    REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    REQUIRE(!scores_opt || aligned4(scores_opt), SDA_ERR_ALIGN, "scores_opt must be 4-byte aligned");
+    char* base = static_cast<char*>(ws);
+    float* scores_ws = reinterpret_cast<float*>(base);
+    const size_t cand_off = score_region_bytes(B, NQ, H_kv, NB_cap);
+    uint64_t* cand = reinterpret_cast<uint64_t*>(base + cand_off);
+    int* counters = reinterpret_cast<int*>(base + cand_off + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k));
+    // one launch (the last scoring workgroup of each row merges per-chunk
+    // candidate lists) unless the lists would be too long for it
+    if (!fused_select_ok(NB_cap, top_k) || env_int("SDA_SELECT_FUSED", 1) == 0) cand = nullptr, counters = nullptr;
+    SelectArgs a{seq_len, nullptr, B * NQ * H_kv, NQ, H_kv, NB_cap, n_init, n_local, top_k, n_sel_max,
                  block_idx, n_sel};
-    return hip_status(launch_select(a, s), "select launch");
+    return hip_status(launch_score_select(static_cast<const uint16_t*>(f), k_tilde, a, B, d, scores_opt, scores_ws,
+                                          cand, counters, static_cast<hipStream_t>(stream)),
+                      "score/select launch");
 }
 
 size_t sda_score_select_multihead_workspace(int B, int NQ, int H_q, int H_kv, int NB_cap, int top_k) {

@@ -22,8 +22,17 @@ struct SelectArgs {
     int32_t* block_idx;
     int32_t* n_sel;
 };
-hipError_t launch_scores(const uint16_t* f, const float* kt, const int32_t* seq_len, int B, int NQ,
-                         int H_kv, int d, int NB_cap, float* scores, hipStream_t s);
+// scores, then exact top-k and block sets.  With `cand` and `counters` (zeroed,
+// one per (b, kv head, vector tile)) the selection runs inside the scoring
+// launch (needs fused_select_ok); otherwise scores go to scores_opt or
+// scores_ws and a second launch selects.
+hipError_t launch_score_select(const uint16_t* f, const float* kt, const SelectArgs& sel, int B, int d,
+                               float* scores_opt, float* scores_ws, uint64_t* cand, int* counters,
+                               hipStream_t s);
+bool fused_select_ok(int NB_cap, int top_k);
+int score_tiles(int NQ);
+// integer from the environment (tuning switches), dflt when unset
+int env_int(const char* name, int dflt);
 hipError_t launch_multihead_scores(const uint16_t* q, const float* kt, const int32_t* seq_len,
                                    int B, int NQ, int H_q, int H_kv, int d, int NB_cap, float tau,
                                    float* z, float* stats, float* scores, hipStream_t s);

@@ -52,7 +52,13 @@ def test_status_strings(L):
 
 
 def test_workspace_sizes(L):
-    assert L.sda_score_select_workspace(8, 1, 8, 2048, 32) == 8 * 8 * 2048 * 4
+    # scores + per-chunk candidate keys (top_k <= 64, NB_cap <= 4096 only), each
+    # padded to 256 B, + one arrival counter per (b, kv head, vector tile)
+    assert L.sda_score_select_workspace(8, 1, 8, 2048, 32) == 8 * 8 * 2048 * 4 + 64 * 8 * 32 * 8 + 8 * 8 * 4
+    assert L.sda_score_select_workspace(1, 3, 1, 3, 1) == 256 + 256 + 1 * 1 * 1 * 4
+    assert L.sda_score_select_workspace(2, 20, 1, 64, 1) == 2 * 20 * 64 * 4 + 512 + 2 * 1 * 2 * 4
+    assert L.sda_score_select_workspace(1, 1, 1, 2048, 65) == 2048 * 4 + 4       # lists too long: no candidates
+    assert L.sda_score_select_workspace(1, 1, 1, 4097, 8) == 16640 + 4            # too many chunks
     assert L.sda_score_select_workspace(0, 1, 8, 2048, 32) == 0
     # multihead: per-head logits plus the summed scores
     assert L.sda_score_select_multihead_workspace(8, 1, 64, 8, 2048, 32) == (8 * 64 * 2048 + 8 * 8 * 2048) * 4
@@ -92,6 +98,8 @@ def test_score_select_validation(L):
     bad = list(args); bad[16] = 100                                       # workspace too small
     assert f(*bad) == WS
     bad = list(args); bad[15] = None
+    assert f(*bad) == WS
+    bad = list(args); bad[14] = P; bad[15] = None                        # counters live in the workspace
     assert f(*bad) == WS
     bad = list(args); bad[6] = 32
     assert f(*bad) == UNSUP

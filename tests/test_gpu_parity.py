@@ -169,6 +169,57 @@ def test_select_small_and_degenerate(T, k):
         assert np.all(bi[0, 0, g, n:] == -1)
 
 
+@pytest.mark.parametrize("NB,T,n_init,n_local,k", [
+    (4096, 4096 * 64, 1, 2, 40),        # 16 chunk lists: the longest the in-launch merge takes
+    (5000, 5000 * 64 - 10, 1, 2, 40),   # past it the selection runs as a second launch
+    (1000, 301 * 64 - 5, 3, 5, 64),     # chunks past the sequence end, longest lists
+    (600, 600 * 64, 0, 0, 1),
+    (2048, 2048 * 64, 1, 2, 65)])       # lists too long for the merge: second launch
+def test_select_long_rows(NB, T, n_init, n_local, k):
+    rng = np.random.default_rng(NB + k)
+    kt = rng.standard_normal((1, 2, NB, 64)) / 8
+    F = rng.standard_normal((1, 1, 2, 64)) / 8
+    bi, ns, Fd = _select_direct(kt, F, T, n_init, n_local, k)
+    nb = O.num_blocks(T)
+    for g in range(2):
+        want, _ = O.select_row(Fd[0, 0, g], O.store_f32(kt[0, g, :nb]), n_init, n_local, k)
+        n = int(ns[0, 0, g])
+        assert list(bi[0, 0, g, :n]) == list(want)
+        assert np.all(bi[0, 0, g, n:] == -1)
+
+
+@pytest.mark.parametrize("NQ", [1, 20])
+def test_fused_select_matches_select_launch(NQ):
+    # selection inside the scoring launch (last-arriving chunk workgroup) and the
+    # separate selection launch read the same scores: identical lists, call after
+    # call, and the arrival counters are back at zero after every call
+    import os
+    cfg = synth.get_config(2)
+    K, _, _ = inputs.kv_layer(cfg, 0, device=DEV)
+    ktg = gpu_ktilde(K, cfg.T)
+    rng = np.random.default_rng(NQ)
+    F = inputs.to_bf16(rng.standard_normal((cfg.B, NQ, cfg.H_kv, cfg.d)) / 8).to(DEV)
+    args = (F, ktg, seq(cfg), cfg.n_init, cfg.n_local, cfg.top_k)
+    old = os.environ.get("SDA_SELECT_FUSED")
+    try:
+        os.environ["SDA_SELECT_FUSED"] = "0"
+        ref_bi, ref_ns = sda.sda_score_select(*args)
+        os.environ["SDA_SELECT_FUSED"] = "1"
+        nbytes = sda.lib().sda_score_select_workspace(cfg.B, NQ, cfg.H_kv, ktg.shape[2], cfg.top_k)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+        n_cnt = cfg.B * cfg.H_kv * (1 if NQ == 1 else 2)
+        for it in range(10):
+            bi, ns = sda.sda_score_select(*args, ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(bi, ref_bi) and torch.equal(ns, ref_ns), it
+            assert int(ws[nbytes - 4 * n_cnt:].count_nonzero()) == 0, it
+    finally:
+        if old is None:
+            os.environ.pop("SDA_SELECT_FUSED", None)
+        else:
+            os.environ["SDA_SELECT_FUSED"] = old
+
+
 def test_select_ties_go_to_lower_index():
     rng = np.random.default_rng(5)
     NB, d = 300, 128
