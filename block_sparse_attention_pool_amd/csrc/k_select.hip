@@ -202,12 +202,13 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
 //
 // FUSED (one vector per query, VPR = 1): the selection runs in the same launch
 // in two levels.  Each chunk workgroup ranks its 256 candidate blocks by the
-// key (score, then lower block index) and writes its best top_k keys, in rank
-// order, to `cand` with write-through stores.  Every chunk workgroup of a
-// (kv row, vector tile) then bumps an agent-scope arrival counter; the last
-// one merges the per-chunk sorted lists (a key's global rank is its rank in
-// its own list plus the number of larger keys in every other list) and writes
-// the block set.  Each block lives in exactly one chunk and a global top-k
+// key (score, then lower block index): each wave sorts its 64 keys by rank
+// counting over register rotations, and two rounds of pairwise merges of the
+// sorted wave lists leave the chunk's best top_k keys in rank order, which go
+// to `cand` with write-through stores.  Every chunk workgroup of a (kv row,
+// vector tile) then bumps an agent-scope arrival counter; the last one merges
+// the per-chunk sorted lists pairwise, round by round, and writes the block
+// set.  Each block lives in exactly one chunk and a global top-k
 // block is within its chunk's top-k, so the merge is exact.
 struct ScoreArgs {
     const uint16_t* vec;
@@ -229,15 +230,56 @@ __device__ __forceinline__ uint64_t block_key(float s, int j) {
     return ((uint64_t)float_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
 }
 
-// number of keys in the descending list L[0..n) that are larger than x
-__device__ __forceinline__ int count_larger(const uint64_t* L, int n, uint64_t x) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (L[mid] > x) lo = mid + 1;
-        else hi = mid;
+// number of keys larger than `key` among the 64 lanes of the wave: the keys
+// travel once round the wave through register rotations
+__device__ __forceinline__ int wave_rank(uint64_t key) {
+    uint32_t hi = (uint32_t)(key >> 32), lo = (uint32_t)key;
+    int r = 0;
+#pragma unroll
+    for (int i = 1; i < kWave; ++i) {
+        hi = wave_ror1(hi);
+        lo = wave_ror1(lo);
+        r += ((((uint64_t)hi) << 32) | lo) > key;
     }
-    return lo;
+    return r;
+}
+
+// number of keys larger than x in the descending list L[0..len), 1 <= len <= 64:
+// the last key of each full 8-key segment tells how many whole segments are
+// larger, then the next segment is counted; two rounds of independent reads
+__device__ __forceinline__ int count_larger(const uint64_t* L, int len, uint64_t x) {
+    uint64_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = L[min(8 * i + 7, len - 1)];      // all reads in bounds, issued together
+    int seg = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) seg += (int)((8 * i + 7 < len) & (v[i] > x));
+    const int base = 8 * seg;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = L[min(base + i, len - 1)];
+    int n = base;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) n += (int)((base + i < len) & (v[i] > x));
+    return n;
+}
+
+// One round of pairwise merges over the workgroup: lists c < nl of `len`
+// descending keys (zero-padded, len >= K) at src + c * ss; the pair
+// (2m, 2m+1) becomes list m of its K largest keys at dst + m * ds.  The list
+// strides are odd numbers of keys so that lists start in different LDS banks.  A key's
+// place in the merged list is its place in its own list plus the number of
+// larger keys in the partner list; keys are distinct apart from the zero
+// padding, whose writes may coincide but carry the same value.
+__device__ __forceinline__ void merge_round(const uint64_t* src, int nl, int len, int ss, uint64_t* dst, int ds,
+                                            int K) {
+    const int items = nl * K;                              // only the first K of a list can stay
+    for (int i = threadIdx.x; i < items; i += 256) {
+        const int c = i / K, p = i - c * K;
+        const uint64_t x = src[c * ss + p];
+        int pos = p;
+        if ((c ^ 1) < nl) pos += count_larger(src + (c ^ 1) * ss, len, x);
+        if (pos < K) dst[(c >> 1) * ds + pos] = x;
+    }
 }
 
 template <int D, int NV, bool FUSED>
@@ -322,38 +364,41 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     }
 
     if constexpr (FUSED) {
-        __shared__ uint64_t keys[kChunk];
-        __shared__ uint64_t lists[kFusedTopK * kFusedChunks];
-        __shared__ int sel_j[kFusedTopK];
+        constexpr int WS = kWave + 1;                      // list strides (odd: spread over banks)
+        __shared__ uint64_t wl[4 * WS];                    // four sorted wave lists of 64
+        __shared__ uint64_t bufA[(kFusedTopK + 1) * kFusedChunks];
+        __shared__ uint64_t bufB[(kFusedTopK + 1) * kFusedChunks / 2];
+        __shared__ __align__(16) int sel_j[kFusedTopK];
         __shared__ int last;
         const SelectArgs& s = a.sel;
         const int K = s.top_k;
+        const int KS = K | 1;                              // odd list stride >= K
         const int nch = gridDim.x;
         const int tid = threadIdx.x;
         const int lo = min(s.n_init, nb);                 // candidates are [lo, hi)
         const int hi = max(lo, nb - s.n_local);
         __syncthreads();                                   // sc complete
 
-        // level 1: this chunk's best K candidates, in rank order
+        // level 1: rank inside each wave, then two rounds of pairwise merges
+        // give this chunk's best K keys in rank order
         const int j = j0 + tid;
         const bool valid = j >= lo && j < hi;
-        const int nvalid = max(0, min(j0 + kChunk, hi) - max(j0, lo));
+        const int nvw = __popcll(__ballot(valid));         // valid lanes of this wave
         for (int v = 0; v < NV; ++v) {
             const int vi = v0 + v;
             if (vi >= nvec) break;                         // uniform over the workgroup
             const uint64_t key = valid ? block_key(sc[v][tid], j) : 0ull;
-            keys[tid] = key;
+            const int wr = wave_rank(key);                 // valid keys: distinct ranks < nvw
+            if (valid) wl[wave * WS + wr] = key;
+            if (lane >= nvw) wl[wave * WS + lane] = 0ull;
             __syncthreads();
-            int rank = 0;
-#pragma unroll 8
-            for (int u = 0; u < kChunk; u += 2) {
-                const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(keys + u);
-                rank += (kk.x > key) + (kk.y > key);
-            }
+            merge_round(wl, 4, kWave, WS, bufA, KS, K);
+            __syncthreads();
+            merge_round(bufA, 2, K, KS, bufB, KS, K);
+            __syncthreads();
             uint64_t* dst = a.cand + ((size_t)((b * a.NQ + vi) * a.H_kv + g) * nch + blockIdx.x) * K;
-            if (valid && rank < K) __hip_atomic_store(dst + rank, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (tid >= nvalid && tid < K) __hip_atomic_store(dst + tid, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();                               // keys is rewritten for the next vector
+            if (tid < K) __hip_atomic_store(dst + tid, bufB[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // the next vector's writes to wl / bufA / bufB come after two more barriers
         }
 
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's lists have landed
@@ -363,40 +408,46 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         __syncthreads();
         if (!last) return;
 
-        // level 2: merge the nch sorted lists of each vector and write its block set
+        // level 2: pairwise merge rounds over the nch chunk lists of each vector,
+        // then the block set
         const int kk = min(K, hi - lo);
-        const int n = nch * K;
         for (int v = 0; v < NV; ++v) {
             const int vi = v0 + v;
             if (vi >= nvec) break;
             const int vrow = (b * a.NQ + vi) * a.H_kv + g;
-            const uint64_t* src = a.cand + (size_t)vrow * n;
-            for (int i = tid; i < n; i += 256)
-                lists[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            for (int i = tid; i < n; i += 256) {
-                const uint64_t x = lists[i];
-                if (!x) continue;
+            const uint64_t* src = a.cand + (size_t)vrow * nch * K;
+            for (int i = tid; i < nch * K; i += 256) {
                 const int c = i / K;
-                int r = i - c * K;
-                for (int c2 = 0; c2 < nch; ++c2)
-                    if (c2 != c) r += count_larger(lists + c2 * K, K, x);
-                if (r < kk) sel_j[r] = (int)(0xFFFFFFFFu - (uint32_t)x);
+                bufA[c * KS + (i - c * K)] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+            __syncthreads();
+            uint64_t* cur = bufA;
+            uint64_t* nxt = bufB;
+            for (int nl = nch; nl > 1; nl = (nl + 1) >> 1) {
+                merge_round(cur, nl, K, KS, nxt, KS, K);
+                __syncthreads();
+                uint64_t* t = cur; cur = nxt; nxt = t;
+            }
+            if (tid < kk) sel_j[tid] = (int)(0xFFFFFFFFu - (uint32_t)cur[tid]);
             __syncthreads();
             int32_t* out = s.block_idx + (size_t)vrow * s.n_sel_max;
             for (int i = tid; i < lo; i += 256) out[i] = i;                 // initial blocks
             if (tid < kk) {                                                  // top-k, ascending
                 const int jt = sel_j[tid];
                 int pos = 0;
-                for (int u = 0; u < kk; ++u) pos += sel_j[u] < jt;
+#pragma unroll
+                for (int u = 0; u < kFusedTopK; u += 4) {
+                    const int4 q = *reinterpret_cast<const int4*>(sel_j + u);
+                    pos += (u + 0 < kk && q.x < jt) + (u + 1 < kk && q.y < jt) +
+                           (u + 2 < kk && q.z < jt) + (u + 3 < kk && q.w < jt);
+                }
                 out[lo + pos] = jt;
             }
             for (int i = tid; i < nb - hi; i += 256) out[lo + kk + i] = hi + i;  // local blocks
             const int total = lo + kk + (nb - hi);
             for (int p = total + tid; p < s.n_sel_max; p += 256) out[p] = -1;
             if (tid == 0) s.n_sel[vrow] = total;
-            __syncthreads();                               // lists / sel_j are reused
+            __syncthreads();                               // bufA / sel_j are reused
         }
         if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
