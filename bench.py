@@ -156,6 +156,31 @@ def timed_graph(step, L, steps):
     return time.perf_counter() - t0, steps
 
 
+def call_time(prepared, reps, copies=8):
+    """Mean device seconds per launch of the prepared calls, from `reps` replays
+    of one graph holding `copies` passes over them, between two HIP events."""
+    warm = torch.cuda.Stream()
+    warm.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(warm):
+        for c in prepared:
+            c.run()
+    torch.cuda.current_stream().wait_stream(warm)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(copies):
+            for c in prepared:
+                c.run()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (reps * copies * len(prepared))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +195,7 @@ def main():
                     help="run layer l+1's selection on a side stream beside layer l's decode "
                          "(slower on this GPU: the two kernels contend for the same bandwidth and CUs)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--call-reps", type=int, default=50, help="graph replays per per-call timing")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -240,26 +266,27 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # per-call device time: events on the launch stream around each call, the
-    # host enqueueing ahead of the GPU
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    t_sel = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    t_dec = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-
     run_step = pipelined_step if args.overlap else step
     if args.no_graph:
+        # eager: events on the launch stream around each call (the host
+        # enqueues ahead of the GPU, so each interval also holds the dispatch)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            run_step(i)
+            step(i, evs[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         steps_timed = args.steps
+        t_sel = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+        t_dec = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
     else:
         wall, steps_timed = timed_graph(run_step, L, args.steps)
+        # per-launch device time of each call: a graph of the ring's launches of
+        # that call alone, replayed back to back between two HIP events on the
+        # stream the graph runs on (inter-kernel gaps included)
+        t_sel = np.array([call_time([c[0] for c in calls], args.call_reps)])
+        t_dec = np.array([call_time([c[1] for c in calls], args.call_reps)])
 
     queries = cfg.B * cfg.NQ
     value = queries * steps_timed / wall
@@ -306,14 +333,15 @@ def main():
             "unit": "GB/s",
             "frac": dec_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": "sda_sparse_decode (attention kernel + split combine)",
+            "kernel": "sda_sparse_decode (attn_kernel; splits merged by the last workgroup of each row)",
             "algorithmic_bytes_per_launch": dec_bytes,
         },
         "kernels_us": {
-            "score_select_mean": t_sel.mean() * 1e6, "score_select_p50": float(np.median(t_sel)) * 1e6,
-            "sparse_decode_mean": t_dec.mean() * 1e6, "sparse_decode_p50": float(np.median(t_dec)) * 1e6,
-            "sparse_decode_p10": float(np.percentile(t_dec, 10)) * 1e6,
-            "sparse_decode_p90": float(np.percentile(t_dec, 90)) * 1e6,
+            "score_select": t_sel.mean() * 1e6,
+            "sparse_decode": t_dec.mean() * 1e6,
+            "timing": ("eager: events around each call" if args.no_graph else
+                       f"graph of {8 * L} back-to-back launches of the call, {args.call_reps} replays "
+                       "between two HIP events"),
         },
         "score_select_gbs": sel_bytes / t_sel.mean() / 1e9,
         "queries_per_s_from_kernels": queries / (t_sel.mean() + t_dec.mean()),

@@ -95,7 +95,11 @@ sda_status_t sda_update_compressed_keys(const void* k, float* k_tilde,
  *   block_idx  i32  [B, NQ, H_kv, n_sel_max] out; n_sel i32 [B, NQ, H_kv] out
  *   scores_opt f32  [B, NQ, H_kv, NB_cap] out or NULL (raw scores, entries past nb undefined)
  * n_sel_max >= n_init + n_local + top_k.  Scores are fp32 (fp32 K~, fp32 sums).
- * Workspace: sda_score_select_workspace() bytes.
+ * Workspace: sda_score_select_workspace() bytes, required even with scores_opt.
+ * It holds arrival counters: zero-fill it before its first use; every
+ * completed call leaves them zero.  Calls sharing a workspace must not overlap
+ * in time.  With top_k <= 64 and NB_cap <= 4096 the selection runs inside the
+ * scoring launch, otherwise as a second launch; the results are identical.
  */
 size_t sda_score_select_workspace(int B, int NQ, int H_kv, int NB_cap, int top_k);
 sda_status_t sda_score_select(const void* f, const float* k_tilde, const int32_t* seq_len,
