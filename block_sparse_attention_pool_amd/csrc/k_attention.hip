@@ -73,10 +73,50 @@ constexpr int kMaxWaves = 10;
 // list of blocks a workgroup walks, and which of the group's queries use each
 struct ListView {
     const int32_t* gidx;   // global list (C == 1 or shared mode), or null
+    const int32_t* gn;     // its entry count (global), read by the engine
     const int32_t* lidx;   // LDS list (exact union)
     const uint32_t* lmask; // LDS membership masks (exact union)
-    int n;
+    int n;                 // entry count of the LDS list
 };
+
+// Read-only int32 the kernel never writes (lengths, block lists): through the
+// constant address space, so that wave-uniform reads become scalar loads
+// that wait on their own counter, not behind the vector loads.
+__device__ __forceinline__ int ld_ro(const int32_t* p) {
+    return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)p;
+}
+
+// Wait until at most N vector memory operations are outstanding; the K tile
+// passes through as in-out operands so no use of it moves above the wait.
+template <int N, int KS>
+__device__ __forceinline__ void kwait(u32x4 (&kf)[4][KS]) {
+    static_assert(KS == 2 || KS == 4, "head dim 64 or 128");
+    if constexpr (KS == 4) {
+        asm volatile("s_waitcnt vmcnt(%16)"
+                     : "+v"(kf[0][0]), "+v"(kf[0][1]), "+v"(kf[0][2]), "+v"(kf[0][3]),
+                       "+v"(kf[1][0]), "+v"(kf[1][1]), "+v"(kf[1][2]), "+v"(kf[1][3]),
+                       "+v"(kf[2][0]), "+v"(kf[2][1]), "+v"(kf[2][2]), "+v"(kf[2][3]),
+                       "+v"(kf[3][0]), "+v"(kf[3][1]), "+v"(kf[3][2]), "+v"(kf[3][3])
+                     : "n"(N) : "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(%8)"
+                     : "+v"(kf[0][0]), "+v"(kf[0][1]), "+v"(kf[1][0]), "+v"(kf[1][1]),
+                       "+v"(kf[2][0]), "+v"(kf[2][1]), "+v"(kf[3][0]), "+v"(kf[3][1])
+                     : "n"(N) : "memory");
+    }
+}
+
+// Every vector load has landed; the Q fragments pass through as in-out operands
+// so their registers stay reserved until here on every path (a wave whose
+// list part is empty never reaches the K wait).
+template <int NT, int KS>
+__device__ __forceinline__ void qwait(u32x4 (&qf)[NT][KS]) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[nt][ks]));
+}
 
 __device__ __forceinline__ void lds_dma16(const void* g, SDA_LDS void* l) {
     __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
@@ -136,38 +176,56 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int task, int r, si
 }
 
 template <int D, int NT>
-__device__ __forceinline__ void run_tile_engine(const AttnArgs& a, const ListView& L, int b, int g, int q0,
+__device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, int b, int g, int q0,
                                                 int Cg, int split, int task, char* smem) {
     constexpr int KS = D / 32;            // QK k-steps
     constexpr int MTD = D / 16;           // PV m-tiles over d
     constexpr int RP = NT * 16;           // padded rows
     const int lane = __lane_id();
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
     const int W = blockDim.x / kWave;     // waves per workgroup (one block each, normally)
     const int li = lane & 15;
     const int lg = lane >> 4;
     const int G = a.G;
     const int R = Cg * G;
-    const int T = a.seq_len[b];
+    // The wave's block ids (global list) arrive by one vector load, lane k
+    // holding its k-th entry, issued before anything else; the length and the
+    // list count are scalar reads; then the Q loads.  The first K/V loads wait
+    // only for these, never for Q.
+    const bool glist = L.gidx != nullptr;
+    const int n_range = glist ? a.n_sel_max : L.n;
+    const int e_begin = (split * n_range) / a.n_split;
+    const int e_end = ((split + 1) * n_range) / a.n_split;
+    const int32_t* slot_row = (a.slot && glist) ? a.slot + (L.gidx - a.block_idx) : nullptr;
+    int e = e_begin + wave;
+    const int T = ld_ro(a.seq_len + b);
+    const int n_g = glist ? ld_ro(L.gn) : 0;
+    int id_v = -1, slot_v = -1;            // entries e + (it + lane) * W, it = 0, 64, ...
+    auto load_ids = [&](int e0) {
+        const int ee = e0 + lane * W;
+        const bool ok = ee < e_end;
+        id_v = ok ? L.gidx[ee] : -1;
+        if (slot_row) slot_v = ok ? slot_row[ee] : -1;
+    };
+    if (glist) load_ids(e);
+    if (glist) L.n = min(max(n_g, 0), a.n_sel_max);
     const int nb = (T + kBlock - 1) / kBlock;
     const int blocks_cap = (a.T_cap + kBlock - 1) / kBlock;
 
     // Q fragments (B operand of S^T = K Q^T): row nt*16 + li, d = ks*32 + lg*8
     u32x4 qf[NT][KS];
     int rowq[NT];
-    bool rowok[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int r = nt * 16 + li;
         const int c = r / G, h = r - c * G;
         rowq[nt] = c;
-        rowok[nt] = r < R;
         const uint16_t* qp = a.q + (((size_t)b * a.NQ + q0 + min(c, Cg - 1)) * a.H_q + (size_t)g * G + h) * D + lg * 8;
+        // padding rows (r >= R) read a real row; their columns are never written back.
+        // Issued as asm like the K loads: the first K wait covers them.
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 v = ldg16_cached(qp + ks * 32);
-            qf[nt][ks] = rowok[nt] ? v : u32x4{0, 0, 0, 0};
-        }
+        for (int ks = 0; ks < KS; ++ks)
+            asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[nt][ks]) : "v"(qp + ks * 32) : "memory");
     }
 
     floatx4 o[MTD][NT];
@@ -187,12 +245,8 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, const ListVie
     const uint16_t* kv_k = a.k + ((size_t)b * a.H_kv + g) * a.T_cap * D;
     const uint16_t* kv_v = a.v + ((size_t)b * a.H_kv + g) * a.T_cap * D;
     // global lists are split over their static width, so a wave's first block
-    // id can be read before the row's entry count arrives; entries past the
-    // count are padding and skipped
-    const int n_range = L.gidx ? a.n_sel_max : L.n;
-    const int e_begin = (split * n_range) / a.n_split;
-    const int e_end = ((split + 1) * n_range) / a.n_split;
-    const int32_t* slot_row = (a.slot && L.gidx) ? a.slot + (L.gidx - a.block_idx) : nullptr;
+    // id is read together with the row's entry count; entries past the count
+    // are padding and skipped
 
     // V direct loads: LDS slot (i, lane) holds row i*VRPI + lane/VLPR, 16-byte piece
     // lane % VLPR of the permuted row; the lane fetches the matching logical piece
@@ -202,25 +256,19 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, const ListVie
     const int v_rb = (lane % VLPR) * 16;
     const int tr_col = (li & 3) * 8;       // bytes inside the 32-byte chunk for the transposed reads
 
-    auto entry = [&](int e, int& j, int& phys, uint32_t& memb) {
-        if (L.gidx) {
-            j = L.gidx[e];
-            phys = slot_row ? slot_row[e] : j;
+    for (int it = 0; e < e_end; e += W, ++it) {
+        int j, phys;
+        uint32_t memb;
+        if (glist) {
+            if (it && (it & (kWave - 1)) == 0) load_ids(e);
+            j = __builtin_amdgcn_readlane(id_v, it & (kWave - 1));
+            phys = slot_row ? __builtin_amdgcn_readlane(slot_v, it & (kWave - 1)) : j;
             memb = 0xffffffffu;
         } else {
             j = L.lidx[e];
             phys = j;
             memb = L.lmask[e];
         }
-    };
-    int e = e_begin + wave;
-    int j_nx = -1, p_nx = -1;
-    uint32_t m_nx = 0;
-    if (e < e_end) entry(e, j_nx, p_nx, m_nx);
-    for (; e < e_end; e += W) {
-        const int j = j_nx, phys = p_nx;
-        const uint32_t memb = m_nx;
-        if (e + W < e_end) entry(e + W, j_nx, p_nx, m_nx);   // next block id, one iteration early
         if (e >= L.n) break;
         if (j < 0 || j >= nb || phys < 0 || phys >= blocks_cap) continue;
         const int nvalid = min(kBlock, T - j * kBlock);
@@ -230,9 +278,21 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, const ListVie
         const int tmax = nvalid - 1;
         const bool full = (nvalid == kBlock) && (memb == 0xffffffffu);   // wave-uniform
 
-        // ---- V into LDS by direct loads, then K into registers (MFMA A layout);
-        //      everything is in flight before the first wait ----------------------------
+        // ---- K into registers (MFMA A layout), then V into LDS by direct loads;
+        //      everything is in flight before the first wait, and QK and the
+        //      softmax wait only for K (V is still on its way) --------------------------
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // previous tile's LDS reads are done
+        // K loads are issued as asm so that the compiler does not fold the V
+        // direct loads issued after them into its wait for K: the explicit
+        // vmcnt wait below lets exactly the kLoads V loads stay in flight.
+        u32x4 kf[4][KS];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const uint32_t off = (uint32_t)min(tok_of(mt, li), tmax) * (D * 2) + lg * 16;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(kf[mt][ks]) : "v"(kb + off + ks * 64) : "memory");
+        }
 #pragma unroll
         for (int i = 0; i < VTile<D>::kLoads; ++i) {
             const int t = i * VRPI + v_lrow;
@@ -240,12 +300,12 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, const ListVie
                                  (uint32_t)(v_rb ^ (VTile<D>::perm(t) << 5));
             lds_dma16(vb + off, vs_lds + i * kWave * 16);
         }
-        u32x4 kf[4][KS];
+        kwait<VTile<D>::kLoads, KS>(kf);                    // K (and everything before it) has landed
+        if (it == 0) {                                       // so have the Q fragments
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const uint32_t off = (uint32_t)min(tok_of(mt, li), tmax) * (D * 2) + lg * 16;
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = ldg16(kb + off + ks * 64);
+                for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[nt][ks]));
         }
         __builtin_amdgcn_sched_barrier(0);
 
@@ -345,6 +405,8 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, const ListVie
             }
         }
     }
+
+    qwait<NT, KS>(qf);
 
     // ---- merge the waves of this workgroup through LDS -------------------------------
     // Each wave publishes (m, l) per row and its o; after one barrier a thread
@@ -461,7 +523,7 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
     const int b = t2 / a.n_groups;
     const int q0 = grp * a.C;
     const int Cg = min(a.C, a.NQ - q0);
-    const int T = a.seq_len[b];
+    const int T = ld_ro(a.seq_len + b);
     const int nb = (T + kBlock - 1) / kBlock;
 
     ListView L{};
@@ -469,9 +531,7 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
     const size_t row0 = ((size_t)b * a.NQ + q0) * a.H_kv + g;   // block_idx row of the group's first query
     if (a.C == 1 || a.mode == 1) {
         L.gidx = a.block_idx + row0 * a.n_sel_max;
-        L.n = min(max(a.n_sel[row0], 0), a.n_sel_max);
-        if (a.union_count && split == 0 && threadIdx.x == 0 && a.C > 1)
-            a.union_count[((size_t)b * a.n_groups + grp) * a.H_kv + g] = L.n;
+        L.gn = a.n_sel + row0;
     } else {
         // exact union of the group's lists: one bitmap per query over the block range
         const int words = (a.NB_cap + 31) / 32;
@@ -529,10 +589,13 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
         L.lidx = lidx;
         L.lmask = lmask;
         L.n = wsum[blockDim.x];
-        if (a.union_count && split == 0 && threadIdx.x == 0)
-            a.union_count[((size_t)b * a.n_groups + grp) * a.H_kv + g] = L.n;
     }
     run_tile_engine<D, NT>(a, L, b, g, q0, Cg, split, task, smem);
+    // written last: no global store precedes the engine's loads, so the
+    // compiler may read lists and lengths through the scalar cache
+    if (a.union_count && a.C > 1 && split == 0 && threadIdx.x == 0)
+        a.union_count[((size_t)b * a.n_groups + grp) * a.H_kv + g] =
+            L.gidx ? min(max(ld_ro(L.gn), 0), a.n_sel_max) : L.n;
 }
 
 // Split merge as its own launch: one wave per (row group, row).
