@@ -57,7 +57,7 @@ def build_layers(cfg, n_layers, dev):
     for l in range(n_layers):
         t0 = time.time()
         K, V, _ = inputs.kv_layer(cfg, l, device=dev)
-        kt = torch.zeros((cfg.B, cfg.H_kv, cfg.NB, cfg.d), dtype=torch.float32, device=dev)
+        kt = torch.zeros((cfg.B, cfg.H_kv, cfg.NB, cfg.d), dtype=torch.bfloat16, device=dev)
         lo = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
         hi = torch.full((cfg.B,), cfg.T, dtype=torch.int32, device=dev)
         sda.sda_update_compressed_keys(K, kt, lo, hi, cfg.T)
@@ -93,7 +93,7 @@ def cpu_baseline(cfg, layers, budget_s=12.0, n_rows=16):
     for (b, g) in rows:
         kk = O.bf16_to_f64(inputs.bf16_bits(ln["K"][b, g]))
         vv = O.bf16_to_f64(inputs.bf16_bits(ln["V"][b, g]))
-        data[(b, g)] = (kk, vv, O.store_f32(O.compressed_keys(kk, T)))
+        data[(b, g)] = (kk, vv, O.store_bf16(O.compressed_keys(kk, T)))
     timed, done, passes = 0.0, 0, 0
     while timed < budget_s:
         Fd = Fds[passes % L]

@@ -7,7 +7,7 @@ from the tensor shapes, allocates outputs and workspace when they are not
 given, and raises SdaError when the library returns a non-zero status.
 
 Layouts (bf16 given as torch.bfloat16, int32 as torch.int32):
-  K, V      [B, H_kv, T_cap, d]      k_tilde   [B, H_kv, NB_cap, d] float32
+  K, V      [B, H_kv, T_cap, d]      k_tilde   [B, H_kv, NB_cap, d] bfloat16
   f         [B, NQ, H_kv, d]         q         [B, NQ, H_q, d]
   block_idx [B, NQ, H_kv, n_sel_max] n_sel     [B, NQ, H_kv]
   out       [B, NQ, H_q, d] float32  lse       [B, NQ, H_q] float32
@@ -168,7 +168,7 @@ def prepare(fn_py, *a, **kw):
 def sda_update_compressed_keys(k, k_tilde, len_old, len_new, max_new_tokens, stream=None):
     """Recompute the mean-pooled block keys touched by tokens [len_old, len_new)."""
     _need(k, "k", torch.bfloat16, 4)
-    _need(k_tilde, "k_tilde", torch.float32, 4)
+    _need(k_tilde, "k_tilde", torch.bfloat16, 4)
     _need(len_old, "len_old", torch.int32, 1)
     _need(len_new, "len_new", torch.int32, 1)
     B, H, T_cap, d = k.shape
@@ -184,7 +184,7 @@ def sda_score_select(f, k_tilde, seq_len, n_init, n_local, top_k, n_sel_max=None
                      n_sel=None, scores=None, ws=None, stream=None, _prepare=False):
     """Indexer scores, exact top-k and block-set assembly; returns (block_idx, n_sel)."""
     _need(f, "f", torch.bfloat16, 4)
-    _need(k_tilde, "k_tilde", torch.float32, 4)
+    _need(k_tilde, "k_tilde", torch.bfloat16, 4)
     _need(seq_len, "seq_len", torch.int32, 1)
     B, NQ, H, d = f.shape
     NB_cap = k_tilde.shape[2]
@@ -214,7 +214,7 @@ def sda_score_select_multihead(q, k_tilde, seq_len, n_init, n_local, top_k, tau,
                                block_idx=None, n_sel=None, scores=None, ws=None, stream=None):
     """G-head softmax-sum selector (comparator); returns (block_idx, n_sel)."""
     _need(q, "q", torch.bfloat16, 4)
-    _need(k_tilde, "k_tilde", torch.float32, 4)
+    _need(k_tilde, "k_tilde", torch.bfloat16, 4)
     _need(seq_len, "seq_len", torch.int32, 1)
     B, NQ, H_q, d = q.shape
     H = k_tilde.shape[1] if H_kv is None else H_kv

@@ -8,23 +8,46 @@
 //
 // One workgroup (256 lanes) per (row, touched block): the 64 x d bf16 tile is
 // read with 16-byte coalesced loads (a 256-byte key row per 16 lanes at
-// d = 128), summed in fp32 per lane, then reduced across the lanes that share
-// columns through LDS.  HBM-bound: 64*d*2 bytes read, d*4 bytes written.
+// d = 128), summed in fp64 per lane, then reduced across the lanes that share
+// columns through LDS.  A sum of bf16 values is exact in fp64 while the
+// block's non-zero magnitudes stay within a factor 2^39 of each other, so
+// the mean (one correctly rounded fp64 division) and its single rounding to
+// the stored bf16 depend on the keys alone, not on the summation order.
+// HBM-bound: 64*d*2 bytes read, d*2 bytes written.
 #include "sda_device.hpp"
 #include "sda_internal.h"
 
 namespace sda {
 
+// Nearest bf16 (ties to even) of an fp64 value, rounded once: first to fp32
+// by rounding to odd (truncate, then set the last bit if anything was cut),
+// which keeps 16 extra bits and a sticky bit, then to nearest even bf16.
+// Rounding to odd with two or more extra bits before rounding to nearest
+// equals a direct rounding to nearest (Boldo and Melquiond, "Emulation of FMA
+// and correctly rounded sums: proved algorithms using rounding to odd").
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+    if (x != x) return 0x7FC0;                               // NaN
+    const float f = (float)x;                                // nearest; may land past x
+    uint32_t u = __float_as_uint(f);
+    const double fd = (double)f;
+    if (fd != x) {
+        if (fabs(fd) > fabs(x)) u -= 1u;                     // one step back toward zero
+        u |= 1u;                                             // inexact: odd
+    }
+    u += 0x7FFFu + ((u >> 16) & 1u);                         // nearest, ties to even
+    return (uint16_t)(u >> 16);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void ktilde_kernel(const uint16_t* __restrict__ k,
-                                                     float* __restrict__ kt,
+                                                     uint16_t* __restrict__ kt,
                                                      const int32_t* __restrict__ len_old,
                                                      const int32_t* __restrict__ len_new,
                                                      int H_kv, int T_cap, int NB_cap) {
     constexpr int LPR = D / 8;          // lanes per key row (8 bf16 per lane)
     constexpr int RPS = 256 / LPR;      // rows per load step
     constexpr int STEPS = kBlock / RPS;
-    __shared__ float red[RPS][D + 4];
+    __shared__ double red[RPS][D + 2];
 
     const int row = blockIdx.y;                 // b * H_kv + g
     const int b = row / H_kv;
@@ -50,29 +73,29 @@ __global__ __launch_bounds__(256) void ktilde_kernel(const uint16_t* __restrict_
         if (r < n) w[s] = ldg16(base + (size_t)r * D);
         else w[s] = u32x4{0, 0, 0, 0};
     }
-    float acc[8];
+    double acc[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0;
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += bf16lo(w[s][i]);
-            acc[2 * i + 1] += bf16hi(w[s][i]);
+            acc[2 * i] += (double)bf16lo(w[s][i]);
+            acc[2 * i + 1] += (double)bf16hi(w[s][i]);
         }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) red[r0][c8 + i] = acc[i];
     __syncthreads();
     if (tid < D) {
-        float s = 0.f;
+        double s = 0.0;
 #pragma unroll
         for (int r = 0; r < RPS; ++r) s += red[r][tid];
-        kt[((size_t)row * NB_cap + j) * D + tid] = s / (float)n;
+        kt[((size_t)row * NB_cap + j) * D + tid] = f64_to_bf16(s / (double)n);
     }
 }
 
-hipError_t launch_update_compressed_keys(const uint16_t* k, float* kt, const int32_t* len_old,
+hipError_t launch_update_compressed_keys(const uint16_t* k, uint16_t* kt, const int32_t* len_old,
                                          const int32_t* len_new, int max_blocks_per_row, int B,
                                          int H_kv, int d, int T_cap, int NB_cap, hipStream_t s) {
     dim3 grid(max_blocks_per_row, B * H_kv);

@@ -1,21 +1,25 @@
 // Block scoring, exact top-k and block-set assembly.
 //
 // Scoring ([SparDA] note eq. (6) and (9), §4.2 step 2; [SSV] note, NSA
-// selection-branch step 1): s_j = f . K~_j for every block of a row, fp32.
+// selection-branch step 1): s_j = f . K~_j for every block of a row, fp32
+// sums of exact bf16 x bf16 products.
 // One workgroup per (batch, KV head, 256-block chunk, vector tile): the
-// chunk of K~ (fp32, 512 bytes per block at d = 128) is streamed once and
+// chunk of K~ (bf16, 256 bytes per block at d = 128) is streamed once and
 // scored against every vector of the tile.  Sixteen lanes share a block row
-// (two 16-byte loads each, 256 contiguous bytes per half row across the
-// sixteen lanes); the 16-lane partial sums are reduced with DPP.  The same
+// (one 16-byte load each at d = 128, 8 bytes at d = 64); the 16-lane partial
+// sums are reduced with DPP.  The same
 // kernel serves the G-head comparator, whose vectors are the G query heads
 // of a KV group (eq. (8)).
 //
-// Selection ([SparDA] eq. (3), eq. (6); §4.2 step 2): one workgroup per row.
+// Selection as its own launch ([SparDA] eq. (3), eq. (6); §4.2 step 2), used
+// when the in-launch selection below does not apply: one workgroup per row.
 // Keys are the order-preserving uint32 image of the fp32 score; an 8-bit
 // radix select over the candidates (blocks neither initial nor local) finds
 // the k-th largest key, equal keys go to the lower block index, and an
 // ordered compaction writes init U local U top-k ascending, padded with -1.
 #include <math.h>
+
+#include <type_traits>
 
 #include "sda_device.hpp"
 #include "sda_internal.h"
@@ -212,7 +216,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
 // block is within its chunk's top-k, so the merge is exact.
 struct ScoreArgs {
     const uint16_t* vec;
-    const float* kt;
+    const uint16_t* kt;      // bf16 [B, H_kv, NB_cap, D]
     const int32_t* seq_len;
     float* out;
     int NQ, H_kv, VPR, NB_cap;
@@ -284,7 +288,8 @@ __device__ __forceinline__ void merge_round(const uint64_t* src, int nl, int len
 
 template <int D, int NV, bool FUSED>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-    constexpr int HALVES = D / 64;          // 16-byte loads per lane per block
+    constexpr int EPL = D / 16;             // bf16 elements per lane of one pooled key (16 lanes per key)
+    using KLoad = typename std::conditional<EPL == 8, u32x4, u32x2>::type;
     const int row = blockIdx.y;             // b * H_kv + g
     const int b = row / a.H_kv, g = row - (row / a.H_kv) * a.H_kv;
     const int nb = min((a.seq_len[b] + kBlock - 1) / kBlock, a.NB_cap);
@@ -298,56 +303,49 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     __shared__ float sc[FUSED ? NV : 1][FUSED ? kChunk : 1];
 
     if (j0 < nb) {
-        // this lane's slice of each vector: dims 4*li..+4 and 64+4*li..+4
-        float fv[NV][HALVES * 4];
+        // this lane's slice of each vector: dims EPL*li .. EPL*li + EPL
+        float fv[NV][EPL];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const int vi = v0 + v;
             const int q = vi / a.VPR, hv = g * a.VPR + (vi - (vi / a.VPR) * a.VPR);
             if (vi < nvec) {
-                const uint16_t* p = a.vec + (((size_t)b * a.NQ + q) * H_vec + hv) * D;
+                const KLoad w = *reinterpret_cast<const KLoad*>(a.vec + (((size_t)b * a.NQ + q) * H_vec + hv) * D +
+                                                                 li * EPL);
+                const uint32_t* wp = reinterpret_cast<const uint32_t*>(&w);
 #pragma unroll
-                for (int h = 0; h < HALVES; ++h) {
-                    const uint2 w = *reinterpret_cast<const uint2*>(p + h * 64 + li * 4);
-                    fv[v][h * 4 + 0] = bf16lo(w.x);
-                    fv[v][h * 4 + 1] = bf16hi(w.x);
-                    fv[v][h * 4 + 2] = bf16lo(w.y);
-                    fv[v][h * 4 + 3] = bf16hi(w.y);
+                for (int i = 0; i < EPL / 2; ++i) {
+                    fv[v][2 * i] = bf16lo(wp[i]);
+                    fv[v][2 * i + 1] = bf16hi(wp[i]);
                 }
             } else {
 #pragma unroll
-                for (int i = 0; i < HALVES * 4; ++i) fv[v][i] = 0.f;
+                for (int i = 0; i < EPL; ++i) fv[v][i] = 0.f;
             }
         }
 
-        const float* ktr = a.kt + (size_t)row * a.NB_cap * D;
-        constexpr int UNR = 4;                       // steps in flight
+        const uint16_t* ktr = a.kt + (size_t)row * a.NB_cap * D + li * EPL;
+        constexpr int UNR = 8;                       // steps in flight
         constexpr int STEPS = kChunk / 16;           // 16 blocks per workgroup step
         for (int s0 = 0; s0 < STEPS; s0 += UNR) {
-            floatx4 kv[UNR][HALVES];
+            KLoad kv[UNR];
             int jj[UNR];
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
                 jj[u] = j0 + (s0 + u) * 16 + wave * 4 + (lane >> 4);
-                const bool ok = jj[u] < nb;
-#pragma unroll
-                for (int h = 0; h < HALVES; ++h) {
-                    if (ok) kv[u][h] = __builtin_nontemporal_load(
-                                reinterpret_cast<const floatx4*>(ktr + (size_t)jj[u] * D + h * 64 + li * 4));
-                    else kv[u][h] = floatx4{0.f, 0.f, 0.f, 0.f};
-                }
+                if (jj[u] < nb) kv[u] = __builtin_nontemporal_load(reinterpret_cast<const KLoad*>(ktr + (size_t)jj[u] * D));
+                else kv[u] = KLoad{};
             }
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
+                const uint32_t* kp = reinterpret_cast<const uint32_t*>(&kv[u]);
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
                     float acc = 0.f;
 #pragma unroll
-                    for (int h = 0; h < HALVES; ++h) {
-                        acc = fmaf(fv[v][h * 4 + 0], kv[u][h][0], acc);
-                        acc = fmaf(fv[v][h * 4 + 1], kv[u][h][1], acc);
-                        acc = fmaf(fv[v][h * 4 + 2], kv[u][h][2], acc);
-                        acc = fmaf(fv[v][h * 4 + 3], kv[u][h][3], acc);
+                    for (int i = 0; i < EPL / 2; ++i) {
+                        acc = fmaf(fv[v][2 * i], bf16lo(kp[i]), acc);
+                        acc = fmaf(fv[v][2 * i + 1], bf16hi(kp[i]), acc);
                     }
                     acc = row16_sum(acc) * a.mult;
                     const int vi = v0 + v;
@@ -478,7 +476,7 @@ bool fused_select_ok(int NB_cap, int top_k) {
     return top_k >= 1 && top_k <= kFusedTopK && score_chunks(NB_cap) <= kFusedChunks;
 }
 
-hipError_t launch_score_select(const uint16_t* f, const float* kt, const SelectArgs& sel, int B, int d,
+hipError_t launch_score_select(const uint16_t* f, const uint16_t* kt, const SelectArgs& sel, int B, int d,
                                float* scores_opt, float* scores_ws, uint64_t* cand, int* counters,
                                hipStream_t s) {
     if (cand && counters) {
@@ -538,7 +536,7 @@ __global__ __launch_bounds__(256) void softmax_sum_kernel(const float* __restric
     }
 }
 
-hipError_t launch_multihead_scores(const uint16_t* q, const float* kt, const int32_t* seq_len,
+hipError_t launch_multihead_scores(const uint16_t* q, const uint16_t* kt, const int32_t* seq_len,
                                    int B, int NQ, int H_q, int H_kv, int d, int NB_cap, float tau,
                                    float* z, float* stats, float* scores, hipStream_t s) {
     (void)stats;

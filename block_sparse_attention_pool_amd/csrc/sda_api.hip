@@ -111,7 +111,7 @@ const char* sda_last_error(void) { return g_err.c_str(); }
 const char* sda_version(void) { return "sda 0.1 gfx950"; }
 
 // ---------------------------------------------------------------------------
-sda_status_t sda_update_compressed_keys(const void* k, float* k_tilde, const int32_t* len_old,
+sda_status_t sda_update_compressed_keys(const void* k, void* k_tilde, const int32_t* len_old,
                                         const int32_t* len_new, int max_new_tokens, int B,
                                         int H_kv, int d, int T_cap, int NB_cap, void* stream) {
     REQUIRE(k && k_tilde && len_old && len_new, SDA_ERR_NULL, "update_compressed_keys: null pointer");
@@ -125,7 +125,8 @@ sda_status_t sda_update_compressed_keys(const void* k, float* k_tilde, const int
     if (max_new_tokens == 0) return SDA_OK;
     int blocks = ceil_div(max_new_tokens, kBlock) + 1;
     if (blocks > NB_cap) blocks = NB_cap;
-    return hip_status(launch_update_compressed_keys(static_cast<const uint16_t*>(k), k_tilde, len_old, len_new,
+    return hip_status(launch_update_compressed_keys(static_cast<const uint16_t*>(k), static_cast<uint16_t*>(k_tilde),
+                                                    len_old, len_new,
                                                     blocks, B, H_kv, d, T_cap, NB_cap,
                                                     static_cast<hipStream_t>(stream)),
                       "update_compressed_keys launch");
@@ -149,7 +150,7 @@ size_t sda_score_select_workspace(int B, int NQ, int H_kv, int NB_cap, int top_k
            (size_t)B * H_kv * score_tiles(NQ) * sizeof(int);
 }
 
-static sda_status_t check_select_common(const float* k_tilde, const int32_t* seq_len, int B, int NQ,
+static sda_status_t check_select_common(const void* k_tilde, const int32_t* seq_len, int B, int NQ,
                                         int H_kv, int d, int NB_cap, int n_init, int n_local, int top_k,
                                         int n_sel_max, const int32_t* block_idx, const int32_t* n_sel) {
     REQUIRE(k_tilde && seq_len && block_idx && n_sel, SDA_ERR_NULL, "score_select: null pointer");
@@ -169,7 +170,7 @@ static sda_status_t check_select_common(const float* k_tilde, const int32_t* seq
     return SDA_OK;
 }
 
-sda_status_t sda_score_select(const void* f, const float* k_tilde, const int32_t* seq_len, int B, int NQ,
+sda_status_t sda_score_select(const void* f, const void* k_tilde, const int32_t* seq_len, int B, int NQ,
                               int H_kv, int d, int NB_cap, int n_init, int n_local, int top_k,
                               int n_sel_max, int32_t* block_idx, int32_t* n_sel, float* scores_opt,
                               void* ws, size_t ws_bytes, void* stream) {
@@ -192,7 +193,7 @@ sda_status_t sda_score_select(const void* f, const float* k_tilde, const int32_t
     if (!fused_select_ok(NB_cap, top_k) || env_int("SDA_SELECT_FUSED", 1) == 0) cand = nullptr, counters = nullptr;
     SelectArgs a{seq_len, nullptr, B * NQ * H_kv, NQ, H_kv, NB_cap, n_init, n_local, top_k, n_sel_max,
                  block_idx, n_sel};
-    return hip_status(launch_score_select(static_cast<const uint16_t*>(f), k_tilde, a, B, d, scores_opt, scores_ws,
+    return hip_status(launch_score_select(static_cast<const uint16_t*>(f), static_cast<const uint16_t*>(k_tilde), a, B, d, scores_opt, scores_ws,
                                           cand, counters, static_cast<hipStream_t>(stream)),
                       "score/select launch");
 }
@@ -203,7 +204,7 @@ size_t sda_score_select_multihead_workspace(int B, int NQ, int H_q, int H_kv, in
            0 * (size_t)top_k;
 }
 
-sda_status_t sda_score_select_multihead(const void* q, const float* k_tilde, const int32_t* seq_len, int B,
+sda_status_t sda_score_select_multihead(const void* q, const void* k_tilde, const int32_t* seq_len, int B,
                                         int NQ, int H_q, int H_kv, int d, int NB_cap, int n_init, int n_local,
                                         int top_k, int n_sel_max, float tau, int32_t* block_idx,
                                         int32_t* n_sel, float* scores_opt, void* ws, size_t ws_bytes,
@@ -221,7 +222,7 @@ sda_status_t sda_score_select_multihead(const void* q, const float* k_tilde, con
     float* z = static_cast<float*>(ws);
     float* scores = scores_opt ? scores_opt : z + multihead_ws_floats(B, NQ, H_q, H_kv, NB_cap);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    TRY(hip_status(launch_multihead_scores(static_cast<const uint16_t*>(q), k_tilde, seq_len, B, NQ, H_q, H_kv,
+    TRY(hip_status(launch_multihead_scores(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_tilde), seq_len, B, NQ, H_q, H_kv,
                                            d, NB_cap, tau, z, nullptr, scores, s),
                    "multihead score launch"));
     SelectArgs a{seq_len, scores, B * NQ * H_kv, NQ, H_kv, NB_cap, n_init, n_local, top_k, n_sel_max,

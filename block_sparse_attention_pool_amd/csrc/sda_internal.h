@@ -9,7 +9,7 @@
 namespace sda {
 
 // ---- compressed keys ----------------------------------------------------------
-hipError_t launch_update_compressed_keys(const uint16_t* k, float* kt, const int32_t* len_old,
+hipError_t launch_update_compressed_keys(const uint16_t* k, uint16_t* kt, const int32_t* len_old,
                                          const int32_t* len_new, int max_blocks_per_row, int B,
                                          int H_kv, int d, int T_cap, int NB_cap, hipStream_t s);
 
@@ -26,14 +26,14 @@ struct SelectArgs {
 // one per (b, kv head, vector tile)) the selection runs inside the scoring
 // launch (needs fused_select_ok); otherwise scores go to scores_opt or
 // scores_ws and a second launch selects.
-hipError_t launch_score_select(const uint16_t* f, const float* kt, const SelectArgs& sel, int B, int d,
+hipError_t launch_score_select(const uint16_t* f, const uint16_t* kt, const SelectArgs& sel, int B, int d,
                                float* scores_opt, float* scores_ws, uint64_t* cand, int* counters,
                                hipStream_t s);
 bool fused_select_ok(int NB_cap, int top_k);
 int score_tiles(int NQ);
 // integer from the environment (tuning switches), dflt when unset
 int env_int(const char* name, int dflt);
-hipError_t launch_multihead_scores(const uint16_t* q, const float* kt, const int32_t* seq_len,
+hipError_t launch_multihead_scores(const uint16_t* q, const uint16_t* kt, const int32_t* seq_len,
                                    int B, int NQ, int H_q, int H_kv, int d, int NB_cap, float tau,
                                    float* z, float* stats, float* scores, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);

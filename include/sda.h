@@ -61,10 +61,13 @@ const char* sda_version(void);
 /*
  * Compressed keys: K~[b,g,j,:] = mean of K[b,g,64j : min(64j+64, len), :]
  * ([SparDA] prerequisites §3, eq. (4) with kernel = stride = 64; kept on the
- * GPU and refreshed as tokens are appended, §4.2 step 1 and §4.6).
+ * GPU and refreshed as tokens are appended, §4.2 step 1 and §4.6), stored in
+ * bf16 like the keys: the mean is formed in fp64 (exact sums of bf16 values
+ * whenever a block's non-zero magnitudes lie within a factor 2^39) and
+ * rounded once to the nearest bf16, ties to even.
  *
  *   k        bf16 [B, H_kv, T_cap, d]        keys (read only)
- *   k_tilde  f32  [B, H_kv, NB_cap, d]       updated in place
+ *   k_tilde  bf16 [B, H_kv, NB_cap, d]       updated in place
  *   len_old  i32  [B]  tokens already pooled; len_new i32 [B] tokens now cached
  *
  * Every block touched by tokens [len_old[b], len_new[b]) is recomputed from
@@ -74,7 +77,7 @@ const char* sda_version(void);
  * are truncated).  Device-side guards: len_new is clamped to T_cap and rows
  * with len_new <= len_old are left unchanged.
  */
-sda_status_t sda_update_compressed_keys(const void* k, float* k_tilde,
+sda_status_t sda_update_compressed_keys(const void* k, void* k_tilde,
                                         const int32_t* len_old, const int32_t* len_new,
                                         int max_new_tokens, int B, int H_kv, int d,
                                         int T_cap, int NB_cap, void* stream);
@@ -90,11 +93,12 @@ sda_status_t sda_update_compressed_keys(const void* k, float* k_tilde,
  * layer l's vector scored against layer l+1's compressed keys (eq. (6)).
  *
  *   f          bf16 [B, NQ, H_kv, d]
- *   k_tilde    f32  [B, H_kv, NB_cap, d]
+ *   k_tilde    bf16 [B, H_kv, NB_cap, d]
  *   seq_len    i32  [B]               (1 <= seq_len <= 64 * NB_cap)
  *   block_idx  i32  [B, NQ, H_kv, n_sel_max] out; n_sel i32 [B, NQ, H_kv] out
  *   scores_opt f32  [B, NQ, H_kv, NB_cap] out or NULL (raw scores, entries past nb undefined)
- * n_sel_max >= n_init + n_local + top_k.  Scores are fp32 (fp32 K~, fp32 sums).
+ * n_sel_max >= n_init + n_local + top_k.  Scores are fp32 sums of the exact
+ * bf16 x bf16 products.
  * Workspace: sda_score_select_workspace() bytes, required even with scores_opt.
  * It holds arrival counters: zero-fill it before its first use; every
  * completed call leaves them zero.  Calls sharing a workspace must not overlap
@@ -102,7 +106,7 @@ sda_status_t sda_update_compressed_keys(const void* k, float* k_tilde,
  * scoring launch, otherwise as a second launch; the results are identical.
  */
 size_t sda_score_select_workspace(int B, int NQ, int H_kv, int NB_cap, int top_k);
-sda_status_t sda_score_select(const void* f, const float* k_tilde, const int32_t* seq_len,
+sda_status_t sda_score_select(const void* f, const void* k_tilde, const int32_t* seq_len,
                               int B, int NQ, int H_kv, int d, int NB_cap,
                               int n_init, int n_local, int top_k, int n_sel_max,
                               int32_t* block_idx, int32_t* n_sel, float* scores_opt,
@@ -120,7 +124,7 @@ sda_status_t sda_score_select(const void* f, const float* k_tilde, const int32_t
  * Workspace: sda_score_select_multihead_workspace() bytes.
  */
 size_t sda_score_select_multihead_workspace(int B, int NQ, int H_q, int H_kv, int NB_cap, int top_k);
-sda_status_t sda_score_select_multihead(const void* q, const float* k_tilde, const int32_t* seq_len,
+sda_status_t sda_score_select_multihead(const void* q, const void* k_tilde, const int32_t* seq_len,
                                         int B, int NQ, int H_q, int H_kv, int d, int NB_cap,
                                         int n_init, int n_local, int top_k, int n_sel_max, float tau,
                                         int32_t* block_idx, int32_t* n_sel, float* scores_opt,

@@ -14,10 +14,14 @@ Sources (cited by page title and section/equation):
             Verification (arXiv 2605.19893).
 
 Arithmetic is float64 throughout.  bf16 inputs arrive as uint16 bit patterns
-and are decoded exactly.  Two places store or decide in float32, because the
-kernel's stored tensor or decision is float32 and an integer result must be
-decided in the same precision on both sides:
-  * the compressed key cache is stored rounded to float32 (``store_f32``);
+and are decoded exactly.  Two places store or decide in a narrower format,
+because the kernel's stored tensor or decision is narrower and an integer
+result must be decided in the same precision on both sides:
+  * the compressed key cache is stored in bf16, the KV cache's format: the
+    float64 block mean rounded once to the nearest bf16, ties to even
+    (``store_bf16``).  A block mean of bf16 keys is exact in float64 when the
+    block's non-zero magnitudes lie within a factor 2^39 of each other, so
+    the stored bits are then a function of the keys alone;
   * top-k ranks block scores after rounding them to float32
     (``decision_scores``); equal float32 scores go to the lower block index.
 
@@ -48,9 +52,17 @@ def bf16_to_f64(bits):
     return b.view(np.float32).astype(np.float64)
 
 
-def store_f32(x):
-    """Round float64 values to the float32 the compressed-key cache stores."""
-    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+def store_bf16(x):
+    """Round float64 values to the nearest bf16 (8 significant bits, 8-bit
+    exponent), ties to even, returned as float64: the compressed-key cache's
+    stored values.  Below the normal range the grid stays at 2^-133 (bf16
+    subnormals); beyond the largest finite bf16 the result is +-inf."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                      # |x| = m * 2^e, 0.5 <= m < 1
+    e = np.maximum(e, -125)                 # the grid of the smallest binade
+    r = np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)   # rint: ties to even
+    big = np.abs(r) >= 2.0 ** 128
+    return np.where(big, np.copysign(np.inf, x), r)
 
 
 def decision_scores(s):

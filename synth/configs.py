@@ -52,7 +52,8 @@ class Config:
         return self.rows * self.n_sel * BLOCK * self.d * 2 * 2
 
     def ktilde_bytes(self):
-        return self.B * self.H_kv * self.NB * self.d * 4
+        """Compressed keys of one layer (bf16): the bytes one scoring pass reads."""
+        return self.B * self.H_kv * self.NB * self.d * 2
 
 
 CONFIGS = {

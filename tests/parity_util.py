@@ -34,10 +34,10 @@ def f64(t):
 # ---------------------------------------------------------------------------
 
 def oracle_kt(K, T, rows):
-    """Oracle compressed keys (as stored: fp32, held in float64) per (b, g)."""
+    """Oracle compressed keys (as stored: bf16, held in float64) per (b, g)."""
     out = {}
     for (b, g) in rows:
-        out[(b, g)] = O.store_f32(O.compressed_keys(f64(K[b, g, :T]), T))
+        out[(b, g)] = O.store_bf16(O.compressed_keys(f64(K[b, g, :T]), T))
     return out
 
 
@@ -126,7 +126,7 @@ def oracle_decode(Qd, rows_kv, b, q, g, G, blocks, T, scale):
 def gpu_ktilde(K, T, NB_cap=None):
     B, H, Tc, d = K.shape
     NB_cap = NB_cap or -(-Tc // 64)
-    kt = torch.zeros((B, H, NB_cap, d), dtype=torch.float32, device=K.device)
+    kt = torch.zeros((B, H, NB_cap, d), dtype=torch.bfloat16, device=K.device)
     lo = torch.zeros(B, dtype=torch.int32, device=K.device)
     hi = torch.full((B,), T, dtype=torch.int32, device=K.device)
     sda.sda_update_compressed_keys(K, kt, lo, hi, T)

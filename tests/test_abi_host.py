@@ -178,5 +178,6 @@ def test_python_binding_rejects_bad_tensors():
                                        torch.zeros(1, dtype=torch.int32), 64)
     kb = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):                                        # CPU tensors are refused
-        sda.sda_update_compressed_keys(kb, torch.zeros((1, 2, 1, 64)), torch.zeros(1, dtype=torch.int32),
+        sda.sda_update_compressed_keys(kb, torch.zeros((1, 2, 1, 64), dtype=torch.bfloat16),
+                                       torch.zeros(1, dtype=torch.int32),
                                        torch.zeros(1, dtype=torch.int32), 64)

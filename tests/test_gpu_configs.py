@@ -76,7 +76,7 @@ def test_c2_llama8b_shaped_full():
     _say("c2: redrawn rows", int((att > 0).sum()))
     ktg = gpu_ktilde(K, cfg.T)
     for (b, g) in kv_rows:
-        assert np.abs(ktg[b, g].double().cpu().numpy() - kt[(b, g)]).max() < 1e-6
+        assert np.array_equal(ktg[b, g].double().cpu().numpy(), kt[(b, g)])      # bit for bit
     bi, ns = sda.sda_score_select(F.to(DEV), ktg, seq(cfg), cfg.n_init, cfg.n_local, cfg.top_k)
     want = oracle_select(cfg, O.bf16_to_f64(bits(F)), kt, rows)
     assert _mismatches(bi, ns, want) == []
@@ -104,7 +104,7 @@ def test_c3_70b_shaped_128k():
     F, att = tie_free_indexer(cfg, 0, kt, sample)          # F of layer l scores layer l+1
     ktg = gpu_ktilde(K, cfg.T)
     for (b, _, g) in sample:
-        assert np.abs(ktg[b, g].double().cpu().numpy() - kt[(b, g)]).max() < 1e-6
+        assert np.array_equal(ktg[b, g].double().cpu().numpy(), kt[(b, g)])      # bit for bit
     bi, ns = sda.sda_score_select(F.to(DEV), ktg, seq(cfg), cfg.n_init, cfg.n_local, cfg.top_k)
     want = oracle_select(cfg, O.bf16_to_f64(bits(F)), kt, sample)
     assert _mismatches(bi, ns, want) == []

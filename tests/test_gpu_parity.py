@@ -58,7 +58,7 @@ def test_c1_full_path():
     _say("c1: compressed keys")
     ktg = gpu_ktilde(Kg, cfg.T)
     for (b, g) in kv_rows:
-        assert np.abs(ktg[b, g].double().cpu().numpy() - kt[(b, g)]).max() < 1e-6
+        assert np.array_equal(ktg[b, g].double().cpu().numpy(), kt[(b, g)])      # bit for bit
     rows = rows_of(cfg)
     F, _ = tie_free_indexer(cfg, 0, kt, rows)
     want = oracle_select(cfg, O.bf16_to_f64(bits(F)), kt, rows)
@@ -122,7 +122,7 @@ def test_ktilde_partial_block_and_incremental_update():
     bulk = gpu_ktilde(Kg, T1)
     nb = O.num_blocks(T1)
     for g in range(2):
-        assert np.abs(bulk[0, g, :nb].double().cpu().numpy() - kt0[(0, g)]).max() < 1e-6
+        assert np.array_equal(bulk[0, g, :nb].double().cpu().numpy(), kt0[(0, g)])   # bit for bit
     # token-by-token on the GPU equals the bulk build bit for bit
     inc = gpu_ktilde(Kg, T0)
     for t in range(T0, T1):
@@ -130,12 +130,15 @@ def test_ktilde_partial_block_and_incremental_update():
         hi = torch.tensor([t + 1], dtype=torch.int32, device=DEV)
         sda.sda_update_compressed_keys(Kg, inc, lo, hi, 1)
     assert torch.equal(inc[:, :, :nb], bulk[:, :, :nb])
-    # and stays within fp32 noise of the oracle's running-mean update
+    # and is the bf16 rounding of the oracle's running-mean update: within half
+    # a bf16 ulp of it (plus the running mean's own fp64 noise)
     kk = f64(K[0, 0, :T1])
     run = O.compressed_keys(kk, T0)
     for t in range(T0, T1):
         run = O.append_token(run, t, kk[t])
-    assert np.abs(inc[0, 0, :nb].double().cpu().numpy() - run).max() < 1e-6
+    got = inc[0, 0, :nb].double().cpu().numpy()
+    half_ulp = np.ldexp(1.0, np.frexp(np.abs(got) + 2.0 ** -133)[1] - 9)
+    assert np.all(np.abs(got - run) <= half_ulp * (1 + 1e-9) + 1e-12)
 
 
 # ---------------------------------------------------------------------------
@@ -143,9 +146,9 @@ def test_ktilde_partial_block_and_incremental_update():
 # ---------------------------------------------------------------------------
 
 def _select_direct(kt_np, F_np, T, n_init, n_local, k):
-    """Run score_select on a hand-made K~ (float32) and F (float32 -> bf16)."""
+    """Run score_select on a hand-made K~ and F (both rounded to bf16)."""
     B, H, NB, d = kt_np.shape
-    ktg = torch.from_numpy(kt_np.astype(np.float32)).to(DEV)
+    ktg = torch.from_numpy(O.store_bf16(kt_np)).to(torch.bfloat16).to(DEV)
     Fb = inputs.to_bf16(F_np)
     bi, ns = sda.sda_score_select(Fb.to(DEV), ktg, torch.full((B,), T, dtype=torch.int32, device=DEV),
                                   n_init, n_local, k)
@@ -162,7 +165,7 @@ def test_select_small_and_degenerate(T, k):
     bi, ns, Fd = _select_direct(kt, F, T, 1, 2, k)
     nb = O.num_blocks(T)
     for g in range(2):
-        want, _ = O.select_row(Fd[0, 0, g], O.store_f32(kt[0, g, :nb]), 1, 2, k)
+        want, _ = O.select_row(Fd[0, 0, g], O.store_bf16(kt[0, g, :nb]), 1, 2, k)
         n = int(ns[0, 0, g])
         assert n == len(want)
         assert list(bi[0, 0, g, :n]) == list(want)
@@ -182,7 +185,7 @@ def test_select_long_rows(NB, T, n_init, n_local, k):
     bi, ns, Fd = _select_direct(kt, F, T, n_init, n_local, k)
     nb = O.num_blocks(T)
     for g in range(2):
-        want, _ = O.select_row(Fd[0, 0, g], O.store_f32(kt[0, g, :nb]), n_init, n_local, k)
+        want, _ = O.select_row(Fd[0, 0, g], O.store_bf16(kt[0, g, :nb]), n_init, n_local, k)
         n = int(ns[0, 0, g])
         assert list(bi[0, 0, g, :n]) == list(want)
         assert np.all(bi[0, 0, g, n:] == -1)
@@ -229,7 +232,7 @@ def test_select_ties_go_to_lower_index():
     F[0, 0, 0] = kt[0, 0, 7] * 50                          # they score highest
     bi, ns, Fd = _select_direct(kt, F, NB * 64, 1, 2, 4)
     assert list(bi[0, 0, 0, :ns[0, 0, 0]]) == [0, 7, 40, 90, 91, 298, 299]
-    want, _ = O.select_row(Fd[0, 0, 0], O.store_f32(kt[0, 0]), 1, 2, 4)
+    want, _ = O.select_row(Fd[0, 0, 0], O.store_bf16(kt[0, 0]), 1, 2, 4)
     assert list(want) == [0, 7, 40, 90, 91, 298, 299]
 
 

@@ -28,6 +28,27 @@ def _param_pin(fn, *args):
     return lambda: fn(*args)
 
 
+@pytest.mark.parametrize("kind", ["truncate", "half_up", "via_float32", "seven_bits"])
+def test_mutant_store_bf16(monkeypatch, kind):
+    real = impl.store_bf16
+
+    def bad(x):
+        x = np.asarray(x, dtype=np.float64)
+        _, e = np.frexp(x)
+        e = np.maximum(e, -125)
+        y = np.ldexp(x, 8 - e)
+        if kind == "truncate":
+            return np.ldexp(np.trunc(y), e - 8)
+        if kind == "half_up":
+            return np.ldexp(np.floor(np.abs(y) + 0.5) * np.sign(y), e - 8)
+        if kind == "via_float32":          # double rounding through float32
+            return real(x.astype(np.float32).astype(np.float64))
+        return np.ldexp(np.rint(np.ldexp(x, 7 - e)), e - 7)
+    _patch(monkeypatch, "store_bf16", bad)
+    assert _fails(pins.test_store_bf16_hand_cases, pins.test_store_bf16_matches_torch_on_float32_values,
+                  pins.test_store_bf16_nearest_brute_force)
+
+
 def test_mutant_pool_divides_by_full_block(monkeypatch):
     def bad(k, T, block=64):
         nb = impl.num_blocks(T, block)

@@ -36,6 +36,46 @@ def test_bf16_decode_exact():
     assert np.array_equal(O.bf16_to_f64(b), t.to(torch.float64).numpy())
 
 
+def test_store_bf16_hand_cases():
+    # grid points stay; halfway cases go to the even neighbour; the ulp of
+    # [1, 2) is 2^-7 and of [2^-126, 2^-125) is 2^-133 (as of the subnormals)
+    u = 2.0 ** -7
+    x = np.array([1.0, 1.0 + u, 1.0 + u / 2, 1.0 + 3 * u / 2, 1.0 + u / 2 + 2.0 ** -40,
+                  -1.0 - u / 2, 3.0, 2.0 ** -126, 2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -134,
+                  0.0, -0.0, 65504.0])
+    want = [1.0, 1.0 + u, 1.0, 1.0 + 2 * u, 1.0 + u, -1.0, 3.0, 2.0 ** -126, 2.0 ** -133, 0.0,
+            2 * 2.0 ** -133, 0.0, -0.0, 65536.0]
+    got = O.store_bf16(x)
+    assert list(got) == want
+    assert np.signbit(got[12])
+    big = (2.0 - 2.0 ** -8) * 2.0 ** 127                    # halfway to 2^128: rounds up, overflows
+    assert O.store_bf16(np.array([big, -big, (2.0 - 2.0 ** -7) * 2.0 ** 127])).tolist() == \
+        [np.inf, -np.inf, (2.0 - 2.0 ** -7) * 2.0 ** 127]
+
+
+def test_store_bf16_matches_torch_on_float32_values():
+    # on values that are exactly float32, one rounding float32 -> bf16 is the
+    # same as float64 -> bf16; torch's conversion rounds to nearest even
+    v = (rng(3).standard_normal(20000) * np.exp(rng(4).uniform(-30, 30, 20000))).astype(np.float32)
+    v[:8] = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -130, 0.0, 7.0, 1e-40, 3e38],
+                     dtype=np.float32)
+    t = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.store_bf16(v.astype(np.float64)), t)
+
+
+def test_store_bf16_nearest_brute_force():
+    # every result is the nearest of the two neighbouring bf16 values (the
+    # even one on a tie), found here by walking the bf16 bit patterns
+    x = rng(5).standard_normal(3000) * 10.0 ** rng(6).integers(-20, 20, 3000)
+    r = O.store_bf16(x)
+    for xi, ri in zip(x, r):
+        b = int(np.array([ri], dtype=np.float32).view(np.uint32)[0]) >> 16
+        assert np.float32(ri).view(np.uint32) & 0xFFFF == 0          # a bf16 value
+        lo, hi = sorted([O.bf16_to_f64(np.array([b - 1], np.uint16))[0] if b & 0x7FFF else ri,
+                         O.bf16_to_f64(np.array([b + 1], np.uint16))[0]])
+        assert abs(xi - ri) <= min(abs(xi - lo), abs(xi - hi))
+
+
 def test_compressed_keys_constant_block():
     k = np.zeros((256, 8))
     for j in range(4):

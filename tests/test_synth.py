@@ -42,5 +42,5 @@ def test_config_byte_counts():
     c3 = synth.get_config(3)
     assert c3.n_sel == 35 and c3.NB == 2048
     assert c3.selected_kv_bytes() == 73_400_320
-    assert c3.ktilde_bytes() == 67_108_864
+    assert c3.ktilde_bytes() == 33_554_432
     assert synth.get_config(1).selected_kv_bytes() == 360_448
