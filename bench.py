@@ -6,14 +6,17 @@ indexer vectors of layer l score layer l+1's compressed keys, top-k picks
 the blocks (sda_score_select), and the query heads of layer l+1 attend to
 them (sda_sparse_decode).  Steps walk a ring of distinct layers whose K/V,
 compressed keys and vectors are all resident in HBM, so every step reads
-cold data as a real layer stack does (the ring is larger than the L2 and
-Infinity caches together).
+cold data as a real layer stack does (the ring of 8 layers touches 0.86 GB
+per pass, well beyond the L2 and Infinity caches together).
 
 Prints one JSON line.  `value` is whole-job queries/s over the timed steps
 (one query = one sequence's decode token); `roofline` prices the decode
 call (attention kernel + split combine) against the 8 TB/s HBM peak on its
 algorithmic bytes (the selected K/V blocks); `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.
+oracle on a bounded sample of the same workload; `rows` measures the other
+rows of the hot path (compressed-key build and per-token refresh, the G-head
+comparator, grouped verification decode, offloaded gather) at their own
+workloads, each against its roofline with the oracle timed beside it.
 
   python bench.py [--steps K] [--warmup W] [--config 3] [--layers L]
   python bench.py --copy-calibration     (plain copy of known size, for counter scaling)
@@ -119,6 +122,278 @@ def cpu_baseline(cfg, layers, budget_s=12.0, n_rows=16):
     }
 
 
+# ---------------------------------------------------------------------------
+# the other rows of the hot path, each at its own workload
+# ---------------------------------------------------------------------------
+
+def graph_time(fn, reps=30, copies=8):
+    """Mean device seconds per call of fn (which must not allocate), from a
+    graph of `copies` calls replayed `reps` times between two HIP events."""
+    warm = torch.cuda.Stream()
+    warm.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(warm):
+        fn()
+    torch.cuda.current_stream().wait_stream(warm)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(copies):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (reps * copies)
+
+
+def eager_time(fn, reps=10):
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
+def oracle_time(fn, budget_s=1.5):
+    """Seconds per call of an oracle function (one thread), repeated for about budget_s."""
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    n, t = 0, 0.0
+    while t < budget_s:
+        t0 = time.perf_counter()
+        fn()
+        t += time.perf_counter() - t0
+        n += 1
+    if limiter is not None and hasattr(limiter, "unregister"):
+        limiter.unregister()
+    return t / n
+
+
+def hbm(nbytes, sec):
+    gbs = nbytes / sec / 1e9
+    return {"achieved_gbs": gbs, "peak_gbs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,
+            "algorithmic_bytes": int(nbytes)}
+
+
+def measure_rows(cfg, layers):
+    """Rows a1, a5, a6 and a7 of the hot path, each timed on the GPU against
+    its roofline with the CPU oracle timed beside it on a small sample."""
+    import oracle as O
+    dev = "cuda"
+    rows = {}
+    T, d, G = cfg.T, cfg.d, cfg.G
+    scale = 1.0 / math.sqrt(d)
+    ln = layers[1 % len(layers)]
+
+    # a1: compressed keys of one 128K layer (bulk build) and the per-token refresh
+    kt = torch.zeros_like(ln["kt"])
+    zero = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+    full = torch.full((cfg.B,), T, dtype=torch.int32, device=dev)
+    prev = torch.full((cfg.B,), T - 1, dtype=torch.int32, device=dev)
+    t_build = eager_time(lambda: sda.sda_update_compressed_keys(ln["K"], kt, zero, full, T), reps=5)
+    t_tok = graph_time(lambda: sda.sda_update_compressed_keys(ln["K"], kt, prev, full, 1))
+    kk = O.bf16_to_f64(inputs.bf16_bits(ln["K"][0, 0]))
+    t_or = oracle_time(lambda: O.store_bf16(O.compressed_keys(kk, T)))
+    nrow = cfg.B * cfg.H_kv
+    rows["a1_compressed_keys"] = {
+        "workload": f"{cfg.name}: K~ of {nrow} (batch, KV head) rows x {cfg.NB} blocks",
+        "build_us": t_build * 1e6, "build_roofline": hbm(cfg.B * cfg.H_kv * T * d * 2 + cfg.ktilde_bytes(), t_build),
+        "per_token_update_us": t_tok * 1e6,
+        "per_token_update_roofline": hbm(nrow * (64 * d * 2 + d * 2), t_tok),
+        "oracle_rows_per_s": 1.0 / t_or, "gpu_rows_per_s": nrow / t_build,
+    }
+
+    # a7: the G-head comparator selector on the same layer
+    nsm = cfg.n_init + cfg.n_local + cfg.top_k
+    bi = torch.empty((cfg.B, 1, cfg.H_kv, nsm), dtype=torch.int32, device=dev)
+    ns = torch.empty((cfg.B, 1, cfg.H_kv), dtype=torch.int32, device=dev)
+    wsm = torch.zeros(sda.lib().sda_score_select_multihead_workspace(cfg.B, 1, cfg.H_q, cfg.H_kv, cfg.NB,
+                                                                    cfg.top_k), dtype=torch.uint8, device=dev)
+    tau = math.sqrt(d)
+    t_mh = graph_time(lambda: sda.sda_score_select_multihead(ln["Q"], ln["kt"], full, cfg.n_init, cfg.n_local,
+                                                             cfg.top_k, tau, block_idx=bi, n_sel=ns, ws=wsm))
+    Qd = O.bf16_to_f64(inputs.bf16_bits(ln["Q"][0, 0, :G]))
+    ktd = O.store_bf16(O.compressed_keys(kk, T))
+    t_or = oracle_time(lambda: O.select_row_multihead(Qd, ktd, cfg.n_init, cfg.n_local, cfg.top_k, tau))
+    rows["a7_comparator"] = {
+        "workload": f"{cfg.name}: G = {G} heads per KV group, tau = sqrt(d)",
+        "us": t_mh * 1e6, "roofline": hbm(cfg.ktilde_bytes(), t_mh),
+        "oracle_rows_per_s": 1.0 / t_or, "gpu_rows_per_s": nrow / t_mh,
+    }
+    rows["a5_grouped"] = measure_grouped(O)
+    rows["a6_offload"] = measure_offload(O)
+    return rows
+
+
+def chain_lists(rng, NB, n, C, keep):
+    """Block lists of C consecutive queries built as a chain: query c+1 keeps
+    `keep` of query c's n blocks and adds n - keep blocks new to the group, so
+    the group's union has exactly n + (C - 1)(n - keep) blocks."""
+    pool = rng.permutation(NB)
+    used = n
+    lists = [np.sort(pool[:n])]
+    for _ in range(1, C):
+        kept = rng.choice(lists[-1], keep, replace=False)
+        new = pool[used:used + n - keep]
+        used += n - keep
+        lists.append(np.sort(np.concatenate([kept, new])))
+    return lists
+
+
+def measure_grouped(O):
+    """a5 at the draft-verification workload: C = 4 queries per group share one
+    pass over their merged block set (gamma = 0.75 by chain construction)."""
+    cfg = synth.get_config(4)
+    dev = "cuda"
+    K, V, _ = inputs.kv_layer(cfg, 0, device=dev)
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0, sigma=0.5), dev)
+    n, C = cfg.top_k, cfg.group_C
+    keep = int(round(0.75 * n))
+    rng = np.random.default_rng(20260624 + 4)
+    bi_np = np.zeros((cfg.B, cfg.NQ, cfg.H_kv, n), dtype=np.int32)
+    for b in range(cfg.B):
+        for g in range(cfg.H_kv):
+            for grp in range(cfg.NQ // C):
+                for c, lst in enumerate(chain_lists(rng, cfg.NB, n, C, keep)):
+                    bi_np[b, grp * C + c, g] = lst
+    bi = torch.from_numpy(bi_np).to(dev)
+    ns = torch.full((cfg.B, cfg.NQ, cfg.H_kv), n, dtype=torch.int32, device=dev)
+    seq = torch.full((cfg.B,), cfg.T, dtype=torch.int32, device=dev)
+    out = torch.empty((cfg.B, cfg.NQ, cfg.H_q, cfg.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, cfg.NQ, cfg.H_q), dtype=torch.float32, device=dev)
+    uc = torch.empty((cfg.B, cfg.NQ // C, cfg.H_kv), dtype=torch.int32, device=dev)
+    res = {"workload": f"{cfg.name}: B={cfg.B}, NQ={cfg.NQ}, C={C}, H_q={cfg.H_q}, H_kv={cfg.H_kv}, "
+                       f"T={cfg.T}, top-{n} per query, adjacent overlap gamma = {keep}/{n} (chain-built lists)"}
+    blk = 64 * cfg.d * 2 * 2
+    for mode, name in ((sda.SDA_GROUP_EXACT, "mode_A"), (sda.SDA_GROUP_SHARED_REP, "mode_B")):
+        ws = torch.zeros(sda.lib().sda_grouped_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d,
+                                                                cfg.NB, C, mode, 0), dtype=torch.uint8,
+                         device=dev)
+        t = graph_time(lambda: sda.sda_grouped_decode(Q, K, V, seq, bi, ns, C, mode=mode, out=out, lse=lse,
+                                                      union_count=uc, ws=ws))
+        blocks = int(uc.sum().item())
+        res[name] = {"us": t * 1e6, "blocks_loaded": blocks, "roofline": hbm(blocks * blk, t)}
+    ws = torch.zeros(sda.lib().sda_sparse_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d, 0),
+                     dtype=torch.uint8, device=dev)
+    t = graph_time(lambda: sda.sda_sparse_decode(Q, K, V, seq, bi, ns, out=out, lse=lse, ws=ws))
+    per_q = cfg.B * cfg.NQ * cfg.H_kv * n
+    res["per_query"] = {"us": t * 1e6, "blocks_loaded": per_q, "roofline": hbm(per_q * blk, t)}
+    res["measured_saving_mode_A"] = 1.0 - res["mode_A"]["blocks_loaded"] / per_q
+    res["formula_saving"] = 1.0 - O.union_size_formula(n, C, keep / n) / (n * C)
+    res["speedup_mode_A_vs_per_query"] = res["per_query"]["us"] / res["mode_A"]["us"]
+    # oracle: one group (C queries x G heads) of one (batch, KV head), mode A
+    kk = O.bf16_to_f64(inputs.bf16_bits(K[0, 0, :cfg.T]))
+    vv = O.bf16_to_f64(inputs.bf16_bits(V[0, 0, :cfg.T]))
+    qd = O.bf16_to_f64(inputs.bf16_bits(Q[0, :C, :cfg.G])).reshape(C, cfg.G, cfg.d)
+    lists = [bi_np[0, c, 0] for c in range(C)]
+    t_or = oracle_time(lambda: O.grouped_row(qd, kk, vv, lists, cfg.T, 1.0 / math.sqrt(cfg.d), O.MODE_EXACT))
+    groups = cfg.B * (cfg.NQ // C) * cfg.H_kv
+    res["oracle_groups_per_s"] = 1.0 / t_or
+    res["gpu_groups_per_s"] = groups / (res["mode_A"]["us"] * 1e-6)
+    del K, V
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_offload(O, n_host_layers=2, chain=8):
+    """a6 at the offload workload: each layer's selected K/V blocks are copied
+    from pinned host memory to a device stage on a side stream while the
+    previous layer's decode runs on the main stream."""
+    cfg = synth.get_config(5)
+    dev = "cuda"
+    T = cfg.T
+    nsm = cfg.n_init + cfg.n_local + cfg.top_k
+    host = []
+    for l in range(n_host_layers):
+        K, V, _ = inputs.kv_layer(cfg, l, device=dev)
+        Kh = torch.empty(K.shape, dtype=torch.bfloat16, pin_memory=True)
+        Vh = torch.empty(V.shape, dtype=torch.bfloat16, pin_memory=True)
+        Kh.copy_(K)
+        Vh.copy_(V)
+        host.append((Kh, Vh))
+        if l == 0:
+            kk = O.bf16_to_f64(inputs.bf16_bits(K[0, 0, :T]))
+            vv = O.bf16_to_f64(inputs.bf16_bits(V[0, 0, :T]))
+        del K, V
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(20260624 + 5)
+    lists = []
+    for l in range(chain):
+        bi_np = np.zeros((cfg.B, 1, cfg.H_kv, nsm), dtype=np.int32)
+        for b in range(cfg.B):
+            for g in range(cfg.H_kv):
+                mid = np.sort(rng.choice(np.arange(cfg.n_init, cfg.NB - cfg.n_local), cfg.top_k, replace=False))
+                bi_np[b, 0, g] = np.concatenate([np.arange(cfg.n_init), mid, np.arange(cfg.NB - cfg.n_local, cfg.NB)])
+        lists.append(torch.from_numpy(bi_np).to(dev))
+    ns = torch.full((cfg.B, 1, cfg.H_kv), nsm, dtype=torch.int32, device=dev)
+    seq = torch.full((cfg.B,), T, dtype=torch.int32, device=dev)
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0), dev)
+    stage_shape = (cfg.B, cfg.H_kv, nsm * 64, cfg.d)
+    stages = [(torch.empty(stage_shape, dtype=torch.bfloat16, device=dev),
+               torch.empty(stage_shape, dtype=torch.bfloat16, device=dev),
+               torch.empty((cfg.B, 1, cfg.H_kv, nsm), dtype=torch.int32, device=dev)) for _ in range(2)]
+    out = torch.empty((cfg.B, 1, cfg.H_q, cfg.d), dtype=torch.float32, device=dev)
+    ws = torch.zeros(sda.lib().sda_sparse_decode_workspace(cfg.B, 1, cfg.H_q, cfg.H_kv, nsm, cfg.d, 0),
+                     dtype=torch.uint8, device=dev)
+
+    def gather(l, st):
+        kh, vh = host[l % n_host_layers]
+        sda.sda_gather_blocks(kh, vh, lists[l], ns, k_stage=st[0], v_stage=st[1], slot=st[2], max_workgroups=256)
+
+    def decode(st, l):
+        sda.sda_sparse_decode(Q, st[0], st[1], seq, lists[l], ns, slot=st[2], out=out, ws=ws)
+
+    t_gather = eager_time(lambda: gather(0, stages[0]), reps=5)
+    gather(0, stages[0])
+    t_dec = eager_time(lambda: decode(stages[0], 0), reps=10)
+    # host-link reference: a plain pinned -> device copy of the same size
+    nbytes = cfg.selected_kv_bytes()
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, pin_memory=True)
+    dst = torch.empty_like(src, device=dev)
+    t_copy = eager_time(lambda: dst.copy_(src, non_blocking=True), reps=5)
+    # the chain: gather layer l+1 on the side stream while layer l decodes
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    gather(0, stages[0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for l in range(chain):
+        if l + 1 < chain:
+            side.wait_stream(main)                      # stage (l+1) % 2 is free again
+            with torch.cuda.stream(side):
+                gather(l + 1, stages[(l + 1) % 2])
+        decode(stages[l % 2], l)
+        main.wait_stream(side)
+    torch.cuda.synchronize()
+    t_chain = time.perf_counter() - t0
+    link = nbytes / t_copy / 1e9
+    gbs = nbytes / t_gather / 1e9
+    t_or = oracle_time(lambda: O.decode_row(O.bf16_to_f64(inputs.bf16_bits(Q[0, 0, :cfg.G].cpu())), kk, vv,
+                                            lists[0][0, 0, 0].cpu().numpy(), T, 1.0 / math.sqrt(cfg.d)))
+    return {
+        "workload": f"{cfg.name}: B={cfg.B}, H_q={cfg.H_q}, H_kv={cfg.H_kv}, T={T}, {nsm} blocks per row from "
+                    f"pinned host memory ({n_host_layers} distinct host layers, chain of {chain})",
+        "gather_us": t_gather * 1e6,
+        "gather_roofline": {"bound": "host link", "achieved_gbs": gbs, "peak_gbs": link,
+                            "peak_kind": "measured pinned host -> device copy of the same size",
+                            "frac": gbs / link, "algorithmic_bytes": int(nbytes)},
+        "decode_from_stage_us": t_dec * 1e6,
+        "chain_ms": t_chain * 1e3,
+        "overlap": (chain * t_dec + (chain - 1) * t_gather) / t_chain,
+        "oracle_rows_per_s": 1.0 / t_or, "gpu_rows_per_s": cfg.B * cfg.H_kv / t_dec,
+    }
+
+
 def copy_calibration(nbytes=1 << 30):
     dev = "cuda"
     a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -187,9 +462,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3)
-    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="skip the other hot-path rows (a1, a5, a6, a7)")
     ap.add_argument("--no-graph", action="store_true", help="time eager prepared calls (for counter runs)")
     ap.add_argument("--overlap", action="store_true",
                     help="run layer l+1's selection on a side stream beside layer l's decode "
@@ -348,6 +624,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, layers)
+    if not args.no_rows:
+        res["rows"] = measure_rows(cfg, layers)
     print(json.dumps(res))
 
 

@@ -29,6 +29,7 @@
 //       tile is permuted so each lane already holds the 8 consecutive tokens
 //       its PV operand needs.
 // HBM-bound: 64*d*2*2 bytes per block and row group; fp32 accumulate.
+#include <limits.h>
 #include <math.h>
 #include <stdlib.h>
 
@@ -533,62 +534,70 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
         L.gidx = a.block_idx + row0 * a.n_sel_max;
         L.gn = a.n_sel + row0;
     } else {
-        // exact union of the group's lists: one bitmap per query over the block range
-        const int words = (a.NB_cap + 31) / 32;
-        uint32_t* bm = reinterpret_cast<uint32_t*>(after_v);               // [C][words]
-        int32_t* lidx = reinterpret_cast<int32_t*>(bm + (size_t)a.C * words);
-        uint32_t* lmask = reinterpret_cast<uint32_t*>(lidx + (size_t)a.C * a.n_sel_max);
-        uint32_t* wsum = lmask + (size_t)a.C * a.n_sel_max;                  // [blockDim.x + 1]
-        for (int i = threadIdx.x; i < Cg * words; i += blockDim.x) bm[i] = 0u;
-        __syncthreads();
-        for (int i = threadIdx.x; i < Cg * a.n_sel_max; i += blockDim.x) {
-            const int c = i / a.n_sel_max, e = i - (i / a.n_sel_max) * a.n_sel_max;
+        // exact union of the group's ascending lists: entry (c, e) joins the
+        // union unless an earlier query of the group, or the entry before it,
+        // lists the same block; its membership mask comes from a binary
+        // search in every list.  Joining entries are compacted in (c, e) order.
+        const int nsm = a.n_sel_max;
+        const int W = blockDim.x / kWave;
+        int32_t* lst = reinterpret_cast<int32_t*>(after_v);                          // [C][nsm]
+        int32_t* lidx = lst + (size_t)a.C * nsm;                                     // [C * nsm]
+        uint32_t* lmask = reinterpret_cast<uint32_t*>(lidx + (size_t)a.C * nsm);     // [C * nsm]
+        int* wtot = reinterpret_cast<int*>(lmask + (size_t)a.C * nsm);              // [W]
+        const int n_ent = Cg * nsm;
+        for (int i = threadIdx.x; i < n_ent; i += blockDim.x) {
+            const int c = i / nsm, e = i - (i / nsm) * nsm;
             const size_t rc = row0 + (size_t)c * a.H_kv;
-            if (e < a.n_sel[rc]) {
-                const int j = a.block_idx[rc * a.n_sel_max + e];
-                if (j >= 0 && j < nb && j < a.NB_cap) atomicOr(&bm[c * words + (j >> 5)], 1u << (j & 31));
+            const int n_c = min(max(a.n_sel[rc], 0), nsm);
+            int j = (e < n_c) ? a.block_idx[rc * nsm + e] : INT_MAX;   // past the count: sorts last
+            if (j < 0 || j >= nb || j >= a.NB_cap) j = INT_MAX;
+            lst[i] = j;
+        }
+        __syncthreads();
+        auto contains = [&](int c, int v) {
+            const int32_t* Lc = lst + c * nsm;
+            int lo = 0, hi = nsm;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (Lc[mid] < v) lo = mid + 1;
+                else hi = mid;
             }
-        }
-        __syncthreads();
-        // union bits per thread-owned word range, exclusive scan, emit ascending
-        const int wpt = (words + blockDim.x - 1) / blockDim.x;
-        const int w0 = threadIdx.x * wpt;
-        int cnt = 0;
-        for (int w = w0; w < min(w0 + wpt, words); ++w) {
-            uint32_t u = 0;
-            for (int c = 0; c < Cg; ++c) u |= bm[c * words + w];
-            cnt += __popc(u);
-        }
-        wsum[threadIdx.x] = cnt;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            int run = 0;
-            for (int t = 0; t < (int)blockDim.x; ++t) {
-                const int v = wsum[t];
-                wsum[t] = run;
-                run += v;
+            return lo < nsm && Lc[lo] == v;
+        };
+        const int lane = __lane_id(), wv = threadIdx.x / kWave;
+        int base = 0;
+        for (int i0 = 0; i0 < n_ent; i0 += blockDim.x) {
+            const int i = i0 + threadIdx.x;
+            bool first = false;
+            uint32_t mk = 0;
+            int v = INT_MAX;
+            if (i < n_ent) {
+                const int c = i / nsm, e = i - (i / nsm) * nsm;
+                v = lst[i];
+                first = v != INT_MAX && !(e > 0 && lst[i - 1] == v);
+                for (int c2 = 0; c2 < c && first; ++c2) first = !contains(c2, v);
+                if (first)
+                    for (int c2 = 0; c2 < Cg; ++c2) mk |= (uint32_t)contains(c2, v) << c2;
             }
-            wsum[blockDim.x] = run;
-        }
-        __syncthreads();
-        int pos = wsum[threadIdx.x];
-        for (int w = w0; w < min(w0 + wpt, words); ++w) {
-            uint32_t u = 0;
-            for (int c = 0; c < Cg; ++c) u |= bm[c * words + w];
-            while (u) {
-                const int bit = __ffs(u) - 1;
-                u &= u - 1;
-                uint32_t mk = 0;
-                for (int c = 0; c < Cg; ++c) mk |= ((bm[c * words + w] >> bit) & 1u) << c;
-                lidx[pos] = w * 32 + bit;
+            const uint64_t bal = __ballot(first);
+            if (lane == 0) wtot[wv] = __popcll(bal);
+            __syncthreads();
+            int off = base, tot = 0;
+            for (int w2 = 0; w2 < W; ++w2) {
+                off += (w2 < wv) ? wtot[w2] : 0;
+                tot += wtot[w2];
+            }
+            if (first) {
+                const int pos = off + __popcll(bal & ((1ull << lane) - 1ull));
+                lidx[pos] = v;
                 lmask[pos] = mk;
-                ++pos;
             }
+            base += tot;
+            __syncthreads();                                   // wtot is rewritten by the next chunk
         }
-        __syncthreads();
         L.lidx = lidx;
         L.lmask = lmask;
-        L.n = wsum[blockDim.x];
+        L.n = base;
     }
     run_tile_engine<D, NT>(a, L, b, g, q0, Cg, split, task, smem);
     // written last: no global store precedes the engine's loads, so the
@@ -624,38 +633,25 @@ int attn_rows_pad(int C, int G) { return (C * G <= 16) ? 16 : 32; }
 constexpr int kCUs = 256;                  // MI355X compute units
 constexpr size_t kLdsPerCU = 160 * 1024;
 
+// LDS of the exact union: the C lists, the union ids and masks, per-wave counts
 static size_t union_extra(int C, int mode, int NB_cap, int n_sel_max, int W) {
+    (void)NB_cap;
     if (C <= 1 || mode != 0) return 0;
-    return (size_t)C * ((NB_cap + 31) / 32) * 4 + (size_t)C * n_sel_max * 8 + ((size_t)W * 64 + 1) * 4;
+    return (size_t)C * n_sel_max * 3 * 4 + (size_t)W * 4;
 }
 
 // Launch shape of the attention kernel: W waves per workgroup, n_split
-// workgroups per row group.  Each wave owns one block of its split, so
-// W = ceil(list / n_split); among the shapes whose workgroups fit the LDS,
-// keep those that need the fewest dispatch rounds, prefer ones that give
-// every CU a workgroup, then the fewest splits (less partial traffic).
+// workgroups per row group; a wave walks its split's entries W apart, so it
+// handles ceil(list / (n_split * W)) blocks one after another.  Cost of a
+// shape = dispatch rounds x blocks per wave.  Among the cheapest, keep the one
+// with the most blocks in flight in the first round (at most all of them),
+// then the one that reaches the most CUs, then the fewest splits (less
+// partial traffic), then the fewest waves.
 AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode, int NB_cap, int n_sel_max,
                    int split_k) {
     const int max_w = rows_pad == 16 ? kMaxWaves : 4;
     const int slots = rows_pad == 16 ? 12 : 4;          // resident waves per CU (VGPR-bound)
-    AttnPlan best{1, 1};
-    long long best_rounds = -1;
-    bool best_full = false;
-    auto consider = [&](int ns, int W) {
-        const size_t lds = smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W);
-        if (lds > kLdsPerCU) return;
-        int per_cu = (int)(kLdsPerCU / lds);
-        if (per_cu * W > slots) per_cu = slots / W;
-        if (per_cu < 1) per_cu = 1;
-        const long long wgs = (long long)tasks * ns;
-        const long long rounds = (wgs + (long long)kCUs * per_cu - 1) / ((long long)kCUs * per_cu);
-        const bool full = wgs >= kCUs;
-        if (best_rounds < 0 || rounds < best_rounds || (rounds == best_rounds && full && !best_full)) {
-            best = AttnPlan{W, ns};
-            best_rounds = rounds;
-            best_full = full;
-        }
-    };
+    if (list_max < 1) list_max = 1;
     if (split_k > 0) {
         int W = (list_max + split_k - 1) / split_k;
         if (W > max_w) W = max_w;
@@ -663,10 +659,33 @@ AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode
         return AttnPlan{W, split_k};
     }
     static const int force_w = env_int("SDA_ATTN_WAVES", 0);
+    AttnPlan best{1, 1};
+    long long best_cost = -1, best_flight = -1, best_cus = -1;
+    const long long total = (long long)tasks * list_max;
     for (int ns = 1; ns <= list_max; ++ns) {
-        const int W = (list_max + ns - 1) / ns;
-        if (W > max_w || (force_w && W != force_w)) continue;
-        consider(ns, W);
+        const int per_split = (list_max + ns - 1) / ns;
+        for (int W = 1; W <= min(max_w, per_split); ++W) {
+            if (force_w && W != force_w) continue;
+            const size_t lds = smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W);
+            if (lds > kLdsPerCU) continue;
+            int per_cu = (int)(kLdsPerCU / lds);
+            if (per_cu * W > slots) per_cu = slots / W;
+            if (per_cu < 1) per_cu = 1;
+            const long long wgs = (long long)tasks * ns;
+            const long long cap = (long long)kCUs * per_cu;
+            const long long rounds = (wgs + cap - 1) / cap;
+            const long long cost = rounds * ((per_split + W - 1) / W);
+            long long flight = (wgs < cap ? wgs : cap) * W;
+            if (flight > total) flight = total;
+            const long long cus = wgs < kCUs ? wgs : kCUs;
+            if (best_cost < 0 || cost < best_cost ||
+                (cost == best_cost && (flight > best_flight || (flight == best_flight && cus > best_cus)))) {
+                best = AttnPlan{W, ns};
+                best_cost = cost;
+                best_flight = flight;
+                best_cus = cus;
+            }
+        }
     }
     return best;
 }
