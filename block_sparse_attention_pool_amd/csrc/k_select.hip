@@ -224,8 +224,10 @@ struct ScoreArgs {
     SelectArgs sel;          // FUSED only
     uint64_t* cand;          // FUSED: [B*NQ*H_kv, chunks, top_k] keys
     int* counters;           // FUSED: [B*H_kv*vector tiles], zero between calls
+    float* stats;            // scores-and-stats mode: [vector rows, chunks] (max, sum of exp(s - max))
 };
 
+constexpr int kScoresOnly = 0, kFusedSelect = 1, kScoresAndStats = 2;   // score_kernel modes
 constexpr int kFusedTopK = 64;       // longest per-chunk list the fused selection keeps
 constexpr int kFusedChunks = 16;     // most chunks it merges (NB_cap <= 4096)
 
@@ -286,8 +288,111 @@ __device__ __forceinline__ void merge_round(const uint64_t* src, int nl, int len
     }
 }
 
-template <int D, int NV, bool FUSED>
+// The selection inside a scoring launch: sc[v][t] holds the score of block
+// j0 + t for vector v0 + v of kv row `row` = b * H_kv + g (the grid is
+// (chunks, B * H_kv, vector tiles)).  Level 1 ranks the chunk, level 2 (the
+// last chunk workgroup of the row and tile to arrive) merges the chunk lists
+// and writes the block sets; see the comment at ScoreArgs.
+template <int NV>
+__device__ __forceinline__ void select_tail(const SelectArgs& s, uint64_t* cand, int* counters,
+                                            const float (*sc)[kChunk], int b, int g, int row, int NQ,
+                                            int H_kv, int nvec, int v0, int j0, int nb) {
+    const int lane = __lane_id();
+    const int wave = threadIdx.x / kWave;
+    constexpr int WS = kWave + 1;                      // list strides (odd: spread over banks)
+    __shared__ uint64_t wl[4 * WS];                    // four sorted wave lists of 64
+    __shared__ uint64_t bufA[(kFusedTopK + 1) * kFusedChunks];
+    __shared__ uint64_t bufB[(kFusedTopK + 1) * kFusedChunks / 2];
+    __shared__ __align__(16) int sel_j[kFusedTopK];
+    __shared__ int last;
+    const int K = s.top_k;
+    const int KS = K | 1;                              // odd list stride >= K
+    const int nch = gridDim.x;
+    const int tid = threadIdx.x;
+    const int lo = min(s.n_init, nb);                 // candidates are [lo, hi)
+    const int hi = max(lo, nb - s.n_local);
+    __syncthreads();                                   // sc complete
+
+    // level 1: rank inside each wave, then two rounds of pairwise merges
+    // give this chunk's best K keys in rank order
+    const int j = j0 + tid;
+    const bool valid = j >= lo && j < hi;
+    const int nvw = __popcll(__ballot(valid));         // valid lanes of this wave
+    for (int v = 0; v < NV; ++v) {
+        const int vi = v0 + v;
+        if (vi >= nvec) break;                         // uniform over the workgroup
+        const uint64_t key = valid ? block_key(sc[v][tid], j) : 0ull;
+        const int wr = wave_rank(key);                 // valid keys: distinct ranks < nvw
+        if (valid) wl[wave * WS + wr] = key;
+        if (lane >= nvw) wl[wave * WS + lane] = 0ull;
+        __syncthreads();
+        merge_round(wl, 4, kWave, WS, bufA, KS, K);
+        __syncthreads();
+        merge_round(bufA, 2, K, KS, bufB, KS, K);
+        __syncthreads();
+        uint64_t* dst = cand + ((size_t)((b * NQ + vi) * H_kv + g) * nch + blockIdx.x) * K;
+        if (tid < K) __hip_atomic_store(dst + tid, bufB[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the next vector's writes to wl / bufA / bufB come after two more barriers
+    }
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's lists have landed
+    __syncthreads();
+    int* cnt = counters + (size_t)row * gridDim.z + blockIdx.z;
+    if (tid == 0) last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nch - 1;
+    __syncthreads();
+    if (!last) return;
+
+    // level 2: pairwise merge rounds over the nch chunk lists of each vector,
+    // then the block set
+    const int kk = min(K, hi - lo);
+    for (int v = 0; v < NV; ++v) {
+        const int vi = v0 + v;
+        if (vi >= nvec) break;
+        const int vrow = (b * NQ + vi) * H_kv + g;
+        const uint64_t* src = cand + (size_t)vrow * nch * K;
+        for (int i = tid; i < nch * K; i += 256) {
+            const int c = i / K;
+            bufA[c * KS + (i - c * K)] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        uint64_t* cur = bufA;
+        uint64_t* nxt = bufB;
+        for (int nl = nch; nl > 1; nl = (nl + 1) >> 1) {
+            merge_round(cur, nl, K, KS, nxt, KS, K);
+            __syncthreads();
+            uint64_t* t = cur; cur = nxt; nxt = t;
+        }
+        if (tid < kk) sel_j[tid] = (int)(0xFFFFFFFFu - (uint32_t)cur[tid]);
+        __syncthreads();
+        int32_t* out = s.block_idx + (size_t)vrow * s.n_sel_max;
+        for (int i = tid; i < lo; i += 256) out[i] = i;                 // initial blocks
+        if (tid < kk) {                                                  // top-k, ascending
+            const int jt = sel_j[tid];
+            int pos = 0;
+#pragma unroll
+            for (int u = 0; u < kFusedTopK; u += 4) {
+                const int4 q = *reinterpret_cast<const int4*>(sel_j + u);
+                pos += (u + 0 < kk && q.x < jt) + (u + 1 < kk && q.y < jt) +
+                       (u + 2 < kk && q.z < jt) + (u + 3 < kk && q.w < jt);
+            }
+            out[lo + pos] = jt;
+        }
+        for (int i = tid; i < nb - hi; i += 256) out[lo + kk + i] = hi + i;  // local blocks
+        const int total = lo + kk + (nb - hi);
+        for (int p = total + tid; p < s.n_sel_max; p += 256) out[p] = -1;
+        if (tid == 0) s.n_sel[vrow] = total;
+        __syncthreads();                               // bufA / sel_j are reused
+    }
+    if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// MODE kScoresAndStats (the G-head comparator): scores go to `out` as in
+// kScoresOnly, and each chunk workgroup also writes, per vector, the max of
+// its chunk's scores and the sum of exp(score - max) over the chunk.
+template <int D, int NV, int MODE>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+    constexpr bool FUSED = MODE == kFusedSelect;
+    constexpr bool LDS_SC = MODE != kScoresOnly;
     constexpr int EPL = D / 16;             // bf16 elements per lane of one pooled key (16 lanes per key)
     using KLoad = typename std::conditional<EPL == 8, u32x4, u32x2>::type;
     const int row = blockIdx.y;             // b * H_kv + g
@@ -300,7 +405,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     const int lane = __lane_id();
     const int li = lane & 15;
     const int wave = threadIdx.x / kWave;
-    __shared__ float sc[FUSED ? NV : 1][FUSED ? kChunk : 1];
+    __shared__ float sc[LDS_SC ? NV : 1][LDS_SC ? kChunk : 1];
 
     if (j0 < nb) {
         // this lane's slice of each vector: dims EPL*li .. EPL*li + EPL
@@ -350,7 +455,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
                     acc = row16_sum(acc) * a.mult;
                     const int vi = v0 + v;
                     if (li == 0 && jj[u] < nb && vi < nvec) {
-                        if constexpr (FUSED) sc[v][jj[u] - j0] = acc;
+                        if constexpr (LDS_SC) sc[v][jj[u] - j0] = acc;
                         if (!FUSED || a.out) {
                             const int q = vi / a.VPR, hv = g * a.VPR + (vi - (vi / a.VPR) * a.VPR);
                             a.out[(((size_t)b * a.NQ + q) * H_vec + hv) * a.NB_cap + jj[u]] = acc;
@@ -361,108 +466,47 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         }
     }
 
-    if constexpr (FUSED) {
-        constexpr int WS = kWave + 1;                      // list strides (odd: spread over banks)
-        __shared__ uint64_t wl[4 * WS];                    // four sorted wave lists of 64
-        __shared__ uint64_t bufA[(kFusedTopK + 1) * kFusedChunks];
-        __shared__ uint64_t bufB[(kFusedTopK + 1) * kFusedChunks / 2];
-        __shared__ __align__(16) int sel_j[kFusedTopK];
-        __shared__ int last;
-        const SelectArgs& s = a.sel;
-        const int K = s.top_k;
-        const int KS = K | 1;                              // odd list stride >= K
-        const int nch = gridDim.x;
-        const int tid = threadIdx.x;
-        const int lo = min(s.n_init, nb);                 // candidates are [lo, hi)
-        const int hi = max(lo, nb - s.n_local);
+    if constexpr (FUSED)
+        select_tail<NV>(a.sel, a.cand, a.counters, sc, b, g, row, a.NQ, a.H_kv, nvec, v0, j0, nb);
+    if constexpr (MODE == kScoresAndStats) {
         __syncthreads();                                   // sc complete
-
-        // level 1: rank inside each wave, then two rounds of pairwise merges
-        // give this chunk's best K keys in rank order
-        const int j = j0 + tid;
-        const bool valid = j >= lo && j < hi;
-        const int nvw = __popcll(__ballot(valid));         // valid lanes of this wave
-        for (int v = 0; v < NV; ++v) {
-            const int vi = v0 + v;
-            if (vi >= nvec) break;                         // uniform over the workgroup
-            const uint64_t key = valid ? block_key(sc[v][tid], j) : 0ull;
-            const int wr = wave_rank(key);                 // valid keys: distinct ranks < nvw
-            if (valid) wl[wave * WS + wr] = key;
-            if (lane >= nvw) wl[wave * WS + lane] = 0ull;
-            __syncthreads();
-            merge_round(wl, 4, kWave, WS, bufA, KS, K);
-            __syncthreads();
-            merge_round(bufA, 2, K, KS, bufB, KS, K);
-            __syncthreads();
-            uint64_t* dst = a.cand + ((size_t)((b * a.NQ + vi) * a.H_kv + g) * nch + blockIdx.x) * K;
-            if (tid < K) __hip_atomic_store(dst + tid, bufB[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            // the next vector's writes to wl / bufA / bufB come after two more barriers
-        }
-
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's lists have landed
-        __syncthreads();
-        int* cnt = a.counters + (size_t)row * gridDim.z + blockIdx.z;
-        if (tid == 0) last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nch - 1;
-        __syncthreads();
-        if (!last) return;
-
-        // level 2: pairwise merge rounds over the nch chunk lists of each vector,
-        // then the block set
-        const int kk = min(K, hi - lo);
-        for (int v = 0; v < NV; ++v) {
+        for (int v = wave; v < NV; v += 4) {               // one wave per vector
             const int vi = v0 + v;
             if (vi >= nvec) break;
-            const int vrow = (b * a.NQ + vi) * a.H_kv + g;
-            const uint64_t* src = a.cand + (size_t)vrow * nch * K;
-            for (int i = tid; i < nch * K; i += 256) {
-                const int c = i / K;
-                bufA[c * KS + (i - c * K)] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            __syncthreads();
-            uint64_t* cur = bufA;
-            uint64_t* nxt = bufB;
-            for (int nl = nch; nl > 1; nl = (nl + 1) >> 1) {
-                merge_round(cur, nl, K, KS, nxt, KS, K);
-                __syncthreads();
-                uint64_t* t = cur; cur = nxt; nxt = t;
-            }
-            if (tid < kk) sel_j[tid] = (int)(0xFFFFFFFFu - (uint32_t)cur[tid]);
-            __syncthreads();
-            int32_t* out = s.block_idx + (size_t)vrow * s.n_sel_max;
-            for (int i = tid; i < lo; i += 256) out[i] = i;                 // initial blocks
-            if (tid < kk) {                                                  // top-k, ascending
-                const int jt = sel_j[tid];
-                int pos = 0;
+            float m = -INFINITY;
 #pragma unroll
-                for (int u = 0; u < kFusedTopK; u += 4) {
-                    const int4 q = *reinterpret_cast<const int4*>(sel_j + u);
-                    pos += (u + 0 < kk && q.x < jt) + (u + 1 < kk && q.y < jt) +
-                           (u + 2 < kk && q.z < jt) + (u + 3 < kk && q.w < jt);
-                }
-                out[lo + pos] = jt;
+            for (int i = 0; i < kChunk / kWave; ++i)
+                if (j0 + lane + i * kWave < nb) m = fmaxf(m, sc[v][lane + i * kWave]);
+            for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+            float l = 0.f;
+            if (m != -INFINITY) {
+#pragma unroll
+                for (int i = 0; i < kChunk / kWave; ++i)
+                    if (j0 + lane + i * kWave < nb) l += expf(sc[v][lane + i * kWave] - m);
             }
-            for (int i = tid; i < nb - hi; i += 256) out[lo + kk + i] = hi + i;  // local blocks
-            const int total = lo + kk + (nb - hi);
-            for (int p = total + tid; p < s.n_sel_max; p += 256) out[p] = -1;
-            if (tid == 0) s.n_sel[vrow] = total;
-            __syncthreads();                               // bufA / sel_j are reused
+            for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off, kWave);
+            if (lane == 0) {
+                const int q = vi / a.VPR, hv = g * a.VPR + (vi - (vi / a.VPR) * a.VPR);
+                float* st = a.stats + ((((size_t)b * a.NQ + q) * H_vec + hv) * gridDim.x + blockIdx.x) * 2;
+                st[0] = m;
+                st[1] = l;
+            }
         }
-        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-template <int D, bool FUSED>
+template <int D, int MODE>
 static void launch_score_d(const ScoreArgs& a, int B, hipStream_t s) {
     const int nvec = a.NQ * a.VPR;
     int nv = 1;
     while (nv < nvec && nv < 16) nv *= 2;
     dim3 grid(score_chunks(a.NB_cap), B * a.H_kv, (nvec + nv - 1) / nv), block(256);
     switch (nv) {
-        case 1: hipLaunchKernelGGL((score_kernel<D, 1, FUSED>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((score_kernel<D, 2, FUSED>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((score_kernel<D, 4, FUSED>), grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((score_kernel<D, 8, FUSED>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((score_kernel<D, 16, FUSED>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((score_kernel<D, 1, MODE>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((score_kernel<D, 2, MODE>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((score_kernel<D, 4, MODE>), grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((score_kernel<D, 8, MODE>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((score_kernel<D, 16, MODE>), grid, block, 0, s, a); break;
     }
 }
 
@@ -480,15 +524,15 @@ hipError_t launch_score_select(const uint16_t* f, const uint16_t* kt, const Sele
                                float* scores_opt, float* scores_ws, uint64_t* cand, int* counters,
                                hipStream_t s) {
     if (cand && counters) {
-        ScoreArgs a{f, kt, sel.seq_len, scores_opt, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, cand, counters};
-        if (d == 128) launch_score_d<128, true>(a, B, s);
-        else launch_score_d<64, true>(a, B, s);
+        ScoreArgs a{f, kt, sel.seq_len, scores_opt, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, cand, counters, nullptr};
+        if (d == 128) launch_score_d<128, kFusedSelect>(a, B, s);
+        else launch_score_d<64, kFusedSelect>(a, B, s);
         return hipGetLastError();
     }
     float* scores = scores_opt ? scores_opt : scores_ws;
-    ScoreArgs a{f, kt, sel.seq_len, scores, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, nullptr, nullptr};
-    if (d == 128) launch_score_d<128, false>(a, B, s);
-    else launch_score_d<64, false>(a, B, s);
+    ScoreArgs a{f, kt, sel.seq_len, scores, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, nullptr, nullptr, nullptr};
+    if (d == 128) launch_score_d<128, kScoresOnly>(a, B, s);
+    else launch_score_d<64, kScoresOnly>(a, B, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     SelectArgs sa = sel;
@@ -499,56 +543,81 @@ hipError_t launch_score_select(const uint16_t* f, const uint16_t* kt, const Sele
 // ---------------------------------------------------------------------------
 // G-head comparator: z = q_h . K~_j / tau, then s_j = sum_h softmax_j(z_h)
 // ---------------------------------------------------------------------------
+// Launch 1 is the scoring kernel with the G heads of a KV group as its
+// vectors (mode kScoresAndStats): z to the workspace plus, per head and chunk,
+// the chunk max and the sum of exp(z - max).  Launch 2, one workgroup per
+// (chunk, kv row, query): merges the row's chunk statistics into each head's
+// softmax max M_h and normaliser L_h, forms s_j = sum_h exp(z_hj - M_h) / L_h
+// for its 256 blocks and runs the in-launch selection on them (or writes the
+// scores for the selection launch when that does not apply).
+// floats of [z, padded to 64 floats][chunk statistics, padded to 64 floats]
 size_t multihead_ws_floats(int B, int NQ, int H_q, int H_kv, int NB_cap) {
     (void)H_kv;
-    return (size_t)B * NQ * H_q * NB_cap;     // z
+    const size_t z = ((size_t)B * NQ * H_q * NB_cap + 63) / 64 * 64;
+    const size_t st = ((size_t)B * NQ * H_q * score_chunks(NB_cap) * 2 + 63) / 64 * 64;
+    return z + st;
 }
 
-// one workgroup per row (b, q, g): per head, max and sum of exp over the row's
-// blocks, then the per-block sum over heads of the normalised weights
-__global__ __launch_bounds__(256) void softmax_sum_kernel(const float* __restrict__ z,
-                                                          const int32_t* __restrict__ seq_len,
-                                                          int NQ, int H_kv, int G, int NB_cap,
-                                                          float* __restrict__ scores) {
-    __shared__ float red[4];
-    __shared__ float mh[32], inv_lh[32];
-    const int row = blockIdx.x;                          // (b*NQ + q)*H_kv + g
-    const int b = row / (NQ * H_kv);
-    const int nb = min((seq_len[b] + kBlock - 1) / kBlock, NB_cap);
-    const float* zr = z + (size_t)row * G * NB_cap;      // heads g*G .. g*G+G-1 are contiguous
-    for (int h = 0; h < G; ++h) {
-        float m = -INFINITY;
-        for (int j = threadIdx.x; j < nb; j += 256) m = fmaxf(m, zr[(size_t)h * NB_cap + j]);
-        m = block_reduce_max(m, red);
-        float l = 0.f;
-        for (int j = threadIdx.x; j < nb; j += 256) l += expf(zr[(size_t)h * NB_cap + j] - m);
-        l = block_reduce_sum(l, red);
-        if (threadIdx.x == 0) {
-            mh[h] = m;
-            inv_lh[h] = 1.f / l;
-        }
+template <bool FUSED>
+__global__ __launch_bounds__(256) void mh_select_kernel(const float* __restrict__ z, const float* __restrict__ stats,
+                                                        SelectArgs sel, int H_q, int G, float* scores_out,
+                                                        uint64_t* cand, int* counters) {
+    __shared__ float sc[1][kChunk];
+    __shared__ float mh[16], il[16];
+    const int row = blockIdx.y;                          // b * H_kv + g
+    const int H_kv = sel.H_kv, NQ = sel.NQ, NB_cap = sel.NB_cap;
+    const int b = row / H_kv, g = row - (row / H_kv) * H_kv;
+    const int q = blockIdx.z;
+    const int nch = gridDim.x;
+    const int nb = min((sel.seq_len[b] + kBlock - 1) / kBlock, NB_cap);
+    const int j0 = blockIdx.x * kChunk;
+    const int tid = threadIdx.x;
+    const size_t hrow0 = ((size_t)b * NQ + q) * H_q + (size_t)g * G;   // first head row of the group
+    if (tid < G) {
+        const float* st = stats + (hrow0 + tid) * nch * 2;
+        float M = -INFINITY;
+        for (int c = 0; c < nch; ++c) M = fmaxf(M, st[2 * c]);
+        float L = 0.f;
+        for (int c = 0; c < nch; ++c)
+            if (st[2 * c] != -INFINITY) L += st[2 * c + 1] * expf(st[2 * c] - M);
+        mh[tid] = M;
+        il[tid] = 1.f / L;
     }
     __syncthreads();
-    for (int j = threadIdx.x; j < nb; j += 256) {
-        float acc = 0.f;
-        for (int h = 0; h < G; ++h) acc += expf(zr[(size_t)h * NB_cap + j] - mh[h]) * inv_lh[h];
-        scores[(size_t)row * NB_cap + j] = acc;
+    const int j = j0 + tid;
+    float sv = 0.f;
+    if (j < nb) {
+        for (int h = 0; h < G; ++h) sv += expf(z[(hrow0 + h) * NB_cap + j] - mh[h]) * il[h];
+        const size_t srow = ((size_t)b * NQ + q) * H_kv + g;
+        if (scores_out) scores_out[srow * NB_cap + j] = sv;
     }
+    sc[0][tid] = sv;
+    if constexpr (FUSED) select_tail<1>(sel, cand, counters, sc, b, g, row, NQ, H_kv, NQ, q, j0, nb);
 }
 
-hipError_t launch_multihead_scores(const uint16_t* q, const uint16_t* kt, const int32_t* seq_len,
-                                   int B, int NQ, int H_q, int H_kv, int d, int NB_cap, float tau,
-                                   float* z, float* stats, float* scores, hipStream_t s) {
-    (void)stats;
-    const int G = H_q / H_kv;
-    ScoreArgs a{q, kt, seq_len, z, NQ, H_kv, G, NB_cap, 1.f / tau, SelectArgs{}, nullptr, nullptr};
-    if (d == 128) launch_score_d<128, false>(a, B, s);
-    else launch_score_d<64, false>(a, B, s);
+hipError_t launch_multihead_select(const uint16_t* q, const uint16_t* kt, const SelectArgs& sel, int B, int H_q,
+                                   int d, float tau, float* z, float* stats, float* scores_opt, float* scores_ws,
+                                   uint64_t* cand, int* counters, hipStream_t s) {
+    const int G = H_q / sel.H_kv;
+    ScoreArgs a{q, kt, sel.seq_len, z, sel.NQ, sel.H_kv, G, sel.NB_cap, 1.f / tau, SelectArgs{}, nullptr, nullptr,
+                stats};
+    if (d == 128) launch_score_d<128, kScoresAndStats>(a, B, s);
+    else launch_score_d<64, kScoresAndStats>(a, B, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(softmax_sum_kernel, dim3(B * NQ * H_kv), dim3(256), 0, s, z, seq_len, NQ,
-                       H_kv, G, NB_cap, scores);
-    return hipGetLastError();
+    dim3 grid(score_chunks(sel.NB_cap), B * sel.H_kv, sel.NQ), block(256);
+    if (cand && counters) {
+        hipLaunchKernelGGL(mh_select_kernel<true>, grid, block, 0, s, z, stats, sel, H_q, G, scores_opt, cand,
+                           counters);
+        return hipGetLastError();
+    }
+    float* scores = scores_opt ? scores_opt : scores_ws;
+    hipLaunchKernelGGL(mh_select_kernel<false>, grid, block, 0, s, z, stats, sel, H_q, G, scores, nullptr, nullptr);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SelectArgs sa = sel;
+    sa.scores = scores;
+    return launch_select(sa, s);
 }
 
 }  // namespace sda

@@ -198,10 +198,13 @@ sda_status_t sda_score_select(const void* f, const void* k_tilde, const int32_t*
                       "score/select launch");
 }
 
+// [z f32 and per-chunk statistics][scores f32, B*NQ*H_kv*NB_cap][candidate keys u64
+// (in-launch selection only)][arrival counters i32, B*H_kv*NQ], 256-B aligned regions
 size_t sda_score_select_multihead_workspace(int B, int NQ, int H_q, int H_kv, int NB_cap, int top_k) {
-    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || NB_cap < 1) return 0;
-    return (multihead_ws_floats(B, NQ, H_q, H_kv, NB_cap) + (size_t)B * NQ * H_kv * NB_cap) * sizeof(float) +
-           0 * (size_t)top_k;
+    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || NB_cap < 1 || top_k < 0) return 0;
+    return pad256(multihead_ws_floats(B, NQ, H_q, H_kv, NB_cap) * sizeof(float)) +
+           score_region_bytes(B, NQ, H_kv, NB_cap) + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k) +
+           (size_t)B * H_kv * NQ * sizeof(int);
 }
 
 sda_status_t sda_score_select_multihead(const void* q, const void* k_tilde, const int32_t* seq_len, int B,
@@ -216,18 +219,26 @@ sda_status_t sda_score_select_multihead(const void* q, const void* k_tilde, cons
     REQUIRE(H_q / H_kv <= 16, SDA_ERR_UNSUPPORTED, "comparator supports G <= 16");
     REQUIRE(tau > 0.f && isfinite(tau), SDA_ERR_SHAPE, "tau must be finite and > 0");
     REQUIRE(aligned16(q), SDA_ERR_ALIGN, "q must be 16-byte aligned");
+    REQUIRE((long long)NQ <= kMaxGridYZ, SDA_ERR_SHAPE, "NQ too large");
     const size_t need = sda_score_select_multihead_workspace(B, NQ, H_q, H_kv, NB_cap, top_k);
     REQUIRE(ws && ws_bytes >= need, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, need);
     REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
-    float* z = static_cast<float*>(ws);
-    float* scores = scores_opt ? scores_opt : z + multihead_ws_floats(B, NQ, H_q, H_kv, NB_cap);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    TRY(hip_status(launch_multihead_scores(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_tilde), seq_len, B, NQ, H_q, H_kv,
-                                           d, NB_cap, tau, z, nullptr, scores, s),
-                   "multihead score launch"));
-    SelectArgs a{seq_len, scores, B * NQ * H_kv, NQ, H_kv, NB_cap, n_init, n_local, top_k, n_sel_max,
+    REQUIRE(!scores_opt || aligned4(scores_opt), SDA_ERR_ALIGN, "scores_opt must be 4-byte aligned");
+    char* base = static_cast<char*>(ws);
+    float* z = reinterpret_cast<float*>(base);
+    float* stats = reinterpret_cast<float*>(base + pad256((size_t)B * NQ * H_q * NB_cap * sizeof(float)));
+    size_t off = pad256(multihead_ws_floats(B, NQ, H_q, H_kv, NB_cap) * sizeof(float));
+    float* scores_ws = reinterpret_cast<float*>(base + off);
+    off += score_region_bytes(B, NQ, H_kv, NB_cap);
+    uint64_t* cand = reinterpret_cast<uint64_t*>(base + off);
+    int* counters = reinterpret_cast<int*>(base + off + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k));
+    if (!fused_select_ok(NB_cap, top_k) || env_int("SDA_SELECT_FUSED", 1) == 0) cand = nullptr, counters = nullptr;
+    SelectArgs a{seq_len, nullptr, B * NQ * H_kv, NQ, H_kv, NB_cap, n_init, n_local, top_k, n_sel_max,
                  block_idx, n_sel};
-    return hip_status(launch_select(a, s), "select launch");
+    return hip_status(launch_multihead_select(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_tilde),
+                                              a, B, H_q, d, tau, z, stats, scores_opt, scores_ws, cand, counters,
+                                              static_cast<hipStream_t>(stream)),
+                      "multihead score/select launch");
 }
 
 // ---------------------------------------------------------------------------

@@ -33,9 +33,12 @@ bool fused_select_ok(int NB_cap, int top_k);
 int score_tiles(int NQ);
 // integer from the environment (tuning switches), dflt when unset
 int env_int(const char* name, int dflt);
-hipError_t launch_multihead_scores(const uint16_t* q, const uint16_t* kt, const int32_t* seq_len,
-                                   int B, int NQ, int H_q, int H_kv, int d, int NB_cap, float tau,
-                                   float* z, float* stats, float* scores, hipStream_t s);
+// G-head comparator: scores plus per-chunk softmax statistics, then per-block
+// sums of the heads' softmax weights and the selection (inside the second
+// launch when cand / counters are given, else a third launch)
+hipError_t launch_multihead_select(const uint16_t* q, const uint16_t* kt, const SelectArgs& sel, int B, int H_q,
+                                   int d, float tau, float* z, float* stats, float* scores_opt, float* scores_ws,
+                                   uint64_t* cand, int* counters, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 size_t multihead_ws_floats(int B, int NQ, int H_q, int H_kv, int NB_cap);
 int score_chunks(int NB_cap);

@@ -61,7 +61,10 @@ def test_workspace_sizes(L):
     assert L.sda_score_select_workspace(1, 1, 1, 4097, 8) == 16640 + 4            # too many chunks
     assert L.sda_score_select_workspace(0, 1, 8, 2048, 32) == 0
     # multihead: per-head logits plus the summed scores
-    assert L.sda_score_select_multihead_workspace(8, 1, 64, 8, 2048, 32) == (8 * 64 * 2048 + 8 * 8 * 2048) * 4
+    # multihead: per-head logits and per-chunk softmax statistics, the summed
+    # scores, candidate keys and arrival counters
+    assert L.sda_score_select_multihead_workspace(8, 1, 64, 8, 2048, 32) == \
+        (8 * 64 * 2048 + 8 * 64 * 8 * 2) * 4 + 8 * 8 * 2048 * 4 + 64 * 8 * 32 * 8 + 8 * 8 * 4
     # decode: 256-byte padded arrival counters, then (m, l) + d floats per padded row per split
     def dec(tasks, splits, rows=16, d=128):
         return (tasks * 4 + 255) // 256 * 256 + tasks * splits * rows * (d + 2) * 4

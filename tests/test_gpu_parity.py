@@ -223,6 +223,37 @@ def test_fused_select_matches_select_launch(NQ):
             os.environ["SDA_SELECT_FUSED"] = old
 
 
+@pytest.mark.parametrize("NQ", [1, 3])
+def test_comparator_fused_select_matches_select_launch(NQ):
+    # the comparator's in-launch selection and its selection launch rank the
+    # same summed softmax weights: identical block lists, counters back at zero
+    import os
+    cfg = synth.get_config(2)
+    K, _, _ = inputs.kv_layer(cfg, 0, device=DEV)
+    ktg = gpu_ktilde(K, cfg.T)
+    rng = np.random.default_rng(40 + NQ)
+    Q = inputs.to_bf16(rng.standard_normal((cfg.B, NQ, cfg.H_q, cfg.d))).to(DEV)
+    args = (Q, ktg, seq(cfg), cfg.n_init, cfg.n_local, cfg.top_k, math.sqrt(cfg.d))
+    old = os.environ.get("SDA_SELECT_FUSED")
+    try:
+        os.environ["SDA_SELECT_FUSED"] = "0"
+        ref_bi, ref_ns = sda.sda_score_select_multihead(*args)
+        os.environ["SDA_SELECT_FUSED"] = "1"
+        nbytes = sda.lib().sda_score_select_multihead_workspace(cfg.B, NQ, cfg.H_q, cfg.H_kv, ktg.shape[2],
+                                                                cfg.top_k)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+        for it in range(5):
+            bi, ns = sda.sda_score_select_multihead(*args, ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(bi, ref_bi) and torch.equal(ns, ref_ns), it
+            assert int(ws[nbytes - 4 * cfg.B * cfg.H_kv * NQ:].count_nonzero()) == 0, it
+    finally:
+        if old is None:
+            os.environ.pop("SDA_SELECT_FUSED", None)
+        else:
+            os.environ["SDA_SELECT_FUSED"] = old
+
+
 def test_select_ties_go_to_lower_index():
     rng = np.random.default_rng(5)
     NB, d = 300, 128
