@@ -2,17 +2,20 @@
 """Benchmark: top-k block-sparse decode on one MI355X.
 
 One step = one layer's decode step of the 70B-shaped 128K workload: the
-indexer vectors of layer l score layer l+1's compressed keys, top-k picks
-the blocks (sda_score_select), and the query heads of layer l+1 attend to
-them (sda_sparse_decode).  Steps walk a ring of distinct layers whose K/V,
-compressed keys and vectors are all resident in HBM, so every step reads
-cold data as a real layer stack does (the ring of 8 layers touches 0.86 GB
-per pass, well beyond the L2 and Infinity caches together).
+query heads of layer l attend to their selected blocks, and the indexer
+vectors of layer l score layer l+1's compressed keys and pick its blocks
+(top-k), both in one sda_decode_step call: a scoring launch leaves per-chunk
+candidate lists, and the decode launch merges them into layer l+1's block
+sets (--step separate: sda_score_select then sda_sparse_decode).  Steps
+walk a ring of distinct layers whose K/V, compressed keys and vectors are
+all resident in HBM, so every step reads cold data as a real layer stack
+does (the ring of 8 layers touches 0.86 GB per pass, well beyond the L2 and
+Infinity caches together).
 
 Prints one JSON line.  `value` is whole-job queries/s over the timed steps
 (one query = one sequence's decode token); `roofline` prices the decode
-call (attention kernel + split combine) against the 8 TB/s HBM peak on its
-algorithmic bytes (the selected K/V blocks); `cpu_baseline` times the CPU
+kernel (attention + split merge, timed alone as sda_sparse_decode) against
+the 8 TB/s HBM peak on its algorithmic bytes (the selected K/V blocks); `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload; `rows` measures the other
 rows of the hot path (compressed-key build and per-token refresh, the G-head
 comparator, grouped verification decode, offloaded gather) at their own
@@ -470,6 +473,9 @@ def main():
     ap.add_argument("--overlap", action="store_true",
                     help="run layer l+1's selection on a side stream beside layer l's decode "
                          "(slower on this GPU: the two kernels contend for the same bandwidth and CUs)")
+    ap.add_argument("--step", choices=("fused", "separate"), default="fused",
+                    help="fused: one sda_decode_step call per layer (the decode launch finishes the next "
+                         "layer's selection); separate: sda_score_select then sda_sparse_decode")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--call-reps", type=int, default=50, help="graph replays per per-call timing")
     args = ap.parse_args()
@@ -511,8 +517,30 @@ def main():
         dc, _ = sda.prepare(sda.sda_sparse_decode, ln["Q"], ln["K"], ln["V"], seq, bi[i], ns[i], out=out,
                             lse=lse, split_k=args.split_k, ws=ws_dec)
         calls.append((sc, dc))
+    # the step entry point: position i decodes layer i with bi[i] and selects
+    # layer i+1's blocks (layer i's indexer vectors, layer i+1's compressed keys)
+    ws_step = torch.zeros(sda.lib().sda_decode_step_workspace(cfg.B, cfg.H_q, cfg.H_kv, cfg.d, n_sel_max,
+                                                              args.split_k, cfg.NB, cfg.top_k),
+                          dtype=torch.uint8, device=dev)
+    step_calls = []
+    for i in range(L):
+        lc, ln = layers[i], layers[(i + 1) % L]
+        pc, _ = sda.prepare(sda.sda_decode_step, lc["Q"], lc["K"], lc["V"], seq, bi[i], ns[i], lc["F"], ln["kt"],
+                            seq, cfg.n_init, cfg.n_local, cfg.top_k, block_idx_next=bi[(i + 1) % L],
+                            n_sel_next=ns[(i + 1) % L], out=out, lse=lse, split_k=args.split_k, ws=ws_step)
+        step_calls.append(pc)
+
+    def fused_step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+            ev[1].record()
+        step_calls[i % L].run()
+        if ev is not None:
+            ev[2].record()
 
     def step(i, ev=None):
+        if args.step == "fused" and not args.overlap:
+            return fused_step(i, ev)
         sc, dc = calls[i % L]
         if ev is not None:
             ev[0].record()
@@ -556,6 +584,7 @@ def main():
         steps_timed = args.steps
         t_sel = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
         t_dec = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+        t_step = float((t_sel + t_dec).mean())
     else:
         wall, steps_timed = timed_graph(run_step, L, args.steps)
         # per-launch device time of each call: a graph of the ring's launches of
@@ -563,6 +592,7 @@ def main():
         # stream the graph runs on (inter-kernel gaps included)
         t_sel = np.array([call_time([c[0] for c in calls], args.call_reps)])
         t_dec = np.array([call_time([c[1] for c in calls], args.call_reps)])
+        t_step = call_time(step_calls, args.call_reps)
 
     queries = cfg.B * cfg.NQ
     value = queries * steps_timed / wall
@@ -600,7 +630,10 @@ def main():
             "config_id": cfg.cid,
             "launch": ("eager prepared calls" if args.no_graph else f"HIP graph of the {L}-layer ring, replayed")
                       + (", layer l+1's score_select beside layer l's sparse_decode (two streams)"
-                         if args.overlap else ", score_select then sparse_decode per layer"),
+                         if args.overlap else
+                         ", one sda_decode_step per layer (a scoring launch writes per-chunk candidate lists of "
+                         "layer l+1; layer l's decode launch merges them into l+1's block sets)"
+                         if args.step == "fused" else ", score_select then sparse_decode per layer"),
         },
         "roofline": {
             "bound": "hbm",
@@ -609,12 +642,15 @@ def main():
             "unit": "GB/s",
             "frac": dec_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": "sda_sparse_decode (attn_kernel; splits merged by the last workgroup of each row)",
+            "kernel": "attn_kernel<128, 1> as launched by sda_sparse_decode (splits merged by the last "
+                      "workgroup of each row), timed alone; the step's decode launch is the same kernel with "
+                      "one extra wave's selection merge per workgroup of split 0",
             "algorithmic_bytes_per_launch": dec_bytes,
         },
         "kernels_us": {
             "score_select": t_sel.mean() * 1e6,
             "sparse_decode": t_dec.mean() * 1e6,
+            "decode_step": t_step * 1e6,
             "timing": ("eager: events around each call" if args.no_graph else
                        f"graph of {8 * L} back-to-back launches of the call, {args.call_reps} replays "
                        "between two HIP events"),

@@ -56,6 +56,9 @@ _SIGNATURES = {
                                     _c_void_p]),
     "sda_gather_blocks": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int,
                                    _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p]),
+    "sda_decode_step_workspace": (_c_size_t, [_c_int] * 8),
+    "sda_decode_step": (_c_int, [_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_void_p, _c_void_p, _c_int]
+                        + [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 3 + [_c_size_t, _c_void_p]),
 }
 
 _lib = None
@@ -157,8 +160,8 @@ class PreparedCall:
 
 def prepare(fn_py, *a, **kw):
     """Run a binding function's checks and allocations without launching and
-    return (PreparedCall, outputs); supported for sda_score_select and
-    sda_sparse_decode."""
+    return (PreparedCall, outputs); supported for sda_score_select,
+    sda_sparse_decode and sda_decode_step."""
     kw["_prepare"] = True
     return fn_py(*a, **kw)
 
@@ -267,6 +270,58 @@ def sda_sparse_decode(q, k, v, seq_len, block_idx, n_sel, scale=None, out=None, 
             (out, lse)
     _check(lib().sda_sparse_decode(*args[:-1], _stream(stream)))
     return out, lse
+
+
+def sda_decode_step(q, k, v, seq_len, block_idx, n_sel, f_next, k_tilde_next, seq_len_next, n_init, n_local,
+                    top_k, n_sel_max_next=None, block_idx_next=None, n_sel_next=None, scale=None, out=None,
+                    lse=None, split_k=0, ws=None, stream=None, _prepare=False):
+    """Layer l's decode plus layer l+1's selection (same results as
+    sda_score_select for l+1 then sda_sparse_decode for l); returns
+    (out, lse, block_idx_next, n_sel_next)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(seq_len, "seq_len", torch.int32, 1)
+    _need(block_idx, "block_idx", torch.int32, 4)
+    _need(n_sel, "n_sel", torch.int32, 3)
+    _need(f_next, "f_next", torch.bfloat16, 4)
+    _need(k_tilde_next, "k_tilde_next", torch.bfloat16, 4)
+    _need(seq_len_next, "seq_len_next", torch.int32, 1)
+    B, NQ, H_q, d = q.shape
+    if NQ != 1:
+        raise ValueError("sda_decode_step takes one query per sequence")
+    H_kv, T_cap = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must both be [B, H_kv, T_cap, d] matching q")
+    if f_next.shape != (B, 1, H_kv, d) or k_tilde_next.shape[:2] != (B, H_kv) or k_tilde_next.shape[3] != d:
+        raise ValueError("f_next [B, 1, H_kv, d] and k_tilde_next [B, H_kv, NB_cap, d] must match q and k")
+    n_sel_max = block_idx.shape[3]
+    NB_cap_next = k_tilde_next.shape[2]
+    if n_sel_max_next is None:
+        n_sel_max_next = n_init + n_local + top_k
+    if scale is None:
+        scale = d ** -0.5
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, 1, H_q, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, 1, H_q), dtype=torch.float32, device=dev)
+    if block_idx_next is None:
+        block_idx_next = torch.empty((B, 1, H_kv, n_sel_max_next), dtype=torch.int32, device=dev)
+    if n_sel_next is None:
+        n_sel_next = torch.empty((B, 1, H_kv), dtype=torch.int32, device=dev)
+    nbytes = lib().sda_decode_step_workspace(B, H_q, H_kv, d, n_sel_max, int(split_k), NB_cap_next, top_k)
+    ws, wsb = _workspace(nbytes, dev, ws)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(block_idx), _ptr(n_sel), n_sel_max, T_cap, B, H_q,
+            H_kv, d, float(scale), _ptr(out), _ptr(lse), int(split_k), _ptr(f_next), _ptr(k_tilde_next),
+            _ptr(seq_len_next), NB_cap_next, n_init, n_local, top_k, n_sel_max_next, _ptr(block_idx_next),
+            _ptr(n_sel_next), _ptr(ws), wsb, None)
+    outs = (out, lse, block_idx_next, n_sel_next)
+    if _prepare:
+        return PreparedCall("sda_decode_step", args, (q, k, v, seq_len, block_idx, n_sel, f_next, k_tilde_next,
+                                                       seq_len_next, ws) + outs), outs
+    _check(lib().sda_decode_step(*args[:-1], _stream(stream)))
+    return outs
 
 
 def sda_grouped_decode(q, k, v, seq_len, block_idx, n_sel, group_C, mode=SDA_GROUP_EXACT, scale=None,

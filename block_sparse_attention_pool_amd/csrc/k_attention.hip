@@ -35,6 +35,7 @@
 
 #include "sda_device.hpp"
 #include "sda_internal.h"
+#include "sda_select_dev.hpp"
 
 namespace sda {
 
@@ -68,6 +69,13 @@ __host__ __device__ inline size_t smem_base(int D, int RP, int W) {
     const size_t v = (size_t)W * kBlock * D * 2;
     const size_t m = (size_t)W * RP * (D + 2) * sizeof(float);
     return ((v > m ? v : m) + 15) / 16 * 16;
+}
+// LDS of the exact union: the C lists, the union ids and masks, per-wave
+// counts (16-byte multiple: the selection-finish buffers follow)
+__host__ __device__ inline size_t union_extra(int C, int mode, int NB_cap, int n_sel_max, int W) {
+    (void)NB_cap;
+    if (C <= 1 || mode != 0) return 0;
+    return ((size_t)C * n_sel_max * 3 * 4 + (size_t)W * 4 + 15) / 16 * 16;
 }
 constexpr int kMaxWaves = 10;
 
@@ -176,9 +184,9 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int task, int r, si
     if (lane == 0 && a.lse) a.lse[oi] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
 }
 
-template <int D, int NT>
+template <int D, int NT, bool FIN>
 __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, int b, int g, int q0,
-                                                int Cg, int split, int task, char* smem) {
+                                                int Cg, int split, int task, char* smem, char* fin_lds) {
     constexpr int KS = D / 32;            // QK k-steps
     constexpr int MTD = D / 16;           // PV m-tiles over d
     constexpr int RP = NT * 16;           // padded rows
@@ -227,6 +235,29 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[nt][ks]) : "v"(qp + ks * 32) : "memory");
+    }
+
+    // the next layer's selection (step entry point): the last wave of the
+    // workgroup, which walks the fewest blocks, brings its selection row's
+    // chunk lists into LDS by direct loads now (no registers held) and merges
+    // them after its own blocks.  Rows go to split 0 first, the split with the
+    // fewest entries.
+    const int fin_row = split * (int)gridDim.y + task;
+    const bool fin_wave = FIN && fin_row < a.fin.rows && wave == W - 1;
+    if (fin_wave) {
+        const int nkeys = a.fin_nch * a.fin.top_k;
+        const int bytes = nkeys * 8;
+        const char* src = reinterpret_cast<const char*>(a.fin_cand + (size_t)fin_row * nkeys);
+        SDA_LDS char* dst = (SDA_LDS char*)fin_lds;
+        // lanes past the row's end re-read its last piece into LDS that the
+        // list region rounds up to (whole 1 KiB rounds)
+        if ((nkeys & 1) == 0) {                              // 16-byte aligned row
+            for (int o = 0; o < bytes; o += kWave * 16)
+                __builtin_amdgcn_global_load_lds(src + min(o + lane * 16, bytes - 16), dst + o, 16, 0, 0);
+        } else {
+            for (int o = 0; o < bytes; o += kWave * 4)
+                __builtin_amdgcn_global_load_lds(src + min(o + lane * 4, bytes - 4), dst + o, 4, 0, 0);
+        }
     }
 
     floatx4 o[MTD][NT];
@@ -407,6 +438,16 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
         }
     }
 
+    if (fin_wave) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the lists have landed in LDS
+        const SelectArgs& f = a.fin;
+        const int fb = fin_row / (f.NQ * f.H_kv);
+        const int fnb = min((ld_ro(f.seq_len + fb) + kBlock - 1) / kBlock, f.NB_cap);
+        uint64_t* lists = reinterpret_cast<uint64_t*>(fin_lds);
+        uint64_t* tmp = reinterpret_cast<uint64_t*>(fin_lds + fin_list_bytes(f.top_k, a.fin_nch));
+        int* sel_j = reinterpret_cast<int*>(tmp + (size_t)f.top_k * ((a.fin_nch + 1) / 2));
+        finish_row_wave(f, lists, tmp, sel_j, a.fin_nch, fin_row, fnb, lane);
+    }
     qwait<NT, KS>(qf);
 
     // ---- merge the waves of this workgroup through LDS -------------------------------
@@ -513,7 +554,8 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
     if (threadIdx.x == 0) __hip_atomic_store(&a.counters[task], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int NT>
+// FIN: the launch also finishes the next layer's selection (fin_cand set)
+template <int D, int NT, bool FIN>
 __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int task = blockIdx.y;
@@ -599,7 +641,8 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
         L.lmask = lmask;
         L.n = base;
     }
-    run_tile_engine<D, NT>(a, L, b, g, q0, Cg, split, task, smem);
+    run_tile_engine<D, NT, FIN>(a, L, b, g, q0, Cg, split, task, smem,
+                           after_v + union_extra(a.C, a.mode, a.NB_cap, a.n_sel_max, blockDim.x / kWave));
     // written last: no global store precedes the engine's loads, so the
     // compiler may read lists and lengths through the scalar cache
     if (a.union_count && a.C > 1 && split == 0 && threadIdx.x == 0)
@@ -633,12 +676,6 @@ int attn_rows_pad(int C, int G) { return (C * G <= 16) ? 16 : 32; }
 constexpr int kCUs = 256;                  // MI355X compute units
 constexpr size_t kLdsPerCU = 160 * 1024;
 
-// LDS of the exact union: the C lists, the union ids and masks, per-wave counts
-static size_t union_extra(int C, int mode, int NB_cap, int n_sel_max, int W) {
-    (void)NB_cap;
-    if (C <= 1 || mode != 0) return 0;
-    return (size_t)C * n_sel_max * 3 * 4 + (size_t)W * 4;
-}
 
 // Launch shape of the attention kernel: W waves per workgroup, n_split
 // workgroups per row group; a wave walks its split's entries W apart, so it
@@ -648,7 +685,7 @@ static size_t union_extra(int C, int mode, int NB_cap, int n_sel_max, int W) {
 // then the one that reaches the most CUs, then the fewest splits (less
 // partial traffic), then the fewest waves.
 AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode, int NB_cap, int n_sel_max,
-                   int split_k) {
+                   int split_k, size_t extra_lds) {
     const int max_w = rows_pad == 16 ? kMaxWaves : 4;
     const int slots = rows_pad == 16 ? 12 : 4;          // resident waves per CU (VGPR-bound)
     if (list_max < 1) list_max = 1;
@@ -656,6 +693,8 @@ AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode
         int W = (list_max + split_k - 1) / split_k;
         if (W > max_w) W = max_w;
         if (W < 1) W = 1;
+        while (W > 1 && smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W) + extra_lds > kLdsPerCU)
+            --W;                                           // fewer waves (each walks more blocks) to fit the LDS
         return AttnPlan{W, split_k};
     }
     static const int force_w = env_int("SDA_ATTN_WAVES", 0);
@@ -666,7 +705,7 @@ AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode
         const int per_split = (list_max + ns - 1) / ns;
         for (int W = 1; W <= min(max_w, per_split); ++W) {
             if (force_w && W != force_w) continue;
-            const size_t lds = smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W);
+            const size_t lds = smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W) + extra_lds;
             if (lds > kLdsPerCU) continue;
             int per_cu = (int)(kLdsPerCU / lds);
             if (per_cu * W > slots) per_cu = slots / W;
@@ -696,21 +735,23 @@ size_t attn_ws_bytes(int tasks, int n_split, int rows_pad, int d) {
     return counters + (size_t)tasks * n_split * rows_pad * ((size_t)d + 2) * sizeof(float);
 }
 
-size_t attn_smem_bytes_host(int d, int rows_pad, int W, int C, int mode, int NB_cap, int n_sel_max) {
-    return smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W);
+size_t attn_smem_bytes_host(int d, int rows_pad, int W, int C, int mode, int NB_cap, int n_sel_max,
+                            size_t extra_lds) {
+    return smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W) + extra_lds;
 }
 
 template <int D, int NT>
 static hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     const int tasks = a.B * a.n_groups * a.H_kv;
-    const size_t smem = attn_smem_bytes_host(D, NT * 16, a.waves, a.C, a.mode, a.NB_cap, a.n_sel_max);
-    auto kern = attn_kernel<D, NT>;
-    static bool lds_granted = false;
-    if (!lds_granted) {
+    const size_t smem = attn_smem_bytes_host(D, NT * 16, a.waves, a.C, a.mode, a.NB_cap, a.n_sel_max,
+                                             a.fin_cand ? finish_lds_bytes(a.fin.top_k, a.fin_nch) : 0);
+    auto kern = a.fin_cand ? attn_kernel<D, NT, true> : attn_kernel<D, NT, false>;
+    static bool lds_granted[2] = {false, false};
+    if (!lds_granted[a.fin_cand != nullptr]) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCU);
         if (e != hipSuccess) return e;
-        lds_granted = true;
+        lds_granted[a.fin_cand != nullptr] = true;
     }
     hipLaunchKernelGGL(kern, dim3(a.n_split, tasks), dim3(a.waves * kWave), smem, s, a);
     hipError_t e = hipGetLastError();

@@ -23,10 +23,10 @@
 
 #include "sda_device.hpp"
 #include "sda_internal.h"
+#include "sda_select_dev.hpp"
 
 namespace sda {
 
-constexpr int kChunk = 256;          // blocks per scoring workgroup
 
 int score_chunks(int NB_cap) { return (NB_cap + kChunk - 1) / kChunk; }
 
@@ -228,65 +228,6 @@ struct ScoreArgs {
 };
 
 constexpr int kScoresOnly = 0, kFusedSelect = 1, kScoresAndStats = 2;   // score_kernel modes
-constexpr int kFusedTopK = 64;       // longest per-chunk list the fused selection keeps
-constexpr int kFusedChunks = 16;     // most chunks it merges (NB_cap <= 4096)
-
-// ordered 64-bit key: larger score first, then lower block index; 0 = no block
-__device__ __forceinline__ uint64_t block_key(float s, int j) {
-    return ((uint64_t)float_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-}
-
-// number of keys larger than `key` among the 64 lanes of the wave: the keys
-// travel once round the wave through register rotations
-__device__ __forceinline__ int wave_rank(uint64_t key) {
-    uint32_t hi = (uint32_t)(key >> 32), lo = (uint32_t)key;
-    int r = 0;
-#pragma unroll
-    for (int i = 1; i < kWave; ++i) {
-        hi = wave_ror1(hi);
-        lo = wave_ror1(lo);
-        r += ((((uint64_t)hi) << 32) | lo) > key;
-    }
-    return r;
-}
-
-// number of keys larger than x in the descending list L[0..len), 1 <= len <= 64:
-// the last key of each full 8-key segment tells how many whole segments are
-// larger, then the next segment is counted; two rounds of independent reads
-__device__ __forceinline__ int count_larger(const uint64_t* L, int len, uint64_t x) {
-    uint64_t v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = L[min(8 * i + 7, len - 1)];      // all reads in bounds, issued together
-    int seg = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) seg += (int)((8 * i + 7 < len) & (v[i] > x));
-    const int base = 8 * seg;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = L[min(base + i, len - 1)];
-    int n = base;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) n += (int)((base + i < len) & (v[i] > x));
-    return n;
-}
-
-// One round of pairwise merges over the workgroup: lists c < nl of `len`
-// descending keys (zero-padded, len >= K) at src + c * ss; the pair
-// (2m, 2m+1) becomes list m of its K largest keys at dst + m * ds.  The list
-// strides are odd numbers of keys so that lists start in different LDS banks.  A key's
-// place in the merged list is its place in its own list plus the number of
-// larger keys in the partner list; keys are distinct apart from the zero
-// padding, whose writes may coincide but carry the same value.
-__device__ __forceinline__ void merge_round(const uint64_t* src, int nl, int len, int ss, uint64_t* dst, int ds,
-                                            int K) {
-    const int items = nl * K;                              // only the first K of a list can stay
-    for (int i = threadIdx.x; i < items; i += 256) {
-        const int c = i / K, p = i - c * K;
-        const uint64_t x = src[c * ss + p];
-        int pos = p;
-        if ((c ^ 1) < nl) pos += count_larger(src + (c ^ 1) * ss, len, x);
-        if (pos < K) dst[(c >> 1) * ds + pos] = x;
-    }
-}
 
 // The selection inside a scoring launch: sc[v][t] holds the score of block
 // j0 + t for vector v0 + v of kv row `row` = b * H_kv + g (the grid is
@@ -326,14 +267,16 @@ __device__ __forceinline__ void select_tail(const SelectArgs& s, uint64_t* cand,
         if (valid) wl[wave * WS + wr] = key;
         if (lane >= nvw) wl[wave * WS + lane] = 0ull;
         __syncthreads();
-        merge_round(wl, 4, kWave, WS, bufA, KS, K);
+        merge_round(wl, 4, kWave, WS, bufA, KS, K, tid, blockDim.x);
         __syncthreads();
-        merge_round(bufA, 2, K, KS, bufB, KS, K);
+        merge_round(bufA, 2, K, KS, bufB, KS, K, tid, blockDim.x);
         __syncthreads();
         uint64_t* dst = cand + ((size_t)((b * NQ + vi) * H_kv + g) * nch + blockIdx.x) * K;
         if (tid < K) __hip_atomic_store(dst + tid, bufB[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // the next vector's writes to wl / bufA / bufB come after two more barriers
     }
+
+    if (!counters) return;                             // lists only: a later launch merges them
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's lists have landed
     __syncthreads();
@@ -342,46 +285,12 @@ __device__ __forceinline__ void select_tail(const SelectArgs& s, uint64_t* cand,
     __syncthreads();
     if (!last) return;
 
-    // level 2: pairwise merge rounds over the nch chunk lists of each vector,
-    // then the block set
-    const int kk = min(K, hi - lo);
+    // level 2: merge the nch chunk lists of each vector, then its block set
     for (int v = 0; v < NV; ++v) {
         const int vi = v0 + v;
         if (vi >= nvec) break;
         const int vrow = (b * NQ + vi) * H_kv + g;
-        const uint64_t* src = cand + (size_t)vrow * nch * K;
-        for (int i = tid; i < nch * K; i += 256) {
-            const int c = i / K;
-            bufA[c * KS + (i - c * K)] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        uint64_t* cur = bufA;
-        uint64_t* nxt = bufB;
-        for (int nl = nch; nl > 1; nl = (nl + 1) >> 1) {
-            merge_round(cur, nl, K, KS, nxt, KS, K);
-            __syncthreads();
-            uint64_t* t = cur; cur = nxt; nxt = t;
-        }
-        if (tid < kk) sel_j[tid] = (int)(0xFFFFFFFFu - (uint32_t)cur[tid]);
-        __syncthreads();
-        int32_t* out = s.block_idx + (size_t)vrow * s.n_sel_max;
-        for (int i = tid; i < lo; i += 256) out[i] = i;                 // initial blocks
-        if (tid < kk) {                                                  // top-k, ascending
-            const int jt = sel_j[tid];
-            int pos = 0;
-#pragma unroll
-            for (int u = 0; u < kFusedTopK; u += 4) {
-                const int4 q = *reinterpret_cast<const int4*>(sel_j + u);
-                pos += (u + 0 < kk && q.x < jt) + (u + 1 < kk && q.y < jt) +
-                       (u + 2 < kk && q.z < jt) + (u + 3 < kk && q.w < jt);
-            }
-            out[lo + pos] = jt;
-        }
-        for (int i = tid; i < nb - hi; i += 256) out[lo + kk + i] = hi + i;  // local blocks
-        const int total = lo + kk + (nb - hi);
-        for (int p = total + tid; p < s.n_sel_max; p += 256) out[p] = -1;
-        if (tid == 0) s.n_sel[vrow] = total;
-        __syncthreads();                               // bufA / sel_j are reused
+        finish_row<true>(s, cand + (size_t)vrow * nch * K, nch, vrow, nb, bufA, bufB, sel_j);
     }
     if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -523,7 +432,7 @@ bool fused_select_ok(int NB_cap, int top_k) {
 hipError_t launch_score_select(const uint16_t* f, const uint16_t* kt, const SelectArgs& sel, int B, int d,
                                float* scores_opt, float* scores_ws, uint64_t* cand, int* counters,
                                hipStream_t s) {
-    if (cand && counters) {
+    if (cand) {            // counters null: level 1 only (the lists), merged by a later launch
         ScoreArgs a{f, kt, sel.seq_len, scores_opt, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, cand, counters, nullptr};
         if (d == 128) launch_score_d<128, kFusedSelect>(a, B, s);
         else launch_score_d<64, kFusedSelect>(a, B, s);

@@ -317,6 +317,104 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
     return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)), "sparse_decode launch");
 }
 
+// ---------------------------------------------------------------------------
+// decode step: layer l's decode with layer l+1's selection finished inside it
+static bool step_fused_plan(int B, int H_q, int H_kv, int d, int n_sel_max, int split_k, int NB_cap_next,
+                            int top_k, AttnPlan* plan) {
+    const int rp = attn_rows_pad(1, H_q / H_kv);
+    const int tasks = B * H_kv;
+    if (!fused_select_ok(NB_cap_next, top_k) || env_int("SDA_STEP_FUSED", 1) == 0) return false;
+    const int nch = score_chunks(NB_cap_next);
+    *plan = attn_plan(d, rp, tasks, n_sel_max, 1, SDA_GROUP_EXACT, 1, n_sel_max, split_k,
+                      finish_lds_bytes(top_k, nch));
+    // one selection row per workgroup (rows fill split 0 first)
+    return (long long)tasks * plan->n_split >= (long long)B * H_kv;
+}
+
+size_t sda_decode_step_workspace(int B, int H_q, int H_kv, int d, int n_sel_max, int split_k, int NB_cap_next,
+                                 int top_k) {
+    if (B < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || NB_cap_next < 1 || top_k < 0 || H_q % H_kv) return 0;
+    AttnPlan plan{};
+    size_t dec;
+    if (step_fused_plan(B, H_q, H_kv, d, n_sel_max, split_k, NB_cap_next, top_k, &plan))
+        dec = attn_ws_bytes(B * H_kv, plan.n_split, attn_rows_pad(1, H_q / H_kv), d);
+    else
+        dec = sda_sparse_decode_workspace(B, 1, H_q, H_kv, n_sel_max, d, split_k);
+    return pad256(dec) + sda_score_select_workspace(B, 1, H_kv, NB_cap_next, top_k);
+}
+
+sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const int32_t* seq_len,
+                             const int32_t* block_idx, const int32_t* n_sel, int n_sel_max, int T_cap, int B,
+                             int H_q, int H_kv, int d, float scale, float* out, float* lse_opt, int split_k,
+                             const void* f_next, const void* k_tilde_next, const int32_t* seq_len_next,
+                             int NB_cap_next, int n_init, int n_local, int top_k, int n_sel_max_next,
+                             int32_t* block_idx_next, int32_t* n_sel_next, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_attn_common(q, k, v, seq_len, block_idx, n_sel, n_sel_max, T_cap, B, 1, H_q, H_kv, d, scale, out,
+                          split_k));
+    REQUIRE(f_next, SDA_ERR_NULL, "decode_step: f_next is null");
+    TRY(check_select_common(k_tilde_next, seq_len_next, B, 1, H_kv, d, NB_cap_next, n_init, n_local, top_k,
+                            n_sel_max_next, block_idx_next, n_sel_next));
+    REQUIRE(aligned16(f_next), SDA_ERR_ALIGN, "f_next must be 16-byte aligned");
+    REQUIRE(block_idx_next != block_idx && n_sel_next != n_sel, SDA_ERR_SHAPE,
+            "the next layer's block lists must not alias this layer's");
+    const size_t need = sda_decode_step_workspace(B, H_q, H_kv, d, n_sel_max, split_k, NB_cap_next, top_k);
+    REQUIRE(ws && ws_bytes >= need, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, need);
+    REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    AttnPlan plan{};
+    const bool fused = step_fused_plan(B, H_q, H_kv, d, n_sel_max, split_k, NB_cap_next, top_k, &plan);
+    const int rp = attn_rows_pad(1, H_q / H_kv);
+    const int tasks = B * H_kv;
+    const size_t dec = fused ? attn_ws_bytes(tasks, plan.n_split, rp, d)
+                             : sda_sparse_decode_workspace(B, 1, H_q, H_kv, n_sel_max, d, split_k);
+    char* dws = static_cast<char*>(ws);
+    char* sws = dws + pad256(dec);
+    const size_t sws_bytes = ws_bytes - pad256(dec);
+    if (!fused) {                                        // the two calls, one after the other
+        TRY(sda_score_select(f_next, k_tilde_next, seq_len_next, B, 1, H_kv, d, NB_cap_next, n_init, n_local, top_k,
+                             n_sel_max_next, block_idx_next, n_sel_next, nullptr, sws, sws_bytes, stream));
+        return sda_sparse_decode(q, k, v, seq_len, block_idx, n_sel, n_sel_max, nullptr, T_cap, B, 1, H_q, H_kv, d,
+                                 scale, out, lse_opt, split_k, dec ? dws : nullptr, dec, stream);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint64_t* cand = reinterpret_cast<uint64_t*>(sws + score_region_bytes(B, 1, H_kv, NB_cap_next));
+    SelectArgs sel{seq_len_next, nullptr, B * H_kv, 1, H_kv, NB_cap_next, n_init, n_local, top_k, n_sel_max_next,
+                   block_idx_next, n_sel_next};
+    TRY(hip_status(launch_score_select(static_cast<const uint16_t*>(f_next), static_cast<const uint16_t*>(k_tilde_next),
+                                       sel, B, d, nullptr, reinterpret_cast<float*>(sws), cand, nullptr, s),
+                   "decode_step score launch"));
+    AttnArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.seq_len = seq_len;
+    a.block_idx = block_idx;
+    a.n_sel = n_sel;
+    a.slot = nullptr;
+    a.out = out;
+    a.lse = lse_opt;
+    a.union_count = nullptr;
+    set_workspace(a, dws, dec, tasks, plan.n_split, rp);
+    a.n_sel_max = n_sel_max;
+    a.T_cap = T_cap;
+    a.NB_cap = ceil_div(T_cap, kBlock);
+    a.B = B;
+    a.NQ = 1;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.G = H_q / H_kv;
+    a.d = d;
+    a.C = 1;
+    a.mode = SDA_GROUP_EXACT;
+    a.n_groups = 1;
+    a.n_split = plan.n_split;
+    a.waves = plan.waves;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.fin_cand = cand;
+    a.fin = sel;
+    a.fin_nch = score_chunks(NB_cap_next);
+    return hip_status(launch_attention(a, s), "decode_step attention launch");
+}
+
 size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap,
                                     int group_C, int mode, int split_k) {
     if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || group_C < 1 || H_q % H_kv || NB_cap < 1)

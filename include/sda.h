@@ -187,6 +187,35 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
                                 int split_k, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * One decode step of the layer pipeline ([SparDA] §4.2 and eq. (6): layer l's
+ * indexer vectors choose layer l+1's blocks while layer l attends).  The
+ * block sets are those of sda_score_select(f_next, k_tilde_next, ...), bit for
+ * bit; out and lse are those of sda_sparse_decode(q, k, v, ...) with one
+ * query per sequence (NQ = 1) up to the order of summation
+ * (bit for bit when both take the same launch shape, e.g. the same split_k
+ * with room left in LDS).  Two launches: the scoring of layer l+1, which
+ * stops at its per-chunk candidate lists, then layer l's decode, in which the
+ * last wave of each workgroup of the first split merges one row's lists into
+ * its block set after its own blocks.  When the lists do not fit that merge
+ * (top_k > 64 or NB_cap_next > 4096) it runs the two calls as they are.
+ *
+ *   q .. split_k           as sda_sparse_decode (NQ = 1, no slot table)
+ *   f_next .. n_sel_next   as sda_score_select for layer l+1 (NQ = 1);
+ *                          block_idx_next / n_sel_next must not alias block_idx / n_sel
+ * Workspace: sda_decode_step_workspace() bytes, zero-filled before first use
+ * (it holds arrival counters that every completed call leaves at zero).
+ */
+size_t sda_decode_step_workspace(int B, int H_q, int H_kv, int d, int n_sel_max, int split_k,
+                                 int NB_cap_next, int top_k);
+sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const int32_t* seq_len,
+                             const int32_t* block_idx, const int32_t* n_sel, int n_sel_max, int T_cap,
+                             int B, int H_q, int H_kv, int d, float scale, float* out, float* lse_opt,
+                             int split_k, const void* f_next, const void* k_tilde_next,
+                             const int32_t* seq_len_next, int NB_cap_next, int n_init, int n_local, int top_k,
+                             int n_sel_max_next, int32_t* block_idx_next, int32_t* n_sel_next,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Offloaded-KV gather ([SparDA] §4.2 steps 3 and 6, §4.5): copy the K and V
  * rows of each row's selected blocks from pinned host memory into a compact
  * device staging buffer, with GPU loads over the host link, on the caller's

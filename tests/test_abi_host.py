@@ -38,7 +38,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
         assert n in sda.exported_symbols(), n
@@ -171,6 +171,25 @@ def test_gather_validation(L):
     assert f(*bad) == SHAPE
     bad = list(base); bad[9] = P_ODD
     assert f(*bad) == ALIGN
+
+
+def test_decode_step_workspace_and_validation(L):
+    # fused: the decode's partials (planned with the merge's LDS) + the
+    # score/select workspace of the next layer; aliasing lists are refused
+    n = L.sda_decode_step_workspace(8, 64, 8, 128, 35, 0, 2048, 32)
+    assert n >= L.sda_score_select_workspace(8, 1, 8, 2048, 32)
+    assert L.sda_decode_step_workspace(0, 64, 8, 128, 35, 0, 2048, 32) == 0
+    f = L.sda_decode_step
+    base = [P, P, P, P, P, P, 35, 4096, 1, 8, 2, 64, 0.125, P, None, 0,
+            P, P, P, 64, 1, 2, 8, 11, P + 256, P + 512, P, 1 << 24, None]
+    bad = list(base); bad[16] = None                                     # f_next
+    assert f(*bad) == NULL
+    bad = list(base); bad[24] = P                                        # block_idx_next aliases block_idx
+    assert f(*bad) == SHAPE
+    bad = list(base); bad[27] = 16                                       # workspace too small
+    assert f(*bad) == WS
+    bad = list(base); bad[23] = 10                                       # n_sel_max_next < 1 + 2 + 8
+    assert f(*bad) == SHAPE
 
 
 def test_python_binding_rejects_bad_tensors():

@@ -254,6 +254,56 @@ def test_comparator_fused_select_matches_select_launch(NQ):
             os.environ["SDA_SELECT_FUSED"] = old
 
 
+# exact: both launches run the same split plan.  At one split the plain decode
+# takes 10 waves (all of the LDS); the step needs LDS for the merge and takes 9.
+@pytest.mark.parametrize("cid,fused,split_k,exact", [(2, "1", 0, False), (2, "0", 0, True), (2, "1", 5, True),
+                                                     (3, "1", 0, False), (3, "1", 7, True), (3, "1", 1, False)])
+def test_decode_step_matches_separate_calls(cid, fused, split_k, exact):
+    # the step entry point (the next layer's selection finished inside this
+    # layer's decode launch; the two calls when fused = 0) against
+    # sda_score_select for the next layer and sda_sparse_decode for this one:
+    # identical block lists; identical outputs when both run the same split
+    # plan, else equal up to the order of the split merge
+    import os
+    cfg = synth.get_config(cid)
+    _say(f"decode step: config {cid}, fused {fused}, split_k {split_k}")
+    K0, V0, _ = inputs.kv_layer(cfg, 0, device=DEV)
+    K1, _, _ = inputs.kv_layer(cfg, 1, device=DEV)
+    kt1 = gpu_ktilde(K1, cfg.T)
+    del K1
+    kt0 = gpu_ktilde(K0, cfg.T)
+    F0 = inputs.to_bf16(inputs.indexer_vectors(cfg, 0)).to(DEV)
+    F1 = inputs.to_bf16(inputs.indexer_vectors(cfg, 1)).to(DEV)
+    Q0 = inputs.to_bf16(inputs.attention_queries(cfg, 0)).to(DEV)
+    sel = (cfg.n_init, cfg.n_local, cfg.top_k)
+    bi0, ns0 = sda.sda_score_select(F0, kt0, seq(cfg), *sel)
+    ref_bi1, ref_ns1 = sda.sda_score_select(F1, kt1, seq(cfg), *sel)
+    ref_out, ref_lse = sda.sda_sparse_decode(Q0, K0, V0, seq(cfg), bi0, ns0, split_k=split_k)
+    old = os.environ.get("SDA_STEP_FUSED")
+    try:
+        os.environ["SDA_STEP_FUSED"] = fused
+        nbytes = sda.lib().sda_decode_step_workspace(cfg.B, cfg.H_q, cfg.H_kv, cfg.d, bi0.shape[-1], split_k,
+                                                     kt1.shape[2], cfg.top_k)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+        for it in range(6):
+            out, lse, bi1, ns1 = sda.sda_decode_step(Q0, K0, V0, seq(cfg), bi0, ns0, F1, kt1, seq(cfg), *sel,
+                                                     split_k=split_k, ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(bi1, ref_bi1) and torch.equal(ns1, ref_ns1), it
+            if exact:
+                assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), it
+            else:
+                assert (out - ref_out).abs().max().item() <= 1e-5, it
+                assert (lse - ref_lse).abs().max().item() <= 1e-5, it
+            if split_k > 1:      # split arrival counters (the workspace's first ints) back at zero
+                assert int(ws[:4 * cfg.B * cfg.H_kv].count_nonzero()) == 0, it
+    finally:
+        if old is None:
+            os.environ.pop("SDA_STEP_FUSED", None)
+        else:
+            os.environ["SDA_STEP_FUSED"] = old
+
+
 def test_select_ties_go_to_lower_index():
     rng = np.random.default_rng(5)
     NB, d = 300, 128
