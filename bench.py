@@ -13,9 +13,10 @@ does (the ring of 8 layers touches 0.86 GB per pass, well beyond the L2 and
 Infinity caches together).
 
 Prints one JSON line.  `value` is whole-job queries/s over the timed steps
-(one query = one sequence's decode token); `roofline` prices the decode
-kernel (attention + split merge, timed alone as sda_sparse_decode) against
-the 8 TB/s HBM peak on its algorithmic bytes (the selected K/V blocks); `cpu_baseline` times the CPU
+(one query = one sequence's decode token); `roofline` prices the step's one
+launch against the 8 TB/s HBM peak on its algorithmic bytes (layer l's
+selected K/V blocks plus layer l+1's compressed keys), `roofline_decode`
+the decode launch alone (sda_sparse_decode, selected K/V bytes); `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload; `rows` measures the other
 rows of the hot path (compressed-key build and per-token refresh, the G-head
 comparator, grouped verification decode, offloaded gather) at their own
@@ -44,8 +45,10 @@ from synth import inputs  # noqa: E402
 
 METRIC = "sparse-decode queries/s + achieved HBM GB/s (% of peak) at 128K ctx"
 HBM_PEAK_GBS = 8000.0
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "sparse_decode_c3_counters.json")
-ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_pool_amd", "csrc", "k_attention.hip")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_c3_counters.json")
+# sources of the measured kernels: counters taken on other sources are stale
+KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_attention_pool_amd", "csrc", f)
+               for f in ("k_attention.hip", "sda_select_dev.hpp", "sda_internal.h", "sda_device.hpp")]
 
 
 def log(*a):
@@ -53,8 +56,11 @@ def log(*a):
 
 
 def kernel_hash():
-    with open(ATTN_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def build_layers(cfg, n_layers, dev):
@@ -599,14 +605,23 @@ def main():
     dec_bytes = cfg.selected_kv_bytes()
     sel_bytes = cfg.ktilde_bytes()
     dec_gbs = dec_bytes / t_dec.mean() / 1e9
-    traffic = None
-    if os.path.exists(PROFILE_COUNTERS):
+    step_fused = args.step == "fused" and not args.overlap
+    # the dominant kernel of the timed step: the step launch (decode of layer l
+    # plus scoring and selection of layer l+1), else the decode launch
+    rl_key = "decode_step" if step_fused else "sparse_decode"
+    rl_bytes = dec_bytes + sel_bytes if step_fused else dec_bytes
+    rl_gbs = rl_bytes / (t_step if step_fused else t_dec.mean()) / 1e9
+
+    def counters_for(key):
+        if not os.path.exists(PROFILE_COUNTERS):
+            return None
         try:
             pc = json.load(open(PROFILE_COUNTERS))
             if pc.get("kernel_hash") == kernel_hash() and pc.get("config") == cfg.cid:
-                traffic = pc.get("hbm_bytes_per_launch")
+                return pc.get(key, {}).get("hbm_bytes_per_launch")
         except Exception:
-            traffic = None
+            return None
+        return None
     res = {
         "metric": METRIC,
         "value": value,
@@ -637,14 +652,25 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
+            "achieved": rl_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": rl_gbs / HBM_PEAK_GBS,
+            "traffic": counters_for(rl_key),
+            "kernel": ("attn_kernel<128, 1, true> (sda_decode_step: layer l's decode and layer l+1's scoring "
+                       "and selection in one launch)" if step_fused else
+                       "attn_kernel<128, 1, false> (sda_sparse_decode; splits merged by the last workgroup of "
+                       "each row)"),
+            "algorithmic_bytes_per_launch": rl_bytes,
+        },
+        # the decode launch alone (sda_sparse_decode), against the same peak
+        "roofline_decode": {
+            "bound": "hbm",
             "achieved": dec_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": dec_gbs / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "kernel": "attn_kernel<128, 1> as launched by sda_sparse_decode (splits merged by the last "
-                      "workgroup of each row), timed alone; the step's decode launch is the same kernel with "
-                      "one extra wave's selection merge per workgroup of split 0",
+            "traffic": counters_for("sparse_decode"),
             "algorithmic_bytes_per_launch": dec_bytes,
         },
         "kernels_us": {

@@ -71,7 +71,7 @@ __host__ __device__ inline size_t smem_base(int D, int RP, int W) {
     return ((v > m ? v : m) + 15) / 16 * 16;
 }
 // LDS of the exact union: the C lists, the union ids and masks, per-wave
-// counts (16-byte multiple: the selection-finish buffers follow)
+// counts
 __host__ __device__ inline size_t union_extra(int C, int mode, int NB_cap, int n_sel_max, int W) {
     (void)NB_cap;
     if (C <= 1 || mode != 0) return 0;
@@ -184,9 +184,124 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int task, int r, si
     if (lane == 0 && a.lse) a.lse[oi] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
 }
 
-template <int D, int NT, bool FIN>
+// ---- decode step: the next layer's scoring and selection ------------------------
+// Workgroup w scores chunks w * per_wg + i (i < per_wg, one per group of four
+// waves) of the next layer's compressed keys against its indexer vectors,
+// keeps each chunk's top-k keys (level 1), and the last workgroup to finish a
+// row's chunks merges them into the row's block set (level 2).  Loads,
+// arithmetic and merges are the scoring launch's, so the block sets equal
+// sda_score_select's bit for bit.  LDS at `sl` (step_lds_bytes): per group the
+// chunk's scores and four wave lists, then the level-2 buffers and flags.
+// These workgroups follow the attention grid: the dispatcher starts them on
+// the compute units the attention workgroups leave, so their loads fill the
+// memory pipe while the attention's split merges and stragglers finish.
+struct StepPos {
+    int grp, t, row, ch, nb;
+    bool has;
+};
+
+__device__ __forceinline__ StepPos step_pos(const AttnArgs& a, int w) {
+    const StepScore& st = a.step;
+    StepPos p;
+    p.grp = threadIdx.x / kChunk;
+    p.t = threadIdx.x % kChunk;
+    const int cid = w * st.per_wg + p.grp;
+    p.has = p.grp < st.per_wg && cid < st.sel.rows * st.cpr;
+    p.row = p.has ? cid / st.cpr : 0;
+    p.ch = p.has ? cid - p.row * st.cpr : 0;
+    p.nb = min((ld_ro(st.sel.seq_len + p.row / st.sel.H_kv) + kBlock - 1) / kBlock, st.sel.NB_cap);
+    return p;
+}
+
+__device__ __forceinline__ char* step_group_lds(const AttnArgs& a, const StepPos& p, char* sl) {
+    return sl + (size_t)min(p.grp, a.step.per_wg - 1) * step_group_lds_bytes(a.step.sel.top_k);
+}
+
+// scores of this group's chunk into LDS (no barrier)
+template <int D>
+__device__ __forceinline__ void step_scores(const AttnArgs& a, const StepPos& p, char* sl) {
+    constexpr int EPL = D / 16;                 // bf16 elements per lane of one pooled key (16 lanes per key)
+    constexpr int STEPS = kChunk / 16;          // 16 blocks per group step, all in flight at once
+    using KLoad = typename std::conditional<EPL == 8, u32x4, u32x2>::type;
+    const StepScore& st = a.step;
+    const int j0 = p.ch * kChunk;
+    if (!p.has || j0 >= p.nb) return;
+    const int lane = p.t % kWave, wave = p.t / kWave, li = lane & 15;
+    float* sc = reinterpret_cast<float*>(step_group_lds(a, p, sl));
+    const KLoad fw = *reinterpret_cast<const KLoad*>(st.vec + (size_t)p.row * D + li * EPL);
+    const uint16_t* ktr = st.kt + (size_t)p.row * st.sel.NB_cap * D + li * EPL;
+    KLoad kv[STEPS];
+    int jj[STEPS];
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+        jj[u] = j0 + u * 16 + wave * 4 + (lane >> 4);
+        // past the length: re-read the last block (cached), result unused
+        kv[u] = __builtin_nontemporal_load(reinterpret_cast<const KLoad*>(ktr + (size_t)min(jj[u], p.nb - 1) * D));
+    }
+    float fv[EPL];
+    const uint32_t* wp = reinterpret_cast<const uint32_t*>(&fw);
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) {
+        fv[2 * i] = bf16lo(wp[i]);
+        fv[2 * i + 1] = bf16hi(wp[i]);
+    }
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+        const float s = key_dot<EPL>(fv, reinterpret_cast<const uint32_t*>(&kv[u]));
+        if (li == 0 && jj[u] < p.nb) sc[jj[u] - j0] = s;
+    }
+}
+
+// level 1 of this group's chunk (every thread of the workgroup calls it)
+__device__ __forceinline__ void step_level1(const AttnArgs& a, const StepPos& p, char* sl) {
+    const StepScore& st = a.step;
+    const int lo = min(st.sel.n_init, p.nb);    // candidates are [lo, hi)
+    const int hi = max(lo, p.nb - st.sel.n_local);
+    char* gl = step_group_lds(a, p, sl);
+    __syncthreads();                            // scores complete
+    chunk_top_k(reinterpret_cast<const float*>(gl), p.ch * kChunk, lo, hi, st.sel.top_k, p.has,
+                reinterpret_cast<uint64_t*>(gl + kChunk * 4), st.cand + ((size_t)p.row * st.cpr + p.ch) * st.sel.top_k,
+                p.t);
+}
+
+// arrival per chunk and level 2 in the last workgroup of each row (every
+// thread of the workgroup calls it; it drains this workgroup's stores)
+__device__ __forceinline__ void step_finish(const AttnArgs& a, const StepPos& p, int w, char* sl) {
+    const StepScore& st = a.step;
+    const SelectArgs& sel = st.sel;
+    const int K = sel.top_k;
+    const int P = pow2_at_least(K);
+    uint64_t* fA = reinterpret_cast<uint64_t*>(sl + (size_t)st.per_wg * step_group_lds_bytes(K));
+    uint64_t* fB = fA + (size_t)P * st.cpr;
+    int* last = reinterpret_cast<int*>(fB + (size_t)P * ((st.cpr + 1) / 2));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // this workgroup's lists have landed
+    __syncthreads();
+    if (p.t == 0 && p.grp < st.per_wg)
+        last[p.grp] = p.has && __hip_atomic_fetch_add(st.counters + p.row, 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT) == st.cpr - 1;
+    __syncthreads();
+    for (int g2 = 0; g2 < st.per_wg; ++g2) {
+        if (!last[g2]) continue;                            // uniform: one LDS flag
+        const int r2 = (w * st.per_wg + g2) / st.cpr;
+        const int nb2 = min((ld_ro(sel.seq_len + r2 / sel.H_kv) + kBlock - 1) / kBlock, sel.NB_cap);
+        finish_row<true>(sel, st.cand + (size_t)r2 * st.cpr * K, st.cpr, r2, nb2, fA, fB);
+        if (threadIdx.x == 0) __hip_atomic_store(st.counters + r2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();                                        // LDS free again
+}
+
+// a workgroup that only scores and selects
+template <int D>
+__device__ __forceinline__ void step_score_role(const AttnArgs& a, int w, char* smem) {
+    const StepPos p = step_pos(a, w);
+    step_scores<D>(a, p, smem);
+    step_level1(a, p, smem);
+    step_finish(a, p, w, smem);
+}
+
+template <int D, int NT>
 __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, int b, int g, int q0,
-                                                int Cg, int split, int task, char* smem, char* fin_lds) {
+                                                int Cg, int split, int task, char* smem) {
     constexpr int KS = D / 32;            // QK k-steps
     constexpr int MTD = D / 16;           // PV m-tiles over d
     constexpr int RP = NT * 16;           // padded rows
@@ -237,28 +352,6 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
             asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[nt][ks]) : "v"(qp + ks * 32) : "memory");
     }
 
-    // the next layer's selection (step entry point): the last wave of the
-    // workgroup, which walks the fewest blocks, brings its selection row's
-    // chunk lists into LDS by direct loads now (no registers held) and merges
-    // them after its own blocks.  Rows go to split 0 first, the split with the
-    // fewest entries.
-    const int fin_row = split * (int)gridDim.y + task;
-    const bool fin_wave = FIN && fin_row < a.fin.rows && wave == W - 1;
-    if (fin_wave) {
-        const int nkeys = a.fin_nch * a.fin.top_k;
-        const int bytes = nkeys * 8;
-        const char* src = reinterpret_cast<const char*>(a.fin_cand + (size_t)fin_row * nkeys);
-        SDA_LDS char* dst = (SDA_LDS char*)fin_lds;
-        // lanes past the row's end re-read its last piece into LDS that the
-        // list region rounds up to (whole 1 KiB rounds)
-        if ((nkeys & 1) == 0) {                              // 16-byte aligned row
-            for (int o = 0; o < bytes; o += kWave * 16)
-                __builtin_amdgcn_global_load_lds(src + min(o + lane * 16, bytes - 16), dst + o, 16, 0, 0);
-        } else {
-            for (int o = 0; o < bytes; o += kWave * 4)
-                __builtin_amdgcn_global_load_lds(src + min(o + lane * 4, bytes - 4), dst + o, 4, 0, 0);
-        }
-    }
 
     floatx4 o[MTD][NT];
 #pragma unroll
@@ -438,16 +531,6 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
         }
     }
 
-    if (fin_wave) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the lists have landed in LDS
-        const SelectArgs& f = a.fin;
-        const int fb = fin_row / (f.NQ * f.H_kv);
-        const int fnb = min((ld_ro(f.seq_len + fb) + kBlock - 1) / kBlock, f.NB_cap);
-        uint64_t* lists = reinterpret_cast<uint64_t*>(fin_lds);
-        uint64_t* tmp = reinterpret_cast<uint64_t*>(fin_lds + fin_list_bytes(f.top_k, a.fin_nch));
-        int* sel_j = reinterpret_cast<int*>(tmp + (size_t)f.top_k * ((a.fin_nch + 1) / 2));
-        finish_row_wave(f, lists, tmp, sel_j, a.fin_nch, fin_row, fnb, lane);
-    }
     qwait<NT, KS>(qf);
 
     // ---- merge the waves of this workgroup through LDS -------------------------------
@@ -554,10 +637,18 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
     if (threadIdx.x == 0) __hip_atomic_store(&a.counters[task], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// FIN: the launch also finishes the next layer's selection (fin_cand set)
-template <int D, int NT, bool FIN>
+// STEP: the decode step; workgroups past the attention grid score and select
+// (the dispatcher starts them as attention workgroups retire)
+template <int D, int NT, bool STEP>
 __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
+    if constexpr (STEP) {
+        const int attn_rows = a.B * a.n_groups * a.H_kv;
+        if ((int)blockIdx.y >= attn_rows) {
+            step_score_role<D>(a, ((int)blockIdx.y - attn_rows) * (int)gridDim.x + (int)blockIdx.x, smem);
+            return;
+        }
+    }
     const int task = blockIdx.y;
     const int split = blockIdx.x;
     const int g = task % a.H_kv;
@@ -641,8 +732,7 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
         L.lmask = lmask;
         L.n = base;
     }
-    run_tile_engine<D, NT, FIN>(a, L, b, g, q0, Cg, split, task, smem,
-                           after_v + union_extra(a.C, a.mode, a.NB_cap, a.n_sel_max, blockDim.x / kWave));
+    run_tile_engine<D, NT>(a, L, b, g, q0, Cg, split, task, smem);
     // written last: no global store precedes the engine's loads, so the
     // compiler may read lists and lengths through the scalar cache
     if (a.union_count && a.C > 1 && split == 0 && threadIdx.x == 0)
@@ -685,7 +775,7 @@ constexpr size_t kLdsPerCU = 160 * 1024;
 // then the one that reaches the most CUs, then the fewest splits (less
 // partial traffic), then the fewest waves.
 AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode, int NB_cap, int n_sel_max,
-                   int split_k, size_t extra_lds) {
+                   int split_k) {
     const int max_w = rows_pad == 16 ? kMaxWaves : 4;
     const int slots = rows_pad == 16 ? 12 : 4;          // resident waves per CU (VGPR-bound)
     if (list_max < 1) list_max = 1;
@@ -693,7 +783,7 @@ AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode
         int W = (list_max + split_k - 1) / split_k;
         if (W > max_w) W = max_w;
         if (W < 1) W = 1;
-        while (W > 1 && smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W) + extra_lds > kLdsPerCU)
+        while (W > 1 && smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W) > kLdsPerCU)
             --W;                                           // fewer waves (each walks more blocks) to fit the LDS
         return AttnPlan{W, split_k};
     }
@@ -705,7 +795,7 @@ AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode
         const int per_split = (list_max + ns - 1) / ns;
         for (int W = 1; W <= min(max_w, per_split); ++W) {
             if (force_w && W != force_w) continue;
-            const size_t lds = smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W) + extra_lds;
+            const size_t lds = smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W);
             if (lds > kLdsPerCU) continue;
             int per_cu = (int)(kLdsPerCU / lds);
             if (per_cu * W > slots) per_cu = slots / W;
@@ -735,25 +825,31 @@ size_t attn_ws_bytes(int tasks, int n_split, int rows_pad, int d) {
     return counters + (size_t)tasks * n_split * rows_pad * ((size_t)d + 2) * sizeof(float);
 }
 
-size_t attn_smem_bytes_host(int d, int rows_pad, int W, int C, int mode, int NB_cap, int n_sel_max,
-                            size_t extra_lds) {
-    return smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W) + extra_lds;
+size_t attn_smem_bytes_host(int d, int rows_pad, int W, int C, int mode, int NB_cap, int n_sel_max) {
+    return smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W);
 }
 
 template <int D, int NT>
 static hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     const int tasks = a.B * a.n_groups * a.H_kv;
-    const size_t smem = attn_smem_bytes_host(D, NT * 16, a.waves, a.C, a.mode, a.NB_cap, a.n_sel_max,
-                                             a.fin_cand ? finish_lds_bytes(a.fin.top_k, a.fin_nch) : 0);
-    auto kern = a.fin_cand ? attn_kernel<D, NT, true> : attn_kernel<D, NT, false>;
+    const bool step = a.step.cand != nullptr;
+    size_t smem = attn_smem_bytes_host(D, NT * 16, a.waves, a.C, a.mode, a.NB_cap, a.n_sel_max);
+    int extra_rows = 0;                        // grid rows of workgroups that only score
+    if (step) {
+        const size_t need = step_lds_bytes(a.step.sel.top_k, a.step.cpr, a.step.per_wg);
+        if (need > smem) smem = need;
+        const int wgs = (a.step.sel.rows * a.step.cpr + a.step.per_wg - 1) / a.step.per_wg;
+        extra_rows = (wgs + a.n_split - 1) / a.n_split;
+    }
+    auto kern = step ? attn_kernel<D, NT, true> : attn_kernel<D, NT, false>;
     static bool lds_granted[2] = {false, false};
-    if (!lds_granted[a.fin_cand != nullptr]) {
+    if (!lds_granted[step]) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCU);
         if (e != hipSuccess) return e;
-        lds_granted[a.fin_cand != nullptr] = true;
+        lds_granted[step] = true;
     }
-    hipLaunchKernelGGL(kern, dim3(a.n_split, tasks), dim3(a.waves * kWave), smem, s, a);
+    hipLaunchKernelGGL(kern, dim3(a.n_split, tasks + extra_rows), dim3(a.waves * kWave), smem, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1 || a.fused_combine) return e;
     hipLaunchKernelGGL((combine_kernel<D, NT * 16>), dim3(tasks, NT * 16), dim3(64), 0, s, a);

@@ -238,16 +238,11 @@ template <int NV>
 __device__ __forceinline__ void select_tail(const SelectArgs& s, uint64_t* cand, int* counters,
                                             const float (*sc)[kChunk], int b, int g, int row, int NQ,
                                             int H_kv, int nvec, int v0, int j0, int nb) {
-    const int lane = __lane_id();
-    const int wave = threadIdx.x / kWave;
-    constexpr int WS = kWave + 1;                      // list strides (odd: spread over banks)
-    __shared__ uint64_t wl[4 * WS];                    // four sorted wave lists of 64
-    __shared__ uint64_t bufA[(kFusedTopK + 1) * kFusedChunks];
-    __shared__ uint64_t bufB[(kFusedTopK + 1) * kFusedChunks / 2];
-    __shared__ __align__(16) int sel_j[kFusedTopK];
+    __shared__ uint64_t wl[4 * kWave];                 // four sorted wave lists of 64
+    __shared__ uint64_t bufA[kFusedTopK * kFusedChunks];
+    __shared__ uint64_t bufB[kFusedTopK * kFusedChunks / 2];
     __shared__ int last;
     const int K = s.top_k;
-    const int KS = K | 1;                              // odd list stride >= K
     const int nch = gridDim.x;
     const int tid = threadIdx.x;
     const int lo = min(s.n_init, nb);                 // candidates are [lo, hi)
@@ -256,27 +251,12 @@ __device__ __forceinline__ void select_tail(const SelectArgs& s, uint64_t* cand,
 
     // level 1: rank inside each wave, then two rounds of pairwise merges
     // give this chunk's best K keys in rank order
-    const int j = j0 + tid;
-    const bool valid = j >= lo && j < hi;
-    const int nvw = __popcll(__ballot(valid));         // valid lanes of this wave
     for (int v = 0; v < NV; ++v) {
         const int vi = v0 + v;
         if (vi >= nvec) break;                         // uniform over the workgroup
-        const uint64_t key = valid ? block_key(sc[v][tid], j) : 0ull;
-        const int wr = wave_rank(key);                 // valid keys: distinct ranks < nvw
-        if (valid) wl[wave * WS + wr] = key;
-        if (lane >= nvw) wl[wave * WS + lane] = 0ull;
-        __syncthreads();
-        merge_round(wl, 4, kWave, WS, bufA, KS, K, tid, blockDim.x);
-        __syncthreads();
-        merge_round(bufA, 2, K, KS, bufB, KS, K, tid, blockDim.x);
-        __syncthreads();
         uint64_t* dst = cand + ((size_t)((b * NQ + vi) * H_kv + g) * nch + blockIdx.x) * K;
-        if (tid < K) __hip_atomic_store(dst + tid, bufB[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // the next vector's writes to wl / bufA / bufB come after two more barriers
+        chunk_top_k(sc[v], j0, lo, hi, K, true, wl, dst, tid);
     }
-
-    if (!counters) return;                             // lists only: a later launch merges them
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's lists have landed
     __syncthreads();
@@ -290,7 +270,7 @@ __device__ __forceinline__ void select_tail(const SelectArgs& s, uint64_t* cand,
         const int vi = v0 + v;
         if (vi >= nvec) break;
         const int vrow = (b * NQ + vi) * H_kv + g;
-        finish_row<true>(s, cand + (size_t)vrow * nch * K, nch, vrow, nb, bufA, bufB, sel_j);
+        finish_row<true>(s, cand + (size_t)vrow * nch * K, nch, vrow, nb, bufA, bufB);
     }
     if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -316,52 +296,49 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     const int wave = threadIdx.x / kWave;
     __shared__ float sc[LDS_SC ? NV : 1][LDS_SC ? kChunk : 1];
 
+    // this lane's slice of each vector (dims EPL*li .. EPL*li + EPL), loaded
+    // raw beside the length read; converted once the key loads are out
+    KLoad fw[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int vi = v0 + v;
+        const int q = vi / a.VPR, hv = g * a.VPR + (vi - (vi / a.VPR) * a.VPR);
+        fw[v] = vi < nvec ? *reinterpret_cast<const KLoad*>(a.vec + (((size_t)b * a.NQ + q) * H_vec + hv) * D +
+                                                             li * EPL)
+                          : KLoad{};
+    }
     if (j0 < nb) {
-        // this lane's slice of each vector: dims EPL*li .. EPL*li + EPL
-        float fv[NV][EPL];
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int vi = v0 + v;
-            const int q = vi / a.VPR, hv = g * a.VPR + (vi - (vi / a.VPR) * a.VPR);
-            if (vi < nvec) {
-                const KLoad w = *reinterpret_cast<const KLoad*>(a.vec + (((size_t)b * a.NQ + q) * H_vec + hv) * D +
-                                                                 li * EPL);
-                const uint32_t* wp = reinterpret_cast<const uint32_t*>(&w);
-#pragma unroll
-                for (int i = 0; i < EPL / 2; ++i) {
-                    fv[v][2 * i] = bf16lo(wp[i]);
-                    fv[v][2 * i + 1] = bf16hi(wp[i]);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < EPL; ++i) fv[v][i] = 0.f;
-            }
-        }
-
         const uint16_t* ktr = a.kt + (size_t)row * a.NB_cap * D + li * EPL;
-        constexpr int UNR = 8;                       // steps in flight
+        constexpr int UNR = NV <= 2 ? 16 : 8;        // steps in flight
         constexpr int STEPS = kChunk / 16;           // 16 blocks per workgroup step
+        float fv[NV][EPL];
         for (int s0 = 0; s0 < STEPS; s0 += UNR) {
             KLoad kv[UNR];
             int jj[UNR];
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
                 jj[u] = j0 + (s0 + u) * 16 + wave * 4 + (lane >> 4);
-                if (jj[u] < nb) kv[u] = __builtin_nontemporal_load(reinterpret_cast<const KLoad*>(ktr + (size_t)jj[u] * D));
-                else kv[u] = KLoad{};
+                // past the length: re-read the last block (cached), result unused
+                kv[u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const KLoad*>(ktr + (size_t)min(jj[u], nb - 1) * D));
+            }
+            if (s0 == 0) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const uint32_t* wp = reinterpret_cast<const uint32_t*>(&fw[v]);
+#pragma unroll
+                    for (int i = 0; i < EPL / 2; ++i) {
+                        fv[v][2 * i] = bf16lo(wp[i]);
+                        fv[v][2 * i + 1] = bf16hi(wp[i]);
+                    }
+                }
             }
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
                 const uint32_t* kp = reinterpret_cast<const uint32_t*>(&kv[u]);
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
-                    float acc = 0.f;
-#pragma unroll
-                    for (int i = 0; i < EPL / 2; ++i) {
-                        acc = fmaf(fv[v][2 * i], bf16lo(kp[i]), acc);
-                        acc = fmaf(fv[v][2 * i + 1], bf16hi(kp[i]), acc);
-                    }
-                    acc = row16_sum(acc) * a.mult;
+                    const float acc = key_dot<EPL>(fv[v], kp) * a.mult;
                     const int vi = v0 + v;
                     if (li == 0 && jj[u] < nb && vi < nvec) {
                         if constexpr (LDS_SC) sc[v][jj[u] - j0] = acc;

@@ -318,17 +318,16 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
 }
 
 // ---------------------------------------------------------------------------
-// decode step: layer l's decode with layer l+1's selection finished inside it
+// decode step: layer l's decode and layer l+1's scoring and selection in one
+// launch (workgroups past the attention grid score and select)
 static bool step_fused_plan(int B, int H_q, int H_kv, int d, int n_sel_max, int split_k, int NB_cap_next,
                             int top_k, AttnPlan* plan) {
-    const int rp = attn_rows_pad(1, H_q / H_kv);
-    const int tasks = B * H_kv;
     if (!fused_select_ok(NB_cap_next, top_k) || env_int("SDA_STEP_FUSED", 1) == 0) return false;
-    const int nch = score_chunks(NB_cap_next);
-    *plan = attn_plan(d, rp, tasks, n_sel_max, 1, SDA_GROUP_EXACT, 1, n_sel_max, split_k,
-                      finish_lds_bytes(top_k, nch));
-    // one selection row per workgroup (rows fill split 0 first)
-    return (long long)tasks * plan->n_split >= (long long)B * H_kv;
+    *plan = attn_plan(d, attn_rows_pad(1, H_q / H_kv), B * H_kv, n_sel_max, 1, SDA_GROUP_EXACT, 1, n_sel_max,
+                      split_k);
+    // a scoring workgroup needs at least one group of four waves
+    return plan->waves >= 4 &&
+           step_lds_bytes(top_k, score_chunks(NB_cap_next), min(plan->waves / 4, 2)) <= 160 * 1024;
 }
 
 size_t sda_decode_step_workspace(int B, int H_q, int H_kv, int d, int n_sel_max, int split_k, int NB_cap_next,
@@ -376,12 +375,9 @@ sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const 
                                  scale, out, lse_opt, split_k, dec ? dws : nullptr, dec, stream);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    uint64_t* cand = reinterpret_cast<uint64_t*>(sws + score_region_bytes(B, 1, H_kv, NB_cap_next));
-    SelectArgs sel{seq_len_next, nullptr, B * H_kv, 1, H_kv, NB_cap_next, n_init, n_local, top_k, n_sel_max_next,
-                   block_idx_next, n_sel_next};
-    TRY(hip_status(launch_score_select(static_cast<const uint16_t*>(f_next), static_cast<const uint16_t*>(k_tilde_next),
-                                       sel, B, d, nullptr, reinterpret_cast<float*>(sws), cand, nullptr, s),
-                   "decode_step score launch"));
+    const size_t cand_off = score_region_bytes(B, 1, H_kv, NB_cap_next);     // same layout as sda_score_select
+    uint64_t* cand = reinterpret_cast<uint64_t*>(sws + cand_off);
+    int* counters = reinterpret_cast<int*>(sws + cand_off + cand_region_bytes(B, 1, H_kv, NB_cap_next, top_k));
     AttnArgs a{};
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
@@ -409,10 +405,15 @@ sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const 
     a.n_split = plan.n_split;
     a.waves = plan.waves;
     a.scale_log2 = scale * 1.4426950408889634f;
-    a.fin_cand = cand;
-    a.fin = sel;
-    a.fin_nch = score_chunks(NB_cap_next);
-    return hip_status(launch_attention(a, s), "decode_step attention launch");
+    a.step.vec = static_cast<const uint16_t*>(f_next);
+    a.step.kt = static_cast<const uint16_t*>(k_tilde_next);
+    a.step.cand = cand;
+    a.step.counters = counters;
+    a.step.sel = SelectArgs{seq_len_next, nullptr, B * H_kv, 1, H_kv, NB_cap_next, n_init, n_local, top_k,
+                            n_sel_max_next, block_idx_next, n_sel_next};
+    a.step.cpr = score_chunks(NB_cap_next);
+    a.step.per_wg = min(plan.waves / 4, 2);
+    return hip_status(launch_attention(a, s), "decode_step launch");
 }
 
 size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap,

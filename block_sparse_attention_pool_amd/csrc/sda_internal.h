@@ -24,23 +24,30 @@ struct SelectArgs {
 };
 // scores, then exact top-k and block sets.  With `cand` and `counters` (zeroed,
 // one per (b, kv head, vector tile)) the selection runs inside the scoring
-// launch (needs fused_select_ok); with `cand` alone the launch stops after the
-// per-chunk candidate lists (a decode launch merges them); otherwise scores go
-// to scores_opt or scores_ws and a second launch selects.
+// launch (needs fused_select_ok); otherwise scores go to scores_opt or
+// scores_ws and a second launch selects.
 hipError_t launch_score_select(const uint16_t* f, const uint16_t* kt, const SelectArgs& sel, int B, int d,
                                float* scores_opt, float* scores_ws, uint64_t* cand, int* counters,
                                hipStream_t s);
 bool fused_select_ok(int NB_cap, int top_k);
 constexpr int kFusedTopK = 64;       // longest per-chunk list the in-launch selection keeps
 constexpr int kFusedChunks = 16;     // most 256-block chunks it merges (NB_cap <= 4096)
-// LDS bytes of one wave's final merge of a row's chunk lists (K keys each, nch
-// chunks): the lists (whole 1 KiB direct-load rounds), the merge's second
-// buffer and the selected block ids
-__host__ __device__ inline size_t fin_list_bytes(int K, int nch) {
-    return ((size_t)K * nch * 8 + 1023) / 1024 * 1024;
+// top-k lists are padded to the smallest power of two >= K (1 for K = 0)
+__host__ __device__ inline int pow2_at_least(int K) {
+    int P = 1;
+    while (P < K) P <<= 1;
+    return P;
 }
-__host__ __device__ inline size_t finish_lds_bytes(int K, int nch) {
-    return fin_list_bytes(K, nch) + (size_t)K * ((nch + 1) / 2) * 8 + kFusedTopK * 4;
+// LDS of the decode step's scoring workgroups: per group of four waves the
+// chunk's scores and four sorted wave lists, then the level-2 buffers and
+// one flag per group
+__host__ __device__ inline size_t step_group_lds_bytes(int K) {
+    (void)K;
+    return 256 * 4 + 4 * 64 * 8;
+}
+__host__ __device__ inline size_t step_lds_bytes(int K, int cpr, int per_wg) {
+    const size_t P = (size_t)pow2_at_least(K);
+    return per_wg * step_group_lds_bytes(K) + (P * cpr + P * ((cpr + 1) / 2)) * 8 + 16;
 }
 int score_tiles(int NQ);
 // integer from the environment (tuning switches), dflt when unset
@@ -56,6 +63,19 @@ size_t multihead_ws_floats(int B, int NQ, int H_q, int H_kv, int NB_cap);
 int score_chunks(int NB_cap);
 
 // ---- attention ------------------------------------------------------------------
+// The next layer's scoring and selection inside a decode launch: each extra
+// workgroup scores per_wg 256-block chunks (one per group of four waves) and
+// keeps each chunk's top-k keys; the last workgroup to finish a row's chunks
+// merges them into the row's block set.
+struct StepScore {
+    const uint16_t* vec;      // next layer's indexer vectors, bf16 [rows, D] (NQ = 1)
+    const uint16_t* kt;       // next layer's compressed keys, bf16 [rows, NB_cap, D]
+    uint64_t* cand;           // [rows, cpr, top_k] per-chunk lists
+    int* counters;            // [rows] chunk arrivals; zero between calls
+    SelectArgs sel;           // rows = B * H_kv
+    int cpr;                  // chunks per row
+    int per_wg;               // chunks per workgroup (groups of four waves)
+};
 struct AttnArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -79,25 +99,19 @@ struct AttnArgs {
     int waves;                // waves per workgroup
     int fused_combine;        // 1: the last split's workgroup merges; 0: separate merge launch
     float scale_log2;         // scale * log2(e)
-    // Optional (the decode-step entry point): finish the next layer's
-    // selection in this launch.  Selection row r is merged by the last (least
-    // loaded) wave of workgroup (split r / tasks, task r % tasks), after its
-    // own blocks; its lists reach LDS by direct loads issued at the start.
-    const uint64_t* fin_cand; // [fin.rows, fin_nch, fin.top_k] keys; null = off
-    SelectArgs fin;
-    int fin_nch;
+    // Optional (the decode-step entry point): workgroups past the attention
+    // grid score the next layer and select its blocks (step.cand null = off)
+    StepScore step;
 };
 struct AttnPlan {
     int waves;                // waves per workgroup
     int n_split;              // workgroups per row group
 };
 int attn_rows_pad(int C, int G);                 // 16 or 32
-// extra_lds: LDS beyond the V tiles and the union (the selection finish)
 AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode, int NB_cap, int n_sel_max,
-                   int split_k, size_t extra_lds = 0);
+                   int split_k);
 size_t attn_ws_bytes(int tasks, int n_split, int rows_pad, int d);
-size_t attn_smem_bytes_host(int d, int rows_pad, int W, int C, int mode, int NB_cap, int n_sel_max,
-                            size_t extra_lds = 0);
+size_t attn_smem_bytes_host(int d, int rows_pad, int W, int C, int mode, int NB_cap, int n_sel_max);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 // ---- offload gather -----------------------------------------------------------------

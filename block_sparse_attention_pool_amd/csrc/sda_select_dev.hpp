@@ -1,6 +1,6 @@
 // Device helpers of the top-k selection shared by the scoring launch and the
-// decode launch that finishes the next layer's selection: ordered block keys,
-// wave ranks, sorted-list merges and the final merge of a row's chunk lists.
+// decode-step launch: ordered block keys, the key score, bitonic networks
+// across lanes, the per-chunk top-k and the final merge of a row's lists.
 #pragma once
 #include "sda_device.hpp"
 #include "sda_internal.h"
@@ -14,149 +14,185 @@ __device__ __forceinline__ uint64_t block_key(float s, int j) {
     return ((uint64_t)float_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
 }
 
-// number of keys larger than `key` among the 64 lanes of the wave: the keys
-// travel once round the wave through register rotations
-__device__ __forceinline__ int wave_rank(uint64_t key) {
-    uint32_t hi = (uint32_t)(key >> 32), lo = (uint32_t)key;
-    int r = 0;
-#pragma unroll
-    for (int i = 1; i < kWave; ++i) {
-        hi = wave_ror1(hi);
-        lo = wave_ror1(lo);
-        r += ((((uint64_t)hi) << 32) | lo) > key;
-    }
-    return r;
+// ---- bitonic networks across the lanes of a wave ------------------------------
+// Lane i exchanges with lane i ^ J: quad permutes (J = 1, 2), swizzles inside
+// 32-lane halves (J = 4, 8, 16), a permute across halves (J = 32).
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+    if constexpr (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+    else if constexpr (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+    else if constexpr (J < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, (J << 10) | 0x1F);
+    else return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32) << 2), (int)x);
+}
+template <int J>
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t x) {
+    return ((uint64_t)lane_xor<J>((uint32_t)(x >> 32)) << 32) | lane_xor<J>((uint32_t)x);
 }
 
-// number of keys larger than x in the descending list L[0..len), 1 <= len <= 64:
-// the last key of each full 8-key segment tells how many whole segments are
-// larger, then the next segment is counted; two rounds of independent reads
-__device__ __forceinline__ int count_larger(const uint64_t* L, int len, uint64_t x) {
-    uint64_t v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = L[min(8 * i + 7, len - 1)];      // all reads in bounds, issued together
-    int seg = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) seg += (int)((8 * i + 7 < len) & (v[i] > x));
-    const int base = 8 * seg;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = L[min(base + i, len - 1)];
-    int n = base;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) n += (int)((base + i < len) & (v[i] > x));
-    return n;
+// compare-exchange with lane ^ J: the lane keeps the larger value if
+// keep_max, else the smaller
+template <int J, typename T>
+__device__ __forceinline__ T cmp_xchg(T v, bool keep_max) {
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit keys");
+    T p;
+    if constexpr (sizeof(T) == 8) p = (T)lane_xor64<J>((uint64_t)v);
+    else p = (T)lane_xor<J>((uint32_t)v);
+    return ((p > v) == keep_max) ? p : v;
 }
 
-// One round of pairwise merges over the workgroup: lists c < nl of `len`
-// descending keys (zero-padded, len >= K) at src + c * ss; the pair
-// (2m, 2m+1) becomes list m of its K largest keys at dst + m * ds.  The list
-// strides are odd numbers of keys so that lists start in different LDS banks.  A key's
-// place in the merged list is its place in its own list plus the number of
-// larger keys in the partner list; keys are distinct apart from the zero
-// padding, whose writes may coincide but carry the same value.
-// `t` and `nt`: this thread's index among the nt threads that share the round.
-__device__ __forceinline__ void merge_round(const uint64_t* src, int nl, int len, int ss, uint64_t* dst, int ds,
-                                            int K, int t, int nt) {
-    const int items = nl * K;                              // only the first K of a list can stay
-    for (int i = t; i < items; i += nt) {
-        const int c = i / K, p = i - c * K;
-        const uint64_t x = src[c * ss + p];
-        int pos = p;
-        if ((c ^ 1) < nl) pos += count_larger(src + (c ^ 1) * ss, len, x);
-        if (pos < K) dst[(c >> 1) * ds + pos] = x;
+// Sort each aligned segment of P lanes (P a power of two <= 64), largest
+// first if DESC, else smallest first.  Stage (k, j): blocks of k lanes
+// alternate direction until the last, which takes the segment's direction.
+template <int P, bool DESC, int k = 2, typename T>
+__device__ __forceinline__ T bitonic_sort(T v, int lane) {
+    // the lane masks of the stages are cheap to recompute: keep the compiler
+    // from hoisting them into long-lived scalar registers
+    if constexpr (k == 2) asm volatile("" : "+v"(lane));
+    if constexpr (k <= P) {
+        const bool blk = (k == P) ? DESC : (((lane & k) == 0) == DESC);
+        if constexpr (k / 2 >= 32) v = cmp_xchg<32>(v, ((lane & 32) == 0) == blk);
+        if constexpr (k / 2 >= 16) v = cmp_xchg<((k / 2) >= 32 ? 16 : k / 2 >= 16 ? 16 : 1)>(v, ((lane & 16) == 0) == blk);
+        if constexpr (k / 2 >= 8) v = cmp_xchg<8>(v, ((lane & 8) == 0) == blk);
+        if constexpr (k / 2 >= 4) v = cmp_xchg<4>(v, ((lane & 4) == 0) == blk);
+        if constexpr (k / 2 >= 2) v = cmp_xchg<2>(v, ((lane & 2) == 0) == blk);
+        v = cmp_xchg<1>(v, ((lane & 1) == 0) == blk);
+        return bitonic_sort<P, DESC, 2 * k>(v, lane);
+    } else {
+        return v;
     }
 }
 
-// Level 2 of the selection for one row: merge the nch sorted chunk lists of
-// the row (K = top_k keys each, at `src`) pairwise, round by round, and write
-// the row's block set init U top-k U local, ascending, padded with -1.  Every
-// thread of the workgroup calls it (it holds barriers).  `coherent`: the lists
-// were written in this launch by other workgroups (agent-scope loads).
-// LDS: bufA (K|1)*nch keys, bufB (K|1)*ceil(nch/2) keys, sel_j kFusedTopK ints.
-template <bool coherent>
-__device__ __forceinline__ void finish_row(const SelectArgs& s, const uint64_t* src, int nch, int vrow, int nb,
-                                           uint64_t* bufA, uint64_t* bufB, int* sel_j) {
-    const int tid = threadIdx.x;
+// Sort a bitonic sequence held by each aligned segment of P lanes, largest first.
+template <int P, typename T>
+__device__ __forceinline__ T bitonic_merge_desc(T v, int lane) {
+    asm volatile("" : "+v"(lane));
+    if constexpr (P >= 64) v = cmp_xchg<32>(v, (lane & 32) == 0);
+    if constexpr (P >= 32) v = cmp_xchg<16>(v, (lane & 16) == 0);
+    if constexpr (P >= 16) v = cmp_xchg<8>(v, (lane & 8) == 0);
+    if constexpr (P >= 8) v = cmp_xchg<4>(v, (lane & 4) == 0);
+    if constexpr (P >= 4) v = cmp_xchg<2>(v, (lane & 2) == 0);
+    if constexpr (P >= 2) v = cmp_xchg<1>(v, (lane & 1) == 0);
+    return v;
+}
+
+// Score of one pooled key against a vector slice: lane li of each 16-lane row
+// holds EPL consecutive dims of both; fused multiply-adds in dim order, then
+// the sum over the 16 lanes.  Every scoring path uses it, so their scores
+// agree bit for bit.
+template <int EPL>
+__device__ __forceinline__ float key_dot(const float (&fv)[EPL], const uint32_t* kp) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) {
+        acc = fmaf(fv[2 * i], bf16lo(kp[i]), acc);
+        acc = fmaf(fv[2 * i + 1], bf16hi(kp[i]), acc);
+    }
+    return row16_sum(acc);
+}
+
+// Level 1 of the selection for one 256-block chunk, by a group of four waves
+// (thread t = 0..255 of the group; the group may be part of a larger
+// workgroup): sc[t] is the score of block j0 + t; the chunk's K <= 64 best
+// keys among blocks in [lo, hi), largest first and zero-padded, go to
+// dst[0..K) with agent-scope stores.  Each wave sorts its 64 keys with a
+// bitonic network; the four sorted lists merge pairwise (the top 64 of two
+// descending lists is the lane-wise max of one and the other reversed, a
+// bitonic sequence).  Every thread of the workgroup calls it (three
+// workgroup barriers); groups without a chunk pass active = false.
+// LDS per group: wl, 4 * 64 keys.
+__device__ __forceinline__ void chunk_top_k(const float* sc, int j0, int lo, int hi, int K, bool active,
+                                            uint64_t* wl, uint64_t* dst, int t) {
+    const int lane = t % kWave, wave = t / kWave;
+    const int j = j0 + t;
+    uint64_t v = 0;
+    if (active) {                                      // uniform over the wave
+        const bool valid = j >= lo && j < hi;
+        v = bitonic_sort<kWave, true>(valid ? block_key(sc[t], j) : 0ull, lane);
+        if (wave & 1) wl[wave * kWave + lane] = v;
+    }
+    __syncthreads();
+    if (active && !(wave & 1)) {
+        const uint64_t p = wl[(wave + 1) * kWave + (kWave - 1 - lane)];
+        v = bitonic_merge_desc<kWave>(v > p ? v : p, lane);
+        if (wave == 2) wl[2 * kWave + lane] = v;
+    }
+    __syncthreads();
+    if (active && wave == 0) {
+        const uint64_t p = wl[2 * kWave + (kWave - 1 - lane)];
+        v = bitonic_merge_desc<kWave>(v > p ? v : p, lane);
+        if (lane < K) __hip_atomic_store(dst + lane, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();                            // wl free for the next chunk
+}
+
+// Level 2 of the selection for one row: the nch chunk lists of the row (K
+// keys each, descending, at `src`) are padded to P = 2^ceil(log2 K) keys and
+// merged pairwise, round by round (one P-lane segment of a wave per pair, a
+// bitonic merge of the lane-wise max of one list and the other reversed);
+// then one wave sorts the kk selected block ids ascending and the row's block
+// set init U top-k U local is written, padded with -1.  Every thread of the
+// workgroup calls it (workgroup barriers).  `coherent`: the lists were
+// written in this launch by other workgroups (agent-scope loads).
+// LDS: bufA nch * P keys, bufB ceil(nch / 2) * P keys (P <= 64).
+template <int P, bool coherent>
+__device__ __forceinline__ void finish_row_p(const SelectArgs& s, const uint64_t* src, int nch, int vrow, int nb,
+                                             uint64_t* bufA, uint64_t* bufB) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, W = blockDim.x / kWave;
     const int K = s.top_k;
-    const int KS = K | 1;
     const int lo = min(s.n_init, nb);                      // candidates are [lo, hi)
     const int hi = max(lo, nb - s.n_local);
     const int kk = min(K, hi - lo);
-    for (int i = tid; i < nch * K; i += blockDim.x) {
-        const int c = i / K;
-        bufA[c * KS + (i - c * K)] =
-            coherent ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : src[i];
+    for (int i = tid; i < nch * P; i += blockDim.x) {
+        const int c = i / P, p = i - c * P;
+        uint64_t x = 0;
+        if (p < K) x = coherent ? __hip_atomic_load(src + c * K + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : src[c * K + p];
+        bufA[i] = x;
     }
     __syncthreads();
     uint64_t* cur = bufA;
     uint64_t* nxt = bufB;
+    constexpr int SPW = kWave / P;                         // pairs per wave and pass
+    const int seg = lane / P, i = lane % P;
     for (int nl = nch; nl > 1; nl = (nl + 1) >> 1) {
-        merge_round(cur, nl, K, KS, nxt, KS, K, tid, blockDim.x);
+        const int np = (nl + 1) >> 1;                      // an odd last list passes through unchanged
+        for (int base = wave * SPW; base < np; base += W * SPW) {
+            const int m = base + seg;
+            const bool ok = m < np;
+            const uint64_t x = ok ? cur[2 * m * P + i] : 0ull;
+            const uint64_t y = (ok && 2 * m + 1 < nl) ? cur[(2 * m + 1) * P + (P - 1 - i)] : 0ull;
+            const uint64_t v = bitonic_merge_desc<P>(x > y ? x : y, lane);
+            if (ok) nxt[m * P + i] = v;
+        }
         __syncthreads();
         uint64_t* t = cur; cur = nxt; nxt = t;
     }
-    if (tid < kk) sel_j[tid] = (int)(0xFFFFFFFFu - (uint32_t)cur[tid]);
-    __syncthreads();
     int32_t* out = s.block_idx + (size_t)vrow * s.n_sel_max;
-    for (int i = tid; i < lo; i += blockDim.x) out[i] = i;                   // initial blocks
-    if (tid < kk) {                                                          // top-k, ascending
-        const int jt = sel_j[tid];
-        int pos = 0;
-#pragma unroll
-        for (int u = 0; u < kFusedTopK; u += 4) {
-            const int4 q = *reinterpret_cast<const int4*>(sel_j + u);
-            pos += (u + 0 < kk && q.x < jt) + (u + 1 < kk && q.y < jt) +
-                   (u + 2 < kk && q.z < jt) + (u + 3 < kk && q.w < jt);
-        }
-        out[lo + pos] = jt;
+    if (wave == 0 && kk > 0) {                             // top-k ids, ascending
+        uint32_t id = lane < kk ? 0xFFFFFFFFu - (uint32_t)cur[lane] : 0xFFFFFFFFu;
+        id = bitonic_sort<kWave, false>(id, lane);
+        if (lane < kk) out[lo + lane] = (int)id;
     }
-    for (int i = tid; i < nb - hi; i += blockDim.x) out[lo + kk + i] = hi + i;  // local blocks
+    for (int i2 = tid; i2 < lo; i2 += blockDim.x) out[i2] = i2;                    // initial blocks
+    for (int i2 = tid; i2 < nb - hi; i2 += blockDim.x) out[lo + kk + i2] = hi + i2;  // local blocks
     const int total = lo + kk + (nb - hi);
     for (int p = total + tid; p < s.n_sel_max; p += blockDim.x) out[p] = -1;
     if (tid == 0) s.n_sel[vrow] = total;
-    __syncthreads();                                       // bufA / sel_j may be reused
+    __syncthreads();                                       // bufA / bufB may be reused
 }
 
-// Level 2 for one row by a single wave, with no workgroup barrier (the other
-// waves of the workgroup go on with their own work): the row's nch chunk
-// lists (K keys each, stride K) are already in LDS at `lists`; `tmp` holds
-// ceil(nch/2) * K keys, `sel_j` kFusedTopK ints.  Same block set as finish_row.
-__device__ __forceinline__ void wave_lds_sync() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's LDS writes are visible to its lanes
-}
-
-__device__ __forceinline__ void finish_row_wave(const SelectArgs& s, uint64_t* lists, uint64_t* tmp, int* sel_j,
-                                                int nch, int vrow, int nb, int lane) {
-    const int K = s.top_k;
-    const int lo = min(s.n_init, nb);
-    const int hi = max(lo, nb - s.n_local);
-    const int kk = min(K, hi - lo);
-    uint64_t* cur = lists;
-    uint64_t* nxt = tmp;
-    for (int nl = nch; nl > 1; nl = (nl + 1) >> 1) {
-        merge_round(cur, nl, K, K, nxt, K, K, lane, kWave);
-        wave_lds_sync();
-        uint64_t* t = cur; cur = nxt; nxt = t;
+template <bool coherent>
+__device__ __forceinline__ void finish_row(const SelectArgs& s, const uint64_t* src, int nch, int vrow, int nb,
+                                           uint64_t* bufA, uint64_t* bufB) {
+    switch (pow2_at_least(s.top_k)) {
+        case 1: finish_row_p<1, coherent>(s, src, nch, vrow, nb, bufA, bufB); break;
+        case 2: finish_row_p<2, coherent>(s, src, nch, vrow, nb, bufA, bufB); break;
+        case 4: finish_row_p<4, coherent>(s, src, nch, vrow, nb, bufA, bufB); break;
+        case 8: finish_row_p<8, coherent>(s, src, nch, vrow, nb, bufA, bufB); break;
+        case 16: finish_row_p<16, coherent>(s, src, nch, vrow, nb, bufA, bufB); break;
+        case 32: finish_row_p<32, coherent>(s, src, nch, vrow, nb, bufA, bufB); break;
+        default: finish_row_p<64, coherent>(s, src, nch, vrow, nb, bufA, bufB); break;
     }
-    if (lane < kk) sel_j[lane] = (int)(0xFFFFFFFFu - (uint32_t)cur[lane]);
-    wave_lds_sync();
-    int32_t* out = s.block_idx + (size_t)vrow * s.n_sel_max;
-    for (int i = lane; i < lo; i += kWave) out[i] = i;
-    if (lane < kk) {
-        const int jt = sel_j[lane];
-        int pos = 0;
-#pragma unroll
-        for (int u = 0; u < kFusedTopK; u += 4) {
-            const int4 q = *reinterpret_cast<const int4*>(sel_j + u);
-            pos += (u + 0 < kk && q.x < jt) + (u + 1 < kk && q.y < jt) +
-                   (u + 2 < kk && q.z < jt) + (u + 3 < kk && q.w < jt);
-        }
-        out[lo + pos] = jt;
-    }
-    for (int i = lane; i < nb - hi; i += kWave) out[lo + kk + i] = hi + i;
-    const int total = lo + kk + (nb - hi);
-    for (int p = total + lane; p < s.n_sel_max; p += kWave) out[p] = -1;
-    if (lane == 0) s.n_sel[vrow] = total;
 }
 
 }  // namespace sda

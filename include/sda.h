@@ -191,13 +191,14 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
  * indexer vectors choose layer l+1's blocks while layer l attends).  The
  * block sets are those of sda_score_select(f_next, k_tilde_next, ...), bit for
  * bit; out and lse are those of sda_sparse_decode(q, k, v, ...) with one
- * query per sequence (NQ = 1) up to the order of summation
- * (bit for bit when both take the same launch shape, e.g. the same split_k
- * with room left in LDS).  Two launches: the scoring of layer l+1, which
- * stops at its per-chunk candidate lists, then layer l's decode, in which the
- * last wave of each workgroup of the first split merges one row's lists into
- * its block set after its own blocks.  When the lists do not fit that merge
- * (top_k > 64 or NB_cap_next > 4096) it runs the two calls as they are.
+ * query per sequence (NQ = 1) up to the order of summation (bit for bit when
+ * both take the same launch shape, e.g. the same split_k).  One launch: the
+ * workgroups of the decode come first; workgroups past them score layer
+ * l+1's compressed keys (a 256-block chunk per four waves, at most two per
+ * workgroup), keep each chunk's top-k
+ * and, in the last workgroup to finish a row, merge the chunk lists into the
+ * row's block set.  When the lists do not fit that (top_k > 64, NB_cap_next
+ * > 4096, or a launch shape of fewer than four waves) it runs the two calls.
  *
  *   q .. split_k           as sda_sparse_decode (NQ = 1, no slot table)
  *   f_next .. n_sel_next   as sda_score_select for layer l+1 (NQ = 1);
