@@ -195,10 +195,10 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
  * both take the same launch shape, e.g. the same split_k).  One launch: the
  * workgroups of the decode come first; workgroups past them score layer
  * l+1's compressed keys (a 256-block chunk per four waves, at most two per
- * workgroup), keep each chunk's top-k
- * and, in the last workgroup to finish a row, merge the chunk lists into the
- * row's block set.  When the lists do not fit that (top_k > 64, NB_cap_next
- * > 4096, or a launch shape of fewer than four waves) it runs the two calls.
+ * workgroup), keep each chunk's top-k and, in the last workgroup to finish a
+ * row, merge the chunk lists into the row's block set.  When the lists do not
+ * fit that (top_k > 64, NB_cap_next > 4096, or a launch shape of fewer than
+ * four waves) it runs the two calls.
  *
  *   q .. split_k           as sda_sparse_decode (NQ = 1, no slot table)
  *   f_next .. n_sel_next   as sda_score_select for layer l+1 (NQ = 1);
