@@ -763,7 +763,6 @@ int env_int(const char* name, int dflt) {
 
 int attn_rows_pad(int C, int G) { return (C * G <= 16) ? 16 : 32; }
 
-constexpr int kCUs = 256;                  // MI355X compute units
 constexpr size_t kLdsPerCU = 160 * 1024;
 
 

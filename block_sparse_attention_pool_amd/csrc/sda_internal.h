@@ -62,6 +62,8 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 size_t multihead_ws_floats(int B, int NQ, int H_q, int H_kv, int NB_cap);
 int score_chunks(int NB_cap);
 
+constexpr int kCUs = 256;                  // MI355X compute units
+
 // ---- attention ------------------------------------------------------------------
 // The next layer's scoring and selection inside a decode launch: each extra
 // workgroup scores per_wg 256-block chunks (one per group of four waves) and

@@ -15,14 +15,29 @@ __device__ __forceinline__ uint64_t block_key(float s, int j) {
 }
 
 // ---- bitonic networks across the lanes of a wave ------------------------------
-// Lane i exchanges with lane i ^ J: quad permutes (J = 1, 2), swizzles inside
-// 32-lane halves (J = 4, 8, 16), a permute across halves (J = 32).
+// Lane i reads the value of lane i ^ J, all in VALU operations: quad
+// permutes (J = 1, 2); row shifts by J up and down, picked by the lane's bit J
+// (J = 4, 8); gfx950's swap of adjacent 16-lane rows (J = 16) and of the two
+// 32-lane halves (J = 32), whose two results hold the partner's value in the
+// lanes of one half each.
 template <int J>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
-    if constexpr (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
-    else if constexpr (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
-    else if constexpr (J < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, (J << 10) | 0x1F);
-    else return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32) << 2), (int)x);
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+    } else if constexpr (J == 4 || J == 8) {
+        const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x100 + J, 0xF, 0xF, false);  // lane + J
+        const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x110 + J, 0xF, 0xF, false);  // lane - J
+        return (__lane_id() & J) ? dn : up;
+    } else if constexpr (J == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (__lane_id() & 16) ? r[0] : r[1];
+    } else {
+        static_assert(J == 32, "lane distance");
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (__lane_id() & 32) ? r[0] : r[1];
+    }
 }
 template <int J>
 __device__ __forceinline__ uint64_t lane_xor64(uint64_t x) {
