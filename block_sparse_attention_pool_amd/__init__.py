@@ -57,6 +57,7 @@ _SIGNATURES = {
     "sda_gather_blocks": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int,
                                    _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p]),
     "sda_decode_step_workspace": (_c_size_t, [_c_int] * 8),
+    "sda_decode_step_is_fused": (_c_int, [_c_int] * 8),
     "sda_decode_step": (_c_int, [_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_void_p, _c_void_p, _c_int]
                         + [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 3 + [_c_size_t, _c_void_p]),
 }

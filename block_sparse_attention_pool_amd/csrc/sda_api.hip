@@ -328,11 +328,20 @@ static bool step_fused_plan(int B, int H_q, int H_kv, int d, int n_sel_max, int 
     // 2 splits, 28.5 us per step, against 30.7 us with the decode's own
     // choice of 4 splits over all units)
     const int tasks = B * H_kv;
-    const int sk = split_k > 0 ? split_k : max(1, kCUs / (2 * tasks));
+    // (and at least four waves per workgroup: a scoring group needs them)
+    const int sk = split_k > 0 ? split_k : max(1, min(kCUs / (2 * tasks), n_sel_max / 4));
     *plan = attn_plan(d, attn_rows_pad(1, H_q / H_kv), tasks, n_sel_max, 1, SDA_GROUP_EXACT, 1, n_sel_max, sk);
     // a scoring workgroup needs at least one group of four waves
     return plan->waves >= 4 &&
            step_lds_bytes(top_k, score_chunks(NB_cap_next), min(plan->waves / 4, 2)) <= 160 * 1024;
+}
+
+int sda_decode_step_is_fused(int B, int H_q, int H_kv, int d, int n_sel_max, int split_k, int NB_cap_next,
+                             int top_k) {
+    if (B < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || NB_cap_next < 1 || top_k < 0 || H_q % H_kv) return 0;
+    if (check_d(d) != SDA_OK) return 0;
+    AttnPlan plan{};
+    return step_fused_plan(B, H_q, H_kv, d, n_sel_max, split_k, NB_cap_next, top_k, &plan) ? 1 : 0;
 }
 
 size_t sda_decode_step_workspace(int B, int H_q, int H_kv, int d, int n_sel_max, int split_k, int NB_cap_next,

@@ -208,6 +208,10 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
  */
 size_t sda_decode_step_workspace(int B, int H_q, int H_kv, int d, int n_sel_max, int split_k,
                                  int NB_cap_next, int top_k);
+/* 1 if sda_decode_step with these sizes runs as one launch, 0 if it runs the
+ * two calls (or the sizes are invalid). */
+int sda_decode_step_is_fused(int B, int H_q, int H_kv, int d, int n_sel_max, int split_k,
+                             int NB_cap_next, int top_k);
 sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const int32_t* seq_len,
                              const int32_t* block_idx, const int32_t* n_sel, int n_sel_max, int T_cap,
                              int B, int H_q, int H_kv, int d, float scale, float* out, float* lse_opt,

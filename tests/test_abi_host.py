@@ -38,7 +38,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
         assert n in sda.exported_symbols(), n
@@ -174,11 +174,20 @@ def test_gather_validation(L):
 
 
 def test_decode_step_workspace_and_validation(L):
-    # fused: the decode's partials (planned with the merge's LDS) + the
-    # score/select workspace of the next layer; aliasing lists are refused
+    # the decode's partials + the score/select workspace of the next layer;
+    # aliasing lists are refused
     n = L.sda_decode_step_workspace(8, 64, 8, 128, 35, 0, 2048, 32)
     assert n >= L.sda_score_select_workspace(8, 1, 8, 2048, 32)
     assert L.sda_decode_step_workspace(0, 64, 8, 128, 35, 0, 2048, 32) == 0
+    # one launch at the 128K shape; two calls when the lists are too long for
+    # the in-launch merge or a workgroup would have fewer than four waves
+    assert L.sda_decode_step_is_fused(8, 64, 8, 128, 35, 0, 2048, 32) == 1
+    assert L.sda_decode_step_is_fused(8, 64, 8, 128, 100, 0, 2048, 97) == 0      # top_k > 64
+    assert L.sda_decode_step_is_fused(8, 64, 8, 128, 35, 0, 5000, 32) == 0       # 20 chunks
+    assert L.sda_decode_step_is_fused(1, 8, 2, 64, 3, 0, 64, 1) == 0             # 3 entries: one wave
+    assert L.sda_decode_step_is_fused(1, 8, 2, 64, 11, 0, 64, 8) == 1
+    assert L.sda_decode_step_is_fused(8, 64, 8, 128, 35, 0, 2048, 0) == 0        # no top-k: two calls
+    assert L.sda_decode_step_is_fused(8, 64, 8, 96, 35, 0, 2048, 32) == 0        # unsupported head dim
     f = L.sda_decode_step
     base = [P, P, P, P, P, P, 35, 4096, 1, 8, 2, 64, 0.125, P, None, 0,
             P, P, P, 64, 1, 2, 8, 11, P + 256, P + 512, P, 1 << 24, None]

@@ -304,6 +304,51 @@ def test_decode_step_matches_separate_calls(cid, fused, split_k, exact):
             os.environ["SDA_STEP_FUSED"] = old
 
 
+@pytest.mark.parametrize("d,top_k,n_init,n_local,split_k", [(128, 32, 1, 2, 0), (64, 8, 0, 3, 0),
+                                                       (128, 64, 2, 0, 3), (128, 5, 3, 1, 2), (64, 16, 1, 2, 1)])
+def test_decode_step_ragged(d, top_k, n_init, n_local, split_k):
+    # ragged lengths in both layers, the next layer's capacity not a multiple
+    # of a chunk, sequences shorter than init + local, one-block sequences:
+    # the step's block sets equal sda_score_select's, its outputs
+    # sda_sparse_decode's (bit for bit with the same explicit split count)
+    B, H_kv, G = 3, 2, 4
+    H_q = H_kv * G
+    T_cap, NBn = 5000, 300
+    gen = torch.Generator(device=DEV).manual_seed(7 * d + top_k)
+    def rnd(*shape, scale=1.0):
+        return (torch.randn(*shape, generator=gen, device=DEV) * scale).to(torch.bfloat16)
+    K, V = rnd(B, H_kv, T_cap, d), rnd(B, H_kv, T_cap, d)
+    Kn = rnd(B, H_kv, NBn * 64, d)
+    Q, F0, F1 = rnd(B, 1, H_q, d), rnd(B, 1, H_kv, d, scale=d ** -0.5), rnd(B, 1, H_kv, d, scale=d ** -0.5)
+    seq0 = torch.tensor([5000, 3000, 65], dtype=torch.int32, device=DEV)
+    seq1 = torch.tensor([NBn * 64 - 5, 64 * 3, 1], dtype=torch.int32, device=DEV)
+    zero = torch.zeros(B, dtype=torch.int32, device=DEV)
+    kt0 = torch.zeros((B, H_kv, -(-T_cap // 64), d), dtype=torch.bfloat16, device=DEV)
+    kt1 = torch.zeros((B, H_kv, NBn, d), dtype=torch.bfloat16, device=DEV)
+    sda.sda_update_compressed_keys(K, kt0, zero, seq0, T_cap)
+    sda.sda_update_compressed_keys(Kn, kt1, zero, seq1, NBn * 64)
+    sel = (n_init, n_local, top_k)
+    bi0, ns0 = sda.sda_score_select(F0, kt0, seq0, *sel)
+    ref_bi1, ref_ns1 = sda.sda_score_select(F1, kt1, seq1, *sel)
+    ref_out, ref_lse = sda.sda_sparse_decode(Q, K, V, seq0, bi0, ns0, split_k=split_k)
+    nsm = bi0.shape[-1]
+    fused = sda.lib().sda_decode_step_is_fused(B, H_q, H_kv, d, nsm, split_k, NBn, top_k)
+    _say(f"ragged step d={d} top_k={top_k} split_k={split_k}: one launch = {fused}")
+    assert fused == 1
+    for it in range(4):
+        out, lse, bi1, ns1 = sda.sda_decode_step(Q, K, V, seq0, bi0, ns0, F1, kt1, seq1, *sel, split_k=split_k)
+        torch.cuda.synchronize()
+        assert torch.equal(ns1, ref_ns1) and torch.equal(bi1, ref_bi1), it
+        if split_k > 0:
+            assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), it
+        else:
+            assert (out - ref_out).abs().max().item() <= 1e-5, it
+            assert ((lse - ref_lse).abs().nan_to_num(0.0)).max().item() <= 1e-5, it
+    # the one-block sequence selects its only block; the three-block one all of its blocks
+    assert int(ns1[2, 0, 0]) == 1 and int(bi1[2, 0, 0, 0]) == 0
+    assert int(ns1[1, 0, 0]) == 3 and list(bi1[1, 0, 0, :3].tolist()) == [0, 1, 2]
+
+
 def test_select_ties_go_to_lower_index():
     rng = np.random.default_rng(5)
     NB, d = 300, 128
