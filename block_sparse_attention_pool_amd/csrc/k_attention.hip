@@ -65,9 +65,12 @@ struct VTile {
 
 // LDS of a workgroup of W waves: W V tiles, reused for the wave merge; the
 // union lists of the grouped mode follow
+// rows of the wave-merge area are padded by 4 floats: rows 16 apart in a wave's
+// write land in different LDS banks
+constexpr int kMergePad = 4;
 __host__ __device__ inline size_t smem_base(int D, int RP, int W) {
     const size_t v = (size_t)W * kBlock * D * 2;
-    const size_t m = (size_t)W * RP * (D + 2) * sizeof(float);
+    const size_t m = (size_t)W * RP * (D + kMergePad + 2) * sizeof(float);
     return ((v > m ? v : m) + 15) / 16 * 16;
 }
 // LDS of the exact union: the C lists, the union ids and masks, per-wave
@@ -540,7 +543,8 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
     __syncthreads();
     float* sm_m = reinterpret_cast<float*>(smem);        // [W][RP]
     float* sm_l = sm_m + W * RP;                          // [W][RP]
-    float* sm_o = sm_l + W * RP;                          // [W][RP][D]
+    float* sm_o = sm_l + W * RP;                          // [W][RP][D + kMergePad]
+    constexpr int OS = D + kMergePad;                     // row stride of sm_o
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int r = nt * 16 + li;
@@ -550,7 +554,7 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
         }
 #pragma unroll
         for (int md = 0; md < MTD; ++md)
-            *reinterpret_cast<floatx4*>(&sm_o[(wave * RP + r) * D + md * 16 + lg * 4]) = o[md][nt];
+            *reinterpret_cast<floatx4*>(&sm_o[(wave * RP + r) * OS + md * 16 + lg * 4]) = o[md][nt];
     }
     __syncthreads();
 
@@ -565,7 +569,7 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
             if (w < W) {
                 mw[w] = sm_m[w * RP + r];
                 lw[w] = sm_l[w * RP + r];
-                ow[w] = *reinterpret_cast<const floatx4*>(&sm_o[(w * RP + r) * D + d4]);
+                ow[w] = *reinterpret_cast<const floatx4*>(&sm_o[(w * RP + r) * OS + d4]);
             } else {
                 mw[w] = -INFINITY;
                 lw[w] = 0.f;
