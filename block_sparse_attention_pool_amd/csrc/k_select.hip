@@ -224,10 +224,9 @@ struct ScoreArgs {
     SelectArgs sel;          // FUSED only
     uint64_t* cand;          // FUSED: [B*NQ*H_kv, chunks, top_k] keys
     int* counters;           // FUSED: [B*H_kv*vector tiles], zero between calls
-    float* stats;            // scores-and-stats mode: [vector rows, chunks] (max, sum of exp(s - max))
 };
 
-constexpr int kScoresOnly = 0, kFusedSelect = 1, kScoresAndStats = 2;   // score_kernel modes
+constexpr int kScoresOnly = 0, kFusedSelect = 1;   // score_kernel modes
 
 // The selection inside a scoring launch: sc[v][t] holds the score of block
 // j0 + t for vector v0 + v of kv row `row` = b * H_kv + g (the grid is
@@ -275,13 +274,10 @@ __device__ __forceinline__ void select_tail(const SelectArgs& s, uint64_t* cand,
     if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// MODE kScoresAndStats (the G-head comparator): scores go to `out` as in
-// kScoresOnly, and each chunk workgroup also writes, per vector, the max of
-// its chunk's scores and the sum of exp(score - max) over the chunk.
 template <int D, int NV, int MODE>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     constexpr bool FUSED = MODE == kFusedSelect;
-    constexpr bool LDS_SC = MODE != kScoresOnly;
+    constexpr bool LDS_SC = FUSED;
     constexpr int EPL = D / 16;             // bf16 elements per lane of one pooled key (16 lanes per key)
     using KLoad = typename std::conditional<EPL == 8, u32x4, u32x2>::type;
     const int row = blockIdx.y;             // b * H_kv + g
@@ -354,31 +350,6 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 
     if constexpr (FUSED)
         select_tail<NV>(a.sel, a.cand, a.counters, sc, b, g, row, a.NQ, a.H_kv, nvec, v0, j0, nb);
-    if constexpr (MODE == kScoresAndStats) {
-        __syncthreads();                                   // sc complete
-        for (int v = wave; v < NV; v += 4) {               // one wave per vector
-            const int vi = v0 + v;
-            if (vi >= nvec) break;
-            float m = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < kChunk / kWave; ++i)
-                if (j0 + lane + i * kWave < nb) m = fmaxf(m, sc[v][lane + i * kWave]);
-            for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-            float l = 0.f;
-            if (m != -INFINITY) {
-#pragma unroll
-                for (int i = 0; i < kChunk / kWave; ++i)
-                    if (j0 + lane + i * kWave < nb) l += expf(sc[v][lane + i * kWave] - m);
-            }
-            for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off, kWave);
-            if (lane == 0) {
-                const int q = vi / a.VPR, hv = g * a.VPR + (vi - (vi / a.VPR) * a.VPR);
-                float* st = a.stats + ((((size_t)b * a.NQ + q) * H_vec + hv) * gridDim.x + blockIdx.x) * 2;
-                st[0] = m;
-                st[1] = l;
-            }
-        }
-    }
 }
 
 template <int D, int MODE>
@@ -409,14 +380,14 @@ bool fused_select_ok(int NB_cap, int top_k) {
 hipError_t launch_score_select(const uint16_t* f, const uint16_t* kt, const SelectArgs& sel, int B, int d,
                                float* scores_opt, float* scores_ws, uint64_t* cand, int* counters,
                                hipStream_t s) {
-    if (cand) {            // counters null: level 1 only (the lists), merged by a later launch
-        ScoreArgs a{f, kt, sel.seq_len, scores_opt, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, cand, counters, nullptr};
+    if (cand) {            // the selection inside the scoring launch
+        ScoreArgs a{f, kt, sel.seq_len, scores_opt, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, cand, counters};
         if (d == 128) launch_score_d<128, kFusedSelect>(a, B, s);
         else launch_score_d<64, kFusedSelect>(a, B, s);
         return hipGetLastError();
     }
     float* scores = scores_opt ? scores_opt : scores_ws;
-    ScoreArgs a{f, kt, sel.seq_len, scores, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, nullptr, nullptr, nullptr};
+    ScoreArgs a{f, kt, sel.seq_len, scores, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, nullptr, nullptr};
     if (d == 128) launch_score_d<128, kScoresOnly>(a, B, s);
     else launch_score_d<64, kScoresOnly>(a, B, s);
     hipError_t e = hipGetLastError();
@@ -429,19 +400,108 @@ hipError_t launch_score_select(const uint16_t* f, const uint16_t* kt, const Sele
 // ---------------------------------------------------------------------------
 // G-head comparator: z = q_h . K~_j / tau, then s_j = sum_h softmax_j(z_h)
 // ---------------------------------------------------------------------------
-// Launch 1 is the scoring kernel with the G heads of a KV group as its
-// vectors (mode kScoresAndStats): z to the workspace plus, per head and chunk,
-// the chunk max and the sum of exp(z - max).  Launch 2, one workgroup per
-// (chunk, kv row, query): merges the row's chunk statistics into each head's
-// softmax max M_h and normaliser L_h, forms s_j = sum_h exp(z_hj - M_h) / L_h
-// for its 256 blocks and runs the in-launch selection on them (or writes the
-// scores for the selection launch when that does not apply).
+// Launch 1 (mh_score_kernel, one workgroup per 256-block chunk, KV row and
+// query): the G heads of the KV group times the chunk's compressed keys as a
+// small dense product on MFMA (keys x dims times dims x heads, four waves of
+// 64 keys), z to the workspace plus, per head and chunk, the chunk max and the
+// sum of exp(z - max).  Launch 2, one workgroup per (chunk, kv row, query):
+// merges the row's chunk statistics into each head's softmax max M_h and
+// normaliser L_h, forms s_j = sum_h exp(z_hj - M_h) / L_h for its 256 blocks
+// and runs the in-launch selection on them (or writes the scores for the
+// selection launch when that does not apply).
 // floats of [z, padded to 64 floats][chunk statistics, padded to 64 floats]
 size_t multihead_ws_floats(int B, int NQ, int H_q, int H_kv, int NB_cap) {
     (void)H_kv;
     const size_t z = ((size_t)B * NQ * H_q * NB_cap + 63) / 64 * 64;
     const size_t st = ((size_t)B * NQ * H_q * score_chunks(NB_cap) * 2 + 63) / 64 * 64;
     return z + st;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void mh_score_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kt,
+                                                       const int32_t* __restrict__ seq_len, float* __restrict__ z,
+                                                       float* __restrict__ stats, int NQ, int H_q, int H_kv, int G,
+                                                       int NB_cap, float mult) {
+    constexpr int KS = D / 32;                          // MFMA k-steps over the head dim
+    __shared__ float red[4][16];
+    const int row = blockIdx.y;                         // b * H_kv + g
+    const int b = row / H_kv, g = row - (row / H_kv) * H_kv;
+    const int qi = blockIdx.z;
+    const int nch = gridDim.x;
+    const int j0 = blockIdx.x * kChunk;
+    const int nb = min((seq_len[b] + kBlock - 1) / kBlock, NB_cap);
+    const int lane = __lane_id(), li = lane & 15, lg = lane >> 4;
+    const int wave = threadIdx.x / kWave;
+    const size_t hrow0 = ((size_t)b * NQ + qi) * H_q + (size_t)g * G;   // first head row of the group
+    const int jw = j0 + wave * kWave;                   // first key of this wave
+    // S^T = K~ Q^T: A = 16 keys x 32 dims, B = 32 dims x 16 heads (heads past G
+    // repeat the last one; their columns are never written)
+    floatx4 sv[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) sv[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (jw < nb) {
+        u32x4 qf[KS], kf[4][KS];
+        const uint16_t* qp = q + (hrow0 + min(li, G - 1)) * D + lg * 8;
+        const uint16_t* kb = kt + (size_t)row * NB_cap * D + lg * 8;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int key = min(jw + mt * 16 + li, nb - 1);   // past the length: a real key, result unused
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = ldg16(kb + (size_t)key * D + ks * 32);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = ldg16_cached(qp + ks * 32);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) sv[mt] = mfma16x16x32(kf[mt][ks], qf[ks], sv[mt]);
+    }
+    // lane (li, lg) holds z of head li for keys jw + mt*16 + lg*4 + i
+    float m = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sv[mt][i] *= mult;
+            if (jw + mt * 16 + lg * 4 + i < nb) m = fmaxf(m, sv[mt][i]);
+        }
+    if (li < G) {
+        float* zr = z + (hrow0 + li) * NB_cap;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int k0 = jw + mt * 16 + lg * 4;
+            if (k0 + 3 < nb) {
+                *reinterpret_cast<floatx4*>(zr + k0) = sv[mt];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (k0 + i < nb) zr[k0 + i] = sv[mt][i];
+            }
+        }
+    }
+    // chunk statistics per head: the max, then the sum of exp(z - max)
+    m = cross4_max(m);
+    if (lg == 0) red[wave][li] = m;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0][li], red[1][li]), fmaxf(red[2][li], red[3][li]));
+    float l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (jw + mt * 16 + lg * 4 + i < nb) l += expf(sv[mt][i] - M);
+    }
+    l = cross4_sum(l);
+    __syncthreads();                                    // the maxima have been read
+    if (lg == 0) red[wave][li] = l;
+    __syncthreads();
+    if (threadIdx.x < G) {
+        const int h = threadIdx.x;
+        float* st = stats + ((hrow0 + h) * nch + blockIdx.x) * 2;
+        st[0] = M;                                      // every wave of the workgroup computed the same M for h
+        st[1] = (red[0][h] + red[1][h]) + (red[2][h] + red[3][h]);
+    }
 }
 
 template <bool FUSED>
@@ -485,13 +545,15 @@ hipError_t launch_multihead_select(const uint16_t* q, const uint16_t* kt, const 
                                    int d, float tau, float* z, float* stats, float* scores_opt, float* scores_ws,
                                    uint64_t* cand, int* counters, hipStream_t s) {
     const int G = H_q / sel.H_kv;
-    ScoreArgs a{q, kt, sel.seq_len, z, sel.NQ, sel.H_kv, G, sel.NB_cap, 1.f / tau, SelectArgs{}, nullptr, nullptr,
-                stats};
-    if (d == 128) launch_score_d<128, kScoresAndStats>(a, B, s);
-    else launch_score_d<64, kScoresAndStats>(a, B, s);
+    dim3 grid(score_chunks(sel.NB_cap), B * sel.H_kv, sel.NQ), block(256);
+    if (d == 128)
+        hipLaunchKernelGGL(mh_score_kernel<128>, grid, block, 0, s, q, kt, sel.seq_len, z, stats, sel.NQ, H_q,
+                           sel.H_kv, G, sel.NB_cap, 1.f / tau);
+    else
+        hipLaunchKernelGGL(mh_score_kernel<64>, grid, block, 0, s, q, kt, sel.seq_len, z, stats, sel.NQ, H_q,
+                           sel.H_kv, G, sel.NB_cap, 1.f / tau);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid(score_chunks(sel.NB_cap), B * sel.H_kv, sel.NQ), block(256);
     if (cand && counters) {
         hipLaunchKernelGGL(mh_select_kernel<true>, grid, block, 0, s, z, stats, sel, H_q, G, scores_opt, cand,
                            counters);
