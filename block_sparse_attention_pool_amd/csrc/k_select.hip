@@ -205,15 +205,15 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
 // (out may be NULL when FUSED).
 //
 // FUSED (one vector per query, VPR = 1): the selection runs in the same launch
-// in two levels.  Each chunk workgroup ranks its 256 candidate blocks by the
-// key (score, then lower block index): each wave sorts its 64 keys by rank
-// counting over register rotations, and two rounds of pairwise merges of the
-// sorted wave lists leave the chunk's best top_k keys in rank order, which go
-// to `cand` with write-through stores.  Every chunk workgroup of a (kv row,
-// vector tile) then bumps an agent-scope arrival counter; the last one merges
-// the per-chunk sorted lists pairwise, round by round, and writes the block
-// set.  Each block lives in exactly one chunk and a global top-k
-// block is within its chunk's top-k, so the merge is exact.
+// in two levels.  Each chunk workgroup orders its 256 candidate blocks by the
+// key (score, then lower block index): each wave sorts its 64 keys with a
+// bitonic network across lanes and the sorted wave lists merge pairwise,
+// leaving the chunk's best top_k keys, largest first, which go to `cand` with
+// write-through stores.  Every chunk workgroup of a (kv row, vector tile)
+// then bumps an agent-scope arrival counter; the last one merges the
+// per-chunk sorted lists pairwise, round by round, and writes the block set.
+// Each block lives in exactly one chunk and a global top-k block is within
+// its chunk's top-k, so the merge is exact.
 struct ScoreArgs {
     const uint16_t* vec;
     const uint16_t* kt;      // bf16 [B, H_kv, NB_cap, D]
@@ -230,7 +230,7 @@ constexpr int kScoresOnly = 0, kFusedSelect = 1;   // score_kernel modes
 
 // The selection inside a scoring launch: sc[v][t] holds the score of block
 // j0 + t for vector v0 + v of kv row `row` = b * H_kv + g (the grid is
-// (chunks, B * H_kv, vector tiles)).  Level 1 ranks the chunk, level 2 (the
+// (chunks, B * H_kv, vector tiles)).  Level 1 orders the chunk, level 2 (the
 // last chunk workgroup of the row and tile to arrive) merges the chunk lists
 // and writes the block sets; see the comment at ScoreArgs.
 template <int NV>
@@ -248,8 +248,7 @@ __device__ __forceinline__ void select_tail(const SelectArgs& s, uint64_t* cand,
     const int hi = max(lo, nb - s.n_local);
     __syncthreads();                                   // sc complete
 
-    // level 1: rank inside each wave, then two rounds of pairwise merges
-    // give this chunk's best K keys in rank order
+    // level 1: this chunk's best K keys, largest first
     for (int v = 0; v < NV; ++v) {
         const int vi = v0 + v;
         if (vi >= nvec) break;                         // uniform over the workgroup

@@ -84,11 +84,6 @@ __device__ __forceinline__ u32x4 ldg16_cached(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
-// the value held by lane (lane - 1) mod 64 (DPP whole-wave rotate right by one)
-__device__ __forceinline__ uint32_t wave_ror1(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x13C, 0xF, 0xF, true);
-}
-
 // order-preserving map float -> uint32 (larger float -> larger key); -0 == +0
 __device__ __forceinline__ uint32_t float_key(float x) {
     uint32_t u = __float_as_uint(x);
