@@ -413,29 +413,38 @@ def copy_calibration(nbytes=1 << 30):
     print(json.dumps({"copy_bytes": nbytes, "launches": 3}))
 
 
-def timed_graph(step, L, steps):
-    """Capture the L-step layer ring as one HIP graph, replay it for exactly
-    `steps` steps (the remainder eagerly) between synchronisations; returns
-    (wall seconds, steps)."""
+def timed_graph(step, L, steps, per_graph=80):
+    """Time exactly `steps` steps as HIP graph replays between synchronisations:
+    one graph holds `per_graph` consecutive steps (a decode token through an
+    80-layer stack, cycling the L resident layers), a second one the remainder;
+    returns (wall seconds, steps)."""
     warm = torch.cuda.Stream()
     warm.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(warm):
         for i in range(L):
             step(i)
     torch.cuda.current_stream().wait_stream(warm)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(L):
-            step(i)
+    per_graph = max(L, per_graph // L * L)          # whole passes over the ring keep the lists chained
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                step(i)
+        return g
+    replays, rest = divmod(steps, per_graph)
+    full = capture(per_graph) if replays else None
+    tail = capture(rest) if rest else None
     torch.cuda.synchronize()
-    replays, rest = divmod(steps, L)
-    graph.replay()
+    for g in (full, tail):                           # one untimed replay of each
+        if g is not None:
+            g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(replays):
-        graph.replay()
-    for i in range(rest):
-        step(i)
+        full.replay()
+    if tail is not None:
+        tail.replay()
     torch.cuda.synchronize()
     return time.perf_counter() - t0, steps
 
@@ -643,7 +652,9 @@ def main():
             "seq_len": cfg.T,
             "parallelism": "single GPU",
             "config_id": cfg.cid,
-            "launch": ("eager prepared calls" if args.no_graph else f"HIP graph of the {L}-layer ring, replayed")
+            "launch": ("eager prepared calls" if args.no_graph else
+                       f"HIP graphs of 80 consecutive steps (a token through an 80-layer stack over the {L} "
+                       "resident layers), replayed")
                       + (", layer l+1's score_select beside layer l's sparse_decode (two streams)"
                          if args.overlap else
                          ", one sda_decode_step per layer (a scoring launch writes per-chunk candidate lists of "
