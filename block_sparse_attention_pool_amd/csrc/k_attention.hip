@@ -316,17 +316,17 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
     const int G = a.G;
     const int R = Cg * G;
     // The wave's block ids (global list) arrive by one vector load, lane k
-    // holding its k-th entry, issued before anything else; the length and the
-    // list count are scalar reads; then the Q loads.  The first K/V loads wait
-    // only for these, never for Q.
+    // holding its k-th entry; the length and the list count are scalar reads
+    // issued beside it, then the Q loads; nothing waits for any of them until
+    // all are issued, so the first K/V loads follow one round trip.
     const bool glist = L.gidx != nullptr;
     const int n_range = glist ? a.n_sel_max : L.n;
     const int e_begin = (split * n_range) / a.n_split;
     const int e_end = ((split + 1) * n_range) / a.n_split;
     const int32_t* slot_row = (a.slot && glist) ? a.slot + (L.gidx - a.block_idx) : nullptr;
     int e = e_begin + wave;
-    const int T = ld_ro(a.seq_len + b);
-    const int n_g = glist ? ld_ro(L.gn) : 0;
+    int T = ld_ro(a.seq_len + b);
+    int n_g = ld_ro(glist ? L.gn : a.seq_len + b);        // unused without a global list
     int id_v = -1, slot_v = -1;            // entries e + (it + lane) * W, it = 0, 64, ...
     auto load_ids = [&](int e0) {
         const int ee = e0 + lane * W;
@@ -335,9 +335,6 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
         if (slot_row) slot_v = ok ? slot_row[ee] : -1;
     };
     if (glist) load_ids(e);
-    if (glist) L.n = min(max(n_g, 0), a.n_sel_max);
-    const int nb = (T + kBlock - 1) / kBlock;
-    const int blocks_cap = (a.T_cap + kBlock - 1) / kBlock;
 
     // Q fragments (B operand of S^T = K Q^T): row nt*16 + li, d = ks*32 + lg*8
     u32x4 qf[NT][KS];
@@ -354,6 +351,11 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
         for (int ks = 0; ks < KS; ++ks)
             asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[nt][ks]) : "v"(qp + ks * 32) : "memory");
     }
+    // the scalar reads are first used here, after every load above is issued
+    asm volatile("" : "+s"(T), "+s"(n_g));
+    if (glist) L.n = min(max(n_g, 0), a.n_sel_max);
+    const int nb = (T + kBlock - 1) / kBlock;
+    const int blocks_cap = (a.T_cap + kBlock - 1) / kBlock;
 
 
     floatx4 o[MTD][NT];
@@ -661,8 +663,6 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
     const int b = t2 / a.n_groups;
     const int q0 = grp * a.C;
     const int Cg = min(a.C, a.NQ - q0);
-    const int T = ld_ro(a.seq_len + b);
-    const int nb = (T + kBlock - 1) / kBlock;
 
     ListView L{};
     char* after_v = smem + smem_base(D, NT * 16, blockDim.x / kWave);
@@ -675,6 +675,9 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
         // union unless an earlier query of the group, or the entry before it,
         // lists the same block; its membership mask comes from a binary
         // search in every list.  Joining entries are compacted in (c, e) order.
+        // (the global-list path reads the length inside the engine, after its
+        // block-id load is on its way: no round trip before that load)
+        const int nb = (ld_ro(a.seq_len + b) + kBlock - 1) / kBlock;
         const int nsm = a.n_sel_max;
         const int W = blockDim.x / kWave;
         int32_t* lst = reinterpret_cast<int32_t*>(after_v);                          // [C][nsm]
