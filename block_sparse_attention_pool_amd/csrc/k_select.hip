@@ -503,36 +503,74 @@ __global__ __launch_bounds__(256) void mh_score_kernel(const uint16_t* __restric
     }
 }
 
+// Second comparator launch, one workgroup per (chunk, KV row, query): each
+// head's softmax max and normaliser over the whole row, from the chunk
+// statistics of the first launch; then s_j = sum over the heads of
+// exp(z_hj - M_h) / L_h for this chunk's blocks, and the selection.  Every
+// global load (this thread's z for all heads, the statistics, the length) is
+// issued before the first wait, so the launch starts with one round trip.
+constexpr int kMaxHeads = 16;
 template <bool FUSED>
 __global__ __launch_bounds__(256) void mh_select_kernel(const float* __restrict__ z, const float* __restrict__ stats,
                                                         SelectArgs sel, int H_q, int G, float* scores_out,
                                                         uint64_t* cand, int* counters) {
     __shared__ float sc[1][kChunk];
-    __shared__ float mh[16], il[16];
+    __shared__ float pm[kMaxHeads][16], pl[kMaxHeads][16];   // per head: 16 partial (max, sum) pairs
+    __shared__ float mh[kMaxHeads], il[kMaxHeads];
     const int row = blockIdx.y;                          // b * H_kv + g
     const int H_kv = sel.H_kv, NQ = sel.NQ, NB_cap = sel.NB_cap;
     const int b = row / H_kv, g = row - (row / H_kv) * H_kv;
     const int q = blockIdx.z;
     const int nch = gridDim.x;
-    const int nb = min((sel.seq_len[b] + kBlock - 1) / kBlock, NB_cap);
     const int j0 = blockIdx.x * kChunk;
     const int tid = threadIdx.x;
     const size_t hrow0 = ((size_t)b * NQ + q) * H_q + (size_t)g * G;   // first head row of the group
+    const int j = j0 + tid;
+    // statistics: thread (sh, sc0) merges head sh's chunks sc0, sc0 + 16, ...;
+    // the first pair is read as one 64-bit load before anything waits
+    const int sh = tid >> 4, sc0 = tid & 15;
+    const float* st = stats + (hrow0 + min(sh, G - 1)) * nch * 2;
+    const bool has0 = sh < G && sc0 < nch;
+    const uint64_t p0 = has0 ? *reinterpret_cast<const uint64_t*>(st + 2 * sc0) : 0;
+    const int len = sel.seq_len[b];
+    // z of this thread's block for every head (past the length or the
+    // capacity: a real entry of the row, result unused)
+    const float* zc = z + hrow0 * NB_cap + min(j, NB_cap - 1);
+    float zv[kMaxHeads];
+#pragma unroll
+    for (int h = 0; h < kMaxHeads; ++h) zv[h] = (h < G) ? zc[(size_t)h * NB_cap] : 0.f;
+    float m = -INFINITY, l = 0.f;
+    auto merge_stat = [&](float cm, float cl) {
+        if (cm != -INFINITY) {                           // an empty chunk adds nothing
+            const float Mn = fmaxf(m, cm);
+            l = l * expf(m - Mn) + cl * expf(cm - Mn);
+            m = Mn;
+        }
+    };
+    if (has0) merge_stat(__uint_as_float((uint32_t)p0), __uint_as_float((uint32_t)(p0 >> 32)));
+    if (sh < G)
+        for (int c = sc0 + 16; c < nch; c += 16) merge_stat(st[2 * c], st[2 * c + 1]);
+    const int nb = min((len + kBlock - 1) / kBlock, NB_cap);
+    pm[sh][sc0] = m;
+    pl[sh][sc0] = l;
+    __syncthreads();
     if (tid < G) {
-        const float* st = stats + (hrow0 + tid) * nch * 2;
         float M = -INFINITY;
-        for (int c = 0; c < nch; ++c) M = fmaxf(M, st[2 * c]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) M = fmaxf(M, pm[tid][i]);
         float L = 0.f;
-        for (int c = 0; c < nch; ++c)
-            if (st[2 * c] != -INFINITY) L += st[2 * c + 1] * expf(st[2 * c] - M);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (pm[tid][i] != -INFINITY) L += pl[tid][i] * expf(pm[tid][i] - M);
         mh[tid] = M;
         il[tid] = 1.f / L;
     }
     __syncthreads();
-    const int j = j0 + tid;
     float sv = 0.f;
     if (j < nb) {
-        for (int h = 0; h < G; ++h) sv += expf(z[(hrow0 + h) * NB_cap + j] - mh[h]) * il[h];
+#pragma unroll
+        for (int h = 0; h < kMaxHeads; ++h)
+            if (h < G) sv += expf(zv[h] - mh[h]) * il[h];
         const size_t srow = ((size_t)b * NQ + q) * H_kv + g;
         if (scores_out) scores_out[srow * NB_cap + j] = sv;
     }
