@@ -30,7 +30,9 @@ Readings of points the pages leave open (numbered as in the design notes):
   mean of the tokens present; the local window is the last n_local blocks;
   init/local blocks do not compete in top-k; output block lists ascend;
   query head h reads KV head floor(h / G); attention scale 1/sqrt(d);
-  the G-head comparator sums per-head softmax over all blocks with tau = sqrt(d).
+  the G-head comparator sums per-head softmax over all blocks with tau = sqrt(d);
+  with overlapping compression (kernel l, stride s) a block's score is the
+  max over the compressed windows that share a token with it.
 
 Parity pins: every function here is pinned by tests under tests/ against
 closed forms, brute force or an independent library routine, except the
@@ -203,6 +205,69 @@ def multihead_scores(q_heads, kt, tau):
 def select_row_multihead(q_heads, kt_stored, n_init, n_local, k, tau):
     nb = kt_stored.shape[0]
     s = decision_scores(multihead_scores(q_heads, kt_stored, tau))
+    cand = candidates(nb, n_init, n_local)
+    return block_set(nb, n_init, n_local, top_k(s, cand, k)), s
+
+
+# ---------------------------------------------------------------------------
+# O12  overlapping compression and max-pool onto the block grid
+#      ([SparDA] prerequisites §3 eq. (4) with general kernel l and stride s;
+#      §4.4: inference compression l = 32, s = 16; §4.3 and fig. 3: the
+#      compressed scores are max-pooled onto the block grid)
+# ---------------------------------------------------------------------------
+
+def num_entries(T, stride):
+    """Compressed entries of a T-token sequence: the windows that start
+    before T, i.e. ceil(T / stride)."""
+    return -(-int(T) // int(stride))
+
+
+def compressed_keys_strided(k, T, window, stride):
+    """eq. (4) with kernel l = window and stride s: entry j is the mean of
+    tokens j*s .. min(j*s + l, T) - 1, for every j with j*s < T.  The last
+    windows are cut at T (Python-slice semantics, as for a partial block).
+    With window = stride = 64 this is compressed_keys.
+    k: float64 [>=T, d].  Returns float64 [ceil(T/s), d]."""
+    T = int(T)
+    n = num_entries(T, stride)
+    out = np.empty((n, k.shape[-1]), dtype=np.float64)
+    for j in range(n):
+        lo, hi = j * stride, min(j * stride + window, T)
+        out[j] = np.mean(k[lo:hi], axis=0)
+    return out
+
+
+def pool_range(J, window, stride, n_entries, block=BLOCK):
+    """Entries whose windows share at least one token with block J (reading:
+    the max-pool window of a block is every compressed window that overlaps
+    it): j*s < (J+1)*block and j*s + l > J*block, clipped to the entries
+    that exist.  Returns the inclusive range (lo, hi)."""
+    lo = max(0, -(-(J * block - window + 1) // stride))
+    hi = min(n_entries - 1, ((J + 1) * block - 1) // stride)
+    return lo, hi
+
+
+def max_pool_blocks(entry_scores, T, window, stride, block=BLOCK):
+    """Block score = max of the scores of the compressed windows that overlap
+    the block.  entry_scores: [ceil(T/s)]; returns [ceil(T/block)]."""
+    e = np.asarray(entry_scores, dtype=np.float64)
+    nb = num_blocks(T, block)
+    out = np.empty(nb, dtype=np.float64)
+    for J in range(nb):
+        lo, hi = pool_range(J, window, stride, e.size, block)
+        out[J] = e[lo:hi + 1].max()
+    return out
+
+
+def select_row_pooled(f, kt_stored, T, window, stride, n_init, n_local, k):
+    """O2-O6 on max-pooled block scores: the indexer scores every compressed
+    entry (ranked in float32, as the kernel decides), the scores are pooled
+    onto the 64-token blocks, then init U local U top-k as in select_row.
+    kt_stored: stored compressed keys [ceil(T/s), d].  Returns (ascending
+    block ids, pooled decision scores)."""
+    s_entries = decision_scores(indexer_scores(f, kt_stored))
+    s = max_pool_blocks(s_entries, T, window, stride)
+    nb = num_blocks(T)
     cand = candidates(nb, n_init, n_local)
     return block_set(nb, n_init, n_local, top_k(s, cand, k)), s
 

@@ -164,3 +164,59 @@ def test_mutant_union_formula_sign(monkeypatch, gamma, want):
     _patch(monkeypatch, "union_size_formula", lambda n, C, g: n * (1 + (C - 1) * g))
     assert _fails(pins.test_union_formula_printed_values,
                   _param_pin(pins.test_union_size_on_chain_constructed_sets, gamma, want))
+
+
+# ---- overlapping compression and block max-pool -------------------------------
+from tests import test_oracle_pooled as pooled  # noqa: E402
+
+
+def _pool_pins():
+    return [_param_pin(pooled.test_pool_range_matches_token_scan, w, s, T)
+            for (w, s) in pooled.SHAPES for T in (40, 200, 320)] + \
+           [pooled.test_pool_spike_cases_32_16, pooled.test_pooled_scores_are_window_means_of_token_dots,
+            pooled.test_pool_straddling_window_lifts_both_blocks_equally]
+
+
+@pytest.mark.parametrize("kind", ["contained", "starts_inside", "one_short", "no_clip"])
+def test_mutant_pool_range(monkeypatch, kind):
+    def bad(J, window, stride, n_entries, block=64):
+        if kind == "contained":            # only windows inside the block
+            lo, hi = -(-(J * block) // stride), ((J + 1) * block - window) // stride
+        elif kind == "starts_inside":      # windows that start inside the block
+            lo, hi = -(-(J * block) // stride), ((J + 1) * block - 1) // stride
+        elif kind == "one_short":          # drops the last overlapping window
+            lo, hi = max(0, -(-(J * block - window + 1) // stride)), ((J + 1) * block - 1) // stride - 1
+        else:                              # windows past the sequence end kept
+            lo, hi = max(0, -(-(J * block - window + 1) // stride)), ((J + 1) * block - 1) // stride
+        return max(lo, 0), min(hi, n_entries + 3) if kind == "no_clip" else min(hi, n_entries - 1)
+    _patch(monkeypatch, "pool_range", bad)
+    assert _fails(*_pool_pins())
+
+
+def test_mutant_pool_mean_not_max(monkeypatch):
+    def bad(entry_scores, T, window, stride, block=64):
+        e = np.asarray(entry_scores, dtype=np.float64)
+        out = []
+        for J in range(impl.num_blocks(T, block)):
+            lo, hi = impl.pool_range(J, window, stride, e.size, block)
+            out.append(e[lo:hi + 1].mean())
+        return np.array(out)
+    _patch(monkeypatch, "max_pool_blocks", bad)
+    assert _fails(pooled.test_pool_straddling_window_lifts_both_blocks_equally,
+                  pooled.test_pooled_scores_are_window_means_of_token_dots)
+
+
+@pytest.mark.parametrize("kind", ["full_divisor", "floor_count", "stride_as_window"])
+def test_mutant_strided_keys(monkeypatch, kind):
+    def bad(k, T, window, stride):
+        n = T // stride if kind == "floor_count" else -(-T // stride)
+        w = stride if kind == "stride_as_window" else window
+        out = []
+        for j in range(n):
+            lo, hi = j * stride, min(j * stride + w, T)
+            out.append(k[lo:hi].sum(0) / (w if kind == "full_divisor" else hi - lo))
+        return np.stack(out)
+    _patch(monkeypatch, "compressed_keys_strided", bad)
+    pins_ = [_param_pin(pooled.test_strided_keys_match_token_scan, w, s, T)
+             for (w, s) in pooled.SHAPES for T in (17, 100, 130)]
+    assert _fails(*pins_)
