@@ -36,7 +36,10 @@ _SIGNATURES = {
     "sda_version": (ctypes.c_char_p, []),
     "sda_update_compressed_keys": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                             _c_int, _c_int, _c_int, _c_int, _c_void_p]),
+    "sda_update_compressed_keys_strided": (_c_int, [_c_void_p] * 4 + [_c_int] * 8 + [_c_void_p]),
     "sda_score_select_workspace": (_c_size_t, [_c_int] * 5),
+    "sda_score_select_pooled_workspace": (_c_size_t, [_c_int] * 6),
+    "sda_score_select_pooled": (_c_int, [_c_void_p] * 3 + [_c_int] * 11 + [_c_void_p] * 4 + [_c_size_t, _c_void_p]),
     "sda_score_select": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                   _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p,
                                   _c_void_p, _c_size_t, _c_void_p]),
@@ -211,6 +214,53 @@ def sda_score_select(f, k_tilde, seq_len, n_init, n_local, top_k, n_sel_max=None
         return PreparedCall("sda_score_select", args, (f, k_tilde, seq_len, block_idx, n_sel, scores, ws)), \
             (block_idx, n_sel)
     _check(lib().sda_score_select(*args[:-1], _stream(stream)))
+    return block_idx, n_sel
+
+
+def sda_update_compressed_keys_strided(k, k_tilde, len_old, len_new, max_new_tokens, window, stride,
+                                       stream=None):
+    """Recompute the overlapping compressed keys (kernel `window`, stride
+    `stride`) touched by tokens [len_old, len_new); k_tilde is [B, H_kv, NC_cap, d]."""
+    _need(k, "k", torch.bfloat16, 4)
+    _need(k_tilde, "k_tilde", torch.bfloat16, 4)
+    _need(len_old, "len_old", torch.int32, 1)
+    _need(len_new, "len_new", torch.int32, 1)
+    B, H, T_cap, d = k.shape
+    if k_tilde.shape[:2] != (B, H) or k_tilde.shape[3] != d or len_old.numel() != B or len_new.numel() != B:
+        raise ValueError("shape mismatch between k, k_tilde and the length arrays")
+    _check(lib().sda_update_compressed_keys_strided(_ptr(k), _ptr(k_tilde), _ptr(len_old), _ptr(len_new),
+                                                    int(max_new_tokens), B, H, d, T_cap, k_tilde.shape[2],
+                                                    int(window), int(stride), _stream(stream)))
+    return k_tilde
+
+
+def sda_score_select_pooled(f, k_tilde, seq_len, window, stride, n_init, n_local, top_k, n_sel_max=None,
+                            block_idx=None, n_sel=None, scores=None, ws=None, stream=None):
+    """Indexer scores on overlapping compressed keys, max-pooled onto the
+    64-token blocks, then top-k and block sets; returns (block_idx, n_sel).
+    scores (optional) is [B, NQ, H_kv, ceil(NC_cap * stride / 64)] float32."""
+    _need(f, "f", torch.bfloat16, 4)
+    _need(k_tilde, "k_tilde", torch.bfloat16, 4)
+    _need(seq_len, "seq_len", torch.int32, 1)
+    B, NQ, H, d = f.shape
+    NC_cap = k_tilde.shape[2]
+    if k_tilde.shape[:2] != (B, H) or k_tilde.shape[3] != d:
+        raise ValueError("k_tilde must be [B, H_kv, NC_cap, d] matching f")
+    if n_sel_max is None:
+        n_sel_max = n_init + n_local + top_k
+    if block_idx is None:
+        block_idx = torch.empty((B, NQ, H, n_sel_max), dtype=torch.int32, device=f.device)
+    if n_sel is None:
+        n_sel = torch.empty((B, NQ, H), dtype=torch.int32, device=f.device)
+    _need(block_idx, "block_idx", torch.int32, 4)
+    _need(n_sel, "n_sel", torch.int32, 3)
+    if scores is not None:
+        _need(scores, "scores", torch.float32, 4)
+    nbytes = lib().sda_score_select_pooled_workspace(B, NQ, H, NC_cap, int(stride), top_k)
+    ws, wsb = _workspace(nbytes, f.device, ws)
+    _check(lib().sda_score_select_pooled(_ptr(f), _ptr(k_tilde), _ptr(seq_len), B, NQ, H, d, NC_cap, int(window),
+                                         int(stride), n_init, n_local, top_k, n_sel_max, _ptr(block_idx),
+                                         _ptr(n_sel), _ptr(scores), _ptr(ws), wsb, _stream(stream)))
     return block_idx, n_sel
 
 

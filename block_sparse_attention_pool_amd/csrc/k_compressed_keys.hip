@@ -1,19 +1,21 @@
-// Compressed-key (mean-pooled block key) build and incremental update.
+// Compressed-key (mean-pooled key) build and incremental update.
 //
-// K~[b,g,j,:] is the mean of the keys of block j ([SparDA] note,
-// prerequisites §3, eq. (4), kernel = stride = 64 tokens).  The cache lives
-// on the GPU and is refreshed when tokens are appended (§4.2 step 1, §4.6).
-// A touched block is recomputed from all of its keys, so a token-by-token
-// update and a bulk build give identical bits.
+// K~[b,g,j,:] is the mean of the keys of window j, tokens
+// [j*s, min(j*s + l, len)) ([SparDA] note, prerequisites §3, eq. (4) with
+// kernel l and stride s: l = s = 64 gives one key per 64-token block; §4.4
+// quotes InfLLM-V2's inference setting l = 32, s = 16, overlapping windows).
+// The cache lives on the GPU and is refreshed when tokens are appended (§4.2
+// step 1, §4.6).  A touched entry is recomputed from all of its keys, so a
+// token-by-token update and a bulk build give identical bits.
 //
-// One workgroup (256 lanes) per (row, touched block): the 64 x d bf16 tile is
-// read with 16-byte coalesced loads (a 256-byte key row per 16 lanes at
-// d = 128), summed in fp64 per lane, then reduced across the lanes that share
-// columns through LDS.  A sum of bf16 values is exact in fp64 while the
-// block's non-zero magnitudes stay within a factor 2^39 of each other, so
+// One workgroup (256 lanes) per (row, touched entry): the <= 64 x d bf16
+// tile is read with 16-byte coalesced loads (a 256-byte key row per 16 lanes
+// at d = 128), summed in fp64 per lane, then reduced across the lanes that
+// share columns through LDS.  A sum of bf16 values is exact in fp64 while the
+// window's non-zero magnitudes stay within a factor 2^39 of each other, so
 // the mean (one correctly rounded fp64 division) and its single rounding to
 // the stored bf16 depend on the keys alone, not on the summation order.
-// HBM-bound: 64*d*2 bytes read, d*2 bytes written.
+// HBM-bound: l*d*2 bytes read, d*2 bytes written per entry.
 #include "sda_device.hpp"
 #include "sda_internal.h"
 
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(256) void ktilde_kernel(const uint16_t* __restrict_
                                                      uint16_t* __restrict__ kt,
                                                      const int32_t* __restrict__ len_old,
                                                      const int32_t* __restrict__ len_new,
-                                                     int H_kv, int T_cap, int NB_cap) {
+                                                     int H_kv, int T_cap, int NC_cap, int window, int stride) {
     constexpr int LPR = D / 8;          // lanes per key row (8 bf16 per lane)
     constexpr int RPS = 256 / LPR;      // rows per load step
     constexpr int STEPS = kBlock / RPS;
@@ -55,12 +57,13 @@ __global__ __launch_bounds__(256) void ktilde_kernel(const uint16_t* __restrict_
     int hi = min(len_new[b], T_cap);
     lo = max(lo, 0);
     if (hi <= lo) return;
-    const int j = lo / kBlock + (int)blockIdx.x;
-    const int j_last = (hi - 1) / kBlock;
-    if (j > j_last || j >= NB_cap) return;
+    // entries touched by tokens [lo, hi): windows that end after lo and start before hi
+    const int j = (lo >= window ? (lo - window) / stride + 1 : 0) + (int)blockIdx.x;
+    const int j_last = (hi - 1) / stride;
+    if (j > j_last || j >= NC_cap) return;
 
-    const int t0 = j * kBlock;
-    const int n = min(kBlock, hi - t0);         // tokens present in this block
+    const int t0 = j * stride;
+    const int n = min(window, hi - t0);         // tokens present in this window (1..64)
     const int tid = threadIdx.x;
     const int c8 = (tid % LPR) * 8;             // first column of this lane
     const int r0 = tid / LPR;
@@ -91,20 +94,21 @@ __global__ __launch_bounds__(256) void ktilde_kernel(const uint16_t* __restrict_
         double s = 0.0;
 #pragma unroll
         for (int r = 0; r < RPS; ++r) s += red[r][tid];
-        kt[((size_t)row * NB_cap + j) * D + tid] = f64_to_bf16(s / (double)n);
+        kt[((size_t)row * NC_cap + j) * D + tid] = f64_to_bf16(s / (double)n);
     }
 }
 
 hipError_t launch_update_compressed_keys(const uint16_t* k, uint16_t* kt, const int32_t* len_old,
-                                         const int32_t* len_new, int max_blocks_per_row, int B,
-                                         int H_kv, int d, int T_cap, int NB_cap, hipStream_t s) {
-    dim3 grid(max_blocks_per_row, B * H_kv);
+                                         const int32_t* len_new, int max_entries_per_row, int B,
+                                         int H_kv, int d, int T_cap, int NC_cap, int window, int stride,
+                                         hipStream_t s) {
+    dim3 grid(max_entries_per_row, B * H_kv);
     if (d == 128)
         hipLaunchKernelGGL(ktilde_kernel<128>, grid, dim3(256), 0, s, k, kt, len_old, len_new, H_kv,
-                           T_cap, NB_cap);
+                           T_cap, NC_cap, window, stride);
     else
         hipLaunchKernelGGL(ktilde_kernel<64>, grid, dim3(256), 0, s, k, kt, len_old, len_new, H_kv,
-                           T_cap, NB_cap);
+                           T_cap, NC_cap, window, stride);
     return hipGetLastError();
 }
 

@@ -351,6 +351,90 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         select_tail<NV>(a.sel, a.cand, a.counters, sc, b, g, row, a.NQ, a.H_kv, nvec, v0, j0, nb);
 }
 
+// Pooled scoring ([SparDA] note: eq. (4) with kernel l and stride s, §4.4
+// InfLLM-V2's inference compression l = 32, s = 16; §4.3 and fig. 3: the
+// compressed scores are max-pooled onto the block grid).  Workgroup
+// (chunk, kv row, query) scores every compressed entry whose window shares a
+// token with one of its 256 blocks (256*64/s entries plus the (l-1)/s
+// windows that reach in from the previous chunk: 1025 at l = 32, s = 16),
+// 16 lanes per entry as in score_kernel, the scores kept in LDS; each lane
+// then takes the max over its block's windows, and the selection runs as in
+// score_kernel on those block scores.
+constexpr int kPoolMaxEntries = kChunk * 64 / 8 + 8;      // stride >= 8, window <= 64
+struct PoolArgs {
+    int window, stride, NC_cap;
+};
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void pooled_score_kernel(ScoreArgs a, PoolArgs pa) {
+    constexpr bool FUSED = MODE == kFusedSelect;
+    constexpr int EPL = D / 16;
+    constexpr int UNR = 16;                                 // entry steps in flight
+    using KLoad = typename std::conditional<EPL == 8, u32x4, u32x2>::type;
+    const int row = blockIdx.y;                             // b * H_kv + g
+    const int b = row / a.H_kv, g = row - (row / a.H_kv) * a.H_kv;
+    const int q = blockIdx.z;                               // one indexer vector per workgroup
+    const int T = a.seq_len[b];
+    const int nb = min((T + kBlock - 1) / kBlock, a.NB_cap);
+    const int ne = min((T + pa.stride - 1) / pa.stride, pa.NC_cap);    // entries present
+    const int j0 = blockIdx.x * kChunk;
+    const int lane = __lane_id();
+    const int li = lane & 15;
+    const int wave = threadIdx.x / kWave;
+    __shared__ float zc[kPoolMaxEntries];
+    __shared__ float sc[1][kChunk];
+
+    const KLoad fw = *reinterpret_cast<const KLoad*>(a.vec + (((size_t)b * a.NQ + q) * a.H_kv + g) * D + li * EPL);
+    if (j0 < nb && ne > 0) {
+        // entries overlapping blocks [j0, min(j0 + 256, nb)): j*s + l > 64*j0 and j*s < 64*min(...)
+        const int lo_num = kBlock * j0 - pa.window + 1;
+        const int e0 = lo_num > 0 ? (lo_num + pa.stride - 1) / pa.stride : 0;
+        const int e1 = min(ne - 1, (kBlock * min(j0 + kChunk, nb) - 1) / pa.stride);
+        const int cnt = e1 - e0 + 1;
+        const uint16_t* ktr = a.kt + (size_t)row * pa.NC_cap * D + li * EPL;
+        float fv[EPL];
+        {
+            const uint32_t* wp = reinterpret_cast<const uint32_t*>(&fw);
+#pragma unroll
+            for (int i = 0; i < EPL / 2; ++i) {
+                fv[2 * i] = bf16lo(wp[i]);
+                fv[2 * i + 1] = bf16hi(wp[i]);
+            }
+        }
+        for (int s0 = 0; s0 * 16 < cnt; s0 += UNR) {
+            KLoad kv[UNR];
+            int jj[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                jj[u] = e0 + (s0 + u) * 16 + wave * 4 + (lane >> 4);
+                // past the chunk's last entry: re-read that entry (cached), result unused
+                kv[u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const KLoad*>(ktr + (size_t)min(jj[u], e1) * D));
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const float acc = key_dot<EPL>(fv, reinterpret_cast<const uint32_t*>(&kv[u])) * a.mult;
+                if (li == 0 && jj[u] <= e1) zc[jj[u] - e0] = acc;
+            }
+        }
+        __syncthreads();
+        // max-pool: block J = j0 + t takes the windows j*s < 64(J+1), j*s + l > 64J
+        const int t = threadIdx.x;
+        const int J = j0 + t;
+        if (J < nb) {
+            const int ln = kBlock * J - pa.window + 1;
+            const int lo = max(e0, ln > 0 ? (ln + pa.stride - 1) / pa.stride : 0);
+            const int hi = min(e1, (kBlock * J + kBlock - 1) / pa.stride);
+            float m = -INFINITY;
+            for (int e = lo; e <= hi; ++e) m = fmaxf(m, zc[e - e0]);
+            sc[0][t] = m;
+            if (a.out) a.out[(((size_t)b * a.NQ + q) * a.H_kv + g) * a.NB_cap + J] = m;
+        }
+    }
+    if constexpr (FUSED)
+        select_tail<1>(a.sel, a.cand, a.counters, sc, b, g, row, a.NQ, a.H_kv, a.NQ, q, j0, nb);
+}
+
 template <int D, int MODE>
 static void launch_score_d(const ScoreArgs& a, int B, hipStream_t s) {
     const int nvec = a.NQ * a.VPR;
@@ -389,6 +473,30 @@ hipError_t launch_score_select(const uint16_t* f, const uint16_t* kt, const Sele
     ScoreArgs a{f, kt, sel.seq_len, scores, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, nullptr, nullptr};
     if (d == 128) launch_score_d<128, kScoresOnly>(a, B, s);
     else launch_score_d<64, kScoresOnly>(a, B, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SelectArgs sa = sel;
+    sa.scores = scores;
+    return launch_select(sa, s);
+}
+
+// pooled scores (one workgroup per chunk, kv row and query), then the
+// selection: in the same launch with cand / counters, else a second launch
+hipError_t launch_score_select_pooled(const uint16_t* f, const uint16_t* kt, const SelectArgs& sel, int B, int d,
+                                      int window, int stride, int NC_cap, float* scores_opt, float* scores_ws,
+                                      uint64_t* cand, int* counters, hipStream_t s) {
+    const PoolArgs pa{window, stride, NC_cap};
+    const dim3 grid(score_chunks(sel.NB_cap), B * sel.H_kv, sel.NQ), block(256);
+    if (cand) {
+        const ScoreArgs a{f, kt, sel.seq_len, scores_opt, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, cand, counters};
+        if (d == 128) hipLaunchKernelGGL((pooled_score_kernel<128, kFusedSelect>), grid, block, 0, s, a, pa);
+        else hipLaunchKernelGGL((pooled_score_kernel<64, kFusedSelect>), grid, block, 0, s, a, pa);
+        return hipGetLastError();
+    }
+    float* scores = scores_opt ? scores_opt : scores_ws;
+    const ScoreArgs a{f, kt, sel.seq_len, scores, sel.NQ, sel.H_kv, 1, sel.NB_cap, 1.f, sel, nullptr, nullptr};
+    if (d == 128) hipLaunchKernelGGL((pooled_score_kernel<128, kScoresOnly>), grid, block, 0, s, a, pa);
+    else hipLaunchKernelGGL((pooled_score_kernel<64, kScoresOnly>), grid, block, 0, s, a, pa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     SelectArgs sa = sel;

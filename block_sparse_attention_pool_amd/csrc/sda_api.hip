@@ -127,9 +127,42 @@ sda_status_t sda_update_compressed_keys(const void* k, void* k_tilde, const int3
     if (blocks > NB_cap) blocks = NB_cap;
     return hip_status(launch_update_compressed_keys(static_cast<const uint16_t*>(k), static_cast<uint16_t*>(k_tilde),
                                                     len_old, len_new,
-                                                    blocks, B, H_kv, d, T_cap, NB_cap,
+                                                    blocks, B, H_kv, d, T_cap, NB_cap, kBlock, kBlock,
                                                     static_cast<hipStream_t>(stream)),
                       "update_compressed_keys launch");
+}
+
+// overlapping compression: window (kernel) and stride in tokens
+static sda_status_t check_pool(int window, int stride) {
+    REQUIRE(stride == 8 || stride == 16 || stride == 32 || stride == 64, SDA_ERR_UNSUPPORTED,
+            "stride=%d: supported strides are 8, 16, 32 and 64 tokens", stride);
+    REQUIRE(window >= stride && window <= 64 && window % stride == 0, SDA_ERR_UNSUPPORTED,
+            "window=%d: must be a multiple of the stride (%d) and at most 64 tokens", window, stride);
+    return SDA_OK;
+}
+
+sda_status_t sda_update_compressed_keys_strided(const void* k, void* k_tilde, const int32_t* len_old,
+                                                const int32_t* len_new, int max_new_tokens, int B, int H_kv,
+                                                int d, int T_cap, int NC_cap, int window, int stride,
+                                                void* stream) {
+    REQUIRE(k && k_tilde && len_old && len_new, SDA_ERR_NULL, "update_compressed_keys_strided: null pointer");
+    TRY(check_d(d));
+    TRY(check_pool(window, stride));
+    REQUIRE(B >= 1 && H_kv >= 1 && T_cap >= 1, SDA_ERR_SHAPE, "B=%d H_kv=%d T_cap=%d must be >= 1", B, H_kv, T_cap);
+    REQUIRE(NC_cap >= ceil_div(T_cap, stride), SDA_ERR_SHAPE, "NC_cap=%d < ceil(T_cap/stride)=%d", NC_cap,
+            ceil_div(T_cap, stride));
+    REQUIRE((long long)B * H_kv <= kMaxGridYZ, SDA_ERR_SHAPE, "B*H_kv=%lld exceeds %d", (long long)B * H_kv, kMaxGridYZ);
+    REQUIRE(max_new_tokens >= 0, SDA_ERR_SHAPE, "max_new_tokens=%d < 0", max_new_tokens);
+    REQUIRE(aligned16(k) && aligned16(k_tilde), SDA_ERR_ALIGN, "k and k_tilde must be 16-byte aligned");
+    REQUIRE(aligned4(len_old) && aligned4(len_new), SDA_ERR_ALIGN, "length arrays must be 4-byte aligned");
+    if (max_new_tokens == 0) return SDA_OK;
+    // tokens [lo, lo + m) touch at most ceil(m / stride) + window / stride entries
+    long long entries = (long long)ceil_div(max_new_tokens, stride) + window / stride;
+    if (entries > NC_cap) entries = NC_cap;
+    return hip_status(launch_update_compressed_keys(static_cast<const uint16_t*>(k), static_cast<uint16_t*>(k_tilde),
+                                                    len_old, len_new, (int)entries, B, H_kv, d, T_cap, NC_cap,
+                                                    window, stride, static_cast<hipStream_t>(stream)),
+                      "update_compressed_keys_strided launch");
 }
 
 // ---------------------------------------------------------------------------
@@ -196,6 +229,48 @@ sda_status_t sda_score_select(const void* f, const void* k_tilde, const int32_t*
     return hip_status(launch_score_select(static_cast<const uint16_t*>(f), static_cast<const uint16_t*>(k_tilde), a, B, d, scores_opt, scores_ws,
                                           cand, counters, static_cast<hipStream_t>(stream)),
                       "score/select launch");
+}
+
+// overlapping compression: [block scores f32, B*NQ*H_kv*NB_cap][candidate keys
+// u64 (in-launch selection only)][arrival counters i32, B*H_kv*NQ], with
+// NB_cap = ceil(NC_cap * stride / 64) blocks per row
+static int pooled_nb_cap(int NC_cap, int stride) { return ceil_div((long long)NC_cap * stride, kBlock); }
+
+size_t sda_score_select_pooled_workspace(int B, int NQ, int H_kv, int NC_cap, int stride, int top_k) {
+    if (B < 1 || NQ < 1 || H_kv < 1 || NC_cap < 1 || stride < 1 || top_k < 0) return 0;
+    const int NB_cap = pooled_nb_cap(NC_cap, stride);
+    return score_region_bytes(B, NQ, H_kv, NB_cap) + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k) +
+           (size_t)B * H_kv * NQ * sizeof(int);
+}
+
+sda_status_t sda_score_select_pooled(const void* f, const void* k_tilde, const int32_t* seq_len, int B, int NQ,
+                                     int H_kv, int d, int NC_cap, int window, int stride, int n_init, int n_local,
+                                     int top_k, int n_sel_max, int32_t* block_idx, int32_t* n_sel,
+                                     float* scores_opt, void* ws, size_t ws_bytes, void* stream) {
+    REQUIRE(f, SDA_ERR_NULL, "score_select_pooled: f is null");
+    TRY(check_pool(window, stride));
+    REQUIRE(NC_cap >= 1 && NC_cap <= (1 << 24), SDA_ERR_SHAPE, "NC_cap=%d out of range", NC_cap);
+    const int NB_cap = pooled_nb_cap(NC_cap, stride);
+    TRY(check_select_common(k_tilde, seq_len, B, NQ, H_kv, d, NB_cap, n_init, n_local, top_k, n_sel_max,
+                            block_idx, n_sel));
+    REQUIRE(aligned16(f), SDA_ERR_ALIGN, "f must be 16-byte aligned");
+    REQUIRE(NQ <= kMaxGridYZ, SDA_ERR_SHAPE, "NQ=%d exceeds %d", NQ, kMaxGridYZ);
+    const size_t need = sda_score_select_pooled_workspace(B, NQ, H_kv, NC_cap, stride, top_k);
+    REQUIRE(ws && ws_bytes >= need, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, need);
+    REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    REQUIRE(!scores_opt || aligned4(scores_opt), SDA_ERR_ALIGN, "scores_opt must be 4-byte aligned");
+    char* base = static_cast<char*>(ws);
+    float* scores_ws = reinterpret_cast<float*>(base);
+    const size_t cand_off = score_region_bytes(B, NQ, H_kv, NB_cap);
+    uint64_t* cand = reinterpret_cast<uint64_t*>(base + cand_off);
+    int* counters = reinterpret_cast<int*>(base + cand_off + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k));
+    if (!fused_select_ok(NB_cap, top_k) || env_int("SDA_SELECT_FUSED", 1) == 0) cand = nullptr, counters = nullptr;
+    SelectArgs a{seq_len, nullptr, B * NQ * H_kv, NQ, H_kv, NB_cap, n_init, n_local, top_k, n_sel_max,
+                 block_idx, n_sel};
+    return hip_status(launch_score_select_pooled(static_cast<const uint16_t*>(f), static_cast<const uint16_t*>(k_tilde),
+                                                 a, B, d, window, stride, NC_cap, scores_opt, scores_ws, cand,
+                                                 counters, static_cast<hipStream_t>(stream)),
+                      "pooled score/select launch");
 }
 
 // [z f32 and per-chunk statistics][scores f32, B*NQ*H_kv*NB_cap][candidate keys u64

@@ -9,9 +9,11 @@
 namespace sda {
 
 // ---- compressed keys ----------------------------------------------------------
+// entry j of a row: mean of tokens [j*stride, min(j*stride + window, len)), window <= 64
 hipError_t launch_update_compressed_keys(const uint16_t* k, uint16_t* kt, const int32_t* len_old,
-                                         const int32_t* len_new, int max_blocks_per_row, int B,
-                                         int H_kv, int d, int T_cap, int NB_cap, hipStream_t s);
+                                         const int32_t* len_new, int max_entries_per_row, int B,
+                                         int H_kv, int d, int T_cap, int NC_cap, int window, int stride,
+                                         hipStream_t s);
 
 // ---- scoring and selection ----------------------------------------------------
 struct SelectArgs {
@@ -30,6 +32,13 @@ hipError_t launch_score_select(const uint16_t* f, const uint16_t* kt, const Sele
                                float* scores_opt, float* scores_ws, uint64_t* cand, int* counters,
                                hipStream_t s);
 bool fused_select_ok(int NB_cap, int top_k);
+// overlapping compression: entries of kernel `window`, stride `stride`
+// (NC_cap per row) scored, max-pooled onto the 64-token blocks (sel.NB_cap
+// per row), then selected as launch_score_select does
+hipError_t launch_score_select_pooled(const uint16_t* f, const uint16_t* kt, const SelectArgs& sel, int B, int d,
+                                      int window, int stride, int NC_cap, float* scores_opt, float* scores_ws,
+                                      uint64_t* cand, int* counters, hipStream_t s);
+
 constexpr int kFusedTopK = 64;       // longest per-chunk list the in-launch selection keeps
 constexpr int kFusedChunks = 16;     // most 256-block chunks it merges (NB_cap <= 4096)
 // top-k lists are padded to the smallest power of two >= K (1 for K = 0)

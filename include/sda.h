@@ -131,6 +131,55 @@ sda_status_t sda_score_select_multihead(const void* q, const void* k_tilde, cons
                                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Overlapping compressed keys ([SparDA] prerequisites §3, eq. (4) with kernel
+ * l = window and stride s = stride; §4.4 quotes InfLLM-V2's inference setting
+ * l = 32, s = 16): entry j of a row is the mean of the keys
+ * K[b,g, j*s : min(j*s + l, len), :] for every j with j*s < len, rounded once
+ * to bf16 as in sda_update_compressed_keys (whose 64/64 case this is).
+ *
+ *   k        bf16 [B, H_kv, T_cap, d]        keys (read only)
+ *   k_tilde  bf16 [B, H_kv, NC_cap, d]       updated in place, NC_cap >= ceil(T_cap / s)
+ *   len_old, len_new, max_new_tokens         as sda_update_compressed_keys
+ *   window   l, a multiple of stride, stride <= l <= 64
+ *   stride   s in {8, 16, 32, 64}
+ * Every entry whose window holds a token of [len_old[b], len_new[b]) is
+ * recomputed from K (token-by-token updates equal a bulk build bit for bit).
+ */
+sda_status_t sda_update_compressed_keys_strided(const void* k, void* k_tilde,
+                                                const int32_t* len_old, const int32_t* len_new,
+                                                int max_new_tokens, int B, int H_kv, int d,
+                                                int T_cap, int NC_cap, int window, int stride,
+                                                void* stream);
+
+/*
+ * Indexer scoring on overlapping compressed keys, max-pooled onto the
+ * 64-token block grid, then top-k and block-set assembly ([SparDA] eq. (6),
+ * (9); §4.4 compression l = 32, s = 16; §4.3 and fig. 3: the compressed
+ * scores are max-pooled to block scores):
+ *   z_j = f . K~_j for every entry j < ceil(seq_len / s);
+ *   S_J = max of z_j over the windows that share a token with block J
+ *         (j*s < 64(J+1) and j*s + l > 64J);
+ *   B = init U local U top_k(S over the other blocks) as in sda_score_select.
+ *
+ *   f          bf16 [B, NQ, H_kv, d]
+ *   k_tilde    bf16 [B, H_kv, NC_cap, d] from sda_update_compressed_keys_strided
+ *   window, stride  as that call
+ *   scores_opt f32 [B, NQ, H_kv, NB_cap] out or NULL: pooled block scores, with
+ *              NB_cap = ceil(NC_cap * stride / 64) (entries past nb undefined)
+ *   other arguments as sda_score_select (1 <= seq_len <= stride * NC_cap).
+ * Workspace: sda_score_select_pooled_workspace() bytes, with the same
+ * zero-fill and no-overlap contract as sda_score_select.  With top_k <= 64
+ * and NB_cap <= 4096 the selection runs inside the scoring launch, otherwise
+ * as a second launch; the results are identical.
+ */
+size_t sda_score_select_pooled_workspace(int B, int NQ, int H_kv, int NC_cap, int stride, int top_k);
+sda_status_t sda_score_select_pooled(const void* f, const void* k_tilde, const int32_t* seq_len,
+                                     int B, int NQ, int H_kv, int d, int NC_cap, int window, int stride,
+                                     int n_init, int n_local, int top_k, int n_sel_max,
+                                     int32_t* block_idx, int32_t* n_sel, float* scores_opt,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Block-sparse decode attention ([SparDA] eq. (7) and §4.2 step 4; [SSV] NSA
  * selection branch step 3): for every query head h of every row,
  *   O = softmax(q_h K_B^T * scale) V_B

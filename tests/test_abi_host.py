@@ -38,7 +38,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
         assert n in sda.exported_symbols(), n
@@ -89,6 +89,58 @@ def test_update_validation(L):
     assert f(P_ODD, P, P, P, 64, 1, 2, 64, 4096, 64, None) == ALIGN
     assert f(P, P, P, P, -1, 1, 2, 64, 4096, 64, None) == SHAPE
     assert f(P, P, P, P, 0, 1, 2, 64, 4096, 64, None) == OK               # nothing to do, nothing launched
+
+
+def test_strided_update_validation(L):
+    f = L.sda_update_compressed_keys_strided
+    # k, k_tilde, len_old, len_new, max_new, B, H_kv, d, T_cap, NC_cap, window, stride, stream
+    ok = [P, P, P, P, 0, 1, 2, 64, 4096, 256, 32, 16, None]
+    assert f(*ok) == OK                                                  # nothing to do, nothing launched
+    bad = list(ok); bad[0] = None
+    assert f(*bad) == NULL
+    bad = list(ok); bad[11] = 12                                         # stride not supported
+    assert f(*bad) == UNSUP
+    bad = list(ok); bad[10] = 24                                         # window not a multiple of the stride
+    assert f(*bad) == UNSUP
+    bad = list(ok); bad[10] = 128; bad[11] = 64                          # window beyond 64 tokens
+    assert f(*bad) == UNSUP
+    bad = list(ok); bad[10] = 8                                          # window shorter than the stride
+    assert f(*bad) == UNSUP
+    bad = list(ok); bad[9] = 255                                         # NC_cap < ceil(T_cap / stride)
+    assert f(*bad) == SHAPE
+    bad = list(ok); bad[1] = P_ODD
+    assert f(*bad) == ALIGN
+    bad = list(ok); bad[4] = -1
+    assert f(*bad) == SHAPE
+
+
+def test_pooled_workspace_and_validation(L):
+    # [block scores over ceil(NC_cap*stride/64) blocks][candidate keys][counters per (b, q, kv head)]
+    assert L.sda_score_select_pooled_workspace(8, 1, 8, 8192, 16, 32) == \
+        8 * 8 * 2048 * 4 + 64 * 8 * 32 * 8 + 8 * 8 * 4
+    # NC_cap 100 at stride 16 = 25 blocks: 600 B of scores (768 padded), 192 B of keys (256), 24 B
+    assert L.sda_score_select_pooled_workspace(2, 3, 1, 100, 16, 4) == 768 + 256 + 2 * 3 * 4
+    assert L.sda_score_select_pooled_workspace(1, 1, 1, 0, 16, 4) == 0
+    f = L.sda_score_select_pooled
+    # f, k_tilde, seq_len, B, NQ, H_kv, d, NC_cap, window, stride, n_init, n_local, top_k, n_sel_max,
+    # block_idx, n_sel, scores, ws, ws_bytes, stream
+    args = [P, P, P, 1, 1, 2, 64, 256, 32, 16, 1, 2, 8, 11, P, P, None, P, 1 << 20, None]
+    bad = list(args); bad[0] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[9] = 24
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[8] = 16; bad[9] = 32                           # window shorter than the stride
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[13] = 10                                       # n_sel_max < 1 + 2 + 8
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[18] = 100
+    assert f(*bad) == WS
+    bad = list(args); bad[7] = 0
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[7] = 90000                                     # beyond the block limit of the select launch
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[1] = P_ODD
+    assert f(*bad) == ALIGN
 
 
 def test_score_select_validation(L):
