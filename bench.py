@@ -750,8 +750,8 @@ def main():
                        "resident layers), replayed")
                       + (", layer l+1's score_select beside layer l's sparse_decode (two streams)"
                          if args.overlap else
-                         ", one sda_decode_step per layer (a scoring launch writes per-chunk candidate lists of "
-                         "layer l+1; layer l's decode launch merges them into l+1's block sets)"
+                         ", one sda_decode_step per layer (one launch: layer l's decode workgroups, then "
+                         "workgroups that score layer l+1's compressed keys and select its block sets)"
                          if args.step == "fused" else ", score_select then sparse_decode per layer"),
         },
         "roofline": {
