@@ -32,7 +32,10 @@ Readings of points the pages leave open (numbered as in the design notes):
   query head h reads KV head floor(h / G); attention scale 1/sqrt(d);
   the G-head comparator sums per-head softmax over all blocks with tau = sqrt(d);
   with overlapping compression (kernel l, stride s) a block's score is the
-  max over the compressed windows that share a token with it.
+  max over the compressed windows that share a token with it; NSA's
+  compressed branch attends to every compressed entry present at length T,
+  its window branch to the last w cached tokens, and the branch gates are
+  inputs (one triple per query head).
 
 Parity pins: every function here is pinned by tests under tests/ against
 closed forms, brute force or an independent library routine, except the
@@ -369,3 +372,64 @@ def union_size_formula(n, C, gamma):
 def saving_formula(C, gamma):
     """Fraction of block loads saved by merging: (C-1) * gamma / C."""
     return (C - 1) * gamma / C
+
+
+# ---------------------------------------------------------------------------
+# O13  NSA's three branches and their gated sum, as the SSV verification
+#      kernel outputs them ([SSV] NSA three-branch derivation, steps 3-6;
+#      verification-kernel algorithm step 3c)
+# ---------------------------------------------------------------------------
+
+def attend_tokens(q, k, v, tokens, scale):
+    """softmax(q K_tok^T * scale) V_tok over the listed token rows; two-pass
+    softmax.  Returns (o [d], lse); an empty token list gives (0, -inf)."""
+    tok = np.asarray(tokens, dtype=np.int64)
+    if tok.size == 0:
+        return np.zeros(k.shape[-1]), -np.inf
+    z = (k[tok] @ np.asarray(q, dtype=np.float64)) * float(scale)
+    m = z.max()
+    p = np.exp(z - m)
+    l = p.sum()
+    return (p @ v[tok]) / l, float(m + np.log(l))
+
+
+def window_tokens(T, window):
+    """The sliding-window branch's tokens: the last `window` cached tokens,
+    [max(0, T - window), T) (the token being decoded is cached, reading 21)."""
+    return np.arange(max(0, int(T) - int(window)), int(T), dtype=np.int64)
+
+
+def nsa_row(q_heads, k, v, kc, vc, blocks, T, n_cmp, window, gates, scale):
+    """Gated NSA output of the G query heads that share one KV head:
+    o_h = g_c * Attn(q_h, K~, V~) + g_s * Attn(q_h, K_B, V_B) + g_w * Attn(q_h, K_win, V_win)
+    with the compressed branch over the n_cmp compressed keys and values
+    (kc, vc: [>= n_cmp, d]), the selection branch over the tokens of the
+    listed blocks, the window branch over the last `window` tokens.
+    gates: [G, 3] (g_c, g_s, g_w) per head.  Returns (out [G, d],
+    branch outputs [3, G, d], branch lse [3, G])."""
+    G = q_heads.shape[0]
+    sel_tok = block_tokens(blocks, T)
+    win_tok = window_tokens(T, window)
+    cmp_tok = np.arange(int(n_cmp), dtype=np.int64)
+    out = np.zeros((G, k.shape[-1]))
+    br = np.zeros((3, G, k.shape[-1]))
+    lse = np.zeros((3, G))
+    for h in range(G):
+        for b, (kk, vv, tok) in enumerate(((kc, vc, cmp_tok), (k, v, sel_tok), (k, v, win_tok))):
+            br[b, h], lse[b, h] = attend_tokens(q_heads[h], kk, vv, tok, scale)
+        out[h] = gates[h, 0] * br[0, h] + gates[h, 1] * br[1, h] + gates[h, 2] * br[2, h]
+    return out, br, lse
+
+
+def grouped_nsa_row(q_rows, k, v, kc, vc, lists, T, n_cmp, window, gates, scale, mode):
+    """The verification kernel's output for one group of C draft queries of
+    one KV head: the selection branch attends to each query's own list
+    (mode A) or the first query's (mode B); the compressed and window
+    branches see the same committed prefix for every query (reading 14).
+    q_rows: [C, G, d]; gates: [C, G, 3].  Returns (out [C, G, d], union_count)."""
+    C = len(lists)
+    active = list(lists) if mode == MODE_EXACT else [lists[0]] * C
+    ucount = len(union_blocks(lists if mode == MODE_EXACT else [lists[0]]))
+    out = np.stack([nsa_row(q_rows[c], k, v, kc, vc, active[c], T, n_cmp, window, gates[c], scale)[0]
+                    for c in range(C)])
+    return out, ucount

@@ -220,3 +220,49 @@ def test_mutant_strided_keys(monkeypatch, kind):
     pins_ = [_param_pin(pooled.test_strided_keys_match_token_scan, w, s, T)
              for (w, s) in pooled.SHAPES for T in (17, 100, 130)]
     assert _fails(*pins_)
+
+
+# ---- NSA three branches ----------------------------------------------------------
+from tests import test_oracle_nsa as nsa  # noqa: E402
+
+
+def _nsa_pins():
+    return [nsa.test_window_tokens_hand_cases, nsa.test_selection_only_gates_equal_block_decode,
+            _param_pin(nsa.test_window_branch_covering_everything_is_dense_attention, 601),
+            nsa.test_aligned_window_equals_decode_over_last_blocks,
+            nsa.test_compressed_branch_with_unit_windows_is_dense_attention, nsa.test_zero_query_closed_forms,
+            nsa.test_tiny_case_plain_python]
+
+
+@pytest.mark.parametrize("kind", ["one_short", "one_long"])
+def test_mutant_window_tokens(monkeypatch, kind):
+    def bad(T, window):
+        lo = max(0, int(T) - int(window) + (1 if kind == "one_short" else -1))
+        return np.arange(lo, int(T), dtype=np.int64)
+    _patch(monkeypatch, "window_tokens", bad)
+    assert _fails(*_nsa_pins())
+
+
+@pytest.mark.parametrize("kind", ["gates_swapped", "cmp_one_short", "selection_on_window", "no_scale_cmp"])
+def test_mutant_nsa_row(monkeypatch, kind):
+    real_attend = impl.attend_tokens
+
+    def bad(q_heads, k, v, kc, vc, blocks, T, n_cmp, window, gates, scale):
+        G = q_heads.shape[0]
+        sel_tok = impl.block_tokens(blocks, T)
+        win_tok = impl.window_tokens(T, window)
+        cmp_tok = np.arange(int(n_cmp) - (1 if kind == "cmp_one_short" else 0))
+        if kind == "selection_on_window":
+            sel_tok = win_tok
+        out = np.zeros((G, k.shape[-1]))
+        br = np.zeros((3, G, k.shape[-1]))
+        lse = np.zeros((3, G))
+        for h in range(G):
+            for b, (kk, vv, tok) in enumerate(((kc, vc, cmp_tok), (k, v, sel_tok), (k, v, win_tok))):
+                sc = 1.0 if (kind == "no_scale_cmp" and b == 0) else scale
+                br[b, h], lse[b, h] = real_attend(q_heads[h], kk, vv, tok, sc)
+            g = gates[h][::-1] if kind == "gates_swapped" else gates[h]
+            out[h] = g[0] * br[0, h] + g[1] * br[1, h] + g[2] * br[2, h]
+        return out, br, lse
+    _patch(monkeypatch, "nsa_row", bad)
+    assert _fails(*_nsa_pins())
