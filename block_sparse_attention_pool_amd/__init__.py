@@ -13,6 +13,7 @@ Layouts (bf16 given as torch.bfloat16, int32 as torch.int32):
   out       [B, NQ, H_q, d] float32  lse       [B, NQ, H_q] float32
 """
 import ctypes
+import math
 import os
 
 import torch
@@ -57,6 +58,9 @@ _SIGNATURES = {
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _c_int,
                                     _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_size_t,
                                     _c_void_p]),
+    "sda_nsa_decode_workspace": (_c_size_t, [_c_int] * 11),
+    "sda_nsa_decode": (_c_int, [_c_void_p] * 8 + [_c_int] * 5 + [_c_void_p] + [_c_int] * 5 + [_c_float]
+                       + [_c_int] * 2 + [_c_void_p] * 4 + [_c_size_t, _c_void_p]),
     "sda_gather_blocks": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int,
                                    _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p]),
     "sda_decode_step_workspace": (_c_size_t, [_c_int] * 8),
@@ -407,6 +411,45 @@ def sda_grouped_decode(q, k, v, seq_len, block_idx, n_sel, group_C, mode=SDA_GRO
                                     n_sel_max, T_cap, int(NB_cap), B, NQ, H_q, H_kv, d, float(scale),
                                     int(group_C), int(mode), _ptr(out), _ptr(lse), _ptr(union_count),
                                     int(split_k), _ptr(ws), wsb, _stream(stream)))
+    return out, lse, union_count
+
+
+def sda_nsa_decode(q, k, v, k_cmp, v_cmp, seq_len, block_idx, n_sel, gates, cmp_stride, window, group_C=1,
+                   mode=SDA_GROUP_EXACT, scale=None, out=None, lse=None, union_count=None, ws=None, stream=None):
+    """NSA verification output (compressed, selected-block and window branches,
+    gated sum) in one launch; returns (out, lse [B, NQ, H_q, 3], union_count)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(k_cmp, "k_cmp", torch.bfloat16, 4)
+    _need(v_cmp, "v_cmp", torch.bfloat16, 4)
+    _need(seq_len, "seq_len", torch.int32, 1)
+    _need(block_idx, "block_idx", torch.int32, 4)
+    _need(n_sel, "n_sel", torch.int32, 3)
+    _need(gates, "gates", torch.float32, 4)
+    B, NQ, H_q, d = q.shape
+    _, H, T_cap, _ = k.shape
+    NC_cap = k_cmp.shape[2]
+    if v.shape != k.shape or v_cmp.shape != k_cmp.shape or k_cmp.shape[:2] != (B, H):
+        raise ValueError("k/v and k_cmp/v_cmp must be [B, H_kv, *, d] pairs")
+    if tuple(gates.shape) != (B, NQ, H_q, 3):
+        raise ValueError("gates must be [B, NQ, H_q, 3]")
+    n_sel_max = block_idx.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty((B, NQ, H_q, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, NQ, H_q, 3), dtype=torch.float32, device=q.device)
+    n_groups = -(-NQ // group_C)
+    if union_count is None and group_C > 1:
+        union_count = torch.empty((B, n_groups, H), dtype=torch.int32, device=q.device)
+    nbytes = lib().sda_nsa_decode_workspace(B, NQ, H_q, H, n_sel_max, d, T_cap, NC_cap, int(window), int(group_C),
+                                            int(mode))
+    ws, wsb = _workspace(nbytes, q.device, ws)
+    _check(lib().sda_nsa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cmp), _ptr(v_cmp), _ptr(seq_len), _ptr(block_idx),
+                                _ptr(n_sel), n_sel_max, T_cap, NC_cap, int(cmp_stride), int(window), _ptr(gates), B,
+                                NQ, H_q, H, d, float(scale), int(group_C), int(mode), _ptr(out), _ptr(lse),
+                                _ptr(union_count), _ptr(ws), wsb, _stream(stream)))
     return out, lse, union_count
 
 

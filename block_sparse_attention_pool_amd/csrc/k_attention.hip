@@ -88,7 +88,19 @@ struct ListView {
     const int32_t* gn;     // its entry count (global), read by the engine
     const int32_t* lidx;   // LDS list (exact union)
     const uint32_t* lmask; // LDS membership masks (exact union)
-    int n;                 // entry count of the LDS list
+    int n;                 // entry count of the LDS list (or of the range)
+    int lo;                // range list (NSA compressed and window branches): blocks lo .. lo + n - 1
+    bool range;
+};
+
+// The buffer and token range one NSA branch attends to (three-branch mode only)
+struct Branch {
+    const uint16_t* kbase;  // key rows of this (b, g) in the branch's buffer
+    const uint16_t* vbase;
+    int row_cap;            // token rows in that buffer
+    int lo_abs, hi_abs;     // valid tokens [lo_abs, hi_abs)
+    int split_local;        // this workgroup's split inside the branch
+    int n_split;            // the branch's splits
 };
 
 // Read-only int32 the kernel never writes (lengths, block lists): through the
@@ -148,19 +160,21 @@ __device__ __forceinline__ float ld_part(const float* p) {
     else return *p;
 }
 template <int D, int RP, bool coherent>
-__device__ __forceinline__ void merge_row(const AttnArgs& a, int task, int r, size_t oi, int lane) {
+__device__ __forceinline__ void merge_splits(const AttnArgs& a, int task, int r, int lane, int s_begin, int s_end,
+                                             float& M, float& Ls, float (&Os)[D / kWave]) {
     constexpr int PER = D / kWave;
     const float* ml = a.part_ml + ((size_t)task * a.n_split * RP + r) * 2;
     const float* po = a.part_o + ((size_t)task * a.n_split * RP + r) * D + lane;
-    float M = -INFINITY, Ls = 0.f, Os[PER];
+    M = -INFINITY;
+    Ls = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) Os[i] = 0.f;
-    for (int s0 = 0; s0 < a.n_split; s0 += kCombineMax) {
+    for (int s0 = s_begin; s0 < s_end; s0 += kCombineMax) {
         float mv[kCombineMax], lv[kCombineMax], ov[kCombineMax][PER];
 #pragma unroll
         for (int k = 0; k < kCombineMax; ++k) {
             const int s2 = s0 + k;
-            const bool ok = s2 < a.n_split;
+            const bool ok = s2 < s_end;
             mv[k] = ok ? ld_part<D, coherent>(ml + (size_t)s2 * RP * 2) : -INFINITY;
             lv[k] = ok ? ld_part<D, coherent>(ml + (size_t)s2 * RP * 2 + 1) : 0.f;
 #pragma unroll
@@ -183,9 +197,39 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int task, int r, si
         }
         M = Mn;
     }
+}
+
+template <int D, int RP, bool coherent>
+__device__ __forceinline__ void merge_row(const AttnArgs& a, int task, int r, size_t oi, int lane) {
+    constexpr int PER = D / kWave;
+    float M, Ls, Os[PER];
+    merge_splits<D, RP, coherent>(a, task, r, lane, 0, a.n_split, M, Ls, Os);
 #pragma unroll
     for (int i = 0; i < PER; ++i) a.out[oi * D + lane + i * kWave] = (Ls > 0.f) ? Os[i] / Ls : 0.f;
     if (lane == 0 && a.lse) a.lse[oi] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
+}
+
+// NSA gated sum ([SSV] NSA derivation step 6): each branch's splits merged by
+// log-sum-exp and normalised, then o = g_c o_c + g_s o_s + g_w o_w; lse per
+// branch (natural log, -inf for a branch with no token)
+template <int D, int RP>
+__device__ __forceinline__ void merge_row_nsa(const AttnArgs& a, int task, int r, size_t oi, int lane) {
+    constexpr int PER = D / kWave;
+    const int bounds[4] = {0, a.ns_c, a.ns_c + a.ns_s, a.n_split};
+    float acc[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int bi = 0; bi < 3; ++bi) {
+        float M, Ls, Os[PER];
+        merge_splits<D, RP, true>(a, task, r, lane, bounds[bi], bounds[bi + 1], M, Ls, Os);
+        const float w = (Ls > 0.f) ? a.gates[oi * 3 + bi] / Ls : 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += Os[i] * w;
+        if (lane == 0 && a.lse) a.lse[oi * 3 + bi] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) a.out[oi * D + lane + i * kWave] = acc[i];
 }
 
 // ---- decode step: the next layer's scoring and selection ------------------------
@@ -307,9 +351,11 @@ __device__ __forceinline__ void step_score_role(const AttnArgs& a, int w, char* 
 // default policy (the decode launch alone); otherwise the other way round (the
 // decode inside the step launch, where the scoring workgroups stream K~ beside
 // it: 24.1 against 26.8 us per step at the 128K workload).
-template <int D, int NT, bool KSTREAM>
+// NSA: the three-branch mode; `br` gives this workgroup's branch buffer,
+// token range and split inside the branch (unused otherwise).
+template <int D, int NT, bool KSTREAM, bool NSA = false>
 __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, int b, int g, int q0,
-                                                int Cg, int split, int task, char* smem) {
+                                                int Cg, int split, int task, char* smem, const Branch& br = Branch{}) {
     constexpr int KS = D / 32;            // QK k-steps
     constexpr int MTD = D / 16;           // PV m-tiles over d
     constexpr int RP = NT * 16;           // padded rows
@@ -326,8 +372,10 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
     // all are issued, so the first K/V loads follow one round trip.
     const bool glist = L.gidx != nullptr;
     const int n_range = glist ? a.n_sel_max : L.n;
-    const int e_begin = (split * n_range) / a.n_split;
-    const int e_end = ((split + 1) * n_range) / a.n_split;
+    const int s_loc = NSA ? br.split_local : split;
+    const int ns_b = NSA ? br.n_split : a.n_split;
+    const int e_begin = (s_loc * n_range) / ns_b;
+    const int e_end = ((s_loc + 1) * n_range) / ns_b;
     const int32_t* slot_row = (a.slot && glist) ? a.slot + (L.gidx - a.block_idx) : nullptr;
     int e = e_begin + wave;
     int T = ld_ro(a.seq_len + b);
@@ -359,8 +407,10 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
     // the scalar reads are first used here, after every load above is issued
     asm volatile("" : "+s"(T), "+s"(n_g));
     if (glist) L.n = min(max(n_g, 0), a.n_sel_max);
-    const int nb = (T + kBlock - 1) / kBlock;
-    const int blocks_cap = (a.T_cap + kBlock - 1) / kBlock;
+    const int hi_abs = NSA ? br.hi_abs : T;            // valid tokens end here
+    const int row_cap = NSA ? br.row_cap : a.T_cap;     // token rows of the buffer
+    const int nb = (hi_abs + kBlock - 1) / kBlock;
+    const int blocks_cap = (row_cap + kBlock - 1) / kBlock;
 
 
     floatx4 o[MTD][NT];
@@ -377,8 +427,8 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
 
     char* vs = smem + (size_t)wave * VTile<D>::kBytes;
     SDA_LDS char* vs_lds = (SDA_LDS char*)(vs);
-    const uint16_t* kv_k = a.k + ((size_t)b * a.H_kv + g) * a.T_cap * D;
-    const uint16_t* kv_v = a.v + ((size_t)b * a.H_kv + g) * a.T_cap * D;
+    const uint16_t* kv_k = NSA ? br.kbase : a.k + ((size_t)b * a.H_kv + g) * a.T_cap * D;
+    const uint16_t* kv_v = NSA ? br.vbase : a.v + ((size_t)b * a.H_kv + g) * a.T_cap * D;
     // global lists are split over their static width, so a wave's first block
     // id is read together with the row's entry count; entries past the count
     // are padding and skipped
@@ -399,6 +449,10 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
             j = __builtin_amdgcn_readlane(id_v, it & (kWave - 1));
             phys = slot_row ? __builtin_amdgcn_readlane(slot_v, it & (kWave - 1)) : j;
             memb = 0xffffffffu;
+        } else if (NSA && L.range) {
+            j = L.lo + e;
+            phys = j;
+            memb = 0xffffffffu;
         } else {
             j = L.lidx[e];
             phys = j;
@@ -406,12 +460,13 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
         }
         if (e >= L.n) break;
         if (j < 0 || j >= nb || phys < 0 || phys >= blocks_cap) continue;
-        const int nvalid = min(kBlock, T - j * kBlock);
-        if (phys * kBlock + nvalid > a.T_cap) continue;
+        const int nvalid = min(kBlock, hi_abs - j * kBlock);
+        if (phys * kBlock + nvalid > row_cap) continue;
+        const int tfirst = NSA ? max(0, br.lo_abs - j * kBlock) : 0;   // first valid token of the block
         const char* kb = reinterpret_cast<const char*>(kv_k + (size_t)phys * kBlock * D);
         const char* vb = reinterpret_cast<const char*>(kv_v + (size_t)phys * kBlock * D);
         const int tmax = nvalid - 1;
-        const bool full = (nvalid == kBlock) && (memb == 0xffffffffu);   // wave-uniform
+        const bool full = (nvalid == kBlock) && (memb == 0xffffffffu) && tfirst == 0;   // wave-uniform
 
         // ---- K into registers (MFMA A layout), then V into LDS by direct loads;
         //      everything is in flight before the first wait, and QK and the
@@ -470,7 +525,8 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (!(live && tok_of(mt, lg * 4 + i) < nvalid)) s[mt][nt][i] = -INFINITY;
+                        if (!(live && tok_of(mt, lg * 4 + i) < nvalid && tok_of(mt, lg * 4 + i) >= tfirst))
+                            s[mt][nt][i] = -INFINITY;
             }
             float mx = -INFINITY;
 #pragma unroll
@@ -646,14 +702,18 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
     if (!*last) return;
     for (int r = wave; r < R; r += W) {
         const int c = r / G, h = r - (r / G) * G;
-        merge_row<D, RP, true>(a, task, r, ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h, lane);
+        const size_t oi = ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h;
+        if constexpr (NSA) merge_row_nsa<D, RP>(a, task, r, oi, lane);
+        else merge_row<D, RP, true>(a, task, r, oi, lane);
     }
     if (threadIdx.x == 0) __hip_atomic_store(&a.counters[task], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // STEP: the decode step; workgroups past the attention grid score and select
-// (the dispatcher starts them as attention workgroups retire)
-template <int D, int NT, bool STEP>
+// (the dispatcher starts them as attention workgroups retire).
+// NSA: the three-branch mode; split x of a row group serves the compressed
+// branch (x < ns_c), the listed blocks (x < ns_c + ns_s) or the window.
+template <int D, int NT, bool STEP, bool NSA = false>
 __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     if constexpr (STEP) {
@@ -673,9 +733,35 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
     const int Cg = min(a.C, a.NQ - q0);
 
     ListView L{};
+    Branch br{};
+    int branch = 1;                                  // NSA: 0 compressed, 1 listed blocks, 2 window
+    if constexpr (NSA) {
+        branch = split < a.ns_c ? 0 : (split < a.ns_c + a.ns_s ? 1 : 2);
+        const int T = ld_ro(a.seq_len + b);
+        const size_t kvrow = (size_t)b * a.H_kv + g;
+        if (branch == 0) {                           // every compressed entry present at length T
+            const int ncmp = min((T + a.cmp_stride - 1) / a.cmp_stride, a.NC_cap);
+            br = Branch{a.kc + kvrow * a.NC_cap * D, a.vc + kvrow * a.NC_cap * D, a.NC_cap, 0, ncmp, split, a.ns_c};
+            L.range = true;
+            L.lo = 0;
+            L.n = (ncmp + kBlock - 1) / kBlock;
+        } else {                                     // the cache: listed blocks, or tokens [T - window, T)
+            const int lo = branch == 2 ? max(0, T - a.window) : 0;
+            const int s0 = branch == 2 ? a.ns_c + a.ns_s : a.ns_c;
+            br = Branch{a.k + kvrow * a.T_cap * D, a.v + kvrow * a.T_cap * D, a.T_cap, lo, T, split - s0,
+                        branch == 2 ? a.n_split - s0 : a.ns_s};
+            if (branch == 2) {
+                L.range = true;
+                L.lo = lo / kBlock;
+                L.n = T > lo ? (T - 1) / kBlock - lo / kBlock + 1 : 0;
+            }
+        }
+    }
     char* after_v = smem + smem_base(D, NT * 16, blockDim.x / kWave);
     const size_t row0 = ((size_t)b * a.NQ + q0) * a.H_kv + g;   // block_idx row of the group's first query
-    if (a.C == 1 || a.mode == 1) {
+    if (NSA && branch != 1) {
+        // range list set above
+    } else if (a.C == 1 || a.mode == 1) {
         L.gidx = a.block_idx + row0 * a.n_sel_max;
         L.gn = a.n_sel + row0;
     } else {
@@ -747,10 +833,10 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
         L.lmask = lmask;
         L.n = base;
     }
-    run_tile_engine<D, NT, !STEP>(a, L, b, g, q0, Cg, split, task, smem);
+    run_tile_engine<D, NT, !STEP, NSA>(a, L, b, g, q0, Cg, split, task, smem, br);
     // written last: no global store precedes the engine's loads, so the
     // compiler may read lists and lengths through the scalar cache
-    if (a.union_count && a.C > 1 && split == 0 && threadIdx.x == 0)
+    if (a.union_count && a.C > 1 && split == (NSA ? a.ns_c : 0) && threadIdx.x == 0)
         a.union_count[((size_t)b * a.n_groups + grp) * a.H_kv + g] =
             L.gidx ? min(max(ld_ro(L.gn), 0), a.n_sel_max) : L.n;
 }
@@ -855,13 +941,14 @@ static hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
         const int wgs = (a.step.sel.rows * a.step.cpr + a.step.per_wg - 1) / a.step.per_wg;
         extra_rows = (wgs + a.n_split - 1) / a.n_split;
     }
-    auto kern = step ? attn_kernel<D, NT, true> : attn_kernel<D, NT, false>;
-    static bool lds_granted[2] = {false, false};
-    if (!lds_granted[step]) {
+    auto kern = step ? attn_kernel<D, NT, true> : a.nsa ? attn_kernel<D, NT, false, true> : attn_kernel<D, NT, false>;
+    const int kind = step ? 1 : a.nsa ? 2 : 0;
+    static bool lds_granted[3] = {false, false, false};
+    if (!lds_granted[kind]) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCU);
         if (e != hipSuccess) return e;
-        lds_granted[step] = true;
+        lds_granted[kind] = true;
     }
     hipLaunchKernelGGL(kern, dim3(a.n_split, tasks + extra_rows), dim3(a.waves * kWave), smem, s, a);
     hipError_t e = hipGetLastError();
@@ -872,7 +959,7 @@ static hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attention(const AttnArgs& a0, hipStream_t s) {
     AttnArgs a = a0;
-    a.fused_combine = env_int("SDA_ATTN_FUSED_COMBINE", 1);   // 0: merge splits in a second launch
+    a.fused_combine = a.nsa ? 1 : env_int("SDA_ATTN_FUSED_COMBINE", 1);   // 0: merge splits in a second launch
     const int rp = attn_rows_pad(a.C, a.G);
     if (a.d == 128) return rp == 16 ? launch_t<128, 1>(a, s) : launch_t<128, 2>(a, s);
     return rp == 16 ? launch_t<64, 1>(a, s) : launch_t<64, 2>(a, s);

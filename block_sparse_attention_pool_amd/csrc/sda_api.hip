@@ -393,6 +393,111 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
 }
 
 // ---------------------------------------------------------------------------
+// NSA three-branch verification output: the launch shape of the listed-block
+// branch (as sda_grouped_decode plans it) fixes the waves per workgroup and
+// the blocks per split; the compressed and window branches get as many splits
+// as their capacity needs at that rate.
+struct NsaPlan {
+    AttnPlan p;
+    int ns_c, ns_s, ns_w;
+};
+static NsaPlan nsa_plan(int d, int rp, int tasks, int group_C, int mode, int T_cap, int n_sel_max, int NC_cap,
+                        int window) {
+    NsaPlan n{};
+    const int list = grouped_list_estimate(group_C, mode, n_sel_max);
+    n.p = attn_plan(d, rp, tasks, list, group_C, mode, ceil_div(T_cap, kBlock), n_sel_max, 0);
+    const int per = max(1, ceil_div(list, n.p.n_split));
+    const int cmp_blocks = ceil_div(NC_cap, kBlock);
+    const int win_blocks = window > 0 ? ceil_div(window, kBlock) + 1 : 0;    // a window may straddle one more block
+    n.ns_s = n.p.n_split;
+    n.ns_c = max(1, ceil_div(cmp_blocks, per));
+    n.ns_w = max(1, ceil_div(win_blocks, per));
+    return n;
+}
+
+size_t sda_nsa_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int T_cap, int NC_cap,
+                                int window, int group_C, int mode) {
+    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || group_C < 1 || H_q % H_kv || T_cap < 1 ||
+        NC_cap < 1 || window < 0)
+        return 0;
+    const int rp = attn_rows_pad(group_C, H_q / H_kv);
+    const int tasks = B * ceil_div(NQ, group_C) * H_kv;
+    const NsaPlan n = nsa_plan(d, rp, tasks, group_C, mode, T_cap, n_sel_max, NC_cap, window);
+    return attn_ws_bytes(tasks, n.ns_c + n.ns_s + n.ns_w, rp, d);
+}
+
+sda_status_t sda_nsa_decode(const void* q, const void* k, const void* v, const void* k_cmp, const void* v_cmp,
+                            const int32_t* seq_len, const int32_t* block_idx, const int32_t* n_sel, int n_sel_max,
+                            int T_cap, int NC_cap, int cmp_stride, int window, const float* gates, int B, int NQ,
+                            int H_q, int H_kv, int d, float scale, int group_C, int mode, float* out,
+                            float* lse_opt, int32_t* union_count_opt, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_attn_common(q, k, v, seq_len, block_idx, n_sel, n_sel_max, T_cap, B, NQ, H_q, H_kv, d, scale, out,
+                          0));
+    REQUIRE(k_cmp && v_cmp && gates, SDA_ERR_NULL, "nsa_decode: compressed cache or gates is null");
+    REQUIRE(aligned16(k_cmp) && aligned16(v_cmp), SDA_ERR_ALIGN, "k_cmp and v_cmp must be 16-byte aligned");
+    REQUIRE(aligned4(gates) && (!lse_opt || aligned4(lse_opt)) && (!union_count_opt || aligned4(union_count_opt)),
+            SDA_ERR_ALIGN, "gates, lse and union_count must be 4-byte aligned");
+    REQUIRE(cmp_stride >= 1 && cmp_stride <= 64, SDA_ERR_UNSUPPORTED, "cmp_stride=%d outside [1, 64]", cmp_stride);
+    REQUIRE(NC_cap >= ceil_div(T_cap, cmp_stride), SDA_ERR_SHAPE, "NC_cap=%d < ceil(T_cap/cmp_stride)=%d", NC_cap,
+            ceil_div(T_cap, cmp_stride));
+    REQUIRE(window >= 0, SDA_ERR_SHAPE, "window=%d < 0", window);
+    REQUIRE(group_C >= 1 && group_C <= 8, SDA_ERR_UNSUPPORTED, "group_C=%d outside [1, 8]", group_C);
+    REQUIRE(mode == SDA_GROUP_EXACT || mode == SDA_GROUP_SHARED_REP, SDA_ERR_SHAPE, "mode=%d", mode);
+    const int G = H_q / H_kv;
+    REQUIRE(group_C * G <= 32, SDA_ERR_UNSUPPORTED, "group_C*G=%d exceeds 32 rows", group_C * G);
+    REQUIRE(ceil_div(T_cap, kBlock) <= kMaxNBCap, SDA_ERR_UNSUPPORTED, "T_cap=%d beyond %d blocks", T_cap, kMaxNBCap);
+    const int n_groups = ceil_div(NQ, group_C);
+    const long long tasks = (long long)B * n_groups * H_kv;
+    REQUIRE(tasks <= kMaxGridYZ, SDA_ERR_SHAPE, "B*groups*H_kv=%lld exceeds %d", tasks, kMaxGridYZ);
+    const int rp = attn_rows_pad(group_C, G);
+    const NsaPlan n = nsa_plan(d, rp, (int)tasks, group_C, mode, T_cap, n_sel_max, NC_cap, window);
+    const int ns = n.ns_c + n.ns_s + n.ns_w;
+    REQUIRE(ns <= kMaxSplits, SDA_ERR_UNSUPPORTED, "%d splits per row group exceed %d", ns, kMaxSplits);
+    const size_t lds = attn_smem_bytes_host(d, rp, n.p.waves, group_C, mode, ceil_div(T_cap, kBlock), n_sel_max);
+    REQUIRE(lds <= kLdsBytes, SDA_ERR_UNSUPPORTED, "group needs %zu bytes of LDS", lds);
+    const size_t need = attn_ws_bytes((int)tasks, ns, rp, d);
+    REQUIRE(ws && ws_bytes >= need, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, need);
+    REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    AttnArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.seq_len = seq_len;
+    a.block_idx = block_idx;
+    a.n_sel = n_sel;
+    a.slot = nullptr;
+    a.out = out;
+    a.lse = lse_opt;
+    a.union_count = union_count_opt;
+    set_workspace(a, ws, need, (int)tasks, ns, rp);
+    a.n_sel_max = n_sel_max;
+    a.T_cap = T_cap;
+    a.NB_cap = ceil_div(T_cap, kBlock);
+    a.B = B;
+    a.NQ = NQ;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.G = G;
+    a.d = d;
+    a.C = group_C;
+    a.mode = mode;
+    a.n_groups = n_groups;
+    a.n_split = ns;
+    a.waves = n.p.waves;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.nsa = 1;
+    a.kc = static_cast<const uint16_t*>(k_cmp);
+    a.vc = static_cast<const uint16_t*>(v_cmp);
+    a.gates = gates;
+    a.NC_cap = NC_cap;
+    a.cmp_stride = cmp_stride;
+    a.window = window;
+    a.ns_c = n.ns_c;
+    a.ns_s = n.ns_s;
+    return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)), "nsa_decode launch");
+}
+
+// ---------------------------------------------------------------------------
 // decode step: layer l's decode and layer l+1's scoring and selection in one
 // launch (workgroups past the attention grid score and select)
 static bool step_fused_plan(int B, int H_q, int H_kv, int d, int n_sel_max, int split_k, int NB_cap_next,

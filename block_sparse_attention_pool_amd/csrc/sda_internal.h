@@ -113,6 +113,16 @@ struct AttnArgs {
     // Optional (the decode-step entry point): workgroups past the attention
     // grid score the next layer and select its blocks (step.cand null = off)
     StepScore step;
+    // NSA three-branch mode (nsa = 1): splits [0, ns_c) attend to the
+    // compressed cache, [ns_c, ns_c + ns_s) to the listed blocks, the rest to
+    // the last `window` tokens; the last workgroup of a row group merges each
+    // branch's splits and writes the gated sum
+    int nsa;
+    const uint16_t* kc;       // compressed keys   [B, H_kv, NC_cap, d]
+    const uint16_t* vc;       // compressed values [B, H_kv, NC_cap, d]
+    const float* gates;       // [B, NQ, H_q, 3]: g_c, g_s, g_w
+    int NC_cap, cmp_stride, window;
+    int ns_c, ns_s;
 };
 struct AttnPlan {
     int waves;                // waves per workgroup

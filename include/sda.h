@@ -236,6 +236,40 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
                                 int split_k, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * NSA verification output with its three branches in one launch ([SSV] NSA
+ * three-branch derivation, steps 3-6; verification-kernel algorithm step 3c):
+ * for every query head h of every query,
+ *   o = g_c * Attn(q_h, K~, V~) + g_s * Attn(q_h, K_B, V_B) + g_w * Attn(q_h, K_win, V_win)
+ * where the compressed branch attends to the ceil(seq_len / cmp_stride)
+ * compressed keys and values present, the selection branch to the listed
+ * blocks exactly as sda_grouped_decode (group_C, mode: the merged set loaded
+ * once per group), and the window branch to tokens [seq_len - window, seq_len).
+ * Each branch keeps its own softmax; the last workgroup of a row group merges
+ * each branch's splits by log-sum-exp, normalises, and writes the gated sum.
+ *
+ *   q .. n_sel_max, T_cap   as sda_grouped_decode (NB_cap = ceil(T_cap / 64))
+ *   k_cmp, v_cmp  bf16 [B, H_kv, NC_cap, d]: compressed keys and values, e.g. from
+ *                 sda_update_compressed_keys(_strided) applied to K and to V
+ *   cmp_stride    tokens per compressed entry's stride (1..64), NC_cap >= ceil(T_cap / cmp_stride)
+ *   window        w >= 0 tokens of the sliding-window branch (0: the branch is empty)
+ *   gates         f32 [B, NQ, H_q, 3]: (g_c, g_s, g_w) per query head
+ *   out           f32 [B, NQ, H_q, d]
+ *   lse_opt       f32 [B, NQ, H_q, 3] or NULL: each branch's log-sum-exp (natural
+ *                 log, -inf for a branch with no token; that branch contributes 0)
+ *   union_count_opt  as sda_grouped_decode
+ * Workspace: sda_nsa_decode_workspace() bytes (always > 0), with the
+ * zero-fill and no-overlap contract of sda_sparse_decode.
+ */
+size_t sda_nsa_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int T_cap,
+                                int NC_cap, int window, int group_C, int mode);
+sda_status_t sda_nsa_decode(const void* q, const void* k, const void* v, const void* k_cmp, const void* v_cmp,
+                            const int32_t* seq_len, const int32_t* block_idx, const int32_t* n_sel,
+                            int n_sel_max, int T_cap, int NC_cap, int cmp_stride, int window,
+                            const float* gates, int B, int NQ, int H_q, int H_kv, int d, float scale,
+                            int group_C, int mode, float* out, float* lse_opt, int32_t* union_count_opt,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
  * One decode step of the layer pipeline ([SparDA] §4.2 and eq. (6): layer l's
  * indexer vectors choose layer l+1's blocks while layer l attends).  The
  * block sets are those of sda_score_select(f_next, k_tilde_next, ...), bit for

@@ -38,7 +38,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = header_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
         assert n in sda.exported_symbols(), n
@@ -140,6 +140,40 @@ def test_pooled_workspace_and_validation(L):
     bad = list(args); bad[7] = 90000                                     # beyond the block limit of the select launch
     assert f(*bad) == UNSUP
     bad = list(args); bad[1] = P_ODD
+    assert f(*bad) == ALIGN
+
+
+def test_nsa_workspace_and_validation(L):
+    # 64 row groups x 9 splits (4 listed, 4 compressed at 2048 keys, 1 window) of 16 padded rows
+    def dec(tasks, splits, rows=16, d=128):
+        return (tasks * 4 + 255) // 256 * 256 + tasks * splits * rows * (d + 2) * 4
+    n = L.sda_nsa_decode_workspace(8, 1, 64, 8, 35, 128, 131072, 2048, 512, 1, 0)
+    assert n in {dec(64, s) for s in range(3, 80)}
+    assert L.sda_nsa_decode_workspace(8, 1, 64, 8, 35, 128, 131072, 2048, -1, 1, 0) == 0
+    f = L.sda_nsa_decode
+    # q, k, v, k_cmp, v_cmp, seq_len, block_idx, n_sel, n_sel_max, T_cap, NC_cap, cmp_stride, window,
+    # gates, B, NQ, H_q, H_kv, d, scale, group_C, mode, out, lse, union_count, ws, ws_bytes, stream
+    args = [P, P, P, P, P, P, P, P, 11, 4096, 64, 64, 512, P, 1, 1, 8, 2, 64, 0.125, 1, 0, P, None, None,
+            P, 1 << 24, None]
+    bad = list(args); bad[3] = None
+    assert f(*bad) == NULL
+    bad = list(args); bad[13] = None                                     # gates
+    assert f(*bad) == NULL
+    bad = list(args); bad[10] = 63                                       # NC_cap < ceil(T_cap / stride)
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[11] = 0
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[12] = -1
+    assert f(*bad) == SHAPE
+    bad = list(args); bad[20] = 9
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[20] = 8; bad[15] = 8; bad[16] = 16             # 8 queries x G = 8 > 32 rows
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[26] = 64
+    assert f(*bad) == WS
+    bad = list(args); bad[4] = P_ODD
+    assert f(*bad) == ALIGN
+    bad = list(args); bad[13] = P + 2
     assert f(*bad) == ALIGN
 
 
