@@ -378,6 +378,43 @@ def measure_grouped(O):
         t = graph_time(grouped_call, copies=n_sets)
         blocks = sum(int(u.sum().item()) for u in ucs) / n_sets       # mean blocks per call
         res[name] = {"us": t * 1e6, "blocks_loaded": blocks, "roofline": hbm(blocks * blk, t)}
+    # NSA's three branches in one launch (exact merge for the listed blocks,
+    # a 512-token window, 64/64 compressed keys and values, random gates)
+    window = 512
+    seq_len_full = torch.full((cfg.B,), cfg.T, dtype=torch.int32, device=dev)
+    zero = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+    kc = torch.zeros((cfg.B, cfg.H_kv, cfg.NB, cfg.d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    sda.sda_update_compressed_keys(K, kc, zero, seq_len_full, cfg.T)
+    sda.sda_update_compressed_keys(V, vc, zero, seq_len_full, cfg.T)
+    gates = torch.rand((cfg.B, cfg.NQ, cfg.H_q, 3), generator=torch.Generator(device=dev).manual_seed(5),
+                       device=dev, dtype=torch.float32)
+    nsa_ws = torch.zeros(sda.lib().sda_nsa_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d, cfg.T,
+                                                            cfg.NB, window, C, sda.SDA_GROUP_EXACT),
+                         dtype=torch.uint8, device=dev)
+    nsa_out = torch.empty_like(out)
+    nsa_lse = torch.empty((cfg.B, cfg.NQ, cfg.H_q, 3), dtype=torch.float32, device=dev)
+    ucs_n = [torch.empty_like(uc) for _ in range(n_sets)]
+    turn = [0]
+
+    def nsa_call():
+        i = turn[0] % n_sets
+        turn[0] += 1
+        sda.sda_nsa_decode(Q, K, V, kc, vc, seq, bis[i], ns, gates, 64, window, group_C=C, mode=sda.SDA_GROUP_EXACT,
+                           out=nsa_out, lse=nsa_lse, union_count=ucs_n[i], ws=nsa_ws)
+    t = graph_time(nsa_call, copies=n_sets)
+    groups = cfg.B * (cfg.NQ // C) * cfg.H_kv
+    sel_blocks = sum(int(u.sum().item()) for u in ucs_n) / n_sets
+    win_blocks = groups * (window // 64)
+    cmp_bytes = groups * cfg.NB * cfg.d * 2 * 2
+    nsa_bytes = (sel_blocks + win_blocks) * blk + cmp_bytes
+    res["nsa_three_branch"] = {
+        "us": t * 1e6, "window": window, "compressed_keys_per_row": cfg.NB,
+        "selected_blocks_loaded": sel_blocks, "window_blocks_loaded": win_blocks,
+        "roofline": hbm(nsa_bytes, t),
+        "extra_us_over_mode_A": t * 1e6 - res["mode_A"]["us"],
+    }
+    del kc, vc
     ws = torch.zeros(sda.lib().sda_sparse_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d, 0),
                      dtype=torch.uint8, device=dev)
     turn = [0]

@@ -393,10 +393,10 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
 }
 
 // ---------------------------------------------------------------------------
-// NSA three-branch verification output: the launch shape of the listed-block
-// branch (as sda_grouped_decode plans it) fixes the waves per workgroup and
-// the blocks per split; the compressed and window branches get as many splits
-// as their capacity needs at that rate.
+// NSA three-branch verification output: the launch is planned as one list of
+// all three branches' blocks per row group (listed, compressed, window), which
+// fixes the waves per workgroup and the blocks per split; each branch then
+// takes splits in proportion to its blocks (at least one).
 struct NsaPlan {
     AttnPlan p;
     int ns_c, ns_s, ns_w;
@@ -405,11 +405,12 @@ static NsaPlan nsa_plan(int d, int rp, int tasks, int group_C, int mode, int T_c
                         int window) {
     NsaPlan n{};
     const int list = grouped_list_estimate(group_C, mode, n_sel_max);
-    n.p = attn_plan(d, rp, tasks, list, group_C, mode, ceil_div(T_cap, kBlock), n_sel_max, 0);
-    const int per = max(1, ceil_div(list, n.p.n_split));
     const int cmp_blocks = ceil_div(NC_cap, kBlock);
     const int win_blocks = window > 0 ? ceil_div(window, kBlock) + 1 : 0;    // a window may straddle one more block
-    n.ns_s = n.p.n_split;
+    const int total = list + cmp_blocks + win_blocks;
+    n.p = attn_plan(d, rp, tasks, total, group_C, mode, ceil_div(T_cap, kBlock), n_sel_max, 0);
+    const int per = max(1, ceil_div(total, n.p.n_split));                   // blocks per split
+    n.ns_s = max(1, ceil_div(list, per));
     n.ns_c = max(1, ceil_div(cmp_blocks, per));
     n.ns_w = max(1, ceil_div(win_blocks, per));
     return n;
