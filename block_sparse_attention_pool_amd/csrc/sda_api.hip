@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "../../include/sda.h"
@@ -393,10 +394,17 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
 }
 
 // ---------------------------------------------------------------------------
-// NSA three-branch verification output: the launch is planned as one list of
-// all three branches' blocks per row group (listed, compressed, window), which
-// fixes the waves per workgroup and the blocks per split; each branch then
-// takes splits in proportion to its blocks (at least one).
+// NSA three-branch verification output.  Launch shape: the most waves per
+// workgroup that still let two workgroups share a compute unit (LDS of the V
+// tiles and the merged lists, resident waves), and as many splits per row
+// group as fill the two slots of every compute unit in one dispatch round
+// (at least one per branch), shared among the branches in proportion to
+// their blocks.  A branch's workgroup walks its blocks W apart, so the
+// longest branch, not the launch as a whole, sets the pace; measured on the
+// 64K verification workload this shape (4 waves, 2/1/1 splits) took 54 us
+// against 62-92 us for shapes with a single slot per compute unit or one
+// split for the 16-block compressed branch.
+constexpr int kNsaMaxWaves = 10;                     // the attention kernel's waves per workgroup
 struct NsaPlan {
     AttnPlan p;
     int ns_c, ns_s, ns_w;
@@ -408,11 +416,16 @@ static NsaPlan nsa_plan(int d, int rp, int tasks, int group_C, int mode, int T_c
     const int cmp_blocks = ceil_div(NC_cap, kBlock);
     const int win_blocks = window > 0 ? ceil_div(window, kBlock) + 1 : 0;    // a window may straddle one more block
     const int total = list + cmp_blocks + win_blocks;
-    n.p = attn_plan(d, rp, tasks, total, group_C, mode, ceil_div(T_cap, kBlock), n_sel_max, 0);
-    const int per = max(1, ceil_div(total, n.p.n_split));                   // blocks per split
-    n.ns_s = max(1, ceil_div(list, per));
-    n.ns_c = max(1, ceil_div(cmp_blocks, per));
-    n.ns_w = max(1, ceil_div(win_blocks, per));
+    const int NB_cap = ceil_div(T_cap, kBlock);
+    const int resident = rp == 16 ? 12 : 4;                 // waves per compute unit (VGPR-bound)
+    int W = std::min(kNsaMaxWaves / 2, resident / 2);
+    while (W > 1 && 2 * attn_smem_bytes_host(d, rp, W, group_C, mode, NB_cap, n_sel_max) > kLdsBytes) --W;
+    const int S = std::max(3, (2 * kCUs) / std::max(tasks, 1));
+    n.ns_c = std::min(cmp_blocks, std::max(1, (S * cmp_blocks + total / 2) / total));
+    n.ns_w = std::max(1, std::min(win_blocks, (S * win_blocks + total / 2) / total));
+    n.ns_s = std::min(std::max(list, 1), std::max(1, S - n.ns_c - n.ns_w));
+    n.ns_c = std::max(1, n.ns_c);
+    n.p = AttnPlan{W, n.ns_s};
     return n;
 }
 
