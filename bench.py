@@ -622,6 +622,8 @@ def main():
                     help="fused: one sda_decode_step call per layer (the decode launch finishes the next "
                          "layer's selection); separate: sda_score_select then sda_sparse_decode")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--step-refresh", action="store_true",
+                    help="the step launch also refreshes the decoded layer's compressed keys for its newest token")
     ap.add_argument("--call-reps", type=int, default=50, help="graph replays per per-call timing")
     args = ap.parse_args()
 
@@ -663,16 +665,21 @@ def main():
                             lse=lse, split_k=args.split_k, ws=ws_dec)
         calls.append((sc, dc))
     # the step entry point: position i decodes layer i with bi[i] and selects
-    # layer i+1's blocks (layer i's indexer vectors, layer i+1's compressed keys)
+    # layer i+1's blocks (layer i's indexer vectors, layer i+1's compressed
+    # keys); --step-refresh also refreshes layer i's compressed keys for its
+    # newest token in the same launch (not part of the metric's step)
     ws_step = torch.zeros(sda.lib().sda_decode_step_workspace(cfg.B, cfg.H_q, cfg.H_kv, cfg.d, n_sel_max,
                                                               args.split_k, cfg.NB, cfg.top_k),
                           dtype=torch.uint8, device=dev)
+    seq_prev = seq - 1
     step_calls = []
     for i in range(L):
         lc, ln = layers[i], layers[(i + 1) % L]
         pc, _ = sda.prepare(sda.sda_decode_step, lc["Q"], lc["K"], lc["V"], seq, bi[i], ns[i], lc["F"], ln["kt"],
                             seq, cfg.n_init, cfg.n_local, cfg.top_k, block_idx_next=bi[(i + 1) % L],
-                            n_sel_next=ns[(i + 1) % L], out=out, lse=lse, split_k=args.split_k, ws=ws_step)
+                            n_sel_next=ns[(i + 1) % L], out=out, lse=lse, split_k=args.split_k,
+                            k_tilde_cur=lc["kt"] if args.step_refresh else None, len_old_cur=seq_prev,
+                            max_new_tokens_cur=1, ws=ws_step)
         step_calls.append(pc)
 
     def fused_step(i, ev=None):
@@ -748,7 +755,10 @@ def main():
     # the dominant kernel of the timed step: the step launch (decode of layer l
     # plus scoring and selection of layer l+1), else the decode launch
     rl_key = "decode_step" if step_fused else "sparse_decode"
-    rl_bytes = dec_bytes + sel_bytes if step_fused else dec_bytes
+    # the step also refreshes the block of layer l's compressed keys that holds
+    # the newest token: 64 keys read and one compressed key written per row
+    ref_bytes = cfg.B * cfg.H_kv * (64 * cfg.d * 2 + cfg.d * 2) if args.step_refresh else 0
+    rl_bytes = dec_bytes + sel_bytes + ref_bytes if step_fused else dec_bytes
     rl_gbs = rl_bytes / (t_step if step_fused else t_dec.mean()) / 1e9
 
     def counters_for(key):
@@ -788,7 +798,9 @@ def main():
                       + (", layer l+1's score_select beside layer l's sparse_decode (two streams)"
                          if args.overlap else
                          ", one sda_decode_step per layer (one launch: layer l's decode workgroups, then "
-                         "workgroups that score layer l+1's compressed keys and select its block sets)"
+                         "workgroups that score layer l+1's compressed keys and select its block sets"
+                         + (", then workgroups that refresh layer l's compressed keys for the newest token)"
+                            if args.step_refresh else ")")
                          if args.step == "fused" else ", score_select then sparse_decode per layer"),
         },
         "roofline": {
@@ -799,7 +811,8 @@ def main():
             "frac": rl_gbs / HBM_PEAK_GBS,
             "traffic": counters_for(rl_key),
             "kernel": ("attn_kernel<128, 1, true> (sda_decode_step: layer l's decode and layer l+1's scoring "
-                       "and selection in one launch)" if step_fused else
+                       "and selection in one launch" + (", with the refresh of layer l's compressed keys)"
+                                                        if args.step_refresh else ")") if step_fused else
                        "attn_kernel<128, 1, false> (sda_sparse_decode; splits merged by the last workgroup of "
                        "each row)"),
             "algorithmic_bytes_per_launch": rl_bytes,

@@ -66,7 +66,8 @@ _SIGNATURES = {
     "sda_decode_step_workspace": (_c_size_t, [_c_int] * 8),
     "sda_decode_step_is_fused": (_c_int, [_c_int] * 8),
     "sda_decode_step": (_c_int, [_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_void_p, _c_void_p, _c_int]
-                        + [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 3 + [_c_size_t, _c_void_p]),
+                        + [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 4 + [_c_int] * 2
+                        + [_c_void_p, _c_size_t, _c_void_p]),
 }
 
 _lib = None
@@ -329,10 +330,12 @@ def sda_sparse_decode(q, k, v, seq_len, block_idx, n_sel, scale=None, out=None, 
 
 def sda_decode_step(q, k, v, seq_len, block_idx, n_sel, f_next, k_tilde_next, seq_len_next, n_init, n_local,
                     top_k, n_sel_max_next=None, block_idx_next=None, n_sel_next=None, scale=None, out=None,
-                    lse=None, split_k=0, ws=None, stream=None, _prepare=False):
+                    lse=None, split_k=0, k_tilde_cur=None, len_old_cur=None, max_new_tokens_cur=1, ws=None,
+                    stream=None, _prepare=False):
     """Layer l's decode plus layer l+1's selection (same results as
-    sda_score_select for l+1 then sda_sparse_decode for l); returns
-    (out, lse, block_idx_next, n_sel_next)."""
+    sda_score_select for l+1 then sda_sparse_decode for l) and, with
+    k_tilde_cur, the refresh of layer l's compressed keys for the tokens
+    [len_old_cur, seq_len); returns (out, lse, block_idx_next, n_sel_next)."""
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
     _need(v, "v", torch.bfloat16, 4)
@@ -365,16 +368,24 @@ def sda_decode_step(q, k, v, seq_len, block_idx, n_sel, f_next, k_tilde_next, se
         block_idx_next = torch.empty((B, 1, H_kv, n_sel_max_next), dtype=torch.int32, device=dev)
     if n_sel_next is None:
         n_sel_next = torch.empty((B, 1, H_kv), dtype=torch.int32, device=dev)
+    NB_cap_cur = 0
+    if k_tilde_cur is not None:
+        _need(k_tilde_cur, "k_tilde_cur", torch.bfloat16, 4)
+        _need(len_old_cur, "len_old_cur", torch.int32, 1)
+        if k_tilde_cur.shape[:2] != (B, H_kv) or k_tilde_cur.shape[3] != d or len_old_cur.numel() != B:
+            raise ValueError("k_tilde_cur [B, H_kv, NB_cap, d] and len_old_cur [B] must match k")
+        NB_cap_cur = k_tilde_cur.shape[2]
     nbytes = lib().sda_decode_step_workspace(B, H_q, H_kv, d, n_sel_max, int(split_k), NB_cap_next, top_k)
     ws, wsb = _workspace(nbytes, dev, ws)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(block_idx), _ptr(n_sel), n_sel_max, T_cap, B, H_q,
             H_kv, d, float(scale), _ptr(out), _ptr(lse), int(split_k), _ptr(f_next), _ptr(k_tilde_next),
             _ptr(seq_len_next), NB_cap_next, n_init, n_local, top_k, n_sel_max_next, _ptr(block_idx_next),
-            _ptr(n_sel_next), _ptr(ws), wsb, None)
+            _ptr(n_sel_next), _ptr(k_tilde_cur), _ptr(len_old_cur), int(max_new_tokens_cur), NB_cap_cur,
+            _ptr(ws), wsb, None)
     outs = (out, lse, block_idx_next, n_sel_next)
     if _prepare:
         return PreparedCall("sda_decode_step", args, (q, k, v, seq_len, block_idx, n_sel, f_next, k_tilde_next,
-                                                       seq_len_next, ws) + outs), outs
+                                                       seq_len_next, ws, k_tilde_cur, len_old_cur) + outs), outs
     _check(lib().sda_decode_step(*args[:-1], _stream(stream)))
     return outs
 

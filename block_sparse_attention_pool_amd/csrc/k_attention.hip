@@ -35,6 +35,7 @@
 
 #include "sda_device.hpp"
 #include "sda_internal.h"
+#include "sda_ktilde_dev.hpp"
 #include "sda_select_dev.hpp"
 
 namespace sda {
@@ -345,6 +346,40 @@ __device__ __forceinline__ void step_score_role(const AttnArgs& a, int w, char* 
     step_scores<D>(a, p, smem);
     step_level1(a, p, smem);
     step_finish(a, p, w, smem);
+}
+
+// The refresh of this layer's compressed keys ([SparDA] §4.2 step 1: the key
+// just appended updates its block's mean): the blocks touched by the tokens
+// [ref_len_old, seq_len) of each row, recomputed whole with the arithmetic of
+// sda_update_compressed_keys.  Item i = (row, i-th touched block).
+template <int D>
+__device__ __forceinline__ bool refresh_item(const AttnArgs& a, int item, int& row, int& j, int& t0, int& n) {
+    const StepScore& st = a.step;
+    row = item / st.ref_blocks;                         // b * H_kv + g
+    if (row >= a.B * a.H_kv) return false;
+    const int b = row / a.H_kv;
+    const int lo = max(ld_ro(st.ref_len_old + b), 0);
+    const int hi = min(ld_ro(a.seq_len + b), a.T_cap);
+    if (hi <= lo) return false;
+    j = lo / kBlock + (item - row * st.ref_blocks);
+    if (j > (hi - 1) / kBlock || j >= st.ref_NB_cap) return false;
+    t0 = j * kBlock;
+    n = min(kBlock, hi - t0);
+    return true;
+}
+
+// by a workgroup of its own, placed after the scoring workgroups: item w, all
+// threads (one barrier).  Measured at the 128K workload: +0.3 us per step
+// launch (+0.9 us per step of the 80-step graph), against 3.4 us for a
+// separate refresh launch; refresh workgroups dispatched before the scoring
+// ones, or the scoring workgroups' idle waves doing the refresh, were slower
+// (+1.8 and +2.1 us per step launch)
+template <int D>
+__device__ __forceinline__ void step_refresh_role(const AttnArgs& a, int w, char* smem) {
+    int row, j, t0, n;
+    if (!refresh_item<D>(a, w, row, j, t0, n)) return;       // uniform over the workgroup
+    ktilde_window<D>(a.k, a.step.ref_kt, row, j, t0, n, a.T_cap, a.step.ref_NB_cap, threadIdx.x,
+                     reinterpret_cast<double (*)[D + 2]>(smem));
 }
 
 // KSTREAM: the K loads carry the non-temporal hint and the V direct loads the
@@ -713,13 +748,24 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
 // (the dispatcher starts them as attention workgroups retire).
 // NSA: the three-branch mode; split x of a row group serves the compressed
 // branch (x < ns_c), the listed blocks (x < ns_c + ns_s) or the window.
-template <int D, int NT, bool STEP, bool NSA = false>
+// REF (with STEP): ref_rows grid rows of workgroups after the scoring ones
+// refresh the decoded layer's compressed keys (a variant of its own, so the
+// step without it keeps its code).
+template <int D, int NT, bool STEP, bool NSA = false, bool REF = false>
 __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     if constexpr (STEP) {
         const int attn_rows = a.B * a.n_groups * a.H_kv;
         if ((int)blockIdx.y >= attn_rows) {
-            step_score_role<D>(a, ((int)blockIdx.y - attn_rows) * (int)gridDim.x + (int)blockIdx.x, smem);
+            const int w = ((int)blockIdx.y - attn_rows) * (int)gridDim.x + (int)blockIdx.x;
+            if constexpr (REF) {
+                const int score_wgs = ((int)gridDim.y - attn_rows - a.step.ref_rows) * (int)gridDim.x;
+                if (w >= score_wgs) {
+                    step_refresh_role<D>(a, w - score_wgs, smem);
+                    return;
+                }
+            }
+            step_score_role<D>(a, w, smem);
             return;
         }
     }
@@ -934,23 +980,33 @@ static hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     const int tasks = a.B * a.n_groups * a.H_kv;
     const bool step = a.step.cand != nullptr;
     size_t smem = attn_smem_bytes_host(D, NT * 16, a.waves, a.C, a.mode, a.NB_cap, a.n_sel_max);
-    int extra_rows = 0;                        // grid rows of workgroups that only score
+    int extra_rows = 0;                        // grid rows of workgroups that only score or refresh
+    AttnArgs aa = a;
     if (step) {
-        const size_t need = step_lds_bytes(a.step.sel.top_k, a.step.cpr, a.step.per_wg);
+        size_t need = step_lds_bytes(a.step.sel.top_k, a.step.cpr, a.step.per_wg);
         if (need > smem) smem = need;
         const int wgs = (a.step.sel.rows * a.step.cpr + a.step.per_wg - 1) / a.step.per_wg;
         extra_rows = (wgs + a.n_split - 1) / a.n_split;
+        aa.step.ref_rows = 0;
+        if (a.step.ref_kt) {
+            const int ref_wgs = a.B * a.H_kv * a.step.ref_blocks;
+            aa.step.ref_rows = (ref_wgs + a.n_split - 1) / a.n_split;
+            extra_rows += aa.step.ref_rows;
+            if (KtildeShape<D>::kLdsBytes > smem) smem = KtildeShape<D>::kLdsBytes;
+        }
     }
-    auto kern = step ? attn_kernel<D, NT, true> : a.nsa ? attn_kernel<D, NT, false, true> : attn_kernel<D, NT, false>;
-    const int kind = step ? 1 : a.nsa ? 2 : 0;
-    static bool lds_granted[3] = {false, false, false};
+    const bool ref = step && a.step.ref_kt != nullptr;
+    auto kern = ref ? attn_kernel<D, NT, true, false, true>
+                    : step ? attn_kernel<D, NT, true> : a.nsa ? attn_kernel<D, NT, false, true> : attn_kernel<D, NT, false>;
+    const int kind = ref ? 3 : step ? 1 : a.nsa ? 2 : 0;
+    static bool lds_granted[4] = {false, false, false, false};
     if (!lds_granted[kind]) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCU);
         if (e != hipSuccess) return e;
         lds_granted[kind] = true;
     }
-    hipLaunchKernelGGL(kern, dim3(a.n_split, tasks + extra_rows), dim3(a.waves * kWave), smem, s, a);
+    hipLaunchKernelGGL(kern, dim3(a.n_split, tasks + extra_rows), dim3(a.waves * kWave), smem, s, aa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1 || a.fused_combine) return e;
     hipLaunchKernelGGL((combine_kernel<D, NT * 16>), dim3(tasks, NT * 16), dim3(64), 0, s, a);

@@ -18,27 +18,9 @@
 // HBM-bound: l*d*2 bytes read, d*2 bytes written per entry.
 #include "sda_device.hpp"
 #include "sda_internal.h"
+#include "sda_ktilde_dev.hpp"
 
 namespace sda {
-
-// Nearest bf16 (ties to even) of an fp64 value, rounded once: first to fp32
-// by rounding to odd (truncate, then set the last bit if anything was cut),
-// which keeps 16 extra bits and a sticky bit, then to nearest even bf16.
-// Rounding to odd with two or more extra bits before rounding to nearest
-// equals a direct rounding to nearest (Boldo and Melquiond, "Emulation of FMA
-// and correctly rounded sums: proved algorithms using rounding to odd").
-__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
-    if (x != x) return 0x7FC0;                               // NaN
-    const float f = (float)x;                                // nearest; may land past x
-    uint32_t u = __float_as_uint(f);
-    const double fd = (double)f;
-    if (fd != x) {
-        if (fabs(fd) > fabs(x)) u -= 1u;                     // one step back toward zero
-        u |= 1u;                                             // inexact: odd
-    }
-    u += 0x7FFFu + ((u >> 16) & 1u);                         // nearest, ties to even
-    return (uint16_t)(u >> 16);
-}
 
 template <int D>
 __global__ __launch_bounds__(256) void ktilde_kernel(const uint16_t* __restrict__ k,
@@ -46,10 +28,7 @@ __global__ __launch_bounds__(256) void ktilde_kernel(const uint16_t* __restrict_
                                                      const int32_t* __restrict__ len_old,
                                                      const int32_t* __restrict__ len_new,
                                                      int H_kv, int T_cap, int NC_cap, int window, int stride) {
-    constexpr int LPR = D / 8;          // lanes per key row (8 bf16 per lane)
-    constexpr int RPS = 256 / LPR;      // rows per load step
-    constexpr int STEPS = kBlock / RPS;
-    __shared__ double red[RPS][D + 2];
+    __shared__ double red[KtildeShape<D>::RPS][D + 2];
 
     const int row = blockIdx.y;                 // b * H_kv + g
     const int b = row / H_kv;
@@ -64,38 +43,7 @@ __global__ __launch_bounds__(256) void ktilde_kernel(const uint16_t* __restrict_
 
     const int t0 = j * stride;
     const int n = min(window, hi - t0);         // tokens present in this window (1..64)
-    const int tid = threadIdx.x;
-    const int c8 = (tid % LPR) * 8;             // first column of this lane
-    const int r0 = tid / LPR;
-
-    const uint16_t* base = k + ((size_t)row * T_cap + t0) * D + c8;
-    u32x4 w[STEPS];
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        const int r = r0 + s * RPS;
-        if (r < n) w[s] = ldg16(base + (size_t)r * D);
-        else w[s] = u32x4{0, 0, 0, 0};
-    }
-    double acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0;
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += (double)bf16lo(w[s][i]);
-            acc[2 * i + 1] += (double)bf16hi(w[s][i]);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) red[r0][c8 + i] = acc[i];
-    __syncthreads();
-    if (tid < D) {
-        double s = 0.0;
-#pragma unroll
-        for (int r = 0; r < RPS; ++r) s += red[r][tid];
-        kt[((size_t)row * NC_cap + j) * D + tid] = f64_to_bf16(s / (double)n);
-    }
+    ktilde_window<D>(k, kt, row, j, t0, n, T_cap, NC_cap, threadIdx.x, red);
 }
 
 // Bulk path for overlapping windows (window > stride): a workgroup first sums

@@ -555,7 +555,9 @@ sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const 
                              int H_q, int H_kv, int d, float scale, float* out, float* lse_opt, int split_k,
                              const void* f_next, const void* k_tilde_next, const int32_t* seq_len_next,
                              int NB_cap_next, int n_init, int n_local, int top_k, int n_sel_max_next,
-                             int32_t* block_idx_next, int32_t* n_sel_next, void* ws, size_t ws_bytes, void* stream) {
+                             int32_t* block_idx_next, int32_t* n_sel_next, void* k_tilde_cur,
+                             const int32_t* len_old_cur, int max_new_tokens_cur, int NB_cap_cur, void* ws,
+                             size_t ws_bytes, void* stream) {
     TRY(check_attn_common(q, k, v, seq_len, block_idx, n_sel, n_sel_max, T_cap, B, 1, H_q, H_kv, d, scale, out,
                           split_k));
     REQUIRE(f_next, SDA_ERR_NULL, "decode_step: f_next is null");
@@ -564,6 +566,18 @@ sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const 
     REQUIRE(aligned16(f_next), SDA_ERR_ALIGN, "f_next must be 16-byte aligned");
     REQUIRE(block_idx_next != block_idx && n_sel_next != n_sel, SDA_ERR_SHAPE,
             "the next layer's block lists must not alias this layer's");
+    if (k_tilde_cur) {                                   // this layer's compressed keys, refreshed in the launch
+        REQUIRE(len_old_cur, SDA_ERR_NULL, "decode_step: len_old_cur is null");
+        REQUIRE(k_tilde_cur != k_tilde_next, SDA_ERR_SHAPE, "this layer's compressed keys alias the next layer's");
+        REQUIRE(NB_cap_cur >= ceil_div(T_cap, kBlock), SDA_ERR_SHAPE, "NB_cap_cur=%d < ceil(T_cap/64)=%d", NB_cap_cur,
+                ceil_div(T_cap, kBlock));
+        REQUIRE(max_new_tokens_cur >= 0, SDA_ERR_SHAPE, "max_new_tokens_cur=%d < 0", max_new_tokens_cur);
+        REQUIRE(aligned16(k_tilde_cur) && aligned4(len_old_cur), SDA_ERR_ALIGN,
+                "k_tilde_cur must be 16-byte and len_old_cur 4-byte aligned");
+    }
+    const bool refresh = k_tilde_cur && max_new_tokens_cur > 0;
+    // m new tokens touch at most floor((m + 62) / 64) + 1 blocks (one for a single token)
+    const int ref_blocks = refresh ? std::min((max_new_tokens_cur + kBlock - 2) / kBlock + 1, NB_cap_cur) : 0;
     const size_t need = sda_decode_step_workspace(B, H_q, H_kv, d, n_sel_max, split_k, NB_cap_next, top_k);
     REQUIRE(ws && ws_bytes >= need, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, need);
     REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -576,7 +590,10 @@ sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const 
     char* dws = static_cast<char*>(ws);
     char* sws = dws + pad256(dec);
     const size_t sws_bytes = ws_bytes - pad256(dec);
-    if (!fused) {                                        // the two calls, one after the other
+    if (!fused) {                                        // the calls one after the other
+        if (refresh)
+            TRY(sda_update_compressed_keys(k, k_tilde_cur, len_old_cur, seq_len, max_new_tokens_cur, B, H_kv, d, T_cap,
+                                           NB_cap_cur, stream));
         TRY(sda_score_select(f_next, k_tilde_next, seq_len_next, B, 1, H_kv, d, NB_cap_next, n_init, n_local, top_k,
                              n_sel_max_next, block_idx_next, n_sel_next, nullptr, sws, sws_bytes, stream));
         return sda_sparse_decode(q, k, v, seq_len, block_idx, n_sel, n_sel_max, nullptr, T_cap, B, 1, H_q, H_kv, d,
@@ -621,6 +638,10 @@ sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const 
                             n_sel_max_next, block_idx_next, n_sel_next};
     a.step.cpr = score_chunks(NB_cap_next);
     a.step.per_wg = min(plan.waves / 4, 2);
+    a.step.ref_kt = refresh ? static_cast<uint16_t*>(k_tilde_cur) : nullptr;
+    a.step.ref_len_old = len_old_cur;
+    a.step.ref_NB_cap = NB_cap_cur;
+    a.step.ref_blocks = ref_blocks;
     return hip_status(launch_attention(a, s), "decode_step launch");
 }
 

@@ -86,6 +86,13 @@ struct StepScore {
     SelectArgs sel;           // rows = B * H_kv
     int cpr;                  // chunks per row
     int per_wg;               // chunks per workgroup (groups of four waves)
+    // Optional: workgroups after the scoring ones refresh this layer's
+    // compressed keys for the tokens [ref_len_old, seq_len) (ref_kt null = off)
+    uint16_t* ref_kt;         // [B, H_kv, ref_NB_cap, D]
+    const int32_t* ref_len_old;
+    int ref_NB_cap;
+    int ref_blocks;           // blocks refreshed per row (grid bound)
+    int ref_rows;             // grid rows of refresh workgroups after the scoring ones (set at launch)
 };
 struct AttnArgs {
     const uint16_t* q;

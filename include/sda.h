@@ -286,6 +286,12 @@ sda_status_t sda_nsa_decode(const void* q, const void* k, const void* v, const v
  *   q .. split_k           as sda_sparse_decode (NQ = 1, no slot table)
  *   f_next .. n_sel_next   as sda_score_select for layer l+1 (NQ = 1);
  *                          block_idx_next / n_sel_next must not alias block_idx / n_sel
+ *   k_tilde_cur            NULL, or layer l's compressed keys bf16 [B, H_kv, NB_cap_cur, d]:
+ *                          the same launch refreshes the blocks touched by the tokens
+ *                          [len_old_cur[b], seq_len[b]) from k, exactly as
+ *                          sda_update_compressed_keys(k, k_tilde_cur, len_old_cur, seq_len,
+ *                          max_new_tokens_cur, ...) does ([SparDA] §4.2 step 1: the key just
+ *                          appended updates its block's mean); it must not alias k_tilde_next
  * Workspace: sda_decode_step_workspace() bytes, zero-filled before first use
  * (it holds arrival counters that every completed call leaves at zero).
  */
@@ -301,7 +307,8 @@ sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const 
                              int split_k, const void* f_next, const void* k_tilde_next,
                              const int32_t* seq_len_next, int NB_cap_next, int n_init, int n_local, int top_k,
                              int n_sel_max_next, int32_t* block_idx_next, int32_t* n_sel_next,
-                             void* ws, size_t ws_bytes, void* stream);
+                             void* k_tilde_cur, const int32_t* len_old_cur, int max_new_tokens_cur,
+                             int NB_cap_cur, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Offloaded-KV gather ([SparDA] §4.2 steps 3 and 6, §4.5): copy the K and V

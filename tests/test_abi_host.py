@@ -276,15 +276,26 @@ def test_decode_step_workspace_and_validation(L):
     assert L.sda_decode_step_is_fused(8, 64, 8, 96, 35, 0, 2048, 32) == 0        # unsupported head dim
     f = L.sda_decode_step
     base = [P, P, P, P, P, P, 35, 4096, 1, 8, 2, 64, 0.125, P, None, 0,
-            P, P, P, 64, 1, 2, 8, 11, P + 256, P + 512, P, 1 << 24, None]
+            P, P, P, 64, 1, 2, 8, 11, P + 256, P + 512, None, None, 1, 0, P, 1 << 24, None]
     bad = list(base); bad[16] = None                                     # f_next
     assert f(*bad) == NULL
     bad = list(base); bad[24] = P                                        # block_idx_next aliases block_idx
     assert f(*bad) == SHAPE
-    bad = list(base); bad[27] = 16                                       # workspace too small
+    bad = list(base); bad[31] = 16                                       # workspace too small
     assert f(*bad) == WS
     bad = list(base); bad[23] = 10                                       # n_sel_max_next < 1 + 2 + 8
     assert f(*bad) == SHAPE
+    # this layer's compressed-key refresh: k_tilde_cur, len_old_cur, max_new_tokens_cur, NB_cap_cur
+    bad = list(base); bad[26] = P + 1024; bad[29] = 64                   # no len_old_cur
+    assert f(*bad) == NULL
+    bad = list(base); bad[26] = P; bad[27] = P; bad[29] = 64             # aliases k_tilde_next
+    assert f(*bad) == SHAPE
+    bad = list(base); bad[26] = P + 1024; bad[27] = P; bad[29] = 63      # NB_cap_cur < ceil(T_cap / 64)
+    assert f(*bad) == SHAPE
+    bad = list(base); bad[26] = P + 1024; bad[27] = P; bad[28] = -1; bad[29] = 64
+    assert f(*bad) == SHAPE
+    bad = list(base); bad[26] = P + 1032; bad[27] = P; bad[29] = 64      # k_tilde_cur not 16-byte aligned
+    assert f(*bad) == ALIGN
 
 
 def test_python_binding_rejects_bad_tensors():

@@ -335,9 +335,16 @@ def test_decode_step_ragged(d, top_k, n_init, n_local, split_k):
     fused = sda.lib().sda_decode_step_is_fused(B, H_q, H_kv, d, nsm, split_k, NBn, top_k)
     _say(f"ragged step d={d} top_k={top_k} split_k={split_k}: one launch = {fused}")
     assert fused == 1
+    # this layer's compressed keys, pooled up to a shorter length: the step
+    # refreshes the blocks the remaining tokens touch (1 to 70 per sequence)
+    old0 = seq0 - torch.tensor([70, 1, 1], dtype=torch.int32, device=DEV)
+    kt0r = torch.zeros_like(kt0)
+    sda.sda_update_compressed_keys(K, kt0r, zero, old0, T_cap)
     for it in range(4):
-        out, lse, bi1, ns1 = sda.sda_decode_step(Q, K, V, seq0, bi0, ns0, F1, kt1, seq1, *sel, split_k=split_k)
+        out, lse, bi1, ns1 = sda.sda_decode_step(Q, K, V, seq0, bi0, ns0, F1, kt1, seq1, *sel, split_k=split_k,
+                                                 k_tilde_cur=kt0r, len_old_cur=old0, max_new_tokens_cur=70)
         torch.cuda.synchronize()
+        assert torch.equal(kt0r, kt0), it
         assert torch.equal(ns1, ref_ns1) and torch.equal(bi1, ref_bi1), it
         if split_k > 0:
             assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), it
