@@ -164,3 +164,47 @@ def test_nsa_gate_reductions_match_existing_calls():
     ones = torch.ones((B, NQ, H), dtype=torch.int32, device=DEV)
     ref_c, _ = sda.sda_sparse_decode(Q, kc, vc, torch.full((B,), nb, dtype=torch.int32, device=DEV), all_blocks, ones)
     assert (o_c - ref_c).abs().max().item() < 1e-5
+
+
+def test_nsa_c4_full_size_sampled_rows():
+    # the verification workload as the bench runs it (T = 64K, B 4, 16 draft
+    # queries in groups of 4, H_q 32, H_kv 8, a 512-token window, 64/64
+    # compressed keys and values, exact merge): every output of three
+    # sampled (batch, group, KV head) tasks against the oracle
+    cfg = synth.get_config(4)
+    C, n, window = cfg.group_C, cfg.top_k, 512
+    _say("nsa c4: draw K/V on the GPU")
+    K, V, _ = inputs.kv_layer(cfg, 0, device=DEV)
+    seq = torch.full((cfg.B,), cfg.T, dtype=torch.int32, device=DEV)
+    zero = torch.zeros(cfg.B, dtype=torch.int32, device=DEV)
+    kc = torch.zeros((cfg.B, cfg.H_kv, cfg.NB, cfg.d), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    sda.sda_update_compressed_keys(K, kc, zero, seq, cfg.T)
+    sda.sda_update_compressed_keys(V, vc, zero, seq, cfg.T)
+    rng = np.random.default_rng(44)
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0, sigma=0.5))
+    gates = torch.from_numpy(rng.uniform(0.0, 1.0, (cfg.B, cfg.NQ, cfg.H_q, 3)).astype(np.float32))
+    bi, ns = _lists(rng, cfg.B, cfg.NQ, cfg.H_kv, [cfg.T] * cfg.B, n, short_rows=False)
+    out, lse, uc = sda.sda_nsa_decode(Q.to(DEV), K, V, kc, vc, seq, torch.from_numpy(bi).to(DEV),
+                                      torch.from_numpy(ns).to(DEV), gates.to(DEV), 64, window, group_C=C)
+    torch.cuda.synchronize()
+    G = cfg.G
+    Qd = O.bf16_to_f64(bits(Q))
+    gd = gates.double().numpy()
+    out_h = out.double().cpu().numpy()
+    err = 0.0
+    for (b, grp, g) in [(0, 0, 0), (1, 2, 5), (3, 3, 7)]:
+        kk, vv = f64(K[b, g].cpu()), f64(V[b, g].cpu())
+        kcd = O.store_bf16(O.compressed_keys(kk, cfg.T))
+        vcd = O.store_bf16(O.compressed_keys(vv, cfg.T))
+        assert np.array_equal(kc[b, g].double().cpu().numpy(), kcd)
+        qs = list(range(grp * C, grp * C + C))
+        lists = [bi[b, q, g, :ns[b, q, g]] for q in qs]
+        assert int(uc[b, grp, g].item()) == len(O.union_blocks(lists))
+        hs = slice(g * G, (g + 1) * G)
+        for c, q in enumerate(qs):
+            o, _, _ = O.nsa_row(Qd[b, q, hs], kk, vv, kcd, vcd, lists[c], cfg.T, cfg.NB, window, gd[b, q, hs],
+                                1.0 / math.sqrt(cfg.d))
+            err = max(err, float(np.abs(out_h[b, q, hs] - o).max()))
+    _say("nsa c4: max |out - oracle|", err)
+    assert err <= TOL
