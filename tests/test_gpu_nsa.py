@@ -121,6 +121,7 @@ CASES = [
     (2, 8, 16, 4, 128, [8192, 6000], 16, 64, 64, 256, 4, 0),    # grouped, exact merge
     (2, 8, 16, 4, 128, [8192, 6000], 16, 32, 16, 200, 4, 1),    # grouped, shared representative
     (1, 6, 8, 2, 64, [2048], 8, 64, 64, 130, 4, 0),             # last group smaller
+    (3, 2, 8, 2, 64, [20, 1, 70], 2, 32, 16, 16, 2, 0),         # shorter than a block: one partial block
 ]
 
 

@@ -134,6 +134,8 @@ SELECT_CASES = [
     (2, 4, 128, [32768, 20000], 32, 16, 1, 2, 16),
     (2, 2, 128, [8192, 5000], 64, 32, 2, 1, 5),
     (1, 2, 64, [4096], 16, 8, 0, 0, 12),
+    (3, 2, 64, [20, 1, 70], 32, 16, 1, 2, 8),      # fewer blocks than the budget: every block
+    (1, 2, 64, [16384], 32, 16, 1, 2, 80),         # top_k past the in-launch selection's 64
 ]
 
 
