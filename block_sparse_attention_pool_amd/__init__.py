@@ -126,24 +126,60 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
-def _need(t, name, dtype, ndim=None, device=True):
+def _need(t, name, dtype, shape=None):
+    """Check a tensor argument: type, dtype, exact shape (None entries match
+    any size; an int for shape means only that many dims) and contiguity.
+    The C ABI cannot see buffer sizes, so every size the kernels index by is
+    checked here; placement is checked by _on_gpu / _on_host once all shapes
+    have passed."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if ndim is not None and t.dim() != ndim:
-        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if isinstance(shape, int):
+        if t.dim() != shape:
+            raise ValueError(f"{name} must have {shape} dims, got shape {tuple(t.shape)}")
+    elif shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(w) != n for w, n in zip(shape, t.shape)):
+            want = tuple("*" if w is None else int(w) for w in shape)
+            raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if device and not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _on_gpu(**tensors):
+    """Every given tensor (None skipped) lives on the current GPU."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.device.index != torch.cuda.current_device():
+            raise ValueError(f"{name} is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
+
+
+def _on_host(**tensors):
+    for name, t in tensors.items():
+        if t.is_cuda:
+            raise ValueError(f"{name} must be a host tensor")
+
+
+def _opt(t, name, dtype, shape):
+    if t is not None:
+        _need(t, name, dtype, shape)
 
 
 def _workspace(nbytes, device, ws=None):
-    """Caller's workspace, or a new zero-filled one (the split decode keeps
-    arrival counters in it that must start at zero)."""
+    """Caller's workspace (a contiguous tensor of at least nbytes bytes), or a
+    new zero-filled one (the split decode keeps arrival counters in it that
+    must start at zero)."""
     if ws is not None:
-        return ws, ws.numel() * ws.element_size()
+        if not isinstance(ws, torch.Tensor) or not ws.is_contiguous():
+            raise ValueError("ws must be a contiguous tensor")
+        have = ws.numel() * ws.element_size()
+        if have < nbytes:
+            raise ValueError(f"ws holds {have} bytes, {nbytes} needed")
+        return ws, have
     if nbytes == 0:
         return None, 0
     return torch.zeros(nbytes, dtype=torch.uint8, device=device), nbytes
@@ -180,39 +216,41 @@ def prepare(fn_py, *a, **kw):
 def sda_update_compressed_keys(k, k_tilde, len_old, len_new, max_new_tokens, stream=None):
     """Recompute the mean-pooled block keys touched by tokens [len_old, len_new)."""
     _need(k, "k", torch.bfloat16, 4)
-    _need(k_tilde, "k_tilde", torch.bfloat16, 4)
-    _need(len_old, "len_old", torch.int32, 1)
-    _need(len_new, "len_new", torch.int32, 1)
     B, H, T_cap, d = k.shape
-    if k_tilde.shape[:2] != (B, H) or k_tilde.shape[3] != d or len_old.numel() != B or len_new.numel() != B:
-        raise ValueError("shape mismatch between k, k_tilde and the length arrays")
+    _need(k_tilde, "k_tilde", torch.bfloat16, (B, H, None, d))
+    _need(len_old, "len_old", torch.int32, (B,))
+    _need(len_new, "len_new", torch.int32, (B,))
+    _on_gpu(k=k, k_tilde=k_tilde, len_old=len_old, len_new=len_new)
     _check(lib().sda_update_compressed_keys(_ptr(k), _ptr(k_tilde), _ptr(len_old), _ptr(len_new),
                                             int(max_new_tokens), B, H, d, T_cap, k_tilde.shape[2],
                                             _stream(stream)))
     return k_tilde
 
 
+def _select_outputs(B, NQ, H, n_sel_max, block_idx, n_sel, dev, suffix=""):
+    if block_idx is None:
+        block_idx = torch.empty((B, NQ, H, n_sel_max), dtype=torch.int32, device=dev)
+    if n_sel is None:
+        n_sel = torch.empty((B, NQ, H), dtype=torch.int32, device=dev)
+    _need(block_idx, "block_idx" + suffix, torch.int32, (B, NQ, H, n_sel_max))
+    _need(n_sel, "n_sel" + suffix, torch.int32, (B, NQ, H))
+    return block_idx, n_sel
+
+
 def sda_score_select(f, k_tilde, seq_len, n_init, n_local, top_k, n_sel_max=None, block_idx=None,
                      n_sel=None, scores=None, ws=None, stream=None, _prepare=False):
     """Indexer scores, exact top-k and block-set assembly; returns (block_idx, n_sel)."""
     _need(f, "f", torch.bfloat16, 4)
-    _need(k_tilde, "k_tilde", torch.bfloat16, 4)
-    _need(seq_len, "seq_len", torch.int32, 1)
     B, NQ, H, d = f.shape
+    _need(k_tilde, "k_tilde", torch.bfloat16, (B, H, None, d))
+    _need(seq_len, "seq_len", torch.int32, (B,))
     NB_cap = k_tilde.shape[2]
-    if k_tilde.shape[:2] != (B, H) or k_tilde.shape[3] != d:
-        raise ValueError("k_tilde must be [B, H_kv, NB_cap, d] matching f")
     if n_sel_max is None:
-        n_sel_max = n_init + n_local + top_k
-    if block_idx is None:
-        block_idx = torch.empty((B, NQ, H, n_sel_max), dtype=torch.int32, device=f.device)
-    if n_sel is None:
-        n_sel = torch.empty((B, NQ, H), dtype=torch.int32, device=f.device)
-    _need(block_idx, "block_idx", torch.int32, 4)
-    _need(n_sel, "n_sel", torch.int32, 3)
-    if scores is not None:
-        _need(scores, "scores", torch.float32, 4)
+        n_sel_max = block_idx.shape[-1] if block_idx is not None else n_init + n_local + top_k
+    block_idx, n_sel = _select_outputs(B, NQ, H, n_sel_max, block_idx, n_sel, f.device)
+    _opt(scores, "scores", torch.float32, (B, NQ, H, NB_cap))
     ws, wsb = _workspace(lib().sda_score_select_workspace(B, NQ, H, NB_cap, top_k), f.device, ws)
+    _on_gpu(f=f, k_tilde=k_tilde, seq_len=seq_len, block_idx=block_idx, n_sel=n_sel, scores=scores, ws=ws)
     args = (_ptr(f), _ptr(k_tilde), _ptr(seq_len), B, NQ, H, d, NB_cap, n_init, n_local,
             top_k, n_sel_max, _ptr(block_idx), _ptr(n_sel), _ptr(scores), _ptr(ws), wsb, None)
     if _prepare:
@@ -227,12 +265,11 @@ def sda_update_compressed_keys_strided(k, k_tilde, len_old, len_new, max_new_tok
     """Recompute the overlapping compressed keys (kernel `window`, stride
     `stride`) touched by tokens [len_old, len_new); k_tilde is [B, H_kv, NC_cap, d]."""
     _need(k, "k", torch.bfloat16, 4)
-    _need(k_tilde, "k_tilde", torch.bfloat16, 4)
-    _need(len_old, "len_old", torch.int32, 1)
-    _need(len_new, "len_new", torch.int32, 1)
     B, H, T_cap, d = k.shape
-    if k_tilde.shape[:2] != (B, H) or k_tilde.shape[3] != d or len_old.numel() != B or len_new.numel() != B:
-        raise ValueError("shape mismatch between k, k_tilde and the length arrays")
+    _need(k_tilde, "k_tilde", torch.bfloat16, (B, H, None, d))
+    _need(len_old, "len_old", torch.int32, (B,))
+    _need(len_new, "len_new", torch.int32, (B,))
+    _on_gpu(k=k, k_tilde=k_tilde, len_old=len_old, len_new=len_new)
     _check(lib().sda_update_compressed_keys_strided(_ptr(k), _ptr(k_tilde), _ptr(len_old), _ptr(len_new),
                                                     int(max_new_tokens), B, H, d, T_cap, k_tilde.shape[2],
                                                     int(window), int(stride), _stream(stream)))
@@ -245,24 +282,17 @@ def sda_score_select_pooled(f, k_tilde, seq_len, window, stride, n_init, n_local
     64-token blocks, then top-k and block sets; returns (block_idx, n_sel).
     scores (optional) is [B, NQ, H_kv, ceil(NC_cap * stride / 64)] float32."""
     _need(f, "f", torch.bfloat16, 4)
-    _need(k_tilde, "k_tilde", torch.bfloat16, 4)
-    _need(seq_len, "seq_len", torch.int32, 1)
     B, NQ, H, d = f.shape
+    _need(k_tilde, "k_tilde", torch.bfloat16, (B, H, None, d))
+    _need(seq_len, "seq_len", torch.int32, (B,))
     NC_cap = k_tilde.shape[2]
-    if k_tilde.shape[:2] != (B, H) or k_tilde.shape[3] != d:
-        raise ValueError("k_tilde must be [B, H_kv, NC_cap, d] matching f")
     if n_sel_max is None:
-        n_sel_max = n_init + n_local + top_k
-    if block_idx is None:
-        block_idx = torch.empty((B, NQ, H, n_sel_max), dtype=torch.int32, device=f.device)
-    if n_sel is None:
-        n_sel = torch.empty((B, NQ, H), dtype=torch.int32, device=f.device)
-    _need(block_idx, "block_idx", torch.int32, 4)
-    _need(n_sel, "n_sel", torch.int32, 3)
-    if scores is not None:
-        _need(scores, "scores", torch.float32, 4)
+        n_sel_max = block_idx.shape[-1] if block_idx is not None else n_init + n_local + top_k
+    block_idx, n_sel = _select_outputs(B, NQ, H, n_sel_max, block_idx, n_sel, f.device)
+    _opt(scores, "scores", torch.float32, (B, NQ, H, -(-NC_cap * int(stride) // BLOCK)))
     nbytes = lib().sda_score_select_pooled_workspace(B, NQ, H, NC_cap, int(stride), top_k)
     ws, wsb = _workspace(nbytes, f.device, ws)
+    _on_gpu(f=f, k_tilde=k_tilde, seq_len=seq_len, block_idx=block_idx, n_sel=n_sel, scores=scores, ws=ws)
     _check(lib().sda_score_select_pooled(_ptr(f), _ptr(k_tilde), _ptr(seq_len), B, NQ, H, d, NC_cap, int(window),
                                          int(stride), n_init, n_local, top_k, n_sel_max, _ptr(block_idx),
                                          _ptr(n_sel), _ptr(scores), _ptr(ws), wsb, _stream(stream)))
@@ -273,51 +303,60 @@ def sda_score_select_multihead(q, k_tilde, seq_len, n_init, n_local, top_k, tau,
                                block_idx=None, n_sel=None, scores=None, ws=None, stream=None):
     """G-head softmax-sum selector (comparator); returns (block_idx, n_sel)."""
     _need(q, "q", torch.bfloat16, 4)
-    _need(k_tilde, "k_tilde", torch.bfloat16, 4)
-    _need(seq_len, "seq_len", torch.int32, 1)
     B, NQ, H_q, d = q.shape
-    H = k_tilde.shape[1] if H_kv is None else H_kv
+    _need(k_tilde, "k_tilde", torch.bfloat16, (B, H_kv, None, d))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    H = k_tilde.shape[1]
     NB_cap = k_tilde.shape[2]
     if n_sel_max is None:
-        n_sel_max = n_init + n_local + top_k
-    if block_idx is None:
-        block_idx = torch.empty((B, NQ, H, n_sel_max), dtype=torch.int32, device=q.device)
-    if n_sel is None:
-        n_sel = torch.empty((B, NQ, H), dtype=torch.int32, device=q.device)
-    if scores is not None:
-        _need(scores, "scores", torch.float32, 4)
+        n_sel_max = block_idx.shape[-1] if block_idx is not None else n_init + n_local + top_k
+    block_idx, n_sel = _select_outputs(B, NQ, H, n_sel_max, block_idx, n_sel, q.device)
+    _opt(scores, "scores", torch.float32, (B, NQ, H, NB_cap))
     nbytes = lib().sda_score_select_multihead_workspace(B, NQ, H_q, H, NB_cap, top_k)
     ws, wsb = _workspace(nbytes, q.device, ws)
+    _on_gpu(q=q, k_tilde=k_tilde, seq_len=seq_len, block_idx=block_idx, n_sel=n_sel, scores=scores, ws=ws)
     _check(lib().sda_score_select_multihead(_ptr(q), _ptr(k_tilde), _ptr(seq_len), B, NQ, H_q, H, d, NB_cap,
                                             n_init, n_local, top_k, n_sel_max, float(tau), _ptr(block_idx),
                                             _ptr(n_sel), _ptr(scores), _ptr(ws), wsb, _stream(stream)))
     return block_idx, n_sel
 
 
+def _attn_inputs(q, k, v, seq_len, block_idx, n_sel, NQ_lists=None):
+    """Checks shared by the decode calls; returns (B, NQ, H_q, d, H_kv, T_cap, n_sel_max)."""
+    _need(q, "q", torch.bfloat16, 4)
+    B, NQ, H_q, d = q.shape
+    _need(k, "k", torch.bfloat16, (B, None, None, d))
+    H_kv, T_cap = k.shape[1], k.shape[2]
+    _need(v, "v", torch.bfloat16, tuple(k.shape))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    _need(block_idx, "block_idx", torch.int32, (B, NQ if NQ_lists is None else NQ_lists, H_kv, None))
+    _need(n_sel, "n_sel", torch.int32, (B, NQ if NQ_lists is None else NQ_lists, H_kv))
+    if H_q % H_kv:
+        raise ValueError(f"H_q={H_q} is not a multiple of H_kv={H_kv}")
+    return B, NQ, H_q, d, H_kv, T_cap, block_idx.shape[3]
+
+
+def _attn_outputs(B, NQ, H_q, d, out, lse, dev, lse_tail=()):
+    if out is None:
+        out = torch.empty((B, NQ, H_q, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, NQ, H_q) + lse_tail, dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, NQ, H_q, d))
+    _need(lse, "lse", torch.float32, (B, NQ, H_q) + lse_tail)
+    return out, lse
+
+
 def sda_sparse_decode(q, k, v, seq_len, block_idx, n_sel, scale=None, out=None, lse=None, slot=None,
                       split_k=0, ws=None, stream=None, _prepare=False):
     """Block-sparse decode attention; returns (out, lse)."""
-    _need(q, "q", torch.bfloat16, 4)
-    _need(k, "k", torch.bfloat16, 4)
-    _need(v, "v", torch.bfloat16, 4)
-    _need(seq_len, "seq_len", torch.int32, 1)
-    _need(block_idx, "block_idx", torch.int32, 4)
-    _need(n_sel, "n_sel", torch.int32, 3)
-    B, NQ, H_q, d = q.shape
-    H_kv, T_cap = k.shape[1], k.shape[2]
-    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
-        raise ValueError("k and v must both be [B, H_kv, T_cap, d] matching q")
-    n_sel_max = block_idx.shape[3]
-    if slot is not None:
-        _need(slot, "slot", torch.int32, 4)
+    B, NQ, H_q, d, H_kv, T_cap, n_sel_max = _attn_inputs(q, k, v, seq_len, block_idx, n_sel)
+    _opt(slot, "slot", torch.int32, tuple(block_idx.shape))
     if scale is None:
         scale = d ** -0.5
-    if out is None:
-        out = torch.empty((B, NQ, H_q, d), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, NQ, H_q), dtype=torch.float32, device=q.device)
+    out, lse = _attn_outputs(B, NQ, H_q, d, out, lse, q.device)
     nbytes = lib().sda_sparse_decode_workspace(B, NQ, H_q, H_kv, n_sel_max, d, int(split_k))
     ws, wsb = _workspace(nbytes, q.device, ws)
+    _on_gpu(q=q, k=k, v=v, seq_len=seq_len, block_idx=block_idx, n_sel=n_sel, slot=slot, out=out, lse=lse, ws=ws)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(block_idx), _ptr(n_sel),
             n_sel_max, _ptr(slot), T_cap, B, NQ, H_q, H_kv, d, float(scale), _ptr(out),
             _ptr(lse), int(split_k), _ptr(ws), wsb, None)
@@ -336,47 +375,31 @@ def sda_decode_step(q, k, v, seq_len, block_idx, n_sel, f_next, k_tilde_next, se
     sda_score_select for l+1 then sda_sparse_decode for l) and, with
     k_tilde_cur, the refresh of layer l's compressed keys for the tokens
     [len_old_cur, seq_len); returns (out, lse, block_idx_next, n_sel_next)."""
-    _need(q, "q", torch.bfloat16, 4)
-    _need(k, "k", torch.bfloat16, 4)
-    _need(v, "v", torch.bfloat16, 4)
-    _need(seq_len, "seq_len", torch.int32, 1)
-    _need(block_idx, "block_idx", torch.int32, 4)
-    _need(n_sel, "n_sel", torch.int32, 3)
-    _need(f_next, "f_next", torch.bfloat16, 4)
-    _need(k_tilde_next, "k_tilde_next", torch.bfloat16, 4)
-    _need(seq_len_next, "seq_len_next", torch.int32, 1)
-    B, NQ, H_q, d = q.shape
+    B, NQ, H_q, d, H_kv, T_cap, n_sel_max = _attn_inputs(q, k, v, seq_len, block_idx, n_sel)
     if NQ != 1:
         raise ValueError("sda_decode_step takes one query per sequence")
-    H_kv, T_cap = k.shape[1], k.shape[2]
-    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
-        raise ValueError("k and v must both be [B, H_kv, T_cap, d] matching q")
-    if f_next.shape != (B, 1, H_kv, d) or k_tilde_next.shape[:2] != (B, H_kv) or k_tilde_next.shape[3] != d:
-        raise ValueError("f_next [B, 1, H_kv, d] and k_tilde_next [B, H_kv, NB_cap, d] must match q and k")
-    n_sel_max = block_idx.shape[3]
+    _need(f_next, "f_next", torch.bfloat16, (B, 1, H_kv, d))
+    _need(k_tilde_next, "k_tilde_next", torch.bfloat16, (B, H_kv, None, d))
+    _need(seq_len_next, "seq_len_next", torch.int32, (B,))
     NB_cap_next = k_tilde_next.shape[2]
     if n_sel_max_next is None:
-        n_sel_max_next = n_init + n_local + top_k
+        n_sel_max_next = block_idx_next.shape[-1] if block_idx_next is not None else n_init + n_local + top_k
     if scale is None:
         scale = d ** -0.5
     dev = q.device
-    if out is None:
-        out = torch.empty((B, 1, H_q, d), dtype=torch.float32, device=dev)
-    if lse is None:
-        lse = torch.empty((B, 1, H_q), dtype=torch.float32, device=dev)
-    if block_idx_next is None:
-        block_idx_next = torch.empty((B, 1, H_kv, n_sel_max_next), dtype=torch.int32, device=dev)
-    if n_sel_next is None:
-        n_sel_next = torch.empty((B, 1, H_kv), dtype=torch.int32, device=dev)
+    out, lse = _attn_outputs(B, 1, H_q, d, out, lse, dev)
+    block_idx_next, n_sel_next = _select_outputs(B, 1, H_kv, n_sel_max_next, block_idx_next, n_sel_next, dev,
+                                                  "_next")
     NB_cap_cur = 0
     if k_tilde_cur is not None:
-        _need(k_tilde_cur, "k_tilde_cur", torch.bfloat16, 4)
-        _need(len_old_cur, "len_old_cur", torch.int32, 1)
-        if k_tilde_cur.shape[:2] != (B, H_kv) or k_tilde_cur.shape[3] != d or len_old_cur.numel() != B:
-            raise ValueError("k_tilde_cur [B, H_kv, NB_cap, d] and len_old_cur [B] must match k")
+        _need(k_tilde_cur, "k_tilde_cur", torch.bfloat16, (B, H_kv, None, d))
+        _need(len_old_cur, "len_old_cur", torch.int32, (B,))
         NB_cap_cur = k_tilde_cur.shape[2]
     nbytes = lib().sda_decode_step_workspace(B, H_q, H_kv, d, n_sel_max, int(split_k), NB_cap_next, top_k)
     ws, wsb = _workspace(nbytes, dev, ws)
+    _on_gpu(q=q, k=k, v=v, seq_len=seq_len, block_idx=block_idx, n_sel=n_sel, f_next=f_next,
+            k_tilde_next=k_tilde_next, seq_len_next=seq_len_next, out=out, lse=lse, block_idx_next=block_idx_next,
+            n_sel_next=n_sel_next, k_tilde_cur=k_tilde_cur, len_old_cur=len_old_cur, ws=ws)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(block_idx), _ptr(n_sel), n_sel_max, T_cap, B, H_q,
             H_kv, d, float(scale), _ptr(out), _ptr(lse), int(split_k), _ptr(f_next), _ptr(k_tilde_next),
             _ptr(seq_len_next), NB_cap_next, n_init, n_local, top_k, n_sel_max_next, _ptr(block_idx_next),
@@ -393,31 +416,23 @@ def sda_decode_step(q, k, v, seq_len, block_idx, n_sel, f_next, k_tilde_next, se
 def sda_grouped_decode(q, k, v, seq_len, block_idx, n_sel, group_C, mode=SDA_GROUP_EXACT, scale=None,
                        NB_cap=None, out=None, lse=None, union_count=None, split_k=0, ws=None, stream=None):
     """SSV grouped verification decode; returns (out, lse, union_count)."""
-    _need(q, "q", torch.bfloat16, 4)
-    _need(k, "k", torch.bfloat16, 4)
-    _need(v, "v", torch.bfloat16, 4)
-    _need(seq_len, "seq_len", torch.int32, 1)
-    _need(block_idx, "block_idx", torch.int32, 4)
-    _need(n_sel, "n_sel", torch.int32, 3)
-    B, NQ, H_q, d = q.shape
-    H_kv, T_cap = k.shape[1], k.shape[2]
-    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
-        raise ValueError("k and v must both be [B, H_kv, T_cap, d] matching q")
-    n_sel_max = block_idx.shape[3]
+    B, NQ, H_q, d, H_kv, T_cap, n_sel_max = _attn_inputs(q, k, v, seq_len, block_idx, n_sel)
     if NB_cap is None:
         NB_cap = -(-T_cap // BLOCK)
     if scale is None:
         scale = d ** -0.5
-    n_groups = -(-NQ // group_C)
-    if out is None:
-        out = torch.empty((B, NQ, H_q, d), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, NQ, H_q), dtype=torch.float32, device=q.device)
+    if int(group_C) < 1:
+        raise ValueError("group_C must be >= 1")
+    n_groups = -(-NQ // int(group_C))
+    out, lse = _attn_outputs(B, NQ, H_q, d, out, lse, q.device)
     if union_count is None:
         union_count = torch.empty((B, n_groups, H_kv), dtype=torch.int32, device=q.device)
+    _need(union_count, "union_count", torch.int32, (B, n_groups, H_kv))
     nbytes = lib().sda_grouped_decode_workspace(B, NQ, H_q, H_kv, n_sel_max, d, int(NB_cap), int(group_C),
                                                 int(mode), int(split_k))
     ws, wsb = _workspace(nbytes, q.device, ws)
+    _on_gpu(q=q, k=k, v=v, seq_len=seq_len, block_idx=block_idx, n_sel=n_sel, out=out, lse=lse,
+            union_count=union_count, ws=ws)
     _check(lib().sda_grouped_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(block_idx), _ptr(n_sel),
                                     n_sel_max, T_cap, int(NB_cap), B, NQ, H_q, H_kv, d, float(scale),
                                     int(group_C), int(mode), _ptr(out), _ptr(lse), _ptr(union_count),
@@ -429,34 +444,24 @@ def sda_nsa_decode(q, k, v, k_cmp, v_cmp, seq_len, block_idx, n_sel, gates, cmp_
                    mode=SDA_GROUP_EXACT, scale=None, out=None, lse=None, union_count=None, ws=None, stream=None):
     """NSA verification output (compressed, selected-block and window branches,
     gated sum) in one launch; returns (out, lse [B, NQ, H_q, 3], union_count)."""
-    _need(q, "q", torch.bfloat16, 4)
-    _need(k, "k", torch.bfloat16, 4)
-    _need(v, "v", torch.bfloat16, 4)
-    _need(k_cmp, "k_cmp", torch.bfloat16, 4)
-    _need(v_cmp, "v_cmp", torch.bfloat16, 4)
-    _need(seq_len, "seq_len", torch.int32, 1)
-    _need(block_idx, "block_idx", torch.int32, 4)
-    _need(n_sel, "n_sel", torch.int32, 3)
-    _need(gates, "gates", torch.float32, 4)
-    B, NQ, H_q, d = q.shape
-    _, H, T_cap, _ = k.shape
+    B, NQ, H_q, d, H, T_cap, n_sel_max = _attn_inputs(q, k, v, seq_len, block_idx, n_sel)
+    _need(k_cmp, "k_cmp", torch.bfloat16, (B, H, None, d))
+    _need(v_cmp, "v_cmp", torch.bfloat16, tuple(k_cmp.shape))
+    _need(gates, "gates", torch.float32, (B, NQ, H_q, 3))
     NC_cap = k_cmp.shape[2]
-    if v.shape != k.shape or v_cmp.shape != k_cmp.shape or k_cmp.shape[:2] != (B, H):
-        raise ValueError("k/v and k_cmp/v_cmp must be [B, H_kv, *, d] pairs")
-    if tuple(gates.shape) != (B, NQ, H_q, 3):
-        raise ValueError("gates must be [B, NQ, H_q, 3]")
-    n_sel_max = block_idx.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    if out is None:
-        out = torch.empty((B, NQ, H_q, d), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, NQ, H_q, 3), dtype=torch.float32, device=q.device)
-    n_groups = -(-NQ // group_C)
+    if int(group_C) < 1:
+        raise ValueError("group_C must be >= 1")
+    out, lse = _attn_outputs(B, NQ, H_q, d, out, lse, q.device, lse_tail=(3,))
+    n_groups = -(-NQ // int(group_C))
     if union_count is None and group_C > 1:
         union_count = torch.empty((B, n_groups, H), dtype=torch.int32, device=q.device)
+    _opt(union_count, "union_count", torch.int32, (B, n_groups, H))
     nbytes = lib().sda_nsa_decode_workspace(B, NQ, H_q, H, n_sel_max, d, T_cap, NC_cap, int(window), int(group_C),
                                             int(mode))
     ws, wsb = _workspace(nbytes, q.device, ws)
+    _on_gpu(q=q, k=k, v=v, k_cmp=k_cmp, v_cmp=v_cmp, seq_len=seq_len, block_idx=block_idx, n_sel=n_sel,
+            gates=gates, out=out, lse=lse, union_count=union_count, ws=ws)
     _check(lib().sda_nsa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cmp), _ptr(v_cmp), _ptr(seq_len), _ptr(block_idx),
                                 _ptr(n_sel), n_sel_max, T_cap, NC_cap, int(cmp_stride), int(window), _ptr(gates), B,
                                 NQ, H_q, H, d, float(scale), int(group_C), int(mode), _ptr(out), _ptr(lse),
@@ -470,14 +475,16 @@ def sda_gather_blocks(k_host, v_host, block_idx, n_sel, k_stage=None, v_stage=No
 
     k_host, v_host: pinned CPU bf16 [B, H_kv, T_cap, d]; block_idx [B, 1, H_kv, n_sel_max]
     or [B, H_kv, n_sel_max]; returns (k_stage, v_stage, slot) with slot shaped like block_idx."""
-    _need(k_host, "k_host", torch.bfloat16, 4, device=False)
-    _need(v_host, "v_host", torch.bfloat16, 4, device=False)
-    if not (k_host.is_pinned() and v_host.is_pinned()):
-        raise ValueError("k_host and v_host must be pinned host memory")
+    _need(k_host, "k_host", torch.bfloat16, 4)
     B, H_kv, T_cap, d = k_host.shape
+    _need(v_host, "v_host", torch.bfloat16, tuple(k_host.shape))
+    if block_idx.dim() == 4:
+        _need(block_idx, "block_idx", torch.int32, (B, 1, H_kv, None))
+        _need(n_sel, "n_sel", torch.int32, (B, 1, H_kv))
+    else:
+        _need(block_idx, "block_idx", torch.int32, (B, H_kv, None))
+        _need(n_sel, "n_sel", torch.int32, (B, H_kv))
     n_sel_max = block_idx.shape[-1]
-    if block_idx.numel() != B * H_kv * n_sel_max or n_sel.numel() != B * H_kv:
-        raise ValueError("block_idx / n_sel must hold one row per (batch, KV head)")
     dev = block_idx.device
     if k_stage is None:
         k_stage = torch.empty((B, H_kv, n_sel_max * BLOCK, d), dtype=torch.bfloat16, device=dev)
@@ -485,6 +492,13 @@ def sda_gather_blocks(k_host, v_host, block_idx, n_sel, k_stage=None, v_stage=No
         v_stage = torch.empty((B, H_kv, n_sel_max * BLOCK, d), dtype=torch.bfloat16, device=dev)
     if slot is None:
         slot = torch.empty(block_idx.shape, dtype=torch.int32, device=dev)
+    _need(k_stage, "k_stage", torch.bfloat16, (B, H_kv, n_sel_max * BLOCK, d))
+    _need(v_stage, "v_stage", torch.bfloat16, (B, H_kv, n_sel_max * BLOCK, d))
+    _need(slot, "slot", torch.int32, tuple(block_idx.shape))
+    _on_host(k_host=k_host, v_host=v_host)
+    if not (k_host.is_pinned() and v_host.is_pinned()):
+        raise ValueError("k_host and v_host must be pinned host memory")
+    _on_gpu(block_idx=block_idx, n_sel=n_sel, k_stage=k_stage, v_stage=v_stage, slot=slot)
     _check(lib().sda_gather_blocks(_ptr(k_host), _ptr(v_host), _ptr(block_idx), _ptr(n_sel), n_sel_max, B,
                                    H_kv, d, T_cap, _ptr(k_stage), _ptr(v_stage), _ptr(slot),
                                    int(max_workgroups), _stream(stream)))

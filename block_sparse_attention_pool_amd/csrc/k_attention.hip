@@ -31,7 +31,6 @@
 // HBM-bound: 64*d*2*2 bytes per block and row group; fp32 accumulate.
 #include <limits.h>
 #include <math.h>
-#include <stdlib.h>
 
 #include "sda_device.hpp"
 #include "sda_internal.h"
@@ -150,17 +149,13 @@ __device__ __forceinline__ void lds_dma16(const void* g, SDA_LDS void* l) {
 
 // Merge the n_split partials (m, l, o) of one output row by log-sum-exp: one
 // wave, lane owns columns lane + 64 i.  Partials are read in batches of
-// kCombineMax with every load of a batch in flight at once.  `coherent`
-// reads with agent-scope atomic loads (partials written moments ago by
-// workgroups on other XCDs); the merge launch reads plainly.  Both paths do
-// the same arithmetic in the same order, so they agree bit for bit.
+// kCombineMax with every load of a batch in flight at once, as agent-scope
+// atomic loads (written moments ago by workgroups on other XCDs).
 constexpr int kCombineMax = 8;
-template <int D, bool coherent>
 __device__ __forceinline__ float ld_part(const float* p) {
-    if constexpr (coherent) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else return *p;
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-template <int D, int RP, bool coherent>
+template <int D, int RP>
 __device__ __forceinline__ void merge_splits(const AttnArgs& a, int task, int r, int lane, int s_begin, int s_end,
                                              float& M, float& Ls, float (&Os)[D / kWave]) {
     constexpr int PER = D / kWave;
@@ -176,10 +171,10 @@ __device__ __forceinline__ void merge_splits(const AttnArgs& a, int task, int r,
         for (int k = 0; k < kCombineMax; ++k) {
             const int s2 = s0 + k;
             const bool ok = s2 < s_end;
-            mv[k] = ok ? ld_part<D, coherent>(ml + (size_t)s2 * RP * 2) : -INFINITY;
-            lv[k] = ok ? ld_part<D, coherent>(ml + (size_t)s2 * RP * 2 + 1) : 0.f;
+            mv[k] = ok ? ld_part(ml + (size_t)s2 * RP * 2) : -INFINITY;
+            lv[k] = ok ? ld_part(ml + (size_t)s2 * RP * 2 + 1) : 0.f;
 #pragma unroll
-            for (int i = 0; i < PER; ++i) ov[k][i] = ok ? ld_part<D, coherent>(po + (size_t)s2 * RP * D + i * kWave) : 0.f;
+            for (int i = 0; i < PER; ++i) ov[k][i] = ok ? ld_part(po + (size_t)s2 * RP * D + i * kWave) : 0.f;
         }
         float Mn = M;
 #pragma unroll
@@ -200,11 +195,11 @@ __device__ __forceinline__ void merge_splits(const AttnArgs& a, int task, int r,
     }
 }
 
-template <int D, int RP, bool coherent>
+template <int D, int RP>
 __device__ __forceinline__ void merge_row(const AttnArgs& a, int task, int r, size_t oi, int lane) {
     constexpr int PER = D / kWave;
     float M, Ls, Os[PER];
-    merge_splits<D, RP, coherent>(a, task, r, lane, 0, a.n_split, M, Ls, Os);
+    merge_splits<D, RP>(a, task, r, lane, 0, a.n_split, M, Ls, Os);
 #pragma unroll
     for (int i = 0; i < PER; ++i) a.out[oi * D + lane + i * kWave] = (Ls > 0.f) ? Os[i] / Ls : 0.f;
     if (lane == 0 && a.lse) a.lse[oi] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
@@ -223,7 +218,7 @@ __device__ __forceinline__ void merge_row_nsa(const AttnArgs& a, int task, int r
 #pragma unroll
     for (int bi = 0; bi < 3; ++bi) {
         float M, Ls, Os[PER];
-        merge_splits<D, RP, true>(a, task, r, lane, bounds[bi], bounds[bi + 1], M, Ls, Os);
+        merge_splits<D, RP>(a, task, r, lane, bounds[bi], bounds[bi + 1], M, Ls, Os);
         const float w = (Ls > 0.f) ? a.gates[oi * 3 + bi] / Ls : 0.f;
 #pragma unroll
         for (int i = 0; i < PER; ++i) acc[i] += Os[i] * w;
@@ -323,11 +318,12 @@ __device__ __forceinline__ void step_finish(const AttnArgs& a, const StepPos& p,
     uint64_t* fA = reinterpret_cast<uint64_t*>(sl + (size_t)st.per_wg * step_group_lds_bytes(K));
     uint64_t* fB = fA + (size_t)P * st.cpr;
     int* last = reinterpret_cast<int*>(fB + (size_t)P * ((st.cpr + 1) / 2));
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // this workgroup's lists have landed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // this wave's list stores have completed
     __syncthreads();
-    if (p.t == 0 && p.grp < st.per_wg)
-        last[p.grp] = p.has && __hip_atomic_fetch_add(st.counters + p.row, 1, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT) == st.cpr - 1;
+    if (p.t == 0 && p.grp < st.per_wg) {
+        last[p.grp] = p.has && arrive(st.counters + p.row) == st.cpr - 1;
+        if (last[p.grp]) acquire_agent();
+    }
     __syncthreads();
     for (int g2 = 0; g2 < st.per_wg; ++g2) {
         if (!last[g2]) continue;                            // uniform: one LDS flag
@@ -702,44 +698,38 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
             if (d4 == 0 && a.lse) a.lse[oi] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
         } else {
             const size_t pi = ((size_t)task * a.n_split + split) * RP + r;
-            if (a.fused_combine) {        // write-through stores: the merging workgroup may sit on another XCD
-                uint64_t* po = reinterpret_cast<uint64_t*>(&a.part_o[pi * D + d4]);
-                __hip_atomic_store(po, ((uint64_t)__float_as_uint(Os[1]) << 32) | __float_as_uint(Os[0]),
+            // agent-scope stores: the merging workgroup may sit on another XCD
+            uint64_t* po = reinterpret_cast<uint64_t*>(&a.part_o[pi * D + d4]);
+            __hip_atomic_store(po, ((uint64_t)__float_as_uint(Os[1]) << 32) | __float_as_uint(Os[0]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(po + 1, ((uint64_t)__float_as_uint(Os[3]) << 32) | __float_as_uint(Os[2]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d4 == 0)
+                __hip_atomic_store(reinterpret_cast<uint64_t*>(&a.part_ml[pi * 2]),
+                                   ((uint64_t)__float_as_uint(Ls) << 32) | __float_as_uint(M),
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(po + 1, ((uint64_t)__float_as_uint(Os[3]) << 32) | __float_as_uint(Os[2]),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (d4 == 0)
-                    __hip_atomic_store(reinterpret_cast<uint64_t*>(&a.part_ml[pi * 2]),
-                                       ((uint64_t)__float_as_uint(Ls) << 32) | __float_as_uint(M),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            } else {
-                *reinterpret_cast<floatx4*>(&a.part_o[pi * D + d4]) = Os;
-                if (d4 == 0) {
-                    a.part_ml[pi * 2] = M;
-                    a.part_ml[pi * 2 + 1] = Ls;
-                }
-            }
         }
     }
-    if (final_out || !a.fused_combine) return;
+    if (final_out) return;
 
     // ---- the last workgroup of this row group merges the splits ----------------------
-    // This workgroup's partial stores are written through to the coherent level;
-    // once they have completed (vmcnt), one agent-scope counter increment per
-    // workgroup tells the last arrival that every split is readable.
+    // Every wave waits for its partial stores to complete; after a barrier one
+    // agent-scope increment per workgroup tells the last arrival, which then
+    // acquires, that every split is readable (arrive()).
     int* last = reinterpret_cast<int*>(smem);           // the merge area is free again
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (threadIdx.x == 0)
-        *last = __hip_atomic_fetch_add(&a.counters[task], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                a.n_split - 1;
+    if (threadIdx.x == 0) {
+        *last = arrive(&a.counters[task]) == a.n_split - 1;
+        if (*last) acquire_agent();
+    }
     __syncthreads();
     if (!*last) return;
     for (int r = wave; r < R; r += W) {
         const int c = r / G, h = r - (r / G) * G;
         const size_t oi = ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h;
         if constexpr (NSA) merge_row_nsa<D, RP>(a, task, r, oi, lane);
-        else merge_row<D, RP, true>(a, task, r, oi, lane);
+        else merge_row<D, RP>(a, task, r, oi, lane);
     }
     if (threadIdx.x == 0) __hip_atomic_store(&a.counters[task], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -887,27 +877,6 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
             L.gidx ? min(max(ld_ro(L.gn), 0), a.n_sel_max) : L.n;
 }
 
-// Split merge as its own launch: one wave per (row group, row).
-template <int D, int RP>
-__global__ __launch_bounds__(64) void combine_kernel(AttnArgs a) {
-    const int task = blockIdx.x;
-    const int r = blockIdx.y;
-    const int g = task % a.H_kv;
-    const int t2 = task / a.H_kv;
-    const int grp = t2 % a.n_groups;
-    const int b = t2 / a.n_groups;
-    const int q0 = grp * a.C;
-    const int Cg = min(a.C, a.NQ - q0);
-    if (r >= Cg * a.G) return;
-    const int c = r / a.G, h = r - (r / a.G) * a.G;
-    merge_row<D, RP, false>(a, task, r, ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * a.G + h, threadIdx.x);
-}
-
-int env_int(const char* name, int dflt) {
-    const char* v = getenv(name);
-    return v ? atoi(v) : dflt;
-}
-
 int attn_rows_pad(int C, int G) { return (C * G <= 16) ? 16 : 32; }
 
 constexpr size_t kLdsPerCU = 160 * 1024;
@@ -933,14 +902,12 @@ AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode
             --W;                                           // fewer waves (each walks more blocks) to fit the LDS
         return AttnPlan{W, split_k};
     }
-    static const int force_w = env_int("SDA_ATTN_WAVES", 0);
     AttnPlan best{1, 1};
     long long best_cost = -1, best_flight = -1, best_cus = -1;
     const long long total = (long long)tasks * list_max;
     for (int ns = 1; ns <= list_max; ++ns) {
         const int per_split = (list_max + ns - 1) / ns;
         for (int W = 1; W <= min(max_w, per_split); ++W) {
-            if (force_w && W != force_w) continue;
             const size_t lds = smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W);
             if (lds > kLdsPerCU) continue;
             int per_cu = (int)(kLdsPerCU / lds);
@@ -998,24 +965,34 @@ static hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     const bool ref = step && a.step.ref_kt != nullptr;
     auto kern = ref ? attn_kernel<D, NT, true, false, true>
                     : step ? attn_kernel<D, NT, true> : a.nsa ? attn_kernel<D, NT, false, true> : attn_kernel<D, NT, false>;
-    const int kind = ref ? 3 : step ? 1 : a.nsa ? 2 : 0;
-    static bool lds_granted[4] = {false, false, false, false};
-    if (!lds_granted[kind]) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCU);
-        if (e != hipSuccess) return e;
-        lds_granted[kind] = true;
-    }
     hipLaunchKernelGGL(kern, dim3(a.n_split, tasks + extra_rows), dim3(a.waves * kWave), smem, s, aa);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.n_split == 1 || a.fused_combine) return e;
-    hipLaunchKernelGGL((combine_kernel<D, NT * 16>), dim3(tasks, NT * 16), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs& a0, hipStream_t s) {
-    AttnArgs a = a0;
-    a.fused_combine = a.nsa ? 1 : env_int("SDA_ATTN_FUSED_COMBINE", 1);   // 0: merge splits in a second launch
+template <int D, int NT>
+static hipError_t grant_lds_t() {
+    const void* kerns[4] = {reinterpret_cast<const void*>(attn_kernel<D, NT, false>),
+                            reinterpret_cast<const void*>(attn_kernel<D, NT, true>),
+                            reinterpret_cast<const void*>(attn_kernel<D, NT, false, true>),
+                            reinterpret_cast<const void*>(attn_kernel<D, NT, true, false, true>)};
+    for (const void* k : kerns) {
+        const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsPerCU);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t attn_grant_lds() {
+    hipError_t e = grant_lds_t<128, 1>();
+    if (e == hipSuccess) e = grant_lds_t<128, 2>();
+    if (e == hipSuccess) e = grant_lds_t<64, 1>();
+    if (e == hipSuccess) e = grant_lds_t<64, 2>();
+    return e;
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+    const hipError_t e = device_setup();
+    if (e != hipSuccess) return e;
     const int rp = attn_rows_pad(a.C, a.G);
     if (a.d == 128) return rp == 16 ? launch_t<128, 1>(a, s) : launch_t<128, 2>(a, s);
     return rp == 16 ? launch_t<64, 1>(a, s) : launch_t<64, 2>(a, s);

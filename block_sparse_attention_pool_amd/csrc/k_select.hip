@@ -259,7 +259,10 @@ __device__ __forceinline__ void select_tail(const SelectArgs& s, uint64_t* cand,
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's lists have landed
     __syncthreads();
     int* cnt = counters + (size_t)row * gridDim.z + blockIdx.z;
-    if (tid == 0) last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nch - 1;
+    if (tid == 0) {
+        last = arrive(cnt) == nch - 1;
+        if (last) acquire_agent();
+    }
     __syncthreads();
     if (!last) return;
 

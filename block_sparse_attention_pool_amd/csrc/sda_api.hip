@@ -224,7 +224,7 @@ sda_status_t sda_score_select(const void* f, const void* k_tilde, const int32_t*
     int* counters = reinterpret_cast<int*>(base + cand_off + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k));
     // one launch (the last scoring workgroup of each row merges per-chunk
     // candidate lists) unless the lists would be too long for it
-    if (!fused_select_ok(NB_cap, top_k) || env_int("SDA_SELECT_FUSED", 1) == 0) cand = nullptr, counters = nullptr;
+    if (!fused_select_ok(NB_cap, top_k)) cand = nullptr, counters = nullptr;
     SelectArgs a{seq_len, nullptr, B * NQ * H_kv, NQ, H_kv, NB_cap, n_init, n_local, top_k, n_sel_max,
                  block_idx, n_sel};
     return hip_status(launch_score_select(static_cast<const uint16_t*>(f), static_cast<const uint16_t*>(k_tilde), a, B, d, scores_opt, scores_ws,
@@ -265,7 +265,7 @@ sda_status_t sda_score_select_pooled(const void* f, const void* k_tilde, const i
     const size_t cand_off = score_region_bytes(B, NQ, H_kv, NB_cap);
     uint64_t* cand = reinterpret_cast<uint64_t*>(base + cand_off);
     int* counters = reinterpret_cast<int*>(base + cand_off + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k));
-    if (!fused_select_ok(NB_cap, top_k) || env_int("SDA_SELECT_FUSED", 1) == 0) cand = nullptr, counters = nullptr;
+    if (!fused_select_ok(NB_cap, top_k)) cand = nullptr, counters = nullptr;
     SelectArgs a{seq_len, nullptr, B * NQ * H_kv, NQ, H_kv, NB_cap, n_init, n_local, top_k, n_sel_max,
                  block_idx, n_sel};
     return hip_status(launch_score_select_pooled(static_cast<const uint16_t*>(f), static_cast<const uint16_t*>(k_tilde),
@@ -308,7 +308,7 @@ sda_status_t sda_score_select_multihead(const void* q, const void* k_tilde, cons
     off += score_region_bytes(B, NQ, H_kv, NB_cap);
     uint64_t* cand = reinterpret_cast<uint64_t*>(base + off);
     int* counters = reinterpret_cast<int*>(base + off + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k));
-    if (!fused_select_ok(NB_cap, top_k) || env_int("SDA_SELECT_FUSED", 1) == 0) cand = nullptr, counters = nullptr;
+    if (!fused_select_ok(NB_cap, top_k)) cand = nullptr, counters = nullptr;
     SelectArgs a{seq_len, nullptr, B * NQ * H_kv, NQ, H_kv, NB_cap, n_init, n_local, top_k, n_sel_max,
                  block_idx, n_sel};
     return hip_status(launch_multihead_select(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_tilde),
@@ -516,7 +516,7 @@ sda_status_t sda_nsa_decode(const void* q, const void* k, const void* v, const v
 // launch (workgroups past the attention grid score and select)
 static bool step_fused_plan(int B, int H_q, int H_kv, int d, int n_sel_max, int split_k, int NB_cap_next,
                             int top_k, AttnPlan* plan) {
-    if (!fused_select_ok(NB_cap_next, top_k) || env_int("SDA_STEP_FUSED", 1) == 0) return false;
+    if (!fused_select_ok(NB_cap_next, top_k)) return false;
     // the decode takes about half of the compute units, so that the scoring
     // workgroups run beside it from the start instead of after it (at 128K:
     // 2 splits, 28.5 us per step, against 30.7 us with the decode's own
@@ -550,6 +550,142 @@ size_t sda_decode_step_workspace(int B, int H_q, int H_kv, int d, int n_sel_max,
     return pad256(dec) + sda_score_select_workspace(B, 1, H_kv, NB_cap_next, top_k);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The decode step's arguments, in the order of the C call.
+struct StepCall {
+    const void* q; const void* k; const void* v; const int32_t* seq_len;
+    const int32_t* block_idx; const int32_t* n_sel; int n_sel_max; int T_cap;
+    int B, H_q, H_kv, d; float scale; float* out; float* lse; int split_k;
+    const void* f_next; const void* k_tilde_next; const int32_t* seq_len_next;
+    int NB_cap_next, n_init, n_local, top_k, n_sel_max_next;
+    int32_t* block_idx_next; int32_t* n_sel_next;
+    void* k_tilde_cur; const int32_t* len_old_cur; int max_new_tokens_cur; int NB_cap_cur;
+};
+
+// Where the step's scratch lives: the decode's split partials and arrival
+// counters, the scoring's scores, per-chunk candidate lists and arrival
+// counters.  Counters must be zero before a call; every completed call
+// leaves them zero.
+struct StepScratch {
+    int* dec_counters; float* part_ml; float* part_o;
+    float* scores; uint64_t* cand; int* sel_counters;
+};
+
+// the decode's plan and partial-buffer bytes (counters excluded)
+struct StepPlan {
+    bool fused;
+    AttnPlan plan;
+    int tasks, rp;
+    size_t partial_bytes;
+};
+
+StepPlan step_plan(const StepCall& c) {
+    StepPlan sp{};
+    sp.tasks = c.B * c.H_kv;
+    sp.rp = attn_rows_pad(1, c.H_q / c.H_kv);
+    sp.fused = step_fused_plan(c.B, c.H_q, c.H_kv, c.d, c.n_sel_max, c.split_k, c.NB_cap_next, c.top_k, &sp.plan);
+    if (!sp.fused)
+        sp.plan = attn_plan(c.d, sp.rp, sp.tasks, c.n_sel_max, 1, SDA_GROUP_EXACT, 1, c.n_sel_max, c.split_k);
+    sp.partial_bytes = sp.plan.n_split > 1
+                           ? (size_t)sp.tasks * sp.plan.n_split * sp.rp * ((size_t)c.d + 2) * sizeof(float)
+                           : 0;
+    return sp;
+}
+
+sda_status_t check_step(const StepCall& c) {
+    TRY(check_attn_common(c.q, c.k, c.v, c.seq_len, c.block_idx, c.n_sel, c.n_sel_max, c.T_cap, c.B, 1, c.H_q,
+                          c.H_kv, c.d, c.scale, c.out, c.split_k));
+    REQUIRE(c.f_next, SDA_ERR_NULL, "decode_step: f_next is null");
+    TRY(check_select_common(c.k_tilde_next, c.seq_len_next, c.B, 1, c.H_kv, c.d, c.NB_cap_next, c.n_init,
+                            c.n_local, c.top_k, c.n_sel_max_next, c.block_idx_next, c.n_sel_next));
+    REQUIRE(aligned16(c.f_next), SDA_ERR_ALIGN, "f_next must be 16-byte aligned");
+    REQUIRE(c.block_idx_next != c.block_idx && c.n_sel_next != c.n_sel, SDA_ERR_SHAPE,
+            "the next layer's block lists must not alias this layer's");
+    REQUIRE((long long)c.B * c.H_kv <= kMaxGridYZ, SDA_ERR_SHAPE, "B*H_kv exceeds %d", kMaxGridYZ);
+    if (c.k_tilde_cur) {                                   // this layer's compressed keys, refreshed in the launch
+        REQUIRE(c.len_old_cur, SDA_ERR_NULL, "decode_step: len_old_cur is null");
+        REQUIRE(c.k_tilde_cur != c.k_tilde_next, SDA_ERR_SHAPE, "this layer's compressed keys alias the next layer's");
+        REQUIRE(c.NB_cap_cur >= ceil_div(c.T_cap, kBlock), SDA_ERR_SHAPE, "NB_cap_cur=%d < ceil(T_cap/64)=%d",
+                c.NB_cap_cur, ceil_div(c.T_cap, kBlock));
+        REQUIRE(c.max_new_tokens_cur >= 0, SDA_ERR_SHAPE, "max_new_tokens_cur=%d < 0", c.max_new_tokens_cur);
+        REQUIRE(aligned16(c.k_tilde_cur) && aligned4(c.len_old_cur), SDA_ERR_ALIGN,
+                "k_tilde_cur must be 16-byte and len_old_cur 4-byte aligned");
+    }
+    return SDA_OK;
+}
+
+// Runs a checked step with its scratch at `w`.
+sda_status_t run_step(const StepCall& c, const StepPlan& sp, const StepScratch& w, hipStream_t s) {
+    const bool refresh = c.k_tilde_cur && c.max_new_tokens_cur > 0;
+    AttnArgs a{};
+    a.q = static_cast<const uint16_t*>(c.q);
+    a.k = static_cast<const uint16_t*>(c.k);
+    a.v = static_cast<const uint16_t*>(c.v);
+    a.seq_len = c.seq_len;
+    a.block_idx = c.block_idx;
+    a.n_sel = c.n_sel;
+    a.slot = nullptr;
+    a.out = c.out;
+    a.lse = c.lse;
+    a.union_count = nullptr;
+    a.counters = sp.plan.n_split > 1 ? w.dec_counters : nullptr;
+    a.part_ml = sp.plan.n_split > 1 ? w.part_ml : nullptr;
+    a.part_o = sp.plan.n_split > 1 ? w.part_o : nullptr;
+    a.n_sel_max = c.n_sel_max;
+    a.T_cap = c.T_cap;
+    a.NB_cap = ceil_div(c.T_cap, kBlock);
+    a.B = c.B;
+    a.NQ = 1;
+    a.H_q = c.H_q;
+    a.H_kv = c.H_kv;
+    a.G = c.H_q / c.H_kv;
+    a.d = c.d;
+    a.C = 1;
+    a.mode = SDA_GROUP_EXACT;
+    a.n_groups = 1;
+    a.n_split = sp.plan.n_split;
+    a.waves = sp.plan.waves;
+    a.scale_log2 = c.scale * 1.4426950408889634f;
+    const SelectArgs sel{c.seq_len_next, nullptr, c.B * c.H_kv, 1, c.H_kv, c.NB_cap_next, c.n_init, c.n_local,
+                         c.top_k, c.n_sel_max_next, c.block_idx_next, c.n_sel_next};
+    if (!sp.fused) {                                     // the calls one after the other
+        if (refresh) {
+            int blocks = ceil_div(c.max_new_tokens_cur, kBlock) + 1;
+            if (blocks > c.NB_cap_cur) blocks = c.NB_cap_cur;
+            TRY(hip_status(launch_update_compressed_keys(static_cast<const uint16_t*>(c.k),
+                                                         static_cast<uint16_t*>(c.k_tilde_cur), c.len_old_cur,
+                                                         c.seq_len, blocks, c.B, c.H_kv, c.d, c.T_cap, c.NB_cap_cur,
+                                                         kBlock, kBlock, s),
+                           "decode_step: compressed-key refresh launch"));
+        }
+        TRY(hip_status(launch_score_select(static_cast<const uint16_t*>(c.f_next),
+                                           static_cast<const uint16_t*>(c.k_tilde_next), sel, c.B, c.d, nullptr,
+                                           w.scores, nullptr, nullptr, s),
+                       "decode_step: score/select launch"));
+        return hip_status(launch_attention(a, s), "decode_step: decode launch");
+    }
+    a.step.vec = static_cast<const uint16_t*>(c.f_next);
+    a.step.kt = static_cast<const uint16_t*>(c.k_tilde_next);
+    a.step.cand = w.cand;
+    a.step.counters = w.sel_counters;
+    a.step.sel = sel;
+    a.step.cpr = score_chunks(c.NB_cap_next);
+    a.step.per_wg = min(sp.plan.waves / 4, 2);
+    // m new tokens touch at most floor((m + 62) / 64) + 1 blocks (one for a single token)
+    a.step.ref_kt = refresh ? static_cast<uint16_t*>(c.k_tilde_cur) : nullptr;
+    a.step.ref_len_old = c.len_old_cur;
+    a.step.ref_NB_cap = c.NB_cap_cur;
+    a.step.ref_blocks = refresh ? std::min((c.max_new_tokens_cur + kBlock - 2) / kBlock + 1, c.NB_cap_cur) : 0;
+    return hip_status(launch_attention(a, s), "decode_step launch");
+}
+
+}  // namespace
+
+extern "C" {
+
 sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const int32_t* seq_len,
                              const int32_t* block_idx, const int32_t* n_sel, int n_sel_max, int T_cap, int B,
                              int H_q, int H_kv, int d, float scale, float* out, float* lse_opt, int split_k,
@@ -558,91 +694,25 @@ sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const 
                              int32_t* block_idx_next, int32_t* n_sel_next, void* k_tilde_cur,
                              const int32_t* len_old_cur, int max_new_tokens_cur, int NB_cap_cur, void* ws,
                              size_t ws_bytes, void* stream) {
-    TRY(check_attn_common(q, k, v, seq_len, block_idx, n_sel, n_sel_max, T_cap, B, 1, H_q, H_kv, d, scale, out,
-                          split_k));
-    REQUIRE(f_next, SDA_ERR_NULL, "decode_step: f_next is null");
-    TRY(check_select_common(k_tilde_next, seq_len_next, B, 1, H_kv, d, NB_cap_next, n_init, n_local, top_k,
-                            n_sel_max_next, block_idx_next, n_sel_next));
-    REQUIRE(aligned16(f_next), SDA_ERR_ALIGN, "f_next must be 16-byte aligned");
-    REQUIRE(block_idx_next != block_idx && n_sel_next != n_sel, SDA_ERR_SHAPE,
-            "the next layer's block lists must not alias this layer's");
-    if (k_tilde_cur) {                                   // this layer's compressed keys, refreshed in the launch
-        REQUIRE(len_old_cur, SDA_ERR_NULL, "decode_step: len_old_cur is null");
-        REQUIRE(k_tilde_cur != k_tilde_next, SDA_ERR_SHAPE, "this layer's compressed keys alias the next layer's");
-        REQUIRE(NB_cap_cur >= ceil_div(T_cap, kBlock), SDA_ERR_SHAPE, "NB_cap_cur=%d < ceil(T_cap/64)=%d", NB_cap_cur,
-                ceil_div(T_cap, kBlock));
-        REQUIRE(max_new_tokens_cur >= 0, SDA_ERR_SHAPE, "max_new_tokens_cur=%d < 0", max_new_tokens_cur);
-        REQUIRE(aligned16(k_tilde_cur) && aligned4(len_old_cur), SDA_ERR_ALIGN,
-                "k_tilde_cur must be 16-byte and len_old_cur 4-byte aligned");
-    }
-    const bool refresh = k_tilde_cur && max_new_tokens_cur > 0;
-    // m new tokens touch at most floor((m + 62) / 64) + 1 blocks (one for a single token)
-    const int ref_blocks = refresh ? std::min((max_new_tokens_cur + kBlock - 2) / kBlock + 1, NB_cap_cur) : 0;
+    const StepCall c{q, k, v, seq_len, block_idx, n_sel, n_sel_max, T_cap, B, H_q, H_kv, d, scale, out, lse_opt,
+                     split_k, f_next, k_tilde_next, seq_len_next, NB_cap_next, n_init, n_local, top_k,
+                     n_sel_max_next, block_idx_next, n_sel_next, k_tilde_cur, len_old_cur, max_new_tokens_cur,
+                     NB_cap_cur};
+    TRY(check_step(c));
     const size_t need = sda_decode_step_workspace(B, H_q, H_kv, d, n_sel_max, split_k, NB_cap_next, top_k);
     REQUIRE(ws && ws_bytes >= need, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, need);
     REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
-    AttnPlan plan{};
-    const bool fused = step_fused_plan(B, H_q, H_kv, d, n_sel_max, split_k, NB_cap_next, top_k, &plan);
-    const int rp = attn_rows_pad(1, H_q / H_kv);
-    const int tasks = B * H_kv;
-    const size_t dec = fused ? attn_ws_bytes(tasks, plan.n_split, rp, d)
-                             : sda_sparse_decode_workspace(B, 1, H_q, H_kv, n_sel_max, d, split_k);
-    char* dws = static_cast<char*>(ws);
-    char* sws = dws + pad256(dec);
-    const size_t sws_bytes = ws_bytes - pad256(dec);
-    if (!fused) {                                        // the calls one after the other
-        if (refresh)
-            TRY(sda_update_compressed_keys(k, k_tilde_cur, len_old_cur, seq_len, max_new_tokens_cur, B, H_kv, d, T_cap,
-                                           NB_cap_cur, stream));
-        TRY(sda_score_select(f_next, k_tilde_next, seq_len_next, B, 1, H_kv, d, NB_cap_next, n_init, n_local, top_k,
-                             n_sel_max_next, block_idx_next, n_sel_next, nullptr, sws, sws_bytes, stream));
-        return sda_sparse_decode(q, k, v, seq_len, block_idx, n_sel, n_sel_max, nullptr, T_cap, B, 1, H_q, H_kv, d,
-                                 scale, out, lse_opt, split_k, dec ? dws : nullptr, dec, stream);
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t cand_off = score_region_bytes(B, 1, H_kv, NB_cap_next);     // same layout as sda_score_select
-    uint64_t* cand = reinterpret_cast<uint64_t*>(sws + cand_off);
-    int* counters = reinterpret_cast<int*>(sws + cand_off + cand_region_bytes(B, 1, H_kv, NB_cap_next, top_k));
-    AttnArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
-    a.seq_len = seq_len;
-    a.block_idx = block_idx;
-    a.n_sel = n_sel;
-    a.slot = nullptr;
-    a.out = out;
-    a.lse = lse_opt;
-    a.union_count = nullptr;
-    set_workspace(a, dws, dec, tasks, plan.n_split, rp);
-    a.n_sel_max = n_sel_max;
-    a.T_cap = T_cap;
-    a.NB_cap = ceil_div(T_cap, kBlock);
-    a.B = B;
-    a.NQ = 1;
-    a.H_q = H_q;
-    a.H_kv = H_kv;
-    a.G = H_q / H_kv;
-    a.d = d;
-    a.C = 1;
-    a.mode = SDA_GROUP_EXACT;
-    a.n_groups = 1;
-    a.n_split = plan.n_split;
-    a.waves = plan.waves;
-    a.scale_log2 = scale * 1.4426950408889634f;
-    a.step.vec = static_cast<const uint16_t*>(f_next);
-    a.step.kt = static_cast<const uint16_t*>(k_tilde_next);
-    a.step.cand = cand;
-    a.step.counters = counters;
-    a.step.sel = SelectArgs{seq_len_next, nullptr, B * H_kv, 1, H_kv, NB_cap_next, n_init, n_local, top_k,
-                            n_sel_max_next, block_idx_next, n_sel_next};
-    a.step.cpr = score_chunks(NB_cap_next);
-    a.step.per_wg = min(plan.waves / 4, 2);
-    a.step.ref_kt = refresh ? static_cast<uint16_t*>(k_tilde_cur) : nullptr;
-    a.step.ref_len_old = len_old_cur;
-    a.step.ref_NB_cap = NB_cap_cur;
-    a.step.ref_blocks = ref_blocks;
-    return hip_status(launch_attention(a, s), "decode_step launch");
+    const StepPlan sp = step_plan(c);
+    // [decode: counters, (m, l), o][score_select's layout: scores, candidate lists, counters]
+    const size_t dec = attn_ws_bytes(sp.tasks, sp.plan.n_split, sp.rp, d);
+    AttnArgs dw{};
+    set_workspace(dw, ws, dec, sp.tasks, sp.plan.n_split, sp.rp);
+    char* sws = static_cast<char*>(ws) + pad256(dec);
+    const size_t cand_off = score_region_bytes(B, 1, H_kv, NB_cap_next);
+    StepScratch w{dw.counters, dw.part_ml, dw.part_o, reinterpret_cast<float*>(sws),
+                  reinterpret_cast<uint64_t*>(sws + cand_off),
+                  reinterpret_cast<int*>(sws + cand_off + cand_region_bytes(B, 1, H_kv, NB_cap_next, top_k))};
+    return run_step(c, sp, w, static_cast<hipStream_t>(stream));
 }
 
 size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap,

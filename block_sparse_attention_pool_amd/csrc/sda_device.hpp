@@ -84,6 +84,26 @@ __device__ __forceinline__ u32x4 ldg16_cached(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// A workgroup's arrival at a counter shared by the workgroups of one row,
+// made by one thread (thread 0): a relaxed agent-scope increment, returning
+// the count before it.  Publication: everything a workgroup hands over (split
+// partials, per-chunk candidate lists) is written with agent-scope atomic
+// stores, which gfx950 writes through the XCD's non-coherent L2 to the
+// agent's coherence point and reports complete (vmcnt) only once they are
+// visible there; every wave waits for its own stores to complete
+// (s_waitcnt vmcnt(0)) before the workgroup barrier that precedes the
+// increment, so all of them are visible to the whole agent before it is
+// issued.  A release fence at agent scope would add an L2 write-back
+// (buffer_wbl2) that these stores do not need; it doubled the decode step's
+// time (46 against 24.7 us at the 128K workload).  Consumption: the arrival
+// that sees the final count calls acquire_agent() (L2 invalidate,
+// buffer_inv; +0.25 us per step) before the barrier that lets its waves read
+// the other workgroups' stores, which they read with agent-scope atomic loads.
+__device__ __forceinline__ int arrive(int* counter) {
+    return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
 // order-preserving map float -> uint32 (larger float -> larger key); -0 == +0
 __device__ __forceinline__ uint32_t float_key(float x) {
     uint32_t u = __float_as_uint(x);

@@ -59,8 +59,6 @@ __host__ __device__ inline size_t step_lds_bytes(int K, int cpr, int per_wg) {
     return per_wg * step_group_lds_bytes(K) + (P * cpr + P * ((cpr + 1) / 2)) * 8 + 16;
 }
 int score_tiles(int NQ);
-// integer from the environment (tuning switches), dflt when unset
-int env_int(const char* name, int dflt);
 // G-head comparator: scores plus per-chunk softmax statistics, then per-block
 // sums of the heads' softmax weights and the selection (inside the second
 // launch when cand / counters are given, else a third launch)
@@ -115,7 +113,6 @@ struct AttnArgs {
     int n_groups;             // ceil(NQ / C)
     int n_split;
     int waves;                // waves per workgroup
-    int fused_combine;        // 1: the last split's workgroup merges; 0: separate merge launch
     float scale_log2;         // scale * log2(e)
     // Optional (the decode-step entry point): workgroups past the attention
     // grid score the next layer and select its blocks (step.cand null = off)
@@ -141,6 +138,15 @@ AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode
 size_t attn_ws_bytes(int tasks, int n_split, int rows_pad, int d);
 size_t attn_smem_bytes_host(int d, int rows_pad, int W, int C, int mode, int NB_cap, int n_sel_max);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// gives every attention kernel the compute unit's whole LDS (160 KB) on the
+// current device; called once per device by device_setup()
+hipError_t attn_grant_lds();
+
+// ---- per-device set-up ----------------------------------------------------------------
+// Done once per device, at the first call of any entry point on it, under a
+// lock: grants the attention kernels their LDS.  The record never changes
+// after it is written and never changes results.
+hipError_t device_setup();
 
 // ---- offload gather -----------------------------------------------------------------
 hipError_t launch_gather(const uint16_t* k_src, const uint16_t* v_src, const int32_t* block_idx,

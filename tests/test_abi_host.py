@@ -309,3 +309,118 @@ def test_python_binding_rejects_bad_tensors():
         sda.sda_update_compressed_keys(kb, torch.zeros((1, 2, 1, 64), dtype=torch.bfloat16),
                                        torch.zeros(1, dtype=torch.int32),
                                        torch.zeros(1, dtype=torch.int32), 64)
+
+
+# ---------------------------------------------------------------------------
+# The binding checks the shape of every tensor argument (defaults and caller
+# outputs alike) before the foreign call: the C ABI cannot see buffer sizes,
+# so a wrong shape would otherwise become an out-of-bounds device access.
+# Here every tensor is a host tensor: with all shapes right, the binding gets
+# as far as its placement check and refuses the host tensors; with one shape
+# wrong it names that argument first.  Nothing reaches the library's calls.
+# ---------------------------------------------------------------------------
+
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _cases():
+    import torch
+    bf, i32, f32 = torch.bfloat16, torch.int32, torch.float32
+    B, NQ, H_q, H_kv, d, T_cap, nsm = 2, 1, 8, 2, 64, 256, 5
+    dec = dict(q=_t((B, NQ, H_q, d), bf), k=_t((B, H_kv, T_cap, d), bf), v=_t((B, H_kv, T_cap, d), bf),
+               seq_len=_t((B,), i32), block_idx=_t((B, NQ, H_kv, nsm), i32), n_sel=_t((B, NQ, H_kv), i32))
+    cases = []
+    # (binding, positional names, fixed kwargs, tensors, the wrong shape of each checked argument)
+    cases.append((sda.sda_sparse_decode, dict(dec),
+                  dict(out=_t((B, NQ, H_q, d), f32), lse=_t((B, NQ, H_q), f32), slot=_t((B, NQ, H_kv, nsm), i32)),
+                  {}, dict(k=(B, H_kv, T_cap, 2 * d), v=(B, H_kv, T_cap + 64, d),
+                           seq_len=(B + 1,), block_idx=(B, NQ + 1, H_kv, nsm), n_sel=(B, NQ, H_kv + 1),
+                           out=(B, NQ, H_q, d - 1), lse=(B, NQ, H_q + 1), slot=(B, NQ, H_kv, nsm + 1))))
+    step = dict(dec, f_next=_t((B, 1, H_kv, d), bf), k_tilde_next=_t((B, H_kv, 8, d), bf),
+                seq_len_next=_t((B,), i32), n_init=1, n_local=1, top_k=3)
+    cases.append((sda.sda_decode_step, step,
+                  dict(block_idx_next=_t((B, 1, H_kv, 5), i32), n_sel_next=_t((B, 1, H_kv), i32),
+                       out=_t((B, 1, H_q, d), f32), lse=_t((B, 1, H_q), f32),
+                       k_tilde_cur=_t((B, H_kv, 4, d), bf), len_old_cur=_t((B,), i32)),
+                  {}, dict(f_next=(B, 1, H_kv + 1, d), k_tilde_next=(B, H_kv, 8, d + 1), seq_len_next=(B - 1,),
+                           block_idx_next=(B, 1, H_kv - 1, 5), n_sel_next=(B, 2, H_kv), out=(B, 1, H_q - 1, d),
+                           lse=(B, 1, H_q, 2), k_tilde_cur=(B + 1, H_kv, 4, d), len_old_cur=(B + 1,),
+                           n_sel=(B, 1, 1))))
+    sel = dict(f=_t((B, NQ, H_kv, d), bf), k_tilde=_t((B, H_kv, 8, d), bf), seq_len=_t((B,), i32),
+               n_init=1, n_local=1, top_k=3)
+    cases.append((sda.sda_score_select, sel,
+                  dict(block_idx=_t((B, NQ, H_kv, 5), i32), n_sel=_t((B, NQ, H_kv), i32),
+                       scores=_t((B, NQ, H_kv, 8), f32)),
+                  {}, dict(k_tilde=(B, H_kv + 1, 8, d), seq_len=(2 * B,), block_idx=(B, NQ, H_kv + 1, 5),
+                           n_sel=(B, NQ + 1, H_kv), scores=(B, NQ, H_kv, 7))))
+    cases.append((sda.sda_score_select_pooled, dict(sel, window=32, stride=16),
+                  dict(block_idx=_t((B, NQ, H_kv, 5), i32), n_sel=_t((B, NQ, H_kv), i32),
+                       scores=_t((B, NQ, H_kv, 2), f32)),
+                  {}, dict(k_tilde=(B, H_kv, 8, d * 2), scores=(B, NQ, H_kv, 8), n_sel=(B, NQ, 1))))
+    cases.append((sda.sda_score_select_multihead,
+                  dict(q=_t((B, NQ, H_q, d), bf), k_tilde=_t((B, H_kv, 8, d), bf), seq_len=_t((B,), i32),
+                       n_init=1, n_local=1, top_k=3, tau=8.0),
+                  dict(block_idx=_t((B, NQ, H_kv, 5), i32), n_sel=_t((B, NQ, H_kv), i32)),
+                  {}, dict(k_tilde=(B + 1, H_kv, 8, d), block_idx=(B, NQ, H_kv + 1, 5), n_sel=(B, NQ))))
+    NQg, C = 4, 2
+    grp = dict(q=_t((B, NQg, H_q, d), bf), k=dec["k"], v=dec["v"], seq_len=dec["seq_len"],
+               block_idx=_t((B, NQg, H_kv, nsm), i32), n_sel=_t((B, NQg, H_kv), i32), group_C=C)
+    cases.append((sda.sda_grouped_decode, grp,
+                  dict(out=_t((B, NQg, H_q, d), f32), lse=_t((B, NQg, H_q), f32),
+                       union_count=_t((B, NQg // C, H_kv), i32)),
+                  {}, dict(block_idx=(B, NQg - 1, H_kv, nsm), union_count=(B, NQg, H_kv),
+                           lse=(B, NQg, H_q, 1), out=(B, NQg, H_q + 8, d))))
+    nsa = dict(grp, k_cmp=_t((B, H_kv, 16, d), bf), v_cmp=_t((B, H_kv, 16, d), bf),
+               gates=_t((B, NQg, H_q, 3), f32), cmp_stride=16, window=64)
+    cases.append((sda.sda_nsa_decode, nsa,
+                  dict(out=_t((B, NQg, H_q, d), f32), lse=_t((B, NQg, H_q, 3), f32),
+                       union_count=_t((B, NQg // C, H_kv), i32)),
+                  {}, dict(k_cmp=(B, H_kv, 16, d + 64), v_cmp=(B, H_kv, 15, d), gates=(B, NQg, H_q, 2),
+                           lse=(B, NQg, H_q), union_count=(B, 1, H_kv))))
+    upd = dict(k=dec["k"], k_tilde=_t((B, H_kv, 4, d), bf), len_old=_t((B,), i32), len_new=_t((B,), i32),
+               max_new_tokens=1)
+    cases.append((sda.sda_update_compressed_keys, upd, {}, {},
+                  dict(k_tilde=(B, H_kv, 4, d // 2), len_old=(B + 1,), len_new=(1,))))
+    cases.append((sda.sda_update_compressed_keys_strided, dict(upd, window=32, stride=16), {}, {},
+                  dict(k_tilde=(B, 1, 4, d), len_new=(B, 1))))
+    return cases
+
+
+def _call(fn, args, kw):
+    return fn(**args, **kw)
+
+
+def test_binding_checks_every_tensor_shape(L):
+    import torch
+    for fn, args, kw, _, wrong in _cases():
+        with pytest.raises(ValueError, match="must be a GPU tensor"):       # every shape right
+            _call(fn, args, kw)
+        for name, shape in wrong.items():
+            a2, kw2 = dict(args), dict(kw)
+            tgt = a2 if name in a2 else kw2
+            tgt[name] = torch.zeros(shape, dtype=tgt[name].dtype)
+            with pytest.raises(ValueError, match=f"^{name} must have shape"):
+                _call(fn, a2, kw2)
+
+
+def test_binding_checks_workspace_and_gather_shapes(L):
+    import torch
+    fn, args, kw, _, _ = _cases()[0]
+    with pytest.raises(ValueError, match="ws holds 16 bytes"):
+        _call(fn, args, dict(kw, split_k=3, ws=torch.zeros(16, dtype=torch.uint8)))
+    B, H_kv, T_cap, d = 2, 2, 256, 64
+    kh = torch.zeros((B, H_kv, T_cap, d), dtype=torch.bfloat16)
+    bi = torch.zeros((B, H_kv, 3), dtype=torch.int32)
+    ns = torch.zeros((B, H_kv), dtype=torch.int32)
+    with pytest.raises(ValueError, match="^v_host must have shape"):
+        sda.sda_gather_blocks(kh, kh[:, :1].contiguous(), bi, ns)
+    with pytest.raises(ValueError, match="^n_sel must have shape"):
+        sda.sda_gather_blocks(kh, kh, bi, ns[:1])
+    with pytest.raises(ValueError, match="^k_stage must have shape"):
+        sda.sda_gather_blocks(kh, kh, bi, ns, k_stage=torch.zeros((B, H_kv, 2 * 64, d), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="^slot must have shape"):
+        sda.sda_gather_blocks(kh, kh, bi, ns, slot=torch.zeros((B, H_kv, 4), dtype=torch.int32))
+    with pytest.raises(ValueError, match="pinned"):                        # shapes right, not pinned
+        sda.sda_gather_blocks(kh, kh, bi, ns)

@@ -130,6 +130,74 @@ def test_c3_70b_shaped_128k():
     assert _mismatches(bm, nm, want_m) == []
 
 
+@pytest.mark.parametrize("refresh", [False, True])
+def test_c3_decode_step_as_benchmarked(refresh):
+    # The timed kernel itself against the oracle: sda_decode_step at the
+    # 128K workload, prepared and run as the benchmark runs it (one launch,
+    # split_k = 0 so the library's plan, zeroed workspace).  Layer 1 attends
+    # over its block lists while layer 1's indexer vectors select layer 2's
+    # blocks ([SparDA] §4.2 steps 2 and 4, eq. (6), (7)).  Checked: layer 2's
+    # block sets bit for bit against the oracle on the sampled rows (tie-free
+    # vectors there), the format of every other row, the output of every
+    # query head within 2e-3 of the oracle over the lists it was given and
+    # its lse within 1e-3; with the refresh, layer 1's compressed keys pooled
+    # up to ragged shorter lengths come back equal to the oracle's bits.
+    cfg = synth.get_config(3)
+    T = cfg.T
+    _say(f"c3 step (refresh={refresh}): draw layers 1 and 2")
+    K1, V1, _ = inputs.kv_layer(cfg, 1, device=DEV)
+    K2, _, _ = inputs.kv_layer(cfg, 2, device=DEV)
+    sample = _c3_sample(cfg)
+    kv_s = [(b, g) for (b, _, g) in sample]
+    kt1 = oracle_kt(K1, T, kv_s)
+    kt2 = oracle_kt(K2, T, kv_s)
+    ktg1 = gpu_ktilde(K1, T)
+    ktg2 = gpu_ktilde(K2, T)
+    del K2
+    F0, _ = tie_free_indexer(cfg, 0, kt1, sample)          # layer 0 chose layer 1's blocks
+    F1, _ = tie_free_indexer(cfg, 1, kt2, sample)          # layer 1 chooses layer 2's
+    sel = (cfg.n_init, cfg.n_local, cfg.top_k)
+    bi1, ns1 = sda.sda_score_select(F0.to(DEV), ktg1, seq(cfg), *sel)
+    assert _mismatches(bi1, ns1, oracle_select(cfg, O.bf16_to_f64(bits(F0)), kt1, sample)) == []
+    Q1 = inputs.to_bf16(inputs.attention_queries(cfg, 1))
+    kw = dict(split_k=0)
+    if refresh:
+        old = torch.tensor([T - 1, T - 64, T - 65, T - 70, T - 1, T - 2, T - 127, T - 33][:cfg.B],
+                           dtype=torch.int32, device=DEV)
+        kt_cur = torch.zeros_like(ktg1)
+        zero = torch.zeros(cfg.B, dtype=torch.int32, device=DEV)
+        sda.sda_update_compressed_keys(K1, kt_cur, zero, old, T)
+        assert not torch.equal(kt_cur, ktg1)
+        kw.update(k_tilde_cur=kt_cur, len_old_cur=old, max_new_tokens_cur=127)
+    nsm = bi1.shape[-1]
+    assert sda.lib().sda_decode_step_is_fused(cfg.B, cfg.H_q, cfg.H_kv, cfg.d, nsm, 0, ktg2.shape[2],
+                                              cfg.top_k) == 1
+    call, (out, lse, bi2, ns2) = sda.prepare(sda.sda_decode_step, Q1.to(DEV), K1, V1, seq(cfg), bi1, ns1,
+                                             F1.to(DEV), ktg2, seq(cfg), *sel, **kw)
+    call.run()
+    torch.cuda.synchronize()
+    want2 = oracle_select(cfg, O.bf16_to_f64(bits(F1)), kt2, sample)
+    assert _mismatches(bi2, ns2, want2) == []
+    assert int(ns2.min()) == int(ns2.max()) == 35
+    b2 = bi2.cpu().numpy()
+    assert np.all(np.diff(b2, axis=-1) > 0) and b2.min() >= 0 and b2.max() < cfg.NB
+    lists = _gpu_lists(bi1, ns1, rows_of(cfg))
+    Qd = O.bf16_to_f64(bits(Q1))
+    rk = SparseRows(K1, V1, T)
+    G = cfg.G
+    err = lerr = 0.0
+    for (b, q, g), blocks in lists.items():
+        o, l = oracle_decode(Qd, rk, b, q, g, G, blocks, T, scale_of(cfg))
+        err = max(err, float(np.abs(out[b, q, g * G:(g + 1) * G].double().cpu().numpy() - o).max()))
+        lerr = max(lerr, float(np.abs(lse[b, q, g * G:(g + 1) * G].double().cpu().numpy() - l).max()))
+    _say(f"c3 step: max abs err {err:.2e}, max lse err {lerr:.2e}")
+    assert err <= TOL and lerr <= 1e-3
+    if refresh:
+        assert torch.equal(kt_cur, ktg1)                    # every row: the bulk build's bits
+        for (b, g) in kv_s:                                 # sampled rows: the oracle's bits
+            assert np.array_equal(kt_cur[b, g].double().cpu().numpy(), kt1[(b, g)])
+
+
 def test_comparator_one_head_equals_indexer():
     # G = 1 and q = f: softmax over blocks is monotone, so the selections agree
     cfg = dataclasses.replace(synth.get_config(1), H_q=2)

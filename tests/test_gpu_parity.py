@@ -14,8 +14,8 @@ import block_sparse_attention_pool_amd as sda
 import oracle as O
 import synth
 from synth import inputs
-from tests.parity_util import (DEV, TOL, SparseRows, bits, f64, gpu_ktilde, oracle_decode, oracle_kt,
-                               oracle_select, rows_of, scale_of, seq, tie_free_indexer)
+from tests.parity_util import (DELTA, DELTA_REL_MH, DEV, TOL, SparseRows, bits, f64, gpu_ktilde, oracle_decode,
+                               oracle_kt, oracle_select, rows_of, scale_of, seq, tie_free_indexer)
 
 pytestmark = pytest.mark.gpu
 
@@ -191,82 +191,104 @@ def test_select_long_rows(NB, T, n_init, n_local, k):
         assert np.all(bi[0, 0, g, n:] == -1)
 
 
-@pytest.mark.parametrize("NQ", [1, 20])
-def test_fused_select_matches_select_launch(NQ):
-    # selection inside the scoring launch (last-arriving chunk workgroup) and the
-    # separate selection launch read the same scores: identical lists, call after
-    # call, and the arrival counters are back at zero after every call
-    import os
+def _gapped_rows(cand, top_k, scores_by_row, gap):
+    """Rows whose top-k cut gap is at least `gap` (selection decided without near-ties)."""
+    return [r for r, s in scores_by_row.items() if O.cut_gap(s, cand, top_k) >= gap]
+
+
+@pytest.mark.parametrize("NQ,top_k", [(1, 16), (20, 16), (1, 80), (3, 80)])
+def test_select_paths_match_oracle(NQ, top_k):
+    # top_k <= 64: the selection runs inside the scoring launch (the last
+    # arriving chunk workgroup merges per-chunk lists); top_k = 80: the
+    # separate radix-select launch.  Both against the oracle on every row
+    # whose cut gap exceeds the float32 score error, call after call, with
+    # the in-launch path's arrival counters back at zero after each call.
     cfg = synth.get_config(2)
     K, _, _ = inputs.kv_layer(cfg, 0, device=DEV)
     ktg = gpu_ktilde(K, cfg.T)
-    rng = np.random.default_rng(NQ)
-    F = inputs.to_bf16(rng.standard_normal((cfg.B, NQ, cfg.H_kv, cfg.d)) / 8).to(DEV)
-    args = (F, ktg, seq(cfg), cfg.n_init, cfg.n_local, cfg.top_k)
-    old = os.environ.get("SDA_SELECT_FUSED")
-    try:
-        os.environ["SDA_SELECT_FUSED"] = "0"
-        ref_bi, ref_ns = sda.sda_score_select(*args)
-        os.environ["SDA_SELECT_FUSED"] = "1"
-        nbytes = sda.lib().sda_score_select_workspace(cfg.B, NQ, cfg.H_kv, ktg.shape[2], cfg.top_k)
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
-        n_cnt = cfg.B * cfg.H_kv * (1 if NQ == 1 else 2)
-        for it in range(10):
-            bi, ns = sda.sda_score_select(*args, ws=ws)
-            torch.cuda.synchronize()
-            assert torch.equal(bi, ref_bi) and torch.equal(ns, ref_ns), it
+    kv_rows = [(b, g) for b in range(cfg.B) for g in range(cfg.H_kv)]
+    kt = oracle_kt(K, cfg.T, kv_rows)
+    rng = np.random.default_rng(NQ + top_k)
+    F = inputs.to_bf16(rng.standard_normal((cfg.B, NQ, cfg.H_kv, cfg.d)) / 8)
+    Fd = O.bf16_to_f64(bits(F))
+    nb = O.num_blocks(cfg.T)
+    cand = O.candidates(nb, cfg.n_init, cfg.n_local)
+    sc = {(b, q, g): O.decision_scores(O.indexer_scores(Fd[b, q, g], kt[(b, g)]))
+          for b in range(cfg.B) for q in range(NQ) for g in range(cfg.H_kv)}
+    rows = _gapped_rows(cand, top_k, sc, DELTA)
+    _say(f"select NQ={NQ} top_k={top_k}: {len(rows)} of {len(sc)} rows tie-free")
+    assert len(rows) >= 0.8 * len(sc)
+    want = {r: O.block_set(nb, cfg.n_init, cfg.n_local, O.top_k(sc[r], cand, top_k)) for r in rows}
+    nbytes = sda.lib().sda_score_select_workspace(cfg.B, NQ, cfg.H_kv, ktg.shape[2], top_k)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    n_cnt = cfg.B * cfg.H_kv * (1 if NQ == 1 else 2)
+    first = None
+    for it in range(6):
+        bi, ns = sda.sda_score_select(F.to(DEV), ktg, seq(cfg), cfg.n_init, cfg.n_local, top_k, ws=ws)
+        torch.cuda.synchronize()
+        if first is None:
+            first = (bi.clone(), ns.clone())
+            _check_selection(cfg, bi, ns, want, rows)
+        assert torch.equal(bi, first[0]) and torch.equal(ns, first[1]), it
+        if top_k <= 64:
             assert int(ws[nbytes - 4 * n_cnt:].count_nonzero()) == 0, it
-    finally:
-        if old is None:
-            os.environ.pop("SDA_SELECT_FUSED", None)
-        else:
-            os.environ["SDA_SELECT_FUSED"] = old
 
 
-@pytest.mark.parametrize("NQ", [1, 3])
-def test_comparator_fused_select_matches_select_launch(NQ):
-    # the comparator's in-launch selection and its selection launch rank the
-    # same summed softmax weights: identical block lists, counters back at zero
-    import os
+@pytest.mark.parametrize("NQ,top_k", [(1, 16), (3, 16), (1, 80)])
+def test_comparator_select_paths_match_oracle(NQ, top_k):
+    # the comparator's in-launch selection (top_k <= 64) and its selection
+    # launch (top_k = 80) against the oracle's summed softmax on every row
+    # with a clear relative cut gap; counters back at zero after each call
     cfg = synth.get_config(2)
     K, _, _ = inputs.kv_layer(cfg, 0, device=DEV)
     ktg = gpu_ktilde(K, cfg.T)
-    rng = np.random.default_rng(40 + NQ)
-    Q = inputs.to_bf16(rng.standard_normal((cfg.B, NQ, cfg.H_q, cfg.d))).to(DEV)
-    args = (Q, ktg, seq(cfg), cfg.n_init, cfg.n_local, cfg.top_k, math.sqrt(cfg.d))
-    old = os.environ.get("SDA_SELECT_FUSED")
-    try:
-        os.environ["SDA_SELECT_FUSED"] = "0"
-        ref_bi, ref_ns = sda.sda_score_select_multihead(*args)
-        os.environ["SDA_SELECT_FUSED"] = "1"
-        nbytes = sda.lib().sda_score_select_multihead_workspace(cfg.B, NQ, cfg.H_q, cfg.H_kv, ktg.shape[2],
-                                                                cfg.top_k)
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
-        for it in range(5):
-            bi, ns = sda.sda_score_select_multihead(*args, ws=ws)
-            torch.cuda.synchronize()
-            assert torch.equal(bi, ref_bi) and torch.equal(ns, ref_ns), it
+    kv_rows = [(b, g) for b in range(cfg.B) for g in range(cfg.H_kv)]
+    kt = oracle_kt(K, cfg.T, kv_rows)
+    rng = np.random.default_rng(40 + NQ + top_k)
+    Q = inputs.to_bf16(rng.standard_normal((cfg.B, NQ, cfg.H_q, cfg.d)))
+    Qd = O.bf16_to_f64(bits(Q))
+    G = cfg.G
+    tau = math.sqrt(cfg.d)
+    nb = O.num_blocks(cfg.T)
+    cand = O.candidates(nb, cfg.n_init, cfg.n_local)
+    rows, want = [], {}
+    for b in range(cfg.B):
+        for q in range(NQ):
+            for g in range(cfg.H_kv):
+                s = O.decision_scores(O.multihead_scores(Qd[b, q, g * G:(g + 1) * G], kt[(b, g)], tau))
+                top = np.sort(s[cand])[::-1][top_k - 1]
+                if O.cut_gap(s, cand, top_k) >= DELTA_REL_MH * abs(top):
+                    rows.append((b, q, g))
+                    want[(b, q, g)] = O.block_set(nb, cfg.n_init, cfg.n_local, O.top_k(s, cand, top_k))
+    _say(f"comparator NQ={NQ} top_k={top_k}: {len(rows)} of {cfg.B * NQ * cfg.H_kv} rows tie-free")
+    assert len(rows) >= 0.8 * cfg.B * NQ * cfg.H_kv
+    nbytes = sda.lib().sda_score_select_multihead_workspace(cfg.B, NQ, cfg.H_q, cfg.H_kv, ktg.shape[2], top_k)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    first = None
+    for it in range(4):
+        bi, ns = sda.sda_score_select_multihead(Q.to(DEV), ktg, seq(cfg), cfg.n_init, cfg.n_local, top_k, tau,
+                                                ws=ws)
+        torch.cuda.synchronize()
+        if first is None:
+            first = (bi.clone(), ns.clone())
+            _check_selection(cfg, bi, ns, want, rows)
+        assert torch.equal(bi, first[0]) and torch.equal(ns, first[1]), it
+        if top_k <= 64:
             assert int(ws[nbytes - 4 * cfg.B * cfg.H_kv * NQ:].count_nonzero()) == 0, it
-    finally:
-        if old is None:
-            os.environ.pop("SDA_SELECT_FUSED", None)
-        else:
-            os.environ["SDA_SELECT_FUSED"] = old
 
 
 # exact: both launches run the same split plan.  At one split the plain decode
 # takes 10 waves (all of the LDS); the step needs LDS for the merge and takes 9.
-@pytest.mark.parametrize("cid,fused,split_k,exact", [(2, "1", 0, False), (2, "0", 0, True), (2, "1", 5, True),
-                                                     (3, "1", 0, False), (3, "1", 7, True), (3, "1", 1, False)])
-def test_decode_step_matches_separate_calls(cid, fused, split_k, exact):
+@pytest.mark.parametrize("cid,split_k,exact", [(2, 0, False), (2, 5, True), (3, 0, False), (3, 7, True),
+                                               (3, 1, False)])
+def test_decode_step_matches_separate_calls(cid, split_k, exact):
     # the step entry point (the next layer's selection finished inside this
-    # layer's decode launch; the two calls when fused = 0) against
+    # layer's decode launch) against
     # sda_score_select for the next layer and sda_sparse_decode for this one:
     # identical block lists; identical outputs when both run the same split
     # plan, else equal up to the order of the split merge
-    import os
     cfg = synth.get_config(cid)
-    _say(f"decode step: config {cid}, fused {fused}, split_k {split_k}")
+    _say(f"decode step: config {cid}, split_k {split_k}")
     K0, V0, _ = inputs.kv_layer(cfg, 0, device=DEV)
     K1, _, _ = inputs.kv_layer(cfg, 1, device=DEV)
     kt1 = gpu_ktilde(K1, cfg.T)
@@ -279,38 +301,32 @@ def test_decode_step_matches_separate_calls(cid, fused, split_k, exact):
     bi0, ns0 = sda.sda_score_select(F0, kt0, seq(cfg), *sel)
     ref_bi1, ref_ns1 = sda.sda_score_select(F1, kt1, seq(cfg), *sel)
     ref_out, ref_lse = sda.sda_sparse_decode(Q0, K0, V0, seq(cfg), bi0, ns0, split_k=split_k)
-    old = os.environ.get("SDA_STEP_FUSED")
-    try:
-        os.environ["SDA_STEP_FUSED"] = fused
-        nbytes = sda.lib().sda_decode_step_workspace(cfg.B, cfg.H_q, cfg.H_kv, cfg.d, bi0.shape[-1], split_k,
-                                                     kt1.shape[2], cfg.top_k)
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
-        for it in range(6):
-            out, lse, bi1, ns1 = sda.sda_decode_step(Q0, K0, V0, seq(cfg), bi0, ns0, F1, kt1, seq(cfg), *sel,
-                                                     split_k=split_k, ws=ws)
-            torch.cuda.synchronize()
-            assert torch.equal(bi1, ref_bi1) and torch.equal(ns1, ref_ns1), it
-            if exact:
-                assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), it
-            else:
-                assert (out - ref_out).abs().max().item() <= 1e-5, it
-                assert (lse - ref_lse).abs().max().item() <= 1e-5, it
-            if split_k > 1:      # split arrival counters (the workspace's first ints) back at zero
-                assert int(ws[:4 * cfg.B * cfg.H_kv].count_nonzero()) == 0, it
-    finally:
-        if old is None:
-            os.environ.pop("SDA_STEP_FUSED", None)
+    nbytes = sda.lib().sda_decode_step_workspace(cfg.B, cfg.H_q, cfg.H_kv, cfg.d, bi0.shape[-1], split_k,
+                                                 kt1.shape[2], cfg.top_k)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    for it in range(6):
+        out, lse, bi1, ns1 = sda.sda_decode_step(Q0, K0, V0, seq(cfg), bi0, ns0, F1, kt1, seq(cfg), *sel,
+                                                 split_k=split_k, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(bi1, ref_bi1) and torch.equal(ns1, ref_ns1), it
+        if exact:
+            assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), it
         else:
-            os.environ["SDA_STEP_FUSED"] = old
+            assert (out - ref_out).abs().max().item() <= 1e-5, it
+            assert (lse - ref_lse).abs().max().item() <= 1e-5, it
+        if split_k != 1:      # split arrival counters (the workspace's first ints) back at zero
+            assert int(ws[:4 * cfg.B * cfg.H_kv].count_nonzero()) == 0, it
 
 
 @pytest.mark.parametrize("d,top_k,n_init,n_local,split_k", [(128, 32, 1, 2, 0), (64, 8, 0, 3, 0),
-                                                       (128, 64, 2, 0, 3), (128, 5, 3, 1, 2), (64, 16, 1, 2, 1)])
+                                                       (128, 64, 2, 0, 3), (128, 5, 3, 1, 2), (64, 16, 1, 2, 1),
+                                                       (128, 80, 1, 2, 0)])
 def test_decode_step_ragged(d, top_k, n_init, n_local, split_k):
     # ragged lengths in both layers, the next layer's capacity not a multiple
     # of a chunk, sequences shorter than init + local, one-block sequences:
     # the step's block sets equal sda_score_select's, its outputs
-    # sda_sparse_decode's (bit for bit with the same explicit split count)
+    # sda_sparse_decode's (bit for bit with the same explicit split count).
+    # top_k = 80 is past the in-launch selection: the step runs the calls.
     B, H_kv, G = 3, 2, 4
     H_q = H_kv * G
     T_cap, NBn = 5000, 300
@@ -334,7 +350,7 @@ def test_decode_step_ragged(d, top_k, n_init, n_local, split_k):
     nsm = bi0.shape[-1]
     fused = sda.lib().sda_decode_step_is_fused(B, H_q, H_kv, d, nsm, split_k, NBn, top_k)
     _say(f"ragged step d={d} top_k={top_k} split_k={split_k}: one launch = {fused}")
-    assert fused == 1
+    assert fused == (1 if top_k <= 64 else 0)
     # this layer's compressed keys, pooled up to a shorter length: the step
     # refreshes the blocks the remaining tokens touch (1 to 70 per sequence)
     old0 = seq0 - torch.tensor([70, 1, 1], dtype=torch.int32, device=DEV)
@@ -482,29 +498,40 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
 
 
-def test_fused_split_merge_matches_merge_launch():
-    # the last-arriving workgroup's merge and the separate merge launch do the
-    # same arithmetic: identical bits, call after call (counters reset each time)
-    import os
+def _gpu_lists_of(bi, ns, rows):
+    bi = bi.cpu().numpy()
+    ns = ns.cpu().numpy()
+    return {r: bi[r][:ns[r]] for r in rows}
+
+
+def test_split_merge_matches_oracle_and_repeats():
+    # the last-arriving workgroup's log-sum-exp merge of the splits: every
+    # split plan within tolerance of the oracle on sampled rows and of each
+    # other; the default plan bit for bit the same call after call (the
+    # arrival counters reset each time)
     cfg = synth.get_config(2)
     K, V, _ = inputs.kv_layer(cfg, 0, device=DEV)
     ktg = gpu_ktilde(K, cfg.T)
     F = inputs.to_bf16(inputs.indexer_vectors(cfg, 0)).to(DEV)
-    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0)).to(DEV)
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0))
     bi, ns = sda.sda_score_select(F, ktg, seq(cfg), cfg.n_init, cfg.n_local, cfg.top_k)
-    old = os.environ.get("SDA_ATTN_FUSED_COMBINE")
-    try:
-        os.environ["SDA_ATTN_FUSED_COMBINE"] = "0"
-        ref, lref = sda.sda_sparse_decode(Q, K, V, seq(cfg), bi, ns)
-        os.environ["SDA_ATTN_FUSED_COMBINE"] = "1"
-        ws = torch.zeros(sda.lib().sda_sparse_decode_workspace(cfg.B, 1, cfg.H_q, cfg.H_kv, bi.shape[-1], cfg.d, 0),
-                         dtype=torch.uint8, device=DEV)
-        for it in range(20):
-            out, lse = sda.sda_sparse_decode(Q, K, V, seq(cfg), bi, ns, ws=ws)
-            torch.cuda.synchronize()
-            assert torch.equal(out, ref) and torch.equal(lse, lref), it
-    finally:
-        if old is None:
-            os.environ.pop("SDA_ATTN_FUSED_COMBINE", None)
-        else:
-            os.environ["SDA_ATTN_FUSED_COMBINE"] = old
+    lists = _gpu_lists_of(bi, ns, [(b, 0, (b + 3) % cfg.H_kv) for b in range(cfg.B)])
+    Qd = O.bf16_to_f64(bits(Q))
+    rk = SparseRows(K, V, cfg.T)
+    Qg = Q.to(DEV)
+    ws = torch.zeros(sda.lib().sda_sparse_decode_workspace(cfg.B, 1, cfg.H_q, cfg.H_kv, bi.shape[-1], cfg.d, 0),
+                     dtype=torch.uint8, device=DEV)
+    ref, lref = sda.sda_sparse_decode(Qg, K, V, seq(cfg), bi, ns, ws=ws)
+    for (b, q, g), blocks in lists.items():
+        o, l = oracle_decode(Qd, rk, b, q, g, cfg.G, blocks, cfg.T, scale_of(cfg))
+        assert np.abs(ref[b, q, g * cfg.G:(g + 1) * cfg.G].double().cpu().numpy() - o).max() <= TOL
+        assert np.abs(lref[b, q, g * cfg.G:(g + 1) * cfg.G].double().cpu().numpy() - l).max() <= 1e-3
+    for it in range(20):
+        out, lse = sda.sda_sparse_decode(Qg, K, V, seq(cfg), bi, ns, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(lse, lref), it
+        assert int(ws[:4 * cfg.B * cfg.H_kv].count_nonzero()) == 0, it
+    for sk in (1, 2, 3, 7, 19):
+        o2, l2 = sda.sda_sparse_decode(Qg, K, V, seq(cfg), bi, ns, split_k=sk)
+        assert (o2 - ref).abs().max().item() <= 1e-5, sk
+        assert (l2 - lref).abs().max().item() <= 1e-5, sk

@@ -139,12 +139,12 @@ SELECT_CASES = [
 ]
 
 
-@pytest.mark.parametrize("fused", [1, 0])
 @pytest.mark.parametrize("case", SELECT_CASES)
-def test_pooled_select_matches_oracle(case, fused, monkeypatch):
+def test_pooled_select_matches_oracle(case):
+    # top_k <= 64: selection inside the scoring launch; top_k = 80: the
+    # separate selection launch
     B, H, d, lens, window, stride, n_init, n_local, top_k = case
-    _say("pooled select", case, "fused" if fused else "two launches")
-    monkeypatch.setenv("SDA_SELECT_FUSED", str(fused))
+    _say("pooled select", case, "in-launch selection" if top_k <= 64 else "two launches")
     cfg = dataclasses.replace(synth.get_config(2), B=B, H_kv=H, H_q=H * 4, d=d, T=max(lens), n_init=n_init,
                               n_local=n_local, top_k=top_k, bias_frac=0.0, bias_beta=0.0)
     K, _, _ = inputs.kv_layer(cfg, 0, device="cpu")
