@@ -68,6 +68,9 @@ _SIGNATURES = {
     "sda_decode_step": (_c_int, [_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_void_p, _c_void_p, _c_int]
                         + [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 4 + [_c_int] * 2
                         + [_c_void_p, _c_size_t, _c_void_p]),
+    "sda_decode_step_noalloc": (_c_int, [_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_void_p, _c_void_p, _c_int]
+                                + [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 4 + [_c_int] * 2
+                                + [_c_void_p]),
 }
 
 _lib = None
@@ -370,7 +373,7 @@ def sda_sparse_decode(q, k, v, seq_len, block_idx, n_sel, scale=None, out=None, 
 def sda_decode_step(q, k, v, seq_len, block_idx, n_sel, f_next, k_tilde_next, seq_len_next, n_init, n_local,
                     top_k, n_sel_max_next=None, block_idx_next=None, n_sel_next=None, scale=None, out=None,
                     lse=None, split_k=0, k_tilde_cur=None, len_old_cur=None, max_new_tokens_cur=1, ws=None,
-                    stream=None, _prepare=False):
+                    stream=None, _prepare=False, _noalloc=False):
     """Layer l's decode plus layer l+1's selection (same results as
     sda_score_select for l+1 then sda_sparse_decode for l) and, with
     k_tilde_cur, the refresh of layer l's compressed keys for the tokens
@@ -395,22 +398,38 @@ def sda_decode_step(q, k, v, seq_len, block_idx, n_sel, f_next, k_tilde_next, se
         _need(k_tilde_cur, "k_tilde_cur", torch.bfloat16, (B, H_kv, None, d))
         _need(len_old_cur, "len_old_cur", torch.int32, (B,))
         NB_cap_cur = k_tilde_cur.shape[2]
-    nbytes = lib().sda_decode_step_workspace(B, H_q, H_kv, d, n_sel_max, int(split_k), NB_cap_next, top_k)
-    ws, wsb = _workspace(nbytes, dev, ws)
+    if _noalloc:
+        ws, wsb = None, 0
+    else:
+        nbytes = lib().sda_decode_step_workspace(B, H_q, H_kv, d, n_sel_max, int(split_k), NB_cap_next, top_k)
+        ws, wsb = _workspace(nbytes, dev, ws)
     _on_gpu(q=q, k=k, v=v, seq_len=seq_len, block_idx=block_idx, n_sel=n_sel, f_next=f_next,
             k_tilde_next=k_tilde_next, seq_len_next=seq_len_next, out=out, lse=lse, block_idx_next=block_idx_next,
             n_sel_next=n_sel_next, k_tilde_cur=k_tilde_cur, len_old_cur=len_old_cur, ws=ws)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(block_idx), _ptr(n_sel), n_sel_max, T_cap, B, H_q,
             H_kv, d, float(scale), _ptr(out), _ptr(lse), int(split_k), _ptr(f_next), _ptr(k_tilde_next),
             _ptr(seq_len_next), NB_cap_next, n_init, n_local, top_k, n_sel_max_next, _ptr(block_idx_next),
-            _ptr(n_sel_next), _ptr(k_tilde_cur), _ptr(len_old_cur), int(max_new_tokens_cur), NB_cap_cur,
-            _ptr(ws), wsb, None)
+            _ptr(n_sel_next), _ptr(k_tilde_cur), _ptr(len_old_cur), int(max_new_tokens_cur), NB_cap_cur)
+    args = args + ((None,) if _noalloc else (_ptr(ws), wsb, None))
     outs = (out, lse, block_idx_next, n_sel_next)
+    name = "sda_decode_step_noalloc" if _noalloc else "sda_decode_step"
     if _prepare:
-        return PreparedCall("sda_decode_step", args, (q, k, v, seq_len, block_idx, n_sel, f_next, k_tilde_next,
-                                                       seq_len_next, ws, k_tilde_cur, len_old_cur) + outs), outs
-    _check(lib().sda_decode_step(*args[:-1], _stream(stream)))
+        return PreparedCall(name, args, (q, k, v, seq_len, block_idx, n_sel, f_next, k_tilde_next, seq_len_next, ws,
+                                         k_tilde_cur, len_old_cur) + outs), outs
+    _check(getattr(lib(), name)(*args[:-1], _stream(stream)))
     return outs
+
+
+def sda_decode_step_noalloc(q, k, v, seq_len, block_idx, n_sel, f_next, k_tilde_next, seq_len_next, n_init,
+                            n_local, top_k, **kw):
+    """sda_decode_step without a workspace: the library's static per-device
+    scratch holds the split partials, counters and candidate lists (for
+    callers that cannot allocate).  Same arguments and results as
+    sda_decode_step, minus ws; calls that overlap on one GPU race."""
+    if "ws" in kw:
+        raise TypeError("sda_decode_step_noalloc takes no workspace")
+    return sda_decode_step(q, k, v, seq_len, block_idx, n_sel, f_next, k_tilde_next, seq_len_next, n_init, n_local,
+                           top_k, _noalloc=True, **kw)
 
 
 def sda_grouped_decode(q, k, v, seq_len, block_idx, n_sel, group_C, mode=SDA_GROUP_EXACT, scale=None,

@@ -715,6 +715,43 @@ sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const 
     return run_step(c, sp, w, static_cast<hipStream_t>(stream));
 }
 
+sda_status_t sda_decode_step_noalloc(const void* q, const void* k, const void* v, const int32_t* seq_len,
+                                     const int32_t* block_idx, const int32_t* n_sel, int n_sel_max, int T_cap,
+                                     int B, int H_q, int H_kv, int d, float scale, float* out, float* lse_opt,
+                                     int split_k, const void* f_next, const void* k_tilde_next,
+                                     const int32_t* seq_len_next, int NB_cap_next, int n_init, int n_local,
+                                     int top_k, int n_sel_max_next, int32_t* block_idx_next, int32_t* n_sel_next,
+                                     void* k_tilde_cur, const int32_t* len_old_cur, int max_new_tokens_cur,
+                                     int NB_cap_cur, void* stream) {
+    const StepCall c{q, k, v, seq_len, block_idx, n_sel, n_sel_max, T_cap, B, H_q, H_kv, d, scale, out, lse_opt,
+                     split_k, f_next, k_tilde_next, seq_len_next, NB_cap_next, n_init, n_local, top_k,
+                     n_sel_max_next, block_idx_next, n_sel_next, k_tilde_cur, len_old_cur, max_new_tokens_cur,
+                     NB_cap_cur};
+    TRY(check_step(c));
+    const StepPlan sp = step_plan(c);
+    // [counter region: decode counters | selection counters][split partials][candidate lists or scores]
+    const size_t dec_cnt = pad256((size_t)sp.tasks * sizeof(int));
+    const size_t sel_cnt = (size_t)B * H_kv * sizeof(int);
+    const size_t cand = (size_t)B * H_kv * score_chunks(NB_cap_next) * top_k * sizeof(uint64_t);
+    const size_t scores = (size_t)B * H_kv * NB_cap_next * sizeof(float);
+    const size_t data = pad256(sp.partial_bytes) + pad256(sp.fused ? cand : scores);
+    REQUIRE(dec_cnt + sel_cnt <= kNoallocCounterBytes && data <= kNoallocScratchBytes - kNoallocCounterBytes,
+            SDA_ERR_WORKSPACE,
+            "decode_step_noalloc: the call needs %zu bytes of counters and %zu of data; the static scratch holds "
+            "%zu and %zu (use sda_decode_step with a workspace)",
+            dec_cnt + sel_cnt, data, kNoallocCounterBytes, kNoallocScratchBytes - kNoallocCounterBytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* base = nullptr;
+    TRY(hip_status(noalloc_scratch(s, &base), "decode_step_noalloc: scratch set-up"));
+    char* dat = base + kNoallocCounterBytes;
+    float* part_ml = reinterpret_cast<float*>(dat);
+    float* part_o = part_ml + (size_t)sp.tasks * sp.plan.n_split * sp.rp * 2;
+    char* sel = dat + pad256(sp.partial_bytes);
+    StepScratch w{reinterpret_cast<int*>(base), part_ml, part_o, reinterpret_cast<float*>(sel),
+                  reinterpret_cast<uint64_t*>(sel), reinterpret_cast<int*>(base + dec_cnt)};
+    return run_step(c, sp, w, s);
+}
+
 size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap,
                                     int group_C, int mode, int split_k) {
     if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || group_C < 1 || H_q % H_kv || NB_cap < 1)

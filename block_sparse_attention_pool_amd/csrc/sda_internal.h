@@ -148,6 +148,15 @@ hipError_t attn_grant_lds();
 // after it is written and never changes results.
 hipError_t device_setup();
 
+// The no-allocation decode step's scratch: a static device array of
+// kNoallocScratchBytes per device, its first kNoallocCounterBytes reserved
+// for arrival counters.  noalloc_scratch() returns its device address on the
+// current device (looked up once per device; the first lookup also clears
+// the counter region with a fill kernel on stream s).
+constexpr size_t kNoallocScratchBytes = (size_t)8 << 20;
+constexpr size_t kNoallocCounterBytes = (size_t)64 << 10;
+hipError_t noalloc_scratch(hipStream_t s, char** ptr);
+
 // ---- offload gather -----------------------------------------------------------------
 hipError_t launch_gather(const uint16_t* k_src, const uint16_t* v_src, const int32_t* block_idx,
                          const int32_t* n_sel, int n_sel_max, int B, int H_kv, int d, int T_cap,

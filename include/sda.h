@@ -311,6 +311,31 @@ sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const 
                              int NB_cap_cur, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sda_decode_step without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  Arguments, results and errors are those
+ * of sda_decode_step (same kernels, same launch plan, bit-identical
+ * results).  The scratch the kernels need (split partials, arrival counters,
+ * per-chunk candidate lists or scores) lives in a static device array of
+ * SDA_NOALLOC_SCRATCH_BYTES per device (its first 64 KiB are arrival
+ * counters), held until the process ends; a call whose scratch would not fit
+ * returns SDA_ERR_WORKSPACE and launches nothing.  The call allocates nothing:
+ * its first call on a device looks up the array's address and clears its
+ * counter region with a fill kernel on `stream`.  Every call on a device
+ * shares that device's array: calls that overlap in time on one GPU race
+ * (order them on one stream).
+ */
+#define SDA_NOALLOC_SCRATCH_BYTES (8u << 20)
+sda_status_t sda_decode_step_noalloc(const void* q, const void* k, const void* v, const int32_t* seq_len,
+                                     const int32_t* block_idx, const int32_t* n_sel, int n_sel_max, int T_cap,
+                                     int B, int H_q, int H_kv, int d, float scale, float* out, float* lse_opt,
+                                     int split_k, const void* f_next, const void* k_tilde_next,
+                                     const int32_t* seq_len_next, int NB_cap_next, int n_init, int n_local,
+                                     int top_k, int n_sel_max_next, int32_t* block_idx_next, int32_t* n_sel_next,
+                                     void* k_tilde_cur, const int32_t* len_old_cur, int max_new_tokens_cur,
+                                     int NB_cap_cur, void* stream);
+
+/*
  * Offloaded-KV gather ([SparDA] §4.2 steps 3 and 6, §4.5): copy the K and V
  * rows of each row's selected blocks from pinned host memory into a compact
  * device staging buffer, with GPU loads over the host link, on the caller's

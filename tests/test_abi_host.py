@@ -38,7 +38,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = header_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
         assert n in sda.exported_symbols(), n
@@ -424,3 +424,15 @@ def test_binding_checks_workspace_and_gather_shapes(L):
         sda.sda_gather_blocks(kh, kh, bi, ns, slot=torch.zeros((B, H_kv, 4), dtype=torch.int32))
     with pytest.raises(ValueError, match="pinned"):                        # shapes right, not pinned
         sda.sda_gather_blocks(kh, kh, bi, ns)
+
+
+def test_noalloc_step_rejects_sizes_beyond_its_scratch(L):
+    # 512 rows x 8 splits of partials (34 MB) exceed the 8 MiB static
+    # scratch: refused on the host, nothing launched
+    f = L.sda_decode_step_noalloc
+    args = [P, P, P, P, P, P, 35, 4096, 64, 64, 8, 128, ctypes.c_float(128 ** -0.5), P, P, 8,
+            P, P, P, 64, 1, 2, 32, 35, P + 4096, P + 8192, None, None, 0, 0, None]
+    assert f(*args) == WS
+    assert "static scratch" in _last()
+    bad = list(args); bad[0] = None                                        # null q: refused first
+    assert f(*bad) == NULL
