@@ -68,7 +68,12 @@ def build_layers(cfg, n_layers, dev):
     layers = []
     for l in range(n_layers):
         t0 = time.time()
-        K, V, _ = inputs.kv_layer(cfg, l, device=dev)
+        # the 8B-shaped workload biases 5 % of each row's blocks along the
+        # direction of the indexer vectors that select them (the previous
+        # layer's in the ring: layer l-1's vectors score layer l's keys)
+        dirs = (inputs.bias_directions(inputs.indexer_vectors(cfg, (l - 1) % n_layers)) if cfg.bias_frac > 0
+                else None)
+        K, V, _ = inputs.kv_layer(cfg, l, device=dev, bias_dirs=dirs)
         kt = torch.zeros((cfg.B, cfg.H_kv, cfg.NB, cfg.d), dtype=torch.bfloat16, device=dev)
         lo = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
         hi = torch.full((cfg.B,), cfg.T, dtype=torch.int32, device=dev)
@@ -82,52 +87,100 @@ def build_layers(cfg, n_layers, dev):
     return layers
 
 
-def cpu_baseline(cfg, layers, budget_s=12.0, n_rows=16):
-    """Time the CPU oracle's per-step work (scores, top-k, block set,
-    attention) on a sample of the same workload: the first n_rows (batch, KV
-    head) rows of layer 1, scored by the indexer vectors of every layer of
-    the ring in turn, until about budget_s seconds of timed work.  Building
-    the oracle's compressed keys is setup, not timed."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads():
+    """Worker threads for the CPU baseline: the cores this process may run
+    on, capped at the GPU's host CPU share (16)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+_CPU_ROW = {}
+
+
+def _cpu_row_init(cid, b, g, n_layers):
+    """Worker set-up (untimed): one (batch, KV head) row of the workload with
+    its keys and values drawn on the host (N(0,1), rounded to bf16: the
+    workload's distributions; the GPU run's device draws are not reproduced
+    here), the oracle's compressed keys of it, and the row's indexer vectors
+    of every ring layer and its query heads (the same host draws the GPU run uses)."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
+        _CPU_ROW["limiter"] = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
-        limiter = None
-    L = len(layers)
-    ln = layers[1 % L]
-    G, T = cfg.G, cfg.T
+        pass
+    torch.set_num_threads(1)
+    cfg = synth.get_config(cid)
+    rng = np.random.Generator(np.random.PCG64(inputs.derive_seed(cid, "cpu_baseline_kv", b, g)))
+    kv = [O.bf16_to_f64(inputs.bf16_bits(inputs.to_bf16(rng.standard_normal((cfg.T, cfg.d), dtype=np.float32))))
+          for _ in range(2)]
+    _CPU_ROW.update(cfg=cfg, k=kv[0], v=kv[1], kt=O.store_bf16(O.compressed_keys(kv[0], cfg.T)),
+                    f=[O.bf16_to_f64(inputs.bf16_bits(inputs.to_bf16(inputs.indexer_vectors(cfg, l)[b, 0, g])))
+                       for l in range(n_layers)],
+                    q=O.bf16_to_f64(inputs.bf16_bits(inputs.to_bf16(
+                        inputs.attention_queries(cfg, 1)[b, 0, g * cfg.G:(g + 1) * cfg.G]))))
+
+
+def _cpu_row_run(budget_s):
+    """Repeat the oracle's per-step work on this worker's row (scores, top-k,
+    block set, attention of the row's query heads), one ring layer's indexer
+    vector after another, for about budget_s seconds; returns (row-steps, seconds)."""
+    import oracle as O
+    r = _CPU_ROW
+    cfg = r["cfg"]
     scale = 1.0 / math.sqrt(cfg.d)
-    rows = [(b, g) for b in range(cfg.B) for g in range(cfg.H_kv)][:n_rows]
-    Qd = O.bf16_to_f64(inputs.bf16_bits(ln["Q"]))
-    Fds = [O.bf16_to_f64(inputs.bf16_bits(l["F"])) for l in layers]
-    data = {}
-    for (b, g) in rows:
-        kk = O.bf16_to_f64(inputs.bf16_bits(ln["K"][b, g]))
-        vv = O.bf16_to_f64(inputs.bf16_bits(ln["V"][b, g]))
-        data[(b, g)] = (kk, vv, O.store_bf16(O.compressed_keys(kk, T)))
-    timed, done, passes = 0.0, 0, 0
-    while timed < budget_s:
-        Fd = Fds[passes % L]
-        for (b, g) in rows:
-            kk, vv, kt = data[(b, g)]
-            t0 = time.perf_counter()
-            blocks, _ = O.select_row(Fd[b, 0, g], kt, cfg.n_init, cfg.n_local, cfg.top_k)
-            O.decode_row(Qd[b, 0, g * G:(g + 1) * G], kk, vv, blocks, T, scale)
-            timed += time.perf_counter() - t0
-            done += 1
-        passes += 1
-    if limiter is not None and hasattr(limiter, "unregister"):
-        limiter.unregister()
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        blocks, _ = O.select_row(r["f"][done % len(r["f"])], r["kt"], cfg.n_init, cfg.n_local, cfg.top_k)
+        O.decode_row(r["q"], r["k"], r["v"], blocks, cfg.T, scale)
+        done += 1
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(cfg, n_layers, budget_s=12.0):
+    """Time the CPU oracle's per-step work on a sample of the workload: one
+    (batch, KV head) row per worker process, all workers at once for about
+    budget_s seconds.  Called before the process touches the GPU, so the
+    workers are plain forks of a process without GPU state."""
+    import multiprocessing as mp
+    nthr = cpu_threads()
+    rows = [(b, g) for b in range(cfg.B) for g in range(cfg.H_kv)][:nthr]
+    ctx = mp.get_context("fork")
+    pools = [ctx.Pool(1, initializer=_cpu_row_init, initargs=(cfg.cid, b, g, n_layers)) for (b, g) in rows]
+    try:
+        for p in pools:                                    # set-up finished everywhere before timing
+            p.apply(time.time)
+        t0 = time.perf_counter()
+        res = [p.apply_async(_cpu_row_run, (budget_s,)) for p in pools]
+        got = [r.get() for r in res]
+        wall = time.perf_counter() - t0
+    finally:
+        for p in pools:
+            p.terminate()
+    done = sum(d for d, _ in got)
     return {
-        "value": done / timed / cfg.H_kv,
+        "value": done / wall / cfg.H_kv,
         "unit": "queries/s",
-        "cores": 1,
+        "cores": len(rows),
         "kind": "oracle",
-        "sample": f"{len(rows)} (batch, KV head) rows of the 128K workload x {passes} passes "
-                  f"(indexer vectors of each ring layer in turn) = {done} row-steps, {timed:.1f} s timed; "
-                  f"float64 NumPy on one thread; per row: scores, top-k, block set, attention of "
-                  f"{cfg.G} heads; a query = one sequence's {cfg.H_kv} KV heads",
+        "cpu": cpu_model(),
+        "sample": f"{len(rows)} (batch, KV head) rows of the {cfg.T // 1024}K workload, one per worker process "
+                  f"({len(rows)} of the {len(os.sched_getaffinity(0))} cores the process may use, capped at the "
+                  f"GPU's 16-core host share), {done} row-steps in {wall:.1f} s of wall time; float64 NumPy, one "
+                  f"BLAS thread per worker; per row-step: scores, top-k, block set, attention of {cfg.G} heads "
+                  f"(indexer vectors of each ring layer in turn); keys and values drawn on the host with the "
+                  f"workload's distributions; a query = one sequence's {cfg.H_kv} KV heads",
     }
 
 
@@ -248,10 +301,65 @@ def measure_rows(cfg, layers):
         "us": t_mh * 1e6, "roofline": hbm(cfg.ktilde_bytes(), t_mh),
         "oracle_rows_per_s": 1.0 / t_or, "gpu_rows_per_s": nrow / t_mh,
     }
+    rows["c2_step"] = measure_step_config(2)
     rows["n1_pooled_select"] = measure_pooled(cfg, layers, O, full, prev)
     rows["a5_grouped"] = measure_grouped(O)
     rows["a6_offload"] = measure_offload(O)
     return rows
+
+
+def measure_step_config(cid, n_layers=8):
+    """The decode step (sda_decode_step: layer l's decode and layer l+1's
+    scoring and selection in one launch) at another workload, over a ring of
+    resident layers like the headline, and the two calls it replaces."""
+    cfg = synth.get_config(cid)
+    dev = "cuda"
+    layers = build_layers(cfg, n_layers, dev)
+    L = len(layers)
+    seq = torch.full((cfg.B,), cfg.T, dtype=torch.int32, device=dev)
+    nsm = cfg.n_init + cfg.n_local + cfg.top_k
+    bi = [torch.empty((cfg.B, 1, cfg.H_kv, nsm), dtype=torch.int32, device=dev) for _ in range(L)]
+    ns = [torch.empty((cfg.B, 1, cfg.H_kv), dtype=torch.int32, device=dev) for _ in range(L)]
+    for i in range(L):
+        sda.sda_score_select(layers[(i - 1) % L]["F"], layers[i]["kt"], seq, cfg.n_init, cfg.n_local, cfg.top_k,
+                             block_idx=bi[i], n_sel=ns[i])
+    out = torch.empty((cfg.B, 1, cfg.H_q, cfg.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, 1, cfg.H_q), dtype=torch.float32, device=dev)
+    ws = torch.zeros(sda.lib().sda_decode_step_workspace(cfg.B, cfg.H_q, cfg.H_kv, cfg.d, nsm, 0, cfg.NB,
+                                                         cfg.top_k), dtype=torch.uint8, device=dev)
+    ws_sel = torch.zeros(sda.lib().sda_score_select_workspace(cfg.B, 1, cfg.H_kv, cfg.NB, cfg.top_k),
+                         dtype=torch.uint8, device=dev)
+    ws_dec = torch.zeros(max(16, sda.lib().sda_sparse_decode_workspace(cfg.B, 1, cfg.H_q, cfg.H_kv, nsm, cfg.d, 0)),
+                         dtype=torch.uint8, device=dev)
+    steps, sels, decs = [], [], []
+    for i in range(L):
+        lc, ln = layers[i], layers[(i + 1) % L]
+        pc, _ = sda.prepare(sda.sda_decode_step, lc["Q"], lc["K"], lc["V"], seq, bi[i], ns[i], lc["F"], ln["kt"],
+                            seq, cfg.n_init, cfg.n_local, cfg.top_k, block_idx_next=bi[(i + 1) % L],
+                            n_sel_next=ns[(i + 1) % L], out=out, lse=lse, ws=ws)
+        steps.append(pc)
+        sc, _ = sda.prepare(sda.sda_score_select, lc["F"], ln["kt"], seq, cfg.n_init, cfg.n_local, cfg.top_k,
+                            block_idx=bi[(i + 1) % L], n_sel=ns[(i + 1) % L], ws=ws_sel)
+        dc, _ = sda.prepare(sda.sda_sparse_decode, lc["Q"], lc["K"], lc["V"], seq, bi[i], ns[i], out=out, lse=lse,
+                            ws=ws_dec)
+        sels.append(sc)
+        decs.append(dc)
+    t_step = call_time(steps, 30)
+    t_sel = call_time(sels, 30)
+    t_dec = call_time(decs, 30)
+    step_bytes = cfg.selected_kv_bytes() + cfg.ktilde_bytes()
+    res = {
+        "workload": f"{cfg.name}: B={cfg.B}, H_q={cfg.H_q}, H_kv={cfg.H_kv}, d={cfg.d}, T={cfg.T}, "
+                    f"{cfg.n_init} init + {cfg.n_local} local + top-{cfg.top_k}, 5 % of blocks biased along "
+                    f"the indexer direction, ring of {L} resident layers",
+        "step_us": t_step * 1e6, "step_roofline": hbm(step_bytes, t_step),
+        "queries_per_s": cfg.B / t_step,
+        "score_select_us": t_sel * 1e6, "score_select_roofline": hbm(cfg.ktilde_bytes(), t_sel),
+        "sparse_decode_us": t_dec * 1e6, "sparse_decode_roofline": hbm(cfg.selected_kv_bytes(), t_dec),
+    }
+    del layers
+    torch.cuda.empty_cache()
+    return res
 
 
 def measure_pooled(cfg, layers, O, full, prev, window=32, stride=16):
@@ -316,129 +424,225 @@ def measure_pooled(cfg, layers, O, full, prev, window=32, stride=16):
     return res
 
 
-def chain_lists(rng, NB, n, C, keep):
-    """Block lists of C consecutive queries built as a chain: query c+1 keeps
-    `keep` of query c's n blocks and adds n - keep blocks new to the group, so
-    the group's union has exactly n + (C - 1)(n - keep) blocks."""
-    pool = rng.permutation(NB)
-    used = n
-    lists = [np.sort(pool[:n])]
-    for _ in range(1, C):
-        kept = rng.choice(lists[-1], keep, replace=False)
-        new = pool[used:used + n - keep]
-        used += n - keep
-        lists.append(np.sort(np.concatenate([kept, new])))
-    return lists
+def adjacent_overlap(bi_np, C):
+    """Mean share of a query's blocks that the next query of its group also
+    selects (lists [B, NQ, H_kv, n], full rows)."""
+    B, NQ, H, n = bi_np.shape
+    vals = []
+    for b in range(B):
+        for g in range(H):
+            for q0 in range(0, NQ, C):
+                for c in range(q0, min(q0 + C, NQ) - 1):
+                    vals.append(len(np.intersect1d(bi_np[b, c, g], bi_np[b, c + 1, g])) / n)
+    return float(np.mean(vals))
 
 
-def measure_grouped(O):
-    """a5 at the draft-verification workload: C = 4 queries per group share one
-    pass over their merged block set (gamma = 0.75 by chain construction)."""
+def distinct_blocks(bi_np, C=None):
+    """Distinct (batch, KV head, block) tiles among the lists; with C, only
+    each group's first list (the shared representative)."""
+    B, NQ, H, n = bi_np.shape
+    tot = 0
+    for b in range(B):
+        for g in range(H):
+            rows = bi_np[b, ::C, g] if C else bi_np[b, :, g]
+            tot += np.unique(rows).size
+    return tot
+
+
+def grouped_lists(cfg, kt, seq, gamma, n_sets):
+    """Draft-query block lists of the verification workload whose adjacent
+    queries share about gamma of their blocks: sigma (the draft noise of the
+    indexer vectors) bisected on the library's own selections, then n_sets
+    independent list sets at that sigma."""
+    dev = "cuda"
+
+    def select(sigma, layer):
+        F = inputs.to_bf16(inputs.indexer_vectors(cfg, layer, sigma=sigma), dev)
+        bi, _ = sda.sda_score_select(F, kt, seq, 0, 0, cfg.top_k)
+        return bi
+    lo, hi = 0.0, 4.0
+    for _ in range(16):
+        mid = 0.5 * (lo + hi)
+        ov = adjacent_overlap(select(mid, 0).cpu().numpy(), cfg.group_C)
+        lo, hi = (mid, hi) if ov > gamma else (lo, mid)
+    sigma = 0.5 * (lo + hi)
+    return sigma, [select(sigma, s) for s in range(n_sets)]
+
+
+def profile_grouped(reps=4):
+    """Eager launches for hardware-counter runs at the verification workload
+    (gamma = 0.75): the per-query decode, mode A, mode B and NSA's three
+    branches, `reps` launches each in that order, on independent list sets."""
     cfg = synth.get_config(4)
     dev = "cuda"
     K, V, _ = inputs.kv_layer(cfg, 0, device=dev)
-    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0, sigma=0.5), dev)
     n, C = cfg.top_k, cfg.group_C
-    keep = int(round(0.75 * n))
-    rng = np.random.default_rng(20260624 + 4)
-    # independent list sets, used in turn: their blocks together exceed the
-    # 256 MB Infinity Cache, so repeated calls read HBM
-    n_sets = 6
-    sets = []
-    for _ in range(n_sets):
-        bi_np = np.zeros((cfg.B, cfg.NQ, cfg.H_kv, n), dtype=np.int32)
-        for b in range(cfg.B):
-            for g in range(cfg.H_kv):
-                for grp in range(cfg.NQ // C):
-                    for c, lst in enumerate(chain_lists(rng, cfg.NB, n, C, keep)):
-                        bi_np[b, grp * C + c, g] = lst
-        sets.append(bi_np)
-    bi_np = sets[0]
-    bis = [torch.from_numpy(x).to(dev) for x in sets]
-    ns = torch.full((cfg.B, cfg.NQ, cfg.H_kv), n, dtype=torch.int32, device=dev)
     seq = torch.full((cfg.B,), cfg.T, dtype=torch.int32, device=dev)
+    zero = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+    kt = torch.zeros((cfg.B, cfg.H_kv, cfg.NB, cfg.d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kt)
+    sda.sda_update_compressed_keys(K, kt, zero, seq, cfg.T)
+    sda.sda_update_compressed_keys(V, vc, zero, seq, cfg.T)
+    sigma, bis = grouped_lists(cfg, kt, seq, 0.75, reps)
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0, sigma=sigma), dev)
+    ns = torch.full((cfg.B, cfg.NQ, cfg.H_kv), n, dtype=torch.int32, device=dev)
+    gates = torch.rand((cfg.B, cfg.NQ, cfg.H_q, 3), generator=torch.Generator(device=dev).manual_seed(5),
+                       device=dev, dtype=torch.float32)
+    wss = {}
+    torch.cuda.synchronize()
+    log(f"profile_grouped: sigma {sigma:.4f}; launches in order: per-query x{reps}, mode A x{reps}, "
+        f"mode B x{reps}, NSA x{reps}")
+    for i in range(reps):
+        sda.sda_sparse_decode(Q, K, V, seq, bis[i], ns)
+    for mode in (sda.SDA_GROUP_EXACT, sda.SDA_GROUP_SHARED_REP):
+        for i in range(reps):
+            sda.sda_grouped_decode(Q, K, V, seq, bis[i], ns, C, mode=mode)
+    for i in range(reps):
+        sda.sda_nsa_decode(Q, K, V, kt, vc, seq, bis[i], ns, gates, 64, 512, group_C=C, mode=sda.SDA_GROUP_EXACT)
+    torch.cuda.synchronize()
+    blk = 64 * cfg.d * 2 * 2
+    bnp = [b.cpu().numpy() for b in bis]
+    print(json.dumps({"profile": "grouped", "gamma": 0.75, "sigma": sigma, "reps": reps,
+                      "distinct_bytes_per_query_or_mode_A": float(np.mean([distinct_blocks(b) for b in bnp])) * blk,
+                      "distinct_bytes_mode_B": float(np.mean([distinct_blocks(b, C) for b in bnp])) * blk}))
+
+
+def measure_grouped(O):
+    """a5 at the draft-verification workload (64K, 16 draft queries per
+    sequence in groups of C = 4): the queries' block lists come from the
+    library's own selection on draft indexer vectors f_c = f0 + sigma eps_c,
+    with sigma bisected so that adjacent queries of a group share gamma of
+    their top-16 blocks, gamma in {0.5, 0.75, 0.9}.  Per gamma: mode A (each
+    union block loaded once per group), mode B (the first query's list), the
+    per-query decode of the same lists, the blocks each launch loads and the
+    distinct (batch, KV head, block) tiles it touches (repeats across the
+    groups of a KV head are cache hits, so rooflines use distinct bytes), and
+    mode B's error against the exact per-query result (mode A)."""
+    cfg = synth.get_config(4)
+    dev = "cuda"
+    K, V, _ = inputs.kv_layer(cfg, 0, device=dev)
+    n, C = cfg.top_k, cfg.group_C
+    kt = torch.zeros((cfg.B, cfg.H_kv, cfg.NB, cfg.d), dtype=torch.bfloat16, device=dev)
+    seq = torch.full((cfg.B,), cfg.T, dtype=torch.int32, device=dev)
+    zero = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+    sda.sda_update_compressed_keys(K, kt, zero, seq, cfg.T)
+    blk = 64 * cfg.d * 2 * 2
+    n_sets = 6                 # independent list sets, used in turn: together they exceed the Infinity Cache
+    ns = torch.full((cfg.B, cfg.NQ, cfg.H_kv), n, dtype=torch.int32, device=dev)
     out = torch.empty((cfg.B, cfg.NQ, cfg.H_q, cfg.d), dtype=torch.float32, device=dev)
     lse = torch.empty((cfg.B, cfg.NQ, cfg.H_q), dtype=torch.float32, device=dev)
-    uc = torch.empty((cfg.B, cfg.NQ // C, cfg.H_kv), dtype=torch.int32, device=dev)
-    res = {"workload": f"{cfg.name}: B={cfg.B}, NQ={cfg.NQ}, C={C}, H_q={cfg.H_q}, H_kv={cfg.H_kv}, "
-                       f"T={cfg.T}, top-{n} per query, adjacent overlap gamma = {keep}/{n} (chain-built lists)"}
-    blk = 64 * cfg.d * 2 * 2
-    for mode, name in ((sda.SDA_GROUP_EXACT, "mode_A"), (sda.SDA_GROUP_SHARED_REP, "mode_B")):
-        ws = torch.zeros(sda.lib().sda_grouped_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d,
-                                                                cfg.NB, C, mode, 0), dtype=torch.uint8,
-                         device=dev)
+    uc_shape = (cfg.B, cfg.NQ // C, cfg.H_kv)
+
+    res = {"workload": f"{cfg.name}: B={cfg.B}, NQ={cfg.NQ}, C={C}, H_q={cfg.H_q}, H_kv={cfg.H_kv}, T={cfg.T}, "
+                       f"top-{n} per query from the library's selection on draft indexer vectors; adjacent "
+                       f"overlap gamma tuned by bisection on the draft noise", "gammas": {}}
+    groups = cfg.B * (cfg.NQ // C) * cfg.H_kv
+    for gamma in cfg.gammas:
+        sigma, bis = grouped_lists(cfg, kt, seq, gamma, n_sets)
+        bnp = [b.cpu().numpy() for b in bis]
+        measured = float(np.mean([adjacent_overlap(b, C) for b in bnp]))
+        Q = inputs.to_bf16(inputs.attention_queries(cfg, 0, sigma=sigma), dev)
+        row = {"sigma": sigma, "measured_gamma": measured}
+        per_q_blocks = cfg.B * cfg.NQ * cfg.H_kv * n
+        dist_all = float(np.mean([distinct_blocks(b) for b in bnp]))
+        dist_rep = float(np.mean([distinct_blocks(b, C) for b in bnp]))
+        outs = {}
+        for mode, name in ((sda.SDA_GROUP_EXACT, "mode_A"), (sda.SDA_GROUP_SHARED_REP, "mode_B")):
+            ws = torch.zeros(sda.lib().sda_grouped_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d,
+                                                                    cfg.NB, C, mode, 0), dtype=torch.uint8,
+                             device=dev)
+            ucs = [torch.empty(uc_shape, dtype=torch.int32, device=dev) for _ in range(n_sets)]
+            turn = [0]
+
+            def grouped_call():
+                i = turn[0] % n_sets
+                turn[0] += 1
+                sda.sda_grouped_decode(Q, K, V, seq, bis[i], ns, C, mode=mode, out=out, lse=lse,
+                                       union_count=ucs[i], ws=ws)
+            t = graph_time(grouped_call, copies=n_sets)
+            loaded = sum(int(u.sum().item()) for u in ucs) / n_sets
+            dist = dist_all if mode == sda.SDA_GROUP_EXACT else dist_rep
+            row[name] = {"us": t * 1e6, "blocks_loaded": loaded, "distinct_blocks": dist,
+                         "roofline": hbm(dist * blk, t), "roofline_loaded": hbm(loaded * blk, t)}
+            o, _, _ = sda.sda_grouped_decode(Q, K, V, seq, bis[0], ns, C, mode=mode, ws=ws)
+            outs[name] = o
+        ws = torch.zeros(sda.lib().sda_sparse_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d, 0),
+                         dtype=torch.uint8, device=dev)
         turn = [0]
 
-        def grouped_call():
+        def per_query_call():
             i = turn[0] % n_sets
             turn[0] += 1
-            sda.sda_grouped_decode(Q, K, V, seq, bis[i], ns, C, mode=mode, out=out, lse=lse,
-                                   union_count=ucs[i], ws=ws)
-        ucs = [torch.empty_like(uc) for _ in range(n_sets)]
-        t = graph_time(grouped_call, copies=n_sets)
-        blocks = sum(int(u.sum().item()) for u in ucs) / n_sets       # mean blocks per call
-        res[name] = {"us": t * 1e6, "blocks_loaded": blocks, "roofline": hbm(blocks * blk, t)}
-    # NSA's three branches in one launch (exact merge for the listed blocks,
-    # a 512-token window, 64/64 compressed keys and values, random gates)
+            sda.sda_sparse_decode(Q, K, V, seq, bis[i], ns, out=out, lse=lse, ws=ws)
+        t = graph_time(per_query_call, copies=n_sets)
+        row["per_query"] = {"us": t * 1e6, "blocks_loaded": per_q_blocks, "distinct_blocks": dist_all,
+                            "roofline": hbm(dist_all * blk, t), "roofline_loaded": hbm(per_q_blocks * blk, t)}
+        row["measured_saving_mode_A"] = 1.0 - row["mode_A"]["blocks_loaded"] / per_q_blocks
+        row["formula_saving"] = 1.0 - O.union_size_formula(n, C, measured) / (n * C)
+        row["speedup_mode_A_vs_per_query"] = row["per_query"]["us"] / row["mode_A"]["us"]
+        # mode B approximates: its error against the exact per-query result
+        dB = (outs["mode_B"] - outs["mode_A"]).abs()
+        row["mode_B_error_vs_exact"] = {"max_abs": dB.max().item(), "mean_abs": dB.mean().item(),
+                                        "rows_exact": float((dB.amax(dim=-1) == 0).float().mean().item())}
+        res["gammas"][f"{gamma:g}"] = row
+        log(f"grouped gamma {gamma}: sigma {sigma:.4f} measured {measured:.3f}; mode A {row['mode_A']['us']:.1f} us, "
+            f"mode B {row['mode_B']['us']:.1f} us, per-query {row['per_query']['us']:.1f} us; mode B max err "
+            f"{row['mode_B_error_vs_exact']['max_abs']:.3e}")
+        if gamma == 0.75:
+            sets75, Q75, dist75 = bis, Q, dist_all
+    # NSA's three branches in one launch at gamma = 0.75 (exact merge for the
+    # listed blocks, a 512-token window, 64/64 compressed keys and values,
+    # random gates)
     window = 512
-    seq_len_full = torch.full((cfg.B,), cfg.T, dtype=torch.int32, device=dev)
-    zero = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
     kc = torch.zeros((cfg.B, cfg.H_kv, cfg.NB, cfg.d), dtype=torch.bfloat16, device=dev)
     vc = torch.zeros_like(kc)
-    sda.sda_update_compressed_keys(K, kc, zero, seq_len_full, cfg.T)
-    sda.sda_update_compressed_keys(V, vc, zero, seq_len_full, cfg.T)
+    sda.sda_update_compressed_keys(K, kc, zero, seq, cfg.T)
+    sda.sda_update_compressed_keys(V, vc, zero, seq, cfg.T)
     gates = torch.rand((cfg.B, cfg.NQ, cfg.H_q, 3), generator=torch.Generator(device=dev).manual_seed(5),
                        device=dev, dtype=torch.float32)
     nsa_ws = torch.zeros(sda.lib().sda_nsa_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d, cfg.T,
                                                             cfg.NB, window, C, sda.SDA_GROUP_EXACT),
                          dtype=torch.uint8, device=dev)
-    nsa_out = torch.empty_like(out)
     nsa_lse = torch.empty((cfg.B, cfg.NQ, cfg.H_q, 3), dtype=torch.float32, device=dev)
-    ucs_n = [torch.empty_like(uc) for _ in range(n_sets)]
+    ucs_n = [torch.empty(uc_shape, dtype=torch.int32, device=dev) for _ in range(n_sets)]
     turn = [0]
 
     def nsa_call():
         i = turn[0] % n_sets
         turn[0] += 1
-        sda.sda_nsa_decode(Q, K, V, kc, vc, seq, bis[i], ns, gates, 64, window, group_C=C, mode=sda.SDA_GROUP_EXACT,
-                           out=nsa_out, lse=nsa_lse, union_count=ucs_n[i], ws=nsa_ws)
+        sda.sda_nsa_decode(Q75, K, V, kc, vc, seq, sets75[i], ns, gates, 64, window, group_C=C,
+                           mode=sda.SDA_GROUP_EXACT, out=out, lse=nsa_lse, union_count=ucs_n[i], ws=nsa_ws)
     t = graph_time(nsa_call, copies=n_sets)
-    groups = cfg.B * (cfg.NQ // C) * cfg.H_kv
     sel_blocks = sum(int(u.sum().item()) for u in ucs_n) / n_sets
     win_blocks = groups * (window // 64)
-    cmp_bytes = groups * cfg.NB * cfg.d * 2 * 2
-    nsa_bytes = (sel_blocks + win_blocks) * blk + cmp_bytes
-    res["nsa_three_branch"] = {
+    cmp_loaded = groups * cfg.NB * cfg.d * 2 * 2
+    # distinct: the window's last 8 blocks and the compressed keys and values
+    # once per (batch, KV head); window blocks also selected counted once
+    kv_rows = cfg.B * cfg.H_kv
+    win_dist = 0
+    for bnp in (sets75[0].cpu().numpy(),):
+        for b in range(cfg.B):
+            for g in range(cfg.H_kv):
+                sel = np.unique(bnp[b, :, g])
+                win_dist += np.setdiff1d(np.arange(cfg.NB - window // 64, cfg.NB), sel).size
+    dist_bytes = (dist75 + win_dist) * blk + kv_rows * cfg.NB * cfg.d * 2 * 2
+    res["nsa_three_branch_gamma_0.75"] = {
         "us": t * 1e6, "window": window, "compressed_keys_per_row": cfg.NB,
         "selected_blocks_loaded": sel_blocks, "window_blocks_loaded": win_blocks,
-        "roofline": hbm(nsa_bytes, t),
-        "extra_us_over_mode_A": t * 1e6 - res["mode_A"]["us"],
+        "distinct_bytes": int(dist_bytes), "roofline": hbm(dist_bytes, t),
+        "roofline_loaded": hbm((sel_blocks + win_blocks) * blk + cmp_loaded, t),
+        "extra_us_over_mode_A": t * 1e6 - res["gammas"]["0.75"]["mode_A"]["us"],
     }
-    del kc, vc
-    ws = torch.zeros(sda.lib().sda_sparse_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d, 0),
-                     dtype=torch.uint8, device=dev)
-    turn = [0]
-
-    def per_query_call():
-        i = turn[0] % n_sets
-        turn[0] += 1
-        sda.sda_sparse_decode(Q, K, V, seq, bis[i], ns, out=out, lse=lse, ws=ws)
-    t = graph_time(per_query_call, copies=n_sets)
-    per_q = cfg.B * cfg.NQ * cfg.H_kv * n
-    res["per_query"] = {"us": t * 1e6, "blocks_loaded": per_q, "roofline": hbm(per_q * blk, t)}
-    res["measured_saving_mode_A"] = 1.0 - res["mode_A"]["blocks_loaded"] / per_q
-    res["formula_saving"] = 1.0 - O.union_size_formula(n, C, keep / n) / (n * C)
-    res["speedup_mode_A_vs_per_query"] = res["per_query"]["us"] / res["mode_A"]["us"]
     # oracle: one group (C queries x G heads) of one (batch, KV head), mode A
     kk = O.bf16_to_f64(inputs.bf16_bits(K[0, 0, :cfg.T]))
     vv = O.bf16_to_f64(inputs.bf16_bits(V[0, 0, :cfg.T]))
-    qd = O.bf16_to_f64(inputs.bf16_bits(Q[0, :C, :cfg.G])).reshape(C, cfg.G, cfg.d)
-    lists = [bi_np[0, c, 0] for c in range(C)]
+    qd = O.bf16_to_f64(inputs.bf16_bits(Q75[0, :C, :cfg.G])).reshape(C, cfg.G, cfg.d)
+    b0 = sets75[0].cpu().numpy()
+    lists = [b0[0, c, 0] for c in range(C)]
     t_or = oracle_time(lambda: O.grouped_row(qd, kk, vv, lists, cfg.T, 1.0 / math.sqrt(cfg.d), O.MODE_EXACT))
-    groups = cfg.B * (cfg.NQ // C) * cfg.H_kv
     res["oracle_groups_per_s"] = 1.0 / t_or
-    res["gpu_groups_per_s"] = groups / (res["mode_A"]["us"] * 1e-6)
-    del K, V
+    res["gpu_groups_per_s_gamma_0.75"] = groups / (res["gammas"]["0.75"]["mode_A"]["us"] * 1e-6)
+    del K, V, kc, vc
     torch.cuda.empty_cache()
     return res
 
@@ -625,20 +829,34 @@ def main():
     ap.add_argument("--step-refresh", action="store_true",
                     help="the step launch also refreshes the decoded layer's compressed keys for its newest token")
     ap.add_argument("--call-reps", type=int, default=50, help="graph replays per per-call timing")
+    ap.add_argument("--profile", choices=("grouped",),
+                    help="only run eager launches of one row for hardware-counter runs, then exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the decode path has no multi-GPU mode "
               "(sharding is described in DESIGN.md, not built)", file=sys.stderr)
         sys.exit(2)
+    # counting devices does not initialise the GPU: the CPU baseline below
+    # forks its workers before anything does
+    if torch.cuda.device_count() < 1:
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    cfg = synth.get_config(args.config)
+    cpu = None
+    if not (args.no_cpu_baseline or args.copy_calibration or args.profile):
+        cpu = cpu_baseline(cfg, args.layers)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.profile == "grouped":
+        sda.lib()
+        profile_grouped()
+        return
 
-    cfg = synth.get_config(args.config)
     dev = "cuda"
     sda.lib()
     log(f"config {cfg.cid}: {cfg.name}; ring of {args.layers} layers")
@@ -838,8 +1056,8 @@ def main():
         "score_select_gbs": sel_bytes / t_sel.mean() / 1e9,
         "queries_per_s_from_kernels": queries / (t_sel.mean() + t_dec.mean()),
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, layers)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     if not args.no_rows:
         res["rows"] = measure_rows(cfg, layers)
     print(json.dumps(res))
