@@ -35,7 +35,10 @@ Readings of points the pages leave open (numbered as in the design notes):
   max over the compressed windows that share a token with it; NSA's
   compressed branch attends to every compressed entry present at length T,
   its window branch to the last w cached tokens, and the branch gates are
-  inputs (one triple per query head).
+  inputs (one triple per query head); in prefill every query position p
+  selects and attends as a decode step at length p + 1 would (per-token
+  selection, causal), with at least one local block so that every scored
+  block is complete.
 
 Parity pins: every function here is pinned by tests under tests/ against
 closed forms, brute force or an independent library routine, except the
@@ -433,3 +436,52 @@ def grouped_nsa_row(q_rows, k, v, kc, vc, lists, T, n_cmp, window, gates, scale,
     out = np.stack([nsa_row(q_rows[c], k, v, kc, vc, active[c], T, n_cmp, window, gates[c], scale)[0]
                     for c in range(C)])
     return out, ucount
+
+
+# ---------------------------------------------------------------------------
+# O14  prefill: block-sparse attention for every query position of a chunk
+#      ([SparDA] eq. (3): the block set B(i) is a function of the query
+#      position i, with the local window next to i; the complexity section's
+#      eq. (13), (15) and (16) count one selection over the N_b compressed
+#      blocks and one top-k attention per query token)
+# ---------------------------------------------------------------------------
+
+def prefill_lengths(pos0, nq):
+    """Tokens visible to each of the nq queries of a prefill chunk whose
+    first query sits at position pos0: query r (position pos0 + r) sees
+    tokens 0 .. pos0 + r, i.e. pos0 + r + 1 of them (causal)."""
+    return np.arange(int(pos0) + 1, int(pos0) + int(nq) + 1, dtype=np.int64)
+
+
+def prefill_select_rows(f_rows, kt_stored, pos0, n_init, n_local, k):
+    """Block sets of the nq query positions of one (sequence, KV head).
+
+    Query r at position p = pos0 + r chooses exactly as a decode step at
+    length p + 1: the blocks present are 0 .. p // 64, the local window is
+    the last n_local of them (the block holding p among them), and top-k
+    ranks the other blocks by f_r . K~_j.  With n_local >= 1 every block that
+    competes in top-k is complete at position p, so the compressed keys of
+    the whole sequence are the ones the query could have seen.
+    f_rows: float64 [nq, d]; kt_stored: [>= (pos0 + nq - 1) // 64 + 1, d].
+    Returns the list of ascending block-id arrays, one per query."""
+    if n_local < 1:
+        raise ValueError("prefill selection needs n_local >= 1 (the block holding the query is local)")
+    out = []
+    for r, T in enumerate(prefill_lengths(pos0, len(f_rows))):
+        nb = num_blocks(T)
+        blocks, _ = select_row(f_rows[r], kt_stored[:nb], n_init, n_local, k)
+        out.append(blocks)
+    return out
+
+
+def prefill_rows(q_rows, k, v, lists, pos0, scale):
+    """Causal block-sparse attention of every query of a prefill chunk:
+    query r (heads q_rows[r], [G, d]) attends to the tokens of its blocks
+    that lie at or before its position pos0 + r.  Returns (out [nq, G, d],
+    lse [nq, G])."""
+    outs, lses = [], []
+    for r, T in enumerate(prefill_lengths(pos0, len(q_rows))):
+        o, l = decode_row(q_rows[r], k, v, lists[r], T, scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)

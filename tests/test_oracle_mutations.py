@@ -266,3 +266,57 @@ def test_mutant_nsa_row(monkeypatch, kind):
         return out, br, lse
     _patch(monkeypatch, "nsa_row", bad)
     assert _fails(*_nsa_pins())
+
+
+# --- prefill -------------------------------------------------------------------
+def _prefill_pins():
+    from tests import test_oracle_prefill as pf
+    return [pf.test_prefill_lengths_hand_cases, pf.test_dense_selection_is_causal_attention,
+            pf.test_first_query_sees_only_token_zero,
+            _param_pin(pf.test_selection_brute_force_every_position, 1, 2, 3),
+            pf.test_each_query_matches_sdpa_on_its_gathered_causal_tokens, pf.test_nothing_after_a_query_matters,
+            pf.test_chunked_prefill_equals_whole]
+
+
+@pytest.mark.parametrize("shift", [-1, 1])
+def test_mutant_prefill_lengths_off_by_one(monkeypatch, shift):
+    def bad(pos0, nq):
+        return np.arange(int(pos0) + 1 + shift, int(pos0) + int(nq) + 1 + shift, dtype=np.int64)
+    _patch(monkeypatch, "prefill_lengths", bad)
+    assert _fails(*_prefill_pins())
+
+
+@pytest.mark.parametrize("kind", ["local_at_sequence_end", "all_blocks_scored", "pos0_ignored"])
+def test_mutant_prefill_select(monkeypatch, kind):
+    def bad(f_rows, kt_stored, pos0, n_init, n_local, k):
+        out = []
+        n_all = kt_stored.shape[0]
+        for r in range(len(f_rows)):
+            p = (0 if kind == "pos0_ignored" else pos0) + r
+            nb = p // 64 + 1
+            if kind == "local_at_sequence_end":
+                blocks, _ = impl.select_row(f_rows[r], kt_stored, n_init, n_local, k)
+                blocks = blocks[blocks < nb]
+            elif kind == "all_blocks_scored":
+                blocks, _ = impl.select_row(f_rows[r], kt_stored[:nb], n_init, 0, k)
+                blocks = np.array(sorted(set(blocks) | set(range(max(0, nb - n_local), nb))))
+            else:
+                blocks, _ = impl.select_row(f_rows[r], kt_stored[:nb], n_init, n_local, k)
+            assert n_all >= nb
+            out.append(blocks)
+        return out
+    _patch(monkeypatch, "prefill_select_rows", bad)
+    assert _fails(*_prefill_pins())
+
+
+def test_mutant_prefill_not_causal(monkeypatch):
+    def bad(q_rows, k, v, lists, pos0, scale):
+        T = k.shape[0]
+        outs, lses = [], []
+        for r in range(len(q_rows)):
+            o, l = impl.decode_row(q_rows[r], k, v, lists[r], T, scale)
+            outs.append(o)
+            lses.append(l)
+        return np.stack(outs), np.stack(lses)
+    _patch(monkeypatch, "prefill_rows", bad)
+    assert _fails(*_prefill_pins())
