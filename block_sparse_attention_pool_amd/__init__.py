@@ -68,6 +68,10 @@ _SIGNATURES = {
     "sda_decode_step": (_c_int, [_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_void_p, _c_void_p, _c_int]
                         + [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 4 + [_c_int] * 2
                         + [_c_void_p, _c_size_t, _c_void_p]),
+    "sda_prefill_select": (_c_int, [_c_void_p] * 3 + [_c_int] * 10 + [_c_void_p] * 3),
+    "sda_prefill_attention_workspace": (_c_size_t, [_c_int] * 7),
+    "sda_prefill_attention": (_c_int, [_c_void_p] * 6 + [_c_int] * 8 + [_c_float, _c_int] + [_c_void_p] * 3
+                              + [_c_size_t, _c_void_p]),
     "sda_decode_step_noalloc": (_c_int, [_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_void_p, _c_void_p, _c_int]
                                 + [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 4 + [_c_int] * 2
                                 + [_c_void_p]),
@@ -486,6 +490,44 @@ def sda_nsa_decode(q, k, v, k_cmp, v_cmp, seq_len, block_idx, n_sel, gates, cmp_
                                 NQ, H_q, H, d, float(scale), int(group_C), int(mode), _ptr(out), _ptr(lse),
                                 _ptr(union_count), _ptr(ws), wsb, _stream(stream)))
     return out, lse, union_count
+
+
+def sda_prefill_select(f, k_tilde, seq_len, pos0, n_init, n_local, top_k, n_sel_max=None, block_idx=None,
+                       n_sel=None, stream=None):
+    """Block sets of every query position of a prefill chunk (query r at
+    position pos0 + r chooses as a decode step at length pos0 + r + 1);
+    returns (block_idx, n_sel)."""
+    _need(f, "f", torch.bfloat16, 4)
+    B, NQ, H, d = f.shape
+    _need(k_tilde, "k_tilde", torch.bfloat16, (B, H, None, d))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    if n_sel_max is None:
+        n_sel_max = block_idx.shape[-1] if block_idx is not None else n_init + n_local + top_k
+    block_idx, n_sel = _select_outputs(B, NQ, H, n_sel_max, block_idx, n_sel, f.device)
+    _on_gpu(f=f, k_tilde=k_tilde, seq_len=seq_len, block_idx=block_idx, n_sel=n_sel)
+    _check(lib().sda_prefill_select(_ptr(f), _ptr(k_tilde), _ptr(seq_len), B, NQ, H, d, k_tilde.shape[2], int(pos0),
+                                    n_init, n_local, top_k, n_sel_max, _ptr(block_idx), _ptr(n_sel),
+                                    _stream(stream)))
+    return block_idx, n_sel
+
+
+def sda_prefill_attention(q, k, v, seq_len, block_idx, n_sel, pos0, scale=None, NB_cap=None, out=None, lse=None,
+                          ws=None, stream=None):
+    """Causal block-sparse attention of every query position of a prefill
+    chunk over its own blocks; returns (out, lse)."""
+    B, NQ, H_q, d, H_kv, T_cap, n_sel_max = _attn_inputs(q, k, v, seq_len, block_idx, n_sel)
+    if NB_cap is None:
+        NB_cap = -(-T_cap // BLOCK)
+    if scale is None:
+        scale = d ** -0.5
+    out, lse = _attn_outputs(B, NQ, H_q, d, out, lse, q.device)
+    nbytes = lib().sda_prefill_attention_workspace(B, NQ, H_q, H_kv, n_sel_max, d, int(NB_cap))
+    ws, wsb = _workspace(nbytes, q.device, ws)
+    _on_gpu(q=q, k=k, v=v, seq_len=seq_len, block_idx=block_idx, n_sel=n_sel, out=out, lse=lse, ws=ws)
+    _check(lib().sda_prefill_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(block_idx), _ptr(n_sel),
+                                       n_sel_max, T_cap, int(NB_cap), B, NQ, H_q, H_kv, d, float(scale), int(pos0),
+                                       _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(stream)))
+    return out, lse
 
 
 def sda_gather_blocks(k_host, v_host, block_idx, n_sel, k_stage=None, v_stage=None, slot=None,

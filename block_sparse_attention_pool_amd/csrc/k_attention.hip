@@ -435,6 +435,12 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
         for (int ks = 0; ks < KS; ++ks)
             asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[nt][ks]) : "v"(qp + ks * 32) : "memory");
     }
+    // prefill: the lane's row (query c of the group) sees tokens below
+    // pos0 + q0 + c + 1; a block below the group's first query is whole for every row
+    int lim[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) lim[nt] = a.prefill ? a.pos0 + q0 + min(rowq[nt], Cg - 1) + 1 : INT_MAX;
+    const int lim_min = a.prefill ? a.pos0 + q0 + 1 : INT_MAX;
     // the scalar reads are first used here, after every load above is issued
     asm volatile("" : "+s"(T), "+s"(n_g));
     if (glist) L.n = min(max(n_g, 0), a.n_sel_max);
@@ -497,7 +503,8 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
         const char* kb = reinterpret_cast<const char*>(kv_k + (size_t)phys * kBlock * D);
         const char* vb = reinterpret_cast<const char*>(kv_v + (size_t)phys * kBlock * D);
         const int tmax = nvalid - 1;
-        const bool full = (nvalid == kBlock) && (memb == 0xffffffffu) && tfirst == 0;   // wave-uniform
+        const bool full = (nvalid == kBlock) && (memb == 0xffffffffu) && tfirst == 0 &&
+                          j * kBlock + kBlock <= lim_min;                               // wave-uniform
 
         // ---- K into registers (MFMA A layout), then V into LDS by direct loads;
         //      everything is in flight before the first wait, and QK and the
@@ -552,11 +559,12 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
         for (int nt = 0; nt < NT; ++nt) {
             if (!full) {
                 const bool live = (memb >> rowq[nt]) & 1u;
+                const int tv = min(nvalid, lim[nt] - j * kBlock);     // tokens of the block this row sees
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (!(live && tok_of(mt, lg * 4 + i) < nvalid && tok_of(mt, lg * 4 + i) >= tfirst))
+                        if (!(live && tok_of(mt, lg * 4 + i) < tv && tok_of(mt, lg * 4 + i) >= tfirst))
                             s[mt][nt][i] = -INFINITY;
             }
             float mx = -INFINITY;
@@ -759,7 +767,7 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
             return;
         }
     }
-    const int task = blockIdx.y;
+    const int task = a.task0 + (int)blockIdx.y;
     const int split = blockIdx.x;
     const int g = task % a.H_kv;
     const int t2 = task / a.H_kv;
@@ -880,6 +888,7 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
 int attn_rows_pad(int C, int G) { return (C * G <= 16) ? 16 : 32; }
 
 constexpr size_t kLdsPerCU = 160 * 1024;
+constexpr int kMaxGridRows = 65535;
 
 
 // Launch shape of the attention kernel: W waves per workgroup, n_split
@@ -965,8 +974,18 @@ static hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     const bool ref = step && a.step.ref_kt != nullptr;
     auto kern = ref ? attn_kernel<D, NT, true, false, true>
                     : step ? attn_kernel<D, NT, true> : a.nsa ? attn_kernel<D, NT, false, true> : attn_kernel<D, NT, false>;
-    hipLaunchKernelGGL(kern, dim3(a.n_split, tasks + extra_rows), dim3(a.waves * kWave), smem, s, aa);
-    return hipGetLastError();
+    if (step) {
+        hipLaunchKernelGGL(kern, dim3(a.n_split, tasks + extra_rows), dim3(a.waves * kWave), smem, s, aa);
+        return hipGetLastError();
+    }
+    // grid rows are row groups; a launch covers at most 65535 of them
+    for (int t0 = 0; t0 < tasks; t0 += kMaxGridRows) {
+        aa.task0 = t0;
+        hipLaunchKernelGGL(kern, dim3(a.n_split, min(kMaxGridRows, tasks - t0)), dim3(a.waves * kWave), smem, s, aa);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int D, int NT>

@@ -752,6 +752,95 @@ sda_status_t sda_decode_step_noalloc(const void* q, const void* k, const void* v
     return run_step(c, sp, w, s);
 }
 
+// ---------------------------------------------------------------------------
+// prefill: per-token selection and causal block-sparse attention
+sda_status_t sda_prefill_select(const void* f, const void* k_tilde, const int32_t* seq_len, int B, int NQ, int H_kv,
+                                int d, int NB_cap, int pos0, int n_init, int n_local, int top_k, int n_sel_max,
+                                int32_t* block_idx, int32_t* n_sel, void* stream) {
+    REQUIRE(f, SDA_ERR_NULL, "prefill_select: f is null");
+    TRY(check_select_common(k_tilde, seq_len, B, NQ, H_kv, d, NB_cap, n_init, n_local, top_k, n_sel_max, block_idx,
+                            n_sel));
+    REQUIRE(aligned16(f), SDA_ERR_ALIGN, "f must be 16-byte aligned");
+    REQUIRE(n_local >= 1, SDA_ERR_SHAPE, "prefill_select: n_local=%d; the block holding a query must be local (>= 1)",
+            n_local);
+    REQUIRE(pos0 >= 0, SDA_ERR_SHAPE, "pos0=%d < 0", pos0);
+    REQUIRE((long long)pos0 + NQ <= (long long)kBlock * NB_cap, SDA_ERR_SHAPE,
+            "positions up to %lld exceed the compressed-key capacity of %lld tokens", (long long)pos0 + NQ - 1,
+            (long long)kBlock * NB_cap);
+    REQUIRE((long long)pos0 + NQ <= (long long)kBlock * kPrefillMaxBlocks, SDA_ERR_UNSUPPORTED,
+            "prefill_select keeps a query's block scores in registers: positions must stay below %d",
+            kBlock * kPrefillMaxBlocks);
+    const PrefillSelectArgs a{static_cast<const uint16_t*>(f), static_cast<const uint16_t*>(k_tilde), seq_len, B, NQ,
+                              H_kv, NB_cap, pos0, n_init, n_local, top_k, n_sel_max, block_idx, n_sel};
+    return hip_status(launch_prefill_select(a, d, static_cast<hipStream_t>(stream)), "prefill_select launch");
+}
+
+// prefill attention runs the grouped engine in exact mode on groups of
+// C consecutive query positions (C * G <= 32 rows per workgroup, C <= 8)
+static int prefill_group(int G) { return std::max(1, std::min(8, 32 / G)); }
+
+size_t sda_prefill_attention_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap) {
+    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv || H_q / H_kv > 32 || n_sel_max < 1 || NB_cap < 1)
+        return 0;
+    return sda_grouped_decode_workspace(B, NQ, H_q, H_kv, n_sel_max, d, NB_cap, prefill_group(H_q / H_kv),
+                                        SDA_GROUP_EXACT, 0);
+}
+
+sda_status_t sda_prefill_attention(const void* q, const void* k, const void* v, const int32_t* seq_len,
+                                   const int32_t* block_idx, const int32_t* n_sel, int n_sel_max, int T_cap,
+                                   int NB_cap, int B, int NQ, int H_q, int H_kv, int d, float scale, int pos0,
+                                   float* out, float* lse_opt, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_attn_common(q, k, v, seq_len, block_idx, n_sel, n_sel_max, T_cap, B, NQ, H_q, H_kv, d, scale, out, 0));
+    REQUIRE(pos0 >= 0 && (long long)pos0 + NQ <= T_cap, SDA_ERR_SHAPE,
+            "query positions [%d, %lld) must lie inside the cache capacity T_cap=%d", pos0, (long long)pos0 + NQ, T_cap);
+    REQUIRE(NB_cap >= ceil_div(T_cap, kBlock) && NB_cap <= kMaxNBCap, SDA_ERR_SHAPE,
+            "NB_cap=%d must lie in [ceil(T_cap/64), %d]", NB_cap, kMaxNBCap);
+    const int G = H_q / H_kv;
+    const int C = prefill_group(G);
+    const int n_groups = ceil_div(NQ, C);
+    const long long tasks = (long long)B * n_groups * H_kv;
+    REQUIRE(tasks <= (1LL << 31) - 1, SDA_ERR_SHAPE, "too many row groups");
+    const int rp = attn_rows_pad(C, G);
+    const AttnPlan plan = attn_plan(d, rp, (int)tasks, grouped_list_estimate(C, SDA_GROUP_EXACT, n_sel_max), C,
+                                    SDA_GROUP_EXACT, NB_cap, n_sel_max, 0);
+    const size_t lds = attn_smem_bytes_host(d, rp, plan.waves, C, SDA_GROUP_EXACT, NB_cap, n_sel_max);
+    REQUIRE(lds <= kLdsBytes, SDA_ERR_UNSUPPORTED, "group needs %zu bytes of LDS", lds);
+    const size_t need = attn_ws_bytes((int)tasks, plan.n_split, rp, d);
+    REQUIRE(need == 0 || (ws && ws_bytes >= need), SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
+            ws ? ws_bytes : 0, need);
+    REQUIRE(need == 0 || aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    AttnArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.seq_len = seq_len;
+    a.block_idx = block_idx;
+    a.n_sel = n_sel;
+    a.slot = nullptr;
+    a.out = out;
+    a.lse = lse_opt;
+    a.union_count = nullptr;
+    set_workspace(a, ws, need, (int)tasks, plan.n_split, rp);
+    a.n_sel_max = n_sel_max;
+    a.T_cap = T_cap;
+    a.NB_cap = NB_cap;
+    a.B = B;
+    a.NQ = NQ;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.G = G;
+    a.d = d;
+    a.C = C;
+    a.mode = SDA_GROUP_EXACT;
+    a.n_groups = n_groups;
+    a.n_split = plan.n_split;
+    a.waves = plan.waves;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.prefill = 1;
+    a.pos0 = pos0;
+    return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)), "prefill_attention launch");
+}
+
 size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap,
                                     int group_C, int mode, int split_k) {
     if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || group_C < 1 || H_q % H_kv || NB_cap < 1)

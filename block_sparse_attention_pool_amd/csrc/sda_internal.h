@@ -69,6 +69,21 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 size_t multihead_ws_floats(int B, int NQ, int H_q, int H_kv, int NB_cap);
 int score_chunks(int NB_cap);
 
+// ---- prefill selection ----------------------------------------------------------
+// query r of a chunk sits at position pos0 + r; its block scores live in
+// registers, so the blocks a query sees are bounded (positions < 64 * 512)
+constexpr int kPrefillMaxBlocks = 512;
+struct PrefillSelectArgs {
+    const uint16_t* f;        // [B, NQ, H_kv, d] indexer vectors
+    const uint16_t* kt;       // [B, H_kv, NB_cap, d] compressed keys
+    const int32_t* seq_len;   // [B] cached tokens; queries at positions >= seq_len get no blocks
+    int B, NQ, H_kv, NB_cap, pos0;
+    int n_init, n_local, top_k, n_sel_max;
+    int32_t* block_idx;       // [B, NQ, H_kv, n_sel_max]
+    int32_t* n_sel;           // [B, NQ, H_kv]
+};
+hipError_t launch_prefill_select(const PrefillSelectArgs& a, int d, hipStream_t s);
+
 constexpr int kCUs = 256;                  // MI355X compute units
 
 // ---- attention ------------------------------------------------------------------
@@ -111,6 +126,9 @@ struct AttnArgs {
     int C;                    // queries per group (1 = plain decode)
     int mode;                 // 0 exact, 1 shared representative
     int n_groups;             // ceil(NQ / C)
+    int prefill;              // 1: query q sits at position pos0 + q and sees tokens 0 .. pos0 + q
+    int pos0;                 //    only (causal prefill); 0: every query sees the whole cache
+    int task0;                // first row group of this launch (launches cover at most 65535)
     int n_split;
     int waves;                // waves per workgroup
     float scale_log2;         // scale * log2(e)

@@ -311,6 +311,56 @@ sda_status_t sda_decode_step(const void* q, const void* k, const void* v, const 
                              int NB_cap_cur, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Prefill selection: a block set for every query position of a prefill
+ * chunk ([SparDA] eq. (3): the set is a function of the query position, the
+ * local window next to it; the complexity section's eq. (13) and (16) count
+ * one selection over the compressed blocks per query token).  Query r sits
+ * at position p = pos0 + r and chooses exactly as sda_score_select does for
+ * a sequence of p + 1 tokens: blocks 0 .. p / 64 exist, {0..n_init-1} and
+ * the last n_local of them are taken, and top-k ranks the others by
+ * f_r . K~_j (fp32 sums of exact bf16 products; ties to the lower block id);
+ * written ascending, padded with -1.  n_local >= 1 (the block holding the
+ * query is always local), so every ranked block is complete at p and the
+ * compressed keys of the whole sequence may be passed.
+ *
+ *   f          bf16 [B, NQ, H_kv, d]    one indexer vector per query position and KV head
+ *   k_tilde    bf16 [B, H_kv, NB_cap, d] (64 * NB_cap >= pos0 + NQ)
+ *   seq_len    i32  [B] cached tokens; a query at a position >= seq_len[b] gets no blocks
+ *   pos0       position of query 0 (0 for a whole-sequence prefill; chunked
+ *              prefill passes the chunk's start)
+ *   block_idx  i32  [B, NQ, H_kv, n_sel_max] out; n_sel i32 [B, NQ, H_kv] out
+ * Positions must stay below 32768 (a query's 512 block scores are kept in
+ * registers); beyond that the call returns SDA_ERR_UNSUPPORTED.
+ */
+sda_status_t sda_prefill_select(const void* f, const void* k_tilde, const int32_t* seq_len, int B, int NQ, int H_kv,
+                                int d, int NB_cap, int pos0, int n_init, int n_local, int top_k, int n_sel_max,
+                                int32_t* block_idx, int32_t* n_sel, void* stream);
+
+/*
+ * Prefill attention: causal block-sparse attention for every query position
+ * of a chunk ([SparDA] eq. (7) per query and the complexity section's eq.
+ * (15): each query token attends to its own k blocks): query r at position
+ * p = pos0 + r, head h, attends to the tokens of its listed blocks that lie
+ * at or before p.  Consecutive query positions share one pass over the union
+ * of their lists (the grouped engine of sda_grouped_decode in exact mode,
+ * groups of min(8, 32 / G) positions), each masked to its own list and its
+ * own position.
+ *
+ *   q          bf16 [B, NQ, H_q, d]
+ *   k, v       bf16 [B, H_kv, T_cap, d] (pos0 + NQ <= T_cap)
+ *   block_idx, n_sel  as sda_prefill_select writes them (ascending per row)
+ *   out f32 [B, NQ, H_q, d]; lse_opt f32 [B, NQ, H_q] or NULL
+ * A query with no visible token gets out = 0 and lse = -inf.
+ * Workspace: sda_prefill_attention_workspace() bytes (0 when one split per
+ * row group), with the zero-fill and no-overlap contract of sda_sparse_decode.
+ */
+size_t sda_prefill_attention_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap);
+sda_status_t sda_prefill_attention(const void* q, const void* k, const void* v, const int32_t* seq_len,
+                                   const int32_t* block_idx, const int32_t* n_sel, int n_sel_max, int T_cap,
+                                   int NB_cap, int B, int NQ, int H_q, int H_kv, int d, float scale, int pos0,
+                                   float* out, float* lse_opt, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * sda_decode_step without a workspace, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops and
  * harnesses that forbid hipMalloc.  Arguments, results and errors are those

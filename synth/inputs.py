@@ -186,3 +186,41 @@ def to_bf16(x, device="cpu"):
 
 def seq_lens(cfg, device="cpu"):
     return torch.full((cfg.B,), cfg.T, dtype=torch.int32, device=device)
+
+
+# --------------------------------------------------------------------------
+# prefill: indexer vectors and queries of every position of a sequence
+# --------------------------------------------------------------------------
+
+PREFILL_RHO = 0.96     # correlation of consecutive positions' indexer vectors
+
+
+def prefill_indexer_vectors(cfg, layer, nq, pos0=0, rho=PREFILL_RHO):
+    """Indexer vectors of nq consecutive positions, float32 numpy
+    [B, nq, H_kv, d]: per (b, KV head) a stationary first-order
+    autoregressive sequence with N(0, 1/d) marginals, f_t = rho f_{t-1} +
+    sqrt(1 - rho^2) e_t (consecutive positions' vectors correlate by rho, so
+    their selections overlap as neighbouring queries' do); positions
+    pos0 .. pos0 + nq - 1 of the sequence drawn from position 0."""
+    from scipy.signal import lfilter
+    B, H, d = cfg.B, cfg.H_kv, cfg.d
+    n = int(pos0) + int(nq)
+    out = np.empty((B, nq, H, d), dtype=np.float32)
+    c = np.sqrt(1.0 - rho * rho)
+    for b in range(B):
+        e = _row_rng(cfg.cid, "Fprefill", layer, b).standard_normal((n, H, d)) / np.sqrt(d)
+        e[0] /= c                                       # stationary start: f_0 = e_0
+        f = lfilter([c], [1.0, -rho], e, axis=0)
+        out[b] = f[pos0:].astype(np.float32)
+    return out
+
+
+def prefill_queries(cfg, layer, nq, device="cpu"):
+    """Attention queries of nq positions, bf16 [B, nq, H_q, d], N(0,1), drawn
+    by torch's generator on `device` (one seed per (config, layer))."""
+    g = _torch_gen(derive_seed(cfg.cid, "Qprefill", layer), device)
+    Q = torch.empty((cfg.B, nq, cfg.H_q, cfg.d), dtype=torch.bfloat16, device=device)
+    for b in range(cfg.B):
+        Q[b].copy_(torch.randn((nq, cfg.H_q, cfg.d), generator=g, device=device, dtype=torch.float32)
+                   .to(torch.bfloat16))
+    return Q

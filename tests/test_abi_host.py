@@ -38,7 +38,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = header_functions()
-    assert len(names) == 22
+    assert len(names) == 25
     for n in names:
         assert hasattr(L, n), n
         assert n in sda.exported_symbols(), n
@@ -436,3 +436,32 @@ def test_noalloc_step_rejects_sizes_beyond_its_scratch(L):
     assert "static scratch" in _last()
     bad = list(args); bad[0] = None                                        # null q: refused first
     assert f(*bad) == NULL
+
+
+def _header_params():
+    """name -> list of parameter types, from include/sda.h."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(sda_[a-z_]+)\s*\(([^)]*)\)\s*;", text):
+        params = [p.strip() for p in m.group(2).split(",") if p.strip() and p.strip() != "void"]
+        out[m.group(1)] = params
+    return out
+
+
+def test_binding_signatures_match_the_header(L):
+    # every bound function takes as many arguments as the header declares,
+    # with floats, 64-bit sizes and pointers where the header has them
+    import ctypes as C
+    params = _header_params()
+    for name, (_, argtypes) in sda._SIGNATURES.items():
+        decl = params[name]
+        assert len(decl) == len(argtypes), (name, len(decl), len(argtypes))
+        for p, t in zip(decl, argtypes):
+            if "*" in p:
+                assert t is C.c_void_p, (name, p)
+            elif p.startswith("float"):
+                assert t is C.c_float, (name, p)
+            elif p.startswith("size_t"):
+                assert t is C.c_size_t, (name, p)
+            else:
+                assert t is C.c_int, (name, p)

@@ -44,3 +44,16 @@ def test_config_byte_counts():
     assert c3.selected_kv_bytes() == 73_400_320
     assert c3.ktilde_bytes() == 33_554_432
     assert synth.get_config(1).selected_kv_bytes() == 360_448
+
+
+def test_prefill_indexer_vectors_are_a_stationary_correlated_sequence():
+    import synth
+    from synth import inputs
+    cfg = synth.get_config(1)
+    F = inputs.prefill_indexer_vectors(cfg, 0, 4000)
+    assert F.shape == (1, 4000, 2, 64)
+    assert abs(F.std() * np.sqrt(cfg.d) - 1.0) < 0.05
+    r = np.mean([np.corrcoef(F[0, :-1, g, i], F[0, 1:, g, i])[0, 1] for g in range(2) for i in range(64)])
+    assert abs(r - inputs.PREFILL_RHO) < 0.01
+    tail = inputs.prefill_indexer_vectors(cfg, 0, 500, pos0=3500)
+    assert np.array_equal(tail, F[:, 3500:])
