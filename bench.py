@@ -26,6 +26,7 @@ workloads, each against its roofline with the oracle timed beside it.
   python bench.py --copy-calibration     (plain copy of known size, for counter scaling)
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -247,12 +248,17 @@ def hbm(nbytes, sec):
             "algorithmic_bytes": int(nbytes)}
 
 
-def measure_rows(cfg, layers):
-    """Rows a1, a5, a6 and a7 of the hot path, each timed on the GPU against
-    its roofline with the CPU oracle timed beside it on a small sample."""
+ROW_NAMES = ("a1", "a7", "c2", "prefill", "pooled", "grouped", "offload")
+
+
+def measure_rows(cfg, layers, only=None):
+    """The other rows of the hot path, each timed on the GPU against its
+    roofline with the CPU oracle timed beside it on a small sample (`only`:
+    a subset of ROW_NAMES)."""
     import oracle as O
     dev = "cuda"
     rows = {}
+    want = set(only or ROW_NAMES)
     T, d, G = cfg.T, cfg.d, cfg.G
     scale = 1.0 / math.sqrt(d)
     ln = layers[1 % len(layers)]
@@ -262,49 +268,57 @@ def measure_rows(cfg, layers):
     zero = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
     full = torch.full((cfg.B,), T, dtype=torch.int32, device=dev)
     prev = torch.full((cfg.B,), T - 1, dtype=torch.int32, device=dev)
-    t_build = eager_time(lambda: sda.sda_update_compressed_keys(ln["K"], kt, zero, full, T), reps=5)
-    t_tok = graph_time(lambda: sda.sda_update_compressed_keys(ln["K"], kt, prev, full, 1))
     kk = O.bf16_to_f64(inputs.bf16_bits(ln["K"][0, 0]))
-    t_or = oracle_time(lambda: O.store_bf16(O.compressed_keys(kk, T)))
     nrow = cfg.B * cfg.H_kv
-    rows["a1_compressed_keys"] = {
-        "workload": f"{cfg.name}: K~ of {nrow} (batch, KV head) rows x {cfg.NB} blocks",
-        "build_us": t_build * 1e6, "build_roofline": hbm(cfg.B * cfg.H_kv * T * d * 2 + cfg.ktilde_bytes(), t_build),
-        "per_token_update_us": t_tok * 1e6,
-        "per_token_update_roofline": hbm(nrow * (64 * d * 2 + d * 2), t_tok),
-        "oracle_rows_per_s": 1.0 / t_or, "gpu_rows_per_s": nrow / t_build,
-    }
+    if "a1" in want:
+        t_build = eager_time(lambda: sda.sda_update_compressed_keys(ln["K"], kt, zero, full, T), reps=5)
+        t_tok = graph_time(lambda: sda.sda_update_compressed_keys(ln["K"], kt, prev, full, 1))
+        t_or = oracle_time(lambda: O.store_bf16(O.compressed_keys(kk, T)))
+        rows["a1_compressed_keys"] = {
+            "workload": f"{cfg.name}: K~ of {nrow} (batch, KV head) rows x {cfg.NB} blocks",
+            "build_us": t_build * 1e6, "build_roofline": hbm(cfg.B * cfg.H_kv * T * d * 2 + cfg.ktilde_bytes(), t_build),
+            "per_token_update_us": t_tok * 1e6,
+            "per_token_update_roofline": hbm(nrow * (64 * d * 2 + d * 2), t_tok),
+            "oracle_rows_per_s": 1.0 / t_or, "gpu_rows_per_s": nrow / t_build,
+        }
 
-    # a7: the G-head comparator selector on the same layer
-    nsm = cfg.n_init + cfg.n_local + cfg.top_k
-    bi = torch.empty((cfg.B, 1, cfg.H_kv, nsm), dtype=torch.int32, device=dev)
-    ns = torch.empty((cfg.B, 1, cfg.H_kv), dtype=torch.int32, device=dev)
-    wsm = torch.zeros(sda.lib().sda_score_select_multihead_workspace(cfg.B, 1, cfg.H_q, cfg.H_kv, cfg.NB,
-                                                                    cfg.top_k), dtype=torch.uint8, device=dev)
-    tau = math.sqrt(d)
-    # one call per resident layer in turn (8 x 33.5 MB of compressed keys: the
-    # working set exceeds the 256 MB Infinity Cache, so every call reads HBM)
-    L = len(layers)
-    turn = [0]
+    if "a7" in want:
+        # a7: the G-head comparator selector on the same layer
+        nsm = cfg.n_init + cfg.n_local + cfg.top_k
+        bi = torch.empty((cfg.B, 1, cfg.H_kv, nsm), dtype=torch.int32, device=dev)
+        ns = torch.empty((cfg.B, 1, cfg.H_kv), dtype=torch.int32, device=dev)
+        wsm = torch.zeros(sda.lib().sda_score_select_multihead_workspace(cfg.B, 1, cfg.H_q, cfg.H_kv, cfg.NB,
+                                                                        cfg.top_k), dtype=torch.uint8, device=dev)
+        tau = math.sqrt(d)
+        # one call per resident layer in turn (8 x 33.5 MB of compressed keys: the
+        # working set exceeds the 256 MB Infinity Cache, so every call reads HBM)
+        L = len(layers)
+        turn = [0]
 
-    def mh_call():
-        lay = layers[turn[0] % L]
-        turn[0] += 1
-        sda.sda_score_select_multihead(lay["Q"], lay["kt"], full, cfg.n_init, cfg.n_local, cfg.top_k, tau,
-                                       block_idx=bi, n_sel=ns, ws=wsm)
-    t_mh = graph_time(mh_call, copies=L)
-    Qd = O.bf16_to_f64(inputs.bf16_bits(ln["Q"][0, 0, :G]))
-    ktd = O.store_bf16(O.compressed_keys(kk, T))
-    t_or = oracle_time(lambda: O.select_row_multihead(Qd, ktd, cfg.n_init, cfg.n_local, cfg.top_k, tau))
-    rows["a7_comparator"] = {
-        "workload": f"{cfg.name}: G = {G} heads per KV group, tau = sqrt(d)",
-        "us": t_mh * 1e6, "roofline": hbm(cfg.ktilde_bytes(), t_mh),
-        "oracle_rows_per_s": 1.0 / t_or, "gpu_rows_per_s": nrow / t_mh,
-    }
-    rows["c2_step"] = measure_step_config(2)
-    rows["n1_pooled_select"] = measure_pooled(cfg, layers, O, full, prev)
-    rows["a5_grouped"] = measure_grouped(O)
-    rows["a6_offload"] = measure_offload(O)
+        def mh_call():
+            lay = layers[turn[0] % L]
+            turn[0] += 1
+            sda.sda_score_select_multihead(lay["Q"], lay["kt"], full, cfg.n_init, cfg.n_local, cfg.top_k, tau,
+                                           block_idx=bi, n_sel=ns, ws=wsm)
+        t_mh = graph_time(mh_call, copies=L)
+        Qd = O.bf16_to_f64(inputs.bf16_bits(ln["Q"][0, 0, :G]))
+        ktd = O.store_bf16(O.compressed_keys(kk, T))
+        t_or = oracle_time(lambda: O.select_row_multihead(Qd, ktd, cfg.n_init, cfg.n_local, cfg.top_k, tau))
+        rows["a7_comparator"] = {
+            "workload": f"{cfg.name}: G = {G} heads per KV group, tau = sqrt(d)",
+            "us": t_mh * 1e6, "roofline": hbm(cfg.ktilde_bytes(), t_mh),
+            "oracle_rows_per_s": 1.0 / t_or, "gpu_rows_per_s": nrow / t_mh,
+        }
+    if "c2" in want:
+        rows["c2_step"] = measure_step_config(2)
+    if "prefill" in want:
+        rows["n2_prefill"] = measure_prefill(2)
+    if "pooled" in want:
+        rows["n1_pooled_select"] = measure_pooled(cfg, layers, O, full, prev)
+    if "grouped" in want:
+        rows["a5_grouped"] = measure_grouped(O)
+    if "offload" in want:
+        rows["a6_offload"] = measure_offload(O)
     return rows
 
 
@@ -358,6 +372,91 @@ def measure_step_config(cid, n_layers=8):
         "sparse_decode_us": t_dec * 1e6, "sparse_decode_roofline": hbm(cfg.selected_kv_bytes(), t_dec),
     }
     del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_prefill(cid=2):
+    """Prefill of a whole 32K sequence at the 8B-shaped layer (B 8, H_q 32,
+    H_kv 8, d 128, 1 init + 2 local + top-16 per query position): the bulk
+    build of the compressed keys, per-token selection and causal
+    block-sparse attention, each timed, the attention priced against the
+    bf16 MFMA peak on eq. (15)'s work (4 d flops per query head and visible
+    key token of its blocks, counted from the lists) and against HBM on the
+    bytes any prefill must move (the layer's K and V once, Q in, out)."""
+    cfg = dataclasses.replace(synth.get_config(cid), bias_frac=0.0, bias_beta=0.0)
+    dev = "cuda"
+    T, G = cfg.T, cfg.G
+    K, V, _ = inputs.kv_layer(cfg, 0, device=dev)
+    F = inputs.to_bf16(inputs.prefill_indexer_vectors(cfg, 0, T), dev)
+    Q = inputs.prefill_queries(cfg, 0, T, device=dev)
+    seq = torch.full((cfg.B,), T, dtype=torch.int32, device=dev)
+    zero = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+    kt = torch.zeros((cfg.B, cfg.H_kv, cfg.NB, cfg.d), dtype=torch.bfloat16, device=dev)
+    nsm = cfg.n_init + cfg.n_local + cfg.top_k
+    bi = torch.empty((cfg.B, T, cfg.H_kv, nsm), dtype=torch.int32, device=dev)
+    ns = torch.empty((cfg.B, T, cfg.H_kv), dtype=torch.int32, device=dev)
+    out = torch.empty((cfg.B, T, cfg.H_q, cfg.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, T, cfg.H_q), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(16, sda.lib().sda_prefill_attention_workspace(cfg.B, T, cfg.H_q, cfg.H_kv, nsm, cfg.d,
+                                                                        cfg.NB)), dtype=torch.uint8, device=dev)
+    sel = (cfg.n_init, cfg.n_local, cfg.top_k)
+    t_keys = eager_time(lambda: sda.sda_update_compressed_keys(K, kt, zero, seq, T), reps=5)
+    t_sel = eager_time(lambda: sda.sda_prefill_select(F, kt, seq, 0, *sel, block_idx=bi, n_sel=ns), reps=5)
+    t_att = eager_time(lambda: sda.sda_prefill_attention(Q, K, V, seq, bi, ns, 0, out=out, lse=lse, ws=ws), reps=3)
+    # work: each query head times the visible tokens of its blocks (causal: a
+    # block at or past the query's own block counts only its first tokens)
+    bi_h = bi.cpu().numpy()
+    ns_h = ns.cpu().numpy()
+    pos = np.arange(T)[None, :, None, None]
+    valid = np.arange(nsm)[None, None, None, :] < ns_h[..., None]
+    vis = np.clip(pos + 1 - bi_h.astype(np.int64) * 64, 0, 64) * valid
+    tokens = int(vis.sum())                            # (query, KV head, visible key) triples
+    att_flops = tokens * G * 4 * cfg.d
+    sel_flops = int(sum(2 * cfg.d * (p // 64 + 1) for p in range(T))) * cfg.B * cfg.H_kv
+    kv_bytes = 2 * cfg.B * cfg.H_kv * T * cfg.d * 2
+    q_bytes = cfg.B * T * cfg.H_q * cfg.d * 2
+    out_bytes = cfg.B * T * cfg.H_q * (cfg.d + 1) * 4
+    min_bytes = kv_bytes + q_bytes + out_bytes + int(bi.numel()) * 4
+    tf = att_flops / t_att / 1e12
+    # adjacent positions' top-k overlap near the end of the sequence (the
+    # correlation of consecutive indexer vectors); the lists there hold
+    # init, top-k and local blocks in ascending order
+    tail = bi_h[:, T - 1025:, :, :]
+    ov = []
+    for b in range(cfg.B):
+        for g in range(cfg.H_kv):
+            for i in range(0, 1024, 16):
+                a0, a1 = tail[b, i, g], tail[b, i + 1, g]
+                top0 = set(a0) - set(range(cfg.n_init)) - set(range((T - 1025 + i) // 64 - 1, (T - 1025 + i) // 64 + 1))
+                top1 = set(a1) - set(range(cfg.n_init)) - set(range((T - 1024 + i) // 64 - 1, (T - 1024 + i) // 64 + 1))
+                ov.append(len(top0 & top1) / max(1, len(top0)))
+    ov = float(np.mean(ov))
+    # blocks the attention loads: the union of each group's lists (groups of
+    # min(8, 32 / G) consecutive positions)
+    C = max(1, min(8, 32 // G))
+    grp = bi_h.reshape(cfg.B, T // C, C, cfg.H_kv, nsm).transpose(0, 1, 3, 2, 4).reshape(cfg.B, T // C, cfg.H_kv, -1)
+    grp = np.sort(grp, axis=-1)
+    loads = int(((np.diff(grp, axis=-1) != 0) & (grp[..., 1:] >= 0)).sum() + (grp[..., 0] >= 0).sum())
+    loaded_bytes = loads * 64 * cfg.d * 2 * 2
+    res = {
+        "workload": f"prefill of {T} tokens at the 8B-shaped layer: B={cfg.B}, H_q={cfg.H_q}, H_kv={cfg.H_kv}, "
+                    f"d={cfg.d}, {cfg.n_init} init + {cfg.n_local} local + top-{cfg.top_k} per query position, "
+                    f"indexer vectors of consecutive positions correlated {inputs.PREFILL_RHO} (adjacent "
+                    f"top-{cfg.top_k} overlap {ov:.2f})",
+        "compressed_keys_us": t_keys * 1e6,
+        "select_us": t_sel * 1e6,
+        "select_roofline": {"bound": "mfma", "achieved_tflops": sel_flops / t_sel / 1e12, "peak_tflops": 2500.0,
+                            "frac": sel_flops / t_sel / 1e12 / 2500.0, "flops": sel_flops},
+        "attention_us": t_att * 1e6,
+        "attention_roofline": {"bound": "mfma", "achieved_tflops": tf, "peak_tflops": 2500.0, "frac": tf / 2500.0,
+                               "flops": att_flops},
+        "attention_hbm": hbm(min_bytes, t_att),
+        "attention_blocks_loaded": loads,
+        "attention_loaded_roofline": hbm(loaded_bytes, t_att),
+        "tokens_per_s": cfg.B * T / (t_keys + t_sel + t_att),
+    }
+    del K, V, F, Q, kt, bi, ns, out, lse, ws
     torch.cuda.empty_cache()
     return res
 
@@ -817,7 +916,8 @@ def main():
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--split-k", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-rows", action="store_true", help="skip the other hot-path rows (a1, a5, a6, a7)")
+    ap.add_argument("--no-rows", action="store_true", help="skip the other hot-path rows")
+    ap.add_argument("--rows", help="comma-separated subset of the other rows: " + ",".join(ROW_NAMES))
     ap.add_argument("--no-graph", action="store_true", help="time eager prepared calls (for counter runs)")
     ap.add_argument("--overlap", action="store_true",
                     help="run layer l+1's selection on a side stream beside layer l's decode "
@@ -1059,7 +1159,7 @@ def main():
     if cpu is not None:
         res["cpu_baseline"] = cpu
     if not args.no_rows:
-        res["rows"] = measure_rows(cfg, layers)
+        res["rows"] = measure_rows(cfg, layers, args.rows.split(",") if args.rows else None)
     print(json.dumps(res))
 
 
