@@ -248,7 +248,7 @@ def hbm(nbytes, sec):
             "algorithmic_bytes": int(nbytes)}
 
 
-ROW_NAMES = ("a1", "a7", "c2", "prefill", "pooled", "grouped", "offload")
+ROW_NAMES = ("a1", "a7", "c2", "prefill", "pooled", "grouped", "chain", "offload")
 
 
 def measure_rows(cfg, layers, only=None):
@@ -317,6 +317,8 @@ def measure_rows(cfg, layers, only=None):
         rows["n1_pooled_select"] = measure_pooled(cfg, layers, O, full, prev)
     if "grouped" in want:
         rows["a5_grouped"] = measure_grouped(O)
+    if "chain" in want:
+        rows["n3_refresh_reuse"] = measure_chain()
     if "offload" in want:
         rows["a6_offload"] = measure_offload(O)
     return rows
@@ -742,6 +744,70 @@ def measure_grouped(O):
     res["oracle_groups_per_s"] = 1.0 / t_or
     res["gpu_groups_per_s_gamma_0.75"] = groups / (res["gammas"]["0.75"]["mode_A"]["us"] * 1e-6)
     del K, V, kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_chain(L=15, schedules=(1, 3, 5), window=512):
+    """NEXT 3 at the verification workload (64K, 16 draft queries per
+    sequence in groups of 4, top-16, 512-token window, 64/64 compressed keys
+    and values): a chain of L NSA layers where every r-th layer routes and
+    caches its block lists and the others reuse them (sda_nsa_chain), for
+    r in `schedules`; T_refresh (routing + the three-branch launch) and
+    T_reuse (the launch alone) per layer, and T_total against R T_refresh +
+    (L - R) T_reuse."""
+    cfg = synth.get_config(4)
+    dev = "cuda"
+    n, C = cfg.top_k, cfg.group_C
+    seq = torch.full((cfg.B,), cfg.T, dtype=torch.int32, device=dev)
+    zero = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+    # the draft noise of the gamma = 0.75 workload, bisected on layer 0
+    K0, _, _ = inputs.kv_layer(cfg, 0, device=dev)
+    kt0 = torch.zeros((cfg.B, cfg.H_kv, cfg.NB, cfg.d), dtype=torch.bfloat16, device=dev)
+    sda.sda_update_compressed_keys(K0, kt0, zero, seq, cfg.T)
+    sigma, _ = grouped_lists(cfg, kt0, seq, 0.75, 1)
+    del K0, kt0
+    layers = []
+    for j in range(L):
+        K, V, _ = inputs.kv_layer(cfg, j, device=dev)
+        kc = torch.zeros((cfg.B, cfg.H_kv, cfg.NB, cfg.d), dtype=torch.bfloat16, device=dev)
+        vc = torch.zeros_like(kc)
+        sda.sda_update_compressed_keys(K, kc, zero, seq, cfg.T)
+        sda.sda_update_compressed_keys(V, vc, zero, seq, cfg.T)
+        gates = torch.rand((cfg.B, cfg.NQ, cfg.H_q, 3), generator=torch.Generator(device=dev).manual_seed(j),
+                           device=dev, dtype=torch.float32)
+        layers.append(dict(q=inputs.to_bf16(inputs.attention_queries(cfg, j, sigma=sigma), dev), k=K, v=V, k_cmp=kc,
+                           v_cmp=vc, k_route=kc, f_route=inputs.to_bf16(inputs.indexer_vectors(cfg, j, sigma=sigma),
+                                                                        dev), gates=gates))
+    res = {"workload": f"{cfg.name}: chain of {L} NSA verification layers (B={cfg.B}, NQ={cfg.NQ}, C={C}, "
+                       f"H_q={cfg.H_q}, H_kv={cfg.H_kv}, T={cfg.T}, top-{n}, window {window}, 64/64 compressed "
+                       f"keys and values), draft routing vectors at the gamma = 0.75 noise", "schedules": {}}
+    bic = torch.empty((cfg.B, cfg.NQ, cfg.H_kv, n), dtype=torch.int32, device=dev)
+    nsc = torch.empty((cfg.B, cfg.NQ, cfg.H_kv), dtype=torch.int32, device=dev)
+    ws = torch.zeros(sda.lib().sda_nsa_chain_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, cfg.d, cfg.T, cfg.NB, window,
+                                                       n, C, sda.SDA_GROUP_EXACT), dtype=torch.uint8, device=dev)
+    times = {}
+    for r in schedules:
+        sched = [j % r == 0 for j in range(L)]
+        call, _ = sda.sda_nsa_chain(layers, sched, seq, n, 64, window, group_C=C, block_idx_cache=bic,
+                                    n_sel_cache=nsc, ws=ws, _prepare=True)
+        times[r] = call_time([call], 20, copies=2)
+    # one layer of each kind: a chain of L reuse layers after one refresh is
+    # what r = L gives; single-layer timings come from the r = 1 and r = L chains
+    t_refresh = times[1] / L if 1 in times else float("nan")
+    callL, _ = sda.sda_nsa_chain(layers, [j == 0 for j in range(L)], seq, n, 64, window, group_C=C,
+                                 block_idx_cache=bic, n_sel_cache=nsc, ws=ws, _prepare=True)
+    t_L = call_time([callL], 20, copies=2)
+    t_reuse = (t_L - t_refresh) / (L - 1)
+    for r in schedules:
+        sched = [j % r == 0 for j in range(L)]
+        R = sum(sched)
+        res["schedules"][f"r={r}"] = {"refresh_layers": R, "reuse_layers": L - R, "T_total_us": times[r] * 1e6,
+                                      "formula_us": (R * t_refresh + (L - R) * t_reuse) * 1e6,
+                                      "saving_vs_all_refresh": 1.0 - times[r] / times[1] if 1 in times else None}
+    res["T_refresh_us"] = t_refresh * 1e6
+    res["T_reuse_us"] = t_reuse * 1e6
+    del layers
     torch.cuda.empty_cache()
     return res
 

@@ -68,6 +68,9 @@ _SIGNATURES = {
     "sda_decode_step": (_c_int, [_c_void_p] * 6 + [_c_int] * 6 + [_c_float, _c_void_p, _c_void_p, _c_int]
                         + [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p] * 4 + [_c_int] * 2
                         + [_c_void_p, _c_size_t, _c_void_p]),
+    "sda_nsa_chain_workspace": (_c_size_t, [_c_int] * 11),
+    "sda_nsa_chain": (_c_int, [_c_void_p] * 2 + [_c_int] + [_c_void_p] + [_c_int] * 12 + [_c_float]
+                      + [_c_void_p] * 3 + [_c_size_t, _c_void_p]),
     "sda_prefill_select": (_c_int, [_c_void_p] * 3 + [_c_int] * 10 + [_c_void_p] * 3),
     "sda_prefill_attention_workspace": (_c_size_t, [_c_int] * 7),
     "sda_prefill_attention": (_c_int, [_c_void_p] * 6 + [_c_int] * 8 + [_c_float, _c_int] + [_c_void_p] * 3
@@ -490,6 +493,79 @@ def sda_nsa_decode(q, k, v, k_cmp, v_cmp, seq_len, block_idx, n_sel, gates, cmp_
                                 NQ, H_q, H, d, float(scale), int(group_C), int(mode), _ptr(out), _ptr(lse),
                                 _ptr(union_count), _ptr(ws), wsb, _stream(stream)))
     return out, lse, union_count
+
+
+class NsaLayer(ctypes.Structure):
+    """sda_nsa_layer of the C ABI: one layer's tensors in a refresh/reuse chain."""
+    _fields_ = [(n, _c_void_p) for n in ("q", "k", "v", "k_cmp", "v_cmp", "k_route", "f_route", "gates", "out",
+                                         "lse")]
+
+
+def sda_nsa_chain(layers, refresh, seq_len, top_n, cmp_stride, window, group_C=1, mode=SDA_GROUP_EXACT, scale=None,
+                  block_idx_cache=None, n_sel_cache=None, ws=None, stream=None, _prepare=False):
+    """Refresh/reuse chain of NSA verification layers: refresh layers route
+    (top_n blocks per row from f_route . k_route) and cache the lists, every
+    layer runs the three-branch NSA output with the cached lists.  `layers`
+    is a list of dicts with q, k, v, k_cmp, v_cmp, gates (and k_route,
+    f_route on refresh layers; out, lse optional); returns
+    ([(out, lse) per layer], block_idx_cache, n_sel_cache)."""
+    L = len(layers)
+    if L < 1 or len(refresh) != L:
+        raise ValueError("one refresh flag per layer, at least one layer")
+    y0 = layers[0]
+    _need(y0["q"], "q", torch.bfloat16, 4)
+    B, NQ, H_q, d = y0["q"].shape
+    _need(y0["k"], "k", torch.bfloat16, (B, None, None, d))
+    H, T_cap = y0["k"].shape[1], y0["k"].shape[2]
+    _need(y0["k_cmp"], "k_cmp", torch.bfloat16, (B, H, None, d))
+    NC_cap = y0["k_cmp"].shape[2]
+    NB_cap = -(-T_cap // BLOCK)
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    if H_q % H:
+        raise ValueError(f"H_q={H_q} is not a multiple of H_kv={H}")
+    dev = y0["q"].device
+    if block_idx_cache is None:
+        block_idx_cache = torch.empty((B, NQ, H, top_n), dtype=torch.int32, device=dev)
+    if n_sel_cache is None:
+        n_sel_cache = torch.empty((B, NQ, H), dtype=torch.int32, device=dev)
+    _need(block_idx_cache, "block_idx_cache", torch.int32, (B, NQ, H, top_n))
+    _need(n_sel_cache, "n_sel_cache", torch.int32, (B, NQ, H))
+    arr = (NsaLayer * L)()
+    outs, keep = [], []
+    for j, y in enumerate(layers):
+        _need(y["q"], f"layers[{j}].q", torch.bfloat16, (B, NQ, H_q, d))
+        for n in ("k", "v"):
+            _need(y[n], f"layers[{j}].{n}", torch.bfloat16, (B, H, T_cap, d))
+        for n in ("k_cmp", "v_cmp"):
+            _need(y[n], f"layers[{j}].{n}", torch.bfloat16, (B, H, NC_cap, d))
+        _need(y["gates"], f"layers[{j}].gates", torch.float32, (B, NQ, H_q, 3))
+        if refresh[j]:
+            _need(y["k_route"], f"layers[{j}].k_route", torch.bfloat16, (B, H, NB_cap, d))
+            _need(y["f_route"], f"layers[{j}].f_route", torch.bfloat16, (B, NQ, H, d))
+        out, lse = _attn_outputs(B, NQ, H_q, d, y.get("out"), y.get("lse"), dev, lse_tail=(3,))
+        outs.append((out, lse))
+        ts = dict(q=y["q"], k=y["k"], v=y["v"], k_cmp=y["k_cmp"], v_cmp=y["v_cmp"], gates=y["gates"], out=out,
+                  lse=lse, k_route=y.get("k_route") if refresh[j] else None,
+                  f_route=y.get("f_route") if refresh[j] else None)
+        _on_gpu(**{f"layers[{j}].{n}": t for n, t in ts.items()})
+        for n, t in ts.items():
+            setattr(arr[j], n, _ptr(t))
+        keep.append(ts)
+    flags = (ctypes.c_uint8 * L)(*[1 if x else 0 for x in refresh])
+    if scale is None:
+        scale = d ** -0.5
+    nbytes = lib().sda_nsa_chain_workspace(B, NQ, H_q, H, d, T_cap, NC_cap, int(window), int(top_n), int(group_C),
+                                           int(mode))
+    ws, wsb = _workspace(nbytes, dev, ws)
+    _on_gpu(seq_len=seq_len, block_idx_cache=block_idx_cache, n_sel_cache=n_sel_cache, ws=ws)
+    args = (ctypes.addressof(arr), ctypes.addressof(flags), L, _ptr(seq_len), B, NQ, H_q, H, d, T_cap, NC_cap,
+            int(cmp_stride), int(window), int(top_n), int(group_C), int(mode), float(scale), _ptr(block_idx_cache),
+            _ptr(n_sel_cache), _ptr(ws), wsb, None)
+    res = (outs, block_idx_cache, n_sel_cache)
+    if _prepare:
+        return PreparedCall("sda_nsa_chain", args, (arr, flags, keep, seq_len, block_idx_cache, n_sel_cache, ws)), res
+    _check(lib().sda_nsa_chain(*args[:-1], _stream(stream)))
+    return res
 
 
 def sda_prefill_select(f, k_tilde, seq_len, pos0, n_init, n_local, top_k, n_sel_max=None, block_idx=None,

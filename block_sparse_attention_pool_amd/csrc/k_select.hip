@@ -441,8 +441,7 @@ __global__ __launch_bounds__(256) void pooled_score_kernel(ScoreArgs a, PoolArgs
 template <int D, int MODE>
 static void launch_score_d(const ScoreArgs& a, int B, hipStream_t s) {
     const int nvec = a.NQ * a.VPR;
-    int nv = 1;
-    while (nv < nvec && nv < 16) nv *= 2;
+    const int nv = score_tile_vectors(nvec, a.NB_cap, B * a.H_kv);
     dim3 grid(score_chunks(a.NB_cap), B * a.H_kv, (nvec + nv - 1) / nv), block(256);
     switch (nv) {
         case 1: hipLaunchKernelGGL((score_kernel<D, 1, MODE>), grid, block, 0, s, a); break;
@@ -453,9 +452,19 @@ static void launch_score_d(const ScoreArgs& a, int B, hipStream_t s) {
     }
 }
 
-int score_tiles(int NQ) {
+// Vectors per scoring workgroup: up to 16 share one read of a chunk's
+// compressed keys, but a workgroup selects for its vectors one after another,
+// so tiles shrink (more workgroups, each key chunk read by several) while the
+// grid would hold fewer than two workgroups per compute unit.
+int score_tile_vectors(int nvec, int NB_cap, int rows) {
     int nv = 1;
-    while (nv < NQ && nv < 16) nv *= 2;
+    while (nv < nvec && nv < 16) nv *= 2;
+    while (nv > 1 && (long long)score_chunks(NB_cap) * rows * ((nvec + nv - 1) / nv) < 2LL * kCUs) nv /= 2;
+    return nv;
+}
+
+int score_tiles(int NQ, int NB_cap, int rows) {
+    const int nv = score_tile_vectors(NQ, NB_cap, rows);
     return (NQ + nv - 1) / nv;
 }
 

@@ -181,7 +181,7 @@ static size_t cand_region_bytes(int B, int NQ, int H_kv, int NB_cap, int top_k) 
 size_t sda_score_select_workspace(int B, int NQ, int H_kv, int NB_cap, int top_k) {
     if (B < 1 || NQ < 1 || H_kv < 1 || NB_cap < 1 || top_k < 0) return 0;
     return score_region_bytes(B, NQ, H_kv, NB_cap) + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k) +
-           (size_t)B * H_kv * score_tiles(NQ) * sizeof(int);
+           (size_t)B * H_kv * score_tiles(NQ, NB_cap, B * H_kv) * sizeof(int);
 }
 
 static sda_status_t check_select_common(const void* k_tilde, const int32_t* seq_len, int B, int NQ,
@@ -750,6 +750,51 @@ sda_status_t sda_decode_step_noalloc(const void* q, const void* k, const void* v
     StepScratch w{reinterpret_cast<int*>(base), part_ml, part_o, reinterpret_cast<float*>(sel),
                   reinterpret_cast<uint64_t*>(sel), reinterpret_cast<int*>(base + dec_cnt)};
     return run_step(c, sp, w, s);
+}
+
+// ---------------------------------------------------------------------------
+// refresh/reuse NSA layer chain: [routing workspace | NSA workspace]
+size_t sda_nsa_chain_workspace(int B, int NQ, int H_q, int H_kv, int d, int T_cap, int NC_cap, int window,
+                               int top_n, int group_C, int mode) {
+    if (T_cap < 1 || top_n < 1) return 0;
+    const size_t nsa = sda_nsa_decode_workspace(B, NQ, H_q, H_kv, top_n, d, T_cap, NC_cap, window, group_C, mode);
+    const size_t sel = sda_score_select_workspace(B, NQ, H_kv, ceil_div(T_cap, kBlock), top_n);
+    if (nsa == 0 || sel == 0) return 0;
+    return pad256(sel) + nsa;
+}
+
+sda_status_t sda_nsa_chain(const sda_nsa_layer* layers, const uint8_t* refresh, int L, const int32_t* seq_len,
+                           int B, int NQ, int H_q, int H_kv, int d, int T_cap, int NC_cap, int cmp_stride,
+                           int window, int top_n, int group_C, int mode, float scale, int32_t* block_idx_cache,
+                           int32_t* n_sel_cache, void* ws, size_t ws_bytes, void* stream) {
+    REQUIRE(layers && refresh && seq_len && block_idx_cache && n_sel_cache, SDA_ERR_NULL, "nsa_chain: null pointer");
+    REQUIRE(L >= 1, SDA_ERR_SHAPE, "nsa_chain: L=%d < 1", L);
+    REQUIRE(refresh[0] != 0, SDA_ERR_SHAPE, "nsa_chain: the first layer must refresh (nothing is cached yet)");
+    REQUIRE(top_n >= 1, SDA_ERR_SHAPE, "nsa_chain: top_n=%d < 1", top_n);
+    for (int j = 0; j < L; ++j) {
+        const sda_nsa_layer& y = layers[j];
+        REQUIRE(y.q && y.k && y.v && y.k_cmp && y.v_cmp && y.gates && y.out, SDA_ERR_NULL,
+                "nsa_chain: layer %d has a null pointer", j);
+        REQUIRE(!refresh[j] || (y.k_route && y.f_route), SDA_ERR_NULL,
+                "nsa_chain: refresh layer %d needs k_route and f_route", j);
+    }
+    const size_t need = sda_nsa_chain_workspace(B, NQ, H_q, H_kv, d, T_cap, NC_cap, window, top_n, group_C, mode);
+    REQUIRE(need > 0, SDA_ERR_SHAPE, "nsa_chain: invalid sizes");
+    REQUIRE(ws && ws_bytes >= need, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, need);
+    REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const int NB_cap = ceil_div(T_cap, kBlock);
+    const size_t sel = pad256(sda_score_select_workspace(B, NQ, H_kv, NB_cap, top_n));
+    char* base = static_cast<char*>(ws);
+    for (int j = 0; j < L; ++j) {
+        const sda_nsa_layer& y = layers[j];
+        if (refresh[j])
+            TRY(sda_score_select(y.f_route, y.k_route, seq_len, B, NQ, H_kv, d, NB_cap, 0, 0, top_n, top_n,
+                                 block_idx_cache, n_sel_cache, nullptr, base, sel, stream));
+        TRY(sda_nsa_decode(y.q, y.k, y.v, y.k_cmp, y.v_cmp, seq_len, block_idx_cache, n_sel_cache, top_n, T_cap,
+                           NC_cap, cmp_stride, window, y.gates, B, NQ, H_q, H_kv, d, scale, group_C, mode, y.out, y.lse,
+                           nullptr, base + sel, ws_bytes - sel, stream));
+    }
+    return SDA_OK;
 }
 
 // ---------------------------------------------------------------------------

@@ -58,7 +58,8 @@ __host__ __device__ inline size_t step_lds_bytes(int K, int cpr, int per_wg) {
     const size_t P = (size_t)pow2_at_least(K);
     return per_wg * step_group_lds_bytes(K) + (P * cpr + P * ((cpr + 1) / 2)) * 8 + 16;
 }
-int score_tiles(int NQ);
+int score_tiles(int NQ, int NB_cap, int rows);            // vector tiles of the scoring grid
+int score_tile_vectors(int nvec, int NB_cap, int rows);    // vectors per scoring workgroup
 // G-head comparator: scores plus per-chunk softmax statistics, then per-block
 // sums of the heads' softmax weights and the selection (inside the second
 // launch when cand / counters are given, else a third launch)

@@ -270,6 +270,44 @@ sda_status_t sda_nsa_decode(const void* q, const void* k, const void* v, const v
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Refresh/reuse layer chain of NSA verification ([SSV] core mechanism 2 and
+ * its scheduling algorithm): layers run in order on `stream`; a refresh
+ * layer (refresh[j] != 0) routes first, s = f . K~ over its 64-token block
+ * keys and top-n per row (sda_score_select with no initial or local blocks,
+ * [SSV] NSA steps 1-2), and caches the lists in block_idx_cache /
+ * n_sel_cache; every layer then runs sda_nsa_decode with the cached lists
+ * (a reuse layer skips routing and inherits the latest refresh layer's
+ * lists).  Refresh layers take two launches, reuse layers one.
+ *
+ *   layers   host array of L layer descriptors (below); k_route and f_route
+ *            are read on refresh layers only
+ *   refresh  host array of L flags; refresh[0] must be non-zero
+ *   block_idx_cache i32 [B, NQ, H_kv, top_n], n_sel_cache i32 [B, NQ, H_kv]:
+ *            the cache (left holding the last refresh layer's lists)
+ *   other arguments as sda_nsa_decode (NB_cap = ceil(T_cap / 64) block keys
+ *   per row in k_route)
+ * Workspace: sda_nsa_chain_workspace() bytes, zero-filled before first use.
+ */
+typedef struct {
+    const void* q;          /* bf16 [B, NQ, H_q, d] */
+    const void* k;          /* bf16 [B, H_kv, T_cap, d] */
+    const void* v;          /* bf16 [B, H_kv, T_cap, d] */
+    const void* k_cmp;      /* bf16 [B, H_kv, NC_cap, d] compressed keys of the compressed branch */
+    const void* v_cmp;      /* bf16 [B, H_kv, NC_cap, d] compressed values */
+    const void* k_route;    /* bf16 [B, H_kv, NB_cap, d] block keys the router scores (refresh layers) */
+    const void* f_route;    /* bf16 [B, NQ, H_kv, d] routing vectors (refresh layers) */
+    const float* gates;     /* f32 [B, NQ, H_q, 3] */
+    float* out;             /* f32 [B, NQ, H_q, d] */
+    float* lse;             /* f32 [B, NQ, H_q, 3] or NULL */
+} sda_nsa_layer;
+size_t sda_nsa_chain_workspace(int B, int NQ, int H_q, int H_kv, int d, int T_cap, int NC_cap, int window,
+                               int top_n, int group_C, int mode);
+sda_status_t sda_nsa_chain(const sda_nsa_layer* layers, const uint8_t* refresh, int L, const int32_t* seq_len,
+                           int B, int NQ, int H_q, int H_kv, int d, int T_cap, int NC_cap, int cmp_stride,
+                           int window, int top_n, int group_C, int mode, float scale, int32_t* block_idx_cache,
+                           int32_t* n_sel_cache, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * One decode step of the layer pipeline ([SparDA] §4.2 and eq. (6): layer l's
  * indexer vectors choose layer l+1's blocks while layer l attends).  The
  * block sets are those of sda_score_select(f_next, k_tilde_next, ...), bit for

@@ -38,7 +38,8 @@ Readings of points the pages leave open (numbered as in the design notes):
   inputs (one triple per query head); in prefill every query position p
   selects and attends as a decode step at length p + 1 would (per-token
   selection, causal), with at least one local block so that every scored
-  block is complete.
+  block is complete; in a refresh/reuse layer chain a reuse layer takes the
+  block lists of the latest refresh layer unchanged.
 
 Parity pins: every function here is pinned by tests under tests/ against
 closed forms, brute force or an independent library routine, except the
@@ -485,3 +486,37 @@ def prefill_rows(q_rows, k, v, lists, pos0, scale):
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)
+
+
+# ---------------------------------------------------------------------------
+# O15  refresh/reuse across layers  ([SSV] core mechanism 2 and its
+#      scheduling algorithm: refresh layers route and cache the selected
+#      block indices, reuse layers skip routing and take the cache;
+#      T_total = R T_refresh + (L - R) T_reuse)
+# ---------------------------------------------------------------------------
+
+def refresh_schedule(L, r):
+    """Refresh every r-th layer, starting with the first: layer j refreshes
+    when j % r == 0 (r = 1: every layer routes)."""
+    return [j % int(r) == 0 for j in range(int(L))]
+
+
+def chain_lists(schedule, route):
+    """The block lists each layer of the chain attends with: a refresh layer
+    j routes (route(j) returns its lists) and replaces the cache; a reuse
+    layer takes the cache as it stands.  The first layer must refresh."""
+    cache = None
+    out = []
+    for j, refresh in enumerate(schedule):
+        if refresh:
+            cache = route(j)
+        elif cache is None:
+            raise ValueError("the first layer of a chain must refresh")
+        out.append(cache)
+    return out
+
+
+def chain_time(schedule, t_refresh, t_reuse):
+    """Verification time of one chain: R refresh layers and L - R reuse layers."""
+    R = sum(1 for x in schedule if x)
+    return R * t_refresh + (len(schedule) - R) * t_reuse

@@ -38,7 +38,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = header_functions()
-    assert len(names) == 25
+    assert len(names) == 27
     for n in names:
         assert hasattr(L, n), n
         assert n in sda.exported_symbols(), n
@@ -55,8 +55,12 @@ def test_workspace_sizes(L):
     # scores + per-chunk candidate keys (top_k <= 64, NB_cap <= 4096 only), each
     # padded to 256 B, + one arrival counter per (b, kv head, vector tile)
     assert L.sda_score_select_workspace(8, 1, 8, 2048, 32) == 8 * 8 * 2048 * 4 + 64 * 8 * 32 * 8 + 8 * 8 * 4
-    assert L.sda_score_select_workspace(1, 3, 1, 3, 1) == 256 + 256 + 1 * 1 * 1 * 4
-    assert L.sda_score_select_workspace(2, 20, 1, 64, 1) == 2 * 20 * 64 * 4 + 512 + 2 * 1 * 2 * 4
+    # (several query vectors: one counter per vector tile; tiles shrink to one
+    # vector each while the grid holds fewer than 512 workgroups)
+    assert L.sda_score_select_workspace(1, 3, 1, 3, 1) == 256 + 256 + 1 * 1 * 3 * 4
+    assert L.sda_score_select_workspace(2, 20, 1, 64, 1) == 2 * 20 * 64 * 4 + 512 + 2 * 1 * 20 * 4
+    assert L.sda_score_select_workspace(4, 16, 8, 1024, 16) == 4 * 16 * 8 * 1024 * 4 + 4 * 16 * 8 * 4 * 16 * 8 + \
+        4 * 8 * 4 * 4                                                      # 4 chunks x 32 rows x 4 tiles of 4
     assert L.sda_score_select_workspace(1, 1, 1, 2048, 65) == 2048 * 4 + 4       # lists too long: no candidates
     assert L.sda_score_select_workspace(1, 1, 1, 4097, 8) == 16640 + 4            # too many chunks
     assert L.sda_score_select_workspace(0, 1, 8, 2048, 32) == 0

@@ -221,7 +221,15 @@ def test_select_paths_match_oracle(NQ, top_k):
     want = {r: O.block_set(nb, cfg.n_init, cfg.n_local, O.top_k(sc[r], cand, top_k)) for r in rows}
     nbytes = sda.lib().sda_score_select_workspace(cfg.B, NQ, cfg.H_kv, ktg.shape[2], top_k)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
-    n_cnt = cfg.B * cfg.H_kv * (1 if NQ == 1 else 2)
+    # one arrival counter per (b, KV head, vector tile); tiles of up to 16
+    # vectors, halved while the grid holds fewer than 512 workgroups
+    chunks = -(-ktg.shape[2] // 256)
+    nv = 1
+    while nv < NQ and nv < 16:
+        nv *= 2
+    while nv > 1 and chunks * cfg.B * cfg.H_kv * -(-NQ // nv) < 512:
+        nv //= 2
+    n_cnt = cfg.B * cfg.H_kv * -(-NQ // nv)
     first = None
     for it in range(6):
         bi, ns = sda.sda_score_select(F.to(DEV), ktg, seq(cfg), cfg.n_init, cfg.n_local, top_k, ws=ws)
