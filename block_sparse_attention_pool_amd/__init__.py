@@ -71,6 +71,9 @@ _SIGNATURES = {
     "sda_nsa_chain_workspace": (_c_size_t, [_c_int] * 11),
     "sda_nsa_chain": (_c_int, [_c_void_p] * 2 + [_c_int] + [_c_void_p] + [_c_int] * 12 + [_c_float]
                       + [_c_void_p] * 3 + [_c_size_t, _c_void_p]),
+    "sda_offload_chain_workspace": (_c_size_t, [_c_int] * 9),
+    "sda_offload_chain": (_c_int, [_c_void_p, _c_int, _c_void_p] + [_c_int] * 8 + [_c_float, _c_void_p, _c_int]
+                          + [_c_void_p] * 2 + [_c_size_t] + [_c_void_p] * 2),
     "sda_prefill_select": (_c_int, [_c_void_p] * 3 + [_c_int] * 10 + [_c_void_p] * 3),
     "sda_prefill_attention_workspace": (_c_size_t, [_c_int] * 7),
     "sda_prefill_attention": (_c_int, [_c_void_p] * 6 + [_c_int] * 8 + [_c_float, _c_int] + [_c_void_p] * 3
@@ -565,6 +568,74 @@ def sda_nsa_chain(layers, refresh, seq_len, top_n, cmp_stride, window, group_C=1
     if _prepare:
         return PreparedCall("sda_nsa_chain", args, (arr, flags, keep, seq_len, block_idx_cache, n_sel_cache, ws)), res
     _check(lib().sda_nsa_chain(*args[:-1], _stream(stream)))
+    return res
+
+
+class OffloadLayer(ctypes.Structure):
+    """sda_offload_layer of the C ABI: one layer of the offloaded decode chain."""
+    _fields_ = [(n, _c_void_p) for n in ("k_host", "v_host", "k_tilde", "q", "f", "out", "lse")]
+
+
+def sda_offload_chain(layers, seq_len, n_init, n_local, top_k, f_first, prefetch_workgroups=64, scale=None,
+                      block_idx=None, ws=None, stream=None, side_stream=None, _prepare=False):
+    """Offloaded-KV decode through L layers with the persistent prefetch pool:
+    each layer's blocks are chosen one layer ahead, copied from pinned host
+    memory by the pool on `side_stream` while the previous layer attends,
+    and attended from a device stage.  `layers`: dicts with k_host, v_host
+    (pinned CPU bf16 [B, H_kv, T_cap, d]), k_tilde, q, f (GPU), out and lse
+    optional.  Returns ([(out, lse) per layer], block_idx [L, B, 1, H_kv, n],
+    ws); the int32 at byte 8 of ws is non-zero if a transfer wait gave up."""
+    L = len(layers)
+    if L < 1:
+        raise ValueError("at least one layer")
+    y0 = layers[0]
+    _need(y0["k_host"], "k_host", torch.bfloat16, 4)
+    B, H, T_cap, d = y0["k_host"].shape
+    _need(y0["q"], "q", torch.bfloat16, (B, 1, None, d))
+    H_q = y0["q"].shape[2]
+    if H_q % H:
+        raise ValueError(f"H_q={H_q} is not a multiple of H_kv={H}")
+    NB_cap = -(-T_cap // BLOCK)
+    nsm = n_init + n_local + top_k
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    _need(f_first, "f_first", torch.bfloat16, (B, 1, H, d))
+    dev = y0["q"].device
+    if block_idx is None:
+        block_idx = torch.empty((L, B, 1, H, nsm), dtype=torch.int32, device=dev)
+    _need(block_idx, "block_idx", torch.int32, (L, B, 1, H, nsm))
+    arr = (OffloadLayer * L)()
+    outs, keep = [], []
+    for j, y in enumerate(layers):
+        for n in ("k_host", "v_host"):
+            _need(y[n], f"layers[{j}].{n}", torch.bfloat16, (B, H, T_cap, d))
+            _on_host(**{f"layers[{j}].{n}": y[n]})
+            if not y[n].is_pinned():
+                raise ValueError(f"layers[{j}].{n} must be pinned host memory")
+        _need(y["k_tilde"], f"layers[{j}].k_tilde", torch.bfloat16, (B, H, NB_cap, d))
+        _need(y["q"], f"layers[{j}].q", torch.bfloat16, (B, 1, H_q, d))
+        _need(y["f"], f"layers[{j}].f", torch.bfloat16, (B, 1, H, d))
+        out, lse = _attn_outputs(B, 1, H_q, d, y.get("out"), y.get("lse"), dev)
+        outs.append((out, lse))
+        dv = dict(k_tilde=y["k_tilde"], q=y["q"], f=y["f"], out=out, lse=lse)
+        _on_gpu(**{f"layers[{j}].{n}": t for n, t in dv.items()})
+        for n, t in list(dv.items()) + [("k_host", y["k_host"]), ("v_host", y["v_host"])]:
+            setattr(arr[j], n, _ptr(t))
+        keep.append((dv, y["k_host"], y["v_host"]))
+    if scale is None:
+        scale = d ** -0.5
+    nbytes = lib().sda_offload_chain_workspace(L, B, H_q, H, d, T_cap, n_init, n_local, top_k)
+    ws, wsb = _workspace(nbytes, dev, ws)
+    _on_gpu(seq_len=seq_len, f_first=f_first, block_idx=block_idx, ws=ws)
+    if side_stream is None:
+        side_stream = torch.cuda.Stream()
+    args = [ctypes.addressof(arr), L, _ptr(seq_len), B, H_q, H, d, T_cap, n_init, n_local, top_k, float(scale),
+            _ptr(f_first), int(prefetch_workgroups), _ptr(block_idx), _ptr(ws), wsb, None, _stream(side_stream)]
+    res = (outs, block_idx, ws)
+    if _prepare:
+        # the stream argument is the second to last here: PreparedCall fills the last one
+        raise ValueError("sda_offload_chain runs eagerly (it starts a pool on a second stream)")
+    args[-2] = _stream(stream)
+    _check(lib().sda_offload_chain(*args))
     return res
 
 

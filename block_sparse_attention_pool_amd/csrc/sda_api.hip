@@ -957,6 +957,160 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
 }
 
 // ---------------------------------------------------------------------------
+// offloaded decode chain with the persistent prefetch pool.  Workspace:
+// [control words, 256 B][lists: L x rows x nsm][n_sel: L x rows][slots: 2 x rows x nsm]
+// [K stages: 2][V stages: 2][score_select workspace][decode workspace]
+namespace {
+
+struct ChainLayout {
+    size_t ctrl, lists, nsel, slots, kst, vst, sel, dec, total;
+    size_t stage_bytes, sel_bytes, dec_bytes;
+};
+
+ChainLayout chain_layout(int L, int B, int H_q, int H_kv, int d, int T_cap, int nsm, int top_k) {
+    ChainLayout c{};
+    const size_t rows = (size_t)B * H_kv;
+    const int NB_cap = ceil_div(T_cap, kBlock);
+    c.stage_bytes = pad256(rows * nsm * kBlock * d * 2);
+    c.sel_bytes = pad256(sda_score_select_workspace(B, 1, H_kv, NB_cap, top_k));
+    c.dec_bytes = pad256(sda_sparse_decode_workspace(B, 1, H_q, H_kv, nsm, d, 0));
+    c.ctrl = 0;
+    c.lists = 256;
+    c.nsel = c.lists + pad256((size_t)L * rows * nsm * 4);
+    c.slots = c.nsel + pad256((size_t)L * rows * 4);
+    c.kst = c.slots + pad256(2 * rows * nsm * 4);
+    c.vst = c.kst + 2 * c.stage_bytes;
+    c.sel = c.vst + 2 * c.stage_bytes;
+    c.dec = c.sel + c.sel_bytes;
+    c.total = c.dec + c.dec_bytes;
+    return c;
+}
+
+constexpr int kPfSpinLimit = 1 << 20;          // polls of ~3.4 us each before a wait gives up
+
+}  // namespace
+
+size_t sda_offload_chain_workspace(int L, int B, int H_q, int H_kv, int d, int T_cap, int n_init, int n_local,
+                                   int top_k) {
+    if (L < 1 || L > kMaxChainLayers || B < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv || T_cap < 1 || n_init < 0 ||
+        n_local < 0 || top_k < 0 || n_init + n_local + top_k < 1)
+        return 0;
+    return chain_layout(L, B, H_q, H_kv, d, T_cap, n_init + n_local + top_k, top_k).total;
+}
+
+sda_status_t sda_offload_chain(const sda_offload_layer* layers, int L, const int32_t* seq_len, int B, int H_q,
+                               int H_kv, int d, int T_cap, int n_init, int n_local, int top_k, float scale,
+                               const void* f_first, int prefetch_workgroups, int32_t* block_idx_opt, void* ws,
+                               size_t ws_bytes, void* stream, void* side_stream) {
+    REQUIRE(layers && seq_len && f_first, SDA_ERR_NULL, "offload_chain: null pointer");
+    REQUIRE(L >= 1 && L <= kMaxChainLayers, SDA_ERR_SHAPE, "offload_chain: L=%d outside [1, %d]", L, kMaxChainLayers);
+    // at most half of the compute units: the stream's own launches must always
+    // find units that no pool workgroup occupies
+    REQUIRE(prefetch_workgroups >= 1 && prefetch_workgroups <= kCUs / 2, SDA_ERR_SHAPE,
+            "prefetch_workgroups=%d outside [1, %d]", prefetch_workgroups, kCUs / 2);
+    REQUIRE(side_stream != stream, SDA_ERR_SHAPE, "offload_chain: the pool needs a stream of its own");
+    TRY(check_d(d));
+    TRY(check_heads(H_q, H_kv));
+    const int nsm = n_init + n_local + top_k;
+    const int NB_cap = ceil_div(T_cap, kBlock);
+    REQUIRE(B >= 1 && T_cap >= 1 && nsm >= 1 && n_init >= 0 && n_local >= 0 && top_k >= 0, SDA_ERR_SHAPE,
+            "offload_chain: bad sizes");
+    REQUIRE((long long)B * H_kv <= kMaxGridYZ, SDA_ERR_SHAPE, "B*H_kv exceeds %d", kMaxGridYZ);
+    REQUIRE(aligned16(f_first), SDA_ERR_ALIGN, "f_first must be 16-byte aligned");
+    const ChainLayout c = chain_layout(L, B, H_q, H_kv, d, T_cap, nsm, top_k);
+    REQUIRE(ws && ws_bytes >= c.total, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0,
+            c.total);
+    REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    PrefetchArgs pa{};
+    char* base = static_cast<char*>(ws);
+    int* ctrl = reinterpret_cast<int*>(base + c.ctrl);
+    const int rows = B * H_kv;
+    int32_t* lists = block_idx_opt ? block_idx_opt : reinterpret_cast<int32_t*>(base + c.lists);
+    int32_t* nsel = reinterpret_cast<int32_t*>(base + c.nsel);
+    for (int j = 0; j < L; ++j) {
+        const sda_offload_layer& y = layers[j];
+        REQUIRE(y.k_host && y.v_host && y.k_tilde && y.q && y.f && y.out, SDA_ERR_NULL,
+                "offload_chain: layer %d has a null pointer", j);
+        REQUIRE(aligned16(y.k_tilde) && aligned16(y.q) && aligned16(y.f) && aligned16(y.out) &&
+                    aligned16(y.k_host) && aligned16(y.v_host),
+                SDA_ERR_ALIGN, "offload_chain: layer %d buffers must be 16-byte aligned", j);
+        void* kd = nullptr;
+        void* vd = nullptr;
+        hipError_t e = hipHostGetDevicePointer(&kd, const_cast<void*>(y.k_host), 0);
+        if (e == hipSuccess) e = hipHostGetDevicePointer(&vd, const_cast<void*>(y.v_host), 0);
+        if (e != hipSuccess)
+            return fail(SDA_ERR_HIP, "offload_chain: layer %d K/V are not pinned, device-mapped host memory: %s", j,
+                        hipGetErrorString(e));
+        PrefetchLayer& p = pa.layer[j];
+        p.k_src = static_cast<const uint16_t*>(kd);
+        p.v_src = static_cast<const uint16_t*>(vd);
+        p.block_idx = lists + (size_t)j * rows * nsm;
+        p.n_sel = nsel + (size_t)j * rows;
+        p.k_stage = reinterpret_cast<uint16_t*>(base + c.kst + (j & 1) * c.stage_bytes);
+        p.v_stage = reinterpret_cast<uint16_t*>(base + c.vst + (j & 1) * c.stage_bytes);
+        p.slot = reinterpret_cast<int32_t*>(base + c.slots) + (size_t)(j & 1) * rows * nsm;
+    }
+    pa.L = L;
+    pa.rows = rows;
+    pa.n_sel_max = nsm;
+    pa.T_cap = T_cap;
+    pa.ctrl = ctrl;
+    pa.spin_limit = kPfSpinLimit;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t side = static_cast<hipStream_t>(side_stream);
+    char* sws = base + c.sel;
+    // the score_select workspace holds arrival counters: clear them (and the
+    // control words) on the stream before anything uses them
+    TRY(hip_status(launch_prefetch_reset(ctrl, s), "offload_chain: reset"));
+    TRY(hip_status(launch_zero_words(sws, c.sel_bytes + c.dec_bytes, s), "offload_chain: workspace clear"));
+    // the pool starts after the reset, on its own stream
+    hipEvent_t ev_start = nullptr, ev_end = nullptr;
+    TRY(hip_status(hipEventCreateWithFlags(&ev_start, hipEventDisableTiming), "offload_chain: event"));
+    hipError_t e = hipEventCreateWithFlags(&ev_end, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(ev_start, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, ev_start, 0);
+    if (e == hipSuccess) e = launch_prefetch_pool(pa, d, prefetch_workgroups, side);
+    if (e == hipSuccess) e = hipEventRecord(ev_end, side);
+    if (e != hipSuccess) {
+        hipEventDestroy(ev_start);
+        if (ev_end) hipEventDestroy(ev_end);
+        return hip_status(e, "offload_chain: pool launch");
+    }
+    sda_status_t st = SDA_OK;
+    const int total = rows * nsm;
+    const size_t stage_tokens = (size_t)nsm * kBlock;
+    auto run = [&]() -> sda_status_t {
+        // layer 0 selects its own blocks with f_first
+        TRY(sda_score_select(f_first, layers[0].k_tilde, seq_len, B, 1, H_kv, d, NB_cap, n_init, n_local, top_k, nsm,
+                             lists, nsel, nullptr, sws, c.sel_bytes, stream));
+        TRY(hip_status(launch_prefetch_enqueue(ctrl, 0, s), "offload_chain: enqueue"));
+        for (int l = 0; l < L; ++l) {
+            if (l + 1 < L) {                               // lookahead: layer l's vectors pick layer l+1's blocks
+                TRY(sda_score_select(layers[l].f, layers[l + 1].k_tilde, seq_len, B, 1, H_kv, d, NB_cap, n_init,
+                                     n_local, top_k, nsm, lists + (size_t)(l + 1) * rows * nsm,
+                                     nsel + (size_t)(l + 1) * rows, nullptr, sws, c.sel_bytes, stream));
+                TRY(hip_status(launch_prefetch_enqueue(ctrl, l + 1, s), "offload_chain: enqueue"));
+            }
+            TRY(hip_status(launch_prefetch_wait(ctrl, l, total, kPfSpinLimit, s), "offload_chain: wait"));
+            const PrefetchLayer& p = pa.layer[l];
+            TRY(sda_sparse_decode(layers[l].q, p.k_stage, p.v_stage, seq_len, p.block_idx, p.n_sel, nsm, p.slot,
+                                  (int)stage_tokens, B, 1, H_q, H_kv, d, scale, layers[l].out, layers[l].lse, 0,
+                                  c.dec_bytes ? base + c.dec : nullptr, c.dec_bytes, stream));
+        }
+        return SDA_OK;
+    };
+    st = run();
+    // end the pool (also after an error) and order the stream after its exit
+    e = launch_prefetch_stop(ctrl, s);
+    hipError_t e2 = hipStreamWaitEvent(s, ev_end, 0);
+    hipEventDestroy(ev_start);
+    hipEventDestroy(ev_end);
+    if (st != SDA_OK) return st;
+    if (e == hipSuccess) e = e2;
+    return hip_status(e, "offload_chain: pool stop");
+}
+
+// ---------------------------------------------------------------------------
 sda_status_t sda_gather_blocks(const void* k_src, const void* v_src, const int32_t* block_idx,
                                const int32_t* n_sel, int n_sel_max, int B, int H_kv, int d, int T_cap,
                                void* k_stage, void* v_stage, int32_t* slot_out, int max_workgroups,

@@ -182,4 +182,30 @@ hipError_t launch_gather(const uint16_t* k_src, const uint16_t* v_src, const int
                          uint16_t* k_stage, uint16_t* v_stage, int32_t* slot_out,
                          int max_workgroups, hipStream_t s);
 
+// ---- persistent prefetch pool (offloaded K/V chain) -------------------------------
+constexpr int kMaxChainLayers = 32;
+constexpr int kPfTail = 0, kPfStop = 1, kPfError = 2, kPfClaim = 8, kPfDone = 8 + kMaxChainLayers;
+constexpr int kPfCtrlInts = 8 + 2 * kMaxChainLayers;
+struct PrefetchLayer {
+    const uint16_t* k_src;    // device-mapped pinned host K [B, H_kv, T_cap, d]
+    const uint16_t* v_src;
+    const int32_t* block_idx; // [B, 1, H_kv, n_sel_max] the layer's block lists
+    const int32_t* n_sel;     // [B, 1, H_kv]
+    uint16_t* k_stage;        // [B, H_kv, n_sel_max * 64, d]
+    uint16_t* v_stage;
+    int32_t* slot;            // [B, 1, H_kv, n_sel_max]
+};
+struct PrefetchArgs {
+    PrefetchLayer layer[kMaxChainLayers];
+    int L, rows, n_sel_max, T_cap;
+    int* ctrl;                // kPfCtrlInts control words
+    int spin_limit;           // polls before a wait gives up
+};
+hipError_t launch_prefetch_reset(int* ctrl, hipStream_t s);
+hipError_t launch_zero_words(void* p, size_t bytes, hipStream_t s);       // fill kernel: bytes / 4 zero words
+hipError_t launch_prefetch_pool(const PrefetchArgs& a, int d, int workgroups, hipStream_t s);
+hipError_t launch_prefetch_enqueue(int* ctrl, int r, hipStream_t s);
+hipError_t launch_prefetch_wait(int* ctrl, int r, int total, int spin_limit, hipStream_t s);
+hipError_t launch_prefetch_stop(int* ctrl, hipStream_t s);
+
 }  // namespace sda

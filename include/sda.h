@@ -424,6 +424,51 @@ sda_status_t sda_decode_step_noalloc(const void* q, const void* k, const void* v
                                      int NB_cap_cur, void* stream);
 
 /*
+ * Offloaded-KV decode chain with a persistent prefetch pool ([SparDA] §4.2,
+ * the decode-step algorithm, steps 2-4 and 6; §4.5 and fig. 5; §4.6 for the
+ * first layer).  The K/V of every layer stay in pinned host memory; the
+ * compressed keys, queries and indexer vectors are on the GPU.  The call
+ * starts a pool of `prefetch_workgroups` long-lived workgroups on
+ * `side_stream` that wait for transfer requests, then runs the layers in
+ * order on `stream`:
+ *   layer 0 selects its own blocks with f_first (§4.6) and enqueues them;
+ *   layer l scores layer l+1's compressed keys with its indexer vector f
+ *     (lookahead), enqueues layer l+1's blocks (the pool copies them from host
+ *     memory into one of two device stages while the stream goes on), waits
+ *     for its own blocks' transfer, and attends over them from the stage.
+ * Waits are bounded: a request that does not complete within about 3 s sets
+ * an error word in the workspace (int at byte offset 8; 0 = no error) and the
+ * chain finishes with undefined outputs for that layer.  On return `stream`
+ * is ordered after the pool's exit (the caller may reuse the workspace).
+ *
+ *   layers    host array of L <= 32 layer descriptors (below)
+ *   seq_len   i32 [B]; all layers hold seq_len[b] tokens
+ *   n_init, n_local, top_k  the block budget of every layer
+ *   f_first   bf16 [B, 1, H_kv, d]: layer 0's own indexer vectors
+ *   prefetch_workgroups  the pool's size (the CU share of the transfer), 1..128: at
+ *             most half of the compute units, so that the stream's launches
+ *             always find units the spinning pool does not hold
+ *   block_idx_opt  i32 [L, B, 1, H_kv, n_init + n_local + top_k] out or NULL:
+ *             the block lists each layer attended
+ * Workspace: sda_offload_chain_workspace() bytes (no zero-fill needed).
+ */
+typedef struct {
+    const void* k_host;     /* bf16 [B, H_kv, T_cap, d], pinned host memory mapped for the device */
+    const void* v_host;
+    const void* k_tilde;    /* bf16 [B, H_kv, NB_cap, d] device: this layer's compressed keys */
+    const void* q;          /* bf16 [B, 1, H_q, d] device */
+    const void* f;          /* bf16 [B, 1, H_kv, d] device: this layer's indexer vectors (score layer l+1) */
+    float* out;             /* f32 [B, 1, H_q, d] device */
+    float* lse;             /* f32 [B, 1, H_q] device or NULL */
+} sda_offload_layer;
+size_t sda_offload_chain_workspace(int L, int B, int H_q, int H_kv, int d, int T_cap, int n_init, int n_local,
+                                   int top_k);
+sda_status_t sda_offload_chain(const sda_offload_layer* layers, int L, const int32_t* seq_len, int B, int H_q,
+                               int H_kv, int d, int T_cap, int n_init, int n_local, int top_k, float scale,
+                               const void* f_first, int prefetch_workgroups, int32_t* block_idx_opt, void* ws,
+                               size_t ws_bytes, void* stream, void* side_stream);
+
+/*
  * Offloaded-KV gather ([SparDA] §4.2 steps 3 and 6, §4.5): copy the K and V
  * rows of each row's selected blocks from pinned host memory into a compact
  * device staging buffer, with GPU loads over the host link, on the caller's
