@@ -812,19 +812,37 @@ def measure_chain(L=15, schedules=(1, 3, 5), window=512):
     return res
 
 
-def measure_offload(O, n_host_layers=2, chain=8):
-    """a6 at the offload workload: each layer's selected K/V blocks are copied
-    from pinned host memory to a device stage on a side stream while the
-    previous layer's decode runs on the main stream."""
+def measure_offload(O, chain=8, pool_sizes=(16, 32, 64, 128)):
+    """a6 and NEXT 4 at the offload workload (256K, B 4, H_q 32, H_kv 8, 1 + 2 +
+    top-32 per layer, 8 layers): the K/V of every layer in pinned host memory
+    (8 distinct layers, 34 GB, unless pinning that much is refused), the
+    compressed keys, queries and indexer vectors on the GPU.  Timed: one
+    layer's gather alone against a plain pinned copy of the same bytes; the
+    decode from the stage; the chain with the persistent prefetch pool
+    (sda_offload_chain; the lookahead selection of layer l+1 inside the loop)
+    for several pool sizes; the same chain with one gather launch per layer
+    on a side stream.  overlap = (sum of the chain's parts run one after the
+    other) / chain time: above 1 when transfers hide behind compute."""
     cfg = synth.get_config(5)
     dev = "cuda"
     T = cfg.T
     nsm = cfg.n_init + cfg.n_local + cfg.top_k
-    host = []
-    for l in range(n_host_layers):
+    seq = torch.full((cfg.B,), T, dtype=torch.int32, device=dev)
+    zero = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+    host, kts, note = [], [], ""
+    for l in range(chain):
         K, V, _ = inputs.kv_layer(cfg, l, device=dev)
-        Kh = torch.empty(K.shape, dtype=torch.bfloat16, pin_memory=True)
-        Vh = torch.empty(V.shape, dtype=torch.bfloat16, pin_memory=True)
+        kt = torch.zeros((cfg.B, cfg.H_kv, cfg.NB, cfg.d), dtype=torch.bfloat16, device=dev)
+        sda.sda_update_compressed_keys(K, kt, zero, seq, T)
+        kts.append(kt)
+        try:
+            Kh = torch.empty(K.shape, dtype=torch.bfloat16, pin_memory=True)
+            Vh = torch.empty(V.shape, dtype=torch.bfloat16, pin_memory=True)
+        except RuntimeError as e:                      # pinning refused: reuse the layers pinned so far
+            note = f"pinning layer {l} refused ({e}); host layers cycle over {len(host)}"
+            log(note)
+            del K, V
+            break
         Kh.copy_(K)
         Vh.copy_(V)
         host.append((Kh, Vh))
@@ -832,74 +850,133 @@ def measure_offload(O, n_host_layers=2, chain=8):
             kk = O.bf16_to_f64(inputs.bf16_bits(K[0, 0, :T]))
             vv = O.bf16_to_f64(inputs.bf16_bits(V[0, 0, :T]))
         del K, V
-    torch.cuda.empty_cache()
-    rng = np.random.default_rng(20260624 + 5)
-    lists = []
-    for l in range(chain):
-        bi_np = np.zeros((cfg.B, 1, cfg.H_kv, nsm), dtype=np.int32)
-        for b in range(cfg.B):
-            for g in range(cfg.H_kv):
-                mid = np.sort(rng.choice(np.arange(cfg.n_init, cfg.NB - cfg.n_local), cfg.top_k, replace=False))
-                bi_np[b, 0, g] = np.concatenate([np.arange(cfg.n_init), mid, np.arange(cfg.NB - cfg.n_local, cfg.NB)])
-        lists.append(torch.from_numpy(bi_np).to(dev))
-    ns = torch.full((cfg.B, 1, cfg.H_kv), nsm, dtype=torch.int32, device=dev)
-    seq = torch.full((cfg.B,), T, dtype=torch.int32, device=dev)
-    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0), dev)
+        torch.cuda.empty_cache()
+    for l in range(len(kts), chain):                   # compressed keys of the cycled layers
+        kts.append(kts[l % len(host)])
+    nh = len(host)
+    Qs = [inputs.to_bf16(inputs.attention_queries(cfg, l), dev) for l in range(chain)]
+    Fs = [inputs.to_bf16(inputs.indexer_vectors(cfg, l), dev) for l in range(chain)]
+    f_first = inputs.to_bf16(inputs.indexer_vectors(cfg, 1000), dev)
+    layers = [dict(k_host=host[l % nh][0], v_host=host[l % nh][1], k_tilde=kts[l], q=Qs[l], f=Fs[l])
+              for l in range(chain)]
+    side = torch.cuda.Stream()
+    res_pool = {}
+    ws = None
+    bi_chain = torch.empty((chain, cfg.B, 1, cfg.H_kv, nsm), dtype=torch.int32, device=dev)
+    for wgs in pool_sizes:
+        outs, _, ws = sda.sda_offload_chain(layers, seq, cfg.n_init, cfg.n_local, cfg.top_k, f_first,
+                                            prefetch_workgroups=wgs, block_idx=bi_chain, ws=ws, side_stream=side)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            sda.sda_offload_chain(layers, seq, cfg.n_init, cfg.n_local, cfg.top_k, f_first, prefetch_workgroups=wgs,
+                                  block_idx=bi_chain, ws=ws, side_stream=side)
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        err = int(ws[8:12].view(torch.int32).item())
+        res_pool[str(wgs)] = {"chain_ms": min(ts) * 1e3, "error_word": err}
+    # parts, each alone: a layer's selection, gather (one launch) and decode from the stage
+    bi = torch.empty((cfg.B, 1, cfg.H_kv, nsm), dtype=torch.int32, device=dev)
+    ns = torch.empty((cfg.B, 1, cfg.H_kv), dtype=torch.int32, device=dev)
+    wsel = torch.zeros(sda.lib().sda_score_select_workspace(cfg.B, 1, cfg.H_kv, cfg.NB, cfg.top_k),
+                       dtype=torch.uint8, device=dev)
+    t_sel = eager_time(lambda: sda.sda_score_select(Fs[0], kts[1], seq, cfg.n_init, cfg.n_local, cfg.top_k,
+                                                    block_idx=bi, n_sel=ns, ws=wsel), reps=5)
     stage_shape = (cfg.B, cfg.H_kv, nsm * 64, cfg.d)
     stages = [(torch.empty(stage_shape, dtype=torch.bfloat16, device=dev),
                torch.empty(stage_shape, dtype=torch.bfloat16, device=dev),
                torch.empty((cfg.B, 1, cfg.H_kv, nsm), dtype=torch.int32, device=dev)) for _ in range(2)]
+    bis = [torch.empty_like(bi) for _ in range(chain)]
+    nss = [torch.empty_like(ns) for _ in range(chain)]
     out = torch.empty((cfg.B, 1, cfg.H_q, cfg.d), dtype=torch.float32, device=dev)
     lse = torch.empty((cfg.B, 1, cfg.H_q), dtype=torch.float32, device=dev)
-    ws = torch.zeros(sda.lib().sda_sparse_decode_workspace(cfg.B, 1, cfg.H_q, cfg.H_kv, nsm, cfg.d, 0),
-                     dtype=torch.uint8, device=dev)
+    wdec = torch.zeros(sda.lib().sda_sparse_decode_workspace(cfg.B, 1, cfg.H_q, cfg.H_kv, nsm, cfg.d, 0),
+                       dtype=torch.uint8, device=dev)
 
-    def gather(l, st):
-        kh, vh = host[l % n_host_layers]
-        sda.sda_gather_blocks(kh, vh, lists[l], ns, k_stage=st[0], v_stage=st[1], slot=st[2], max_workgroups=256)
+    def select(l):                      # layer l's blocks: its own vectors at l = 0, else layer l-1's
+        sda.sda_score_select(f_first if l == 0 else Fs[l - 1], kts[l], seq, cfg.n_init, cfg.n_local, cfg.top_k,
+                             block_idx=bis[l], n_sel=nss[l], ws=wsel)
 
-    def decode(st, l):
-        sda.sda_sparse_decode(Q, st[0], st[1], seq, lists[l], ns, slot=st[2], out=out, lse=lse, ws=ws)
+    def gather(l):
+        st = stages[l % 2]
+        sda.sda_gather_blocks(host[l % nh][0], host[l % nh][1], bis[l], nss[l], k_stage=st[0], v_stage=st[1],
+                              slot=st[2], max_workgroups=128)
 
-    t_gather = eager_time(lambda: gather(0, stages[0]), reps=5)
-    gather(0, stages[0])
-    t_dec = graph_time(lambda: decode(stages[0], 0))
+    def decode(l):
+        st = stages[l % 2]
+        sda.sda_sparse_decode(Qs[l], st[0], st[1], seq, bis[l], nss[l], slot=st[2], out=out, lse=lse, ws=wdec)
+
+    select(0)
+    t_gather = eager_time(lambda: gather(0), reps=5)
+    gather(0)
+    t_dec = eager_time(lambda: decode(0), reps=10)
+    # the per-layer-launch chain: the side stream gathers layer l+1 while the
+    # stream decodes layer l, the selection of l+1 inside the loop
+    main = torch.cuda.current_stream()
+
+    def launch_chain_ordered():
+        select(0)
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            gather(0)
+        done = [None] * chain
+        done[0] = torch.cuda.Event()
+        done[0].record(side)
+        for l in range(chain):
+            if l + 1 < chain:
+                select(l + 1)
+                side.wait_stream(main)
+                with torch.cuda.stream(side):
+                    gather(l + 1)
+                done[l + 1] = torch.cuda.Event()
+                done[l + 1].record(side)
+            main.wait_event(done[l])
+            decode(l)
+    launch_chain_ordered()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        launch_chain_ordered()
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    t_launch_chain = min(ts)
     # host-link reference: a plain pinned -> device copy of the same size
     nbytes = cfg.selected_kv_bytes()
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, pin_memory=True)
     dst = torch.empty_like(src, device=dev)
     t_copy = eager_time(lambda: dst.copy_(src, non_blocking=True), reps=5)
-    # the chain: gather layer l+1 on the side stream while layer l decodes
-    side = torch.cuda.Stream()
-    main = torch.cuda.current_stream()
-    gather(0, stages[0])
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for l in range(chain):
-        if l + 1 < chain:
-            side.wait_stream(main)                      # stage (l+1) % 2 is free again
-            with torch.cuda.stream(side):
-                gather(l + 1, stages[(l + 1) % 2])
-        decode(stages[l % 2], l)
-        main.wait_stream(side)
-    torch.cuda.synchronize()
-    t_chain = time.perf_counter() - t0
     link = nbytes / t_copy / 1e9
     gbs = nbytes / t_gather / 1e9
-    t_or = oracle_time(lambda: O.decode_row(O.bf16_to_f64(inputs.bf16_bits(Q[0, 0, :cfg.G].cpu())), kk, vv,
-                                            lists[0][0, 0, 0].cpu().numpy(), T, 1.0 / math.sqrt(cfg.d)))
-    return {
-        "workload": f"{cfg.name}: B={cfg.B}, H_q={cfg.H_q}, H_kv={cfg.H_kv}, T={T}, {nsm} blocks per row from "
-                    f"pinned host memory ({n_host_layers} distinct host layers, chain of {chain})",
+    parts = chain * (t_sel + t_gather + t_dec)
+    best = min(res_pool.items(), key=lambda kv: kv[1]["chain_ms"])
+    for v in res_pool.values():
+        v["overlap"] = parts / (v["chain_ms"] * 1e-3)
+        v["host_link_gbs"] = chain * nbytes / (v["chain_ms"] * 1e-3) / 1e9
+    t_or = oracle_time(lambda: O.decode_row(O.bf16_to_f64(inputs.bf16_bits(Qs[0][0, 0, :cfg.G].cpu())), kk, vv,
+                                            bis[0][0, 0, 0].cpu().numpy(), T, 1.0 / math.sqrt(cfg.d)))
+    res = {
+        "workload": f"{cfg.name}: B={cfg.B}, H_q={cfg.H_q}, H_kv={cfg.H_kv}, T={T}, {nsm} blocks per row and layer "
+                    f"from pinned host memory, {nh} distinct host layers ({2 * nh * cfg.B * cfg.H_kv * T * cfg.d * 2 / 1e9:.1f}"
+                    f" GB pinned), chain of {chain}" + (f"; {note}" if note else ""),
         "gather_us": t_gather * 1e6,
         "gather_roofline": {"bound": "host link", "achieved_gbs": gbs, "peak_gbs": link,
                             "peak_kind": "measured pinned host -> device copy of the same size",
                             "frac": gbs / link, "algorithmic_bytes": int(nbytes)},
+        "select_us": t_sel * 1e6,
         "decode_from_stage_us": t_dec * 1e6,
-        "chain_ms": t_chain * 1e3,
-        "overlap": (chain * t_dec + (chain - 1) * t_gather) / t_chain,
+        "sum_of_parts_ms": parts * 1e3,
+        "persistent_pool": res_pool,
+        "persistent_pool_best": {"workgroups": int(best[0]), **best[1]},
+        "per_layer_gather_launches": {"chain_ms": t_launch_chain * 1e3, "overlap": parts / t_launch_chain,
+                                      "host_link_gbs": chain * nbytes / t_launch_chain / 1e9},
+        "transfer_bound_ms": chain * nbytes / (link * 1e9) * 1e3,
         "oracle_rows_per_s": 1.0 / t_or, "gpu_rows_per_s": cfg.B * cfg.H_kv / t_dec,
     }
+    del layers, host, kts
+    torch.cuda.empty_cache()
+    return res
 
 
 def copy_calibration(nbytes=1 << 30):
