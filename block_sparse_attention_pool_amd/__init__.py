@@ -49,6 +49,9 @@ _SIGNATURES = {
                                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                                             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
                                             _c_void_p]),
+    "sda_score_select_multihead_pooled_workspace": (_c_size_t, [_c_int] * 7),
+    "sda_score_select_multihead_pooled": (_c_int, [_c_void_p] * 3 + [_c_int] * 12 + [_c_float] + [_c_void_p] * 4
+                                          + [_c_size_t, _c_void_p]),
     "sda_sparse_decode_workspace": (_c_size_t, [_c_int] * 7),
     "sda_sparse_decode": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
                                    _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
@@ -331,6 +334,32 @@ def sda_score_select_multihead(q, k_tilde, seq_len, n_init, n_local, top_k, tau,
     _check(lib().sda_score_select_multihead(_ptr(q), _ptr(k_tilde), _ptr(seq_len), B, NQ, H_q, H, d, NB_cap,
                                             n_init, n_local, top_k, n_sel_max, float(tau), _ptr(block_idx),
                                             _ptr(n_sel), _ptr(scores), _ptr(ws), wsb, _stream(stream)))
+    return block_idx, n_sel
+
+
+def sda_score_select_multihead_pooled(q, k_tilde, seq_len, window, stride, n_init, n_local, top_k, tau, H_kv=None,
+                                      n_sel_max=None, block_idx=None, n_sel=None, scores=None, ws=None, stream=None):
+    """InfLLM-V2's G-head selector on overlapping compressed keys (kernel
+    `window`, stride `stride`): per-head softmax over the entries, sum over
+    the heads, max-pool onto the 64-token blocks, then top-k; returns
+    (block_idx, n_sel)."""
+    _need(q, "q", torch.bfloat16, 4)
+    B, NQ, H_q, d = q.shape
+    _need(k_tilde, "k_tilde", torch.bfloat16, (B, H_kv, None, d))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    H = k_tilde.shape[1]
+    NC_cap = k_tilde.shape[2]
+    if n_sel_max is None:
+        n_sel_max = block_idx.shape[-1] if block_idx is not None else n_init + n_local + top_k
+    block_idx, n_sel = _select_outputs(B, NQ, H, n_sel_max, block_idx, n_sel, q.device)
+    _opt(scores, "scores", torch.float32, (B, NQ, H, -(-NC_cap * int(stride) // BLOCK)))
+    nbytes = lib().sda_score_select_multihead_pooled_workspace(B, NQ, H_q, H, NC_cap, int(stride), top_k)
+    ws, wsb = _workspace(nbytes, q.device, ws)
+    _on_gpu(q=q, k_tilde=k_tilde, seq_len=seq_len, block_idx=block_idx, n_sel=n_sel, scores=scores, ws=ws)
+    _check(lib().sda_score_select_multihead_pooled(_ptr(q), _ptr(k_tilde), _ptr(seq_len), B, NQ, H_q, H, d, NC_cap,
+                                                   int(window), int(stride), n_init, n_local, top_k, n_sel_max,
+                                                   float(tau), _ptr(block_idx), _ptr(n_sel), _ptr(scores), _ptr(ws),
+                                                   wsb, _stream(stream)))
     return block_idx, n_sel
 
 

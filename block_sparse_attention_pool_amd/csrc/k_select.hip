@@ -540,7 +540,7 @@ template <int D>
 __global__ __launch_bounds__(256) void mh_score_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kt,
                                                        const int32_t* __restrict__ seq_len, float* __restrict__ z,
                                                        float* __restrict__ stats, int NQ, int H_q, int H_kv, int G,
-                                                       int NB_cap, float mult) {
+                                                       int NB_cap, float mult, int stride) {
     constexpr int KS = D / 32;                          // MFMA k-steps over the head dim
     __shared__ float red[4][16];
     const int row = blockIdx.y;                         // b * H_kv + g
@@ -548,7 +548,8 @@ __global__ __launch_bounds__(256) void mh_score_kernel(const uint16_t* __restric
     const int qi = blockIdx.z;
     const int nch = gridDim.x;
     const int j0 = blockIdx.x * kChunk;
-    const int nb = min((seq_len[b] + kBlock - 1) / kBlock, NB_cap);
+    // compressed entries present (one per `stride` tokens; 64 for block keys)
+    const int nb = min((seq_len[b] + stride - 1) / stride, NB_cap);
     const int lane = __lane_id(), li = lane & 15, lg = lane >> 4;
     const int wave = threadIdx.x / kWave;
     const size_t hrow0 = ((size_t)b * NQ + qi) * H_q + (size_t)g * G;   // first head row of the group
@@ -705,10 +706,10 @@ hipError_t launch_multihead_select(const uint16_t* q, const uint16_t* kt, const 
     dim3 grid(score_chunks(sel.NB_cap), B * sel.H_kv, sel.NQ), block(256);
     if (d == 128)
         hipLaunchKernelGGL(mh_score_kernel<128>, grid, block, 0, s, q, kt, sel.seq_len, z, stats, sel.NQ, H_q,
-                           sel.H_kv, G, sel.NB_cap, 1.f / tau);
+                           sel.H_kv, G, sel.NB_cap, 1.f / tau, kBlock);
     else
         hipLaunchKernelGGL(mh_score_kernel<64>, grid, block, 0, s, q, kt, sel.seq_len, z, stats, sel.NQ, H_q,
-                           sel.H_kv, G, sel.NB_cap, 1.f / tau);
+                           sel.H_kv, G, sel.NB_cap, 1.f / tau, kBlock);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (cand && counters) {
@@ -718,6 +719,124 @@ hipError_t launch_multihead_select(const uint16_t* q, const uint16_t* kt, const 
     }
     float* scores = scores_opt ? scores_opt : scores_ws;
     hipLaunchKernelGGL(mh_select_kernel<false>, grid, block, 0, s, z, stats, sel, H_q, G, scores, nullptr, nullptr);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SelectArgs sa = sel;
+    sa.scores = scores;
+    return launch_select(sa, s);
+}
+
+// InfLLM-V2's selector on overlapping compressed keys ([SparDA] §4.3 eq. (8)
+// and fig. 3: per-head softmax, sum over the G heads, max-pool onto the block
+// grid; §4.4: kernel l = 32, stride s = 16 at inference).  Launch 1 is
+// mh_score_kernel over the compressed entries (chunks of 256 entries);
+// launch 2, one workgroup per (256-block chunk, KV row, query), merges each
+// head's softmax statistics over all entry chunks, forms the entry sums
+// s_e = sum_h exp(z_he - M_h) / L_h for every entry whose window overlaps
+// its blocks (at most 256 * 64 / s + l / s of them, in LDS), takes for each
+// block the max over its overlapping windows (the pooled index's reading of
+// the overlap) and runs the selection as the other selectors do.
+template <bool FUSED>
+__global__ __launch_bounds__(256) void mh_pooled_select_kernel(const float* __restrict__ z,
+                                                               const float* __restrict__ stats, SelectArgs sel,
+                                                               int H_q, int G, int window, int stride, int NC_cap,
+                                                               int n_ech, float* scores_out, uint64_t* cand,
+                                                               int* counters) {
+    __shared__ float sc[1][kChunk];
+    __shared__ float se[kPoolMaxEntries];
+    __shared__ float pm[kMaxHeads][16], pl[kMaxHeads][16];
+    __shared__ float mh[kMaxHeads], il[kMaxHeads];
+    const int row = blockIdx.y;
+    const int H_kv = sel.H_kv, NQ = sel.NQ, NB_cap = sel.NB_cap;
+    const int b = row / H_kv, g = row - (row / H_kv) * H_kv;
+    const int q = blockIdx.z;
+    const int j0 = blockIdx.x * kChunk;
+    const int tid = threadIdx.x;
+    const size_t hrow0 = ((size_t)b * NQ + q) * H_q + (size_t)g * G;
+    const int sh = tid >> 4, sc0 = tid & 15;
+    const float* st = stats + (hrow0 + min(sh, G - 1)) * n_ech * 2;
+    float m = -INFINITY, l = 0.f;
+    if (sh < G)
+        for (int c = sc0; c < n_ech; c += 16) {
+            const float cm = st[2 * c], cl = st[2 * c + 1];
+            if (cm != -INFINITY) {
+                const float Mn = fmaxf(m, cm);
+                l = l * expf(m - Mn) + cl * expf(cm - Mn);
+                m = Mn;
+            }
+        }
+    pm[sh][sc0] = m;
+    pl[sh][sc0] = l;
+    __syncthreads();
+    if (tid < G) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) M = fmaxf(M, pm[tid][i]);
+        float L = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (pm[tid][i] != -INFINITY) L += pl[tid][i] * expf(pm[tid][i] - M);
+        mh[tid] = M;
+        il[tid] = 1.f / L;
+    }
+    __syncthreads();
+    const int len = sel.seq_len[b];
+    const int nb = min((len + kBlock - 1) / kBlock, NB_cap);
+    const int ne = min((len + stride - 1) / stride, NC_cap);
+    float sv = 0.f;
+    if (j0 < nb && ne > 0) {
+        // entries overlapping blocks [j0, min(j0 + 256, nb)): j s + l > 64 j0 and j s < 64 min(...)
+        const int lo_num = kBlock * j0 - window + 1;
+        const int e0 = lo_num > 0 ? (lo_num + stride - 1) / stride : 0;
+        const int e1 = min(ne - 1, (kBlock * min(j0 + kChunk, nb) - 1) / stride);
+        for (int e = e0 + tid; e <= e1; e += blockDim.x) {
+            const float* zc = z + hrow0 * NC_cap + e;
+            float s = 0.f;
+#pragma unroll
+            for (int h = 0; h < kMaxHeads; ++h)
+                if (h < G) s += expf(zc[(size_t)h * NC_cap] - mh[h]) * il[h];
+            se[e - e0] = s;
+        }
+        __syncthreads();
+        const int J = j0 + tid;
+        if (J < nb) {
+            const int ln = kBlock * J - window + 1;
+            const int lo = max(e0, ln > 0 ? (ln + stride - 1) / stride : 0);
+            const int hi = min(e1, (kBlock * J + kBlock - 1) / stride);
+            float mx = -INFINITY;
+            for (int e = lo; e <= hi; ++e) mx = fmaxf(mx, se[e - e0]);
+            sv = mx;
+            if (scores_out) scores_out[(((size_t)b * NQ + q) * H_kv + g) * NB_cap + J] = mx;
+        }
+    }
+    sc[0][tid] = sv;
+    if constexpr (FUSED) select_tail<1>(sel, cand, counters, sc, b, g, row, NQ, H_kv, NQ, q, j0, nb);
+}
+
+hipError_t launch_multihead_select_pooled(const uint16_t* q, const uint16_t* kt, const SelectArgs& sel, int B,
+                                          int H_q, int d, float tau, int window, int stride, int NC_cap, float* z,
+                                          float* stats, float* scores_opt, float* scores_ws, uint64_t* cand,
+                                          int* counters, hipStream_t s) {
+    const int G = H_q / sel.H_kv;
+    const int n_ech = score_chunks(NC_cap);
+    dim3 grid1(n_ech, B * sel.H_kv, sel.NQ), block(256);
+    if (d == 128)
+        hipLaunchKernelGGL(mh_score_kernel<128>, grid1, block, 0, s, q, kt, sel.seq_len, z, stats, sel.NQ, H_q,
+                           sel.H_kv, G, NC_cap, 1.f / tau, stride);
+    else
+        hipLaunchKernelGGL(mh_score_kernel<64>, grid1, block, 0, s, q, kt, sel.seq_len, z, stats, sel.NQ, H_q,
+                           sel.H_kv, G, NC_cap, 1.f / tau, stride);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 grid2(score_chunks(sel.NB_cap), B * sel.H_kv, sel.NQ);
+    if (cand && counters) {
+        hipLaunchKernelGGL(mh_pooled_select_kernel<true>, grid2, block, 0, s, z, stats, sel, H_q, G, window, stride,
+                           NC_cap, n_ech, scores_opt, cand, counters);
+        return hipGetLastError();
+    }
+    float* scores = scores_opt ? scores_opt : scores_ws;
+    hipLaunchKernelGGL(mh_pooled_select_kernel<false>, grid2, block, 0, s, z, stats, sel, H_q, G, window, stride,
+                       NC_cap, n_ech, scores, nullptr, nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     SelectArgs sa = sel;

@@ -317,6 +317,55 @@ sda_status_t sda_score_select_multihead(const void* q, const void* k_tilde, cons
                       "multihead score/select launch");
 }
 
+// InfLLM-V2's selector on overlapping compressed keys: [z and chunk statistics
+// over the NC_cap entries][block scores][candidate keys][arrival counters]
+size_t sda_score_select_multihead_pooled_workspace(int B, int NQ, int H_q, int H_kv, int NC_cap, int stride,
+                                                   int top_k) {
+    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || NC_cap < 1 || stride < 1 || top_k < 0) return 0;
+    const int NB_cap = pooled_nb_cap(NC_cap, stride);
+    return pad256(multihead_ws_floats(B, NQ, H_q, H_kv, NC_cap) * sizeof(float)) +
+           score_region_bytes(B, NQ, H_kv, NB_cap) + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k) +
+           (size_t)B * H_kv * NQ * sizeof(int);
+}
+
+sda_status_t sda_score_select_multihead_pooled(const void* q, const void* k_tilde, const int32_t* seq_len, int B,
+                                               int NQ, int H_q, int H_kv, int d, int NC_cap, int window, int stride,
+                                               int n_init, int n_local, int top_k, int n_sel_max, float tau,
+                                               int32_t* block_idx, int32_t* n_sel, float* scores_opt, void* ws,
+                                               size_t ws_bytes, void* stream) {
+    REQUIRE(q, SDA_ERR_NULL, "score_select_multihead_pooled: q is null");
+    TRY(check_pool(window, stride));
+    REQUIRE(NC_cap >= 1 && NC_cap <= (1 << 24), SDA_ERR_SHAPE, "NC_cap=%d out of range", NC_cap);
+    const int NB_cap = pooled_nb_cap(NC_cap, stride);
+    TRY(check_select_common(k_tilde, seq_len, B, NQ, H_kv, d, NB_cap, n_init, n_local, top_k, n_sel_max, block_idx,
+                            n_sel));
+    TRY(check_heads(H_q, H_kv));
+    REQUIRE(H_q / H_kv <= 16, SDA_ERR_UNSUPPORTED, "comparator supports G <= 16");
+    REQUIRE(tau > 0.f && isfinite(tau), SDA_ERR_SHAPE, "tau must be finite and > 0");
+    REQUIRE(aligned16(q), SDA_ERR_ALIGN, "q must be 16-byte aligned");
+    REQUIRE((long long)NQ <= kMaxGridYZ, SDA_ERR_SHAPE, "NQ too large");
+    const size_t need = sda_score_select_multihead_pooled_workspace(B, NQ, H_q, H_kv, NC_cap, stride, top_k);
+    REQUIRE(ws && ws_bytes >= need, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, need);
+    REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    REQUIRE(!scores_opt || aligned4(scores_opt), SDA_ERR_ALIGN, "scores_opt must be 4-byte aligned");
+    char* base = static_cast<char*>(ws);
+    float* z = reinterpret_cast<float*>(base);
+    float* stats = reinterpret_cast<float*>(base + pad256((size_t)B * NQ * H_q * NC_cap * sizeof(float)));
+    size_t off = pad256(multihead_ws_floats(B, NQ, H_q, H_kv, NC_cap) * sizeof(float));
+    float* scores_ws = reinterpret_cast<float*>(base + off);
+    off += score_region_bytes(B, NQ, H_kv, NB_cap);
+    uint64_t* cand = reinterpret_cast<uint64_t*>(base + off);
+    int* counters = reinterpret_cast<int*>(base + off + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k));
+    if (!fused_select_ok(NB_cap, top_k)) cand = nullptr, counters = nullptr;
+    SelectArgs a{seq_len, nullptr, B * NQ * H_kv, NQ, H_kv, NB_cap, n_init, n_local, top_k, n_sel_max,
+                 block_idx, n_sel};
+    return hip_status(launch_multihead_select_pooled(static_cast<const uint16_t*>(q),
+                                                     static_cast<const uint16_t*>(k_tilde), a, B, H_q, d, tau, window,
+                                                     stride, NC_cap, z, stats, scores_opt, scores_ws, cand, counters,
+                                                     static_cast<hipStream_t>(stream)),
+                      "multihead pooled score/select launch");
+}
+
 // ---------------------------------------------------------------------------
 size_t sda_sparse_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int split_k) {
     if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || H_q % H_kv) return 0;

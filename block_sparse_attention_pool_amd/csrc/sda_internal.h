@@ -67,6 +67,12 @@ hipError_t launch_multihead_select(const uint16_t* q, const uint16_t* kt, const 
                                    int d, float tau, float* z, float* stats, float* scores_opt, float* scores_ws,
                                    uint64_t* cand, int* counters, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+// the G-head comparator on overlapping compressed entries (kernel `window`,
+// stride `stride`, NC_cap per row), max-pooled onto the 64-token blocks
+hipError_t launch_multihead_select_pooled(const uint16_t* q, const uint16_t* kt, const SelectArgs& sel, int B,
+                                          int H_q, int d, float tau, int window, int stride, int NC_cap, float* z,
+                                          float* stats, float* scores_opt, float* scores_ws, uint64_t* cand,
+                                          int* counters, hipStream_t s);
 size_t multihead_ws_floats(int B, int NQ, int H_q, int H_kv, int NB_cap);
 int score_chunks(int NB_cap);
 

@@ -131,6 +131,31 @@ sda_status_t sda_score_select_multihead(const void* q, const void* k_tilde, cons
                                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * InfLLM-V2's block selector on overlapping compressed keys, the setting of
+ * the pages' selection-cost comparison ([SparDA] §4.3 eq. (8) and fig. 3:
+ * the G query heads of the KV group score every compressed key, each head's
+ * scores pass through a softmax over all entries, the G softmaxes are summed,
+ * and the sums are max-pooled onto the 64-token block grid; §4.4: kernel
+ * l = 32, stride s = 16 at inference): for each row,
+ *   s_e = sum_h softmax_e(q_h . K~_e / tau) over the ceil(seq_len / s) entries;
+ *   S_J = max of s_e over the windows that share a token with block J;
+ *   then init, local and top-k as sda_score_select.
+ * Arguments as sda_score_select_multihead, with k_tilde from
+ * sda_update_compressed_keys_strided ([B, H_kv, NC_cap, d]) and window /
+ * stride as sda_score_select_pooled; scores_opt [B, NQ, H_kv,
+ * ceil(NC_cap * stride / 64)] or NULL.  Workspace:
+ * sda_score_select_multihead_pooled_workspace() bytes, zero-filled before
+ * first use.
+ */
+size_t sda_score_select_multihead_pooled_workspace(int B, int NQ, int H_q, int H_kv, int NC_cap, int stride,
+                                                   int top_k);
+sda_status_t sda_score_select_multihead_pooled(const void* q, const void* k_tilde, const int32_t* seq_len, int B,
+                                               int NQ, int H_q, int H_kv, int d, int NC_cap, int window, int stride,
+                                               int n_init, int n_local, int top_k, int n_sel_max, float tau,
+                                               int32_t* block_idx, int32_t* n_sel, float* scores_opt, void* ws,
+                                               size_t ws_bytes, void* stream);
+
+/*
  * Overlapping compressed keys ([SparDA] prerequisites §3, eq. (4) with kernel
  * l = window and stride s = stride; §4.4 quotes InfLLM-V2's inference setting
  * l = 32, s = 16): entry j of a row is the mean of the keys

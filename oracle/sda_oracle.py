@@ -279,6 +279,21 @@ def select_row_pooled(f, kt_stored, T, window, stride, n_init, n_local, k):
     return block_set(nb, n_init, n_local, top_k(s, cand, k)), s
 
 
+def select_row_multihead_pooled(q_heads, kt_stored, T, window, stride, n_init, n_local, k, tau):
+    """InfLLM-V2's selector on overlapping compressed keys ([SparDA] §4.3
+    eq. (8) and fig. 3: per-head softmax over the compressed entries, sum over
+    the heads, max-pool onto the block grid; §4.4: l = 32, s = 16): the
+    summed softmax weight of every entry (ranked in float32, as the kernel
+    decides), max-pooled over the windows that share a token with each
+    block, then init U local U top-k.  kt_stored: [ceil(T/s), d].  Returns
+    (ascending block ids, pooled decision scores)."""
+    s_entries = decision_scores(multihead_scores(q_heads, kt_stored, tau))
+    s = max_pool_blocks(s_entries, T, window, stride)
+    nb = num_blocks(T)
+    cand = candidates(nb, n_init, n_local)
+    return block_set(nb, n_init, n_local, top_k(s, cand, k)), s
+
+
 # ---------------------------------------------------------------------------
 # O7  attention over the selected blocks  ([SparDA] eq. (7); [SSV] NSA
 #     selection-branch attention, step 3)

@@ -38,7 +38,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = header_functions()
-    assert len(names) == 29
+    assert len(names) == 31
     for n in names:
         assert hasattr(L, n), n
         assert n in sda.exported_symbols(), n

@@ -320,3 +320,32 @@ def test_mutant_prefill_not_causal(monkeypatch):
         return np.stack(outs), np.stack(lses)
     _patch(monkeypatch, "prefill_rows", bad)
     assert _fails(*_prefill_pins())
+
+
+@pytest.mark.parametrize("kind", ["sum_then_softmax", "mean_pool", "softmax_after_pool"])
+def test_mutant_multihead_pooled(monkeypatch, kind):
+    from tests import test_oracle_pooled as pp
+
+    def bad(q_heads, kt_stored, T, window, stride, n_init, n_local, k, tau):
+        if kind == "sum_then_softmax":             # raw head scores summed, one softmax
+            z = (np.asarray(q_heads) @ kt_stored.T).sum(0) / tau
+            e = np.exp(z - z.max())
+            s_e = impl.decision_scores(e / e.sum())
+            s = impl.max_pool_blocks(s_e, T, window, stride)
+        elif kind == "mean_pool":
+            s_e = impl.decision_scores(impl.multihead_scores(q_heads, kt_stored, tau))
+            nb = impl.num_blocks(T)
+            s = np.array([s_e[impl.pool_range(J, window, stride, s_e.size)[0]:
+                              impl.pool_range(J, window, stride, s_e.size)[1] + 1].mean() for J in range(nb)])
+        else:                                      # pool raw scores, softmax over blocks
+            z = (np.asarray(q_heads) @ kt_stored.T) / tau
+            pooled = np.stack([impl.max_pool_blocks(zh, T, window, stride) for zh in z])
+            pooled = pooled - pooled.max(axis=1, keepdims=True)
+            e = np.exp(pooled)
+            s = impl.decision_scores((e / e.sum(axis=1, keepdims=True)).sum(0))
+        nb = impl.num_blocks(T)
+        cand = impl.candidates(nb, n_init, n_local)
+        return impl.block_set(nb, n_init, n_local, impl.top_k(s, cand, k)), s
+    _patch(monkeypatch, "select_row_multihead_pooled", bad)
+    assert _fails(pp.test_multihead_pooled_64_64_is_the_plain_comparator,
+                  pp.test_multihead_pooled_block_scores_by_token_scan)

@@ -157,3 +157,54 @@ def test_pooled_selection_brute_force_small():
             want = sorted(set(range(min(n_init, nb))) | set(range(max(0, nb - n_local), nb)) | set(best))
             got, _ = O.select_row_pooled(f, kt, T, window, stride, n_init, n_local, kk)
             assert list(got) == want
+
+
+# ---------------------------------------------------------------------------
+# InfLLM-V2's G-head selector on overlapping compressed keys
+# ---------------------------------------------------------------------------
+
+def test_multihead_pooled_64_64_is_the_plain_comparator():
+    rng = np.random.default_rng(21)
+    T = 64 * 40 + 9
+    k = rng.standard_normal((T, 16))
+    kt = O.compressed_keys_strided(k, T, 64, 64)
+    qh = rng.standard_normal((4, 16))
+    a, sa = O.select_row_multihead_pooled(qh, kt, T, 64, 64, 1, 2, 5, 4.0)
+    b, sb = O.select_row_multihead(qh, kt, 1, 2, 5, 4.0)
+    assert list(a) == list(b) and np.array_equal(sa, sb)
+
+
+def test_multihead_pooled_one_head_ranks_like_the_pooled_indexer():
+    # one head: the entry softmax is a monotone map of the raw scores, and a
+    # max commutes with a monotone map, so the block ranking is the indexer's
+    rng = np.random.default_rng(22)
+    T = 64 * 50
+    k = rng.standard_normal((T, 16))
+    kt = O.compressed_keys_strided(k, T, 32, 16)
+    f = rng.standard_normal(16)
+    a, _ = O.select_row_multihead_pooled(f[None], kt, T, 32, 16, 1, 2, 7, 3.0)
+    b, _ = O.select_row_pooled(f, kt, T, 32, 16, 1, 2, 7)
+    assert list(a) == list(b)
+
+
+def test_multihead_pooled_block_scores_by_token_scan():
+    # block score = the largest summed softmax weight among the windows that
+    # hold one of the block's tokens; softmax written out with plain exp
+    rng = np.random.default_rng(23)
+    T, window, stride, d, G, tau = 64 * 6 + 30, 32, 16, 8, 3, 2.0
+    k = rng.standard_normal((T, d))
+    kt = O.compressed_keys_strided(k, T, window, stride)
+    qh = rng.standard_normal((G, d))
+    members = _windows_by_token_scan(T, window, stride)
+    ssum = {}
+    for h in range(G):
+        z = {j: float(qh[h] @ kt[j]) / tau for j in members}
+        zmax = max(z.values())
+        tot = sum(np.exp(v - zmax) for v in z.values())
+        for j in members:
+            ssum[j] = ssum.get(j, 0.0) + np.exp(z[j] - zmax) / tot
+    _, got = O.select_row_multihead_pooled(qh, kt, T, window, stride, 0, 1, 2, tau)
+    for J in range(O.num_blocks(T)):
+        toks = set(range(J * 64, min(J * 64 + 64, T)))
+        want = max(ssum[j] for j, ts in members.items() if toks & set(ts))
+        assert abs(got[J] - want) <= 1e-7 * max(1.0, want)
