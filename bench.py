@@ -304,9 +304,20 @@ def measure_rows(cfg, layers, only=None):
         Qd = O.bf16_to_f64(inputs.bf16_bits(ln["Q"][0, 0, :G]))
         ktd = O.store_bf16(O.compressed_keys(kk, T))
         t_or = oracle_time(lambda: O.select_row_multihead(Qd, ktd, cfg.n_init, cfg.n_local, cfg.top_k, tau))
+        wss = torch.zeros(sda.lib().sda_score_select_workspace(cfg.B, 1, cfg.H_kv, cfg.NB, cfg.top_k),
+                          dtype=torch.uint8, device=dev)
+        turn[0] = 0
+
+        def sel_call():
+            lay = layers[turn[0] % L]
+            turn[0] += 1
+            sda.sda_score_select(lay["F"], lay["kt"], full, cfg.n_init, cfg.n_local, cfg.top_k, block_idx=bi,
+                                 n_sel=ns, ws=wss)
+        t_fc = graph_time(sel_call, copies=L)
         rows["a7_comparator"] = {
             "workload": f"{cfg.name}: G = {G} heads per KV group, tau = sqrt(d)",
             "us": t_mh * 1e6, "roofline": hbm(cfg.ktilde_bytes(), t_mh),
+            "forecast_select_us": t_fc * 1e6, "g_head_over_forecast": t_mh / t_fc,
             "oracle_rows_per_s": 1.0 / t_or, "gpu_rows_per_s": nrow / t_mh,
         }
     if "c2" in want:
@@ -500,6 +511,19 @@ def measure_pooled(cfg, layers, O, full, prev, window=32, stride=16):
         sda.sda_score_select_pooled(layers[i]["F"], kts[(i + 1) % L], full, window, stride, cfg.n_init,
                                     cfg.n_local, cfg.top_k, block_idx=bi, n_sel=ns, ws=ws)
     t_sel = graph_time(pooled_call, copies=L)
+    # InfLLM-V2's own selector in the same setting: the G query heads of the
+    # next layer, per-head softmax over the compressed entries, sum, max-pool
+    wsm = torch.zeros(sda.lib().sda_score_select_multihead_pooled_workspace(cfg.B, 1, cfg.H_q, cfg.H_kv, nc, stride,
+                                                                           cfg.top_k), dtype=torch.uint8, device=dev)
+    tau = math.sqrt(d)
+    turn[0] = 0
+
+    def mh_pooled_call():
+        i = turn[0] % L
+        turn[0] += 1
+        sda.sda_score_select_multihead_pooled(layers[(i + 1) % L]["Q"], kts[(i + 1) % L], full, window, stride,
+                                              cfg.n_init, cfg.n_local, cfg.top_k, tau, block_idx=bi, n_sel=ns, ws=wsm)
+    t_mh = graph_time(mh_pooled_call, copies=L)
     # oracle: one row's window means, scores, pool and selection
     kk = O.bf16_to_f64(inputs.bf16_bits(K0[0, 0]))
     f0 = O.bf16_to_f64(inputs.bf16_bits(layers[0]["F"][0, 0, 0]))
@@ -516,6 +540,9 @@ def measure_pooled(cfg, layers, O, full, prev, window=32, stride=16):
         "per_token_update_roofline": hbm(nrow * tok_bytes, t_tok),
         "select_us": t_sel * 1e6,
         "select_roofline": hbm(kt_bytes, t_sel),
+        "g_head_select_us": t_mh * 1e6,
+        "g_head_select_roofline": hbm(kt_bytes, t_mh),
+        "g_head_over_forecast": t_mh / t_sel,
         "oracle_rows_per_s_keys": 1.0 / t_or_keys,
         "oracle_rows_per_s_select": 1.0 / t_or_sel,
         "gpu_rows_per_s_select": nrow / t_sel,
@@ -1303,6 +1330,15 @@ def main():
         res["cpu_baseline"] = cpu
     if not args.no_rows:
         res["rows"] = measure_rows(cfg, layers, args.rows.split(",") if args.rows else None)
+        # the pages' selection-cost comparison: the G-head selector's time over
+        # the one-head indexer's on the same compressed keys
+        ratio = {}
+        if "a7_comparator" in res["rows"]:
+            ratio["64/64 blocks"] = res["rows"]["a7_comparator"]["g_head_over_forecast"]
+        if "n1_pooled_select" in res["rows"]:
+            ratio["32/16 compressed keys, max-pooled"] = res["rows"]["n1_pooled_select"]["g_head_over_forecast"]
+        if ratio:
+            res["selection_cost_ratio_g_head_over_forecast"] = ratio
     print(json.dumps(res))
 
 

@@ -255,3 +255,73 @@ def test_c3_pooled_128k_sampled_rows():
             rest = [j for j in cand if j not in chosen]
             assert len(top) == cfg.top_k
             assert sc[b, 0, g, top].min() >= sc[b, 0, g, rest].max()
+
+
+# ---------------------------------------------------------------------------
+# InfLLM-V2's G-head selector on overlapping compressed keys
+# ---------------------------------------------------------------------------
+
+MH_CASES = [
+    # (B, H_kv, G, d, lengths, window, stride, n_init, n_local, top_k)
+    (2, 2, 8, 128, [16384, 9000], 32, 16, 1, 2, 16),
+    (1, 2, 4, 64, [4096], 32, 16, 1, 2, 8),
+    (2, 1, 8, 128, [20, 4000], 64, 32, 0, 1, 5),
+    (1, 2, 8, 128, [16384], 32, 16, 1, 2, 80),        # top_k past the in-launch selection
+]
+
+
+@pytest.mark.parametrize("case", MH_CASES)
+def test_multihead_pooled_select_matches_oracle(case):
+    import math
+    B, H, G, d, lens, window, stride, n_init, n_local, k = case
+    _say("multihead pooled", case)
+    T_cap = max(lens)
+    cfg = dataclasses.replace(synth.get_config(2), B=B, H_kv=H, H_q=H * G, d=d, T=T_cap, n_init=n_init,
+                              n_local=n_local, top_k=k, bias_frac=0.0, bias_beta=0.0)
+    K, _, _ = inputs.kv_layer(cfg, 0, device="cpu")
+    kt = _strided_gpu(K.to(DEV), None, window, stride, lens=lens)
+    ktc = {(b, g): _oracle_strided(K, b, g, lens[b], window, stride) for b in range(B) for g in range(H)}
+    tau = math.sqrt(d)
+    rng = np.random.default_rng(len(lens) * 7 + k)
+    Qf = rng.standard_normal((B, 1, H * G, d)).astype(np.float32)
+    for _ in range(100):          # re-draw the heads of rows whose top-k cut is a near-tie
+        Q = inputs.to_bf16(Qf)
+        Qd = O.bf16_to_f64(bits(Q))
+        bad = []
+        for b in range(B):
+            for g in range(H):
+                _, s = O.select_row_multihead_pooled(Qd[b, 0, g * G:(g + 1) * G], ktc[(b, g)], lens[b], window,
+                                                     stride, n_init, n_local, k, tau)
+                cand = O.candidates(O.num_blocks(lens[b]), n_init, n_local)
+                if k < cand.size and O.cut_gap(s, cand, k) < 1e-4 * abs(np.sort(s[cand])[::-1][k - 1]):
+                    bad.append((b, g))
+        if not bad:
+            break
+        for (b, g) in bad:
+            Qf[b, 0, g * G:(g + 1) * G] = rng.standard_normal((G, d))
+    seq = torch.as_tensor(lens, dtype=torch.int32, device=DEV)
+    NB_cap = -(-kt.shape[2] * stride // 64)
+    scores = torch.full((B, 1, H, NB_cap), float("nan"), dtype=torch.float32, device=DEV)
+    bi, ns = sda.sda_score_select_multihead_pooled(Q.to(DEV), kt, seq, window, stride, n_init, n_local, k, tau,
+                                                   scores=scores)
+    torch.cuda.synchronize()
+    rows, want, worst, skipped = [], {}, 0.0, 0
+    for b in range(B):
+        for g in range(H):
+            T = lens[b]
+            sel, s = O.select_row_multihead_pooled(Qd[b, 0, g * G:(g + 1) * G], ktc[(b, g)], T, window, stride,
+                                                   n_init, n_local, k, tau)
+            got = scores[b, 0, g, :s.size].double().cpu().numpy()
+            worst = max(worst, float(np.abs(got - s).max() / max(1e-30, np.abs(s).max())))
+            cand = O.candidates(O.num_blocks(T), n_init, n_local)
+            if k < cand.size:
+                top = np.sort(s[cand])[::-1][k - 1]
+                if O.cut_gap(s, cand, k) < 1e-4 * abs(top):
+                    skipped += 1
+                    continue
+            rows.append((b, 0, g))
+            want[(b, 0, g)] = sel
+    _say(f"  max relative |block score - oracle| {worst:.2e}; {len(rows)} rows compared, {skipped} near-ties")
+    assert worst < 1e-4
+    assert skipped == 0
+    _check_rows(bi, ns, want, rows)
