@@ -888,6 +888,7 @@ __global__ __launch_bounds__(NT == 1 ? kMaxWaves * 64 : 256) void attn_kernel(At
 int attn_rows_pad(int C, int G) { return (C * G <= 16) ? 16 : 32; }
 
 constexpr size_t kLdsPerCU = 160 * 1024;
+constexpr int kPlanMaxSplits = 1024;          // the planner tries at most this many splits
 constexpr int kMaxGridRows = 65535;
 
 
@@ -914,7 +915,7 @@ AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode
     AttnPlan best{1, 1};
     long long best_cost = -1, best_flight = -1, best_cus = -1;
     const long long total = (long long)tasks * list_max;
-    for (int ns = 1; ns <= list_max; ++ns) {
+    for (int ns = 1; ns <= min(list_max, kPlanMaxSplits); ++ns) {
         const int per_split = (list_max + ns - 1) / ns;
         for (int W = 1; W <= min(max_w, per_split); ++W) {
             const size_t lds = smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W);

@@ -28,7 +28,7 @@
 namespace sda {
 
 
-int score_chunks(int NB_cap) { return (NB_cap + kChunk - 1) / kChunk; }
+int score_chunks(int NB_cap) { return (int)(((long long)NB_cap + kChunk - 1) / kChunk); }
 
 // ---------------------------------------------------------------------------
 // block-wide helpers (256 threads)
@@ -459,13 +459,13 @@ static void launch_score_d(const ScoreArgs& a, int B, hipStream_t s) {
 int score_tile_vectors(int nvec, int NB_cap, int rows) {
     int nv = 1;
     while (nv < nvec && nv < 16) nv *= 2;
-    while (nv > 1 && (long long)score_chunks(NB_cap) * rows * ((nvec + nv - 1) / nv) < 2LL * kCUs) nv /= 2;
+    while (nv > 1 && (long long)score_chunks(NB_cap) * rows * (((long long)nvec + nv - 1) / nv) < 2LL * kCUs) nv /= 2;
     return nv;
 }
 
 int score_tiles(int NQ, int NB_cap, int rows) {
     const int nv = score_tile_vectors(NQ, NB_cap, rows);
-    return (NQ + nv - 1) / nv;
+    return (int)(((long long)NQ + nv - 1) / nv);
 }
 
 bool fused_select_ok(int NB_cap, int top_k) {

@@ -7,6 +7,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <climits>
+#include <initializer_list>
 #include <string>
 
 #include "../../include/sda.h"
@@ -41,9 +43,30 @@ constexpr int kBlock = SDA_BLOCK_TOKENS;
 constexpr int kMaxGridYZ = 65535;
 constexpr int kMaxNBCap = 16384;      // select keeps <= 64 keys per lane
 constexpr int kMaxSplits = 1024;
+constexpr int kMaxListLen = 65536;   // entries per block list (4M tokens of selected context)
 constexpr size_t kLdsBytes = 160 * 1024;
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// every count the kernels and the planners form in int (rows, row groups,
+// blocks of all rows) must fit in int: the product of the given sizes, each
+// at least 1, is checked before any of them is multiplied in int
+bool fits_int(std::initializer_list<long long> xs) {
+    long long p = 1;
+    for (const long long x : xs) {
+        if (x < 1 || p > INT_MAX / x) return false;
+        p *= x;
+    }
+    return true;
+}
+
+// the sizes every attention-family workspace query and call share: row
+// counts that fit in int, a supported head dim and GQA ratio, lists of at
+// most kMaxListLen entries, split_k in [0, kMaxSplits]
+bool attn_sizes_ok(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int split_k) {
+    return fits_int({B, NQ, H_q}) && H_kv >= 1 && H_q % H_kv == 0 && H_q / H_kv <= 32 && (d == 64 || d == 128) &&
+           n_sel_max >= 1 && n_sel_max <= kMaxListLen && split_k >= 0 && split_k <= kMaxSplits;
+}
 
 #define REQUIRE(cond, st, ...)                    \
     do {                                          \
@@ -95,7 +118,10 @@ void set_workspace(AttnArgs& a, void* ws, size_t need, int tasks, int ns, int rp
 extern "C" {
 
 const char* sda_status_string(sda_status_t s) {
-    switch (s) {
+    // a C caller may pass any int: read the bits, not an out-of-range enum value
+    int v;
+    memcpy(&v, &s, sizeof v);
+    switch (v) {
         case SDA_OK: return "SDA_OK";
         case SDA_ERR_NULL: return "SDA_ERR_NULL";
         case SDA_ERR_SHAPE: return "SDA_ERR_SHAPE";
@@ -132,6 +158,8 @@ sda_status_t sda_update_compressed_keys(const void* k, void* k_tilde, const int3
                                                     static_cast<hipStream_t>(stream)),
                       "update_compressed_keys launch");
 }
+
+static bool stride_ok(int stride) { return stride == 8 || stride == 16 || stride == 32 || stride == 64; }
 
 // overlapping compression: window (kernel) and stride in tokens
 static sda_status_t check_pool(int window, int stride) {
@@ -179,7 +207,7 @@ static size_t cand_region_bytes(int B, int NQ, int H_kv, int NB_cap, int top_k) 
 }
 
 size_t sda_score_select_workspace(int B, int NQ, int H_kv, int NB_cap, int top_k) {
-    if (B < 1 || NQ < 1 || H_kv < 1 || NB_cap < 1 || top_k < 0) return 0;
+    if (!fits_int({B, NQ, H_kv}) || NB_cap < 1 || NB_cap > kMaxNBCap || top_k < 0) return 0;
     return score_region_bytes(B, NQ, H_kv, NB_cap) + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k) +
            (size_t)B * H_kv * score_tiles(NQ, NB_cap, B * H_kv) * sizeof(int);
 }
@@ -197,7 +225,7 @@ static sda_status_t check_select_common(const void* k_tilde, const int32_t* seq_
     REQUIRE(n_sel_max >= 1 && (long long)n_sel_max >= (long long)n_init + n_local + top_k, SDA_ERR_SHAPE,
             "n_sel_max=%d < n_init+n_local+top_k=%lld", n_sel_max, (long long)n_init + n_local + top_k);
     REQUIRE((long long)B * H_kv <= kMaxGridYZ, SDA_ERR_SHAPE, "B*H_kv exceeds %d", kMaxGridYZ);
-    REQUIRE((long long)B * NQ * H_kv <= (1LL << 31) - 1, SDA_ERR_SHAPE, "too many rows");
+    REQUIRE(fits_int({B, NQ, H_kv}), SDA_ERR_SHAPE, "B*NQ*H_kv exceeds the int range");
     REQUIRE(aligned16(k_tilde), SDA_ERR_ALIGN, "k_tilde must be 16-byte aligned");
     REQUIRE(aligned4(seq_len) && aligned4(block_idx) && aligned4(n_sel), SDA_ERR_ALIGN,
             "int32 arrays must be 4-byte aligned");
@@ -238,7 +266,9 @@ sda_status_t sda_score_select(const void* f, const void* k_tilde, const int32_t*
 static int pooled_nb_cap(int NC_cap, int stride) { return ceil_div((long long)NC_cap * stride, kBlock); }
 
 size_t sda_score_select_pooled_workspace(int B, int NQ, int H_kv, int NC_cap, int stride, int top_k) {
-    if (B < 1 || NQ < 1 || H_kv < 1 || NC_cap < 1 || stride < 1 || top_k < 0) return 0;
+    if (!fits_int({B, NQ, H_kv}) || !stride_ok(stride) || NC_cap < 1 || pooled_nb_cap(NC_cap, stride) > kMaxNBCap ||
+        top_k < 0)
+        return 0;
     const int NB_cap = pooled_nb_cap(NC_cap, stride);
     return score_region_bytes(B, NQ, H_kv, NB_cap) + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k) +
            (size_t)B * H_kv * NQ * sizeof(int);
@@ -277,7 +307,7 @@ sda_status_t sda_score_select_pooled(const void* f, const void* k_tilde, const i
 // [z f32 and per-chunk statistics][scores f32, B*NQ*H_kv*NB_cap][candidate keys u64
 // (in-launch selection only)][arrival counters i32, B*H_kv*NQ], 256-B aligned regions
 size_t sda_score_select_multihead_workspace(int B, int NQ, int H_q, int H_kv, int NB_cap, int top_k) {
-    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || NB_cap < 1 || top_k < 0) return 0;
+    if (!fits_int({B, NQ, H_q}) || H_kv < 1 || H_q % H_kv || NB_cap < 1 || NB_cap > kMaxNBCap || top_k < 0) return 0;
     return pad256(multihead_ws_floats(B, NQ, H_q, H_kv, NB_cap) * sizeof(float)) +
            score_region_bytes(B, NQ, H_kv, NB_cap) + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k) +
            (size_t)B * H_kv * NQ * sizeof(int);
@@ -321,7 +351,9 @@ sda_status_t sda_score_select_multihead(const void* q, const void* k_tilde, cons
 // over the NC_cap entries][block scores][candidate keys][arrival counters]
 size_t sda_score_select_multihead_pooled_workspace(int B, int NQ, int H_q, int H_kv, int NC_cap, int stride,
                                                    int top_k) {
-    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || NC_cap < 1 || stride < 1 || top_k < 0) return 0;
+    if (!fits_int({B, NQ, H_q}) || H_kv < 1 || H_q % H_kv || !stride_ok(stride) || NC_cap < 1 ||
+        NC_cap > kMaxNBCap * (kBlock / stride) || top_k < 0)
+        return 0;
     const int NB_cap = pooled_nb_cap(NC_cap, stride);
     return pad256(multihead_ws_floats(B, NQ, H_q, H_kv, NC_cap) * sizeof(float)) +
            score_region_bytes(B, NQ, H_kv, NB_cap) + cand_region_bytes(B, NQ, H_kv, NB_cap, top_k) +
@@ -368,7 +400,7 @@ sda_status_t sda_score_select_multihead_pooled(const void* q, const void* k_tild
 
 // ---------------------------------------------------------------------------
 size_t sda_sparse_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int split_k) {
-    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || H_q % H_kv) return 0;
+    if (!attn_sizes_ok(B, NQ, H_q, H_kv, n_sel_max, d, split_k)) return 0;
     const int G = H_q / H_kv;
     const int rp = attn_rows_pad(1, G);
     const int tasks = B * NQ * H_kv;
@@ -385,6 +417,8 @@ static sda_status_t check_attn_common(const void* q, const void* k, const void* 
     TRY(check_heads(H_q, H_kv));
     REQUIRE(B >= 1 && NQ >= 1 && T_cap >= 1 && n_sel_max >= 1, SDA_ERR_SHAPE,
             "B=%d NQ=%d T_cap=%d n_sel_max=%d must be >= 1", B, NQ, T_cap, n_sel_max);
+    REQUIRE(n_sel_max <= kMaxListLen, SDA_ERR_UNSUPPORTED, "n_sel_max=%d exceeds %d entries", n_sel_max, kMaxListLen);
+    REQUIRE(fits_int({B, NQ, H_q}), SDA_ERR_SHAPE, "B*NQ*H_q exceeds the int range");
     REQUIRE(split_k >= 0 && split_k <= kMaxSplits, SDA_ERR_SHAPE, "split_k=%d outside [0, %d]", split_k, kMaxSplits);
     REQUIRE(isfinite(scale) && scale > 0.f, SDA_ERR_SHAPE, "scale must be finite and > 0");
     REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), SDA_ERR_ALIGN,
@@ -480,8 +514,9 @@ static NsaPlan nsa_plan(int d, int rp, int tasks, int group_C, int mode, int T_c
 
 size_t sda_nsa_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int T_cap, int NC_cap,
                                 int window, int group_C, int mode) {
-    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || group_C < 1 || H_q % H_kv || T_cap < 1 ||
-        NC_cap < 1 || window < 0)
+    if (!attn_sizes_ok(B, NQ, H_q, H_kv, n_sel_max, d, 0) || group_C < 1 || group_C > 8 ||
+        group_C * (H_q / H_kv) > 32 || T_cap < 1 || ceil_div(T_cap, kBlock) > kMaxNBCap || NC_cap < 1 ||
+        window < 0 || (mode != SDA_GROUP_EXACT && mode != SDA_GROUP_SHARED_REP))
         return 0;
     const int rp = attn_rows_pad(group_C, H_q / H_kv);
     const int tasks = B * ceil_div(NQ, group_C) * H_kv;
@@ -581,15 +616,18 @@ static bool step_fused_plan(int B, int H_q, int H_kv, int d, int n_sel_max, int 
 
 int sda_decode_step_is_fused(int B, int H_q, int H_kv, int d, int n_sel_max, int split_k, int NB_cap_next,
                              int top_k) {
-    if (B < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || NB_cap_next < 1 || top_k < 0 || H_q % H_kv) return 0;
-    if (check_d(d) != SDA_OK) return 0;
+    if (!attn_sizes_ok(B, 1, H_q, H_kv, n_sel_max, d, split_k) || NB_cap_next < 1 || NB_cap_next > kMaxNBCap ||
+        top_k < 0)
+        return 0;
     AttnPlan plan{};
     return step_fused_plan(B, H_q, H_kv, d, n_sel_max, split_k, NB_cap_next, top_k, &plan) ? 1 : 0;
 }
 
 size_t sda_decode_step_workspace(int B, int H_q, int H_kv, int d, int n_sel_max, int split_k, int NB_cap_next,
                                  int top_k) {
-    if (B < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || NB_cap_next < 1 || top_k < 0 || H_q % H_kv) return 0;
+    if (!attn_sizes_ok(B, 1, H_q, H_kv, n_sel_max, d, split_k) || NB_cap_next < 1 || NB_cap_next > kMaxNBCap ||
+        top_k < 0)
+        return 0;
     AttnPlan plan{};
     size_t dec;
     if (step_fused_plan(B, H_q, H_kv, d, n_sel_max, split_k, NB_cap_next, top_k, &plan))
@@ -874,8 +912,7 @@ sda_status_t sda_prefill_select(const void* f, const void* k_tilde, const int32_
 static int prefill_group(int G) { return std::max(1, std::min(8, 32 / G)); }
 
 size_t sda_prefill_attention_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap) {
-    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv || H_q / H_kv > 32 || n_sel_max < 1 || NB_cap < 1)
-        return 0;
+    if (!attn_sizes_ok(B, NQ, H_q, H_kv, n_sel_max, d, 0) || NB_cap < 1 || NB_cap > kMaxNBCap) return 0;
     return sda_grouped_decode_workspace(B, NQ, H_q, H_kv, n_sel_max, d, NB_cap, prefill_group(H_q / H_kv),
                                         SDA_GROUP_EXACT, 0);
 }
@@ -937,7 +974,9 @@ sda_status_t sda_prefill_attention(const void* q, const void* k, const void* v, 
 
 size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap,
                                     int group_C, int mode, int split_k) {
-    if (B < 1 || NQ < 1 || H_q < 1 || H_kv < 1 || n_sel_max < 1 || group_C < 1 || H_q % H_kv || NB_cap < 1)
+    if (!attn_sizes_ok(B, NQ, H_q, H_kv, n_sel_max, d, split_k) || group_C < 1 || group_C > 8 ||
+        group_C * (H_q / H_kv) > 32 || NB_cap < 1 || NB_cap > kMaxNBCap ||
+        (mode != SDA_GROUP_EXACT && mode != SDA_GROUP_SHARED_REP))
         return 0;
     const int G = H_q / H_kv;
     const int n_groups = ceil_div(NQ, group_C);
@@ -1041,8 +1080,9 @@ constexpr int kPfSpinLimit = 1 << 20;          // polls of ~3.4 us each before a
 
 size_t sda_offload_chain_workspace(int L, int B, int H_q, int H_kv, int d, int T_cap, int n_init, int n_local,
                                    int top_k) {
-    if (L < 1 || L > kMaxChainLayers || B < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv || T_cap < 1 || n_init < 0 ||
-        n_local < 0 || top_k < 0 || n_init + n_local + top_k < 1)
+    const long long nsm = (long long)n_init + n_local + top_k;
+    if (L < 1 || L > kMaxChainLayers || !attn_sizes_ok(B, 1, H_q, H_kv, 1, d, 0) || T_cap < 1 ||
+        ceil_div(T_cap, kBlock) > kMaxNBCap || n_init < 0 || n_local < 0 || top_k < 0 || nsm < 1 || nsm > kMaxListLen)
         return 0;
     return chain_layout(L, B, H_q, H_kv, d, T_cap, n_init + n_local + top_k, top_k).total;
 }
@@ -1060,10 +1100,12 @@ sda_status_t sda_offload_chain(const sda_offload_layer* layers, int L, const int
     REQUIRE(side_stream != stream, SDA_ERR_SHAPE, "offload_chain: the pool needs a stream of its own");
     TRY(check_d(d));
     TRY(check_heads(H_q, H_kv));
+    REQUIRE(B >= 1 && T_cap >= 1 && n_init >= 0 && n_local >= 0 && top_k >= 0, SDA_ERR_SHAPE,
+            "offload_chain: bad sizes");
+    REQUIRE((long long)n_init + n_local + top_k >= 1 && (long long)n_init + n_local + top_k <= kMaxListLen,
+            SDA_ERR_SHAPE, "offload_chain: n_init+n_local+top_k outside [1, %d]", kMaxListLen);
     const int nsm = n_init + n_local + top_k;
     const int NB_cap = ceil_div(T_cap, kBlock);
-    REQUIRE(B >= 1 && T_cap >= 1 && nsm >= 1 && n_init >= 0 && n_local >= 0 && top_k >= 0, SDA_ERR_SHAPE,
-            "offload_chain: bad sizes");
     REQUIRE((long long)B * H_kv <= kMaxGridYZ, SDA_ERR_SHAPE, "B*H_kv exceeds %d", kMaxGridYZ);
     REQUIRE(aligned16(f_first), SDA_ERR_ALIGN, "f_first must be 16-byte aligned");
     const ChainLayout c = chain_layout(L, B, H_q, H_kv, d, T_cap, nsm, top_k);
@@ -1121,8 +1163,8 @@ sda_status_t sda_offload_chain(const sda_offload_layer* layers, int L, const int
     if (e == hipSuccess) e = launch_prefetch_pool(pa, d, prefetch_workgroups, side);
     if (e == hipSuccess) e = hipEventRecord(ev_end, side);
     if (e != hipSuccess) {
-        hipEventDestroy(ev_start);
-        if (ev_end) hipEventDestroy(ev_end);
+        (void)hipEventDestroy(ev_start);
+        if (ev_end) (void)hipEventDestroy(ev_end);
         return hip_status(e, "offload_chain: pool launch");
     }
     sda_status_t st = SDA_OK;
@@ -1152,8 +1194,8 @@ sda_status_t sda_offload_chain(const sda_offload_layer* layers, int L, const int
     // end the pool (also after an error) and order the stream after its exit
     e = launch_prefetch_stop(ctrl, s);
     hipError_t e2 = hipStreamWaitEvent(s, ev_end, 0);
-    hipEventDestroy(ev_start);
-    hipEventDestroy(ev_end);
+    (void)hipEventDestroy(ev_start);
+    (void)hipEventDestroy(ev_end);
     if (st != SDA_OK) return st;
     if (e == hipSuccess) e = e2;
     return hip_status(e, "offload_chain: pool stop");
@@ -1170,7 +1212,7 @@ sda_status_t sda_gather_blocks(const void* k_src, const void* v_src, const int32
     REQUIRE(B >= 1 && H_kv >= 1 && n_sel_max >= 1 && T_cap >= 1, SDA_ERR_SHAPE,
             "B=%d H_kv=%d n_sel_max=%d T_cap=%d must be >= 1", B, H_kv, n_sel_max, T_cap);
     REQUIRE(max_workgroups >= 0, SDA_ERR_SHAPE, "max_workgroups=%d < 0", max_workgroups);
-    REQUIRE((long long)B * H_kv * n_sel_max <= (1LL << 31) - 1, SDA_ERR_SHAPE, "too many entries");
+    REQUIRE(fits_int({B, H_kv, n_sel_max}), SDA_ERR_SHAPE, "B*H_kv*n_sel_max exceeds the int range");
     REQUIRE(aligned16(k_src) && aligned16(v_src) && aligned16(k_stage) && aligned16(v_stage), SDA_ERR_ALIGN,
             "source and stage buffers must be 16-byte aligned");
     REQUIRE(aligned4(block_idx) && aligned4(n_sel) && aligned4(slot_out), SDA_ERR_ALIGN,
