@@ -445,9 +445,9 @@ def measure_prefill(cid=2):
                 top1 = set(a1) - set(range(cfg.n_init)) - set(range((T - 1024 + i) // 64 - 1, (T - 1024 + i) // 64 + 1))
                 ov.append(len(top0 & top1) / max(1, len(top0)))
     ov = float(np.mean(ov))
-    # blocks the attention loads: the union of each group's lists (groups of
-    # min(8, 32 / G) consecutive positions)
-    C = max(1, min(8, 32 // G))
+    # blocks the attention loads: the union of each tile's lists (tiles of
+    # min(32, 128 / G) consecutive positions, one fetch per block and tile)
+    C = max(1, min(32, 128 // G))
     grp = bi_h.reshape(cfg.B, T // C, C, cfg.H_kv, nsm).transpose(0, 1, 3, 2, 4).reshape(cfg.B, T // C, cfg.H_kv, -1)
     grp = np.sort(grp, axis=-1)
     loads = int(((np.diff(grp, axis=-1) != 0) & (grp[..., 1:] >= 0)).sum() + (grp[..., 0] >= 0).sum())

@@ -32,36 +32,13 @@
 #include <limits.h>
 #include <math.h>
 
+#include "sda_attn_dev.hpp"
 #include "sda_device.hpp"
 #include "sda_internal.h"
 #include "sda_ktilde_dev.hpp"
 #include "sda_select_dev.hpp"
 
 namespace sda {
-
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4i16;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-#define SDA_LDS __attribute__((address_space(3)))
-
-// token held in QK A-operand row m of m-tile mt
-__device__ __forceinline__ int tok_of(int mt, int m) {
-    return (mt >> 1) * 32 + (m >> 2) * 8 + (mt & 1) * 4 + (m & 3);
-}
-
-// Wave-private V tile in LDS: 64 rows of d bf16.  The 32-byte chunks of row
-// t are XOR-permuted by perm(t) so that the transposed reads (16 rows of one
-// logical chunk per instruction) spread over the banks; the direct loads
-// write 16-byte pieces in lane order, so each lane fetches the piece that
-// belongs at its LDS slot.
-template <int D>
-struct VTile {
-    static constexpr int kRowBytes = D * 2;
-    static constexpr int kBytes = kBlock * kRowBytes;
-    static constexpr int kLoads = kBytes / (kWave * 16);      // direct loads per lane
-    __device__ static __forceinline__ int perm(int t) {
-        return D == 128 ? (((t >> 3) & 3) | ((t & 1) << 2)) : ((t >> 3) & 3);
-    }
-};
 
 // LDS of a workgroup of W waves: W V tiles, reused for the wave merge; the
 // union lists of the grouped mode follow
@@ -103,13 +80,6 @@ struct Branch {
     int n_split;            // the branch's splits
 };
 
-// Read-only int32 the kernel never writes (lengths, block lists): through the
-// constant address space, so that wave-uniform reads become scalar loads
-// that wait on their own counter, not behind the vector loads.
-__device__ __forceinline__ int ld_ro(const int32_t* p) {
-    return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)p;
-}
-
 // Wait until at most N vector memory operations are outstanding; the K tile
 // passes through as in-out operands so no use of it moves above the wait.
 template <int N, int KS>
@@ -140,11 +110,6 @@ __device__ __forceinline__ void qwait(u32x4 (&qf)[NT][KS]) {
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[nt][ks]));
-}
-
-template <int AUX = 0>
-__device__ __forceinline__ void lds_dma16(const void* g, SDA_LDS void* l) {
-    __builtin_amdgcn_global_load_lds(g, l, 16, 0, AUX);
 }
 
 // Merge the n_split partials (m, l, o) of one output row by log-sum-exp: one
@@ -435,12 +400,6 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
         for (int ks = 0; ks < KS; ++ks)
             asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[nt][ks]) : "v"(qp + ks * 32) : "memory");
     }
-    // prefill: the lane's row (query c of the group) sees tokens below
-    // pos0 + q0 + c + 1; a block below the group's first query is whole for every row
-    int lim[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) lim[nt] = a.prefill ? a.pos0 + q0 + min(rowq[nt], Cg - 1) + 1 : INT_MAX;
-    const int lim_min = a.prefill ? a.pos0 + q0 + 1 : INT_MAX;
     // the scalar reads are first used here, after every load above is issued
     asm volatile("" : "+s"(T), "+s"(n_g));
     if (glist) L.n = min(max(n_g, 0), a.n_sel_max);
@@ -503,8 +462,7 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
         const char* kb = reinterpret_cast<const char*>(kv_k + (size_t)phys * kBlock * D);
         const char* vb = reinterpret_cast<const char*>(kv_v + (size_t)phys * kBlock * D);
         const int tmax = nvalid - 1;
-        const bool full = (nvalid == kBlock) && (memb == 0xffffffffu) && tfirst == 0 &&
-                          j * kBlock + kBlock <= lim_min;                               // wave-uniform
+        const bool full = (nvalid == kBlock) && (memb == 0xffffffffu) && tfirst == 0;   // wave-uniform
 
         // ---- K into registers (MFMA A layout), then V into LDS by direct loads;
         //      everything is in flight before the first wait, and QK and the
@@ -559,12 +517,11 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
         for (int nt = 0; nt < NT; ++nt) {
             if (!full) {
                 const bool live = (memb >> rowq[nt]) & 1u;
-                const int tv = min(nvalid, lim[nt] - j * kBlock);     // tokens of the block this row sees
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (!(live && tok_of(mt, lg * 4 + i) < tv && tok_of(mt, lg * 4 + i) >= tfirst))
+                        if (!(live && tok_of(mt, lg * 4 + i) < nvalid && tok_of(mt, lg * 4 + i) >= tfirst))
                             s[mt][nt][i] = -INFINITY;
             }
             float mx = -INFINITY;

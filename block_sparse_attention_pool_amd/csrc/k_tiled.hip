@@ -1,0 +1,371 @@
+// Row-tiled block-sparse attention: many query rows of one KV head share
+// every block load.  Used for prefill, where every query position attends to
+// its own block set ([SparDA] eq. (3) and (7) per position; the complexity
+// section's eq. (15) counts k blocks of attention per query token).
+//
+// A workgroup owns a tile of Cq consecutive queries of one (b, g): R = Cq*G
+// rows (query, head), 16 per wave, kept in registers for the whole walk (the
+// Q fragments, the online-softmax state and the O accumulators).  The tile's
+// block lists are merged into a bitmap in LDS (bit c of word j: query c lists
+// block j).  The workgroup walks the set blocks in ascending order and loads
+// each block's K and V once into LDS with direct loads, NBUF blocks in
+// flight; every wave computes only the blocks that one of its queries lists
+// and masks each row to its own list and, in prefill, to the tokens at or
+// before its position.  A row belongs to one wave, so nothing is merged: each
+// wave normalises and writes its own rows.
+//
+// Per block and wave (16 rows):
+//   S^T[tok][row] = K[tok][:] . Q[row][:]     16x16x32 bf16 MFMA; K is the A
+//       operand, kept in LDS in operand order (the direct loads place each
+//       lane's 16 bytes of every (m-tile, k-step) operand side by side), so
+//       a wave reads an operand with one conflict-free 16-byte read at an
+//       immediate offset.
+//   online softmax per row in fp32 (exp2, scale * log2(e) folded in).
+//   O^T[d][row] += V^T[d][tok] P^T[tok][row]  V^T from LDS transpose reads
+//       of the decode's V tile layout; P split into two bf16 parts (hi + lo).
+// The work is a dense contraction per block (R x 64 x d twice), so it runs on
+// MFMA; what bounds it is how often a block is fetched, which the tile size
+// sets (one fetch per tile instead of one per group of a few positions).
+#include <limits.h>
+#include <math.h>
+
+#include "sda_attn_dev.hpp"
+#include "sda_device.hpp"
+#include "sda_internal.h"
+
+namespace sda {
+
+namespace {
+
+// blocks in flight per workgroup: two K and V buffers (64 KB at d = 128) let
+// two workgroups share a compute unit, which measured faster (21 against
+// 38 ms on the 32K prefill) than three or four buffers with one workgroup
+constexpr int kBufs = 2;
+
+// the first block above j whose bitmap word is set (nb if none); wave-uniform
+__device__ __forceinline__ int next_set(const uint32_t* bm, int j, int nb) {
+    const int lane = __lane_id();
+    for (int base = j + 1; base < nb; base += kWave) {
+        const int idx = base + lane;
+        const uint64_t bal = __ballot(idx < nb && bm[idx] != 0u);
+        if (bal) return base + __builtin_ctzll(bal);
+    }
+    return nb;
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int D, int W, int NBUF>
+__global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
+    constexpr int KS = D / 32;                   // QK k-steps
+    constexpr int MTD = D / 16;                  // PV m-tiles over d
+    constexpr int ROWB = D * 2;                  // bytes per token row
+    constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+    constexpr int TILE = kBlock * ROWB;          // bytes of one K (or V) tile
+    constexpr int PPL = TILE / 16 / (W * kWave); // 16-byte pieces per lane per tile
+    static_assert(4 * KS == W * PPL, "one K operand per direct load");
+    constexpr int LPB = 2 * PPL;                 // direct loads per lane per block (K and V)
+    static_assert(PPL >= 1 && (NBUF - 1) * LPB <= 63, "vmcnt range");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    SDA_LDS char* lds = (SDA_LDS char*)smem;
+    uint32_t* bm = reinterpret_cast<uint32_t*>(smem + (size_t)NBUF * 2 * TILE);
+
+    // tile -> (b, g, query tile): consecutive workgroups go to the eight XCDs
+    // in turn, so when the (b, g) pairs come in multiples of eight, XCD x
+    // walks the query tiles of pairs x, x + 8, ... from the last one down (the
+    // longest lists first), and tiles that share blocks share an L2
+    const int wg = blockIdx.x;
+    const int P = a.B * a.H_kv;
+    int pair, tile;
+    if ((P & 7) == 0) {
+        const int slot = wg >> 3;
+        pair = (slot / a.n_tiles) * 8 + (wg & 7);
+        tile = a.n_tiles - 1 - slot % a.n_tiles;
+    } else {
+        pair = wg / a.n_tiles;
+        tile = a.n_tiles - 1 - wg % a.n_tiles;
+    }
+    const int b = pair / a.H_kv, g = pair - (pair / a.H_kv) * a.H_kv;
+    const int q0 = tile * a.Cq;
+    const int Cg = min(a.Cq, a.NQ - q0);
+    const int G = a.G;
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int li = lane & 15, lg = lane >> 4;
+    const int T = min(ld_ro(a.seq_len + b), a.T_cap);
+    int nb = (max(T, 0) + kBlock - 1) / kBlock;
+    if (a.prefill) nb = min(nb, (a.pos0 + q0 + Cg - 1) / kBlock + 1);
+    nb = min(nb, min(a.NB_cap, a.bm_words));
+
+    // this lane's row and the wave's queries
+    const int r = wave * 16 + li;
+    const int c = r / G, h = r - (r / G) * G;
+    const bool row_ok = c < Cg;
+    const int cc = min(c, Cg - 1);
+    const int cw0 = (wave * 16) / G, cw1 = min((wave * 16 + 15) / G, Cg - 1);
+    const uint32_t wmask = cw1 >= cw0 ? (uint32_t)((((uint64_t)1 << (cw1 + 1)) - 1) & ~(((uint64_t)1 << cw0) - 1)) : 0u;
+    const int lim = a.prefill ? a.pos0 + q0 + cc + 1 : INT_MAX;     // tokens below lim are visible
+    const int lim_w = a.prefill ? a.pos0 + q0 + min(cw0, Cg - 1) + 1 : INT_MAX;   // the wave's smallest
+    const bool wave_real = wave * 16 + 16 <= Cg * G;
+
+    // Q fragments (B operand): row r, dims ks * 32 + lg * 8
+    u32x4 qf[KS];
+    {
+        const uint16_t* qp = a.q + (((size_t)b * a.NQ + q0 + cc) * a.H_q + (size_t)g * G + h) * D + lg * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = ldg16(qp + ks * 32);
+    }
+
+    // the tile's bitmap
+    for (int i = threadIdx.x; i < nb; i += W * kWave) bm[i] = 0u;
+    __syncthreads();
+    {
+        const int nsm = a.n_sel_max;
+        for (int i = threadIdx.x; i < Cg * nsm; i += W * kWave) {
+            const int qc = i / nsm, e = i - (i / nsm) * nsm;
+            const size_t row = ((size_t)b * a.NQ + q0 + qc) * a.H_kv + g;
+            const int n = min(max(a.n_sel[row], 0), nsm);
+            if (e < n) {
+                const int j = a.block_idx[row * nsm + e];
+                if (j >= 0 && j < nb) atomicOr(&bm[j], 1u << qc);
+            }
+        }
+    }
+    // the Q fragments have landed: pass them through an asm so the compiler
+    // counts no load of them against the direct loads below
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
+    __syncthreads();
+
+    const uint16_t* kbase = a.k + ((size_t)b * a.H_kv + g) * a.T_cap * D;
+    const uint16_t* vbase = a.v + ((size_t)b * a.H_kv + g) * a.T_cap * D;
+    auto issue = [&](int j, int slot) {
+        const int tmax = min(kBlock - 1, T - 1 - j * kBlock);
+        const char* kb = reinterpret_cast<const char*>(kbase + (size_t)j * kBlock * D);
+        const char* vb = reinterpret_cast<const char*>(vbase + (size_t)j * kBlock * D);
+        SDA_LDS char* kl = lds + (size_t)slot * 2 * TILE;
+        SDA_LDS char* vl = kl + TILE;
+        // K: load i of this wave fills operand op = wave + W i, i.e. m-tile
+        // op / KS and k-step op % KS; lane l brings token tok_of(mt, l % 16),
+        // dims 32 ks + 8 (l / 16) .. + 7
+#pragma unroll
+        for (int i = 0; i < PPL; ++i) {
+            const int op = wave + W * i;
+            const int mt = op / KS, ks = op - (op / KS) * KS;
+            const int tr = min(tok_of(mt, li), tmax);
+            lds_dma16(kb + (size_t)tr * ROWB + ks * 64 + lg * 16, kl + op * kWave * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < PPL; ++i) {
+            const int base = (wave + W * i) * kWave;
+            const int pi = base + lane;
+            const int t = pi / CPR, pc = pi - (pi / CPR) * CPR;
+            const int tr = min(t, tmax);
+            lds_dma16(vb + (size_t)tr * ROWB + ((pc << 4) ^ (VTile<D>::perm(t) << 5)), vl + base * 16);
+        }
+    };
+
+    floatx4 o[MTD];
+#pragma unroll
+    for (int i = 0; i < MTD; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float csc = a.scale_log2;
+    const int v_lane = (lg * 8 + (li >> 2)) * ROWB + (li & 3) * 8;   // row 8 lg + li / 4, column bytes
+    const int v_perm = VTile<D>::perm(lg * 8 + (li >> 2));
+
+    // blocks in flight: jq[i] is in slot (it + i) % NBUF
+    int jq[NBUF];
+    int jn = next_set(bm, -1, nb);
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) {
+        jq[i] = jn;
+        if (jn < nb) {
+            issue(jn, i);
+            jn = next_set(bm, jn, nb);
+        }
+    }
+    for (int it = 0; jq[0] < nb; ++it) {
+        const int j = jq[0];
+        const int slot = it % NBUF;
+        jq[NBUF - 1] = jn;
+        if (jn < nb) {
+            issue(jn, (it + NBUF - 1) % NBUF);
+            jn = next_set(bm, jn, nb);
+        }
+        // wait for block j: the loads of the blocks issued after it may stay in flight
+        int after = 0;
+#pragma unroll
+        for (int i = 1; i < NBUF; ++i) after += jq[i] < nb ? 1 : 0;
+        if constexpr (NBUF >= 4) {
+            if (after >= 3) vm_wait<3 * LPB>();
+            else if (after == 2) vm_wait<2 * LPB>();
+            else if (after == 1) vm_wait<LPB>();
+            else vm_wait<0>();
+        } else if constexpr (NBUF == 3) {
+            if (after >= 2) vm_wait<2 * LPB>();
+            else if (after == 1) vm_wait<LPB>();
+            else vm_wait<0>();
+        } else {
+            if (after >= 1) vm_wait<LPB>();
+            else vm_wait<0>();
+        }
+        __syncthreads();                                     // every wave's share of block j has landed
+
+        const uint32_t mk = bm[j];
+        if (mk & wmask) {                                    // wave-uniform
+            SDA_LDS const char* kl = lds + (size_t)slot * 2 * TILE;
+            SDA_LDS const char* vl = kl + TILE;
+            const int nvalid = min(kBlock, T - j * kBlock);
+            // every row of the wave is a real row that lists j and sees all of it
+            const bool full = nvalid == kBlock && wave_real && (mk & wmask) == wmask && j * kBlock + kBlock <= lim_w;
+            floatx4 s[4];
+            SDA_LDS const char* kq = kl + lane * 16;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const u32x4 ka = *reinterpret_cast<SDA_LDS const u32x4*>(kq + (mt * KS + ks) * kWave * 16);
+                    acc = mfma16x16x32(ka, qf[ks], acc);
+                }
+                s[mt] = acc;
+            }
+            if (!full) {
+                // output i of m-tile mt is token tok_of(mt, 4 lg + i) = 8 lg + e(mt, i):
+                // it counts when e < thr
+                const bool live = row_ok && ((mk >> cc) & 1u);
+                const int thr = (live ? min(nvalid, lim - j * kBlock) : 0) - lg * 8;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!((mt >> 1) * 32 + (mt & 1) * 4 + i < thr)) s[mt][i] = -INFINITY;
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) mx = fmaxf(mx, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
+            mx = cross4_max(mx) * csc;
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = m_new != -INFINITY ? m_new : 0.f;
+            float psum = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[mt][i], csc, -m_use));
+                    s[mt][i] = p;
+                    psum += p;
+                }
+            psum = cross4_sum(psum);
+            if (m_run != -INFINITY) {
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+                l_run *= alpha;
+#pragma unroll
+                for (int i = 0; i < MTD; ++i) {
+                    o[i][0] *= alpha;
+                    o[i][1] *= alpha;
+                    o[i][2] *= alpha;
+                    o[i][3] *= alpha;
+                }
+            }
+            l_run += psum;
+            m_run = m_new;
+            u32x4 pf[2], pl[2];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float p0 = s[2 * kh + (w >> 1)][(w & 1) * 2];
+                    const float p1 = s[2 * kh + (w >> 1)][(w & 1) * 2 + 1];
+                    const bf16x2 hi = {(__bf16)p0, (__bf16)p1};
+                    const bf16x2 lo = {(__bf16)(p0 - (float)hi[0]), (__bf16)(p1 - (float)hi[1])};
+                    pf[kh][w] = __builtin_bit_cast(uint32_t, hi);
+                    pl[kh][w] = __builtin_bit_cast(uint32_t, lo);
+                }
+            // V^T operands: token t = 32 kh + 8 lg + 4 hh + li / 4, whose chunk
+            // permutation perm(t) is the lane's own (kh and hh do not enter it),
+            // so one address per md and the (kh, hh) offsets are immediates
+#pragma unroll
+            for (int md = 0; md < MTD; ++md) {
+                SDA_LDS const char* vq = vl + v_lane + ((md ^ v_perm) << 5);
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    u32x4 va;
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const v4i16 rr = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (SDA_LDS v4i16*)(vq + (kh * 32 + hh * 4) * ROWB));
+                        const uint2 u = __builtin_bit_cast(uint2, rr);
+                        va[2 * hh] = u.x;
+                        va[2 * hh + 1] = u.y;
+                    }
+                    o[md] = mfma16x16x32(va, pf[kh], o[md]);
+                    o[md] = mfma16x16x32(va, pl[kh], o[md]);
+                }
+            }
+        }
+        __syncthreads();                                     // slot is free for the block NBUF ahead
+#pragma unroll
+        for (int i = 0; i < NBUF - 1; ++i) jq[i] = jq[i + 1];
+    }
+
+    if (row_ok && r < Cg * G) {
+        const size_t oi = ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h;
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+        for (int md = 0; md < MTD; ++md)
+            *reinterpret_cast<floatx4*>(&a.out[oi * D + md * 16 + lg * 4]) =
+                floatx4{o[md][0] * inv, o[md][1] * inv, o[md][2] * inv, o[md][3] * inv};
+        if (lg == 0 && a.lse) a.lse[oi] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
+template <int D, int W, int NBUF>
+hipError_t launch_tw(const TiledArgs& a, hipStream_t s) {
+    const size_t lds = tiled_lds_bytes(D, a.bm_words);
+    const unsigned tiles = (unsigned)((size_t)a.B * a.H_kv * a.n_tiles);
+    hipLaunchKernelGGL((tiled_attn_kernel<D, W, NBUF>), dim3(tiles), dim3(W * 64), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// up to 128 rows (32 queries) per tile; waves: the next power of two that
+// holds them (2, 4 or 8), padding rows idle
+int tiled_queries_per_tile(int G) { return G >= 1 && G <= 32 ? (128 / G < 32 ? 128 / G : 32) : 0; }
+int tiled_waves(int G) {
+    const int w = (tiled_queries_per_tile(G) * G + 15) / 16;
+    return w <= 2 ? 2 : (w <= 4 ? 4 : 8);
+}
+
+size_t tiled_lds_bytes(int d, int bm_words) { return (size_t)kBufs * 2 * kBlock * d * 2 + (size_t)bm_words * 4; }
+
+hipError_t tiled_grant_lds() {
+    const void* kerns[] = {reinterpret_cast<const void*>(tiled_attn_kernel<128, 8, kBufs>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 4, kBufs>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 2, kBufs>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 8, kBufs>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 4, kBufs>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 2, kBufs>)};
+    for (const void* k : kerns) {
+        const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTiledLdsMax);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_tiled_attention(const TiledArgs& a, int d, hipStream_t s) {
+    const hipError_t e = device_setup();
+    if (e != hipSuccess) return e;
+    if (tiled_lds_bytes(d, a.bm_words) > kTiledLdsMax) return hipErrorInvalidValue;
+    const int W = tiled_waves(a.G);
+    if (d == 128) return W == 8 ? launch_tw<128, 8, kBufs>(a, s) : W == 4 ? launch_tw<128, 4, kBufs>(a, s)
+                                                                         : launch_tw<128, 2, kBufs>(a, s);
+    return W == 8 ? launch_tw<64, 8, kBufs>(a, s) : W == 4 ? launch_tw<64, 4, kBufs>(a, s) : launch_tw<64, 2, kBufs>(a, s);
+}
+
+}  // namespace sda

@@ -907,14 +907,10 @@ sda_status_t sda_prefill_select(const void* f, const void* k_tilde, const int32_
     return hip_status(launch_prefill_select(a, d, static_cast<hipStream_t>(stream)), "prefill_select launch");
 }
 
-// prefill attention runs the grouped engine in exact mode on groups of
-// C consecutive query positions (C * G <= 32 rows per workgroup, C <= 8)
-static int prefill_group(int G) { return std::max(1, std::min(8, 32 / G)); }
-
 size_t sda_prefill_attention_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap) {
-    if (!attn_sizes_ok(B, NQ, H_q, H_kv, n_sel_max, d, 0) || NB_cap < 1 || NB_cap > kMaxNBCap) return 0;
-    return sda_grouped_decode_workspace(B, NQ, H_q, H_kv, n_sel_max, d, NB_cap, prefill_group(H_q / H_kv),
-                                        SDA_GROUP_EXACT, 0);
+    // the row-tiled engine merges nothing across workgroups: no workspace
+    (void)B, (void)NQ, (void)H_q, (void)H_kv, (void)n_sel_max, (void)d, (void)NB_cap;
+    return 0;
 }
 
 sda_status_t sda_prefill_attention(const void* q, const void* k, const void* v, const int32_t* seq_len,
@@ -927,49 +923,38 @@ sda_status_t sda_prefill_attention(const void* q, const void* k, const void* v, 
     REQUIRE(NB_cap >= ceil_div(T_cap, kBlock) && NB_cap <= kMaxNBCap, SDA_ERR_SHAPE,
             "NB_cap=%d must lie in [ceil(T_cap/64), %d]", NB_cap, kMaxNBCap);
     const int G = H_q / H_kv;
-    const int C = prefill_group(G);
-    const int n_groups = ceil_div(NQ, C);
-    const long long tasks = (long long)B * n_groups * H_kv;
-    REQUIRE(tasks <= (1LL << 31) - 1, SDA_ERR_SHAPE, "too many row groups");
-    const int rp = attn_rows_pad(C, G);
-    const AttnPlan plan = attn_plan(d, rp, (int)tasks, grouped_list_estimate(C, SDA_GROUP_EXACT, n_sel_max), C,
-                                    SDA_GROUP_EXACT, NB_cap, n_sel_max, 0);
-    const size_t lds = attn_smem_bytes_host(d, rp, plan.waves, C, SDA_GROUP_EXACT, NB_cap, n_sel_max);
-    REQUIRE(lds <= kLdsBytes, SDA_ERR_UNSUPPORTED, "group needs %zu bytes of LDS", lds);
-    const size_t need = attn_ws_bytes((int)tasks, plan.n_split, rp, d);
-    REQUIRE(need == 0 || (ws && ws_bytes >= need), SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
-            ws ? ws_bytes : 0, need);
-    REQUIRE(need == 0 || aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
-    AttnArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
-    a.seq_len = seq_len;
-    a.block_idx = block_idx;
-    a.n_sel = n_sel;
-    a.slot = nullptr;
-    a.out = out;
-    a.lse = lse_opt;
-    a.union_count = nullptr;
-    set_workspace(a, ws, need, (int)tasks, plan.n_split, rp);
-    a.n_sel_max = n_sel_max;
-    a.T_cap = T_cap;
-    a.NB_cap = NB_cap;
-    a.B = B;
-    a.NQ = NQ;
-    a.H_q = H_q;
-    a.H_kv = H_kv;
-    a.G = G;
-    a.d = d;
-    a.C = C;
-    a.mode = SDA_GROUP_EXACT;
-    a.n_groups = n_groups;
-    a.n_split = plan.n_split;
-    a.waves = plan.waves;
-    a.scale_log2 = scale * 1.4426950408889634f;
-    a.prefill = 1;
-    a.pos0 = pos0;
-    return hip_status(launch_attention(a, static_cast<hipStream_t>(stream)), "prefill_attention launch");
+    // the row-tiled engine: up to 128 rows of consecutive positions per
+    // workgroup, every block of their union fetched once into LDS
+    const int bm_words = std::min(NB_cap, ceil_div((long long)pos0 + NQ, kBlock));
+    REQUIRE(tiled_lds_bytes(d, bm_words) <= kTiledLdsMax, SDA_ERR_UNSUPPORTED,
+            "a block bitmap of %d words does not fit in LDS", bm_words);
+    TiledArgs t{};
+    t.q = static_cast<const uint16_t*>(q);
+    t.k = static_cast<const uint16_t*>(k);
+    t.v = static_cast<const uint16_t*>(v);
+    t.seq_len = seq_len;
+    t.block_idx = block_idx;
+    t.n_sel = n_sel;
+    t.out = out;
+    t.lse = lse_opt;
+    t.n_sel_max = n_sel_max;
+    t.T_cap = T_cap;
+    t.NB_cap = NB_cap;
+    t.B = B;
+    t.NQ = NQ;
+    t.H_q = H_q;
+    t.H_kv = H_kv;
+    t.G = G;
+    t.Cq = tiled_queries_per_tile(G);
+    t.n_tiles = ceil_div(NQ, t.Cq);
+    t.prefill = 1;
+    t.pos0 = pos0;
+    t.bm_words = bm_words;
+    t.scale_log2 = scale * 1.4426950408889634f;
+    REQUIRE(fits_int({B, H_kv, t.n_tiles}), SDA_ERR_SHAPE, "too many query tiles");
+    (void)ws;
+    (void)ws_bytes;
+    return hip_status(launch_tiled_attention(t, d, static_cast<hipStream_t>(stream)), "prefill_attention launch");
 }
 
 size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap,

@@ -133,8 +133,6 @@ struct AttnArgs {
     int C;                    // queries per group (1 = plain decode)
     int mode;                 // 0 exact, 1 shared representative
     int n_groups;             // ceil(NQ / C)
-    int prefill;              // 1: query q sits at position pos0 + q and sees tokens 0 .. pos0 + q
-    int pos0;                 //    only (causal prefill); 0: every query sees the whole cache
     int task0;                // first row group of this launch (launches cover at most 65535)
     int n_split;
     int waves;                // waves per workgroup
@@ -166,6 +164,34 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // gives every attention kernel the compute unit's whole LDS (160 KB) on the
 // current device; called once per device by device_setup()
 hipError_t attn_grant_lds();
+
+// ---- row-tiled attention (prefill) --------------------------------------------------
+// A workgroup holds up to 128 rows (Cq queries x G heads) of one (b, g) and
+// walks the union of their block lists through LDS (two blocks in flight, so
+// that two workgroups share a compute unit); see k_tiled.hip.
+constexpr size_t kTiledLdsMax = 160 * 1024;
+struct TiledArgs {
+    const uint16_t* q;        // [B, NQ, H_q, d]
+    const uint16_t* k;        // [B, H_kv, T_cap, d]
+    const uint16_t* v;
+    const int32_t* seq_len;   // [B]
+    const int32_t* block_idx; // [B, NQ, H_kv, n_sel_max] ascending
+    const int32_t* n_sel;     // [B, NQ, H_kv]
+    float* out;               // [B, NQ, H_q, d]
+    float* lse;               // [B, NQ, H_q] or null
+    int n_sel_max, T_cap, NB_cap;
+    int B, NQ, H_q, H_kv, G;
+    int Cq;                   // queries per tile
+    int n_tiles;              // ceil(NQ / Cq)
+    int prefill, pos0;        // prefill: query q sees tokens below pos0 + q + 1
+    int bm_words;             // bitmap words in LDS: >= the blocks any tile may list
+    float scale_log2;
+};
+int tiled_queries_per_tile(int G);
+int tiled_waves(int G);
+size_t tiled_lds_bytes(int d, int bm_words);
+hipError_t tiled_grant_lds();
+hipError_t launch_tiled_attention(const TiledArgs& a, int d, hipStream_t s);
 
 // ---- per-device set-up ----------------------------------------------------------------
 // Done once per device, at the first call of any entry point on it, under a

@@ -47,6 +47,7 @@ hipError_t device_setup() {
     std::lock_guard<std::mutex> guard(g_setup_lock);
     if (g_ready[dev].load(std::memory_order_relaxed)) return hipSuccess;
     e = attn_grant_lds();
+    if (e == hipSuccess) e = tiled_grant_lds();
     if (e != hipSuccess) return e;
     g_ready[dev].store(true, std::memory_order_release);
     return hipSuccess;

@@ -404,18 +404,18 @@ sda_status_t sda_prefill_select(const void* f, const void* k_tilde, const int32_
  * of a chunk ([SparDA] eq. (7) per query and the complexity section's eq.
  * (15): each query token attends to its own k blocks): query r at position
  * p = pos0 + r, head h, attends to the tokens of its listed blocks that lie
- * at or before p.  Consecutive query positions share one pass over the union
- * of their lists (the grouped engine of sda_grouped_decode in exact mode,
- * groups of min(8, 32 / G) positions), each masked to its own list and its
- * own position.
+ * at or before p.  Tiles of min(32, 128 / G) consecutive positions share
+ * one pass over the union of their lists, each block fetched once into LDS
+ * for the tile and every row masked to its own list and its own position.
  *
  *   q          bf16 [B, NQ, H_q, d]
  *   k, v       bf16 [B, H_kv, T_cap, d] (pos0 + NQ <= T_cap)
  *   block_idx, n_sel  as sda_prefill_select writes them (ascending per row)
  *   out f32 [B, NQ, H_q, d]; lse_opt f32 [B, NQ, H_q] or NULL
  * A query with no visible token gets out = 0 and lse = -inf.
- * Workspace: sda_prefill_attention_workspace() bytes (0 when one split per
- * row group), with the zero-fill and no-overlap contract of sda_sparse_decode.
+ * Workspace: none is needed (sda_prefill_attention_workspace() returns 0;
+ * ws may be NULL and is not read).  Lists hold block ids below
+ * ceil(T_cap / 64) <= NB_cap <= 16384.
  */
 size_t sda_prefill_attention_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap);
 sda_status_t sda_prefill_attention(const void* q, const void* k, const void* v, const int32_t* seq_len,

@@ -189,3 +189,67 @@ def test_prefill_select_refuses_positions_past_its_register_budget():
     with pytest.raises(sda.SdaError, match="registers"):
         sda.sda_prefill_select(f, kt, seq, 32768 - 63, 1, 2, 8)
     assert cfg.d == 64
+
+
+ATT_CASES = [
+    # (B, H_kv, G, d, lens, pos0, nq, n_sel_max): the row-tiled engine at every
+    # wave count (G = 1: 2 waves, 2: 4, 3: 8 with idle padding rows, 4, 16 and
+    # 32: 8), ragged lengths, a chunk offset, lists holding blocks past the
+    # query's position (masked by causality) and empty lists
+    (2, 2, 1, 64, [300, 700], 0, 700, 7),
+    (1, 1, 2, 128, [400], 129, 200, 9),
+    (2, 2, 3, 64, [520, 260], 0, 520, 6),
+    (1, 2, 4, 128, [3000], 0, 3000, 12),
+    (1, 1, 16, 128, [450], 10, 300, 8),
+    (1, 1, 32, 64, [333], 0, 333, 5),
+]
+
+
+@pytest.mark.parametrize("case", ATT_CASES)
+def test_prefill_attention_on_drawn_lists(case):
+    B, H, G, d, lens, pos0, nq, nsm = case
+    _say("prefill attention", case)
+    T_cap = max(lens)
+    gen = torch.Generator().manual_seed(1000 + G * 7 + d)
+    K = torch.randn((B, H, T_cap, d), generator=gen).to(torch.bfloat16)
+    V = torch.randn((B, H, T_cap, d), generator=gen).to(torch.bfloat16)
+    Q = torch.randn((B, nq, H * G, d), generator=gen).to(torch.bfloat16)
+    rng = np.random.default_rng(G * 100 + d)
+    bi = np.full((B, nq, H, nsm), -1, dtype=np.int32)
+    ns = np.zeros((B, nq, H), dtype=np.int32)
+    nb_all = -(-T_cap // 64)
+    for b in range(B):
+        for r in range(nq):
+            p = pos0 + r
+            for g in range(H):
+                if rng.random() < 0.03:
+                    continue                                   # an empty list
+                top = min(nb_all, p // 64 + 2)                 # may reach one block past the position
+                n = int(rng.integers(1, min(nsm, top) + 1))
+                blocks = np.sort(rng.choice(top, size=n, replace=False))
+                bi[b, r, g, :n] = blocks
+                ns[b, r, g] = n
+    seq = torch.as_tensor(lens, dtype=torch.int32, device=DEV)
+    out, lse = sda.sda_prefill_attention(Q.to(DEV), K.to(DEV), V.to(DEV), seq, torch.as_tensor(bi, device=DEV),
+                                         torch.as_tensor(ns, device=DEV), pos0)
+    torch.cuda.synchronize()
+    Kd, Vd, Qd = _f64(K), _f64(V), _f64(Q)
+    o, l = out.double().cpu().numpy(), lse.double().cpu().numpy()
+    err = lerr = 0.0
+    for b in range(B):
+        for g in range(H):
+            # a query sees tokens below min(its position + 1, the cached length)
+            for r in range(nq):
+                T = min(pos0 + r + 1, lens[b])
+                blocks = bi[b, r, g, :ns[b, r, g]]
+                qh = Qd[b, r, g * G:(g + 1) * G]
+                toks = O.block_tokens(blocks, T) if len(blocks) else np.zeros(0, dtype=np.int64)
+                if len(toks) == 0:
+                    assert np.all(o[b, r, g * G:(g + 1) * G] == 0), (b, r, g)
+                    assert np.all(np.isneginf(l[b, r, g * G:(g + 1) * G])), (b, r, g)
+                    continue
+                want, wl = O.decode_row(qh, Kd[b, g], Vd[b, g], blocks, T, d ** -0.5)
+                err = max(err, float(np.abs(o[b, r, g * G:(g + 1) * G] - want).max()))
+                lerr = max(lerr, float(np.abs(l[b, r, g * G:(g + 1) * G] - wl).max()))
+    _say(f"  max abs err {err:.2e}, lse {lerr:.2e}")
+    assert err <= TOL and lerr <= 1e-3
