@@ -694,6 +694,27 @@ def measure_grouped(O):
                          "roofline": hbm(dist * blk, t), "roofline_loaded": hbm(loaded * blk, t)}
             o, _, _ = sda.sda_grouped_decode(Q, K, V, seq, bis[0], ns, C, mode=mode, ws=ws)
             outs[name] = o
+        # exact verification with all NQ draft queries of a sequence as one
+        # group (NQ * G = 128 rows: the row-tiled engine, its union split among
+        # workgroups): each distinct block is fetched once per (batch, KV head)
+        CA = cfg.NQ
+        ws = torch.zeros(max(16, sda.lib().sda_grouped_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d,
+                                                                        cfg.NB, CA, sda.SDA_GROUP_EXACT, 0)),
+                         dtype=torch.uint8, device=dev)
+        ucs = [torch.empty((cfg.B, 1, cfg.H_kv), dtype=torch.int32, device=dev) for _ in range(n_sets)]
+        turn = [0]
+
+        def tiled_call():
+            i = turn[0] % n_sets
+            turn[0] += 1
+            sda.sda_grouped_decode(Q, K, V, seq, bis[i], ns, CA, mode=sda.SDA_GROUP_EXACT, out=out, lse=lse,
+                                   union_count=ucs[i], ws=ws)
+        t = graph_time(tiled_call, copies=n_sets)
+        loaded = sum(int(u.sum().item()) for u in ucs) / n_sets
+        o16, _, _ = sda.sda_grouped_decode(Q, K, V, seq, bis[0], ns, CA, mode=sda.SDA_GROUP_EXACT, ws=ws)
+        row["exact_one_group_of_16"] = {"us": t * 1e6, "blocks_loaded": loaded, "distinct_blocks": dist_all,
+                                        "roofline": hbm(dist_all * blk, t), "roofline_loaded": hbm(loaded * blk, t),
+                                        "max_abs_diff_vs_mode_A": (o16 - outs["mode_A"]).abs().max().item()}
         ws = torch.zeros(sda.lib().sda_sparse_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d, 0),
                          dtype=torch.uint8, device=dev)
         turn = [0]
@@ -708,13 +729,15 @@ def measure_grouped(O):
         row["measured_saving_mode_A"] = 1.0 - row["mode_A"]["blocks_loaded"] / per_q_blocks
         row["formula_saving"] = 1.0 - O.union_size_formula(n, C, measured) / (n * C)
         row["speedup_mode_A_vs_per_query"] = row["per_query"]["us"] / row["mode_A"]["us"]
+        row["speedup_one_group_vs_per_query"] = row["per_query"]["us"] / row["exact_one_group_of_16"]["us"]
         # mode B approximates: its error against the exact per-query result
         dB = (outs["mode_B"] - outs["mode_A"]).abs()
         row["mode_B_error_vs_exact"] = {"max_abs": dB.max().item(), "mean_abs": dB.mean().item(),
                                         "rows_exact": float((dB.amax(dim=-1) == 0).float().mean().item())}
         res["gammas"][f"{gamma:g}"] = row
         log(f"grouped gamma {gamma}: sigma {sigma:.4f} measured {measured:.3f}; mode A {row['mode_A']['us']:.1f} us, "
-            f"mode B {row['mode_B']['us']:.1f} us, per-query {row['per_query']['us']:.1f} us; mode B max err "
+            f"mode B {row['mode_B']['us']:.1f} us, per-query {row['per_query']['us']:.1f} us, one group of 16 "
+            f"{row['exact_one_group_of_16']['us']:.1f} us; mode B max err "
             f"{row['mode_B_error_vs_exact']['max_abs']:.3e}")
         if gamma == 0.75:
             sets75, Q75, dist75 = bis, Q, dist_all

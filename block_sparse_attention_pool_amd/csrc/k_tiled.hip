@@ -77,7 +77,9 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     // in turn, so when the (b, g) pairs come in multiples of eight, XCD x
     // walks the query tiles of pairs x, x + 8, ... from the last one down (the
     // longest lists first), and tiles that share blocks share an L2
-    const int wg = blockIdx.x;
+    const int S = a.n_split;
+    const int split = (int)(blockIdx.x % (unsigned)S);
+    const int wg = (int)(blockIdx.x / (unsigned)S);
     const int P = a.B * a.H_kv;
     int pair, tile;
     if ((P & 7) == 0) {
@@ -141,6 +143,35 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qf[ks]));
     __syncthreads();
 
+    // the union's size and this split's share of it: entries [e0, e1) in
+    // ascending block order; jn = the block of entry e0
+    int n_u = 0, e0 = 0, e1 = 0, jn = nb;
+    {
+        for (int base = 0; base < nb; base += kWave) {
+            const int idx = base + lane;
+            n_u += __popcll(__ballot(idx < nb && bm[idx] != 0u));
+        }
+        e0 = (int)(((long long)split * n_u) / S);
+        e1 = (int)(((long long)(split + 1) * n_u) / S);
+        if (e0 < e1) {
+            int seen = 0;
+            for (int base = 0; base < nb; base += kWave) {
+                const int idx = base + lane;
+                uint64_t bal = __ballot(idx < nb && bm[idx] != 0u);
+                const int cnt = __popcll(bal);
+                if (e0 < seen + cnt) {
+                    for (int k = e0 - seen; k > 0; --k) bal &= bal - 1;     // drop the lower set bits
+                    jn = base + __builtin_ctzll(bal);
+                    break;
+                }
+                seen += cnt;
+            }
+        }
+    }
+    if (a.union_count && split == 0 && threadIdx.x == 0)
+        a.union_count[((size_t)b * a.n_tiles + tile) * a.H_kv + g] = n_u;
+    int to_issue = e1 - e0;                 // blocks of this split not yet issued
+
     const uint16_t* kbase = a.k + ((size_t)b * a.H_kv + g) * a.T_cap * D;
     const uint16_t* vbase = a.v + ((size_t)b * a.H_kv + g) * a.T_cap * D;
     auto issue = [&](int j, int slot) {
@@ -178,14 +209,14 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     const int v_perm = VTile<D>::perm(lg * 8 + (li >> 2));
 
     // blocks in flight: jq[i] is in slot (it + i) % NBUF
+    auto advance = [&](int j) { return --to_issue > 0 ? next_set(bm, j, nb) : nb; };
     int jq[NBUF];
-    int jn = next_set(bm, -1, nb);
 #pragma unroll
     for (int i = 0; i < NBUF - 1; ++i) {
         jq[i] = jn;
         if (jn < nb) {
             issue(jn, i);
-            jn = next_set(bm, jn, nb);
+            jn = advance(jn);
         }
     }
     for (int it = 0; jq[0] < nb; ++it) {
@@ -194,7 +225,7 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
         jq[NBUF - 1] = jn;
         if (jn < nb) {
             issue(jn, (it + NBUF - 1) % NBUF);
-            jn = next_set(bm, jn, nb);
+            jn = advance(jn);
         }
         // wait for block j: the loads of the blocks issued after it may stay in flight
         int after = 0;
@@ -313,21 +344,97 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
         for (int i = 0; i < NBUF - 1; ++i) jq[i] = jq[i + 1];
     }
 
-    if (row_ok && r < Cg * G) {
-        const size_t oi = ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h;
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    if (S == 1) {
+        if (row_ok && r < Cg * G) {
+            const size_t oi = ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h;
+            const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
-        for (int md = 0; md < MTD; ++md)
-            *reinterpret_cast<floatx4*>(&a.out[oi * D + md * 16 + lg * 4]) =
-                floatx4{o[md][0] * inv, o[md][1] * inv, o[md][2] * inv, o[md][3] * inv};
-        if (lg == 0 && a.lse) a.lse[oi] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+            for (int md = 0; md < MTD; ++md)
+                *reinterpret_cast<floatx4*>(&a.out[oi * D + md * 16 + lg * 4]) =
+                    floatx4{o[md][0] * inv, o[md][1] * inv, o[md][2] * inv, o[md][3] * inv};
+            if (lg == 0 && a.lse) a.lse[oi] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+        }
+        return;
     }
+
+    // ---- split-K: publish (m, l, o) of every row, the last workgroup merges ----
+    // Agent-scope stores (write-through: the merging workgroup may sit on
+    // another XCD), completed before one agent-scope increment per workgroup;
+    // the last arrival acquires and reads them with agent-scope loads.
+    constexpr int RP = W * 16;
+    const size_t tg = (size_t)pair * a.n_tiles + tile;          // this tile
+    {
+        const size_t pr = (tg * S + split) * RP + r;
+        uint64_t* po = reinterpret_cast<uint64_t*>(a.part_o + pr * D + lg * 4);
+#pragma unroll
+        for (int md = 0; md < MTD; ++md) {
+            __hip_atomic_store(po + md * 8, ((uint64_t)__float_as_uint(o[md][1]) << 32) | __float_as_uint(o[md][0]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(po + md * 8 + 1, ((uint64_t)__float_as_uint(o[md][3]) << 32) | __float_as_uint(o[md][2]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (lg == 0)
+            __hip_atomic_store(reinterpret_cast<uint64_t*>(a.part_ml + pr * 2),
+                               ((uint64_t)__float_as_uint(l_run) << 32) | __float_as_uint(m_run), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the flag lives in the bitmap's first word: every wave is past its last
+    // read of the bitmap at the barrier below (the kernel uses no static LDS,
+    // so that the whole 160 KB can be granted to the dynamic part)
+    volatile int* s_last = reinterpret_cast<volatile int*>(bm);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int last = arrive(a.counters + tg) == S - 1;
+        if (last) acquire_agent();
+        *s_last = last;
+    }
+    __syncthreads();
+    if (!*s_last) return;
+    // each wave merges its own 16 rows: lane = (row lane / 4, columns D / 4 * (lane % 4) ..)
+    constexpr int CPL = D / 4;                                   // columns per lane
+    const int mr = wave * 16 + lane / 4;
+    const int mc = (lane & 3) * CPL;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < S; ++s2)
+        M = fmaxf(M, __hip_atomic_load(a.part_ml + ((tg * S + s2) * RP + mr) * 2, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT));
+    float L = 0.f, acc[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
+    if (M != -INFINITY) {
+        for (int s2 = 0; s2 < S; ++s2) {
+            const size_t pr = (tg * S + s2) * RP + mr;
+            const float ms = __hip_atomic_load(a.part_ml + pr * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float ls = __hip_atomic_load(a.part_ml + pr * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float sc = __builtin_amdgcn_exp2f(ms - M);                      // 0 for an empty split
+            L += ls * sc;
+            const uint64_t* po = reinterpret_cast<const uint64_t*>(a.part_o + pr * D + mc);
+#pragma unroll
+            for (int i = 0; i < CPL / 2; ++i) {
+                const uint64_t w2 = __hip_atomic_load(po + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                acc[2 * i] += __uint_as_float((uint32_t)w2) * sc;
+                acc[2 * i + 1] += __uint_as_float((uint32_t)(w2 >> 32)) * sc;
+            }
+        }
+    }
+    const int mcq = mr / G, mh = mr - (mr / G) * G;
+    if (mcq < Cg && mr < Cg * G) {
+        const size_t oi = ((size_t)b * a.NQ + q0 + mcq) * a.H_q + (size_t)g * G + mh;
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; i += 4)
+            *reinterpret_cast<floatx4*>(&a.out[oi * D + mc + i]) =
+                floatx4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv};
+        if ((lane & 3) == 0 && a.lse) a.lse[oi] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(a.counters + tg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int W, int NBUF>
 hipError_t launch_tw(const TiledArgs& a, hipStream_t s) {
     const size_t lds = tiled_lds_bytes(D, a.bm_words);
-    const unsigned tiles = (unsigned)((size_t)a.B * a.H_kv * a.n_tiles);
+    const unsigned tiles = (unsigned)((size_t)a.B * a.H_kv * a.n_tiles * a.n_split);
     hipLaunchKernelGGL((tiled_attn_kernel<D, W, NBUF>), dim3(tiles), dim3(W * 64), lds, s, a);
     return hipGetLastError();
 }
@@ -337,9 +444,17 @@ hipError_t launch_tw(const TiledArgs& a, hipStream_t s) {
 // up to 128 rows (32 queries) per tile; waves: the next power of two that
 // holds them (2, 4 or 8), padding rows idle
 int tiled_queries_per_tile(int G) { return G >= 1 && G <= 32 ? (128 / G < 32 ? 128 / G : 32) : 0; }
-int tiled_waves(int G) {
-    const int w = (tiled_queries_per_tile(G) * G + 15) / 16;
+int tiled_waves_rows(int rows) {
+    const int w = (rows + 15) / 16;
     return w <= 2 ? 2 : (w <= 4 ? 4 : 8);
+}
+int tiled_waves(int G) { return tiled_waves_rows(tiled_queries_per_tile(G) * G); }
+
+// split-K workspace: [counters, 256-byte padded][(m, l) per split and row][o per split and row]
+size_t tiled_ws_bytes(int tiles, int n_split, int waves, int d) {
+    if (n_split <= 1) return 0;
+    const size_t rows = (size_t)tiles * n_split * waves * 16;
+    return ((size_t)tiles * 4 + 255) / 256 * 256 + rows * 2 * 4 + rows * (size_t)d * 4;
 }
 
 size_t tiled_lds_bytes(int d, int bm_words) { return (size_t)kBufs * 2 * kBlock * d * 2 + (size_t)bm_words * 4; }
@@ -362,7 +477,7 @@ hipError_t launch_tiled_attention(const TiledArgs& a, int d, hipStream_t s) {
     const hipError_t e = device_setup();
     if (e != hipSuccess) return e;
     if (tiled_lds_bytes(d, a.bm_words) > kTiledLdsMax) return hipErrorInvalidValue;
-    const int W = tiled_waves(a.G);
+    const int W = tiled_waves_rows(a.Cq * a.G);
     if (d == 128) return W == 8 ? launch_tw<128, 8, kBufs>(a, s) : W == 4 ? launch_tw<128, 4, kBufs>(a, s)
                                                                          : launch_tw<128, 2, kBufs>(a, s);
     return W == 8 ? launch_tw<64, 8, kBufs>(a, s) : W == 4 ? launch_tw<64, 4, kBufs>(a, s) : launch_tw<64, 2, kBufs>(a, s);

@@ -951,22 +951,41 @@ sda_status_t sda_prefill_attention(const void* q, const void* k, const void* v, 
     t.pos0 = pos0;
     t.bm_words = bm_words;
     t.scale_log2 = scale * 1.4426950408889634f;
+    t.n_split = 1;
     REQUIRE(fits_int({B, H_kv, t.n_tiles}), SDA_ERR_SHAPE, "too many query tiles");
     (void)ws;
     (void)ws_bytes;
     return hip_status(launch_tiled_attention(t, d, static_cast<hipStream_t>(stream)), "prefill_attention launch");
 }
 
+// Exact grouped verification with more than 32 rows per group (C * G up to
+// 128, C up to 32) runs on the row-tiled engine: the group's union walked
+// once through LDS, shared among S workgroups (split-K) so that a few groups
+// still fill the chip.
+static bool grouped_on_tiles(int group_C, int G, int mode) {
+    return mode == SDA_GROUP_EXACT && group_C * G > 32 && group_C * G <= 128 && group_C <= 32;
+}
+// splits: about four waves per compute unit over the launch (measured at the
+// 64K verification workload: 16-query groups best at 4 splits, 48.7 us against
+// 51.9 at 8 and 106 at 1; 8-query groups at 4, 37.3 against 61.1 at 8)
+static int grouped_tile_splits(int tiles, int waves, int split_k) {
+    if (split_k > 0) return std::min(split_k, 64);
+    return std::max(1, std::min(16, 4 * kCUs / std::max(tiles * waves, 1)));
+}
+
 size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap,
                                     int group_C, int mode, int split_k) {
-    if (!attn_sizes_ok(B, NQ, H_q, H_kv, n_sel_max, d, split_k) || group_C < 1 || group_C > 8 ||
-        group_C * (H_q / H_kv) > 32 || NB_cap < 1 || NB_cap > kMaxNBCap ||
-        (mode != SDA_GROUP_EXACT && mode != SDA_GROUP_SHARED_REP))
+    if (!attn_sizes_ok(B, NQ, H_q, H_kv, n_sel_max, d, split_k) || group_C < 1 || group_C > 32 || NB_cap < 1 ||
+        NB_cap > kMaxNBCap || (mode != SDA_GROUP_EXACT && mode != SDA_GROUP_SHARED_REP))
         return 0;
     const int G = H_q / H_kv;
     const int n_groups = ceil_div(NQ, group_C);
-    const int rp = attn_rows_pad(group_C, G);
     const int tasks = B * n_groups * H_kv;
+    if (grouped_on_tiles(group_C, G, mode))
+        return tiled_ws_bytes(tasks, grouped_tile_splits(tasks, tiled_waves_rows(group_C * G), split_k),
+                              tiled_waves_rows(group_C * G), d);
+    if (group_C > 8 || group_C * G > 32) return 0;
+    const int rp = attn_rows_pad(group_C, G);
     const AttnPlan p = attn_plan(d, rp, tasks, grouped_list_estimate(group_C, mode, n_sel_max), group_C, mode,
                                  NB_cap, n_sel_max, split_k);
     return attn_ws_bytes(tasks, p.n_split, rp, d);
@@ -979,15 +998,60 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
                                 void* ws, size_t ws_bytes, void* stream) {
     TRY(check_attn_common(q, k, v, seq_len, block_idx, n_sel, n_sel_max, T_cap, B, NQ, H_q, H_kv, d, scale, out,
                           split_k));
-    REQUIRE(group_C >= 1 && group_C <= 8, SDA_ERR_UNSUPPORTED, "group_C=%d outside [1, 8]", group_C);
     REQUIRE(mode == SDA_GROUP_EXACT || mode == SDA_GROUP_SHARED_REP, SDA_ERR_SHAPE, "mode=%d", mode);
     const int G = H_q / H_kv;
-    REQUIRE(group_C * G <= 32, SDA_ERR_UNSUPPORTED, "group_C*G=%d exceeds 32 rows", group_C * G);
     REQUIRE(NB_cap >= ceil_div(T_cap, kBlock) && NB_cap <= kMaxNBCap, SDA_ERR_SHAPE,
             "NB_cap=%d must lie in [ceil(T_cap/64), %d]", NB_cap, kMaxNBCap);
     REQUIRE(!union_count_opt || aligned4(union_count_opt), SDA_ERR_ALIGN, "union_count must be 4-byte aligned");
+    REQUIRE(group_C >= 1 && group_C <= 32, SDA_ERR_UNSUPPORTED, "group_C=%d outside [1, 32]", group_C);
     const int n_groups = ceil_div(NQ, group_C);
     const long long tasks = (long long)B * n_groups * H_kv;
+    if (grouped_on_tiles(group_C, G, mode)) {
+        REQUIRE(tasks <= (1LL << 24), SDA_ERR_SHAPE, "B*groups*H_kv=%lld exceeds %d", tasks, 1 << 24);
+        const int W = tiled_waves_rows(group_C * G);
+        const int S = grouped_tile_splits((int)tasks, W, split_k);
+        const size_t need = tiled_ws_bytes((int)tasks, S, W, d);
+        REQUIRE(tiled_lds_bytes(d, NB_cap) <= kTiledLdsMax, SDA_ERR_UNSUPPORTED, "NB_cap=%d: bitmap beyond LDS", NB_cap);
+        REQUIRE(need == 0 || (ws && ws_bytes >= need), SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
+                ws ? ws_bytes : 0, need);
+        REQUIRE(need == 0 || aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+        TiledArgs t{};
+        t.q = static_cast<const uint16_t*>(q);
+        t.k = static_cast<const uint16_t*>(k);
+        t.v = static_cast<const uint16_t*>(v);
+        t.seq_len = seq_len;
+        t.block_idx = block_idx;
+        t.n_sel = n_sel;
+        t.out = out;
+        t.lse = lse_opt;
+        t.n_sel_max = n_sel_max;
+        t.T_cap = T_cap;
+        t.NB_cap = NB_cap;
+        t.B = B;
+        t.NQ = NQ;
+        t.H_q = H_q;
+        t.H_kv = H_kv;
+        t.G = G;
+        t.Cq = group_C;
+        t.n_tiles = n_groups;
+        t.prefill = 0;
+        t.pos0 = 0;
+        t.bm_words = NB_cap;
+        t.scale_log2 = scale * 1.4426950408889634f;
+        t.n_split = S;
+        t.union_count = union_count_opt;
+        if (need) {
+            char* base = static_cast<char*>(ws);
+            const size_t rows = (size_t)tasks * S * W * 16;
+            t.counters = reinterpret_cast<int*>(base);
+            t.part_ml = reinterpret_cast<float*>(base + pad256((size_t)tasks * 4));
+            t.part_o = t.part_ml + rows * 2;
+        }
+        return hip_status(launch_tiled_attention(t, d, static_cast<hipStream_t>(stream)), "grouped_decode launch");
+    }
+    REQUIRE(group_C <= 8, SDA_ERR_UNSUPPORTED, "group_C=%d outside [1, 8]", group_C);
+    REQUIRE(group_C * G <= 32, SDA_ERR_UNSUPPORTED,
+            "group_C*G=%d exceeds 32 rows (up to 128 are supported in exact mode)", group_C * G);
     REQUIRE(tasks <= kMaxGridYZ, SDA_ERR_SHAPE, "B*groups*H_kv=%lld exceeds %d", tasks, kMaxGridYZ);
     const int rp = attn_rows_pad(group_C, G);
     const AttnPlan plan = attn_plan(d, rp, (int)tasks, grouped_list_estimate(group_C, mode, n_sel_max), group_C,

@@ -186,9 +186,18 @@ struct TiledArgs {
     int prefill, pos0;        // prefill: query q sees tokens below pos0 + q + 1
     int bm_words;             // bitmap words in LDS: >= the blocks any tile may list
     float scale_log2;
+    // split-K (n_split > 1): the union of a tile is shared among n_split
+    // workgroups; each writes (m, l, o) of its rows and the last to arrive merges
+    int n_split;
+    float* part_o;            // [tiles, n_split, 16 W, d]
+    float* part_ml;           // [tiles, n_split, 16 W, 2]
+    int* counters;            // [tiles]; zero between calls
+    int32_t* union_count;     // [B, n_tiles, H_kv] blocks in each tile's union, or null
 };
 int tiled_queries_per_tile(int G);
+int tiled_waves_rows(int rows);   // 2, 4 or 8 waves for up to 128 rows
 int tiled_waves(int G);
+size_t tiled_ws_bytes(int tiles, int n_split, int waves, int d);
 size_t tiled_lds_bytes(int d, int bm_words);
 hipError_t tiled_grant_lds();
 hipError_t launch_tiled_attention(const TiledArgs& a, int d, hipStream_t s);

@@ -240,12 +240,18 @@ def test_grouped_validation(L):
     f = L.sda_grouped_decode
     base = [P, P, P, P, P, P, 16, 65536, 1024, 4, 16, 32, 8, 128, 0.088, 4, 0, P, None, None, 0, P,
             1 << 28, None]
-    bad = list(base); bad[15] = 9                                         # C > 8
+    bad = list(base); bad[15] = 9; bad[16] = 1                            # shared mode: C > 8
+    assert f(*bad) == UNSUP
+    bad = list(base); bad[15] = 33                                        # C > 32
     assert f(*bad) == UNSUP
     bad = list(base); bad[16] = 2
     assert f(*bad) == SHAPE
-    bad = list(base); bad[11] = 64; bad[15] = 8                            # C*G = 64 rows
+    bad = list(base); bad[11] = 64; bad[15] = 8; bad[16] = 1              # shared mode: C*G = 64 rows
     assert f(*bad) == UNSUP
+    bad = list(base); bad[11] = 256; bad[15] = 8                          # exact mode: C*G = 256 rows
+    assert f(*bad) == UNSUP
+    bad = list(base); bad[15] = 16; bad[22] = 16                          # exact, C*G = 64: the tiled
+    assert f(*bad) == WS                                                  # engine's split workspace
     bad = list(base); bad[8] = 10                                         # NB_cap below T_cap/64
     assert f(*bad) == SHAPE
 

@@ -292,6 +292,22 @@ def test_c4_grouped_verification(c4_data, gamma):
                     sl = slice(g * G, (g + 1) * G)
                     errA = max(errA, np.abs(outA[b, c, sl].double().cpu().numpy() - oa[ci]).max())
                     errB = max(errB, np.abs(outB[b, c, sl].double().cpu().numpy() - ob[ci]).max())
+    # all 16 draft queries of a sequence as one exact group (C * G = 128 rows:
+    # the row-tiled engine, its union shared among split-K workgroups)
+    out16, _, u16 = sda.sda_grouped_decode(Qg, K, V, seq(cfg), bi, ns, cfg.NQ, sda.SDA_GROUP_EXACT)
+    u16 = u16.cpu().numpy()
+    err16 = 0.0
+    for b in range(cfg.B):
+        for g in range(cfg.H_kv):
+            lists = [want[(b, c, g)] for c in range(cfg.NQ)]
+            assert u16[b, 0, g] == len(O.union_blocks(lists))
+            qrows = np.stack([Qd[b, c, g * G:(g + 1) * G] for c in range(cfg.NQ)])
+            kf, vf = rk.get(b, g, O.union_blocks(lists))
+            o16, _, _ = O.grouped_row(qrows, kf, vf, lists, cfg.T, scale_of(cfg), O.MODE_EXACT)
+            err16 = max(err16, np.abs(out16[b, :, g * G:(g + 1) * G].double().cpu().numpy() - o16).max())
+    _say(f"c4: gamma {gamma}: one group of {cfg.NQ}: err {err16:.2e}, mean union {u16.mean():.2f}")
+    assert err16 <= TOL
+    assert (out16 - per_q).abs().max().item() < 1e-4
     dAB = (outA - per_q).abs().max().item()
     n = cfg.top_k
     _say(f"c4: gamma {gamma}: errA {errA:.2e} errB {errB:.2e} |A - per-query| {dAB:.2e} "
