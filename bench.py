@@ -1100,6 +1100,25 @@ def call_time(prepared, reps, copies=8):
     return e0.elapsed_time(e1) * 1e-3 / (reps * copies * len(prepared))
 
 
+def launch_distribution(prepared, n=60):
+    """Per-launch device time of a call: n eager launches cycling over the
+    prepared calls (the resident layers), each bracketed by HIP events on the
+    stream it runs on; median, p10 and p90 in us.  Each interval also holds
+    the dispatch of its launch, so these sit a little above the graph means."""
+    for c in prepared:
+        c.run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record()
+        prepared[i % len(prepared)].run()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)), "p90": float(np.percentile(t, 90)),
+            "launches": n}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -1348,7 +1367,16 @@ def main():
         },
         "score_select_gbs": sel_bytes / t_sel.mean() / 1e9,
         "queries_per_s_from_kernels": queries / (t_sel.mean() + t_dec.mean()),
+        # one query = one sequence's token through all query heads of the layer
+        "head_queries_per_s": value * cfg.H_q,
     }
+    if not args.no_graph:
+        res["kernels_us_per_launch"] = {
+            "score_select": launch_distribution([c[0] for c in calls]),
+            "sparse_decode": launch_distribution([c[1] for c in calls]),
+            "decode_step": launch_distribution(step_calls),
+            "timing": "eager launches cycling over the resident layers, HIP events around each on its stream",
+        }
     if cpu is not None:
         res["cpu_baseline"] = cpu
     if not args.no_rows:
