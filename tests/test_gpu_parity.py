@@ -543,3 +543,95 @@ def test_split_merge_matches_oracle_and_repeats():
         o2, l2 = sda.sda_sparse_decode(Qg, K, V, seq(cfg), bi, ns, split_k=sk)
         assert (o2 - ref).abs().max().item() <= 1e-5, sk
         assert (l2 - lref).abs().max().item() <= 1e-5, sk
+
+
+def _replays_match(g, outs, refs, eager_between):
+    for r in range(4):
+        for o in outs:
+            o.fill_(-7) if o.dtype == torch.int32 else o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, ref in zip(outs, refs):
+            assert torch.equal(o, ref), r
+        eager_between()
+        torch.cuda.synchronize()
+
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def test_graph_replay_of_decode_step_and_tiled_calls():
+    # the one-launch decode step (as the benchmark captures it), the row-tiled
+    # prefill attention and the tiled exact grouped decode with split-K (its
+    # arrival counters must be back at zero after every replay): every
+    # replay, with eager work and synchronisations in between, equals the
+    # eager result bit for bit
+    cfg = synth.get_config(1)
+    K, V, _ = inputs.kv_layer(cfg, 0, device=DEV)
+    ktg = gpu_ktilde(K, cfg.T)
+    F = inputs.to_bf16(inputs.indexer_vectors(cfg, 0)).to(DEV)
+    Q = inputs.to_bf16(inputs.attention_queries(cfg, 0)).to(DEV)
+    s = seq(cfg)
+    bi, ns = sda.sda_score_select(F, ktg, s, 1, 2, 8)
+    step, souts = sda.prepare(sda.sda_decode_step, Q, K, V, s, bi, ns, F, ktg, s, 1, 2, 8)
+    step.run()
+    torch.cuda.synchronize()
+    refs = [o.clone() for o in souts]
+    g = _capture(step.run)
+    _replays_match(g, list(souts), refs, lambda: sda.sda_sparse_decode(Q, K, V, s, bi, ns, split_k=2))
+
+    # prefill attention over a 2048-token chunk of the same cache
+    NQ = 2048
+    Qp = torch.randn((cfg.B, NQ, cfg.H_q, cfg.d), generator=torch.Generator(device=DEV).manual_seed(3),
+                     device=DEV).to(torch.bfloat16)
+    Fp = torch.randn((cfg.B, NQ, cfg.H_kv, cfg.d), generator=torch.Generator(device=DEV).manual_seed(4),
+                     device=DEV).to(torch.bfloat16)
+    pbi, pns = sda.sda_prefill_select(Fp, ktg, s, 1000, 1, 2, 8)
+    pout = torch.empty((cfg.B, NQ, cfg.H_q, cfg.d), dtype=torch.float32, device=DEV)
+    plse = torch.empty((cfg.B, NQ, cfg.H_q), dtype=torch.float32, device=DEV)
+
+    def prefill():
+        sda.sda_prefill_attention(Qp, K, V, s, pbi, pns, 1000, out=pout, lse=plse)
+    prefill()
+    torch.cuda.synchronize()
+    prefs = [pout.clone(), plse.clone()]
+    g = _capture(prefill)
+    _replays_match(g, [pout, plse], prefs, lambda: sda.sda_sparse_decode(Q, K, V, s, bi, ns))
+
+    # exact grouped decode with all 16 queries of a sequence in one group (G = 4:
+    # 64 rows, the tiled engine) and three splits
+    NQg = 16
+    Qg = torch.randn((cfg.B, NQg, cfg.H_q, cfg.d), generator=torch.Generator(device=DEV).manual_seed(5),
+                     device=DEV).to(torch.bfloat16)
+    Fg = torch.randn((cfg.B, NQg, cfg.H_kv, cfg.d), generator=torch.Generator(device=DEV).manual_seed(6),
+                     device=DEV).to(torch.bfloat16)
+    gbi, gns = sda.sda_score_select(Fg, ktg, s, 1, 2, 8)
+    nbytes = sda.lib().sda_grouped_decode_workspace(cfg.B, NQg, cfg.H_q, cfg.H_kv, gbi.shape[-1], cfg.d, cfg.NB,
+                                                    NQg, sda.SDA_GROUP_EXACT, 3)
+    assert nbytes > 0
+    gws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    gout = torch.empty((cfg.B, NQg, cfg.H_q, cfg.d), dtype=torch.float32, device=DEV)
+    glse = torch.empty((cfg.B, NQg, cfg.H_q), dtype=torch.float32, device=DEV)
+    guc = torch.empty((cfg.B, 1, cfg.H_kv), dtype=torch.int32, device=DEV)
+
+    def grouped():
+        sda.sda_grouped_decode(Qg, K, V, s, gbi, gns, NQg, sda.SDA_GROUP_EXACT, out=gout, lse=glse,
+                               union_count=guc, split_k=3, ws=gws)
+    grouped()
+    torch.cuda.synchronize()
+    grefs = [gout.clone(), glse.clone(), guc.clone()]
+    g = _capture(grouped)
+    _replays_match(g, [gout, glse, guc], grefs, lambda: sda.sda_sparse_decode(Q, K, V, s, bi, ns))
+    # the per-query decode of the same lists agrees
+    pq, _ = sda.sda_sparse_decode(Qg, K, V, s, gbi, gns)
+    assert (gout - pq).abs().max().item() < 1e-4

@@ -100,6 +100,39 @@ def test_noalloc_step_matches_workspace_step_as_shapes_change():
     _compare("ragged again", *small)
 
 
+def test_noalloc_step_replays_in_a_graph():
+    # the callers this entry point serves capture it: a prepared call
+    # captured in a HIP graph (after one eager call, which sets the scratch
+    # up), replayed with eager work in between, equals the workspace step
+    args, kw = _case_ragged(32)
+    kw = dict(kw)
+    kw["k_tilde_cur"] = None
+    kw.pop("len_old_cur", None)
+    kw.pop("max_new_tokens_cur", None)
+    ref = [t.clone() for t in sda.sda_decode_step(*args, **kw)]
+    call, outs = sda.prepare(sda.sda_decode_step_noalloc, *args, **kw)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call.run()
+    for r in range(4):
+        for o in outs:
+            o.fill_(-7) if o.dtype == torch.int32 else o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        out, lse, bi, ns = outs
+        assert torch.equal(bi, ref[2]) and torch.equal(ns, ref[3]), r
+        assert (out - ref[0]).abs().max().item() <= 1e-5, r
+        # eager work between replays: the workspace step on the other buffers
+        sda.sda_decode_step(*args, **kw)
+        torch.cuda.synchronize()
+
+
 def test_noalloc_rejects_a_call_beyond_its_scratch():
     B, H_kv, G, d, T = 64, 8, 8, 128, 4096
     z = lambda *s, dt=torch.bfloat16: torch.zeros(s, dtype=dt, device=DEV)
