@@ -8,8 +8,9 @@
 // Q fragments, the online-softmax state and the O accumulators).  The tile's
 // block lists are merged into a bitmap in LDS (bit c of word j: query c lists
 // block j).  The workgroup walks the set blocks in ascending order and loads
-// each block's K and V once into LDS with direct loads, NBUF blocks in
-// flight; every wave computes only the blocks that one of its queries lists
+// each block's K and V once into LDS with direct loads, the next block in
+// flight while the current one is computed (two slots, one barrier per
+// block); every wave computes only the blocks that one of its queries lists
 // and masks each row to its own list and, in prefill, to the tokens at or
 // before its position.  A row belongs to one wave, so nothing is merged: each
 // wave normalises and writes its own rows.
@@ -39,7 +40,9 @@ namespace {
 
 // blocks in flight per workgroup: two K and V buffers (64 KB at d = 128) let
 // two workgroups share a compute unit, which measured faster (21 against
-// 38 ms on the 32K prefill) than three or four buffers with one workgroup
+// 38 ms on the 32K prefill) than three or four buffers with one workgroup;
+// with two slots one barrier per block suffices (19.1 against 22.0 ms with a
+// second barrier that freed the slot)
 constexpr int kBufs = 2;
 
 // the first block above j whose bitmap word is set (nb if none); wave-uniform
@@ -67,8 +70,7 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     constexpr int TILE = kBlock * ROWB;          // bytes of one K (or V) tile
     constexpr int PPL = TILE / 16 / (W * kWave); // 16-byte pieces per lane per tile
     static_assert(4 * KS == W * PPL, "one K operand per direct load");
-    constexpr int LPB = 2 * PPL;                 // direct loads per lane per block (K and V)
-    static_assert(PPL >= 1 && (NBUF - 1) * LPB <= 63, "vmcnt range");
+    static_assert(PPL >= 1, "at least one piece per lane");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     SDA_LDS char* lds = (SDA_LDS char*)smem;
     uint32_t* bm = reinterpret_cast<uint32_t*>(smem + (size_t)NBUF * 2 * TILE);
@@ -208,43 +210,27 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     const int v_lane = (lg * 8 + (li >> 2)) * ROWB + (li & 3) * 8;   // row 8 lg + li / 4, column bytes
     const int v_perm = VTile<D>::perm(lg * 8 + (li >> 2));
 
-    // blocks in flight: jq[i] is in slot (it + i) % NBUF
+    // Two slots, one barrier per block: at the top of iteration it the wave
+    // waits for its share of block j (the only loads it has in flight), and
+    // the barrier then says both that all of j has landed and that every wave
+    // is done with block it - 1, whose slot the loads of the next block fill
+    // while j is computed.
+    static_assert(NBUF == 2, "one barrier per block needs exactly two slots");
     auto advance = [&](int j) { return --to_issue > 0 ? next_set(bm, j, nb) : nb; };
-    int jq[NBUF];
-#pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) {
-        jq[i] = jn;
-        if (jn < nb) {
-            issue(jn, i);
-            jn = advance(jn);
-        }
+    int j = jn;
+    if (j < nb) {
+        issue(j, 0);
+        jn = advance(j);
     }
-    for (int it = 0; jq[0] < nb; ++it) {
-        const int j = jq[0];
-        const int slot = it % NBUF;
-        jq[NBUF - 1] = jn;
-        if (jn < nb) {
-            issue(jn, (it + NBUF - 1) % NBUF);
-            jn = advance(jn);
+    for (int it = 0; j < nb; ++it) {
+        const int slot = it & 1;
+        vm_wait<0>();
+        __syncthreads();
+        const int jnext = jn;
+        if (jnext < nb) {
+            issue(jnext, slot ^ 1);
+            jn = advance(jnext);
         }
-        // wait for block j: the loads of the blocks issued after it may stay in flight
-        int after = 0;
-#pragma unroll
-        for (int i = 1; i < NBUF; ++i) after += jq[i] < nb ? 1 : 0;
-        if constexpr (NBUF >= 4) {
-            if (after >= 3) vm_wait<3 * LPB>();
-            else if (after == 2) vm_wait<2 * LPB>();
-            else if (after == 1) vm_wait<LPB>();
-            else vm_wait<0>();
-        } else if constexpr (NBUF == 3) {
-            if (after >= 2) vm_wait<2 * LPB>();
-            else if (after == 1) vm_wait<LPB>();
-            else vm_wait<0>();
-        } else {
-            if (after >= 1) vm_wait<LPB>();
-            else vm_wait<0>();
-        }
-        __syncthreads();                                     // every wave's share of block j has landed
 
         const uint32_t mk = bm[j];
         if (mk & wmask) {                                    // wave-uniform
@@ -339,9 +325,7 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
                 }
             }
         }
-        __syncthreads();                                     // slot is free for the block NBUF ahead
-#pragma unroll
-        for (int i = 0; i < NBUF - 1; ++i) jq[i] = jq[i + 1];
+        j = jnext;
     }
 
     if (S == 1) {
