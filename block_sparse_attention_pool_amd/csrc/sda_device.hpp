@@ -1,5 +1,5 @@
 // Device helpers shared by the gfx950 kernels: bf16 storage, vector types,
-// wave64 cross-lane reductions (DPP inside a 16-lane row, permute across
+// wave64 cross-lane reductions (DPP inside a 16-lane row, row swaps across
 // rows) and the 16x16x32 bf16 MFMA.
 #pragma once
 
@@ -53,19 +53,23 @@ __device__ __forceinline__ float row16_max(float x) {
     return x;
 }
 
-// value of lane (lane ^ mask) for mask in {16, 32}: across 16-lane rows
-__device__ __forceinline__ float xor_lane(float x, int mask) {
-    int lane = __lane_id();
-    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
-}
-// max / sum over the four lanes {l, l^16, l^32, l^48}
+// max / sum over the four lanes {l, l^16, l^32, l^48}, with the gfx950 row
+// swaps (VALU, no LDS round trip): permlane16_swap(x, x) hands lane l the
+// pair (value of the even row, value of the odd row) of its two 16-lane rows,
+// permlane32_swap the pair of its two 32-lane halves, so each step combines
+// the two entries of the pair.  The pair is the same two values on both
+// lanes, so every lane of the four ends with the same bits.
 __device__ __forceinline__ float cross4_max(float x) {
-    x = fmaxf(x, xor_lane(x, 16));
-    return fmaxf(x, xor_lane(x, 32));
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float cross4_sum(float x) {
-    x += xor_lane(x, 16);
-    return x + xor_lane(x, 32);
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // ---- MFMA -------------------------------------------------------------------
