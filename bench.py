@@ -695,7 +695,7 @@ def measure_grouped(O):
             o, _, _ = sda.sda_grouped_decode(Q, K, V, seq, bis[0], ns, C, mode=mode, ws=ws)
             outs[name] = o
         # exact verification with all NQ draft queries of a sequence as one
-        # group (NQ * G = 128 rows: the row-tiled engine, its union split among
+        # group (NQ * G = 64 rows at G = 4: the row-tiled engine, its union split among
         # workgroups): each distinct block is fetched once per (batch, KV head)
         CA = cfg.NQ
         ws = torch.zeros(max(16, sda.lib().sda_grouped_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d,

@@ -300,13 +300,16 @@ __device__ __forceinline__ void step_finish(const AttnArgs& a, const StepPos& p,
     __syncthreads();                                        // LDS free again
 }
 
-// a workgroup that only scores and selects
+// a workgroup that only scores and selects: `passes` rounds of per_wg chunks
 template <int D>
 __device__ __forceinline__ void step_score_role(const AttnArgs& a, int w, char* smem) {
-    const StepPos p = step_pos(a, w);
-    step_scores<D>(a, p, smem);
-    step_level1(a, p, smem);
-    step_finish(a, p, w, smem);
+    for (int pass = 0; pass < a.step.passes; ++pass) {
+        const int vw = w * a.step.passes + pass;
+        const StepPos p = step_pos(a, vw);
+        step_scores<D>(a, p, smem);
+        step_level1(a, p, smem);
+        step_finish(a, p, vw, smem);
+    }
 }
 
 // The refresh of this layer's compressed keys ([SparDA] §4.2 step 1: the key
@@ -919,7 +922,8 @@ static hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     if (step) {
         size_t need = step_lds_bytes(a.step.sel.top_k, a.step.cpr, a.step.per_wg);
         if (need > smem) smem = need;
-        const int wgs = (a.step.sel.rows * a.step.cpr + a.step.per_wg - 1) / a.step.per_wg;
+        const int per = a.step.per_wg * a.step.passes;
+        const int wgs = (a.step.sel.rows * a.step.cpr + per - 1) / per;
         extra_rows = (wgs + a.n_split - 1) / a.n_split;
         aa.step.ref_rows = 0;
         if (a.step.ref_kt) {

@@ -105,7 +105,8 @@ struct StepScore {
     int* counters;            // [rows] chunk arrivals; zero between calls
     SelectArgs sel;           // rows = B * H_kv
     int cpr;                  // chunks per row
-    int per_wg;               // chunks per workgroup (groups of four waves)
+    int per_wg;               // chunks per workgroup pass (groups of four waves)
+    int passes;               // passes per scoring workgroup (chunks w * passes * per_wg ..)
     // Optional: workgroups after the scoring ones refresh this layer's
     // compressed keys for the tokens [ref_len_old, seq_len) (ref_kt null = off)
     uint16_t* ref_kt;         // [B, H_kv, ref_NB_cap, D]

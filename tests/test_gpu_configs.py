@@ -292,7 +292,7 @@ def test_c4_grouped_verification(c4_data, gamma):
                     sl = slice(g * G, (g + 1) * G)
                     errA = max(errA, np.abs(outA[b, c, sl].double().cpu().numpy() - oa[ci]).max())
                     errB = max(errB, np.abs(outB[b, c, sl].double().cpu().numpy() - ob[ci]).max())
-    # all 16 draft queries of a sequence as one exact group (C * G = 128 rows:
+    # all 16 draft queries of a sequence as one exact group (C * G = 64 rows at G = 4:
     # the row-tiled engine, its union shared among split-K workgroups)
     out16, _, u16 = sda.sda_grouped_decode(Qg, K, V, seq(cfg), bi, ns, cfg.NQ, sda.SDA_GROUP_EXACT)
     u16 = u16.cpu().numpy()
