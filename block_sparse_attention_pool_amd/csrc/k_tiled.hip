@@ -1,19 +1,24 @@
 // Row-tiled block-sparse attention: many query rows of one KV head share
 // every block load.  Used for prefill, where every query position attends to
 // its own block set ([SparDA] eq. (3) and (7) per position; the complexity
-// section's eq. (15) counts k blocks of attention per query token).
+// section's eq. (15) counts k blocks of attention per query token), and for
+// exact verification of groups of more than 32 query heads ([SSV] core
+// mechanism 1: the union of the group's lists loaded once).
 //
 // A workgroup owns a tile of Cq consecutive queries of one (b, g): R = Cq*G
 // rows (query, head), 16 per wave, kept in registers for the whole walk (the
 // Q fragments, the online-softmax state and the O accumulators).  The tile's
 // block lists are merged into a bitmap in LDS (bit c of word j: query c lists
 // block j).  The workgroup walks the set blocks in ascending order and loads
-// each block's K and V once into LDS with direct loads, the next block in
-// flight while the current one is computed (two slots, one barrier per
-// block); every wave computes only the blocks that one of its queries lists
-// and masks each row to its own list and, in prefill, to the tokens at or
-// before its position.  A row belongs to one wave, so nothing is merged: each
-// wave normalises and writes its own rows.
+// each block's K and V once into LDS with direct loads, later blocks in
+// flight while the current one is computed (two slots in prefill, up to four
+// in verification; one barrier per block); every wave computes only the
+// blocks that one of its queries lists and masks each row to its own list
+// and, in prefill, to the tokens at or before its position.  A row belongs to
+// one wave, so nothing is merged inside a workgroup: each wave normalises and
+// writes its own rows.  Verification tiles may split their union among
+// several workgroups (split-K), whose (m, l, o) partials the last to finish
+// merges.
 //
 // Per block and wave (16 rows):
 //   S^T[tok][row] = K[tok][:] . Q[row][:]     16x16x32 bf16 MFMA; K is the A
@@ -28,6 +33,7 @@
 // MFMA; what bounds it is how often a block is fetched, which the tile size
 // sets (one fetch per tile instead of one per group of a few positions).
 #include <limits.h>
+#include <type_traits>
 #include <math.h>
 
 #include "sda_attn_dev.hpp"
@@ -38,12 +44,16 @@ namespace sda {
 
 namespace {
 
-// blocks in flight per workgroup: two K and V buffers (64 KB at d = 128) let
-// two workgroups share a compute unit, which measured faster (21 against
-// 38 ms on the 32K prefill) than three or four buffers with one workgroup;
-// with two slots one barrier per block suffices (19.1 against 22.0 ms with a
-// second barrier that freed the slot)
-constexpr int kBufs = 2;
+// Blocks in flight per workgroup (slots of K and V in LDS).  Prefill keeps
+// two (64 KB at d = 128), so that two workgroups share a compute unit: that
+// measured faster (21 against 38 ms on the 32K prefill) than three or four
+// slots with one workgroup.  Verification tiles walk a few blocks each
+// between a prologue and a split merge, so there the block's load latency is
+// the cost and the host grants as many slots as LDS holds beside the bitmap
+// (up to four).
+constexpr int kPrefillBufs = 2;
+constexpr int kMaxBufs = 4;
+constexpr int kPre = 4;          // list entries per thread loaded in the prologue
 
 // the first block above j whose bitmap word is set (nb if none); wave-uniform
 __device__ __forceinline__ int next_set(const uint32_t* bm, int j, int nb) {
@@ -56,32 +66,70 @@ __device__ __forceinline__ int next_set(const uint32_t* bm, int j, int nb) {
     return nb;
 }
 
+// Bits k of the result: word w0 + k of the bitmap is set and below nb (16
+// words from w0, a multiple of 16; the bitmap is allocated and cleared in
+// whole multiples of 16 words).
+__device__ __forceinline__ uint32_t set_words16(const uint32_t* bm, int w0, int nb) {
+    if (w0 >= nb) return 0u;
+    const u32x4* p = reinterpret_cast<const u32x4*>(bm + w0);
+    const u32x4 x0 = p[0], x1 = p[1], x2 = p[2], x3 = p[3];
+    uint32_t m = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        m |= (x0[k] != 0u ? 1u : 0u) << k;
+        m |= (x1[k] != 0u ? 1u : 0u) << (4 + k);
+        m |= (x2[k] != 0u ? 1u : 0u) << (8 + k);
+        m |= (x3[k] != 0u ? 1u : 0u) << (12 + k);
+    }
+    const int valid = nb - w0;
+    return valid >= 16 ? m : (m & ((1u << valid) - 1u));
+}
+
+// Wave sum of a per-lane count in [0, 16] and the sum over lower lanes, from
+// one ballot per bit of the count.
+__device__ __forceinline__ void wave_count_scan(int cnt, int& below, int& total) {
+    below = 0;
+    total = 0;
+#pragma unroll
+    for (int bit = 0; bit < 5; ++bit) {
+        const uint64_t bal = __ballot((cnt >> bit) & 1);
+        below += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))
+                 << bit;
+        total += __popcll(bal) << bit;
+    }
+}
+
 template <int N>
 __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, int W, int NBUF>
+// GRP: verification tiles (split-K, up to kMaxBufs slots); otherwise prefill
+// (one workgroup per tile, kPrefillBufs slots)
+template <int D, int W, bool GRP>
 __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     constexpr int KS = D / 32;                   // QK k-steps
     constexpr int MTD = D / 16;                  // PV m-tiles over d
     constexpr int ROWB = D * 2;                  // bytes per token row
     constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
     constexpr int TILE = kBlock * ROWB;          // bytes of one K (or V) tile
-    constexpr int PPL = TILE / 16 / (W * kWave); // 16-byte pieces per lane per tile
+    constexpr int NT = W * kWave;                // threads
+    constexpr int PPL = TILE / 16 / NT;          // 16-byte pieces per lane per tile
     static_assert(4 * KS == W * PPL, "one K operand per direct load");
     static_assert(PPL >= 1, "at least one piece per lane");
+    static_assert(4 * PPL < 64, "two blocks' loads fit the vmcnt counter");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     SDA_LDS char* lds = (SDA_LDS char*)smem;
-    uint32_t* bm = reinterpret_cast<uint32_t*>(smem + (size_t)NBUF * 2 * TILE);
+    const int nbuf = GRP ? a.nbuf : kPrefillBufs;
+    uint32_t* bm = reinterpret_cast<uint32_t*>(smem + (size_t)nbuf * 2 * TILE);
 
     // tile -> (b, g, query tile): consecutive workgroups go to the eight XCDs
     // in turn, so when the (b, g) pairs come in multiples of eight, XCD x
     // walks the query tiles of pairs x, x + 8, ... from the last one down (the
     // longest lists first), and tiles that share blocks share an L2
-    const int S = a.n_split;
-    const int split = (int)(blockIdx.x % (unsigned)S);
-    const int wg = (int)(blockIdx.x / (unsigned)S);
+    const int S = GRP ? a.n_split : 1;
+    const int split = GRP ? (int)(blockIdx.x % (unsigned)S) : 0;
+    const int wg = GRP ? (int)(blockIdx.x / (unsigned)S) : (int)blockIdx.x;
     const int P = a.B * a.H_kv;
     int pair, tile;
     if ((P & 7) == 0) {
@@ -99,10 +147,9 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int li = lane & 15, lg = lane >> 4;
+    // the length, the Q fragments and the tile's first list entries are all
+    // requested before any of them is waited for
     const int T = min(ld_ro(a.seq_len + b), a.T_cap);
-    int nb = (max(T, 0) + kBlock - 1) / kBlock;
-    if (a.prefill) nb = min(nb, (a.pos0 + q0 + Cg - 1) / kBlock + 1);
-    nb = min(nb, min(a.NB_cap, a.bm_words));
 
     // this lane's row and the wave's queries
     const int r = wave * 16 + li;
@@ -122,22 +169,45 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = ldg16(qp + ks * 32);
     }
+    // entry i = (query i / n_sel_max, position i % n_sel_max) of the tile's
+    // lists; the first kPre per thread are loaded here (indexes clamped into
+    // the lists so the loads need no branch), the rest after the clear
+    const int nsm = a.n_sel_max;
+    const int n_ent = Cg * nsm;
+    const int nbmax = min(a.NB_cap, a.bm_words);         // blocks the bitmap holds
+    int pj[kPre], pn[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const int i = min((int)threadIdx.x + u * NT, n_ent - 1);
+        const int qc = i / nsm, e = i - qc * nsm;
+        const size_t row = ((size_t)b * a.NQ + q0 + qc) * a.H_kv + g;
+        pn[u] = a.n_sel[row];
+        pj[u] = a.block_idx[row * nsm + e];
+    }
 
     // the tile's bitmap
-    for (int i = threadIdx.x; i < nb; i += W * kWave) bm[i] = 0u;
+    const int bm_alloc = (a.bm_words + 15) & ~15;
+    for (int i = threadIdx.x; i < bm_alloc; i += NT) bm[i] = 0u;
     __syncthreads();
-    {
-        const int nsm = a.n_sel_max;
-        for (int i = threadIdx.x; i < Cg * nsm; i += W * kWave) {
-            const int qc = i / nsm, e = i - (i / nsm) * nsm;
-            const size_t row = ((size_t)b * a.NQ + q0 + qc) * a.H_kv + g;
-            const int n = min(max(a.n_sel[row], 0), nsm);
-            if (e < n) {
-                const int j = a.block_idx[row * nsm + e];
-                if (j >= 0 && j < nb) atomicOr(&bm[j], 1u << qc);
-            }
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const int i = (int)threadIdx.x + u * NT;
+        const int qc = i / nsm, e = i - qc * nsm;
+        const int n = min(max(pn[u], 0), nsm);
+        if (i < n_ent && e < n && pj[u] >= 0 && pj[u] < nbmax) atomicOr(&bm[pj[u]], 1u << qc);
+    }
+    for (int i = threadIdx.x + kPre * NT; i < n_ent; i += NT) {
+        const int qc = i / nsm, e = i - qc * nsm;
+        const size_t row = ((size_t)b * a.NQ + q0 + qc) * a.H_kv + g;
+        const int n = min(max(a.n_sel[row], 0), nsm);
+        if (e < n) {
+            const int j = a.block_idx[row * nsm + e];
+            if (j >= 0 && j < nbmax) atomicOr(&bm[j], 1u << qc);
         }
     }
+    int nb = (max(T, 0) + kBlock - 1) / kBlock;
+    if (a.prefill) nb = min(nb, (a.pos0 + q0 + Cg - 1) / kBlock + 1);
+    nb = min(nb, nbmax);
     // the Q fragments have landed: pass them through an asm so the compiler
     // counts no load of them against the direct loads below
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -146,34 +216,39 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     __syncthreads();
 
     // the union's size and this split's share of it: entries [e0, e1) in
-    // ascending block order; jn = the block of entry e0
+    // ascending block order; jn = the block of entry e0.  Lane l looks at
+    // words 16 l .. 16 l + 15 of each 1024-word chunk.
     int n_u = 0, e0 = 0, e1 = 0, jn = nb;
-    {
-        for (int base = 0; base < nb; base += kWave) {
-            const int idx = base + lane;
-            n_u += __popcll(__ballot(idx < nb && bm[idx] != 0u));
-        }
-        e0 = (int)(((long long)split * n_u) / S);
-        e1 = (int)(((long long)(split + 1) * n_u) / S);
-        if (e0 < e1) {
-            int seen = 0;
-            for (int base = 0; base < nb; base += kWave) {
-                const int idx = base + lane;
-                uint64_t bal = __ballot(idx < nb && bm[idx] != 0u);
-                const int cnt = __popcll(bal);
-                if (e0 < seen + cnt) {
-                    for (int k = e0 - seen; k > 0; --k) bal &= bal - 1;     // drop the lower set bits
-                    jn = base + __builtin_ctzll(bal);
-                    break;
-                }
-                seen += cnt;
+    for (int base = 0; base < nb; base += 16 * kWave) {
+        int below, tot;
+        wave_count_scan(__popc(set_words16(bm, base + lane * 16, nb)), below, tot);
+        n_u += tot;
+    }
+    e0 = (int)(((long long)split * n_u) / S);
+    e1 = (int)(((long long)(split + 1) * n_u) / S);
+    if (e0 < e1) {
+        int seen = 0;
+        for (int base = 0; base < nb; base += 16 * kWave) {
+            const int w0 = base + lane * 16;
+            uint32_t m16 = set_words16(bm, w0, nb);
+            const int cnt = __popc(m16);
+            int below, tot;
+            wave_count_scan(cnt, below, tot);
+            if (e0 < seen + tot) {                               // wave-uniform
+                const int k = e0 - seen - below;                 // rank inside this lane's words
+                const bool own = k >= 0 && k < cnt;
+                if (own)
+                    for (int t = k; t > 0; --t) m16 &= m16 - 1u;     // drop the lower set bits
+                const int pos = own ? w0 + __builtin_ctz(m16) : 0;
+                const uint64_t ob = __ballot(own);
+                jn = __builtin_amdgcn_readlane(pos, __builtin_ctzll(ob));
+                break;
             }
+            seen += tot;
         }
     }
     if (a.union_count && split == 0 && threadIdx.x == 0)
         a.union_count[((size_t)b * a.n_tiles + tile) * a.H_kv + g] = n_u;
-    int to_issue = e1 - e0;                 // blocks of this split not yet issued
-
     const uint16_t* kbase = a.k + ((size_t)b * a.H_kv + g) * a.T_cap * D;
     const uint16_t* vbase = a.v + ((size_t)b * a.H_kv + g) * a.T_cap * D;
     auto issue = [&](int j, int slot) {
@@ -210,28 +285,8 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     const int v_lane = (lg * 8 + (li >> 2)) * ROWB + (li & 3) * 8;   // row 8 lg + li / 4, column bytes
     const int v_perm = VTile<D>::perm(lg * 8 + (li >> 2));
 
-    // Two slots, one barrier per block: at the top of iteration it the wave
-    // waits for its share of block j (the only loads it has in flight), and
-    // the barrier then says both that all of j has landed and that every wave
-    // is done with block it - 1, whose slot the loads of the next block fill
-    // while j is computed.
-    static_assert(NBUF == 2, "one barrier per block needs exactly two slots");
-    auto advance = [&](int j) { return --to_issue > 0 ? next_set(bm, j, nb) : nb; };
-    int j = jn;
-    if (j < nb) {
-        issue(j, 0);
-        jn = advance(j);
-    }
-    for (int it = 0; j < nb; ++it) {
-        const int slot = it & 1;
-        vm_wait<0>();
-        __syncthreads();
-        const int jnext = jn;
-        if (jnext < nb) {
-            issue(jnext, slot ^ 1);
-            jn = advance(jnext);
-        }
-
+    // the work of block j, whose K and V sit in `slot`
+    auto compute = [&](int j, int slot) {
         const uint32_t mk = bm[j];
         if (mk & wmask) {                                    // wave-uniform
             SDA_LDS const char* kl = lds + (size_t)slot * 2 * TILE;
@@ -325,10 +380,66 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
                 }
             }
         }
-        j = jnext;
+    };
+
+    // nbuf slots, one barrier per block: blocks go to slots in turn and up to
+    // nbuf - 1 are in flight.  At the top of iteration it the wave waits for
+    // its share of block it (the loads of the blocks issued after it may stay
+    // in flight: they are the last ones it issued), and the barrier then says
+    // both that all of it has landed and that every wave is done with the
+    // block before it, whose slot the next block's loads fill while it is
+    // computed.
+    int to_issue = e1 - e0;                 // blocks of this split not yet issued
+    if constexpr (!GRP) {
+        // two slots: the block issued in one iteration is computed in the next
+        auto advance = [&](int j) { return --to_issue > 0 ? next_set(bm, j, nb) : nb; };
+        int j = jn;
+        if (j < nb) {
+            issue(j, 0);
+            jn = advance(j);
+        }
+        for (int it = 0; j < nb; ++it) {
+            const int slot = it & 1;
+            vm_wait<0>();
+            __syncthreads();
+            const int jnext = jn;
+            if (jnext < nb) {
+                issue(jnext, slot ^ 1);
+                jn = advance(jnext);
+            }
+            compute(j, slot);
+            j = jnext;
+        }
+    } else {
+        int j_iss = jn, n_iss = 0, islot = 0;   // the next block to issue, blocks issued, its slot
+        int ring0 = nb, ring1 = nb, ring2 = nb, ring3 = nb;   // the block in each slot (wave-uniform)
+        auto issue_next = [&]() {
+            issue(j_iss, islot);
+            ring0 = islot == 0 ? j_iss : ring0;
+            ring1 = islot == 1 ? j_iss : ring1;
+            ring2 = islot == 2 ? j_iss : ring2;
+            ring3 = islot == 3 ? j_iss : ring3;
+            ++n_iss;
+            islot = islot + 1 == nbuf ? 0 : islot + 1;
+            j_iss = --to_issue > 0 ? next_set(bm, j_iss, nb) : nb;
+        };
+        for (int s0 = 0; s0 < nbuf - 1 && j_iss < nb; ++s0) issue_next();
+        const int share = e1 - e0;
+        int slot = 0;
+        for (int it = 0; it < share; ++it) {
+            const int ahead = n_iss - it - 1;                // blocks issued after this one, at most nbuf - 2
+            if (ahead >= 2) vm_wait<4 * PPL>();
+            else if (ahead == 1) vm_wait<2 * PPL>();
+            else vm_wait<0>();
+            __syncthreads();
+            const int j = slot == 0 ? ring0 : slot == 1 ? ring1 : slot == 2 ? ring2 : ring3;
+            if (j_iss < nb) issue_next();
+            compute(j, slot);
+            slot = slot + 1 == nbuf ? 0 : slot + 1;
+        }
     }
 
-    if (S == 1) {
+    if (!GRP || S == 1) {
         if (row_ok && r < Cg * G) {
             const size_t oi = ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h;
             const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -341,6 +452,7 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
         return;
     }
 
+    if constexpr (GRP) {
     // ---- split-K: publish (m, l, o) of every row, the last workgroup merges ----
     // Agent-scope stores (write-through: the merging workgroup may sit on
     // another XCD), completed before one agent-scope increment per workgroup;
@@ -375,51 +487,97 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     }
     __syncthreads();
     if (!*s_last) return;
-    // each wave merges its own 16 rows: lane = (row lane / 4, columns D / 4 * (lane % 4) ..)
-    constexpr int CPL = D / 4;                                   // columns per lane
-    const int mr = wave * 16 + lane / 4;
-    const int mc = (lane & 3) * CPL;
+    // each wave merges its own 16 rows.  Lane r (and r + 16, r + 32, r + 48)
+    // reads row r's (m, l) of every split and forms the row's maximum, scale
+    // factors and normaliser; the o partials are read one row per load (lane
+    // = D / 64 adjacent columns, so a load covers the row's contiguous
+    // bytes), every load of a batch of kMergeBatch splits in flight together
+    // (indexes clamped to the last split, so no branch separates them), and
+    // summed in split order with the row's factor taken from lane r.
+    constexpr int CPL = D / kWave;                               // columns per lane
+    using ovec = typename std::conditional<CPL == 2, uint64_t, uint32_t>::type;
+    constexpr int kMlBatch = 16, kMergeBatch = 4;
+    const int r16 = lane & 15;
+    const size_t row0 = tg * S * RP + (size_t)wave * 16;        // split 0, the wave's first row
+    const uint64_t* pml = reinterpret_cast<const uint64_t*>(a.part_ml) + row0 + r16;
+    const ovec* pob = reinterpret_cast<const ovec*>(a.part_o + row0 * D) + lane;   // rows kWave ovecs apart
     float M = -INFINITY;
-    for (int s2 = 0; s2 < S; ++s2)
-        M = fmaxf(M, __hip_atomic_load(a.part_ml + ((tg * S + s2) * RP + mr) * 2, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT));
-    float L = 0.f, acc[CPL];
+    for (int s0 = 0; s0 < S; s0 += kMlBatch) {
+        uint64_t w[kMlBatch];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
-    if (M != -INFINITY) {
-        for (int s2 = 0; s2 < S; ++s2) {
-            const size_t pr = (tg * S + s2) * RP + mr;
-            const float ms = __hip_atomic_load(a.part_ml + pr * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float ls = __hip_atomic_load(a.part_ml + pr * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float sc = __builtin_amdgcn_exp2f(ms - M);                      // 0 for an empty split
-            L += ls * sc;
-            const uint64_t* po = reinterpret_cast<const uint64_t*>(a.part_o + pr * D + mc);
+        for (int i = 0; i < kMlBatch; ++i)
+            w[i] = __hip_atomic_load(pml + (size_t)min(s0 + i, S - 1) * RP, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-            for (int i = 0; i < CPL / 2; ++i) {
-                const uint64_t w2 = __hip_atomic_load(po + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                acc[2 * i] += __uint_as_float((uint32_t)w2) * sc;
-                acc[2 * i + 1] += __uint_as_float((uint32_t)(w2 >> 32)) * sc;
+        for (int i = 0; i < kMlBatch; ++i) M = fmaxf(M, __uint_as_float((uint32_t)w[i]));
+    }
+    float L = 0.f, acc[16][CPL];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+        for (int cc2 = 0; cc2 < CPL; ++cc2) acc[rr][cc2] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+        uint64_t w[kMergeBatch];
+        ovec ov[kMergeBatch][16];
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+            const size_t sp = (size_t)min(s0 + i, S - 1) * RP;
+            w[i] = __hip_atomic_load(pml + sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr)
+                ov[i][rr] = __hip_atomic_load(pob + (sp + rr) * kWave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+            if (s0 + i < S) {
+                const float ms = __uint_as_float((uint32_t)w[i]);
+                const float ls = __uint_as_float((uint32_t)(w[i] >> 32));
+                // 0 for an empty split, and for every split of a row no split saw
+                const float sc = M != -INFINITY ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
+                L += ls * sc;
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const float scr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), rr));
+                    if constexpr (CPL == 2) {
+                        acc[rr][0] += __uint_as_float((uint32_t)ov[i][rr]) * scr;
+                        acc[rr][1] += __uint_as_float((uint32_t)((uint64_t)ov[i][rr] >> 32)) * scr;
+                    } else {
+                        acc[rr][0] += __uint_as_float((uint32_t)ov[i][rr]) * scr;
+                    }
+                }
             }
         }
     }
-    const int mcq = mr / G, mh = mr - (mr / G) * G;
-    if (mcq < Cg && mr < Cg * G) {
-        const size_t oi = ((size_t)b * a.NQ + q0 + mcq) * a.H_q + (size_t)g * G + mh;
-        const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float inv_l = L > 0.f ? 1.f / L : 0.f;                 // lane r16's row
 #pragma unroll
-        for (int i = 0; i < CPL; i += 4)
-            *reinterpret_cast<floatx4*>(&a.out[oi * D + mc + i]) =
-                floatx4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv};
-        if ((lane & 3) == 0 && a.lse) a.lse[oi] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+    for (int rr = 0; rr < 16; ++rr) {
+        const int mr = wave * 16 + rr;
+        const int mcq = mr / G, mh = mr - (mr / G) * G;
+        if (mcq < Cg && mr < Cg * G) {                           // wave-uniform
+            const size_t oi = ((size_t)b * a.NQ + q0 + mcq) * a.H_q + (size_t)g * G + mh;
+            const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_l), rr));
+            if constexpr (CPL == 2)
+                *reinterpret_cast<float2*>(&a.out[oi * D + lane * 2]) = float2{acc[rr][0] * inv, acc[rr][1] * inv};
+            else
+                a.out[oi * D + lane] = acc[rr][0] * inv;
+        }
+    }
+    {
+        const int mr = wave * 16 + r16;
+        const int mcq = mr / G, mh = mr - (mr / G) * G;
+        if (lane < 16 && mcq < Cg && mr < Cg * G && a.lse) {
+            const size_t oi = ((size_t)b * a.NQ + q0 + mcq) * a.H_q + (size_t)g * G + mh;
+            a.lse[oi] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+        }
     }
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + tg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
-template <int D, int W, int NBUF>
+template <int D, int W, bool GRP>
 hipError_t launch_tw(const TiledArgs& a, hipStream_t s) {
-    const size_t lds = tiled_lds_bytes(D, a.bm_words);
-    const unsigned tiles = (unsigned)((size_t)a.B * a.H_kv * a.n_tiles * a.n_split);
-    hipLaunchKernelGGL((tiled_attn_kernel<D, W, NBUF>), dim3(tiles), dim3(W * 64), lds, s, a);
+    const size_t lds = tiled_lds_bytes(D, a.bm_words, GRP ? a.nbuf : kPrefillBufs);
+    const unsigned tiles = (unsigned)((size_t)a.B * a.H_kv * a.n_tiles * (GRP ? a.n_split : 1));
+    hipLaunchKernelGGL((tiled_attn_kernel<D, W, GRP>), dim3(tiles), dim3(W * 64), lds, s, a);
     return hipGetLastError();
 }
 
@@ -441,15 +599,28 @@ size_t tiled_ws_bytes(int tiles, int n_split, int waves, int d) {
     return ((size_t)tiles * 4 + 255) / 256 * 256 + rows * 2 * 4 + rows * (size_t)d * 4;
 }
 
-size_t tiled_lds_bytes(int d, int bm_words) { return (size_t)kBufs * 2 * kBlock * d * 2 + (size_t)bm_words * 4; }
+// slots of K and V, then the bitmap in whole multiples of 16 words
+size_t tiled_lds_bytes(int d, int bm_words, int nbuf) {
+    return (size_t)nbuf * 2 * kBlock * d * 2 + (size_t)((bm_words + 15) / 16 * 16) * 4;
+}
+
+int tiled_grouped_bufs(int d, int bm_words) {
+    for (int n = kMaxBufs; n >= 2; --n)
+        if (tiled_lds_bytes(d, bm_words, n) <= kTiledLdsMax) return n;
+    return 0;
+}
 
 hipError_t tiled_grant_lds() {
-    const void* kerns[] = {reinterpret_cast<const void*>(tiled_attn_kernel<128, 8, kBufs>),
-                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 4, kBufs>),
-                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 2, kBufs>),
-                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 8, kBufs>),
-                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 4, kBufs>),
-                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 2, kBufs>)};
+    const void* kerns[] = {reinterpret_cast<const void*>(tiled_attn_kernel<128, 8, false>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 4, false>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 2, false>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 8, false>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 4, false>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 2, false>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 8, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 4, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 8, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 4, true>)};
     for (const void* k : kerns) {
         const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTiledLdsMax);
         if (e != hipSuccess) return e;
@@ -457,14 +628,24 @@ hipError_t tiled_grant_lds() {
     return hipSuccess;
 }
 
+// prefill (a.prefill set): kPrefillBufs slots, one workgroup per tile;
+// verification: a.nbuf slots (2 .. 4) and a.n_split workgroups per tile, on
+// 4 or 8 waves
 hipError_t launch_tiled_attention(const TiledArgs& a, int d, hipStream_t s) {
     const hipError_t e = device_setup();
     if (e != hipSuccess) return e;
-    if (tiled_lds_bytes(d, a.bm_words) > kTiledLdsMax) return hipErrorInvalidValue;
     const int W = tiled_waves_rows(a.Cq * a.G);
-    if (d == 128) return W == 8 ? launch_tw<128, 8, kBufs>(a, s) : W == 4 ? launch_tw<128, 4, kBufs>(a, s)
-                                                                         : launch_tw<128, 2, kBufs>(a, s);
-    return W == 8 ? launch_tw<64, 8, kBufs>(a, s) : W == 4 ? launch_tw<64, 4, kBufs>(a, s) : launch_tw<64, 2, kBufs>(a, s);
+    if (a.prefill) {
+        if (a.n_split != 1 || tiled_lds_bytes(d, a.bm_words, kPrefillBufs) > kTiledLdsMax) return hipErrorInvalidValue;
+        if (d == 128) return W == 8 ? launch_tw<128, 8, false>(a, s) : W == 4 ? launch_tw<128, 4, false>(a, s)
+                                                                             : launch_tw<128, 2, false>(a, s);
+        return W == 8 ? launch_tw<64, 8, false>(a, s) : W == 4 ? launch_tw<64, 4, false>(a, s)
+                                                              : launch_tw<64, 2, false>(a, s);
+    }
+    if (a.nbuf < 2 || a.nbuf > kMaxBufs || a.n_split < 1 || W < 4 || tiled_lds_bytes(d, a.bm_words, a.nbuf) > kTiledLdsMax)
+        return hipErrorInvalidValue;
+    if (d == 128) return W == 8 ? launch_tw<128, 8, true>(a, s) : launch_tw<128, 4, true>(a, s);
+    return W == 8 ? launch_tw<64, 8, true>(a, s) : launch_tw<64, 4, true>(a, s);
 }
 
 }  // namespace sda

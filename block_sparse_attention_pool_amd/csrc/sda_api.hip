@@ -936,7 +936,7 @@ sda_status_t sda_prefill_attention(const void* q, const void* k, const void* v, 
     // the row-tiled engine: up to 128 rows of consecutive positions per
     // workgroup, every block of their union fetched once into LDS
     const int bm_words = std::min(NB_cap, ceil_div((long long)pos0 + NQ, kBlock));
-    REQUIRE(tiled_lds_bytes(d, bm_words) <= kTiledLdsMax, SDA_ERR_UNSUPPORTED,
+    REQUIRE(tiled_lds_bytes(d, bm_words, 2) <= kTiledLdsMax, SDA_ERR_UNSUPPORTED,
             "a block bitmap of %d words does not fit in LDS", bm_words);
     TiledArgs t{};
     t.q = static_cast<const uint16_t*>(q);
@@ -960,6 +960,7 @@ sda_status_t sda_prefill_attention(const void* q, const void* k, const void* v, 
     t.prefill = 1;
     t.pos0 = pos0;
     t.bm_words = bm_words;
+    t.nbuf = 2;
     t.scale_log2 = scale * 1.4426950408889634f;
     t.n_split = 1;
     REQUIRE(fits_int({B, H_kv, t.n_tiles}), SDA_ERR_SHAPE, "too many query tiles");
@@ -1021,7 +1022,8 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
         const int W = tiled_waves_rows(group_C * G);
         const int S = grouped_tile_splits((int)tasks, W, split_k);
         const size_t need = tiled_ws_bytes((int)tasks, S, W, d);
-        REQUIRE(tiled_lds_bytes(d, NB_cap) <= kTiledLdsMax, SDA_ERR_UNSUPPORTED, "NB_cap=%d: bitmap beyond LDS", NB_cap);
+        const int nbuf = tiled_grouped_bufs(d, NB_cap);
+        REQUIRE(nbuf >= 2, SDA_ERR_UNSUPPORTED, "NB_cap=%d: bitmap beyond LDS", NB_cap);
         REQUIRE(need == 0 || (ws && ws_bytes >= need), SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
                 ws ? ws_bytes : 0, need);
         REQUIRE(need == 0 || aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -1047,6 +1049,7 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
         t.prefill = 0;
         t.pos0 = 0;
         t.bm_words = NB_cap;
+        t.nbuf = nbuf;
         t.scale_log2 = scale * 1.4426950408889634f;
         t.n_split = S;
         t.union_count = union_count_opt;

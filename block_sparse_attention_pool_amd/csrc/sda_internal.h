@@ -186,6 +186,7 @@ struct TiledArgs {
     int n_tiles;              // ceil(NQ / Cq)
     int prefill, pos0;        // prefill: query q sees tokens below pos0 + q + 1
     int bm_words;             // bitmap words in LDS: >= the blocks any tile may list
+    int nbuf;                 // verification tiles: K/V slots in LDS (2 .. 4); prefill uses 2
     float scale_log2;
     // split-K (n_split > 1): the union of a tile is shared among n_split
     // workgroups; each writes (m, l, o) of its rows and the last to arrive merges
@@ -199,7 +200,8 @@ int tiled_queries_per_tile(int G);
 int tiled_waves_rows(int rows);   // 2, 4 or 8 waves for up to 128 rows
 int tiled_waves(int G);
 size_t tiled_ws_bytes(int tiles, int n_split, int waves, int d);
-size_t tiled_lds_bytes(int d, int bm_words);
+size_t tiled_lds_bytes(int d, int bm_words, int nbuf);
+int tiled_grouped_bufs(int d, int bm_words);   // most slots (<= 4) that fit beside the bitmap; 0 if none
 hipError_t tiled_grant_lds();
 hipError_t launch_tiled_attention(const TiledArgs& a, int d, hipStream_t s);
 
