@@ -852,17 +852,38 @@ constexpr int kPlanMaxSplits = 1024;          // the planner tries at most this 
 constexpr int kMaxGridRows = 65535;
 
 
+// Workgroups of one shape that a compute unit holds at once: its LDS share,
+// and the wave slots of its four SIMDs (slots_simd waves each at the engine's
+// register count).  Workgroups of up to four waves pack over the SIMDs; a
+// larger one takes ceil(W / 4) slots on every SIMD (measured on gfx950 with
+// workgroups that hold their compute unit: at 150-168 VGPRs, three waves per
+// SIMD, five- to ten-wave workgroups run one per compute unit, four-wave ones
+// three, two-wave ones six).
+static int wgs_per_cu(int W, size_t lds, int slots_simd) {
+    const int by_lds = (int)(kLdsPerCU / lds);
+    const int by_slots = W <= 4 ? (4 * slots_simd) / W : slots_simd / ((W + 3) / 4);
+    return max(1, min(by_lds, by_slots));
+}
+
 // Launch shape of the attention kernel: W waves per workgroup, n_split
 // workgroups per row group; a wave walks its split's entries W apart, so it
 // handles ceil(list / (n_split * W)) blocks one after another.  Cost of a
-// shape = dispatch rounds x blocks per wave.  Among the cheapest, keep the one
-// with the most blocks in flight in the first round (at most all of them),
-// then the one that reaches the most CUs, then the fewest splits (less
-// partial traffic), then the fewest waves.
+// shape = dispatch rounds x (kRoundCost + blocks per wave): a round's head
+// (launch, block ids, first K) and tail (merges) cost about two blocks' time
+// (at the 64K verification workload, 19 blocks per row: one round of
+// four-wave workgroups, five blocks per wave, 29.2 us; two rounds of
+// ten-wave ones, two blocks per wave, 34.2 us; two rounds of five-wave
+// ones 32.2 us).  Workgroups take at least four waves (or the split's whole
+// share): single-wave workgroups of many splits measured slower still (42.5
+// us there).  Among the cheapest, keep the one with the most blocks in
+// flight in the first round (at most all of them), then the one that
+// reaches the most CUs, then the fewest splits (less partial traffic), then
+// the fewest waves.
+constexpr int kRoundCost = 2;
 AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode, int NB_cap, int n_sel_max,
                    int split_k) {
     const int max_w = rows_pad == 16 ? kMaxWaves : 4;
-    const int slots = rows_pad == 16 ? 12 : 4;          // resident waves per CU (VGPR-bound)
+    const int slots_simd = rows_pad == 16 ? 3 : 1;     // resident waves per SIMD (168 or 356 VGPRs)
     if (list_max < 1) list_max = 1;
     if (split_k > 0) {
         int W = (list_max + split_k - 1) / split_k;
@@ -877,16 +898,14 @@ AttnPlan attn_plan(int d, int rows_pad, int tasks, int list_max, int C, int mode
     const long long total = (long long)tasks * list_max;
     for (int ns = 1; ns <= min(list_max, kPlanMaxSplits); ++ns) {
         const int per_split = (list_max + ns - 1) / ns;
-        for (int W = 1; W <= min(max_w, per_split); ++W) {
+        for (int W = min(4, per_split); W <= min(max_w, per_split); ++W) {
             const size_t lds = smem_base(d, rows_pad, W) + union_extra(C, mode, NB_cap, n_sel_max, W);
             if (lds > kLdsPerCU) continue;
-            int per_cu = (int)(kLdsPerCU / lds);
-            if (per_cu * W > slots) per_cu = slots / W;
-            if (per_cu < 1) per_cu = 1;
+            const int per_cu = wgs_per_cu(W, lds, slots_simd);
             const long long wgs = (long long)tasks * ns;
             const long long cap = (long long)kCUs * per_cu;
             const long long rounds = (wgs + cap - 1) / cap;
-            const long long cost = rounds * ((per_split + W - 1) / W);
+            const long long cost = rounds * (kRoundCost + (per_split + W - 1) / W);
             long long flight = (wgs < cap ? wgs : cap) * W;
             if (flight > total) flight = total;
             const long long cus = wgs < kCUs ? wgs : kCUs;
