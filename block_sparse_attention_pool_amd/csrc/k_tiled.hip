@@ -104,10 +104,21 @@ __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Waves per workgroup: RW row waves (16 rows each), times two in verification
+// tiles of up to 64 rows, whose two waves per 16 rows take the two 32-token
+// halves of every block (each keeps its own softmax state; the pair merges
+// at the end), so the chain of dependent work per block is halved.
+template <int RW, bool GRP>
+constexpr int tiled_ksplit() { return GRP && RW <= 4 ? 2 : 1; }
+
 // GRP: verification tiles (split-K, up to kMaxBufs slots); otherwise prefill
 // (one workgroup per tile, kPrefillBufs slots)
-template <int D, int W, bool GRP>
-__global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
+template <int D, int RW, bool GRP>
+__global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_attn_kernel(TiledArgs a) {
+    constexpr int KSPLIT = tiled_ksplit<RW, GRP>();
+    constexpr int W = RW * KSPLIT;               // waves
+    constexpr int MTH = 4 / KSPLIT;              // QK m-tiles (16 tokens each) of a wave
+    constexpr int KHH = 2 / KSPLIT;              // PV token halves (32 tokens each) of a wave
     constexpr int KS = D / 32;                   // QK k-steps
     constexpr int MTD = D / 16;                  // PV m-tiles over d
     constexpr int ROWB = D * 2;                  // bytes per token row
@@ -146,21 +157,23 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     const int G = a.G;
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int rw = wave % RW;                     // the wave's 16 rows
+    const int th = wave / RW;                     // and its token share of each block
     const int li = lane & 15, lg = lane >> 4;
     // the length, the Q fragments and the tile's first list entries are all
     // requested before any of them is waited for
     const int T = min(ld_ro(a.seq_len + b), a.T_cap);
 
     // this lane's row and the wave's queries
-    const int r = wave * 16 + li;
+    const int r = rw * 16 + li;
     const int c = r / G, h = r - (r / G) * G;
     const bool row_ok = c < Cg;
     const int cc = min(c, Cg - 1);
-    const int cw0 = (wave * 16) / G, cw1 = min((wave * 16 + 15) / G, Cg - 1);
+    const int cw0 = (rw * 16) / G, cw1 = min((rw * 16 + 15) / G, Cg - 1);
     const uint32_t wmask = cw1 >= cw0 ? (uint32_t)((((uint64_t)1 << (cw1 + 1)) - 1) & ~(((uint64_t)1 << cw0) - 1)) : 0u;
     const int lim = a.prefill ? a.pos0 + q0 + cc + 1 : INT_MAX;     // tokens below lim are visible
     const int lim_w = a.prefill ? a.pos0 + q0 + min(cw0, Cg - 1) + 1 : INT_MAX;   // the wave's smallest
-    const bool wave_real = wave * 16 + 16 <= Cg * G;
+    const bool wave_real = rw * 16 + 16 <= Cg * G;
 
     // Q fragments (B operand): row r, dims ks * 32 + lg * 8
     u32x4 qf[KS];
@@ -294,10 +307,11 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
             const int nvalid = min(kBlock, T - j * kBlock);
             // every row of the wave is a real row that lists j and sees all of it
             const bool full = nvalid == kBlock && wave_real && (mk & wmask) == wmask && j * kBlock + kBlock <= lim_w;
-            floatx4 s[4];
-            SDA_LDS const char* kq = kl + lane * 16;
+            // m-tiles th * MTH .. (tokens 32 th .. 32 th + 31 when split)
+            floatx4 s[MTH];
+            SDA_LDS const char* kq = kl + lane * 16 + th * (MTH * KS * kWave * 16);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int mt = 0; mt < MTH; ++mt) {
                 floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
@@ -307,25 +321,25 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
                 s[mt] = acc;
             }
             if (!full) {
-                // output i of m-tile mt is token tok_of(mt, 4 lg + i) = 8 lg + e(mt, i):
+                // output i of m-tile mg is token tok_of(mg, 4 lg + i) = 8 lg + e(mg, i):
                 // it counts when e < thr
                 const bool live = row_ok && ((mk >> cc) & 1u);
-                const int thr = (live ? min(nvalid, lim - j * kBlock) : 0) - lg * 8;
+                const int thr = (live ? min(nvalid, lim - j * kBlock) : 0) - lg * 8 - th * 32;
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+                for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (!((mt >> 1) * 32 + (mt & 1) * 4 + i < thr)) s[mt][i] = -INFINITY;
             }
             float mx = -INFINITY;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) mx = fmaxf(mx, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
+            for (int mt = 0; mt < MTH; ++mt) mx = fmaxf(mx, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
             mx = cross4_max(mx) * csc;
             const float m_new = fmaxf(m_run, mx);
             const float m_use = m_new != -INFINITY ? m_new : 0.f;
             float psum = 0.f;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < MTH; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float p = __builtin_amdgcn_exp2f(fmaf(s[mt][i], csc, -m_use));
@@ -346,9 +360,9 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
             }
             l_run += psum;
             m_run = m_new;
-            u32x4 pf[2], pl[2];
+            u32x4 pf[KHH], pl[KHH];
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
+            for (int kh = 0; kh < KHH; ++kh)
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const float p0 = s[2 * kh + (w >> 1)][(w & 1) * 2];
@@ -363,9 +377,9 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
             // so one address per md and the (kh, hh) offsets are immediates
 #pragma unroll
             for (int md = 0; md < MTD; ++md) {
-                SDA_LDS const char* vq = vl + v_lane + ((md ^ v_perm) << 5);
+                SDA_LDS const char* vq = vl + v_lane + ((md ^ v_perm) << 5) + th * (32 * ROWB);
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh) {
+                for (int kh = 0; kh < KHH; ++kh) {
                     u32x4 va;
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
@@ -439,8 +453,40 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
         }
     }
 
+    if constexpr (KSPLIT == 2) {
+        // the two waves of each 16 rows merge their token halves: the second
+        // puts (m, l, o) in LDS (the slots are free once every wave is past
+        // the barrier), the first reads them with the same lane layout
+        float* xo = reinterpret_cast<float*>(smem);                     // [RW][MTD][64] x 4
+        float* xm = xo + RW * MTD * kWave * 4;                          // [RW][64]
+        float* xl = xm + RW * kWave;
+        __syncthreads();
+        if (th == 1) {
+#pragma unroll
+            for (int md = 0; md < MTD; ++md)
+                *reinterpret_cast<floatx4*>(xo + ((rw * MTD + md) * kWave + lane) * 4) = o[md];
+            xm[rw * kWave + lane] = m_run;
+            xl[rw * kWave + lane] = l_run;
+        }
+        __syncthreads();
+        if (th == 0) {
+            const float m2 = xm[rw * kWave + lane], l2 = xl[rw * kWave + lane];
+            const float M = fmaxf(m_run, m2);
+            const float a1 = M != -INFINITY ? __builtin_amdgcn_exp2f(m_run - M) : 0.f;
+            const float a2 = M != -INFINITY ? __builtin_amdgcn_exp2f(m2 - M) : 0.f;
+            l_run = l_run * a1 + l2 * a2;
+            m_run = M;
+#pragma unroll
+            for (int md = 0; md < MTD; ++md) {
+                const floatx4 o2 = *reinterpret_cast<const floatx4*>(xo + ((rw * MTD + md) * kWave + lane) * 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[md][i] = o[md][i] * a1 + o2[i] * a2;
+            }
+        }
+    }
+
     if (!GRP || S == 1) {
-        if (row_ok && r < Cg * G) {
+        if (th == 0 && row_ok && r < Cg * G) {
             const size_t oi = ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h;
             const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
@@ -457,9 +503,10 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     // Agent-scope stores (write-through: the merging workgroup may sit on
     // another XCD), completed before one agent-scope increment per workgroup;
     // the last arrival acquires and reads them with agent-scope loads.
-    constexpr int RP = W * 16;
+    constexpr int RP = RW * 16;                                  // rows of a tile
+    constexpr int RPW = RP / W;                                  // rows each wave merges
     const size_t tg = (size_t)pair * a.n_tiles + tile;          // this tile
-    {
+    if (th == 0) {
         const size_t pr = (tg * S + split) * RP + r;
         uint64_t* po = reinterpret_cast<uint64_t*>(a.part_o + pr * D + lg * 4);
 #pragma unroll
@@ -487,18 +534,18 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     }
     __syncthreads();
     if (!*s_last) return;
-    // each wave merges its own 16 rows.  Lane r (and r + 16, r + 32, r + 48)
-    // reads row r's (m, l) of every split and forms the row's maximum, scale
-    // factors and normaliser; the o partials are read one row per load (lane
-    // = D / 64 adjacent columns, so a load covers the row's contiguous
-    // bytes), every load of a batch of kMergeBatch splits in flight together
-    // (indexes clamped to the last split, so no branch separates them), and
-    // summed in split order with the row's factor taken from lane r.
+    // each wave merges RPW rows.  Lane r (and r + RPW, ...) reads row r's
+    // (m, l) of every split and forms the row's maximum, scale factors and
+    // normaliser; the o partials are read one row per load (lane = D / 64
+    // adjacent columns, so a load covers the row's contiguous bytes), every
+    // load of a batch of kMergeBatch splits in flight together (indexes
+    // clamped to the last split, so no branch separates them), and summed in
+    // split order with the row's factor taken from lane r.
     constexpr int CPL = D / kWave;                               // columns per lane
     using ovec = typename std::conditional<CPL == 2, uint64_t, uint32_t>::type;
     constexpr int kMlBatch = 16, kMergeBatch = 4;
-    const int r16 = lane & 15;
-    const size_t row0 = tg * S * RP + (size_t)wave * 16;        // split 0, the wave's first row
+    const int r16 = lane % RPW;
+    const size_t row0 = tg * S * RP + (size_t)wave * RPW;       // split 0, the wave's first row
     const uint64_t* pml = reinterpret_cast<const uint64_t*>(a.part_ml) + row0 + r16;
     const ovec* pob = reinterpret_cast<const ovec*>(a.part_o + row0 * D) + lane;   // rows kWave ovecs apart
     float M = -INFINITY;
@@ -510,20 +557,20 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
 #pragma unroll
         for (int i = 0; i < kMlBatch; ++i) M = fmaxf(M, __uint_as_float((uint32_t)w[i]));
     }
-    float L = 0.f, acc[16][CPL];
+    float L = 0.f, acc[RPW][CPL];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr)
+    for (int rr = 0; rr < RPW; ++rr)
 #pragma unroll
         for (int cc2 = 0; cc2 < CPL; ++cc2) acc[rr][cc2] = 0.f;
     for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
         uint64_t w[kMergeBatch];
-        ovec ov[kMergeBatch][16];
+        ovec ov[kMergeBatch][RPW];
 #pragma unroll
         for (int i = 0; i < kMergeBatch; ++i) {
             const size_t sp = (size_t)min(s0 + i, S - 1) * RP;
             w[i] = __hip_atomic_load(pml + sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr)
+            for (int rr = 0; rr < RPW; ++rr)
                 ov[i][rr] = __hip_atomic_load(pob + (sp + rr) * kWave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
@@ -535,7 +582,7 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
                 const float sc = M != -INFINITY ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
                 L += ls * sc;
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
+                for (int rr = 0; rr < RPW; ++rr) {
                     const float scr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), rr));
                     if constexpr (CPL == 2) {
                         acc[rr][0] += __uint_as_float((uint32_t)ov[i][rr]) * scr;
@@ -549,8 +596,8 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     }
     const float inv_l = L > 0.f ? 1.f / L : 0.f;                 // lane r16's row
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-        const int mr = wave * 16 + rr;
+    for (int rr = 0; rr < RPW; ++rr) {
+        const int mr = wave * RPW + rr;
         const int mcq = mr / G, mh = mr - (mr / G) * G;
         if (mcq < Cg && mr < Cg * G) {                           // wave-uniform
             const size_t oi = ((size_t)b * a.NQ + q0 + mcq) * a.H_q + (size_t)g * G + mh;
@@ -562,9 +609,9 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
         }
     }
     {
-        const int mr = wave * 16 + r16;
+        const int mr = wave * RPW + r16;
         const int mcq = mr / G, mh = mr - (mr / G) * G;
-        if (lane < 16 && mcq < Cg && mr < Cg * G && a.lse) {
+        if (lane < RPW && mcq < Cg && mr < Cg * G && a.lse) {
             const size_t oi = ((size_t)b * a.NQ + q0 + mcq) * a.H_q + (size_t)g * G + mh;
             a.lse[oi] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
         }
@@ -573,11 +620,11 @@ __global__ __launch_bounds__(W * 64) void tiled_attn_kernel(TiledArgs a) {
     }
 }
 
-template <int D, int W, bool GRP>
+template <int D, int RW, bool GRP>
 hipError_t launch_tw(const TiledArgs& a, hipStream_t s) {
     const size_t lds = tiled_lds_bytes(D, a.bm_words, GRP ? a.nbuf : kPrefillBufs);
     const unsigned tiles = (unsigned)((size_t)a.B * a.H_kv * a.n_tiles * (GRP ? a.n_split : 1));
-    hipLaunchKernelGGL((tiled_attn_kernel<D, W, GRP>), dim3(tiles), dim3(W * 64), lds, s, a);
+    hipLaunchKernelGGL((tiled_attn_kernel<D, RW, GRP>), dim3(tiles), dim3(RW * tiled_ksplit<RW, GRP>() * 64), lds, s, a);
     return hipGetLastError();
 }
 
