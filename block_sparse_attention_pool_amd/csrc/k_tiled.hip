@@ -538,26 +538,20 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
     // (m, l) of every split and forms the row's maximum, scale factors and
     // normaliser; the o partials are read one row per load (lane = D / 64
     // adjacent columns, so a load covers the row's contiguous bytes), every
-    // load of a batch of kMergeBatch splits in flight together (indexes
-    // clamped to the last split, so no branch separates them), and summed in
-    // split order with the row's factor taken from lane r.
+    // load of a batch of splits in flight together (indexes clamped to the
+    // last split, so no branch separates them), and summed in split order
+    // with the row's factor taken from lane r.
     constexpr int CPL = D / kWave;                               // columns per lane
     using ovec = typename std::conditional<CPL == 2, uint64_t, uint32_t>::type;
-    constexpr int kMlBatch = 16, kMergeBatch = 4;
+    constexpr int kMergeBatch = RPW <= 8 ? 8 : 4;
     const int r16 = lane % RPW;
     const size_t row0 = tg * S * RP + (size_t)wave * RPW;       // split 0, the wave's first row
     const uint64_t* pml = reinterpret_cast<const uint64_t*>(a.part_ml) + row0 + r16;
     const ovec* pob = reinterpret_cast<const ovec*>(a.part_o + row0 * D) + lane;   // rows kWave ovecs apart
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < S; s0 += kMlBatch) {
-        uint64_t w[kMlBatch];
-#pragma unroll
-        for (int i = 0; i < kMlBatch; ++i)
-            w[i] = __hip_atomic_load(pml + (size_t)min(s0 + i, S - 1) * RP, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int i = 0; i < kMlBatch; ++i) M = fmaxf(M, __uint_as_float((uint32_t)w[i]));
-    }
-    float L = 0.f, acc[RPW][CPL];
+    // one batch of kMergeBatch splits: their (m, l) words and o rows all in
+    // flight together, then the batch folded into the running (M, L, acc) by
+    // log-sum-exp (a single batch, the usual case, is the plain merge)
+    float M = -INFINITY, L = 0.f, acc[RPW][CPL];
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr)
 #pragma unroll
@@ -573,6 +567,22 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
             for (int rr = 0; rr < RPW; ++rr)
                 ov[i][rr] = __hip_atomic_load(pob + (sp + rr) * kWave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        float Mb = M;
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) Mb = fmaxf(Mb, __uint_as_float((uint32_t)w[i]));
+        if (s0 > 0) {
+            // earlier batches: rescale every row by its own factor (lane r's
+            // row r; 1 while the row has seen nothing), in every lane
+            const float al = (M != -INFINITY && Mb != M) ? __builtin_amdgcn_exp2f(M - Mb) : 1.f;
+            L *= al;
+#pragma unroll
+            for (int rr = 0; rr < RPW; ++rr) {
+                const float alr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), rr));
+#pragma unroll
+                for (int cc2 = 0; cc2 < CPL; ++cc2) acc[rr][cc2] *= alr;
+            }
+        }
+        M = Mb;
 #pragma unroll
         for (int i = 0; i < kMergeBatch; ++i) {
             if (s0 + i < S) {
@@ -638,6 +648,10 @@ int tiled_waves_rows(int rows) {
     return w <= 2 ? 2 : (w <= 4 ? 4 : 8);
 }
 int tiled_waves(int G) { return tiled_waves_rows(tiled_queries_per_tile(G) * G); }
+int tiled_grouped_rw(int rows) {
+    const int w = (rows + 15) / 16;
+    return w <= 1 ? 1 : (w <= 2 ? 2 : (w <= 4 ? 4 : 8));
+}
 
 // split-K workspace: [counters, 256-byte padded][(m, l) per split and row][o per split and row]
 size_t tiled_ws_bytes(int tiles, int n_split, int waves, int d) {
@@ -666,8 +680,12 @@ hipError_t tiled_grant_lds() {
                            reinterpret_cast<const void*>(tiled_attn_kernel<64, 2, false>),
                            reinterpret_cast<const void*>(tiled_attn_kernel<128, 8, true>),
                            reinterpret_cast<const void*>(tiled_attn_kernel<128, 4, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 2, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 1, true>),
                            reinterpret_cast<const void*>(tiled_attn_kernel<64, 8, true>),
-                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 4, true>)};
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 4, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 2, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 1, true>)};
     for (const void* k : kerns) {
         const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTiledLdsMax);
         if (e != hipSuccess) return e;
@@ -677,22 +695,27 @@ hipError_t tiled_grant_lds() {
 
 // prefill (a.prefill set): kPrefillBufs slots, one workgroup per tile;
 // verification: a.nbuf slots (2 .. 4) and a.n_split workgroups per tile, on
-// 4 or 8 waves
+// 1, 2, 4 or 8 row waves
 hipError_t launch_tiled_attention(const TiledArgs& a, int d, hipStream_t s) {
     const hipError_t e = device_setup();
     if (e != hipSuccess) return e;
-    const int W = tiled_waves_rows(a.Cq * a.G);
     if (a.prefill) {
+        const int W = tiled_waves_rows(a.Cq * a.G);
         if (a.n_split != 1 || tiled_lds_bytes(d, a.bm_words, kPrefillBufs) > kTiledLdsMax) return hipErrorInvalidValue;
         if (d == 128) return W == 8 ? launch_tw<128, 8, false>(a, s) : W == 4 ? launch_tw<128, 4, false>(a, s)
                                                                              : launch_tw<128, 2, false>(a, s);
         return W == 8 ? launch_tw<64, 8, false>(a, s) : W == 4 ? launch_tw<64, 4, false>(a, s)
                                                               : launch_tw<64, 2, false>(a, s);
     }
-    if (a.nbuf < 2 || a.nbuf > kMaxBufs || a.n_split < 1 || W < 4 || tiled_lds_bytes(d, a.bm_words, a.nbuf) > kTiledLdsMax)
+    const int RW = tiled_grouped_rw(a.Cq * a.G);
+    if (a.nbuf < 2 || a.nbuf > kMaxBufs || a.n_split < 1 || a.Cq * a.G > 128 ||
+        tiled_lds_bytes(d, a.bm_words, a.nbuf) > kTiledLdsMax)
         return hipErrorInvalidValue;
-    if (d == 128) return W == 8 ? launch_tw<128, 8, true>(a, s) : launch_tw<128, 4, true>(a, s);
-    return W == 8 ? launch_tw<64, 8, true>(a, s) : launch_tw<64, 4, true>(a, s);
+    if (d == 128)
+        return RW == 8 ? launch_tw<128, 8, true>(a, s) : RW == 4 ? launch_tw<128, 4, true>(a, s)
+             : RW == 2 ? launch_tw<128, 2, true>(a, s) : launch_tw<128, 1, true>(a, s);
+    return RW == 8 ? launch_tw<64, 8, true>(a, s) : RW == 4 ? launch_tw<64, 4, true>(a, s)
+         : RW == 2 ? launch_tw<64, 2, true>(a, s) : launch_tw<64, 1, true>(a, s);
 }
 
 }  // namespace sda

@@ -969,19 +969,31 @@ sda_status_t sda_prefill_attention(const void* q, const void* k, const void* v, 
     return hip_status(launch_tiled_attention(t, d, static_cast<hipStream_t>(stream)), "prefill_attention launch");
 }
 
-// Exact grouped verification with more than 32 rows per group (C * G up to
-// 128, C up to 32) runs on the row-tiled engine: the group's union walked
-// once through LDS, shared among S workgroups (split-K) so that a few groups
-// still fill the chip.
+// Exact grouped verification of two or more queries (C * G up to 128 rows, C
+// up to 32) runs on the row-tiled engine: the group's union walked once
+// through LDS, shared among S workgroups (split-K) so that a few groups still
+// fill the chip.
 static bool grouped_on_tiles(int group_C, int G, int mode) {
-    return mode == SDA_GROUP_EXACT && group_C * G > 32 && group_C * G <= 128 && group_C <= 32;
+    return mode == SDA_GROUP_EXACT && group_C >= 2 && group_C * G <= 128 && group_C <= 32;
 }
-// splits: about four waves per compute unit over the launch (measured at the
-// 64K verification workload: 16-query groups best at 4 splits, 48.7 us against
-// 51.9 at 8 and 106 at 1; 8-query groups at 4, 37.3 against 61.1 at 8)
-static int grouped_tile_splits(int tiles, int waves, int split_k) {
-    if (split_k > 0) return std::min(split_k, 64);
-    return std::max(1, std::min(16, 4 * kCUs / std::max(tiles * waves, 1)));
+// Splits and K/V slots: one workgroup per compute unit with as many slots as
+// LDS holds (up to four), S = CUs / tiles; when that leaves fewer than four
+// splits and two-slot workgroups fit twice per compute unit, two slots and
+// twice the splits.
+struct TilePlan {
+    int S, nbuf;
+};
+static TilePlan grouped_tile_plan(int tiles, int d, int NB_cap, int split_k) {
+    const int nb_max = tiled_grouped_bufs(d, NB_cap);
+    const bool two_fit = 2 * tiled_lds_bytes(d, NB_cap, 2) <= kTiledLdsMax;
+    tiles = std::max(tiles, 1);
+    if (split_k > 0) {
+        const int S = std::min(split_k, 64);
+        return TilePlan{S, ((long long)tiles * S > kCUs && two_fit) ? 2 : nb_max};
+    }
+    const int S1 = std::max(1, std::min(16, kCUs / tiles));
+    if (S1 < 4 && two_fit) return TilePlan{std::max(1, std::min(16, 2 * kCUs / tiles)), 2};
+    return TilePlan{S1, nb_max};
 }
 
 size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap,
@@ -993,8 +1005,7 @@ size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_
     const int n_groups = ceil_div(NQ, group_C);
     const int tasks = B * n_groups * H_kv;
     if (grouped_on_tiles(group_C, G, mode))
-        return tiled_ws_bytes(tasks, grouped_tile_splits(tasks, tiled_waves_rows(group_C * G), split_k),
-                              tiled_waves_rows(group_C * G), d);
+        return tiled_ws_bytes(tasks, grouped_tile_plan(tasks, d, NB_cap, split_k).S, tiled_grouped_rw(group_C * G), d);
     if (group_C > 8 || group_C * G > 32) return 0;
     const int rp = attn_rows_pad(group_C, G);
     const AttnPlan p = attn_plan(d, rp, tasks, grouped_list_estimate(group_C, mode, n_sel_max), group_C, mode,
@@ -1019,11 +1030,11 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
     const long long tasks = (long long)B * n_groups * H_kv;
     if (grouped_on_tiles(group_C, G, mode)) {
         REQUIRE(tasks <= (1LL << 24), SDA_ERR_SHAPE, "B*groups*H_kv=%lld exceeds %d", tasks, 1 << 24);
-        const int W = tiled_waves_rows(group_C * G);
-        const int S = grouped_tile_splits((int)tasks, W, split_k);
-        const size_t need = tiled_ws_bytes((int)tasks, S, W, d);
-        const int nbuf = tiled_grouped_bufs(d, NB_cap);
-        REQUIRE(nbuf >= 2, SDA_ERR_UNSUPPORTED, "NB_cap=%d: bitmap beyond LDS", NB_cap);
+        const int RW = tiled_grouped_rw(group_C * G);
+        REQUIRE(tiled_grouped_bufs(d, NB_cap) >= 2, SDA_ERR_UNSUPPORTED, "NB_cap=%d: bitmap beyond LDS", NB_cap);
+        const TilePlan tp = grouped_tile_plan((int)tasks, d, NB_cap, split_k);
+        const int S = tp.S;
+        const size_t need = tiled_ws_bytes((int)tasks, S, RW, d);
         REQUIRE(need == 0 || (ws && ws_bytes >= need), SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
                 ws ? ws_bytes : 0, need);
         REQUIRE(need == 0 || aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -1049,13 +1060,13 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
         t.prefill = 0;
         t.pos0 = 0;
         t.bm_words = NB_cap;
-        t.nbuf = nbuf;
+        t.nbuf = tp.nbuf;
         t.scale_log2 = scale * 1.4426950408889634f;
         t.n_split = S;
         t.union_count = union_count_opt;
         if (need) {
             char* base = static_cast<char*>(ws);
-            const size_t rows = (size_t)tasks * S * W * 16;
+            const size_t rows = (size_t)tasks * S * RW * 16;
             t.counters = reinterpret_cast<int*>(base);
             t.part_ml = reinterpret_cast<float*>(base + pad256((size_t)tasks * 4));
             t.part_o = t.part_ml + rows * 2;

@@ -199,6 +199,7 @@ struct TiledArgs {
 int tiled_queries_per_tile(int G);
 int tiled_waves_rows(int rows);   // 2, 4 or 8 waves for up to 128 rows
 int tiled_waves(int G);
+int tiled_grouped_rw(int rows);   // verification tiles: 1, 2, 4 or 8 row waves for up to 128 rows
 size_t tiled_ws_bytes(int tiles, int n_split, int waves, int d);
 size_t tiled_lds_bytes(int d, int bm_words, int nbuf);
 int tiled_grouped_bufs(int d, int bm_words);   // most slots (<= 4) that fit beside the bitmap; 0 if none
