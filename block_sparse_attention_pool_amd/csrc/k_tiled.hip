@@ -508,14 +508,10 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
     const size_t tg = (size_t)pair * a.n_tiles + tile;          // this tile
     if (th == 0) {
         const size_t pr = (tg * S + split) * RP + r;
-        uint64_t* po = reinterpret_cast<uint64_t*>(a.part_o + pr * D + lg * 4);
+        // o: 16 bytes per lane and m-tile (4 lanes fill 64 contiguous bytes of a row)
+        float* pbase = a.part_o + (tg * S + split) * RP * D;
 #pragma unroll
-        for (int md = 0; md < MTD; ++md) {
-            __hip_atomic_store(po + md * 8, ((uint64_t)__float_as_uint(o[md][1]) << 32) | __float_as_uint(o[md][0]),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(po + md * 8 + 1, ((uint64_t)__float_as_uint(o[md][3]) << 32) | __float_as_uint(o[md][2]),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        for (int md = 0; md < MTD; ++md) st_agent16(pbase, (uint32_t)((r * D + md * 16 + lg * 4) * 4), o[md]);
         if (lg == 0)
             __hip_atomic_store(reinterpret_cast<uint64_t*>(a.part_ml + pr * 2),
                                ((uint64_t)__float_as_uint(l_run) << 32) | __float_as_uint(m_run), __ATOMIC_RELAXED,

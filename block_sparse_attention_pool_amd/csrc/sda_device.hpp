@@ -108,6 +108,16 @@ __device__ __forceinline__ int arrive(int* counter) {
 }
 __device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
+// 16 bytes stored at byte offset `off` of a region that starts at the
+// wave-uniform `base`, with the same device-scope cache bit (sc1, written
+// through to the coherence point) as the agent-scope atomic stores above,
+// through a buffer store so that the compiler sees the store (and keeps its
+// data registers intact until the store has read them).
+__device__ __forceinline__ void st_agent16(void* base, uint32_t off, floatx4 v) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 16);
+}
+
 // order-preserving map float -> uint32 (larger float -> larger key); -0 == +0
 __device__ __forceinline__ uint32_t float_key(float x) {
     uint32_t u = __float_as_uint(x);
