@@ -599,8 +599,9 @@ def grouped_lists(cfg, kt, seq, gamma, n_sets):
 
 def profile_grouped(reps=4):
     """Eager launches for hardware-counter runs at the verification workload
-    (gamma = 0.75): the per-query decode, mode A, mode B and NSA's three
-    branches, `reps` launches each in that order, on independent list sets."""
+    (gamma = 0.75): the per-query decode, mode A, mode B, NSA's three
+    branches and exact verification of all 16 draft queries as one group,
+    `reps` launches each in that order, on independent list sets."""
     cfg = synth.get_config(4)
     dev = "cuda"
     K, V, _ = inputs.kv_layer(cfg, 0, device=dev)
@@ -619,7 +620,7 @@ def profile_grouped(reps=4):
     wss = {}
     torch.cuda.synchronize()
     log(f"profile_grouped: sigma {sigma:.4f}; launches in order: per-query x{reps}, mode A x{reps}, "
-        f"mode B x{reps}, NSA x{reps}")
+        f"mode B x{reps}, NSA x{reps}, one group of {cfg.NQ} x{reps}")
     for i in range(reps):
         sda.sda_sparse_decode(Q, K, V, seq, bis[i], ns)
     for mode in (sda.SDA_GROUP_EXACT, sda.SDA_GROUP_SHARED_REP):
@@ -627,6 +628,11 @@ def profile_grouped(reps=4):
             sda.sda_grouped_decode(Q, K, V, seq, bis[i], ns, C, mode=mode)
     for i in range(reps):
         sda.sda_nsa_decode(Q, K, V, kt, vc, seq, bis[i], ns, gates, 64, 512, group_C=C, mode=sda.SDA_GROUP_EXACT)
+    ws16 = torch.zeros(max(16, sda.lib().sda_grouped_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d,
+                                                                      cfg.NB, cfg.NQ, sda.SDA_GROUP_EXACT, 0)),
+                       dtype=torch.uint8, device=dev)
+    for i in range(reps):
+        sda.sda_grouped_decode(Q, K, V, seq, bis[i], ns, cfg.NQ, mode=sda.SDA_GROUP_EXACT, ws=ws16)
     torch.cuda.synchronize()
     blk = 64 * cfg.d * 2 * 2
     bnp = [b.cpu().numpy() for b in bis]

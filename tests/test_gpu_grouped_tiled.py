@@ -1,11 +1,14 @@
-"""GPU parity of exact grouped verification on the row-tiled engine (groups
-of more than 32 rows, C * G up to 128) against the oracle's grouped_row in
-exact mode ([SSV] core mechanism 1: each query attends to its own list, the
-union of the group's lists is fetched once).
+"""GPU parity of exact grouped verification on the row-tiled engine (every
+group of two or more queries, C * G up to 128 rows) against the oracle's
+grouped_row in exact mode ([SSV] core mechanism 1: each query attends to its
+own list, the union of the group's lists is fetched once).
 
 Drawn ascending lists with ragged lengths, empty lists, a last group smaller
-than C, every wave count (64, 96 and 128 rows), split-K from one workgroup
-per group to more splits than union blocks, and the union counts.
+than C, every row-wave count (16, 32, 64, 96 and 128 rows, and groups of
+fewer rows than a wave), both slot plans (four slots with one workgroup per
+compute unit, two slots and twice the splits when there are many groups),
+split-K from one workgroup per group to more splits than union blocks, and
+the union counts.
 """
 import sys
 
@@ -39,6 +42,11 @@ CASES = [
     (1, 1, 8, 64, [700], 20, 8, 9, 3),               # 64 rows, NQ not a multiple of C
     (2, 1, 4, 128, [2500, 2500], 32, 32, 10, 40),    # 128 rows of 32 queries; more splits than blocks
     (1, 2, 8, 64, [900], 12, 12, 7, 5),              # 96 rows: 8 waves, two of them idle
+    (2, 4, 4, 128, [3000, 2000], 16, 4, 12, 0),      # 16 rows: one row wave (two token-half waves)
+    (4, 8, 4, 128, [2048, 1500, 2048, 777], 16, 4, 19, 0),   # 128 groups: two slots, twice the splits
+    (1, 2, 16, 128, [4000], 6, 2, 11, 0),            # 32 rows: two row waves, NQ not a multiple of C
+    (2, 2, 1, 64, [1500, 900], 7, 3, 8, 2),          # 3 rows in a 16-row wave
+    (1, 4, 8, 64, [3100], 8, 2, 13, 64),             # 16 rows, the most splits
 ]
 
 
@@ -98,10 +106,12 @@ def test_grouped_exact_on_tiles(case):
     assert err <= TOL and lerr <= 1e-3
 
 
-def test_grouped_tiles_repeat_bit_identically():
+@pytest.mark.parametrize("B,H,G,C", [(2, 4, 8, 16), (4, 8, 4, 4)])
+def test_grouped_tiles_repeat_bit_identically(B, H, G, C):
     # the split merge's arrival counters are left at zero: calls in a row on
     # one workspace give identical results
-    B, H, G, d, T, NQ, C = 2, 4, 8, 128, 4096, 16, 16
+    d, T, NQ = 128, 4096, 16
+    _say("grouped tiles repeat", B, H, G, C)
     gen = torch.Generator().manual_seed(5)
     K = torch.randn((B, H, T, d), generator=gen).to(torch.bfloat16).to(DEV)
     V = torch.randn((B, H, T, d), generator=gen).to(torch.bfloat16).to(DEV)
@@ -123,4 +133,4 @@ def test_grouped_tiles_repeat_bit_identically():
             first = (out.clone(), lse.clone())
         else:
             assert torch.equal(out, first[0]) and torch.equal(lse, first[1])
-    assert int(ws[:4 * B * H].view(torch.int32).abs().sum().item()) == 0
+    assert int(ws[:4 * B * H * (-(-NQ // C))].view(torch.int32).abs().sum().item()) == 0
