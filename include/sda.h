@@ -249,10 +249,12 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
  *   union_count_opt i32 [B, ceil(NQ / group_C), H_kv] out or NULL: blocks loaded
  *   per group (size of the merged set, or of the first list in shared mode).
  * Other arguments (workspace contract included) as sda_sparse_decode.
- * group_C * G <= 32 and group_C <= 8; in exact mode also larger groups, up
- * to group_C * G = 128 rows and group_C = 32, on the row-tiled engine (the
- * group's union walked once through LDS, shared among split_k workgroups,
- * 0 = chosen by the library).
+ * Shared mode: group_C * G <= 32 and group_C <= 8.  Exact mode: group_C * G
+ * up to 128 rows and group_C up to 32; groups of two or more queries run on
+ * the row-tiled engine (the group's union walked once through LDS, shared
+ * among split_k workgroups, 0 = chosen by the library), group_C = 1 is the
+ * per-query decode.  NB_cap blocks of bitmap must fit in LDS beside two K/V
+ * slots (NB_cap <= 16384 at d = 128), else SDA_ERR_UNSUPPORTED.
  */
 size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap,
                                     int group_C, int mode, int split_k);
