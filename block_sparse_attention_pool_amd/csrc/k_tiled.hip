@@ -278,7 +278,7 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
             const int op = wave + W * i;
             const int mt = op / KS, ks = op - (op / KS) * KS;
             const int tr = min(tok_of(mt, li), tmax);
-            lds_dma16(kb + (size_t)tr * ROWB + ks * 64 + lg * 16, kl + op * kWave * 16);
+            lds_dma16_async(kb + (size_t)tr * ROWB + ks * 64 + lg * 16, kl + op * kWave * 16);
         }
 #pragma unroll
         for (int i = 0; i < PPL; ++i) {
@@ -286,7 +286,7 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
             const int pi = base + lane;
             const int t = pi / CPR, pc = pi - (pi / CPR) * CPR;
             const int tr = min(t, tmax);
-            lds_dma16(vb + (size_t)tr * ROWB + ((pc << 4) ^ (VTile<D>::perm(t) << 5)), vl + base * 16);
+            lds_dma16_async(vb + (size_t)tr * ROWB + ((pc << 4) ^ (VTile<D>::perm(t) << 5)), vl + base * 16);
         }
     };
 
@@ -415,7 +415,7 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
         for (int it = 0; j < nb; ++it) {
             const int slot = it & 1;
             vm_wait<0>();
-            __syncthreads();
+            barrier_lds();
             const int jnext = jn;
             if (jnext < nb) {
                 issue(jnext, slot ^ 1);
@@ -445,7 +445,7 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
             if (ahead >= 2) vm_wait<4 * PPL>();
             else if (ahead == 1) vm_wait<2 * PPL>();
             else vm_wait<0>();
-            __syncthreads();
+            barrier_lds();
             const int j = slot == 0 ? ring0 : slot == 1 ? ring1 : slot == 2 ? ring2 : ring3;
             if (j_iss < nb) issue_next();
             compute(j, slot);

@@ -45,4 +45,23 @@ __device__ __forceinline__ void lds_dma16(const void* g, SDA_LDS void* l) {
     __builtin_amdgcn_global_load_lds(g, l, 16, 0, AUX);
 }
 
+// The same direct load, issued as assembly: the compiler then does not know
+// that it writes LDS, so it adds no wait for it before later LDS reads (it
+// would wait for every direct load in flight, the prefetched blocks
+// included); the caller waits for it with an explicit vmcnt wait.  M0 holds
+// the wave-uniform LDS address (one wait state between setting M0 and the
+// load).
+__device__ __forceinline__ void lds_dma16_async(const void* g, SDA_LDS void* l) {
+    const uint32_t m = (uint32_t)(uintptr_t)l;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
+}
+
+// A workgroup barrier that waits for this wave's LDS operations but not for
+// its vector memory loads (the direct loads of later blocks stay in flight).
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace sda
