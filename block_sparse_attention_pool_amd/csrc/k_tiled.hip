@@ -54,6 +54,7 @@ namespace {
 constexpr int kPrefillBufs = 2;
 constexpr int kMaxBufs = 4;
 constexpr int kPre = 4;          // list entries per thread loaded in the prologue
+constexpr float kLazyMax = 8.f;  // a row's reference maximum lags its true maximum by at most this (log2)
 
 // the first block above j whose bitmap word is set (nb if none); wave-uniform
 __device__ __forceinline__ int next_set(const uint32_t* bm, int j, int nb) {
@@ -335,7 +336,12 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
 #pragma unroll
             for (int mt = 0; mt < MTH; ++mt) mx = fmaxf(mx, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
             mx = cross4_max(mx) * csc;
-            const float m_new = fmaxf(m_run, mx);
+            // the reference maximum of a row moves only when a block's
+            // maximum exceeds it by more than kLazyMax (log2 units): most
+            // blocks then skip the rescale of o, and the probabilities stay
+            // below 2^kLazyMax (fp32 sums; P keeps its hi + lo bf16 parts)
+            const bool grow = m_run == -INFINITY || mx > m_run + kLazyMax;
+            const float m_new = grow ? fmaxf(m_run, mx) : m_run;
             const float m_use = m_new != -INFINITY ? m_new : 0.f;
             float psum = 0.f;
 #pragma unroll
@@ -347,8 +353,9 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
                     psum += p;
                 }
             psum = cross4_sum(psum);
-            if (m_run != -INFINITY) {
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            const bool rescale = grow && m_run != -INFINITY;
+            if (__ballot(rescale)) {                             // wave-uniform
+                const float alpha = rescale ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
                 l_run *= alpha;
 #pragma unroll
                 for (int i = 0; i < MTD; ++i) {
