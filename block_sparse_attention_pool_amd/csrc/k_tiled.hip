@@ -48,9 +48,10 @@ namespace {
 // two (64 KB at d = 128), so that two workgroups share a compute unit: that
 // measured faster (21 against 38 ms on the 32K prefill) than three or four
 // slots with one workgroup.  Verification tiles walk a few blocks each
-// between a prologue and a split merge, so there the block's load latency is
-// the cost and the host grants as many slots as LDS holds beside the bitmap
-// (up to four).
+// between a prologue and a split merge; the host grants them as many slots
+// as LDS holds beside the bitmap (up to four, one workgroup per compute
+// unit), or two when there are enough tiles for two workgroups per compute
+// unit.
 constexpr int kPrefillBufs = 2;
 constexpr int kMaxBufs = 4;
 constexpr int kPre = 4;          // list entries per thread loaded in the prologue
