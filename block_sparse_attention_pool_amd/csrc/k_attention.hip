@@ -193,6 +193,68 @@ __device__ __forceinline__ void merge_row_nsa(const AttnArgs& a, int task, int r
     for (int i = 0; i < PER; ++i) a.out[oi * D + lane + i * kWave] = acc[i];
 }
 
+// The same gated sum for two rows at once (rr[1] < 0: one row) when the row
+// group has at most kCombineMax splits: every split of both rows (the three
+// branches' splits are consecutive) and their gates in one batch of loads,
+// then each branch merged from registers, in the same order as above.
+template <int D, int RP>
+__device__ __forceinline__ void merge_rows_nsa2(const AttnArgs& a, int task, const int (&rr)[2],
+                                                const size_t (&oi)[2], int lane) {
+    constexpr int PER = D / kWave;
+    const int bounds[4] = {0, a.ns_c, a.ns_c + a.ns_s, a.n_split};
+    float mv[2][kCombineMax], lv[2][kCombineMax], ov[2][kCombineMax][PER], gt[2][3];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = rr[q] < 0 ? rr[0] : rr[q];
+        const float* ml = a.part_ml + ((size_t)task * a.n_split * RP + r) * 2;
+        const float* po = a.part_o + ((size_t)task * a.n_split * RP + r) * D + lane;
+#pragma unroll
+        for (int k = 0; k < kCombineMax; ++k) {
+            const bool ok = k < a.n_split;
+            mv[q][k] = ok ? ld_part(ml + (size_t)k * RP * 2) : -INFINITY;
+            lv[q][k] = ok ? ld_part(ml + (size_t)k * RP * 2 + 1) : 0.f;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) ov[q][k][i] = ok ? ld_part(po + (size_t)k * RP * D + i * kWave) : 0.f;
+        }
+        const size_t o3 = (rr[q] < 0 ? oi[0] : oi[q]) * 3;
+#pragma unroll
+        for (int bi = 0; bi < 3; ++bi) gt[q][bi] = a.gates[o3 + bi];
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        if (rr[q] < 0) continue;                                 // wave-uniform
+        float acc[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int bi = 0; bi < 3; ++bi) {
+            float M = -INFINITY, Ls = 0.f, Os[PER];
+#pragma unroll
+            for (int i = 0; i < PER; ++i) Os[i] = 0.f;
+#pragma unroll
+            for (int k = 0; k < kCombineMax; ++k)
+                if (k >= bounds[bi] && k < bounds[bi + 1]) M = fmaxf(M, mv[q][k]);
+            if (M != -INFINITY) {
+#pragma unroll
+                for (int k = 0; k < kCombineMax; ++k)
+                    if (k >= bounds[bi] && k < bounds[bi + 1]) {
+                        const float sc = __builtin_amdgcn_exp2f(mv[q][k] - M);   // 0 for an empty split
+                        Ls += lv[q][k] * sc;
+#pragma unroll
+                        for (int i = 0; i < PER; ++i) Os[i] += ov[q][k][i] * sc;
+                    }
+            }
+            const float w = (Ls > 0.f) ? gt[q][bi] / Ls : 0.f;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) acc[i] += Os[i] * w;
+            if (lane == 0 && a.lse)
+                a.lse[oi[q] * 3 + bi] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) a.out[oi[q] * D + lane + i * kWave] = acc[i];
+    }
+}
+
 // ---- decode step: the next layer's scoring and selection ------------------------
 // Workgroup w scores chunks w * per_wg + i (i < per_wg, one per group of four
 // waves) of the next layer's compressed keys against its indexer vectors,
@@ -693,11 +755,19 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
     }
     __syncthreads();
     if (!*last) return;
-    for (int r = wave; r < R; r += W) {
-        const int c = r / G, h = r - (r / G) * G;
-        const size_t oi = ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h;
-        if constexpr (NSA) merge_row_nsa<D, RP>(a, task, r, oi, lane);
-        else merge_row<D, RP>(a, task, r, oi, lane);
+    auto out_row = [&](int r) { return ((size_t)b * a.NQ + q0 + r / G) * a.H_q + (size_t)g * G + (r - (r / G) * G); };
+    if (NSA && a.n_split <= kCombineMax) {
+        // two rows per wave at a time, all their loads in flight together
+        for (int r = wave; r < R; r += 2 * W) {
+            const int rr[2] = {r, r + W < R ? r + W : -1};
+            const size_t oi[2] = {out_row(r), rr[1] >= 0 ? out_row(rr[1]) : 0};
+            if constexpr (NSA) merge_rows_nsa2<D, RP>(a, task, rr, oi, lane);
+        }
+    } else {
+        for (int r = wave; r < R; r += W) {
+            if constexpr (NSA) merge_row_nsa<D, RP>(a, task, r, out_row(r), lane);
+            else merge_row<D, RP>(a, task, r, out_row(r), lane);
+        }
     }
     if (threadIdx.x == 0) __hip_atomic_store(&a.counters[task], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
