@@ -770,12 +770,15 @@ def measure_grouped(O):
         sda.sda_nsa_decode(Q75, K, V, kc, vc, seq, sets75[i], ns, gates, 64, window, group_C=C,
                            mode=sda.SDA_GROUP_EXACT, out=out, lse=nsa_lse, union_count=ucs_n[i], ws=nsa_ws)
     t = graph_time(nsa_call, copies=n_sets)
-    sel_blocks = sum(int(u.sum().item()) for u in ucs_n) / n_sets
-    win_blocks = groups * (window // 64)
-    cmp_loaded = groups * cfg.NB * cfg.d * 2 * 2
+    # loaded: a row tile holds the 16 queries of one (batch, KV head) (64
+    # rows) and loads the union of their lists, the window's blocks and the
+    # compressed keys and values once
+    kv_rows = cfg.B * cfg.H_kv
+    sel_blocks = dist75
+    win_blocks = kv_rows * (window // 64)
+    cmp_loaded = kv_rows * cfg.NB * cfg.d * 2 * 2
     # distinct: the window's last 8 blocks and the compressed keys and values
     # once per (batch, KV head); window blocks also selected counted once
-    kv_rows = cfg.B * cfg.H_kv
     win_dist = 0
     for bnp in (sets75[0].cpu().numpy(),):
         for b in range(cfg.B):

@@ -113,10 +113,39 @@ __device__ __forceinline__ void vm_wait() {
 template <int RW, bool GRP>
 constexpr int tiled_ksplit() { return GRP && RW <= 4 ? 2 : 1; }
 
+// NSA three-branch mode: the n_split workgroups of a tile go to the branches
+// in proportion to their blocks, at least one to each branch that has any:
+// first one split per non-empty branch, then each further split to the
+// branch with the most blocks per split (the lower branch on a tie).  Every
+// workgroup of the tile computes the same counts, so all agree without
+// communicating.  With no block anywhere, all splits fall to the last branch.
+__device__ __forceinline__ void nsa_assign(int S, int n0, int n1, int n2, int& s0, int& s1) {
+    int c0 = n0 > 0, c1 = n1 > 0, c2 = n2 > 0;
+    if (c0 + c1 + c2 == 0) {
+        s0 = s1 = 0;
+        return;
+    }
+    for (int k = c0 + c1 + c2; k < S; ++k) {
+        // n_i / c_i against n_j / c_j by cross products (a branch with c = 0 has n = 0)
+        const bool t01 = (long long)n0 * c1 >= (long long)n1 * c0;
+        const int bx = t01 ? 0 : 1;
+        const int nx = t01 ? n0 : n1, cx = t01 ? c0 : c1;
+        const bool tx2 = (long long)nx * c2 >= (long long)n2 * cx;
+        const int best = tx2 ? bx : 2;
+        c0 += best == 0;
+        c1 += best == 1;
+        c2 += best == 2;
+    }
+    s0 = c0;
+    s1 = c1;
+}
+
 // GRP: verification tiles (split-K, up to kMaxBufs slots); otherwise prefill
-// (one workgroup per tile, kPrefillBufs slots)
-template <int D, int RW, bool GRP>
+// (one workgroup per tile, kPrefillBufs slots).  NSA (with GRP): the
+// three-branch mode.
+template <int D, int RW, bool GRP, bool NSA = false>
 __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_attn_kernel(TiledArgs a) {
+    static_assert(GRP || !NSA, "the three-branch mode runs on verification tiles");
     constexpr int KSPLIT = tiled_ksplit<RW, GRP>();
     constexpr int W = RW * KSPLIT;               // waves
     constexpr int MTH = 4 / KSPLIT;              // QK m-tiles (16 tokens each) of a wave
@@ -239,9 +268,45 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
         wave_count_scan(__popc(set_words16(bm, base + lane * 16, nb)), below, tot);
         n_u += tot;
     }
-    e0 = (int)(((long long)split * n_u) / S);
-    e1 = (int)(((long long)(split + 1) * n_u) / S);
-    if (e0 < e1) {
+    // the split's branch (NSA), its block range and its share of the range:
+    // tokens [lo, hi) of the rows kbase / vbase point at are visible, blocks
+    // are walked below jend
+    int branch = 1, bsplit = split, bS = S, n_s0 = 0, n_s1 = S;
+    int lo = 0, hi = T, jend = nb;
+    const size_t kvrow = (size_t)b * a.H_kv + g;
+    const uint16_t* kbase = a.k + kvrow * a.T_cap * D;
+    const uint16_t* vbase = a.v + kvrow * a.T_cap * D;
+    if constexpr (NSA) {
+        // compressed entries present at length T, and the window [T - window, T)
+        const int ncmp = min((max(T, 0) + a.cmp_stride - 1) / a.cmp_stride, a.NC_cap);
+        const int wlo = max(0, T - a.window);
+        const int n_c = (ncmp + kBlock - 1) / kBlock;
+        const int n_w = T > wlo ? (T - 1) / kBlock - wlo / kBlock + 1 : 0;
+        nsa_assign(S, n_c, n_u, n_w, n_s0, n_s1);
+        branch = split < n_s0 ? 0 : (split < n_s0 + n_s1 ? 1 : 2);
+        bsplit = branch == 0 ? split : (branch == 1 ? split - n_s0 : split - n_s0 - n_s1);
+        bS = branch == 0 ? n_s0 : (branch == 1 ? n_s1 : S - n_s0 - n_s1);
+        if (branch != 1) {
+            const int cnt = branch == 0 ? n_c : n_w;
+            const int rb = branch == 0 ? 0 : wlo / kBlock;
+            if (branch == 0) {
+                kbase = a.kc + kvrow * a.NC_cap * D;
+                vbase = a.vc + kvrow * a.NC_cap * D;
+                hi = ncmp;
+            } else {
+                lo = wlo;
+            }
+            e0 = bS > 0 ? (int)(((long long)bsplit * cnt) / bS) : 0;
+            e1 = bS > 0 ? (int)(((long long)(bsplit + 1) * cnt) / bS) : 0;
+            jn = rb + e0;                                // = jend when the share is empty
+            jend = rb + e1;
+        }
+    }
+    if (branch == 1) {
+        e0 = (int)(((long long)bsplit * n_u) / bS);
+        e1 = (int)(((long long)(bsplit + 1) * n_u) / bS);
+    }
+    if (branch == 1 && e0 < e1) {
         int seen = 0;
         for (int base = 0; base < nb; base += 16 * kWave) {
             const int w0 = base + lane * 16;
@@ -262,12 +327,13 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
             seen += tot;
         }
     }
-    if (a.union_count && split == 0 && threadIdx.x == 0)
+    if (!NSA && a.union_count && split == 0 && threadIdx.x == 0)
         a.union_count[((size_t)b * a.n_tiles + tile) * a.H_kv + g] = n_u;
-    const uint16_t* kbase = a.k + ((size_t)b * a.H_kv + g) * a.T_cap * D;
-    const uint16_t* vbase = a.v + ((size_t)b * a.H_kv + g) * a.T_cap * D;
+    // the block after j in the walk: the bitmap's next set word, or j + 1 in
+    // a block range
+    auto next_blk = [&](int j) { return (NSA && branch != 1) ? j + 1 : next_set(bm, j, nb); };
     auto issue = [&](int j, int slot) {
-        const int tmax = min(kBlock - 1, T - 1 - j * kBlock);
+        const int tmax = min(kBlock - 1, hi - 1 - j * kBlock);
         const char* kb = reinterpret_cast<const char*>(kbase + (size_t)j * kBlock * D);
         const char* vb = reinterpret_cast<const char*>(vbase + (size_t)j * kBlock * D);
         SDA_LDS char* kl = lds + (size_t)slot * 2 * TILE;
@@ -302,13 +368,14 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
 
     // the work of block j, whose K and V sit in `slot`
     auto compute = [&](int j, int slot) {
-        const uint32_t mk = bm[j];
+        const uint32_t mk = (NSA && branch != 1) ? ~0u : bm[j];   // every query sees a range block
         if (mk & wmask) {                                    // wave-uniform
             SDA_LDS const char* kl = lds + (size_t)slot * 2 * TILE;
             SDA_LDS const char* vl = kl + TILE;
-            const int nvalid = min(kBlock, T - j * kBlock);
+            const int nvalid = min(kBlock, hi - j * kBlock);
             // every row of the wave is a real row that lists j and sees all of it
-            const bool full = nvalid == kBlock && wave_real && (mk & wmask) == wmask && j * kBlock + kBlock <= lim_w;
+            const bool full = nvalid == kBlock && wave_real && (mk & wmask) == wmask && j * kBlock + kBlock <= lim_w &&
+                              (!NSA || j * kBlock >= lo);
             // m-tiles th * MTH .. (tokens 32 th .. 32 th + 31 when split)
             floatx4 s[MTH];
             SDA_LDS const char* kq = kl + lane * 16 + th * (MTH * KS * kWave * 16);
@@ -332,6 +399,15 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (!((mt >> 1) * 32 + (mt & 1) * 4 + i < thr)) s[mt][i] = -INFINITY;
+                if constexpr (NSA) {
+                    // the window's first block: tokens below lo are not in it
+                    const int lthr = lo - j * kBlock - lg * 8 - th * 32;
+#pragma unroll
+                    for (int mt = 0; mt < MTH; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if ((mt >> 1) * 32 + (mt & 1) * 4 + i < lthr) s[mt][i] = -INFINITY;
+                }
             }
             float mx = -INFINITY;
 #pragma unroll
@@ -414,7 +490,7 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
     int to_issue = e1 - e0;                 // blocks of this split not yet issued
     if constexpr (!GRP) {
         // two slots: the block issued in one iteration is computed in the next
-        auto advance = [&](int j) { return --to_issue > 0 ? next_set(bm, j, nb) : nb; };
+        auto advance = [&](int j) { return --to_issue > 0 ? next_blk(j) : nb; };
         int j = jn;
         if (j < nb) {
             issue(j, 0);
@@ -434,7 +510,7 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
         }
     } else {
         int j_iss = jn, n_iss = 0, islot = 0;   // the next block to issue, blocks issued, its slot
-        int ring0 = nb, ring1 = nb, ring2 = nb, ring3 = nb;   // the block in each slot (wave-uniform)
+        int ring0 = jend, ring1 = jend, ring2 = jend, ring3 = jend;   // the block in each slot (wave-uniform)
         auto issue_next = [&]() {
             issue(j_iss, islot);
             ring0 = islot == 0 ? j_iss : ring0;
@@ -443,9 +519,9 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
             ring3 = islot == 3 ? j_iss : ring3;
             ++n_iss;
             islot = islot + 1 == nbuf ? 0 : islot + 1;
-            j_iss = --to_issue > 0 ? next_set(bm, j_iss, nb) : nb;
+            j_iss = --to_issue > 0 ? next_blk(j_iss) : jend;
         };
-        for (int s0 = 0; s0 < nbuf - 1 && j_iss < nb; ++s0) issue_next();
+        for (int s0 = 0; s0 < nbuf - 1 && j_iss < jend; ++s0) issue_next();
         const int share = e1 - e0;
         int slot = 0;
         for (int it = 0; it < share; ++it) {
@@ -455,7 +531,7 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
             else vm_wait<0>();
             barrier_lds();
             const int j = slot == 0 ? ring0 : slot == 1 ? ring1 : slot == 2 ? ring2 : ring3;
-            if (j_iss < nb) issue_next();
+            if (j_iss < jend) issue_next();
             compute(j, slot);
             slot = slot + 1 == nbuf ? 0 : slot + 1;
         }
@@ -493,7 +569,7 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
         }
     }
 
-    if (!GRP || S == 1) {
+    if (!GRP || (!NSA && S == 1)) {
         if (th == 0 && row_ok && r < Cg * G) {
             const size_t oi = ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h;
             const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -525,6 +601,23 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
                                ((uint64_t)__float_as_uint(l_run) << 32) | __float_as_uint(m_run), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
+    if constexpr (NSA) {
+        // the listed blocks' union of each group of Cu queries (counted while
+        // the stores above are on their way): wave w counts groups w, w + W, ..
+        if (a.union_count && split == 0 && a.Cu > 1) {
+            for (int u = wave; u * a.Cu < Cg; u += W) {
+                const int c0 = u * a.Cu, c1 = min(c0 + a.Cu, Cg);
+                const uint32_t gm = (uint32_t)((((uint64_t)1 << c1) - 1) & ~(((uint64_t)1 << c0) - 1));
+                int cnt = 0;
+                for (int base = 0; base < nb; base += kWave) {
+                    const int i = base + lane;
+                    cnt += __popcll(__ballot(i < nb && (bm[i] & gm) != 0u));
+                }
+                if (lane == 0)
+                    a.union_count[((size_t)b * a.n_ugroups + (size_t)tile * (a.Cq / a.Cu) + u) * a.H_kv + g] = cnt;
+            }
+        }
+    }
     // the flag lives in the bitmap's first word: every wave is past its last
     // read of the bitmap at the barrier below (the kernel uses no static LDS,
     // so that the whole 160 KB can be granted to the dynamic part)
@@ -555,54 +648,165 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
     // one batch of kMergeBatch splits: their (m, l) words and o rows all in
     // flight together, then the batch folded into the running (M, L, acc) by
     // log-sum-exp (a single batch, the usual case, is the plain merge)
+    // lane r16's row of the output: whether it is a real row, and its place in out / lse
+    auto row16 = [&](bool& ok, size_t& oi) {
+        const int mr = wave * RPW + r16;
+        const int mcq = mr / G, mh = mr - (mr / G) * G;
+        ok = mcq < Cg && mr < Cg * G;
+        oi = ((size_t)b * a.NQ + q0 + min(mcq, Cg - 1)) * a.H_q + (size_t)g * G + mh;
+    };
     float M = -INFINITY, L = 0.f, acc[RPW][CPL];
+    if constexpr (NSA) {
+        // the gated sum: each branch's splits (bnd[bi] .. bnd[bi + 1]) merged and
+        // normalised, then o = g_c o_c + g_s o_s + g_w o_w, one lse per branch
+        // (natural log, -inf for a branch that saw no token)
+        const int bnd[4] = {0, n_s0, n_s0 + n_s1, S};
+        float gt[3], oacc[RPW][CPL];
+        bool ok16;
+        size_t oi16;
+        row16(ok16, oi16);
 #pragma unroll
-    for (int rr = 0; rr < RPW; ++rr)
+        for (int bi = 0; bi < 3; ++bi) gt[bi] = ok16 ? a.gates[oi16 * 3 + bi] : 0.f;
 #pragma unroll
-        for (int cc2 = 0; cc2 < CPL; ++cc2) acc[rr][cc2] = 0.f;
-    for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+        for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+            for (int cc2 = 0; cc2 < CPL; ++cc2) oacc[rr][cc2] = 0.f;
+        // a batch of splits: their (m, l) words and o rows, batch entry i = split base + i
         uint64_t w[kMergeBatch];
         ovec ov[kMergeBatch][RPW];
+        auto load_batch = [&](int base, int s_hi) {
 #pragma unroll
-        for (int i = 0; i < kMergeBatch; ++i) {
-            const size_t sp = (size_t)min(s0 + i, S - 1) * RP;
-            w[i] = __hip_atomic_load(pml + sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = 0; i < kMergeBatch; ++i) {
+                const size_t sp = (size_t)min(base + i, s_hi - 1) * RP;
+                w[i] = __hip_atomic_load(pml + sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int rr = 0; rr < RPW; ++rr)
+                    ov[i][rr] = __hip_atomic_load(pob + (sp + rr) * kWave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        };
+        // with at most one batch of splits, every split of every branch is
+        // loaded at once and each branch folds its own entries of that batch
+        const bool one_batch = S <= kMergeBatch;
+        if (one_batch) load_batch(0, S);
+#pragma unroll
+        for (int bi = 0; bi < 3; ++bi) {
+            if (bi > 0) {
+                M = -INFINITY;
+                L = 0.f;
+            }
 #pragma unroll
             for (int rr = 0; rr < RPW; ++rr)
-                ov[i][rr] = __hip_atomic_load(pob + (sp + rr) * kWave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        float Mb = M;
 #pragma unroll
-        for (int i = 0; i < kMergeBatch; ++i) Mb = fmaxf(Mb, __uint_as_float((uint32_t)w[i]));
-        if (s0 > 0) {
-            // earlier batches: rescale every row by its own factor (lane r's
-            // row r; 1 while the row has seen nothing), in every lane
-            const float al = (M != -INFINITY && Mb != M) ? __builtin_amdgcn_exp2f(M - Mb) : 1.f;
-            L *= al;
+                for (int cc2 = 0; cc2 < CPL; ++cc2) acc[rr][cc2] = 0.f;
+            const int s_lo = bnd[bi], s_hi = bnd[bi + 1];
+            for (int s0 = s_lo; s0 < s_hi; s0 += kMergeBatch) {
+                if (!one_batch) load_batch(s0, s_hi);
+                const int base = one_batch ? 0 : s0;
+                // entry i belongs to this pass when split base + i lies in [s0, s_hi)
+                float Mb = M;
 #pragma unroll
-            for (int rr = 0; rr < RPW; ++rr) {
-                const float alr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), rr));
+                for (int i = 0; i < kMergeBatch; ++i)
+                    if (!one_batch || (i >= s0 && i < s_hi)) Mb = fmaxf(Mb, __uint_as_float((uint32_t)w[i]));
+                if (s0 > s_lo) {
+                    // earlier batches: rescale every row by its own factor (lane r's
+                    // row r; 1 while the row has seen nothing), in every lane
+                    const float al = (M != -INFINITY && Mb != M) ? __builtin_amdgcn_exp2f(M - Mb) : 1.f;
+                    L *= al;
 #pragma unroll
-                for (int cc2 = 0; cc2 < CPL; ++cc2) acc[rr][cc2] *= alr;
+                    for (int rr = 0; rr < RPW; ++rr) {
+                        const float alr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), rr));
+#pragma unroll
+                        for (int cc2 = 0; cc2 < CPL; ++cc2) acc[rr][cc2] *= alr;
+                    }
+                }
+                M = Mb;
+#pragma unroll
+                for (int i = 0; i < kMergeBatch; ++i) {
+                    if (base + i >= s0 && base + i < s_hi) {
+                        const float ms = __uint_as_float((uint32_t)w[i]);
+                        const float ls = __uint_as_float((uint32_t)(w[i] >> 32));
+                        // 0 for an empty split, and for every split of a row no split saw
+                        const float sc = M != -INFINITY ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
+                        L += ls * sc;
+#pragma unroll
+                        for (int rr = 0; rr < RPW; ++rr) {
+                            const float scr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), rr));
+                            if constexpr (CPL == 2) {
+                                acc[rr][0] += __uint_as_float((uint32_t)ov[i][rr]) * scr;
+                                acc[rr][1] += __uint_as_float((uint32_t)((uint64_t)ov[i][rr] >> 32)) * scr;
+                            } else {
+                                acc[rr][0] += __uint_as_float((uint32_t)ov[i][rr]) * scr;
+                            }
+                        }
+                    }
+                }
             }
-        }
-        M = Mb;
-#pragma unroll
-        for (int i = 0; i < kMergeBatch; ++i) {
-            if (s0 + i < S) {
-                const float ms = __uint_as_float((uint32_t)w[i]);
-                const float ls = __uint_as_float((uint32_t)(w[i] >> 32));
-                // 0 for an empty split, and for every split of a row no split saw
-                const float sc = M != -INFINITY ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
-                L += ls * sc;
+            {
+                const float wgt = L > 0.f ? gt[bi] / L : 0.f;
 #pragma unroll
                 for (int rr = 0; rr < RPW; ++rr) {
-                    const float scr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), rr));
-                    if constexpr (CPL == 2) {
-                        acc[rr][0] += __uint_as_float((uint32_t)ov[i][rr]) * scr;
-                        acc[rr][1] += __uint_as_float((uint32_t)((uint64_t)ov[i][rr] >> 32)) * scr;
-                    } else {
-                        acc[rr][0] += __uint_as_float((uint32_t)ov[i][rr]) * scr;
+                    const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), rr));
+#pragma unroll
+                    for (int cc2 = 0; cc2 < CPL; ++cc2) oacc[rr][cc2] += acc[rr][cc2] * wr;
+                }
+                if (lane < RPW && ok16 && a.lse)
+                    a.lse[oi16 * 3 + bi] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+            for (int cc2 = 0; cc2 < CPL; ++cc2) acc[rr][cc2] = oacc[rr][cc2];
+        L = 1.f;                                                     // acc is the output
+    } else {
+    #pragma unroll
+        for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+            for (int cc2 = 0; cc2 < CPL; ++cc2) acc[rr][cc2] = 0.f;
+        for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+            uint64_t w[kMergeBatch];
+            ovec ov[kMergeBatch][RPW];
+#pragma unroll
+            for (int i = 0; i < kMergeBatch; ++i) {
+                const size_t sp = (size_t)min(s0 + i, S - 1) * RP;
+                w[i] = __hip_atomic_load(pml + sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int rr = 0; rr < RPW; ++rr)
+                    ov[i][rr] = __hip_atomic_load(pob + (sp + rr) * kWave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            float Mb = M;
+#pragma unroll
+            for (int i = 0; i < kMergeBatch; ++i) Mb = fmaxf(Mb, __uint_as_float((uint32_t)w[i]));
+            if (s0 > 0) {
+                // earlier batches: rescale every row by its own factor (lane r's
+                // row r; 1 while the row has seen nothing), in every lane
+                const float al = (M != -INFINITY && Mb != M) ? __builtin_amdgcn_exp2f(M - Mb) : 1.f;
+                L *= al;
+#pragma unroll
+                for (int rr = 0; rr < RPW; ++rr) {
+                    const float alr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), rr));
+#pragma unroll
+                    for (int cc2 = 0; cc2 < CPL; ++cc2) acc[rr][cc2] *= alr;
+                }
+            }
+            M = Mb;
+#pragma unroll
+            for (int i = 0; i < kMergeBatch; ++i) {
+                if (s0 + i < S) {
+                    const float ms = __uint_as_float((uint32_t)w[i]);
+                    const float ls = __uint_as_float((uint32_t)(w[i] >> 32));
+                    // 0 for an empty split, and for every split of a row no split saw
+                    const float sc = M != -INFINITY ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
+                    L += ls * sc;
+#pragma unroll
+                    for (int rr = 0; rr < RPW; ++rr) {
+                        const float scr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), rr));
+                        if constexpr (CPL == 2) {
+                            acc[rr][0] += __uint_as_float((uint32_t)ov[i][rr]) * scr;
+                            acc[rr][1] += __uint_as_float((uint32_t)((uint64_t)ov[i][rr] >> 32)) * scr;
+                        } else {
+                            acc[rr][0] += __uint_as_float((uint32_t)ov[i][rr]) * scr;
+                        }
                     }
                 }
             }
@@ -622,24 +826,33 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
                 a.out[oi * D + lane] = acc[rr][0] * inv;
         }
     }
-    {
-        const int mr = wave * RPW + r16;
-        const int mcq = mr / G, mh = mr - (mr / G) * G;
-        if (lane < RPW && mcq < Cg && mr < Cg * G && a.lse) {
-            const size_t oi = ((size_t)b * a.NQ + q0 + mcq) * a.H_q + (size_t)g * G + mh;
-            a.lse[oi] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
-        }
+    if constexpr (!NSA) {
+        bool ok16;
+        size_t oi16;
+        row16(ok16, oi16);
+        if (lane < RPW && ok16 && a.lse) a.lse[oi16] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
     }
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + tg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-template <int D, int RW, bool GRP>
+template <int D, int RW, bool GRP, bool NSA = false>
 hipError_t launch_tw(const TiledArgs& a, hipStream_t s) {
     const size_t lds = tiled_lds_bytes(D, a.bm_words, GRP ? a.nbuf : kPrefillBufs);
     const unsigned tiles = (unsigned)((size_t)a.B * a.H_kv * a.n_tiles * (GRP ? a.n_split : 1));
-    hipLaunchKernelGGL((tiled_attn_kernel<D, RW, GRP>), dim3(tiles), dim3(RW * tiled_ksplit<RW, GRP>() * 64), lds, s, a);
+    hipLaunchKernelGGL((tiled_attn_kernel<D, RW, GRP, NSA>), dim3(tiles), dim3(RW * tiled_ksplit<RW, GRP>() * 64),
+                       lds, s, a);
     return hipGetLastError();
+}
+
+// verification tiles of RW row waves, plain or three-branch
+template <int D>
+hipError_t launch_grouped(const TiledArgs& a, int RW, hipStream_t s) {
+    if (a.nsa)
+        return RW == 8 ? launch_tw<D, 8, true, true>(a, s) : RW == 4 ? launch_tw<D, 4, true, true>(a, s)
+             : RW == 2 ? launch_tw<D, 2, true, true>(a, s) : launch_tw<D, 1, true, true>(a, s);
+    return RW == 8 ? launch_tw<D, 8, true>(a, s) : RW == 4 ? launch_tw<D, 4, true>(a, s)
+         : RW == 2 ? launch_tw<D, 2, true>(a, s) : launch_tw<D, 1, true>(a, s);
 }
 
 }  // namespace
@@ -689,7 +902,15 @@ hipError_t tiled_grant_lds() {
                            reinterpret_cast<const void*>(tiled_attn_kernel<64, 8, true>),
                            reinterpret_cast<const void*>(tiled_attn_kernel<64, 4, true>),
                            reinterpret_cast<const void*>(tiled_attn_kernel<64, 2, true>),
-                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 1, true>)};
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 1, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 8, true, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 4, true, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 2, true, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<128, 1, true, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 8, true, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 4, true, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 2, true, true>),
+                           reinterpret_cast<const void*>(tiled_attn_kernel<64, 1, true, true>)};
     for (const void* k : kerns) {
         const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTiledLdsMax);
         if (e != hipSuccess) return e;
@@ -712,14 +933,13 @@ hipError_t launch_tiled_attention(const TiledArgs& a, int d, hipStream_t s) {
                                                               : launch_tw<64, 2, false>(a, s);
     }
     const int RW = tiled_grouped_rw(a.Cq * a.G);
-    if (a.nbuf < 2 || a.nbuf > kMaxBufs || a.n_split < 1 || a.Cq * a.G > 128 ||
+    if (a.nbuf < 2 || a.nbuf > kMaxBufs || a.n_split < 1 || a.Cq * a.G > 128 || a.Cq > 32 ||
         tiled_lds_bytes(d, a.bm_words, a.nbuf) > kTiledLdsMax)
         return hipErrorInvalidValue;
-    if (d == 128)
-        return RW == 8 ? launch_tw<128, 8, true>(a, s) : RW == 4 ? launch_tw<128, 4, true>(a, s)
-             : RW == 2 ? launch_tw<128, 2, true>(a, s) : launch_tw<128, 1, true>(a, s);
-    return RW == 8 ? launch_tw<64, 8, true>(a, s) : RW == 4 ? launch_tw<64, 4, true>(a, s)
-         : RW == 2 ? launch_tw<64, 2, true>(a, s) : launch_tw<64, 1, true>(a, s);
+    // the three-branch mode: a split per branch, and groups of Cu queries that tile Cq
+    if (a.nsa && (a.n_split < 3 || a.Cu < 1 || a.Cq % a.Cu != 0 || a.cmp_stride < 1))
+        return hipErrorInvalidValue;
+    return d == 128 ? launch_grouped<128>(a, RW, s) : launch_grouped<64>(a, RW, s);
 }
 
 }  // namespace sda

@@ -488,6 +488,37 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
 // against 62-92 us for shapes with a single slot per compute unit or one
 // split for the 16-block compressed branch.
 constexpr int kNsaMaxWaves = 10;                     // the attention kernel's waves per workgroup
+
+// Exact-mode NSA verification of two or more queries per (batch, KV head)
+// runs on the row-tiled engine: a tile holds as many whole groups of group_C
+// queries as fit in 128 rows and 32 queries (all of them when they fit), so
+// the compressed cache and the window are loaded once per tile rather than
+// once per group, and the listed blocks' union once per tile.  Every tile
+// gets S >= 3 workgroups, which it shares among the branches at run time in
+// proportion to their block counts; K/V slots as for grouped verification.
+struct NsaTiles {
+    int Cq, n_tiles, tiles, RW, S, nbuf;
+};
+struct TilePlan {
+    int S, nbuf;
+};
+static TilePlan grouped_tile_plan(int tiles, int d, int NB_cap, int split_k);
+static NsaTiles nsa_tiles(int B, int NQ, int H_q, int H_kv, int d, int T_cap, int group_C, int mode) {
+    NsaTiles t{};
+    const int G = H_kv > 0 ? H_q / H_kv : 0;
+    if (mode != SDA_GROUP_EXACT || G < 1 || group_C < 1 || group_C > 32 || group_C * G > 128) return t;
+    const int cq = std::min((std::min(32, 128 / G) / group_C) * group_C, ceil_div(NQ, group_C) * group_C);
+    const int NB_cap = ceil_div(T_cap, kBlock);
+    if (cq < 2 || tiled_grouped_bufs(d, NB_cap) < 2) return t;
+    t.Cq = cq;
+    t.n_tiles = ceil_div(NQ, cq);
+    t.tiles = B * H_kv * t.n_tiles;
+    t.RW = tiled_grouped_rw(cq * G);
+    const TilePlan tp = grouped_tile_plan(t.tiles, d, NB_cap, 0);
+    t.S = std::max(3, tp.S);
+    t.nbuf = tp.nbuf;
+    return t;
+}
 struct NsaPlan {
     AttnPlan p;
     int ns_c, ns_s, ns_w;
@@ -514,10 +545,13 @@ static NsaPlan nsa_plan(int d, int rp, int tasks, int group_C, int mode, int T_c
 
 size_t sda_nsa_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int T_cap, int NC_cap,
                                 int window, int group_C, int mode) {
-    if (!attn_sizes_ok(B, NQ, H_q, H_kv, n_sel_max, d, 0) || group_C < 1 || group_C > 8 ||
-        group_C * (H_q / H_kv) > 32 || T_cap < 1 || ceil_div(T_cap, kBlock) > kMaxNBCap || NC_cap < 1 ||
-        window < 0 || (mode != SDA_GROUP_EXACT && mode != SDA_GROUP_SHARED_REP))
+    if (!attn_sizes_ok(B, NQ, H_q, H_kv, n_sel_max, d, 0) || group_C < 1 || group_C > 32 || T_cap < 1 ||
+        ceil_div(T_cap, kBlock) > kMaxNBCap || NC_cap < 1 || window < 0 ||
+        (mode != SDA_GROUP_EXACT && mode != SDA_GROUP_SHARED_REP))
         return 0;
+    const NsaTiles nt = nsa_tiles(B, NQ, H_q, H_kv, d, T_cap, group_C, mode);
+    if (nt.Cq) return tiled_ws_bytes(nt.tiles, nt.S, nt.RW, d);
+    if (group_C > 8 || group_C * (H_q / H_kv) > 32) return 0;
     const int rp = attn_rows_pad(group_C, H_q / H_kv);
     const int tasks = B * ceil_div(NQ, group_C) * H_kv;
     const NsaPlan n = nsa_plan(d, rp, tasks, group_C, mode, T_cap, n_sel_max, NC_cap, window);
@@ -539,11 +573,60 @@ sda_status_t sda_nsa_decode(const void* q, const void* k, const void* v, const v
     REQUIRE(NC_cap >= ceil_div(T_cap, cmp_stride), SDA_ERR_SHAPE, "NC_cap=%d < ceil(T_cap/cmp_stride)=%d", NC_cap,
             ceil_div(T_cap, cmp_stride));
     REQUIRE(window >= 0, SDA_ERR_SHAPE, "window=%d < 0", window);
-    REQUIRE(group_C >= 1 && group_C <= 8, SDA_ERR_UNSUPPORTED, "group_C=%d outside [1, 8]", group_C);
     REQUIRE(mode == SDA_GROUP_EXACT || mode == SDA_GROUP_SHARED_REP, SDA_ERR_SHAPE, "mode=%d", mode);
-    const int G = H_q / H_kv;
-    REQUIRE(group_C * G <= 32, SDA_ERR_UNSUPPORTED, "group_C*G=%d exceeds 32 rows", group_C * G);
+    REQUIRE(group_C >= 1 && group_C <= 32, SDA_ERR_UNSUPPORTED, "group_C=%d outside [1, 32]", group_C);
     REQUIRE(ceil_div(T_cap, kBlock) <= kMaxNBCap, SDA_ERR_UNSUPPORTED, "T_cap=%d beyond %d blocks", T_cap, kMaxNBCap);
+    const int G = H_q / H_kv;
+    const NsaTiles nt = nsa_tiles(B, NQ, H_q, H_kv, d, T_cap, group_C, mode);
+    if (nt.Cq) {
+        REQUIRE((long long)nt.tiles <= (1LL << 24), SDA_ERR_SHAPE, "B*tiles*H_kv=%d exceeds %d", nt.tiles, 1 << 24);
+        const size_t need = tiled_ws_bytes(nt.tiles, nt.S, nt.RW, d);
+        REQUIRE(ws && ws_bytes >= need, SDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0,
+                need);
+        REQUIRE(aligned16(ws), SDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+        TiledArgs t{};
+        t.q = static_cast<const uint16_t*>(q);
+        t.k = static_cast<const uint16_t*>(k);
+        t.v = static_cast<const uint16_t*>(v);
+        t.seq_len = seq_len;
+        t.block_idx = block_idx;
+        t.n_sel = n_sel;
+        t.out = out;
+        t.lse = lse_opt;
+        t.n_sel_max = n_sel_max;
+        t.T_cap = T_cap;
+        t.NB_cap = ceil_div(T_cap, kBlock);
+        t.B = B;
+        t.NQ = NQ;
+        t.H_q = H_q;
+        t.H_kv = H_kv;
+        t.G = G;
+        t.Cq = nt.Cq;
+        t.n_tiles = nt.n_tiles;
+        t.bm_words = t.NB_cap;
+        t.nbuf = nt.nbuf;
+        t.scale_log2 = scale * 1.4426950408889634f;
+        t.n_split = nt.S;
+        t.union_count = union_count_opt;
+        char* base = static_cast<char*>(ws);
+        const size_t rows = (size_t)nt.tiles * nt.S * nt.RW * 16;
+        t.counters = reinterpret_cast<int*>(base);
+        t.part_ml = reinterpret_cast<float*>(base + pad256((size_t)nt.tiles * 4));
+        t.part_o = t.part_ml + rows * 2;
+        t.nsa = 1;
+        t.kc = static_cast<const uint16_t*>(k_cmp);
+        t.vc = static_cast<const uint16_t*>(v_cmp);
+        t.gates = gates;
+        t.NC_cap = NC_cap;
+        t.cmp_stride = cmp_stride;
+        t.window = window;
+        t.Cu = group_C;
+        t.n_ugroups = ceil_div(NQ, group_C);
+        return hip_status(launch_tiled_attention(t, d, static_cast<hipStream_t>(stream)), "nsa_decode launch");
+    }
+    REQUIRE(group_C <= 8, SDA_ERR_UNSUPPORTED, "group_C=%d outside [1, 8] (up to 32 in exact mode)", group_C);
+    REQUIRE(group_C * G <= 32, SDA_ERR_UNSUPPORTED,
+            "group_C*G=%d exceeds 32 rows (up to 128 in exact mode)", group_C * G);
     const int n_groups = ceil_div(NQ, group_C);
     const long long tasks = (long long)B * n_groups * H_kv;
     REQUIRE(tasks <= kMaxGridYZ, SDA_ERR_SHAPE, "B*groups*H_kv=%lld exceeds %d", tasks, kMaxGridYZ);
@@ -980,9 +1063,6 @@ static bool grouped_on_tiles(int group_C, int G, int mode) {
 // LDS holds (up to four), S = CUs / tiles; when that leaves fewer than four
 // splits and two-slot workgroups fit twice per compute unit, two slots and
 // twice the splits.
-struct TilePlan {
-    int S, nbuf;
-};
 static TilePlan grouped_tile_plan(int tiles, int d, int NB_cap, int split_k) {
     const int nb_max = tiled_grouped_bufs(d, NB_cap);
     const bool two_fit = 2 * tiled_lds_bytes(d, NB_cap, 2) <= kTiledLdsMax;

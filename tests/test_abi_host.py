@@ -163,6 +163,14 @@ def test_nsa_workspace_and_validation(L):
     n = L.sda_nsa_decode_workspace(8, 1, 64, 8, 35, 128, 131072, 2048, 512, 1, 0)
     assert n in {dec(64, s) for s in range(3, 80)}
     assert L.sda_nsa_decode_workspace(8, 1, 64, 8, 35, 128, 131072, 2048, -1, 1, 0) == 0
+    # exact verification of 16 queries in groups of 4 (G = 4): one tile of all 16 queries (64 rows) per
+    # (batch, KV head), 32 tiles x 8 splits, the same as grouped verification's split-K workspace
+    n16 = L.sda_nsa_decode_workspace(4, 16, 32, 8, 16, 128, 65536, 1024, 512, 4, 0)
+    assert n16 == dec(32, 8, rows=64)
+    assert n16 == L.sda_grouped_decode_workspace(4, 1, 32, 8, 16, 128, 1024, 16, 0, 0)
+    # shared-representative mode keeps the per-group launch (16 padded rows per group of 4 x G = 4)
+    assert L.sda_nsa_decode_workspace(4, 16, 32, 8, 16, 128, 65536, 1024, 512, 4, 1) in \
+        {dec(128, s) for s in range(3, 80)}
     f = L.sda_nsa_decode
     # q, k, v, k_cmp, v_cmp, seq_len, block_idx, n_sel, n_sel_max, T_cap, NC_cap, cmp_stride, window,
     # gates, B, NQ, H_q, H_kv, d, scale, group_C, mode, out, lse, union_count, ws, ws_bytes, stream
@@ -178,9 +186,13 @@ def test_nsa_workspace_and_validation(L):
     assert f(*bad) == UNSUP
     bad = list(args); bad[12] = -1
     assert f(*bad) == SHAPE
-    bad = list(args); bad[20] = 9
+    bad = list(args); bad[20] = 9; bad[21] = 1                           # shared mode: group_C <= 8
     assert f(*bad) == UNSUP
-    bad = list(args); bad[20] = 8; bad[15] = 8; bad[16] = 16             # 8 queries x G = 8 > 32 rows
+    bad = list(args); bad[20] = 8; bad[15] = 8; bad[16] = 16; bad[21] = 1   # shared: 8 x G = 8 > 32 rows
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[20] = 33                                       # exact mode: group_C <= 32
+    assert f(*bad) == UNSUP
+    bad = list(args); bad[20] = 8; bad[15] = 8; bad[16] = 64             # exact: 8 x G = 32 > 128 rows
     assert f(*bad) == UNSUP
     bad = list(args); bad[26] = 64
     assert f(*bad) == WS

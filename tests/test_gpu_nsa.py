@@ -122,6 +122,13 @@ CASES = [
     (2, 8, 16, 4, 128, [8192, 6000], 16, 32, 16, 200, 4, 1),    # grouped, shared representative
     (1, 6, 8, 2, 64, [2048], 8, 64, 64, 130, 4, 0),             # last group smaller
     (3, 2, 8, 2, 64, [20, 1, 70], 2, 32, 16, 16, 2, 0),         # shorter than a block: one partial block
+    # exact mode with two or more queries per (batch, KV head) runs on row tiles that hold every group
+    (2, 8, 32, 4, 128, [8192, 6000], 16, 64, 64, 256, 8, 0),    # 8 queries x G = 8: 64 rows in one group
+    (1, 4, 8, 2, 64, [4096], 11, 32, 16, 300, 1, 0),            # one query per group, four share a tile
+    (2, 6, 8, 2, 64, [4096, 3001], 11, 32, 16, 100, 2, 0),      # unaligned window, 4x more compressed entries
+    (1, 32, 32, 8, 64, [2048], 8, 64, 64, 130, 4, 0),           # 32 queries x G = 4: a 128-row tile
+    (1, 40, 16, 4, 64, [3000], 9, 32, 16, 64, 4, 0),            # two tiles per KV head, the second of 8 queries
+    (1, 4, 8, 2, 128, [5000], 8, 64, 64, 0, 2, 0),              # no window
 ]
 
 
