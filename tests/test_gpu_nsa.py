@@ -51,6 +51,8 @@ def _lists(rng, B, NQ, H, lens, n_sel_max, short_rows=True):
     ns = np.zeros((B, NQ, H), dtype=np.int32)
     for b in range(B):
         nb = -(-lens[b] // 64)
+        if nb == 0:
+            continue                                     # an empty sequence lists nothing
         for q in range(NQ):
             for g in range(H):
                 n = min(n_sel_max, nb)
@@ -129,6 +131,7 @@ CASES = [
     (1, 32, 32, 8, 64, [2048], 8, 64, 64, 130, 4, 0),           # 32 queries x G = 4: a 128-row tile
     (1, 40, 16, 4, 64, [3000], 9, 32, 16, 64, 4, 0),            # two tiles per KV head, the second of 8 queries
     (1, 4, 8, 2, 128, [5000], 8, 64, 64, 0, 2, 0),              # no window
+    (2, 4, 8, 2, 64, [0, 100], 4, 32, 16, 50, 2, 0),            # an empty sequence: every branch empty
 ]
 
 
@@ -216,3 +219,33 @@ def test_nsa_c4_full_size_sampled_rows():
             err = max(err, float(np.abs(out_h[b, q, hs] - o).max()))
     _say("nsa c4: max |out - oracle|", err)
     assert err <= TOL
+
+
+def test_nsa_tiles_repeat_bit_identically():
+    # the row-tiled three-branch launch on one workspace: a call, a call of
+    # another shape (its split counters must come back to zero), then the
+    # first call again, whose output and lse must repeat bit for bit
+    B, H_q, H, d, lens = 2, 16, 4, 128, [8192, 6000]
+    cfg = dataclasses.replace(synth.get_config(2), B=B, H_q=H_q, H_kv=H, d=d, T=max(lens), NQ=8,
+                              bias_frac=0.0, bias_beta=0.0)
+    K, V, _ = inputs.kv_layer(cfg, 0, device=DEV)
+    kc, vc = _compressed(K, lens, 64, 64), _compressed(V, lens, 64, 64)
+    rng = np.random.default_rng(17)
+    seq = torch.as_tensor(lens, dtype=torch.int32, device=DEV)
+
+    def make(NQ):
+        Q = inputs.to_bf16(rng.standard_normal((B, NQ, H_q, d)).astype(np.float32)).to(DEV)
+        gates = torch.from_numpy(rng.uniform(0.0, 1.0, (B, NQ, H_q, 3)).astype(np.float32)).to(DEV)
+        bi, ns = _lists(rng, B, NQ, H, lens, 16)
+        return Q, gates, torch.from_numpy(bi).to(DEV), torch.from_numpy(ns).to(DEV)
+    a, b = make(8), make(6)
+    need = max(sda.lib().sda_nsa_decode_workspace(B, nq, H_q, H, 16, d, max(lens), kc.shape[2], w, 4, 0)
+               for nq, w in ((8, 256), (6, 130)))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    o1, l1, u1 = sda.sda_nsa_decode(a[0], K, V, kc, vc, seq, a[2], a[3], a[1], 64, 256, group_C=4, ws=ws)
+    o1, l1, u1 = o1.clone(), l1.clone(), u1.clone()
+    sda.sda_nsa_decode(b[0], K, V, kc, vc, seq, b[2], b[3], b[1], 64, 130, group_C=4, ws=ws)
+    o2, l2, u2 = sda.sda_nsa_decode(a[0], K, V, kc, vc, seq, a[2], a[3], a[1], 64, 256, group_C=4, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(u1, u2)
+    assert torch.equal(torch.nan_to_num(l1, neginf=-1e30), torch.nan_to_num(l2, neginf=-1e30))
