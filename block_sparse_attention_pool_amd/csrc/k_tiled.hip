@@ -327,8 +327,27 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
             seen += tot;
         }
     }
-    if (!NSA && a.union_count && split == 0 && threadIdx.x == 0)
-        a.union_count[((size_t)b * a.n_tiles + tile) * a.H_kv + g] = n_u;
+    // union_count: a tile of one group writes its union's size here; a tile
+    // of several groups of Cu queries counts each group's union from the
+    // bitmap after its walk (group_unions below)
+    if (GRP && a.union_count && split == 0 && a.Cu == a.Cq && threadIdx.x == 0)
+        a.union_count[((size_t)b * a.n_ugroups + tile) * a.H_kv + g] = n_u;
+    // wave w counts the union of groups w, w + W, ... of the tile's Cu-query
+    // groups (the bitmap is intact until the split merge's flag)
+    auto group_unions = [&]() {
+        if (!GRP || !a.union_count || split != 0 || a.Cu >= a.Cq) return;
+        for (int u = wave; u * a.Cu < Cg; u += W) {
+            const int c0 = u * a.Cu, c1 = min(c0 + a.Cu, Cg);
+            const uint32_t gm = (uint32_t)((((uint64_t)1 << c1) - 1) & ~(((uint64_t)1 << c0) - 1));
+            int cnt = 0;
+            for (int base = 0; base < nb; base += kWave) {
+                const int i = base + lane;
+                cnt += __popcll(__ballot(i < nb && (bm[i] & gm) != 0u));
+            }
+            if (lane == 0)
+                a.union_count[((size_t)b * a.n_ugroups + (size_t)tile * (a.Cq / a.Cu) + u) * a.H_kv + g] = cnt;
+        }
+    };
     // the block after j in the walk: the bitmap's next set word, or j + 1 in
     // a block range
     auto next_blk = [&](int j) { return (NSA && branch != 1) ? j + 1 : next_set(bm, j, nb); };
@@ -570,6 +589,7 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
     }
 
     if (!GRP || (!NSA && S == 1)) {
+        group_unions();
         if (th == 0 && row_ok && r < Cg * G) {
             const size_t oi = ((size_t)b * a.NQ + q0 + c) * a.H_q + (size_t)g * G + h;
             const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -601,23 +621,7 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
                                ((uint64_t)__float_as_uint(l_run) << 32) | __float_as_uint(m_run), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
-    if constexpr (NSA) {
-        // the listed blocks' union of each group of Cu queries (counted while
-        // the stores above are on their way): wave w counts groups w, w + W, ..
-        if (a.union_count && split == 0 && a.Cu > 1) {
-            for (int u = wave; u * a.Cu < Cg; u += W) {
-                const int c0 = u * a.Cu, c1 = min(c0 + a.Cu, Cg);
-                const uint32_t gm = (uint32_t)((((uint64_t)1 << c1) - 1) & ~(((uint64_t)1 << c0) - 1));
-                int cnt = 0;
-                for (int base = 0; base < nb; base += kWave) {
-                    const int i = base + lane;
-                    cnt += __popcll(__ballot(i < nb && (bm[i] & gm) != 0u));
-                }
-                if (lane == 0)
-                    a.union_count[((size_t)b * a.n_ugroups + (size_t)tile * (a.Cq / a.Cu) + u) * a.H_kv + g] = cnt;
-            }
-        }
-    }
+    group_unions();                         // while the stores above are on their way
     // the flag lives in the bitmap's first word: every wave is past its last
     // read of the bitmap at the barrier below (the kernel uses no static LDS,
     // so that the whole 160 KB can be granted to the dynamic part)
@@ -937,7 +941,8 @@ hipError_t launch_tiled_attention(const TiledArgs& a, int d, hipStream_t s) {
         tiled_lds_bytes(d, a.bm_words, a.nbuf) > kTiledLdsMax)
         return hipErrorInvalidValue;
     // the three-branch mode: a split per branch, and groups of Cu queries that tile Cq
-    if (a.nsa && (a.n_split < 3 || a.Cu < 1 || a.Cq % a.Cu != 0 || a.cmp_stride < 1))
+    // groups of Cu queries tile Cq; the three-branch mode needs a split per branch
+    if (a.Cu < 1 || a.Cq % a.Cu != 0 || (a.nsa && (a.n_split < 3 || a.cmp_stride < 1)))
         return hipErrorInvalidValue;
     return d == 128 ? launch_grouped<128>(a, RW, s) : launch_grouped<64>(a, RW, s);
 }

@@ -194,19 +194,18 @@ struct TiledArgs {
     float* part_o;            // [tiles, n_split, 16 W, d]
     float* part_ml;           // [tiles, n_split, 16 W, 2]
     int* counters;            // [tiles]; zero between calls
-    int32_t* union_count;     // [B, n_tiles, H_kv] blocks in each tile's union, or null
+    int32_t* union_count;     // [B, n_ugroups, H_kv] blocks in each group's union, or null
+    int Cu, n_ugroups;        // verification: groups of Cu queries (Cu divides Cq), ceil(NQ / Cu)
     // NSA three-branch mode (nsa = 1, verification tiles only): every tile
     // splits its n_split workgroups among the compressed cache, its listed
     // blocks and the window in proportion to their block counts (computed
     // alike by every workgroup of the tile); the last to arrive merges each
-    // branch and writes the gated sum and the three lse.  union_count is then
-    // per group of Cu queries: [B, n_ugroups, H_kv], Cu dividing Cq.
+    // branch and writes the gated sum and the three lse.
     int nsa;
     const uint16_t* kc;       // compressed keys   [B, H_kv, NC_cap, d]
     const uint16_t* vc;       // compressed values [B, H_kv, NC_cap, d]
     const float* gates;       // [B, NQ, H_q, 3]: g_c, g_s, g_w
     int NC_cap, cmp_stride, window;
-    int Cu, n_ugroups;
 };
 int tiled_queries_per_tile(int G);
 int tiled_waves_rows(int rows);   // 2, 4 or 8 waves for up to 128 rows
