@@ -1,9 +1,11 @@
 // Row-tiled block-sparse attention: many query rows of one KV head share
 // every block load.  Used for prefill, where every query position attends to
 // its own block set ([SparDA] eq. (3) and (7) per position; the complexity
-// section's eq. (15) counts k blocks of attention per query token), and for
-// exact verification of groups of more than 32 query heads ([SSV] core
-// mechanism 1: the union of the group's lists loaded once).
+// section's eq. (15) counts k blocks of attention per query token), for
+// exact verification of groups of two or more draft queries ([SSV] core
+// mechanism 1: the union of the group's lists loaded once), and for NSA's
+// three branches in exact mode ([SSV] NSA derivation steps 3-6: the
+// compressed cache, the listed blocks and the window, gated).
 //
 // A workgroup owns a tile of Cq consecutive queries of one (b, g): R = Cq*G
 // rows (query, head), 16 per wave, kept in registers for the whole walk (the
@@ -18,7 +20,10 @@
 // one wave, so nothing is merged inside a workgroup: each wave normalises and
 // writes its own rows.  Verification tiles may split their union among
 // several workgroups (split-K), whose (m, l, o) partials the last to finish
-// merges.
+// merges.  In the NSA mode each split walks one branch: a contiguous range
+// of compressed blocks or of window blocks (every query of the tile sees
+// them), or its share of the listed union; the merge keeps the branches
+// apart and applies the gates.
 //
 // Per block and wave (16 rows):
 //   S^T[tok][row] = K[tok][:] . Q[row][:]     16x16x32 bf16 MFMA; K is the A
