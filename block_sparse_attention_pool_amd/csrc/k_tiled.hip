@@ -340,7 +340,7 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
     // wave w counts the union of groups w, w + W, ... of the tile's Cu-query
     // groups (the bitmap is intact until the split merge's flag)
     auto group_unions = [&]() {
-        if (!GRP || !a.union_count || split != 0 || a.Cu >= a.Cq) return;
+        if (!GRP || !a.union_count || split != 0 || a.Cu >= a.Cq || a.Cu < 2) return;   // groups of one: no count
         for (int u = wave; u * a.Cu < Cg; u += W) {
             const int c0 = u * a.Cu, c1 = min(c0 + a.Cu, Cg);
             const uint32_t gm = (uint32_t)((((uint64_t)1 << c1) - 1) & ~(((uint64_t)1 << c0) - 1));

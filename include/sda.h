@@ -247,7 +247,8 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
  *   SDA_GROUP_SHARED_REP every query attends to the group's first list.
  *   block_idx must be ascending per row (as sda_score_select writes it).
  *   union_count_opt i32 [B, ceil(NQ / group_C), H_kv] out or NULL: blocks loaded
- *   per group (size of the merged set, or of the first list in shared mode).
+ *   per group (size of the merged set, or of the first list in shared mode);
+ *   written for group_C >= 2 only.
  * Other arguments (workspace contract included) as sda_sparse_decode.
  * Shared mode: group_C * G <= 32 and group_C <= 8.  Exact mode: group_C * G
  * up to 128 rows and group_C up to 32; groups of two or more queries run on
