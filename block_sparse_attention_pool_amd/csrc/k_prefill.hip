@@ -20,8 +20,9 @@
 //
 // Top-k per query without sorting: the largest threshold tau on the
 // order-preserving 32-bit score keys with at least k candidates at or above
-// it, found one bit at a time from the top (32 counting passes, each summed
-// over the query's four lanes); keys above tau are taken, and keys equal to
+// it, found one bit at a time from the top (up to 32 counting passes, each
+// summed over the query's four lanes, until exactly k keys lie at or above
+// the threshold so far); keys above tau are taken, and keys equal to
 // tau fill the rest in ascending block order (ties to the lower block id).
 // The block set (initial, local and chosen blocks) is written ascending by a
 // prefix count over the blocks in id order.
@@ -118,8 +119,13 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(PrefillSelectArgs a
         }
     }
 
-    // threshold: the largest tau with at least k_eff candidate keys >= tau
+    // threshold: the largest tau with at least k_eff candidate keys >= tau.
+    // Once exactly k_eff keys lie at or above the tau found so far, the lower
+    // bits can only raise tau inside the gap below the k_eff-th key: the keys
+    // at or above it, and so the chosen set, stay the same.  The wave stops
+    // when all its queries are there (most of them well before bit 0).
     uint32_t tau = 0u;
+    int at_tau = -1;                                     // keys >= tau, once tau has moved
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t t = tau | (1u << bit);
         int c = 0;
@@ -128,7 +134,12 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(PrefillSelectArgs a
             if (mt < nmt_s)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) c += key[mt][i] >= t ? 1 : 0;
-        if (sum4(c) >= k_eff) tau = t;
+        c = sum4(c);
+        if (c >= k_eff) {
+            tau = t;
+            at_tau = c;
+        }
+        if (__ballot(live && k_eff > 0 && at_tau != k_eff) == 0) break;
     }
     if (k_eff == 0) tau = 0xffffffffu;                   // nothing chosen (no finite key reaches it)
     int gt = 0, eq = 0;
