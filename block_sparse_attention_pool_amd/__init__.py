@@ -502,9 +502,9 @@ def sda_nsa_decode(q, k, v, k_cmp, v_cmp, seq_len, block_idx, n_sel, gates, cmp_
                    mode=SDA_GROUP_EXACT, scale=None, out=None, lse=None, union_count=None, ws=None, stream=None):
     """NSA verification output (compressed, selected-block and window branches,
     gated sum) in one launch; returns (out, lse [B, NQ, H_q, 3], union_count).
-    Exact mode takes group_C up to 32 and group_C * G up to 128 rows (two or
+    group_C up to 32 and group_C * G up to 128 rows in either mode (two or
     more queries per KV head run on row tiles that load the compressed cache
-    and the window once per tile); shared mode group_C <= 8, group_C * G <= 32."""
+    and the window once per tile)."""
     B, NQ, H_q, d, H, T_cap, n_sel_max = _attn_inputs(q, k, v, seq_len, block_idx, n_sel)
     _need(k_cmp, "k_cmp", torch.bfloat16, (B, H, None, d))
     _need(v_cmp, "v_cmp", torch.bfloat16, tuple(k_cmp.shape))

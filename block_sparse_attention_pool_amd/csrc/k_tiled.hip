@@ -220,7 +220,9 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
     }
     // entry i = (query i / n_sel_max, position i % n_sel_max) of the tile's
     // lists; the first kPre per thread are loaded here (indexes clamped into
-    // the lists so the loads need no branch), the rest after the clear
+    // the lists so the loads need no branch), the rest after the clear.  In
+    // shared-representative mode (rep) a query takes the list of its group's
+    // first query.
     const int nsm = a.n_sel_max;
     const int n_ent = Cg * nsm;
     const int nbmax = min(a.NB_cap, a.bm_words);         // blocks the bitmap holds
@@ -229,7 +231,7 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
     for (int u = 0; u < kPre; ++u) {
         const int i = min((int)threadIdx.x + u * NT, n_ent - 1);
         const int qc = i / nsm, e = i - qc * nsm;
-        const size_t row = ((size_t)b * a.NQ + q0 + qc) * a.H_kv + g;
+        const size_t row = ((size_t)b * a.NQ + q0 + (a.rep ? qc - qc % a.Cu : qc)) * a.H_kv + g;
         pn[u] = a.n_sel[row];
         pj[u] = a.block_idx[row * nsm + e];
     }
@@ -247,7 +249,7 @@ __global__ __launch_bounds__((RW * tiled_ksplit<RW, GRP>() * 64)) void tiled_att
     }
     for (int i = threadIdx.x + kPre * NT; i < n_ent; i += NT) {
         const int qc = i / nsm, e = i - qc * nsm;
-        const size_t row = ((size_t)b * a.NQ + q0 + qc) * a.H_kv + g;
+        const size_t row = ((size_t)b * a.NQ + q0 + (a.rep ? qc - qc % a.Cu : qc)) * a.H_kv + g;
         const int n = min(max(a.n_sel[row], 0), nsm);
         if (e < n) {
             const int j = a.block_idx[row * nsm + e];

@@ -489,8 +489,9 @@ sda_status_t sda_sparse_decode(const void* q, const void* k, const void* v, cons
 // split for the 16-block compressed branch.
 constexpr int kNsaMaxWaves = 10;                     // the attention kernel's waves per workgroup
 
-// Exact-mode NSA verification of two or more queries per (batch, KV head)
-// runs on the row-tiled engine: a tile holds as many whole groups of group_C
+// NSA verification of two or more queries per (batch, KV head) runs on the
+// row-tiled engine (in shared mode every query takes its group's first
+// list): a tile holds as many whole groups of group_C
 // queries as fit in 128 rows and 32 queries (all of them when they fit), so
 // the compressed cache and the window are loaded once per tile rather than
 // once per group, and the listed blocks' union once per tile.  Every tile
@@ -511,7 +512,7 @@ static TilePlan grouped_tile_plan(int tiles, int d, int NB_cap, int split_k);
 static NsaTiles nsa_tiles(int B, int NQ, int H_q, int H_kv, int d, int T_cap, int group_C, int mode) {
     NsaTiles t{};
     const int G = H_kv > 0 ? H_q / H_kv : 0;
-    if (mode != SDA_GROUP_EXACT || G < 1 || group_C < 1 || group_C > 32 || group_C * G > 128) return t;
+    if (G < 1 || group_C < 1 || group_C > 32 || group_C * G > 128) return t;
     const int cq = verify_tile_queries(NQ, group_C, G);
     const int NB_cap = ceil_div(T_cap, kBlock);
     if (cq < 2 || tiled_grouped_bufs(d, NB_cap) < 2) return t;
@@ -627,11 +628,13 @@ sda_status_t sda_nsa_decode(const void* q, const void* k, const void* v, const v
         t.window = window;
         t.Cu = group_C;
         t.n_ugroups = ceil_div(NQ, group_C);
+        t.rep = mode == SDA_GROUP_SHARED_REP;
         return hip_status(launch_tiled_attention(t, d, static_cast<hipStream_t>(stream)), "nsa_decode launch");
     }
-    REQUIRE(group_C <= 8, SDA_ERR_UNSUPPORTED, "group_C=%d outside [1, 8] (up to 32 in exact mode)", group_C);
-    REQUIRE(group_C * G <= 32, SDA_ERR_UNSUPPORTED,
-            "group_C*G=%d exceeds 32 rows (up to 128 in exact mode)", group_C * G);
+    REQUIRE(group_C * G <= 128, SDA_ERR_UNSUPPORTED, "group_C*G=%d exceeds 128 rows", group_C * G);
+    REQUIRE(group_C <= 8 && group_C * G <= 32, SDA_ERR_UNSUPPORTED,
+            "group_C=%d, G=%d: beyond 8 queries and 32 rows a group needs row tiles (two or more queries per "
+            "KV head, a bitmap of %d blocks within LDS)", group_C, G, ceil_div(T_cap, kBlock));
     const int n_groups = ceil_div(NQ, group_C);
     const long long tasks = (long long)B * n_groups * H_kv;
     REQUIRE(tasks <= kMaxGridYZ, SDA_ERR_SHAPE, "B*groups*H_kv=%lld exceeds %d", tasks, kMaxGridYZ);

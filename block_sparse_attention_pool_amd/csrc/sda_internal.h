@@ -196,6 +196,7 @@ struct TiledArgs {
     int* counters;            // [tiles]; zero between calls
     int32_t* union_count;     // [B, n_ugroups, H_kv] blocks in each group's union, or null
     int Cu, n_ugroups;        // verification: groups of Cu queries (Cu divides Cq), ceil(NQ / Cu)
+    int rep;                  // verification: every query takes its group's first list (shared mode)
     // NSA three-branch mode (nsa = 1, verification tiles only): every tile
     // splits its n_split workgroups among the compressed cache, its listed
     // blocks and the window in proportion to their block counts (computed

@@ -277,14 +277,13 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
  * once per group), and the window branch to tokens [seq_len - window, seq_len).
  * Each branch keeps its own softmax; the last workgroup of a row group merges
  * each branch's splits by log-sum-exp, normalises, and writes the gated sum.
- * In exact mode with two or more queries per KV head, row tiles of as many
- * whole groups as fit in 128 rows and 32 queries (all NQ queries when they
- * fit) load the compressed cache and the window once per tile; the result
- * is the same per query as with tiles of one group.
+ * With two or more queries per KV head, row tiles of as many whole groups as
+ * fit in 128 rows and 32 queries (all NQ queries when they fit) load the
+ * compressed cache and the window once per tile; the result is the same per
+ * query as with tiles of one group.
  *
  *   q .. n_sel_max, T_cap   as sda_grouped_decode (NB_cap = ceil(T_cap / 64))
- *   group_C, mode  exact mode: group_C <= 32 and group_C * G <= 128; shared
- *                  mode: group_C <= 8 and group_C * G <= 32 (SDA_ERR_UNSUPPORTED
+ *   group_C, mode  group_C <= 32 and group_C * G <= 128 (SDA_ERR_UNSUPPORTED
  *                  beyond)
  *   k_cmp, v_cmp  bf16 [B, H_kv, NC_cap, d]: compressed keys and values, e.g. from
  *                 sda_update_compressed_keys(_strided) applied to K and to V

@@ -168,9 +168,11 @@ def test_nsa_workspace_and_validation(L):
     n16 = L.sda_nsa_decode_workspace(4, 16, 32, 8, 16, 128, 65536, 1024, 512, 4, 0)
     assert n16 == dec(32, 8, rows=64)
     assert n16 == L.sda_grouped_decode_workspace(4, 1, 32, 8, 16, 128, 1024, 16, 0, 0)
-    # shared-representative mode keeps the per-group launch (16 padded rows per group of 4 x G = 4)
-    assert L.sda_nsa_decode_workspace(4, 16, 32, 8, 16, 128, 65536, 1024, 512, 4, 1) in \
-        {dec(128, s) for s in range(3, 80)}
+    # shared-representative mode runs on the same tiles
+    assert L.sda_nsa_decode_workspace(4, 16, 32, 8, 16, 128, 65536, 1024, 512, 4, 1) == n16
+    # one query per KV head in groups of one keeps the per-group launch (16 padded rows)
+    assert L.sda_nsa_decode_workspace(4, 1, 32, 8, 16, 128, 65536, 1024, 512, 1, 1) in \
+        {dec(32, s) for s in range(3, 80)}
     f = L.sda_nsa_decode
     # q, k, v, k_cmp, v_cmp, seq_len, block_idx, n_sel, n_sel_max, T_cap, NC_cap, cmp_stride, window,
     # gates, B, NQ, H_q, H_kv, d, scale, group_C, mode, out, lse, union_count, ws, ws_bytes, stream
@@ -186,10 +188,10 @@ def test_nsa_workspace_and_validation(L):
     assert f(*bad) == UNSUP
     bad = list(args); bad[12] = -1
     assert f(*bad) == SHAPE
-    bad = list(args); bad[20] = 9; bad[21] = 1                           # shared mode: group_C <= 8
+    bad = list(args); bad[20] = 33; bad[21] = 1                          # group_C <= 32 in either mode
     assert f(*bad) == UNSUP
-    bad = list(args); bad[20] = 8; bad[15] = 8; bad[16] = 16; bad[21] = 1   # shared: 8 x G = 8 > 32 rows
-    assert f(*bad) == UNSUP
+    bad = list(args); bad[16] = 128                                      # one query of G = 64 heads: no
+    assert f(*bad) == UNSUP                                              # tile, and beyond 32 rows
     bad = list(args); bad[20] = 33                                       # exact mode: group_C <= 32
     assert f(*bad) == UNSUP
     bad = list(args); bad[20] = 8; bad[15] = 8; bad[16] = 64             # exact: 8 x G = 32 > 128 rows

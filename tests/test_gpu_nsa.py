@@ -132,6 +132,8 @@ CASES = [
     (1, 40, 16, 4, 64, [3000], 9, 32, 16, 64, 4, 0),            # two tiles per KV head, the second of 8 queries
     (1, 4, 8, 2, 128, [5000], 8, 64, 64, 0, 2, 0),              # no window
     (2, 4, 8, 2, 64, [0, 100], 4, 32, 16, 50, 2, 0),            # an empty sequence: every branch empty
+    (2, 8, 32, 4, 128, [8192, 6000], 16, 64, 64, 256, 8, 1),    # shared mode, 64 rows per group
+    (1, 12, 16, 4, 64, [3000], 9, 32, 16, 100, 3, 1),           # shared mode, four groups of 3 in a tile
 ]
 
 
