@@ -757,8 +757,9 @@ def measure_grouped(O):
     sda.sda_update_compressed_keys(V, vc, zero, seq, cfg.T)
     gates = torch.rand((cfg.B, cfg.NQ, cfg.H_q, 3), generator=torch.Generator(device=dev).manual_seed(5),
                        device=dev, dtype=torch.float32)
-    nsa_ws = torch.zeros(sda.lib().sda_nsa_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d, cfg.T,
-                                                            cfg.NB, window, C, sda.SDA_GROUP_EXACT),
+    nsa_ws = torch.zeros(max(sda.lib().sda_nsa_decode_workspace(cfg.B, cfg.NQ, cfg.H_q, cfg.H_kv, n, cfg.d, cfg.T,
+                                                                cfg.NB, window, C, m)
+                             for m in (sda.SDA_GROUP_EXACT, sda.SDA_GROUP_SHARED_REP)),
                          dtype=torch.uint8, device=dev)
     nsa_lse = torch.empty((cfg.B, cfg.NQ, cfg.H_q, 3), dtype=torch.float32, device=dev)
     ucs_n = [torch.empty(uc_shape, dtype=torch.int32, device=dev) for _ in range(n_sets)]
@@ -793,6 +794,18 @@ def measure_grouped(O):
         "roofline_loaded": hbm((sel_blocks + win_blocks) * blk + cmp_loaded, t),
         "extra_us_over_mode_A": t * 1e6 - res["gammas"]["0.75"]["mode_A"]["us"],
     }
+    # the same three branches in shared-representative mode (every query takes
+    # its group's first list)
+    turn[0] = 0
+
+    def nsa_call_b():
+        i = turn[0] % n_sets
+        turn[0] += 1
+        sda.sda_nsa_decode(Q75, K, V, kc, vc, seq, sets75[i], ns, gates, 64, window, group_C=C,
+                           mode=sda.SDA_GROUP_SHARED_REP, out=out, lse=nsa_lse, union_count=ucs_n[i], ws=nsa_ws)
+    tb = graph_time(nsa_call_b, copies=n_sets)
+    res["nsa_three_branch_gamma_0.75"]["mode_B_us"] = tb * 1e6
+    log(f"NSA three branches at gamma 0.75: exact {t * 1e6:.1f} us, shared representative {tb * 1e6:.1f} us")
     # oracle: one group (C queries x G heads) of one (batch, KV head), mode A
     kk = O.bf16_to_f64(inputs.bf16_bits(K[0, 0, :cfg.T]))
     vv = O.bf16_to_f64(inputs.bf16_bits(V[0, 0, :cfg.T]))
