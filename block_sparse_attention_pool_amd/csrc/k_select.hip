@@ -228,6 +228,34 @@ struct ScoreArgs {
 
 constexpr int kScoresOnly = 0, kFusedSelect = 1;   // score_kernel modes
 
+// Level 1 for one vector by one wave (workgroups of several vectors give each
+// wave its own): lane l holds blocks l, l + 64, l + 128 and l + 192 of the
+// chunk; each quarter is sorted across the lanes, then the quarters are
+// merged pairwise (the lane-wise larger of one sorted list and the other
+// reversed is bitonic and holds the pair's best 64), and the best K keys of
+// the chunk are stored, largest first, as the four-wave level 1 does.
+__device__ __forceinline__ uint64_t lane_reverse64(uint64_t x, int lane) {
+    const int src = (lane ^ (kWave - 1)) << 2;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ void wave_chunk_top_k(const float* sc, int j0, int lo, int hi, int K, uint64_t* dst,
+                                                 int lane) {
+    uint64_t q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = i * kWave + lane, j = j0 + t;
+        q[i] = bitonic_sort<kWave, true>((j >= lo && j < hi) ? block_key(sc[t], j) : 0ull, lane);
+    }
+    const uint64_t r1 = lane_reverse64(q[1], lane), r3 = lane_reverse64(q[3], lane);
+    const uint64_t a = bitonic_merge_desc<kWave>(q[0] > r1 ? q[0] : r1, lane);
+    const uint64_t b = bitonic_merge_desc<kWave>(q[2] > r3 ? q[2] : r3, lane);
+    const uint64_t rb = lane_reverse64(b, lane);
+    const uint64_t c = bitonic_merge_desc<kWave>(a > rb ? a : rb, lane);
+    if (lane < K) __hip_atomic_store(dst + lane, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The selection inside a scoring launch: sc[v][t] holds the score of block
 // j0 + t for vector v0 + v of kv row `row` = b * H_kv + g (the grid is
 // (chunks, B * H_kv, vector tiles)).  Level 1 orders the chunk, level 2 (the
@@ -248,12 +276,21 @@ __device__ __forceinline__ void select_tail(const SelectArgs& s, uint64_t* cand,
     const int hi = max(lo, nb - s.n_local);
     __syncthreads();                                   // sc complete
 
-    // level 1: this chunk's best K keys, largest first
-    for (int v = 0; v < NV; ++v) {
-        const int vi = v0 + v;
-        if (vi >= nvec) break;                         // uniform over the workgroup
-        uint64_t* dst = cand + ((size_t)((b * NQ + vi) * H_kv + g) * nch + blockIdx.x) * K;
-        chunk_top_k(sc[v], j0, lo, hi, K, true, wl, dst, tid);
+    // level 1: this chunk's best K keys, largest first (one vector: the four
+    // waves together; several: a wave per vector, the vectors in parallel)
+    if constexpr (NV == 1) {
+        if (v0 < nvec) {                               // uniform over the workgroup
+            uint64_t* dst = cand + ((size_t)((b * NQ + v0) * H_kv + g) * nch + blockIdx.x) * K;
+            chunk_top_k(sc[0], j0, lo, hi, K, true, wl, dst, tid);
+        }
+    } else {
+        const int lane = tid % kWave, wave = tid / kWave;
+        for (int v = wave; v < NV; v += (int)blockDim.x / kWave) {
+            const int vi = v0 + v;
+            if (vi >= nvec) break;                     // uniform over the wave
+            uint64_t* dst = cand + ((size_t)((b * NQ + vi) * H_kv + g) * nch + blockIdx.x) * K;
+            wave_chunk_top_k(sc[v], j0, lo, hi, K, dst, lane);
+        }
     }
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's lists have landed

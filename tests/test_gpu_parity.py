@@ -196,7 +196,7 @@ def _gapped_rows(cand, top_k, scores_by_row, gap):
     return [r for r, s in scores_by_row.items() if O.cut_gap(s, cand, top_k) >= gap]
 
 
-@pytest.mark.parametrize("NQ,top_k", [(1, 16), (20, 16), (1, 80), (3, 80)])
+@pytest.mark.parametrize("NQ,top_k", [(1, 16), (20, 16), (7, 16), (64, 16), (1, 80), (3, 80)])
 def test_select_paths_match_oracle(NQ, top_k):
     # top_k <= 64: the selection runs inside the scoring launch (the last
     # arriving chunk workgroup merges per-chunk lists); top_k = 80: the
