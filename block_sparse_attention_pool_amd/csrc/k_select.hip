@@ -304,11 +304,34 @@ __device__ __forceinline__ void select_tail(const SelectArgs& s, uint64_t* cand,
     if (!last) return;
 
     // level 2: merge the nch chunk lists of each vector, then its block set
-    for (int v = 0; v < NV; ++v) {
-        const int vi = v0 + v;
-        if (vi >= nvec) break;
-        const int vrow = (b * NQ + vi) * H_kv + g;
-        finish_row<true>(s, cand + (size_t)vrow * nch * K, nch, vrow, nb, bufA, bufB);
+    if constexpr (NV == 1) {
+        if (v0 < nvec) {
+            const int vrow = (b * NQ + v0) * H_kv + g;
+            finish_row<true>(s, cand + (size_t)vrow * nch * K, nch, vrow, nb, bufA, bufB);
+        }
+    } else {
+        // the lists of all the workgroup's vectors are requested in one batch
+        // (when they fit) rather than one vector's after another's merge
+        constexpr int kPreKeys = 2048;
+        __shared__ uint64_t pre[kPreKeys];
+        const int per = nch * K;
+        const bool fits = NV * per <= kPreKeys;
+        if (fits) {
+            for (int i = tid; i < NV * per; i += blockDim.x) {
+                const int v = i / per, vi = v0 + v;
+                if (vi < nvec)
+                    pre[i] = __hip_atomic_load(cand + (size_t)((b * NQ + vi) * H_kv + g) * per + (i - v * per),
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+        }
+        for (int v = 0; v < NV; ++v) {
+            const int vi = v0 + v;
+            if (vi >= nvec) break;
+            const int vrow = (b * NQ + vi) * H_kv + g;
+            if (fits) finish_row<false>(s, pre + v * per, nch, vrow, nb, bufA, bufB);
+            else finish_row<true>(s, cand + (size_t)vrow * per, nch, vrow, nb, bufA, bufB);
+        }
     }
     if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
