@@ -256,6 +256,34 @@ __device__ __forceinline__ void wave_chunk_top_k(const float* sc, int j0, int lo
     if (lane < K) __hip_atomic_store(dst + lane, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Level 2 for one vector by one wave, when its nch chunk lists, each padded
+// to P = 2^ceil(log2 K) keys, fit in the 64 lanes (lane = chunk * P + key):
+// one sort of all of them across the lanes leaves the vector's best keys in
+// the first lanes, the same keys the pairwise merges of the four-wave level
+// 2 keep; then the block set is written as there (initial blocks, the chosen
+// ids ascending, local blocks, -1 padding) and the vector's count.
+__device__ __forceinline__ void wave_finish_row(const SelectArgs& s, const uint64_t* lists, int nch, int P,
+                                                int vrow, int nb, int lane) {
+    const int K = s.top_k;
+    const int lo = min(s.n_init, nb);                      // candidates are [lo, hi)
+    const int hi = max(lo, nb - s.n_local);
+    const int kk = min(K, hi - lo);
+    const int c = lane / P, p = lane - (lane / P) * P;
+    uint64_t x = (c < nch && p < K) ? lists[c * K + p] : 0ull;
+    x = bitonic_sort<kWave, true>(x, lane);
+    int32_t* out = s.block_idx + (size_t)vrow * s.n_sel_max;
+    if (kk > 0) {
+        uint32_t id = lane < kk ? 0xFFFFFFFFu - (uint32_t)x : 0xFFFFFFFFu;
+        id = bitonic_sort<kWave, false>(id, lane);
+        if (lane < kk) out[lo + lane] = (int)id;
+    }
+    for (int i = lane; i < lo; i += kWave) out[i] = i;                          // initial blocks
+    for (int i = lane; i < nb - hi; i += kWave) out[lo + kk + i] = hi + i;      // local blocks
+    const int total = lo + kk + (nb - hi);
+    for (int i = total + lane; i < s.n_sel_max; i += kWave) out[i] = -1;
+    if (lane == 0) s.n_sel[vrow] = total;
+}
+
 // The selection inside a scoring launch: sc[v][t] holds the score of block
 // j0 + t for vector v0 + v of kv row `row` = b * H_kv + g (the grid is
 // (chunks, B * H_kv, vector tiles)).  Level 1 orders the chunk, level 2 (the
@@ -325,12 +353,23 @@ __device__ __forceinline__ void select_tail(const SelectArgs& s, uint64_t* cand,
             }
             __syncthreads();
         }
-        for (int v = 0; v < NV; ++v) {
-            const int vi = v0 + v;
-            if (vi >= nvec) break;
-            const int vrow = (b * NQ + vi) * H_kv + g;
-            if (fits) finish_row<false>(s, pre + v * per, nch, vrow, nb, bufA, bufB);
-            else finish_row<true>(s, cand + (size_t)vrow * per, nch, vrow, nb, bufA, bufB);
+        const int P = pow2_at_least(K);
+        if (fits && nch * P <= kWave) {
+            // a wave per vector, the vectors in parallel
+            const int lane = tid % kWave, wave = tid / kWave;
+            for (int v = wave; v < NV; v += (int)blockDim.x / kWave) {
+                const int vi = v0 + v;
+                if (vi >= nvec) break;                     // uniform over the wave
+                wave_finish_row(s, pre + v * per, nch, P, (b * NQ + vi) * H_kv + g, nb, lane);
+            }
+        } else {
+            for (int v = 0; v < NV; ++v) {
+                const int vi = v0 + v;
+                if (vi >= nvec) break;
+                const int vrow = (b * NQ + vi) * H_kv + g;
+                if (fits) finish_row<false>(s, pre + v * per, nch, vrow, nb, bufA, bufB);
+                else finish_row<true>(s, cand + (size_t)vrow * per, nch, vrow, nb, bufA, bufB);
+            }
         }
     }
     if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
