@@ -18,8 +18,9 @@
 // Tile engine (one wave, one 64-token block; rows = the C*G query heads,
 // padded to 16 or 32):
 //   S^T[tok][row] = K[tok][:] . Q[row][:]    16x16x32 bf16 MFMA.  K is the A
-//       operand, loaded from HBM straight into MFMA layout (16-byte loads,
-//       rows past the sequence end clamped, no branches).
+//       operand, loaded from HBM in whole 128-byte lines (16-byte loads,
+//       rows past the sequence end clamped, no branches) and brought into
+//       MFMA layout by one DPP exchange per register pair (kswap).
 //   online softmax per row in fp32 (exp2 with scale*log2(e) folded in).
 //   O^T[d][row] += V^T[d][tok] P^T[tok][row]  16x16x32 bf16 MFMA.  V moves
 //       HBM -> LDS by direct (DMA) loads, never occupying VGPRs, and is read
@@ -98,6 +99,31 @@ __device__ __forceinline__ void kwait(u32x4 (&kf)[4][KS]) {
                        "+v"(kf[2][0]), "+v"(kf[2][1]), "+v"(kf[3][0]), "+v"(kf[3][1])
                      : "n"(N) : "memory");
     }
+}
+
+// K tile from whole-line loads to the MFMA A layout.  Load kf[mt][2h + x]
+// holds, in lane l, row tok_of(mt, 8x + l%8) and the 16-byte piece
+// (l/16) + 4 ((l/8) % 2) of the row's 128-byte line h: every load reads 8
+// whole lines (loads of 64 bytes from each of 16 rows, two per line, streamed
+// up to 1.3x slower once a wave walks more than one block).  The A layout
+// wants lane l to hold row tok_of(mt, l%16) and piece 4k + l/16 of line h in
+// kf[mt][2h + k].  Lanes with l%16 < 8 of load x = 0 and lanes with l%16 >= 8
+// of load x = 1 already do; the other halves trade places with the lane 8
+// apart in the same 16-lane row (DPP row rotation by 8, write-masked to
+// lane groups 2-3 or 0-1 of each row).
+template <int KS>
+__device__ __forceinline__ void kswap(u32x4 (&kf)[4][KS]) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int h = 0; h < KS / 2; ++h) {
+            const u32x4 a = kf[mt][2 * h], b = kf[mt][2 * h + 1];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                kf[mt][2 * h][c] = (uint32_t)__builtin_amdgcn_update_dpp((int)a[c], (int)b[c], 0x128, 0xF, 0xC, false);
+                kf[mt][2 * h + 1][c] = (uint32_t)__builtin_amdgcn_update_dpp((int)b[c], (int)a[c], 0x128, 0xF, 0x3, false);
+            }
+        }
 }
 
 // Every vector load has landed; the Q fragments pass through as in-out operands
@@ -536,17 +562,22 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
         // K loads are issued as asm so that the compiler does not fold the V
         // direct loads issued after them into its wait for K: the explicit
         // vmcnt wait below lets exactly the kLoads V loads stay in flight.
+        // Each load covers whole 128-byte lines: load (mt, h, x) brings rows
+        // tok_of(mt, 8x + l%8) x bytes [128h, 128h + 128) (see kswap).
         u32x4 kf[4][KS];
+        const uint32_t kline = (uint32_t)(((lane >> 4) + 4 * ((lane >> 3) & 1)) * 16);   // piece inside a line
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const uint32_t off = (uint32_t)min(tok_of(mt, li), tmax) * (D * 2) + lg * 16;
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                if constexpr (KSTREAM)
-                    asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(kf[mt][ks]) : "v"(kb + off + ks * 64) : "memory");
-                else
-                    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(kf[mt][ks]) : "v"(kb + off + ks * 64) : "memory");
-        }
+            for (int x = 0; x < 2; ++x) {
+                const uint32_t off = (uint32_t)min(tok_of(mt, 8 * x + (lane & 7)), tmax) * (D * 2) + kline;
+#pragma unroll
+                for (int h = 0; h < KS / 2; ++h)
+                    if constexpr (KSTREAM)
+                        asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(kf[mt][2 * h + x]) : "v"(kb + off + h * 128) : "memory");
+                    else
+                        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(kf[mt][2 * h + x]) : "v"(kb + off + h * 128) : "memory");
+            }
 #pragma unroll
         for (int i = 0; i < VTile<D>::kLoads; ++i) {
             const int t = i * VRPI + v_lrow;
@@ -555,6 +586,7 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
             lds_dma16<KSTREAM ? 0 : 2>(vb + off, vs_lds + i * kWave * 16);   // 2: non-temporal
         }
         kwait<VTile<D>::kLoads, KS>(kf);                    // K (and everything before it) has landed
+        kswap<KS>(kf);
         if (it == 0) {                                       // so have the Q fragments
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
