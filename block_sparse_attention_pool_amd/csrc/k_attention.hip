@@ -101,31 +101,6 @@ __device__ __forceinline__ void kwait(u32x4 (&kf)[4][KS]) {
     }
 }
 
-// K tile from whole-line loads to the MFMA A layout.  Load kf[mt][2h + x]
-// holds, in lane l, row tok_of(mt, 8x + l%8) and the 16-byte piece
-// (l/16) + 4 ((l/8) % 2) of the row's 128-byte line h: every load reads 8
-// whole lines (loads of 64 bytes from each of 16 rows, two per line, streamed
-// up to 1.3x slower once a wave walks more than one block).  The A layout
-// wants lane l to hold row tok_of(mt, l%16) and piece 4k + l/16 of line h in
-// kf[mt][2h + k].  Lanes with l%16 < 8 of load x = 0 and lanes with l%16 >= 8
-// of load x = 1 already do; the other halves trade places with the lane 8
-// apart in the same 16-lane row (DPP row rotation by 8, write-masked to
-// lane groups 2-3 or 0-1 of each row).
-template <int KS>
-__device__ __forceinline__ void kswap(u32x4 (&kf)[4][KS]) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int h = 0; h < KS / 2; ++h) {
-            const u32x4 a = kf[mt][2 * h], b = kf[mt][2 * h + 1];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                kf[mt][2 * h][c] = (uint32_t)__builtin_amdgcn_update_dpp((int)a[c], (int)b[c], 0x128, 0xF, 0xC, false);
-                kf[mt][2 * h + 1][c] = (uint32_t)__builtin_amdgcn_update_dpp((int)b[c], (int)a[c], 0x128, 0xF, 0x3, false);
-            }
-        }
-}
-
 // Every vector load has landed; the Q fragments pass through as in-out operands
 // so their registers stay reserved until here on every path (a wave whose
 // list part is empty never reaches the K wait).

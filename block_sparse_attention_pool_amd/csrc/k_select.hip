@@ -664,13 +664,19 @@ __global__ __launch_bounds__(256) void mh_score_kernel(const uint16_t* __restric
     if (jw < nb) {
         u32x4 qf[KS], kf[4][KS];
         const uint16_t* qp = q + (hrow0 + min(li, G - 1)) * D + lg * 8;
-        const uint16_t* kb = kt + (size_t)row * NB_cap * D + lg * 8;
+        // whole 128-byte lines per load, then kswap to the A layout (lane l:
+        // key jw + 16 mt + l % 16, dims 32 ks + 8 (l / 16))
+        const char* kb = reinterpret_cast<const char*>(kt + (size_t)row * NB_cap * D) +
+                         ((lane >> 4) + 4 * ((lane >> 3) & 1)) * 16;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int key = min(jw + mt * 16 + li, nb - 1);   // past the length: a real key, result unused
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = ldg16(kb + (size_t)key * D + ks * 32);
-        }
+            for (int x = 0; x < 2; ++x) {
+                const int key = min(jw + mt * 16 + 8 * x + (lane & 7), nb - 1);   // past the length: a real key, result unused
+#pragma unroll
+                for (int h = 0; h < KS / 2; ++h) kf[mt][2 * h + x] = ldg16(kb + (size_t)key * D * 2 + h * 128);
+            }
+        kswap<KS>(kf);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = ldg16_cached(qp + ks * 32);
 #pragma unroll
