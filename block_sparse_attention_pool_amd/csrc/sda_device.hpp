@@ -81,29 +81,35 @@ __device__ __forceinline__ floatx4 mfma16x16x32(const u32x4& a, const u32x4& b, 
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// A tile of 64 rows (keys) from whole-line loads to the MFMA A layout.  Load kf[mt][2h + x]
-// holds, in lane l, row tok_of(mt, 8x + l%8) and the 16-byte piece
-// (l/16) + 4 ((l/8) % 2) of the row's 128-byte line h: every load reads 8
-// whole lines (loads of 64 bytes from each of 16 rows, two per line, streamed
-// up to 1.3x slower once a wave walks more than one block).  The A layout
-// wants lane l to hold row tok_of(mt, l%16) and piece 4k + l/16 of line h in
-// kf[mt][2h + k].  Lanes with l%16 < 8 of load x = 0 and lanes with l%16 >= 8
-// of load x = 1 already do; the other halves trade places with the lane 8
-// apart in the same 16-lane row (DPP row rotation by 8, write-masked to
-// lane groups 2-3 or 0-1 of each row).
+// Registers of a 16-row MFMA A tile (m-tile mt) loaded in whole 128-byte
+// lines.  Load kf[mt][2h + x] holds, in lane l, tile row 8x + l%8 (the
+// tile's row order: tok_of in the decode, consecutive keys elsewhere) and
+// the 16-byte piece (l/16) + 4 ((l/8) % 2) of that row's line h, so every
+// load reads 8 whole lines.  (The direct A-layout load reads 64 bytes from
+// each of 16 rows, so two loads fetch halves of each line; it streamed up to
+// 1.3x slower once a wave walks more than one tile.)  The A layout wants
+// lane l to hold tile row l%16 and piece 4k + l/16 of line h in
+// kf[mt][2h + k].  Lanes with l%16 < 8 of load x = 0 and lanes with
+// l%16 >= 8 of load x = 1 already do; the other halves trade places with the
+// lane 8 apart in the same 16-lane row (DPP row rotation by 8, write-masked
+// to lane groups 2-3 or 0-1 of each row).
+// kswap1 exchanges one m-tile's registers, kswap the four of a 64-row tile.
+template <int KS>
+__device__ __forceinline__ void kswap1(u32x4 (&kf)[KS]) {
+#pragma unroll
+    for (int h = 0; h < KS / 2; ++h) {
+        const u32x4 a = kf[2 * h], b = kf[2 * h + 1];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            kf[2 * h][c] = (uint32_t)__builtin_amdgcn_update_dpp((int)a[c], (int)b[c], 0x128, 0xF, 0xC, false);
+            kf[2 * h + 1][c] = (uint32_t)__builtin_amdgcn_update_dpp((int)b[c], (int)a[c], 0x128, 0xF, 0x3, false);
+        }
+    }
+}
 template <int KS>
 __device__ __forceinline__ void kswap(u32x4 (&kf)[4][KS]) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int h = 0; h < KS / 2; ++h) {
-            const u32x4 a = kf[mt][2 * h], b = kf[mt][2 * h + 1];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                kf[mt][2 * h][c] = (uint32_t)__builtin_amdgcn_update_dpp((int)a[c], (int)b[c], 0x128, 0xF, 0xC, false);
-                kf[mt][2 * h + 1][c] = (uint32_t)__builtin_amdgcn_update_dpp((int)b[c], (int)a[c], 0x128, 0xF, 0x3, false);
-            }
-        }
+    for (int mt = 0; mt < 4; ++mt) kswap1<KS>(kf[mt]);
 }
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) {
