@@ -735,12 +735,10 @@ __device__ __forceinline__ void run_tile_engine(const AttnArgs& a, ListView L, i
             if (d4 == 0 && a.lse) a.lse[oi] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994531f : -INFINITY;
         } else {
             const size_t pi = ((size_t)task * a.n_split + split) * RP + r;
-            // agent-scope stores: the merging workgroup may sit on another XCD
-            uint64_t* po = reinterpret_cast<uint64_t*>(&a.part_o[pi * D + d4]);
-            __hip_atomic_store(po, ((uint64_t)__float_as_uint(Os[1]) << 32) | __float_as_uint(Os[0]),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(po + 1, ((uint64_t)__float_as_uint(Os[3]) << 32) | __float_as_uint(Os[2]),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // device-scope (write-through) stores: the merging workgroup may
+            // sit on another XCD; the four columns go out as one 16-byte
+            // store from the split's wave-uniform base
+            st_agent16(a.part_o + ((size_t)task * a.n_split + split) * RP * D, (uint32_t)((r * D + d4) * 4), Os);
             if (d4 == 0)
                 __hip_atomic_store(reinterpret_cast<uint64_t*>(&a.part_ml[pi * 2]),
                                    ((uint64_t)__float_as_uint(Ls) << 32) | __float_as_uint(M),
