@@ -1084,6 +1084,10 @@ static TilePlan grouped_tile_plan(int tiles, int d, int NB_cap, int split_k) {
     return TilePlan{S1, nb_max};
 }
 
+// queries per tile of exact grouped verification: as many whole groups as
+// fit in 128 rows (of G heads) and 32 queries, as for NSA
+static int grouped_tile_queries(int NQ, int group_C, int G) { return verify_tile_queries(NQ, group_C, G); }
+
 size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_max, int d, int NB_cap,
                                     int group_C, int mode, int split_k) {
     if (!attn_sizes_ok(B, NQ, H_q, H_kv, n_sel_max, d, split_k) || group_C < 1 || group_C > 32 || NB_cap < 1 ||
@@ -1092,8 +1096,11 @@ size_t sda_grouped_decode_workspace(int B, int NQ, int H_q, int H_kv, int n_sel_
     const int G = H_q / H_kv;
     const int n_groups = ceil_div(NQ, group_C);
     const int tasks = B * n_groups * H_kv;
-    if (grouped_on_tiles(group_C, G, mode))
-        return tiled_ws_bytes(tasks, grouped_tile_plan(tasks, d, NB_cap, split_k).S, tiled_grouped_rw(group_C * G), d);
+    if (grouped_on_tiles(group_C, G, mode)) {
+        const int cq = grouped_tile_queries(NQ, group_C, G);
+        const int tiles = B * ceil_div(NQ, cq) * H_kv;
+        return tiled_ws_bytes(tiles, grouped_tile_plan(tiles, d, NB_cap, split_k).S, tiled_grouped_rw(cq * G), d);
+    }
     if (group_C > 8 || group_C * G > 32) return 0;
     const int rp = attn_rows_pad(group_C, G);
     const AttnPlan p = attn_plan(d, rp, tasks, grouped_list_estimate(group_C, mode, n_sel_max), group_C, mode,
@@ -1118,13 +1125,13 @@ sda_status_t sda_grouped_decode(const void* q, const void* k, const void* v, con
     const long long tasks = (long long)B * n_groups * H_kv;
     if (grouped_on_tiles(group_C, G, mode)) {
         REQUIRE(tasks <= (1LL << 24), SDA_ERR_SHAPE, "B*groups*H_kv=%lld exceeds %d", tasks, 1 << 24);
-        // one tile per group: tiles of several groups (as NSA uses) measured
-        // slower here (25.8 against 23.7 us for groups of 4 at the 64K
-        // verification workload), their longer walks outweighing the loads
-        // they share
-        const int cq = group_C;
-        const int n_tiles = n_groups;
-        const int tiles = (int)tasks;
+        // tiles of several whole groups: the union of the tile's lists is
+        // loaded once and every row masked to its own list, with the union
+        // counted per group (groups of 4 at the 64K verification workload:
+        // 25.8 against 27.1 us with a tile per group, alternated on one box)
+        const int cq = grouped_tile_queries(NQ, group_C, G);
+        const int n_tiles = ceil_div(NQ, cq);
+        const int tiles = B * n_tiles * H_kv;
         const int RW = tiled_grouped_rw(cq * G);
         REQUIRE(tiled_grouped_bufs(d, NB_cap) >= 2, SDA_ERR_UNSUPPORTED, "NB_cap=%d: bitmap beyond LDS", NB_cap);
         const TilePlan tp = grouped_tile_plan(tiles, d, NB_cap, split_k);

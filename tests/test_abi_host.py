@@ -76,16 +76,20 @@ def test_workspace_sizes(L):
     assert n in {dec(64, s) for s in range(2, 36)}
     assert L.sda_sparse_decode_workspace(8, 1, 64, 8, 35, 128, 7) == dec(64, 7)
     assert L.sda_sparse_decode_workspace(8, 1, 64, 8, 35, 128, 1) == 0
-    assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 1024, 4, 0, 3) == dec(4 * 4 * 8, 3)
+    # exact groups of 4 at G = 4: tiles of all 16 queries (64 rows), one per (b, KV head)
+    assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 1024, 4, 0, 3) == dec(4 * 8, 3, rows=64)
     assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 0, 4, 0, 3) == 0      # NB_cap < 1
-    # exact groups on the row-tiled engine: partials per split for the tile's
+    # exact groups on the row-tiled engine: a tile holds as many whole groups
+    # as fit in 128 rows and 32 queries; partials per split for the tile's
     # rows (16 per row wave); the library's split count fills the compute
     # units once (one workgroup each), or twice with two-slot workgroups when
     # that gives fewer than four splits
     assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 1024, 16, 0, 0) == dec(32, 8, rows=64)
-    assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 1024, 4, 0, 0) == dec(128, 4, rows=16)
-    assert L.sda_grouped_decode_workspace(4, 16, 64, 8, 16, 128, 1024, 2, 0, 0) == dec(256, 2, rows=16)
-    assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 1024, 8, 0, 0) == dec(64, 4, rows=32)
+    assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 1024, 4, 0, 0) == dec(32, 8, rows=64)
+    assert L.sda_grouped_decode_workspace(4, 16, 64, 8, 16, 128, 1024, 2, 0, 0) == dec(32, 8, rows=128)
+    assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 1024, 8, 0, 0) == dec(32, 8, rows=64)
+    # groups of 3: tiles of 18 queries (six groups, the last holding one query; 72 rows on 8 row waves)
+    assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 1024, 3, 0, 0) == dec(32, 8, rows=128)
     assert L.sda_grouped_decode_workspace(4, 16, 32, 8, 16, 128, 1024, 4, 1, 0) > 0  # shared mode: grouped engine
 
 
